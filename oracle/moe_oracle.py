@@ -1,0 +1,407 @@
+"""Plain CPU oracle for the forward pass of a top-k routed MoE FFN layer.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import or call this module: only
+the tests, the smoke check and the CPU-baseline leg of the benchmark use it. It shares no
+code with the HIP library; both receive the same seeded inputs and nothing else.
+
+Pages cited (by title):
+  [P2] "Twinkle首发适配Deepseek-V4系列模型高效训练" (www.wmrh.cn/news/44033)
+  [P3] "DeepSpeed ZeRO-3与MoE显存精算实战指南" (m.nlpx.cn/news/237350)
+  [P4] "手搓一个LLaMA4-MoE" (www.nxmr.cn/news/140631)
+
+Arithmetic: every dot product and sum is done in float64 (numpy; matrix products use the BLAS
+dgemm as a primitive) and rounded once at the storage points the layer defines: router
+logits to fp32; H, Y and the output to the storage dtype (bf16 round-to-nearest-even or fp32);
+gate weights to fp32. The selection key is formed in fp32 exactly as the layer does (an fp32
+add, then an fp32 divide), because it decides an integer (the chosen experts).
+
+Readings where the pages are silent or disagree (each is listed with its reason in the design
+notes): select on the key, lowest expert index wins ties, -0.0 ties +0.0; weights are the
+softmax restricted to the selected logits; noise changes selection only; capacity keeps the
+first C assignments of an expert in (token, slot) order; a dropped slot contributes zero;
+aux losses use pre-drop counts.
+
+Every function is pinned by the CPU tests in tests/test_oracle_pins.py (brute force, closed
+forms, invariants and a hand-worked example). There is no "parity unpinned" function.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------------------------
+# storage rounding
+# ---------------------------------------------------------------------------------------------
+
+def round_bf16(a) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value (ties to even), returned as float64.
+
+    bfloat16 keeps 8 significant bits and the fp32 exponent range; the quantum of a value with
+    binary exponent e (a = m * 2**e, 0.5 <= |m| < 1) is 2**(e - 8), floored at the subnormal
+    quantum 2**-133.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    _, e = np.frexp(a)
+    q_exp = np.maximum(e, -125) - 8
+    return np.ldexp(np.rint(np.ldexp(a, -q_exp)), q_exp)
+
+
+def round_storage(a, storage: str) -> np.ndarray:
+    """Round float64 values to the storage dtype ("bf16" or "f32"); float64 result."""
+    if storage == "bf16":
+        return round_bf16(a)
+    if storage == "f32":
+        return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+    raise ValueError(f"unknown storage dtype {storage!r}")
+
+
+def _f64(a) -> np.ndarray:
+    """Exact widening of fp32 / bf16 (given as float32) data to float64."""
+    if hasattr(a, "detach"):          # a torch tensor: bf16 -> fp32 is exact
+        a = a.detach().float().cpu().numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+def _f32(a) -> np.ndarray:
+    if hasattr(a, "detach"):
+        a = a.detach().float().cpu().numpy()
+    return np.asarray(a, dtype=np.float32)
+
+
+# ---------------------------------------------------------------------------------------------
+# routing  ([P2 §3.1], [P4 §1.3, §2.4])
+# ---------------------------------------------------------------------------------------------
+
+def router_logits(x, w_router, bias=None) -> np.ndarray:
+    """logits[t, e] = sum_c x[t, c] * W_r[e, c] + b[e], exact in float64, rounded once to fp32.
+
+    P4 §2.4: the router is a linear layer producing one score per expert; P2 §3.1 writes
+    scores = W_router x. The per-expert bias is the workload's load-skew term.
+    """
+    l = _f64(x) @ _f64(w_router).T
+    if bias is not None:
+        l = l + _f64(bias)[None, :]
+    return l.astype(np.float32)
+
+
+def selection_keys(logits, gumbel=None, tau: float = 1.0) -> np.ndarray:
+    """fp32 key that top-k ranks: the logits, or (logits + g) / tau with Gumbel noise g.
+
+    P2 §3.1 forms the noisy logits as (logits + gumbel) / temperature and ranks them with top-k.
+    Computed in fp32: one rounded add, then one rounded divide by tau (tau itself held in fp32).
+    """
+    l = _f32(logits)
+    if gumbel is None:
+        return l.copy()
+    s = np.add(l, _f32(gumbel), dtype=np.float32)
+    return np.divide(s, np.float32(tau), dtype=np.float32)
+
+
+def top_k(keys, k: int) -> np.ndarray:
+    """ids[t, :] = the k largest keys of row t, in descending order, lowest index on ties.
+
+    P2 §3.1 and P4 §1.3: each token goes to the k experts with the highest scores. Done as k
+    rounds of "take the largest key not taken yet"; np.argmax returns the first maximum, so the
+    lowest expert index wins a tie, and -0.0 compares equal to +0.0.
+    """
+    kf = _f64(keys)
+    if not np.all(np.isfinite(kf)):
+        raise ValueError("oracle top_k: keys must be finite")
+    T, E = kf.shape
+    if not 1 <= k <= E:
+        raise ValueError("oracle top_k: need 1 <= k <= E")
+    work = kf.copy()
+    ids = np.empty((T, k), dtype=np.int32)
+    rows = np.arange(T)
+    for j in range(k):
+        pick = np.argmax(work, axis=1)
+        ids[:, j] = pick
+        work[rows, pick] = -np.inf
+    return ids
+
+
+def router_probs(logits, tau: float = 1.0) -> np.ndarray:
+    """probs[t, :] = softmax(logits[t, :] / tau) over all experts, float64 (clean logits).
+
+    P2 §3.1 (probs = softmax(scores / temperature)); P4 §3.2 averages these per expert for the
+    auxiliary loss.
+    """
+    s = _f64(logits) / float(np.float32(tau))
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    return p / p.sum(axis=1, keepdims=True)
+
+
+def gate_weights(logits, ids, tau: float = 1.0, renormalize: bool = True) -> np.ndarray:
+    """Gate weight of each selected expert, fp32.
+
+    P4 §2.4: the output is the weighted sum of the chosen experts' outputs, weighted by the
+    softmax router scores. renormalize=True: softmax over the k selected (clean) logits / tau,
+    so a token's weights sum to 1. renormalize=False: the full-softmax probability of each
+    selected expert (the page's literal wording).
+    """
+    ids = np.asarray(ids)
+    if renormalize:
+        s = _f64(logits) / float(np.float32(tau))
+        sel = np.take_along_axis(s, ids.astype(np.int64), axis=1)
+        sel = sel - sel.max(axis=1, keepdims=True)
+        e = np.exp(sel)
+        w = e / e.sum(axis=1, keepdims=True)
+    else:
+        p = router_probs(logits, tau)
+        w = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    return w.astype(np.float32)
+
+
+def topk_gap(keys, k: int) -> np.ndarray:
+    """Gap between the k-th and (k+1)-th largest key of each row (fp32 keys); +inf when k == E."""
+    kf = np.sort(_f64(keys), axis=1)[:, ::-1]
+    if k >= kf.shape[1]:
+        return np.full(kf.shape[0], np.inf)
+    return kf[:, k - 1] - kf[:, k]
+
+
+@dataclasses.dataclass
+class Routing:
+    logits: np.ndarray      # [T, E] fp32
+    keys: np.ndarray        # [T, E] fp32
+    ids: np.ndarray         # [T, k] int32
+    weights: np.ndarray     # [T, k] fp32
+    probs: np.ndarray       # [T, E] float64
+
+
+def route(x=None, w_router=None, bias=None, gumbel=None, tau: float = 1.0, k: int = 2,
+          renormalize: bool = True, logits=None) -> Routing:
+    """Router logits -> key -> top-k -> gate weights, plus the full softmax for the aux loss.
+
+    With `logits` given, routing runs on those fp32 logits (the bias is taken as already in
+    them) instead of computing x W_r^T + b.
+    """
+    if logits is None:
+        logits = router_logits(x, w_router, bias)
+    logits = _f32(logits)
+    keys = selection_keys(logits, gumbel, tau)
+    ids = top_k(keys, k)
+    weights = gate_weights(logits, ids, tau, renormalize)
+    probs = router_probs(logits, tau)
+    return Routing(logits, keys, ids, weights, probs)
+
+
+# ---------------------------------------------------------------------------------------------
+# capacity and dispatch  ([P3 §3.1, §3.4, §5.1], [P4 §2.4])
+# ---------------------------------------------------------------------------------------------
+
+def capacity_from_factor(T: int, k: int, E: int, factor: Optional[tuple]) -> int:
+    """Per-expert capacity C = ceil(cf * T * k / E), exact in integers for cf = num / den.
+
+    P3 gives capacity factors (1.2 in its MoE config, "default 1.0, use 1.2 to 1.5") and an
+    absolute per-expert cap flag, but no formula; this is the plain reading. No limit -> C = T.
+    """
+    if factor is None:
+        return T
+    num, den = factor
+    return -((-num * T * k) // (den * E))
+
+
+@dataclasses.dataclass
+class Dispatch:
+    counts_pre: np.ndarray  # [E] int32: assignments per expert before the capacity cut
+    counts: np.ndarray      # [E] int32: kept assignments per expert
+    offsets: np.ndarray     # [E+1] int32: exclusive scan of counts
+    perm_token: np.ndarray  # [N] int32: token of each permuted row
+    row_of: np.ndarray      # [T, k] int32: permuted row of each kept slot, -1 if dropped
+    dropped: np.ndarray     # [T, k] uint8
+    n_dropped: int
+    xp: Optional[np.ndarray]  # [N, d] gathered rows (same dtype as x), or None
+
+
+def dispatch(ids, num_experts: int, capacity: int, x=None) -> Dispatch:
+    """Counting sort of the (token, slot) assignments by expert, in token order, with capacity.
+
+    P4 §2.4: sort the [B, K] index by expert id, count tokens per expert, split into
+    per-expert segments and gather the tokens with a table lookup. P3: at most `capacity`
+    assignments per expert are kept; the rest are dropped. Kept assignments of expert e fill
+    rows offsets[e] .. offsets[e] + counts[e] - 1 in token order.
+    """
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    E = num_experts
+    counts_pre = np.zeros(E, dtype=np.int64)
+    pos = np.full((T, k), -1, dtype=np.int64)
+    dropped = np.zeros((T, k), dtype=np.uint8)
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            if not 0 <= e < E:
+                raise ValueError("oracle dispatch: expert id out of range")
+            if counts_pre[e] < capacity:
+                pos[t, j] = counts_pre[e]
+            else:
+                dropped[t, j] = 1
+            counts_pre[e] += 1
+    counts = np.minimum(counts_pre, max(capacity, 0))
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    N = int(offsets[-1])
+    row_of = np.full((T, k), -1, dtype=np.int64)
+    perm_token = np.full(N, -1, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            if not dropped[t, j]:
+                row = offsets[ids[t, j]] + pos[t, j]
+                row_of[t, j] = row
+                perm_token[row] = t
+    xp = None
+    if x is not None:
+        if hasattr(x, "detach"):      # torch tensor: keep its dtype (a bitwise row copy)
+            import torch
+            xp = x.detach().cpu()[torch.from_numpy(perm_token.astype(np.int64))]
+        else:
+            xp = np.asarray(x)[perm_token]
+    return Dispatch(counts_pre.astype(np.int32), counts.astype(np.int32), offsets.astype(np.int32),
+                    perm_token.astype(np.int32), row_of.astype(np.int32), dropped,
+                    int(dropped.sum()), xp)
+
+
+# ---------------------------------------------------------------------------------------------
+# experts and combine  ([P4 §2.4])
+# ---------------------------------------------------------------------------------------------
+
+def silu(a) -> np.ndarray:
+    """SiLU(a) = a * sigmoid(a) = a / (1 + exp(-a)), float64."""
+    a = np.asarray(a, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return a / (1.0 + np.exp(-a))
+
+
+def expert_ffn(xp, offsets, w1, w2, storage: str):
+    """Per-expert two-layer FFN over the permuted rows: Y_e = W2_e SiLU(W1_e x).
+
+    P4 §2.4: each expert is a two-layer FFN like a standard Transformer FFN. W1 is [E, f, d]
+    and W2 is [E, d, f] (out-features by in-features). H = SiLU(Xp_e W1_e^T) is rounded to the
+    storage dtype, then Y_e = H_e W2_e^T is rounded to the storage dtype. Returns float64
+    arrays (H [N, f], Y [N, d]) holding storage-representable values.
+    """
+    xp = _f64(xp)
+    w1 = _f64(w1)
+    w2 = _f64(w2)
+    E, f, d = w1.shape
+    N = xp.shape[0]
+    h = np.zeros((N, f), dtype=np.float64)
+    y = np.zeros((N, d), dtype=np.float64)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        h[r0:r1] = round_storage(silu(xp[r0:r1] @ w1[e].T), storage)
+        y[r0:r1] = round_storage(h[r0:r1] @ w2[e].T, storage)
+    return h, y
+
+
+def combine(y, row_of, weights, storage: str, d: Optional[int] = None) -> np.ndarray:
+    """out[t] = sum over kept slots j (ascending) of w[t, j] * Y[row_of[t, j]], rounded once.
+
+    P4 §2.4: each token's output is the weighted sum of its chosen experts' outputs. A dropped
+    slot adds nothing and the remaining weights are not rescaled; a token whose slots are all
+    dropped gets zeros.
+    """
+    y = _f64(y)
+    row_of = np.asarray(row_of)
+    w = _f64(weights)
+    T, k = row_of.shape
+    d = y.shape[1] if d is None else d
+    out = np.zeros((T, d), dtype=np.float64)
+    for j in range(k):
+        kept = row_of[:, j] >= 0
+        if np.any(kept):
+            out[kept] += w[kept, j][:, None] * y[row_of[kept, j]]
+    return round_storage(out, storage)
+
+
+# ---------------------------------------------------------------------------------------------
+# auxiliary load-balance losses  ([P4 §3.2], [P3 §3.2])
+# ---------------------------------------------------------------------------------------------
+
+def aux_loss(probs, counts_pre, k: int, coef: float):
+    """(aux_switch, aux_balance), float64.
+
+    aux_switch (P4 §3.2): coef * E * sum_i f_i * P_i with f_i = counts_pre[i] / (T k), the
+    fraction of routed assignments that chose expert i, and P_i the mean router probability of
+    expert i over the tokens. Uniform routing gives coef * sum_i P_i = coef.
+    aux_balance (P3 §3.2): coef * sum_i (p_i - k/E)^2 with p_i = counts_pre[i] / T, the
+    per-token probability that expert i is selected; its uniform value is k/E, so it is zero
+    for perfectly uniform routing.
+    """
+    probs = np.asarray(probs, dtype=np.float64)
+    T, E = probs.shape
+    cp = np.asarray(counts_pre, dtype=np.float64)
+    P = probs.mean(axis=0)
+    f = cp / (T * k)
+    aux_switch = coef * E * float(np.sum(f * P))
+    aux_balance = coef * float(np.sum((cp / T - k / E) ** 2))
+    return aux_switch, aux_balance
+
+
+# ---------------------------------------------------------------------------------------------
+# the whole layer
+# ---------------------------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class Forward:
+    routing: Routing
+    dispatch: Dispatch
+    capacity: int
+    h: np.ndarray
+    y: np.ndarray
+    out: np.ndarray
+    aux: tuple
+
+
+def forward(x, w_router, w1, w2, *, k: int, storage: str, bias=None, gumbel=None,
+            tau: float = 1.0, capacity: Optional[int] = None, renormalize: bool = True,
+            aux_coef: float = 0.01, logits=None) -> Forward:
+    """Router -> top-k -> capacity + dispatch -> expert FFN -> weighted combine, plus aux."""
+    T = x.shape[0]
+    E = w1.shape[0]
+    C = T if capacity is None or capacity < 0 else capacity
+    r = route(x, w_router, bias, gumbel, tau, k, renormalize, logits)
+    dp = dispatch(r.ids, E, C, x)
+    h, y = expert_ffn(dp.xp, dp.offsets, w1, w2, storage)
+    out = combine(y, dp.row_of, r.weights, storage, d=x.shape[1])
+    aux = aux_loss(r.probs, dp.counts_pre, k, aux_coef)
+    return Forward(r, dp, C, h, y, out, aux)
+
+
+def forward_rows(x, w1, w2, ids, weights, dropped, token_idx, storage: str) -> np.ndarray:
+    """Output rows of selected tokens only, straight from the layer's definition.
+
+    out[t] = sum over kept j of w[t, j] * W2_e SiLU(W1_e x_t) with the storage roundings of H
+    and Y; used to check sampled tokens at full size without running the whole oracle.
+    """
+    ids = np.asarray(ids)
+    w = _f64(weights)
+    dropped = np.asarray(dropped)
+    expert_cache = {}
+
+    def expert(e):
+        if e not in expert_cache:
+            expert_cache[e] = (_f64(w1[e]), _f64(w2[e]))
+        return expert_cache[e]
+
+    rows = []
+    for t in token_idx:
+        xt = _f64(x[t])
+        acc = np.zeros(xt.shape[0], dtype=np.float64)
+        for j in range(ids.shape[1]):
+            if dropped[t, j]:
+                continue
+            e = int(ids[t, j])
+            w1e, w2e = expert(e)
+            h = round_storage(silu(w1e @ xt), storage)
+            y = round_storage(w2e @ h, storage)
+            acc += w[t, j] * y
+        rows.append(round_storage(acc, storage))
+    return np.stack(rows) if rows else np.zeros((0, x.shape[1]))
