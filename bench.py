@@ -1,0 +1,160 @@
+"""Benchmark of the MoE-layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload main_bf16] [--no-cpu-baseline]
+
+One step = one moe_forward call (router, dispatch, both grouped GEMMs, combine, aux loss) over
+the workload's seeded synthetic batch, with inputs already resident in HBM. W untimed steps,
+then exactly K timed steps between two device synchronisations. Per-kernel times come from
+HIP events recorded by the library between its kernels on the launch stream.
+
+Prints one JSON line: tokens/s of the whole layer, the roofline of the dominant kernel (the
+first grouped GEMM, MFMA bound), and the CPU oracle timed on a bounded sample of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer fwd tokens/sec + grouped-GEMM TFLOP/s (% bf16 MFMA peak), E=8 top-2"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    return ap.parse_args()
+
+
+def cpu_baseline(w, inp, ntok: int) -> dict:
+    """The oracle, as it stands, on the first `ntok` tokens of the workload (all weights)."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    ntok = min(ntok, w.T)
+    x = inp["x"][:ntok]
+    g = inp["gumbel"][:ntok] if inp["gumbel"] is not None else None
+    C = oracle.capacity_from_factor(ntok, w.top_k, w.num_experts, w.capacity_factor)
+    t0 = time.perf_counter()
+    oracle.forward(x, inp["w_router"], inp["w1"], inp["w2"], k=w.top_k, storage=w.dtype, bias=inp["bias"],
+                   gumbel=g, tau=w.temperature, capacity=C, renormalize=w.renormalize, aux_coef=w.aux_coef)
+    dt = time.perf_counter() - t0
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {ntok} of {w.T} tokens of {w.name} with all expert weights "
+                      f"(oracle.forward, float64, numpy/OpenBLAS); {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer has no multi-GPU path here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_02_amd as moe
+    from sparse_mixture_experts_02_amd.binding import FORWARD_KERNEL_NAMES, MOE_FORWARD_NUM_KERNELS
+    from sparse_mixture_experts_02_amd.inputs import MAIN, WORKLOADS, inputs_digest, make_inputs
+
+    name = args.workload or MAIN
+    w = WORKLOADS[name]
+    torch.cuda.set_device(0)
+    inp = make_inputs(w)
+    digest = inputs_digest(inp)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    cfg = moe.config_for(w)
+    ws = moe.new_workspace(cfg)
+    out = torch.empty(w.T, w.d_model, dtype=cfg.torch_dtype, device="cuda")
+    aux = torch.empty(2, dtype=torch.float32, device="cuda")
+    offsets = torch.empty(w.num_experts + 1, dtype=torch.int32, device="cuda")
+    nd = torch.empty(1, dtype=torch.int32, device="cuda")
+    nev = MOE_FORWARD_NUM_KERNELS + 1
+    events = [moe.HipEvents(nev) for _ in range(args.steps)]
+
+    def step(ev=None):
+        moe.moe_forward(cfg, dev["x"], dev["w_router"], dev["w1"], dev["w2"], out, aux, ws, bias=dev["bias"],
+                        gumbel=dev["gumbel"], debug={"offsets": offsets, "n_dropped": nd}, events=ev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    per_kernel = np.zeros((args.steps, MOE_FORWARD_NUM_KERNELS))
+    for i, ev in enumerate(events):
+        for j in range(MOE_FORWARD_NUM_KERNELS):
+            per_kernel[i, j] = ev.elapsed_ms(j, j + 1)
+        ev.close()
+    kms = per_kernel.mean(axis=0)
+    N = int(offsets[-1].item())
+    n_dropped = int(nd.item())
+
+    T, d, f = w.T, w.d_model, w.d_ffn
+    a = 2 if w.dtype == "bf16" else 4
+    flop_gemm = 2.0 * N * d * f                     # per grouped GEMM launch
+    names = list(FORWARD_KERNEL_NAMES)
+    t_g1 = kms[names.index("gemm1_silu")] * 1e-3
+    t_g2 = kms[names.index("gemm2")] * 1e-3
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    g1_tflops = flop_gemm / t_g1 / 1e12
+    gemm_tflops = 2 * flop_gemm / (t_g1 + t_g2) / 1e12
+    dispatch_bytes = T * d * a + N * d * a + 12 * T * w.top_k
+    combine_bytes = N * d * a + T * d * a + 8 * T * w.top_k
+    t_disp = sum(kms[names.index(n)] for n in ("dispatch_hist", "dispatch_scan", "dispatch_gather")) * 1e-3
+    t_comb = kms[names.index("combine")] * 1e-3
+
+    line = {
+        "metric": METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian inputs and random-init weights of the workload's shapes)",
+        "config": {"workload": w.name, "T": T, "d_model": d, "d_ffn": f, "num_experts": w.num_experts,
+                   "top_k": w.top_k, "capacity": cfg.capacity, "temperature": w.temperature,
+                   "gumbel": w.gumbel, "router_bias": w.router_bias, "parallelism": "single GPU"},
+        "roofline": {"kernel": "gemm1_silu", "bound": "mfma", "achieved": g1_tflops, "peak": peak,
+                     "unit": "TFLOP/s", "frac": g1_tflops / peak, "traffic": None},
+        "gemm_tflops": gemm_tflops,
+        "gemm_frac_of_peak": gemm_tflops / peak,
+        "kernel_ms": {n: float(v) for n, v in zip(names, kms)},
+        "dispatch_gbs": dispatch_bytes / t_disp / 1e9,
+        "combine_gbs": combine_bytes / t_comb / 1e9,
+        "kept_rows": N,
+        "n_dropped": n_dropped,
+        "inputs_sha256": digest,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_sample_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

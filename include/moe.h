@@ -1,0 +1,220 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) forward pass of a top-k routed MoE FFN layer.
+ *
+ * Pages cited (by title):
+ *   [P2] "Twinkle首发适配Deepseek-V4系列模型高效训练" (www.wmrh.cn/news/44033)
+ *   [P3] "DeepSpeed ZeRO-3与MoE显存精算实战指南" (m.nlpx.cn/news/237350)
+ *   [P4] "手搓一个LLaMA4-MoE" (www.nxmr.cn/news/140631)
+ *
+ * Notation: T tokens, d = d_model, f = d_ffn, E experts, k = top-k, C = per-expert capacity,
+ * N = number of kept (token, slot) assignments (N <= T*k). All matrices are row-major and
+ * contiguous. "act" is the activation storage type (x, Xp, H, Y, out) and "wt" the expert
+ * weight type (W1, W2); both are fp32 or both are bf16. Router weight, bias, Gumbel noise,
+ * logits, probabilities and gate weights are always fp32.
+ *
+ * Conventions shared by every call:
+ *  - Ownership: every buffer is caller-owned device memory (except where "host" is stated).
+ *    The library never allocates or frees device memory. Scratch space comes from the
+ *    caller's workspace `ws` of at least moe_workspace_bytes(cfg) bytes, 256-byte aligned.
+ *  - Streams: each call enqueues its kernels on `stream` and returns without synchronising;
+ *    outputs are valid once the stream has reached that point. Calls that overlap on the same
+ *    buffers or the same workspace race; the library keeps no state between calls.
+ *  - Errors: every call returns a moe_status_t. Arguments are validated on the host before any
+ *    launch; on a validation error nothing is launched. A failed kernel launch returns
+ *    MOE_ERR_HIP. Inputs must be finite; results for NaN/Inf inputs are unspecified.
+ *  - Determinism: no floating-point atomics; two calls with the same inputs give bitwise equal
+ *    outputs.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* a null required pointer or a size/value out of range     */
+  MOE_ERR_UNSUPPORTED = 2,        /* a valid but unsupported combination (e.g. mixed dtypes)    */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed                 */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+/* Capacity value meaning "no limit" (C = T). */
+#define MOE_NO_CAPACITY (-1)
+
+/* Limits checked by moe_validate_config. */
+#define MOE_MAX_EXPERTS 64
+#define MOE_MAX_TOP_K 8
+#define MOE_MAX_TOKENS (1 << 24)
+
+/*
+ * Layer configuration. Parameter names follow P4 §2.1 (num_experts, num_experts_per_token,
+ * aux_loss_coef), P3 (capacity: an absolute per-expert cap, its --moe_expert_capacity) and
+ * P2 (router_temperature).
+ */
+typedef struct {
+  int32_t T;             /* tokens, 1 .. MOE_MAX_TOKENS                                        */
+  int32_t d_model;       /* d, a positive multiple of 8                                         */
+  int32_t d_ffn;         /* f, a positive multiple of 8                                         */
+  int32_t num_experts;   /* E, 1 .. MOE_MAX_EXPERTS                                             */
+  int32_t top_k;         /* k, 1 .. min(E, MOE_MAX_TOP_K)                                       */
+  int32_t capacity;      /* C >= 0 kept assignments per expert, or MOE_NO_CAPACITY              */
+  float   temperature;   /* tau > 0: softmax and Gumbel keys use logits / tau (P2 §3.1)         */
+  int32_t renormalize;   /* 1: gate weights = softmax over the k selected logits / tau;
+                            0: gate weights = full softmax probability of each selected expert  */
+  float   aux_coef;      /* coefficient of both aux losses (P4 §2.1 uses 0.01)                 */
+  moe_dtype_t act_dtype;     /* x, Xp, H, Y, out                                               */
+  moe_dtype_t weight_dtype;  /* W1, W2 (must equal act_dtype)                                  */
+} moe_config_t;
+
+/* Static text for a status code (never NULL). Host only. */
+const char* moe_status_string(moe_status_t status);
+
+/* Checks a configuration on the host; touches no GPU. Returns MOE_OK, MOE_ERR_INVALID_ARGUMENT
+ * (cfg NULL, a size out of the ranges above, tau not finite and > 0, capacity < -1) or
+ * MOE_ERR_UNSUPPORTED (act_dtype != weight_dtype or an unknown dtype). */
+moe_status_t moe_validate_config(const moe_config_t* cfg);
+
+/* C = ceil(cf * T * k / E) for the decimal capacity factor cf = cf_num / cf_den, in exact
+ * integer arithmetic (P3 §3.4 and §5.1 give factors such as 1.2 but no formula; this is the
+ * plain reading). Returns -1 if T, k, E, cf_num or cf_den is not positive. Host only. */
+int32_t moe_capacity_from_factor(int32_t T, int32_t k, int32_t E, int32_t cf_num, int32_t cf_den);
+
+/* Workspace bytes that every call below accepts for this configuration (0 if cfg is invalid).
+ * moe_forward keeps Xp, H and Y there: about (2 d + f) * T * k * sizeof(act) plus O(T k). */
+size_t moe_workspace_bytes(const moe_config_t* cfg);
+
+/*
+ * Router: logits, selection key, top-k and gate weights for every token.
+ * [P2 §3.1] scores = W_router x, probs = softmax(scores / tau), top-k; with Gumbel noise the
+ * ranked key is (logits + g) / tau. [P4 §2.4] a linear router, top-k, softmax weights.
+ *   x          [T, d] act          token hidden states (ignored when logits_in != NULL)
+ *   w_router   [E, d] fp32         router weight (ignored when logits_in != NULL)
+ *   bias       [E] fp32 or NULL    per-expert logit bias, added after the product
+ *   gumbel     [T, E] fp32 or NULL noise; when given, key = fl32(fl32(logit + g) / tau),
+ *                                  otherwise key = logit. Noise changes selection only.
+ *   logits_in  [T, E] fp32 or NULL route these final logits instead of computing x W_r^T + b
+ *   logits_out [T, E] fp32 or NULL the router logits (fp32 accumulation of x W_r^T, + bias)
+ *   probs_out  [T, E] fp32 or NULL softmax(logits / tau) over all E
+ *   ids        [T, k] int32        selected experts, descending key, lowest index on ties
+ *                                  (-0.0 ties +0.0)
+ *   weights    [T, k] fp32         gate weight of each selected expert (see renormalize)
+ * Workspace: per-block probability sums used by moe_forward's aux loss (unused here).
+ */
+moe_status_t moe_route(const moe_config_t* cfg, const void* x, const float* w_router,
+                       const float* bias, const float* gumbel, const float* logits_in,
+                       float* logits_out, float* probs_out, int32_t* ids, float* weights,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Dispatch: per-expert histogram, capacity cut, offsets and stable permutation, and the row
+ * gather Xp[row] = x[perm_token[row]]. [P4 §2.4] sort the [T, k] index by expert id, count
+ * tokens per expert, split into segments, gather tokens by table lookup; [P3 §3.1] cap the
+ * tokens per expert. Assignments are taken in (token, slot) order; the first C of each expert
+ * are kept, the rest dropped.
+ *   ids        [T, k] int32 device, each in [0, E) and distinct within a token (as moe_route
+ *                                  gives; other values are not checked and give unspecified
+ *                                  results)
+ *   x          [T, d] act
+ *   counts_pre [E] int32           assignments per expert before the cut
+ *   counts     [E] int32           kept per expert = min(counts_pre, C)
+ *   offsets    [E+1] int32         exclusive scan of counts; offsets[E] = N
+ *   perm_token [T*k] int32         token of row r for r < N (entries >= N untouched)
+ *   row_of     [T, k] int32        row of each kept slot, -1 if dropped
+ *   dropped    [T, k] uint8        1 if the slot was dropped
+ *   n_dropped  [1] int32           T*k - N
+ *   xp         [T*k, d] act        gathered rows; rows >= N untouched
+ */
+moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* ids, const void* x,
+                          int32_t* counts_pre, int32_t* counts, int32_t* offsets,
+                          int32_t* perm_token, int32_t* row_of, uint8_t* dropped,
+                          int32_t* n_dropped, void* xp, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
+ * Expert FFN as two grouped GEMMs over the expert segments given by offsets.
+ * [P4 §2.4] each expert is a two-layer FFN. For rows r in [offsets[e], offsets[e+1]):
+ *   H[r] = SiLU(Xp[r] W1[e]^T)   (fp32 accumulate, SiLU in fp32, one rounding to act)
+ *   Y[r] = H[r] W2[e]^T          (fp32 accumulate, one rounding to act)
+ *   xp      [T*k, d] act   w1 [E, f, d] wt   w2 [E, d, f] wt   offsets [E+1] int32 device
+ *   h       [T*k, f] act   (scratch output, rows >= N untouched)
+ *   y       [T*k, d] act   (rows >= N untouched)
+ * offsets must be non-decreasing with offsets[0] = 0 and offsets[E] <= T*k.
+ */
+moe_status_t moe_expert_ffn(const moe_config_t* cfg, const void* xp, const int32_t* offsets,
+                            const void* w1, const void* w2, void* h, void* y, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Weighted combine (unpermute). [P4 §2.4] a token's output is the sum of its selected
+ * experts' outputs weighted by the gate weights:
+ *   out[t] = sum_{j = 0..k-1, row_of[t,j] >= 0} weights[t,j] * y[row_of[t,j]]
+ * accumulated in fp32 in slot order, rounded once to act. A token with every slot dropped gets
+ * zeros. y [T*k, d] act, row_of [T, k] int32 (entries < T*k), weights [T, k] fp32,
+ * out [T, d] act.
+ */
+moe_status_t moe_combine(const moe_config_t* cfg, const void* y, const int32_t* row_of,
+                         const float* weights, void* out, hipStream_t stream);
+
+/*
+ * Auxiliary load-balance losses, aux[0] = aux_switch, aux[1] = aux_balance (device fp32):
+ *   P_i = mean_t softmax(logits_t / tau)_i   (from probs when given, else from logits)
+ *   aux_switch  = coef * E * sum_i (counts_pre[i] / (T k)) * P_i            [P4 §3.2]
+ *   aux_balance = coef * sum_i (counts_pre[i] / T - k / E)^2                [P3 §3.2]
+ * aux_switch is coef for uniform routing; aux_balance is 0 for perfectly uniform counts.
+ *   probs [T, E] fp32 or NULL, logits [T, E] fp32 (used when probs is NULL),
+ *   counts_pre [E] int32 (pre-capacity counts from moe_dispatch).
+ */
+moe_status_t moe_aux_loss(const moe_config_t* cfg, const float* probs, const float* logits,
+                          const int32_t* counts_pre, float* aux, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
+ * Optional outputs and timing hooks of moe_forward. Every pointer may be NULL; a non-NULL
+ * device pointer receives the named tensor (shapes as in the calls above). When `events` is
+ * non-NULL it holds n_events >= MOE_FORWARD_NUM_KERNELS + 1 created hipEvent_t; events[i] is
+ * recorded on `stream` before kernel i and events[MOE_FORWARD_NUM_KERNELS] after the last, so
+ * hipEventElapsedTime gives per-kernel times. Kernel order: route, dispatch-histogram,
+ * dispatch-scan, dispatch-gather, gemm1 (W1 + SiLU), gemm2 (W2), combine, aux.
+ */
+#define MOE_FORWARD_NUM_KERNELS 8
+typedef struct {
+  float*   logits;      /* [T, E] */
+  float*   probs;       /* [T, E] */
+  int32_t* ids;         /* [T, k] */
+  float*   weights;     /* [T, k] */
+  int32_t* counts_pre;  /* [E]    */
+  int32_t* counts;      /* [E]    */
+  int32_t* offsets;     /* [E+1]  */
+  int32_t* perm_token;  /* [T*k]  */
+  int32_t* row_of;      /* [T, k] */
+  uint8_t* dropped;     /* [T, k] */
+  int32_t* n_dropped;   /* [1]    */
+  void*    xp;          /* [T*k, d] act */
+  void*    h;           /* [T*k, f] act */
+  void*    y;           /* [T*k, d] act */
+  hipEvent_t* events;
+  int32_t  n_events;
+} moe_debug_outputs;
+
+/*
+ * The whole layer: route -> dispatch -> expert FFN -> combine, plus both aux losses
+ * (P4 §2.4 and §3.2, P2 §3.1, P3 §3.1-3.2). Inputs as in the calls above; out [T, d] act;
+ * aux [2] fp32 device. dbg may be NULL.
+ */
+moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_router,
+                         const float* bias, const float* gumbel, const void* w1, const void* w2,
+                         void* out, float* aux, moe_debug_outputs* dbg, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -41,7 +41,7 @@ def round_bf16(a) -> np.ndarray:
 
     bfloat16 keeps 8 significant bits and the fp32 exponent range; the quantum of a value with
     binary exponent e (a = m * 2**e, 0.5 <= |m| < 1) is 2**(e - 8), floored at the subnormal
-    quantum 2**-133.
+    quantum 2**-133; np.rint rounds half to even.
     """
     a = np.asarray(a, dtype=np.float64)
     _, e = np.frexp(a)
@@ -271,10 +271,15 @@ def dispatch(ids, num_experts: int, capacity: int, x=None) -> Dispatch:
 # ---------------------------------------------------------------------------------------------
 
 def silu(a) -> np.ndarray:
-    """SiLU(a) = a * sigmoid(a) = a / (1 + exp(-a)), float64."""
+    """SiLU(a) = a * sigmoid(a) = a / (1 + exp(-a)), float64 (in place on a temporary)."""
     a = np.asarray(a, dtype=np.float64)
     with np.errstate(over="ignore"):
-        return a / (1.0 + np.exp(-a))
+        if a.ndim == 0:
+            return np.float64(a / (1.0 + np.exp(-a)))
+        den = np.negative(a)
+        np.exp(den, out=den)
+    den += 1.0
+    return np.divide(a, den, out=den)
 
 
 def expert_ffn(xp, offsets, w1, w2, storage: str):

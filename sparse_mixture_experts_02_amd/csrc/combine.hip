@@ -1,0 +1,171 @@
+// Weighted combine (unpermute) and the auxiliary load-balance losses.
+//
+// [P4 §2.4] a token's output is the weighted sum of its selected experts' outputs, the weights
+// being the softmax router scores. [P4 §3.2] aux = E * sum_i f_i P_i; [P3 §3.2]
+// aux = lambda * sum_i (p_i - uniform)^2.
+#include "moe_internal.h"
+
+namespace moe {
+
+// One wave per token; each lane owns 8 consecutive columns per step. The k rows of Y are read
+// with 16-byte loads (bf16) and accumulated in fp32 in slot order, then rounded once.
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= p.T) return;
+  const int k = p.k;
+  int my_row = -1;
+  float my_w = 0.0f;
+  if (lane < k) {
+    my_row = p.row_of[(size_t)t * k + lane];
+    my_w = p.weights[(size_t)t * k + lane];
+    if (my_row >= p.max_rows) my_row = -1;
+  }
+  int rows[MOE_MAX_TOP_K_DEV];
+  float ws[MOE_MAX_TOP_K_DEV];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOP_K_DEV; ++j) {
+    rows[j] = (j < k) ? __shfl(my_row, j) : -1;
+    ws[j] = (j < k) ? __shfl(my_w, j) : 0.0f;
+  }
+  const int d = p.d;
+  for (int c = lane * 8; c < d; c += 64 * 8) {
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOP_K_DEV; ++j) {
+      if (rows[j] < 0) continue;
+      float v[8];
+      if constexpr (BF16) {
+        const uint4 u = *(const uint4*)((const uint16_t*)p.y + (size_t)rows[j] * d + c);
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[2 * q] = bf16_bits_to_f32(wd[q] & 0xFFFFu);
+          v[2 * q + 1] = bf16_bits_to_f32(wd[q] >> 16);
+        }
+      } else {
+        const float4 a = *(const float4*)((const float*)p.y + (size_t)rows[j] * d + c);
+        const float4 b = *(const float4*)((const float*)p.y + (size_t)rows[j] * d + c + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = fmaf(ws[j], v[q], acc[q]);
+    }
+    if constexpr (BF16) {
+      uint4 o;
+      o.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
+      o.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
+      o.z = f32_to_bf16_bits(acc[4]) | (f32_to_bf16_bits(acc[5]) << 16);
+      o.w = f32_to_bf16_bits(acc[6]) | (f32_to_bf16_bits(acc[7]) << 16);
+      *(uint4*)((uint16_t*)p.out + (size_t)t * d + c) = o;
+    } else {
+      *(float4*)((float*)p.out + (size_t)t * d + c) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      *(float4*)((float*)p.out + (size_t)t * d + c + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+  }
+}
+
+hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s) {
+  const int grid = (p.T + 3) / 4;
+  if (bf16) combine_kernel<true><<<grid, 256, 0, s>>>(p);
+  else combine_kernel<false><<<grid, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------ aux losses
+
+constexpr int PROBSUM_TOKENS = 256;  // tokens per block of the stand-alone probability sum
+
+// Per-block sums of softmax(logits / tau) (or of given probabilities) per expert, in double.
+// Thread layout: EPAD = E rounded up to a power of two lanes per token, 256 / EPAD tokens at a
+// time; partial sums are combined in LDS in a fixed order.
+__global__ __launch_bounds__(256) void probsum_kernel(ProbSumParams p) {
+  __shared__ double part[256];
+  const int tid = threadIdx.x;
+  const int E = p.E;
+  int EPAD = 1;
+  while (EPAD < E) EPAD <<= 1;
+  const int e = tid % EPAD;
+  const int sub = tid / EPAD;
+  const int nsub = 256 / EPAD;
+  const int t0 = blockIdx.x * PROBSUM_TOKENS;
+  const int t1 = min(p.T, t0 + PROBSUM_TOKENS);
+  double acc = 0.0;
+  for (int t = t0 + sub; t < t1; t += nsub) {
+    float prob = 0.0f;
+    if (p.probs) {
+      prob = (e < E) ? p.probs[(size_t)t * E + e] : 0.0f;
+    } else {
+      const float* row = p.logits + (size_t)t * E;
+      float mx = -INFINITY;
+      for (int q = 0; q < E; ++q) mx = fmaxf(mx, row[q]);
+      float s = 0.0f;
+      for (int q = 0; q < E; ++q) s = __fadd_rn(s, expf(__fdiv_rn(__fsub_rn(row[q], mx), p.tau)));
+      prob = (e < E) ? __fdiv_rn(expf(__fdiv_rn(__fsub_rn(row[e], mx), p.tau)), s) : 0.0f;
+    }
+    acc += (double)prob;
+  }
+  part[tid] = acc;
+  __syncthreads();
+  if (tid < E) {
+    double s = 0.0;
+    for (int q = 0; q < nsub; ++q) s += part[q * EPAD + tid];
+    p.psum[(size_t)blockIdx.x * E + tid] = s;
+  }
+}
+
+int probsum_num_blocks(int T) { return (T + PROBSUM_TOKENS - 1) / PROBSUM_TOKENS; }
+
+hipError_t launch_probsum(const ProbSumParams& p, hipStream_t s) {
+  probsum_kernel<<<probsum_num_blocks(p.T), 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+// One block: P_i = (sum of the partial sums) / T in a fixed order (256 lanes split the parts
+// of each expert, then a fixed-order combine), then both losses in double, stored as fp32.
+__global__ __launch_bounds__(256) void aux_final_kernel(AuxParams p) {
+  __shared__ double part[256];
+  __shared__ double P[MOE_MAX_EXPERTS_DEV];
+  const int tid = threadIdx.x;
+  const int E = p.E;
+  int EPAD = 1;
+  while (EPAD < E) EPAD <<= 1;
+  const int e = tid % EPAD;
+  const int sub = tid / EPAD;
+  const int nsub = 256 / EPAD;
+  double acc = 0.0;
+  if (e < E)
+    for (int q = sub; q < p.nparts; q += nsub) acc += p.psum[(size_t)q * E + e];
+  part[tid] = acc;
+  __syncthreads();
+  if (tid < E) {
+    double s = 0.0;
+    for (int q = 0; q < nsub; ++q) s += part[q * EPAD + tid];
+    P[tid] = s / (double)p.T;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double sw = 0.0, sb = 0.0;
+    const double tk = (double)p.T * (double)p.k;
+    const double uni = (double)p.k / (double)E;
+    for (int q = 0; q < E; ++q) {
+      const double c = (double)p.counts_pre[q];
+      sw += (c / tk) * P[q];
+      const double dv = c / (double)p.T - uni;
+      sb += dv * dv;
+    }
+    p.aux[0] = (float)((double)p.coef * (double)E * sw);
+    p.aux[1] = (float)((double)p.coef * sb);
+  }
+}
+
+hipError_t launch_aux_final(const AuxParams& p, hipStream_t s) {
+  aux_final_kernel<<<1, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace moe

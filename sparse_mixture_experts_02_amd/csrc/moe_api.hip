@@ -1,0 +1,377 @@
+// Host side of the C ABI declared in include/moe.h: validation, workspace carve-up and the
+// kernel sequence of each call. No call allocates device memory or synchronises the stream.
+#include "../../include/moe.h"
+
+#include <math.h>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kMaxDim = 32768;
+
+struct Layout {
+  size_t wsplit, psum, blk_hist, blk_base, rank_local, probsum;
+  size_t logits, ids, weights, counts_pre, counts, offsets, perm, row_of, dropped, ndrop;
+  size_t xp, h, y;
+  size_t total;
+};
+
+size_t act_size(const moe_config_t& c) { return c.act_dtype == MOE_BF16 ? 2 : 4; }
+
+Layout layout(const moe_config_t& c) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  const size_t T = (size_t)c.T, k = (size_t)c.top_k, E = (size_t)c.num_experts;
+  const size_t d = (size_t)c.d_model, f = (size_t)c.d_ffn, TK = T * k, a = act_size(c);
+  const size_t EP = 16 * (size_t)route_expert_tiles(c.num_experts);
+  L.wsplit = take(3 * EP * d * 2);
+  L.psum = take((size_t)route_num_waves(c.T) * E * sizeof(double));
+  const size_t nb = (size_t)dispatch_num_blocks((int)TK);
+  L.blk_hist = take(nb * E * 4);
+  L.blk_base = take(nb * E * 4);
+  L.rank_local = take(TK * 4);
+  L.probsum = take((size_t)probsum_num_blocks(c.T) * E * sizeof(double));
+  L.logits = take(T * E * 4);
+  L.ids = take(TK * 4);
+  L.weights = take(TK * 4);
+  L.counts_pre = take(E * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.perm = take(TK * 4);
+  L.row_of = take(TK * 4);
+  L.dropped = take(TK);
+  L.ndrop = take(4);
+  L.xp = take(TK * d * a);
+  L.h = take(TK * f * a);
+  L.y = take(TK * d * a);
+  L.total = off;
+  return L;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                         \
+  do {                                        \
+    const moe_status_t st_ = (expr);          \
+    if (st_ != MOE_OK) return st_;            \
+  } while (0)
+
+#define MOE_LAUNCH(expr) MOE_TRY(hip_status(expr))
+
+moe_status_t check_ws(const moe_config_t* cfg, const void* ws, size_t ws_bytes) {
+  if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < layout(*cfg).total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return MOE_OK;
+}
+
+uint8_t* at(void* ws, size_t off) { return (uint8_t*)ws + off; }
+
+int capacity_of(const moe_config_t& c) { return c.capacity < 0 ? -1 : c.capacity; }
+
+// ---- the kernel sequences, shared by the single-step calls and moe_forward
+
+moe_status_t run_route(const moe_config_t& c, const void* x, const float* w_router, const float* bias,
+                       const float* gumbel, const float* logits_in, float* logits_out, float* probs_out,
+                       int32_t* ids, float* weights, double* psum, void* ws, hipStream_t s) {
+  const Layout L = layout(c);
+  const bool bf16 = c.act_dtype == MOE_BF16;
+  const void* wsrc = w_router;
+  if (!logits_in && bf16) {
+    MOE_LAUNCH(launch_route_split(w_router, c.num_experts, c.d_model, at(ws, L.wsplit), s));
+    wsrc = at(ws, L.wsplit);
+  }
+  RouteParams p{};
+  p.T = c.T;
+  p.d = c.d_model;
+  p.E = c.num_experts;
+  p.k = c.top_k;
+  p.tau = c.temperature;
+  p.renormalize = c.renormalize;
+  p.x = x;
+  p.wsplit = wsrc;
+  p.bias = logits_in ? nullptr : bias;
+  p.gumbel = gumbel;
+  p.logits_in = logits_in;
+  p.logits_out = logits_out;
+  p.probs_out = probs_out;
+  p.ids = ids;
+  p.weights = weights;
+  p.psum = psum;
+  MOE_LAUNCH(launch_route(p, bf16, s));
+  return MOE_OK;
+}
+
+moe_status_t run_hist(const moe_config_t& c, const int32_t* ids, void* ws, hipStream_t s) {
+  const Layout L = layout(c);
+  HistParams p{};
+  p.TK = c.T * c.top_k;
+  p.E = c.num_experts;
+  p.ids = ids;
+  p.blk_hist = (int32_t*)at(ws, L.blk_hist);
+  p.rank_local = (int32_t*)at(ws, L.rank_local);
+  MOE_LAUNCH(launch_hist(p, s));
+  return MOE_OK;
+}
+
+moe_status_t run_scan(const moe_config_t& c, int32_t* counts_pre, int32_t* counts, int32_t* offsets,
+                      int32_t* n_dropped, void* ws, hipStream_t s) {
+  const Layout L = layout(c);
+  ScanParams p{};
+  p.TK = c.T * c.top_k;
+  p.nb = dispatch_num_blocks(p.TK);
+  p.E = c.num_experts;
+  p.capacity = capacity_of(c);
+  p.blk_hist = (const int32_t*)at(ws, L.blk_hist);
+  p.blk_base = (int32_t*)at(ws, L.blk_base);
+  p.counts_pre = counts_pre;
+  p.counts = counts;
+  p.offsets = offsets;
+  p.n_dropped = n_dropped;
+  MOE_LAUNCH(launch_scan(p, s));
+  return MOE_OK;
+}
+
+moe_status_t run_gather(const moe_config_t& c, const int32_t* ids, const void* x, const int32_t* offsets,
+                        int32_t* perm_token, int32_t* row_of, uint8_t* dropped, void* xp, void* ws,
+                        hipStream_t s) {
+  const Layout L = layout(c);
+  GatherParams p{};
+  p.T = c.T;
+  p.k = c.top_k;
+  p.E = c.num_experts;
+  p.row_bytes = (int)(c.d_model * act_size(c));
+  p.capacity = capacity_of(c);
+  p.ids = ids;
+  p.blk_base = (const int32_t*)at(ws, L.blk_base);
+  p.rank_local = (const int32_t*)at(ws, L.rank_local);
+  p.offsets = offsets;
+  p.x = (const uint8_t*)x;
+  p.row_of = row_of;
+  p.dropped = dropped;
+  p.perm_token = perm_token;
+  p.xp = (uint8_t*)xp;
+  MOE_LAUNCH(launch_gather(p, s));
+  return MOE_OK;
+}
+
+moe_status_t run_gemm(const moe_config_t& c, const void* a, const void* b, void* out, const int32_t* offsets,
+                      int n, int kdim, bool silu, hipStream_t s) {
+  GemmParams p{};
+  p.E = c.num_experts;
+  p.N = n;
+  p.K = kdim;
+  p.max_rows = c.T * c.top_k;
+  p.A = a;
+  p.B = b;
+  p.C = out;
+  p.offsets = offsets;
+  MOE_LAUNCH(launch_gemm(p, c.act_dtype == MOE_BF16, silu, s));
+  return MOE_OK;
+}
+
+moe_status_t run_combine(const moe_config_t& c, const void* y, const int32_t* row_of, const float* weights,
+                         void* out, hipStream_t s) {
+  CombineParams p{};
+  p.T = c.T;
+  p.d = c.d_model;
+  p.k = c.top_k;
+  p.max_rows = c.T * c.top_k;
+  p.y = y;
+  p.row_of = row_of;
+  p.weights = weights;
+  p.out = out;
+  MOE_LAUNCH(launch_combine(p, c.act_dtype == MOE_BF16, s));
+  return MOE_OK;
+}
+
+moe_status_t run_aux_final(const moe_config_t& c, const double* psum, int nparts, const int32_t* counts_pre,
+                           float* aux, hipStream_t s) {
+  AuxParams p{};
+  p.T = c.T;
+  p.E = c.num_experts;
+  p.k = c.top_k;
+  p.nparts = nparts;
+  p.coef = c.aux_coef;
+  p.tau = c.temperature;
+  p.psum = psum;
+  p.counts_pre = counts_pre;
+  p.aux = aux;
+  MOE_LAUNCH(launch_aux_final(p, s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+moe_status_t moe_validate_config(const moe_config_t* c) {
+  if (!c) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->T < 1 || c->T > MOE_MAX_TOKENS) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->d_model < 8 || c->d_model > kMaxDim || c->d_model % 8) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->d_ffn < 8 || c->d_ffn > kMaxDim || c->d_ffn % 8) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->num_experts < 1 || c->num_experts > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARGUMENT;
+  const int kmax = c->num_experts < MOE_MAX_TOP_K ? c->num_experts : MOE_MAX_TOP_K;
+  if (c->top_k < 1 || c->top_k > kmax) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->capacity < MOE_NO_CAPACITY) return MOE_ERR_INVALID_ARGUMENT;
+  if (!(isfinite(c->temperature) && c->temperature > 0.0f)) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (!isfinite(c->aux_coef)) return MOE_ERR_INVALID_ARGUMENT;
+  const bool dt_ok = (c->act_dtype == MOE_F32 || c->act_dtype == MOE_BF16) &&
+                     (c->weight_dtype == MOE_F32 || c->weight_dtype == MOE_BF16);
+  if (!dt_ok) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->act_dtype != c->weight_dtype) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int32_t moe_capacity_from_factor(int32_t T, int32_t k, int32_t E, int32_t cf_num, int32_t cf_den) {
+  if (T <= 0 || k <= 0 || E <= 0 || cf_num <= 0 || cf_den <= 0) return -1;
+  const long long num = (long long)cf_num * T * k;
+  const long long den = (long long)cf_den * E;
+  const long long c = (num + den - 1) / den;
+  return c > 0x7fffffffLL ? 0x7fffffff : (int32_t)c;
+}
+
+size_t moe_workspace_bytes(const moe_config_t* cfg) {
+  if (moe_validate_config(cfg) != MOE_OK) return 0;
+  return layout(*cfg).total;
+}
+
+moe_status_t moe_route(const moe_config_t* cfg, const void* x, const float* w_router, const float* bias,
+                       const float* gumbel, const float* logits_in, float* logits_out, float* probs_out,
+                       int32_t* ids, float* weights, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(moe_validate_config(cfg));
+  if (!ids || !weights) return MOE_ERR_INVALID_ARGUMENT;
+  if (!logits_in && (!x || !w_router || !aligned16(x))) return MOE_ERR_INVALID_ARGUMENT;
+  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  return run_route(*cfg, x, w_router, bias, gumbel, logits_in, logits_out, probs_out, ids, weights, nullptr,
+                   ws, stream);
+}
+
+moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* ids, const void* x, int32_t* counts_pre,
+                          int32_t* counts, int32_t* offsets, int32_t* perm_token, int32_t* row_of,
+                          uint8_t* dropped, int32_t* n_dropped, void* xp, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  MOE_TRY(moe_validate_config(cfg));
+  if (!ids || !x || !counts_pre || !counts || !offsets || !perm_token || !row_of || !dropped || !n_dropped ||
+      !xp)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(xp)) return MOE_ERR_INVALID_ARGUMENT;
+  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  MOE_TRY(run_hist(*cfg, ids, ws, stream));
+  MOE_TRY(run_scan(*cfg, counts_pre, counts, offsets, n_dropped, ws, stream));
+  return run_gather(*cfg, ids, x, offsets, perm_token, row_of, dropped, xp, ws, stream);
+}
+
+moe_status_t moe_expert_ffn(const moe_config_t* cfg, const void* xp, const int32_t* offsets, const void* w1,
+                            const void* w2, void* h, void* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(moe_validate_config(cfg));
+  if (!xp || !offsets || !w1 || !w2 || !h || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(xp) || !aligned16(w1) || !aligned16(w2) || !aligned16(h) || !aligned16(y))
+    return MOE_ERR_INVALID_ARGUMENT;
+  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  MOE_TRY(run_gemm(*cfg, xp, w1, h, offsets, cfg->d_ffn, cfg->d_model, true, stream));
+  return run_gemm(*cfg, h, w2, y, offsets, cfg->d_model, cfg->d_ffn, false, stream);
+}
+
+moe_status_t moe_combine(const moe_config_t* cfg, const void* y, const int32_t* row_of, const float* weights,
+                         void* out, hipStream_t stream) {
+  MOE_TRY(moe_validate_config(cfg));
+  if (!y || !row_of || !weights || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(y) || !aligned16(out)) return MOE_ERR_INVALID_ARGUMENT;
+  return run_combine(*cfg, y, row_of, weights, out, stream);
+}
+
+moe_status_t moe_aux_loss(const moe_config_t* cfg, const float* probs, const float* logits,
+                          const int32_t* counts_pre, float* aux, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(moe_validate_config(cfg));
+  if ((!probs && !logits) || !counts_pre || !aux) return MOE_ERR_INVALID_ARGUMENT;
+  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  const Layout L = layout(*cfg);
+  ProbSumParams p{};
+  p.T = cfg->T;
+  p.E = cfg->num_experts;
+  p.tau = cfg->temperature;
+  p.probs = probs;
+  p.logits = logits;
+  p.psum = (double*)at(ws, L.probsum);
+  MOE_LAUNCH(launch_probsum(p, stream));
+  return run_aux_final(*cfg, p.psum, probsum_num_blocks(cfg->T), counts_pre, aux, stream);
+}
+
+moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_router, const float* bias,
+                         const float* gumbel, const void* w1, const void* w2, void* out, float* aux,
+                         moe_debug_outputs* dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(moe_validate_config(cfg));
+  if (!x || !w_router || !w1 || !w2 || !out || !aux) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(out)) return MOE_ERR_INVALID_ARGUMENT;
+  MOE_TRY(check_ws(cfg, ws, ws_bytes));
+  moe_debug_outputs none{};
+  const moe_debug_outputs& D = dbg ? *dbg : none;
+  if (D.events && D.n_events < MOE_FORWARD_NUM_KERNELS + 1) return MOE_ERR_INVALID_ARGUMENT;
+  if ((D.xp && !aligned16(D.xp)) || (D.h && !aligned16(D.h)) || (D.y && !aligned16(D.y)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const Layout L = layout(*cfg);
+  const moe_config_t& c = *cfg;
+  auto pick = [&](void* user, size_t off) { return user ? user : (void*)at(ws, off); };
+  float* logits = (float*)D.logits;  // written only when requested
+  float* probs = D.probs;
+  int32_t* ids = (int32_t*)pick(D.ids, L.ids);
+  float* weights = (float*)pick(D.weights, L.weights);
+  int32_t* counts_pre = (int32_t*)pick(D.counts_pre, L.counts_pre);
+  int32_t* counts = (int32_t*)pick(D.counts, L.counts);
+  int32_t* offsets = (int32_t*)pick(D.offsets, L.offsets);
+  int32_t* perm = (int32_t*)pick(D.perm_token, L.perm);
+  int32_t* row_of = (int32_t*)pick(D.row_of, L.row_of);
+  uint8_t* dropped = (uint8_t*)pick(D.dropped, L.dropped);
+  int32_t* ndrop = (int32_t*)pick(D.n_dropped, L.ndrop);
+  void* xp = pick(D.xp, L.xp);
+  void* h = pick(D.h, L.h);
+  void* y = pick(D.y, L.y);
+  double* psum = (double*)at(ws, L.psum);
+  int ev = 0;
+  auto mark = [&]() -> moe_status_t {
+    if (!D.events) return MOE_OK;
+    return hip_status(hipEventRecord(D.events[ev++], stream));
+  };
+  MOE_TRY(mark());
+  MOE_TRY(run_route(c, x, w_router, bias, gumbel, nullptr, logits, probs, ids, weights, psum, ws, stream));
+  MOE_TRY(mark());
+  MOE_TRY(run_hist(c, ids, ws, stream));
+  MOE_TRY(mark());
+  MOE_TRY(run_scan(c, counts_pre, counts, offsets, ndrop, ws, stream));
+  MOE_TRY(mark());
+  MOE_TRY(run_gather(c, ids, x, offsets, perm, row_of, dropped, xp, ws, stream));
+  MOE_TRY(mark());
+  MOE_TRY(run_gemm(c, xp, w1, h, offsets, c.d_ffn, c.d_model, true, stream));
+  MOE_TRY(mark());
+  MOE_TRY(run_gemm(c, h, w2, y, offsets, c.d_model, c.d_ffn, false, stream));
+  MOE_TRY(mark());
+  MOE_TRY(run_combine(c, y, row_of, weights, out, stream));
+  MOE_TRY(mark());
+  MOE_TRY(run_aux_final(c, psum, route_num_waves(c.T), counts_pre, aux, stream));
+  MOE_TRY(mark());
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,148 @@
+// Internal declarations shared by the kernel files and the host API of libmoe.
+// Not part of the public ABI (that is include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ------------------------------------------------------------------------------ tile constants
+
+// Device-side copies of the public limits (include/moe.h).
+constexpr int MOE_MAX_EXPERTS_DEV = 64;
+constexpr int MOE_MAX_TOP_K_DEV = 8;
+
+// Router: one wave per tile of ROUTE_TILE tokens (two 16-row MFMA tiles); the grid is capped so
+// the per-wave probability partial sums stay small.
+constexpr int ROUTE_TILE = 32;
+constexpr int ROUTE_MAX_WAVES = 2048;
+
+// Dispatch: assignments per histogram block.
+constexpr int DISPATCH_CHUNK = 512;
+
+// Grouped GEMM tile (rows of the permuted activations x output columns).
+constexpr int GEMM_BM = 128;
+constexpr int GEMM_BN = 128;
+
+// ------------------------------------------------------------------------------ device helpers
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t u16) { return __uint_as_float(u16 << 16); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ------------------------------------------------------------------------------ kernel params
+
+struct RouteParams {
+  int T, d, E, k;
+  float tau;
+  int renormalize;
+  const void* x;            // [T, d] act
+  const void* wsplit;       // bf16 mode: [3][16*ET][d] bf16 split of W_r; fp32 mode: W_r [E, d]
+  const float* bias;        // [E] or null
+  const float* gumbel;      // [T, E] or null
+  const float* logits_in;   // [T, E] or null (skip the product)
+  float* logits_out;        // [T, E] or null
+  float* probs_out;         // [T, E] or null
+  int32_t* ids;             // [T, k]
+  float* weights;           // [T, k]
+  double* psum;             // [gridDim][E] per-wave probability sums, or null
+};
+
+struct HistParams {
+  int TK, E;                // TK = T * k assignments
+  const int32_t* ids;       // [TK]
+  int32_t* blk_hist;        // [nb][E]
+  int32_t* rank_local;      // [TK]
+};
+
+struct ScanParams {
+  int nb, E, capacity, TK;
+  const int32_t* blk_hist;  // [nb][E]
+  int32_t* blk_base;        // [nb][E]
+  int32_t* counts_pre;      // [E]
+  int32_t* counts;          // [E]
+  int32_t* offsets;         // [E+1]
+  int32_t* n_dropped;       // [1]
+};
+
+struct GatherParams {
+  int T, k, E, row_bytes, capacity;
+  const int32_t* ids;
+  const int32_t* blk_base;
+  const int32_t* rank_local;
+  const int32_t* offsets;
+  const uint8_t* x;
+  int32_t* row_of;
+  uint8_t* dropped;
+  int32_t* perm_token;
+  uint8_t* xp;
+};
+
+struct GemmParams {
+  int E, N, K;              // output columns N, reduction length K (per expert)
+  int max_rows;             // rows of A/C allocated (T * k)
+  const void* A;            // [rows, K] act
+  const void* B;            // [E, N, K] weights
+  void* C;                  // [rows, N] act
+  const int32_t* offsets;   // [E+1]
+};
+
+struct CombineParams {
+  int T, d, k;
+  int max_rows;             // rows of y (T * k); a row index outside [0, max_rows) counts as dropped
+  const void* y;
+  const int32_t* row_of;
+  const float* weights;
+  void* out;
+};
+
+struct AuxParams {
+  int T, E, k, nparts;
+  float coef;
+  float tau;
+  const double* psum;       // [nparts][E]
+  const int32_t* counts_pre;
+  float* aux;
+};
+
+struct ProbSumParams {
+  int T, E;
+  float tau;
+  const float* probs;       // [T, E] or null
+  const float* logits;      // [T, E] (used when probs is null)
+  double* psum;             // [gridDim][E]
+};
+
+// ------------------------------------------------------------------------------ launchers
+// Each returns the launch status (hipGetLastError after the launch).
+
+int route_num_waves(int T);
+int route_expert_tiles(int E);
+hipError_t launch_route_split(const float* w_router, int E, int d, void* wsplit, hipStream_t s);
+hipError_t launch_route(const RouteParams& p, bool bf16, hipStream_t s);
+
+int dispatch_num_blocks(int TK);
+hipError_t launch_hist(const HistParams& p, hipStream_t s);
+hipError_t launch_scan(const ScanParams& p, hipStream_t s);
+hipError_t launch_gather(const GatherParams& p, hipStream_t s);
+
+int gemm_max_mtiles(int max_rows, int E);
+hipError_t launch_gemm(const GemmParams& p, bool bf16, bool silu, hipStream_t s);
+
+hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s);
+
+int probsum_num_blocks(int T);
+hipError_t launch_probsum(const ProbSumParams& p, hipStream_t s);
+hipError_t launch_aux_final(const AuxParams& p, hipStream_t s);
+
+}  // namespace moe

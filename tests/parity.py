@@ -1,0 +1,175 @@
+"""Shared parity machinery: run the HIP path with every intermediate captured, run the oracle
+on the same seeded inputs, and compare them step by step.
+
+Protocol (the same inputs go to both sides):
+* Mode R: the oracle routes the GPU's fp32 logits (same noise, tau, k, capacity). Expert ids,
+  counts, offsets, permutation, row map, drop mask and drop count must be bit-exact; gate
+  weights within 1e-6 absolute; the gathered rows bitwise equal to x.
+* Mode E: the oracle's own logits (fp64 dot products rounded to fp32) against the GPU's; ids
+  must agree for every token whose oracle gap between the k-th and (k+1)-th key is >= 1e-4.
+* FFN / combine / aux against the oracle run on the Mode-R routing: normwise error
+  max|gpu - ref| / max|ref| <= 2e-2 (bf16) or 1e-5 (fp32); aux relative error <= 1e-5.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+import oracle
+import sparse_mixture_experts_02_amd as moe
+from sparse_mixture_experts_02_amd.inputs import Workload, make_inputs
+
+GAP = 1e-4
+W_TOL = 1e-6
+AUX_RTOL = 1e-5
+NORM_TOL = {"bf16": 2e-2, "f32": 1e-5}
+
+
+def to_device(inp: dict, device="cuda") -> dict:
+    return {k: (v.to(device) if v is not None else None) for k, v in inp.items()}
+
+
+def capacity_of(w: Workload) -> int:
+    return oracle.capacity_from_factor(w.T, w.top_k, w.num_experts, w.capacity_factor)
+
+
+def run_gpu(cfg: moe.MoEConfig, dinp: dict) -> dict:
+    """moe_forward with every intermediate captured; returns CPU tensors."""
+    T, d, f, E, k = cfg.T, cfg.d_model, cfg.d_ffn, cfg.num_experts, cfg.top_k
+    dev = dinp["x"].device
+    dt = cfg.torch_dtype
+    i32 = dict(dtype=torch.int32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dbg = {
+        "logits": torch.empty(T, E, **f32), "probs": torch.empty(T, E, **f32),
+        "ids": torch.empty(T, k, **i32), "weights": torch.empty(T, k, **f32),
+        "counts_pre": torch.empty(E, **i32), "counts": torch.empty(E, **i32),
+        "offsets": torch.empty(E + 1, **i32), "perm_token": torch.full((T * k,), -7, **i32),
+        "row_of": torch.empty(T, k, **i32), "dropped": torch.empty(T, k, dtype=torch.uint8, device=dev),
+        "n_dropped": torch.empty(1, **i32), "xp": torch.zeros(T * k, d, dtype=dt, device=dev),
+        "h": torch.zeros(T * k, f, dtype=dt, device=dev), "y": torch.zeros(T * k, d, dtype=dt, device=dev),
+    }
+    out, aux = moe.forward(cfg, dinp["x"], dinp["w_router"], dinp["w1"], dinp["w2"], bias=dinp["bias"],
+                           gumbel=dinp["gumbel"], debug=dbg)
+    torch.cuda.synchronize()
+    res = {k_: v.cpu() for k_, v in dbg.items()}
+    res["out"] = out.cpu()
+    res["aux"] = aux.cpu()
+    return res
+
+
+def normwise(gpu, ref) -> float:
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    if r.size == 0:
+        return 0.0
+    m = np.max(np.abs(r))
+    return float(np.max(np.abs(g - r)) / m) if m > 0 else float(np.max(np.abs(g)))
+
+
+@dataclasses.dataclass
+class Report:
+    name: str
+    logits_max_abs: float
+    near_ties: int
+    ids_mismatch_outside_ties: int
+    n_kept: int
+    n_dropped: int
+    w_max_abs: float
+    h_err: Optional[float]
+    y_err: Optional[float]
+    out_err: float
+    aux_rel: tuple
+
+
+def check_routing_and_dispatch(w: Workload, cfg: moe.MoEConfig, inp: dict, g: dict):
+    """Mode R and Mode E routing checks plus bit-exact dispatch; returns (routing, dispatch,
+    near-tie count, logits diff, ids mismatches outside near ties)."""
+    T, k, E = cfg.T, cfg.top_k, cfg.num_experts
+    C = cfg.capacity if cfg.capacity >= 0 else T
+    # Mode R: route the GPU's logits
+    r = oracle.route(logits=g["logits"].numpy(), gumbel=inp["gumbel"], tau=cfg.temperature, k=k,
+                     renormalize=cfg.renormalize)
+    assert np.array_equal(g["ids"].numpy(), r.ids), "Mode R: expert ids differ"
+    w_err = float(np.max(np.abs(g["weights"].numpy().astype(np.float64) - r.weights))) if T else 0.0
+    assert w_err <= W_TOL, f"Mode R: gate weights differ by {w_err}"
+    probs_err = float(np.max(np.abs(g["probs"].numpy() - r.probs)))
+    assert probs_err <= W_TOL, f"router probabilities differ by {probs_err}"
+    # Mode E: the oracle's own logits
+    re = oracle.route(inp["x"], inp["w_router"], inp["bias"], inp["gumbel"], cfg.temperature, k, cfg.renormalize)
+    l_err = float(np.max(np.abs(g["logits"].numpy().astype(np.float64) - re.logits)))
+    scale = max(1.0, float(np.max(np.abs(re.logits))))
+    assert l_err <= 1e-5 * scale, f"Mode E: logits differ by {l_err}"
+    gap = oracle.topk_gap(re.keys, k)
+    clear = gap >= GAP
+    mism = int(np.sum(np.any(g["ids"].numpy() != re.ids, axis=1) & clear))
+    assert mism == 0, f"Mode E: {mism} tokens with a clear top-k gap route differently"
+    # dispatch, bit-exact on the Mode-R ids
+    dp = oracle.dispatch(r.ids, E, C, inp["x"])
+    N = int(dp.offsets[-1])
+    assert np.array_equal(g["counts_pre"].numpy(), dp.counts_pre), "counts_pre differ"
+    assert np.array_equal(g["counts"].numpy(), dp.counts), "counts differ"
+    assert np.array_equal(g["offsets"].numpy(), dp.offsets), "offsets differ"
+    assert np.array_equal(g["perm_token"].numpy()[:N], dp.perm_token), "perm_token differs"
+    assert np.array_equal(g["row_of"].numpy(), dp.row_of), "row_of differs"
+    assert np.array_equal(g["dropped"].numpy(), dp.dropped), "dropped differs"
+    assert int(g["n_dropped"][0]) == dp.n_dropped, "n_dropped differs"
+    xp = g["xp"][:N]
+    assert torch.equal(xp.view(torch.int16) if xp.dtype == torch.bfloat16 else xp.view(torch.int32),
+                       dp.xp.view(torch.int16) if dp.xp.dtype == torch.bfloat16 else dp.xp.view(torch.int32)), \
+        "gathered rows differ"
+    return r, dp, int(np.sum(~clear)), l_err, mism, w_err
+
+
+def check_full(name: str, w: Workload, cfg: moe.MoEConfig, inp: dict, g: dict, sample_tokens=None) -> Report:
+    """Every check; with sample_tokens, FFN/combine are checked on those tokens only."""
+    storage = cfg.dtype
+    r, dp, nties, l_err, mism, w_err = check_routing_and_dispatch(w, cfg, inp, g)
+    N = int(dp.offsets[-1])
+    tol = NORM_TOL[storage]
+    h_err = y_err = None
+    if sample_tokens is None:
+        h, y = oracle.expert_ffn(g["xp"][:N], dp.offsets, inp["w1"], inp["w2"], storage)
+        h_err = normwise(g["h"][:N].float().numpy(), h)
+        y_err = normwise(g["y"][:N].float().numpy(), y)
+        assert h_err <= tol, f"H normwise error {h_err}"
+        assert y_err <= tol, f"Y normwise error {y_err}"
+        out_ref = oracle.combine(y, dp.row_of, g["weights"].numpy(), storage, d=cfg.d_model)
+        out_err = normwise(g["out"].float().numpy(), out_ref)
+        # the combine alone, on the GPU's own Y: the fp32 accumulation error (k roundings, each
+        # relative to the magnitude of the terms) plus one final rounding to the storage type
+        gy = g["y"][:N].float().numpy().astype(np.float64)
+        out_from_gpu_y = oracle.combine(gy, dp.row_of, g["weights"].numpy(), storage, d=cfg.d_model)
+        mag = np.zeros_like(out_from_gpu_y)
+        gw = np.abs(g["weights"].numpy().astype(np.float64))
+        for j in range(cfg.top_k):
+            kept = dp.row_of[:, j] >= 0
+            mag[kept] += gw[kept, j][:, None] * np.abs(gy[dp.row_of[kept, j]])
+        ulp = 2.0 ** -7 if storage == "bf16" else 2.0 ** -22
+        dev = np.abs(g["out"].float().numpy() - out_from_gpu_y)
+        bound = ulp * np.abs(out_from_gpu_y) + cfg.top_k * 2.0 ** -23 * mag + 1e-38
+        assert np.all(dev <= bound), f"combine deviates beyond its rounding bound: {np.max(dev - bound)}"
+    else:
+        rows = oracle.forward_rows(inp["x"], inp["w1"], inp["w2"], r.ids, g["weights"].numpy(), dp.dropped,
+                                   sample_tokens, storage)
+        out_err = normwise(g["out"][sample_tokens].float().numpy(), rows)
+    assert out_err <= tol, f"output normwise error {out_err}"
+    # aux from the GPU's probabilities (Mode R) and the pre-cut counts
+    a_switch, a_bal = oracle.aux_loss(r.probs, dp.counts_pre, cfg.top_k, cfg.aux_coef)
+    ga = g["aux"].numpy().astype(np.float64)
+    rel = (abs(ga[0] - a_switch) / max(abs(a_switch), 1e-30), abs(ga[1] - a_bal) / max(abs(a_bal), 1e-30))
+    assert rel[0] <= AUX_RTOL, f"aux_switch {ga[0]} vs {a_switch}"
+    assert rel[1] <= AUX_RTOL or abs(ga[1] - a_bal) <= 1e-12, f"aux_balance {ga[1]} vs {a_bal}"
+    return Report(name, l_err, nties, mism, N, dp.n_dropped, w_err, h_err, y_err, out_err, rel)
+
+
+def run_and_check(name: str, w: Workload, cfg: Optional[moe.MoEConfig] = None, sample_tokens=None) -> Report:
+    inp = make_inputs(w)
+    cfg = cfg or moe.config_for(w)
+    g = run_gpu(cfg, to_device(inp))
+    rep = check_full(name, w, cfg, inp, g, sample_tokens)
+    print(rep, flush=True)
+    return rep
