@@ -36,7 +36,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens of the CPU-oracle sample (0 = the whole workload)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed steps, run one elementwise copy of this many MiB (a known-size "
+                         "kernel to scale hardware byte counters against)")
     return ap.parse_args()
 
 
@@ -45,7 +49,7 @@ def cpu_baseline(w, inp, ntok: int) -> dict:
     import oracle
     from threadpoolctl import threadpool_info
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    ntok = min(ntok, w.T)
+    ntok = w.T if ntok <= 0 else min(ntok, w.T)
     x = inp["x"][:ntok]
     g = inp["gumbel"][:ntok] if inp["gumbel"] is not None else None
     C = oracle.capacity_from_factor(ntok, w.top_k, w.num_experts, w.capacity_factor)
@@ -100,6 +104,15 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)   # reads n*4 bytes, writes n*4 bytes
+        torch.cuda.synchronize()
+        del src, dst
 
     per_kernel = np.zeros((args.steps, MOE_FORWARD_NUM_KERNELS))
     for i, ev in enumerate(events):
