@@ -32,8 +32,8 @@ Layout layout(const moe_config_t& c) {
   const size_t T = (size_t)c.T, k = (size_t)c.top_k, E = (size_t)c.num_experts;
   const size_t d = (size_t)c.d_model, f = (size_t)c.d_ffn, TK = T * k, a = act_size(c);
   const size_t EP = 16 * (size_t)route_expert_tiles(c.num_experts);
-  L.wsplit = take(3 * EP * d * 2);
-  L.psum = take((size_t)route_num_waves(c.T) * E * sizeof(double));
+  L.wsplit = take(3 * EP * (size_t)route_padded_d(c.d_model) * 2);
+  L.psum = take((size_t)route_max_parts(c.T) * E * sizeof(double));
   const size_t nb = (size_t)dispatch_num_blocks((int)TK);
   L.blk_hist = take(nb * E * 4);
   L.blk_base = take(nb * E * 4);
@@ -93,6 +93,7 @@ moe_status_t run_route(const moe_config_t& c, const void* x, const float* w_rout
   RouteParams p{};
   p.T = c.T;
   p.d = c.d_model;
+  p.dpad = route_padded_d(c.d_model);
   p.E = c.num_experts;
   p.k = c.top_k;
   p.tau = c.temperature;
@@ -369,7 +370,8 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
   MOE_TRY(mark());
   MOE_TRY(run_combine(c, y, row_of, weights, out, stream));
   MOE_TRY(mark());
-  MOE_TRY(run_aux_final(c, psum, route_num_waves(c.T), counts_pre, aux, stream));
+  MOE_TRY(run_aux_final(c, psum, route_num_parts(c.T, c.num_experts, c.act_dtype == MOE_BF16, false), counts_pre,
+                        aux, stream));
   MOE_TRY(mark());
   return MOE_OK;
 }

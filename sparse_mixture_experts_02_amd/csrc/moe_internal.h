@@ -14,8 +14,8 @@ namespace moe {
 constexpr int MOE_MAX_EXPERTS_DEV = 64;
 constexpr int MOE_MAX_TOP_K_DEV = 8;
 
-// Router: one wave per tile of ROUTE_TILE tokens (two 16-row MFMA tiles); the grid is capped so
-// the per-wave probability partial sums stay small.
+// Generic router: one wave per tile of ROUTE_TILE tokens (two 16-row MFMA tiles); the grid is
+// capped so the per-wave probability partial sums stay small.
 constexpr int ROUTE_TILE = 32;
 constexpr int ROUTE_MAX_WAVES = 2048;
 
@@ -44,10 +44,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 struct RouteParams {
   int T, d, E, k;
+  int dpad;                 // row length of the split weight planes (d rounded up to 128)
   float tau;
   int renormalize;
   const void* x;            // [T, d] act
-  const void* wsplit;       // bf16 mode: [3][16*ET][d] bf16 split of W_r; fp32 mode: W_r [E, d]
+  const void* wsplit;       // bf16 mode: [3][16*ET][dpad] bf16 split of W_r; fp32 mode: W_r [E, d]
   const float* bias;        // [E] or null
   const float* gumbel;      // [T, E] or null
   const float* logits_in;   // [T, E] or null (skip the product)
@@ -55,7 +56,7 @@ struct RouteParams {
   float* probs_out;         // [T, E] or null
   int32_t* ids;             // [T, k]
   float* weights;           // [T, k]
-  double* psum;             // [gridDim][E] per-wave probability sums, or null
+  double* psum;             // [route_num_parts][E] per-wave probability sums, or null
 };
 
 struct HistParams {
@@ -126,8 +127,10 @@ struct ProbSumParams {
 // ------------------------------------------------------------------------------ launchers
 // Each returns the launch status (hipGetLastError after the launch).
 
-int route_num_waves(int T);
 int route_expert_tiles(int E);
+int route_padded_d(int d);
+int route_num_parts(int T, int E, bool bf16, bool logits_in);   // rows of psum a launch writes
+int route_max_parts(int T);
 hipError_t launch_route_split(const float* w_router, int E, int d, void* wsplit, hipStream_t s);
 hipError_t launch_route(const RouteParams& p, bool bf16, hipStream_t s);
 
