@@ -44,6 +44,28 @@ def parse():
     return ap.parse_args()
 
 
+def recorded_traffic(workload: str, kernel: str):
+    """HBM-side bytes per dispatch (FETCH_SIZE + WRITE_SIZE, calibrated) recorded in
+    profiles/traffic_<workload>.txt for `kernel`, or None when no record exists or the grouped
+    GEMM source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    src = os.path.join(ROOT, "sparse_mixture_experts_02_amd", "csrc", "gemm_big.hip")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if line.startswith("# ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("gemm_big.hip sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    try:
+        return int(rec[f"{kernel} fetch_bytes"]) + int(rec[f"{kernel} write_bytes"])
+    except KeyError:
+        return None
+
+
 def cpu_baseline(w, inp, ntok: int) -> dict:
     """The oracle, as it stands, on the first `ntok` tokens of the workload (all weights)."""
     import oracle
@@ -130,7 +152,9 @@ def main():
     t_g1 = kms[names.index("gemm1_silu")] * 1e-3
     t_g2 = kms[names.index("gemm2")] * 1e-3
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    g1_tflops = flop_gemm / t_g1 / 1e12
+    dom = "gemm1_silu" if t_g1 >= t_g2 else "gemm2"          # the dominant kernel
+    t_dom = max(t_g1, t_g2)
+    dom_tflops = flop_gemm / t_dom / 1e12
     gemm_tflops = 2 * flop_gemm / (t_g1 + t_g2) / 1e12
     dispatch_bytes = T * d * a + N * d * a + 12 * T * w.top_k
     combine_bytes = N * d * a + T * d * a + 8 * T * w.top_k
@@ -153,11 +177,15 @@ def main():
         "config": {"workload": w.name, "T": T, "d_model": d, "d_ffn": f, "num_experts": w.num_experts,
                    "top_k": w.top_k, "capacity": cfg.capacity, "temperature": w.temperature,
                    "gumbel": w.gumbel, "router_bias": w.router_bias, "parallelism": "single GPU"},
-        "roofline": {"kernel": "gemm1_silu", "bound": "mfma", "achieved": g1_tflops, "peak": peak,
-                     "unit": "TFLOP/s", "frac": g1_tflops / peak, "traffic": None},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": dom_tflops, "peak": peak,
+                     "unit": "TFLOP/s", "frac": dom_tflops / peak, "traffic": recorded_traffic(w.name, dom),
+                     "traffic_unit": "bytes per dispatch beyond L2 (FETCH_SIZE+WRITE_SIZE, calibrated)",
+                     "algorithmic_bytes": N * d * a + w.num_experts * d * f * a + N * f * a},
         "gemm_tflops": gemm_tflops,
         "gemm_frac_of_peak": gemm_tflops / peak,
         "kernel_ms": {n: float(v) for n, v in zip(names, kms)},
+        "route_gbs": (T * d * a + w.num_experts * d * 4 + T * w.num_experts * 4 * (2 if w.gumbel else 1)
+                      + 8 * T * w.top_k) / (kms[names.index("route")] * 1e-3) / 1e9,
         "dispatch_gbs": dispatch_bytes / t_disp / 1e9,
         "combine_gbs": combine_bytes / t_comb / 1e9,
         "kept_rows": N,
