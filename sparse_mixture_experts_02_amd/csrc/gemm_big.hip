@@ -1,30 +1,32 @@
-// Grouped expert GEMM, large-segment variant (bf16): a 256 x 256 output tile per workgroup.
+// Grouped expert GEMM, large-segment variant (bf16): persistent workgroups, 256 x 256 tiles.
 //
 //   C[r, n] = act( sum_k A[r, k] * B[e, n, k] ),  r in expert e's segment of the permuted rows,
 // with act = SiLU for the first FFN layer (P4 §2.4: every expert is a two-layer FFN).
 //
 // Layout of the work:
+//  * One workgroup per CU (the grid is at most 256 workgroups), each walking a list of output
+//    tiles. Tiles of all experts are numbered on the device from the segment offsets; each of the
+//    8 XCDs (workgroup ids are dealt to XCDs round robin) works through one contiguous range of
+//    tile ids, ordered in groups of 4 m-tiles x all n-tiles so that the tiles running together on
+//    one XCD share rows of A and B in its L2.
 //  * 4 waves in a 2 x 2 arrangement, each owning a 128 x 128 quarter of the tile as 8 x 8
-//    v_mfma_f32_16x16x32_bf16 blocks (256 fp32 accumulators per lane, kept in AGPRs). On this
-//    chip the 16x16x32 form sustains a higher rate than 32x32x16.
-//  * K advances 64 elements (128 bytes of every row, whole 128-byte lines) per stage. Two LDS
-//    stages (2 x (A + B) x 256 rows x 128 B = 128 KiB) are filled by gfx950's direct global ->
-//    LDS 16-byte loads, so no registers stage the data; stage s + 1 is requested when stage s
-//    starts.
-//  * A stage is two k-steps of 32. Operand fragments are read one k-step ahead, interleaved
-//    with the MFMAs. The one barrier per stage sits in the middle of the second k-step: after it
-//    stage s + 1 is complete in LDS and stage s's buffer is free, and the fragment reads of
-//    stage s + 1 overlap the remaining MFMAs of stage s.
-//  * LDS rows are 128 B with the eight 16-byte chunks XOR-swizzled by (row / 2) mod 8: 16 lanes
-//    reading 16 consecutive rows at one chunk then touch all 64 banks once.
-//  * The MFMA's first operand is the weight tile (its 16 rows are output features) and the
-//    second the activation tile, so each lane ends with 4 consecutive output features of one
-//    row: the epilogue (SiLU in fp32, one rounding to bf16) stores 8 bytes per lane.
-//  * Tiles of all experts are numbered on the device from the segment offsets. Workgroup ids
-//    are remapped so that each of the 8 XCDs (ids are dealt to XCDs round robin) works through
-//    one contiguous range of tiles, ordered in groups of 4 m-tiles x all n-tiles, so that the
-//    tiles running together on one XCD share rows of A and B in its L2.
-// K must be a multiple of 64.
+//    v_mfma_f32_16x16x32_bf16 blocks (256 fp32 accumulators per lane, kept in AGPRs).
+//  * K advances 64 elements (128 bytes of every row) per stage. Two LDS stages (2 x (A + B) x
+//    256 rows x 128 B = 128 KiB) are filled by direct buffer -> LDS 16-byte loads; stage s + 1 is
+//    requested when stage s starts. A stage is two k-steps of 32; operand fragments are read one
+//    k-step ahead, interleaved with the MFMAs, and the one barrier per stage sits in the middle of
+//    the second k-step.
+//  * The loads address rows through buffer resources whose size is the tile's valid rows of A (or
+//    of B): rows past a segment's end or past N fall outside the resource and are not fetched.
+//    They only feed accumulators whose outputs are never stored.
+//  * Overlapped tile boundary: once the last stage of a tile has been read from LDS, the first two
+//    stages of the next tile are requested, and the epilogue (SiLU in fp32, one rounding to bf16)
+//    of the finished tile runs while they load.
+//  * Epilogue: the MFMA leaves 4 consecutive output features of one row per lane; it is turned
+//    into whole output rows through a small per-wave LDS area (see the epilogue) and stored with
+//    16-byte buffer stores, 4 rows x 256 contiguous bytes per instruction, through a buffer
+//    resource sized to the tile's valid rows (lanes past N get an out-of-range offset).
+// K must be a multiple of 64 and N of 8.
 #include "moe_internal.h"
 
 namespace moe {
@@ -34,8 +36,12 @@ constexpr int BIG_BM = 256, BIG_BN = 256;
 constexpr int ROWB = 128;                     // staged bytes of one row per stage (64 bf16)
 constexpr int TILE_BYTES = BIG_BM * ROWB;     // one operand, one stage: 32 KiB
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;   // A + B
-constexpr int NSTAGE = 2;
 constexpr int GROUP_M = 4;
+constexpr int MAX_WGS = 256;                  // one workgroup per CU
+constexpr int EPI_BYTES = 16 * 256;            // per wave: 16 output rows x 128 bf16
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * ROWB + ((chunk ^ ((row >> 1) & 7)) << 4);
@@ -48,127 +54,147 @@ __device__ __forceinline__ float silu_fast(float v) {
   return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// acc += A * B on v_mfma_f32_16x16x32_bf16 with the accumulator bound to AGPRs. Written as inline
-// asm so that all 256 accumulators of a lane stay in the AGPR file: left to itself the register
-// allocator shuffles some of them through VGPRs inside the main loop. Same-shape MFMAs chained
-// on one accumulator are interlocked by the hardware; the first read of the results after the
-// loop is preceded by explicit wait states.
+// acc += A * B on v_mfma_f32_16x16x32_bf16 with the accumulator bound to AGPRs (inline asm keeps
+// all 256 accumulators of a lane in the AGPR file). Same-shape MFMAs chained on one accumulator
+// are interlocked by the hardware; the first read of the results after the loop is preceded by
+// explicit wait states.
 __device__ __forceinline__ void mfma_16x16x32(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
-// One direct global -> LDS 16-byte load per lane (gfx950 global_load_lds_dwordx4): lane l reads
-// sbase + voff and writes LDS bytes [lds_addr + 16 l, lds_addr + 16 l + 16). M0 carries the LDS
-// address and is restored afterwards. Issued as inline asm so that the compiler does not wait
-// on it before unrelated LDS reads; the kernel counts these loads and waits (vmcnt) itself.
-__device__ __forceinline__ void load_lds16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+// Raw buffer resource (stride 0) over `bytes` bytes from `base`: lanes whose offset is at or past
+// `bytes` are out of range (loads fetch nothing, stores write nothing).
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return i32x4_t{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)),
+                 __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
+// One direct buffer -> LDS 16-byte load per lane: lane l reads rsrc + voff and writes LDS bytes
+// [lds_addr + 16 l, lds_addr + 16 l + 16). M0 carries the LDS address and is restored afterwards.
+// Inline asm, so the compiler neither waits on it nor reorders it against the other inline asm;
+// the kernel counts these loads and waits (vmcnt) itself.
+__device__ __forceinline__ void load_lds16(i32x4_t rsrc, uint32_t voff, uint32_t lds_addr) {
   uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
                : "=&s"(saved)
-               : "s"(lds_addr), "v"(voff), "s"(sbase)
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
                : "memory");
 }
 
-__device__ __forceinline__ void wait_loads_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// One 16-byte buffer store per lane; lanes that must not write carry an out-of-range offset. The
+// output is not read again by this kernel, so it is stored with the non-temporal hint and does not
+// displace the operand rows that the XCD's L2 is serving to the other tiles. The compiler does not
+// see inside the asm, so the wait states that a store of more than 64 bits needs before a VALU
+// instruction may overwrite its data registers are part of it.
+__device__ __forceinline__ void store16(i32x4_t rsrc, uint32_t voff, u32x4_t v) {
+  asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen nt\n\ts_nop 1" ::"v"(v), "v"(voff), "s"(rsrc) : "memory");
+}
+
+// Waits until every vector-memory operation of the wave has completed (the direct-to-LDS loads
+// are not assumed to complete in issue order, so no partial count is used).
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+struct Tile {
+  int e, row0, rows, n0, cols;
+};
 }  // namespace
 
 template <bool SILU>
 __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
+
+  __shared__ int seg[MOE_MAX_EXPERTS_DEV + 1];
+  __shared__ __attribute__((aligned(16))) uint8_t epi[4 * EPI_BYTES];
 
   const int tid = threadIdx.x;
   const int E = p.E, N = p.N;
   // Segment bounds, clamped into [0, max_rows] and made non-decreasing so that no offsets value
-  // can send a block outside the buffers. Every lane walks the (uniform) offsets itself: the
-  // LDS is entirely taken by the stage ring.
-  auto bound = [&](int e, int prev) {
-    const int o = p.offsets[e];
-    return o < prev ? prev : (o > p.max_rows ? p.max_rows : o);
-  };
-  const int base0 = bound(0, 0);
-  int MT = 0;
-  {
-    int prev = base0;
-    for (int e = 1; e <= E; ++e) {
-      const int o = bound(e, prev);
-      MT += (o - prev + BIG_BM - 1) / BIG_BM;
-      prev = o;
+  // can send a tile outside the buffers. Kept in LDS: tiles are decoded between the kernel's own
+  // counted memory operations, where a global load (and the wait for it) would not belong.
+  if (tid == 0) {
+    int prev = 0;
+    for (int e = 0; e <= E; ++e) {
+      const int o = p.offsets[e];
+      prev = o < prev ? prev : (o > p.max_rows ? p.max_rows : o);
+      seg[e] = prev;
     }
   }
+  __syncthreads();
+  int MT = 0;
+  for (int e = 0; e < E; ++e) MT += (seg[e + 1] - seg[e] + BIG_BM - 1) / BIG_BM;
   const int NT = (N + BIG_BN - 1) / BIG_BN;
   const int total = MT * NT;
-  const int wg = blockIdx.x;
-  if (wg >= total) return;
-  // XCD-aware remap: XCD x (= wg mod 8) takes a contiguous range of tile ids.
-  const int q = total >> 3, rem = total & 7, xcd = wg & 7, local = wg >> 3;
-  const int id = (xcd < rem) ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
-  const int group = id / (GROUP_M * NT);
-  const int first_m = group * GROUP_M;
-  const int gm = min(GROUP_M, MT - first_m);
-  const int in_group = id - group * GROUP_M * NT;
-  const int mt = first_m + in_group % gm;
-  const int nt = in_group / gm;
-  int e = 0, row0 = 0, row_end = 0;
-  {
-    int prev = base0, tstart = 0;
+  // This XCD's contiguous range of tile ids, walked by its workgroups with a stride of their count.
+  const int G = gridDim.x, xcd = blockIdx.x & 7;
+  const int q = total >> 3, rem = total & 7;
+  const int cnt = (xcd < rem) ? q + 1 : q;
+  const int start = (xcd < rem) ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q;
+  const int step = (G - xcd + 7) >> 3;
+  int local = blockIdx.x >> 3;
+  if (local >= cnt) return;
+
+  auto decode = [&](int id) {
+    const int group = id / (GROUP_M * NT);
+    const int first_m = group * GROUP_M;
+    const int gm = min(GROUP_M, MT - first_m);
+    const int in_group = id - group * GROUP_M * NT;
+    const int mt = first_m + in_group % gm;
+    const int nt = in_group / gm;
+    Tile t{0, 0, 0, nt * BIG_BN, min(N - nt * BIG_BN, BIG_BN)};
+    int tstart = 0;
     for (int ee = 0; ee < E; ++ee) {
-      const int o = bound(ee + 1, prev);
-      const int t = (o - prev + BIG_BM - 1) / BIG_BM;
-      if (mt < tstart + t) {
-        e = ee;
-        row0 = prev + (mt - tstart) * BIG_BM;
-        row_end = o;
+      const int lo = seg[ee], hi = seg[ee + 1];
+      const int n = (hi - lo + BIG_BM - 1) / BIG_BM;
+      if (mt < tstart + n) {
+        t.e = ee;
+        t.row0 = lo + (mt - tstart) * BIG_BM;
+        t.rows = min(hi - t.row0, BIG_BM);
         break;
       }
-      tstart += t;
-      prev = o;
+      tstart += n;
     }
-  }
-  if (row_end <= row0) return;   // unreachable for mt < MT; keeps every address below in range
-  const int n0 = nt * BIG_BN;
-  const int rowbytes = p.K * 2;
-  const uint8_t* __restrict__ A = (const uint8_t*)p.A;
-  const uint8_t* __restrict__ B = (const uint8_t*)p.B + (size_t)e * N * rowbytes;
+    return t;
+  };
 
-  // Direct loads: one instruction moves 16 rows x 64 B; lane l lands at byte 16 l of the
-  // instruction's 1 KiB, i.e. row l / 4, slot l % 4, and loads the global chunk that the
-  // swizzle puts in that slot. Wave w fills rows [64 w, 64 w + 64) of both tiles. Rows past the
-  // segment (or past N) are clamped to a valid row: they only feed outputs the epilogue masks.
+  const int rowbytes = p.K * 2;
+  const int nk = rowbytes / ROWB;
+  const uint8_t* __restrict__ A = (const uint8_t*)p.A;
+  const uint8_t* __restrict__ B = (const uint8_t*)p.B;
+  uint16_t* __restrict__ C = (uint16_t*)p.C;
+
+  // Direct loads: one instruction moves 8 rows x 128 B; lane l lands at byte 16 l of the
+  // instruction's 1 KiB, i.e. row l / 8, slot l % 8, and loads the global chunk that the swizzle
+  // puts in that slot. Wave w fills rows [64 w, 64 w + 64) of both operand tiles; the offsets
+  // (relative to the tile's first row) are the same for A and B.
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint32_t offA[8], offB[8];
+  uint32_t voff[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = w * 64 + i * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ (((i & 1) << 2) | (lane >> 4));
-    const int ra = min(row0 + r, row_end - 1);
-    const int rb = min(n0 + r, N - 1);
-    offA[i] = (uint32_t)ra * (uint32_t)rowbytes + chunk * 16;
-    offB[i] = (uint32_t)rb * (uint32_t)rowbytes + chunk * 16;
+    voff[i] = (uint32_t)r * (uint32_t)rowbytes + chunk * 16;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  const int nk = rowbytes / ROWB;
-  auto issue = [&](int kt) {
+  // Requests stage kt (clamped to the last one: a harmless reload) of tile t into buffer kt & 1.
+  auto issue = [&](const Tile& t, int kt) {
     const int st = min(kt, nk - 1);
-    const uint8_t* akt = A + (size_t)st * ROWB;
-    const uint8_t* bkt = B + (size_t)st * ROWB;
+    const i32x4_t ra = make_rsrc(A + (size_t)t.row0 * rowbytes + st * ROWB, (uint32_t)t.rows * rowbytes);
+    const i32x4_t rb = make_rsrc(B + ((size_t)t.e * N + t.n0) * rowbytes + st * ROWB, (uint32_t)t.cols * rowbytes);
     const uint32_t sa = lds0 + (kt & 1) * STAGE_BYTES + w * 64 * ROWB;
     const uint32_t sb = sa + TILE_BYTES;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      load_lds16(akt, offA[i], sa + i * 8 * ROWB);
-      load_lds16(bkt, offB[i], sb + i * 8 * ROWB);
+      load_lds16(ra, voff[i], sa + i * 8 * ROWB);
+      load_lds16(rb, voff[i], sb + i * 8 * ROWB);
     }
   };
 
   const int wm = w >> 1, wn = w & 1;
   const int fr = lane & 15, fc = lane >> 4;   // fragment row within 16, 16-byte chunk
   f32x4_t acc[8][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
   bf16x8_t xa[2][8], wb[2][8];
   auto frag_x = [&](int buf, int stage, int ks, int i) {
     const uint8_t* sa = smem + (stage & 1) * STAGE_BYTES;
@@ -179,86 +205,137 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p) {
     wb[buf][j] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(sb + lds_off(wn * 128 + j * 16 + fr, ks * 4 + fc)));
   };
 
-  issue(0);
-  wait_loads_all();
-  __syncthreads();
+  Tile cur = decode(start + local);
+  issue(cur, 0);
+  issue(cur, 1);
+  while (true) {
+    const int nlocal = local + step;
+    const bool more = nlocal < cnt;
+    const Tile nxt = more ? decode(start + nlocal) : cur;
+    // Stages 0 and 1 of `cur` are in flight (and the previous tile's epilogue stores).
+    wait_vm_all();
+    __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) frag_x(0, 0, 0, i);
+    for (int i = 0; i < 8; ++i) frag_x(0, 0, 0, i);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) frag_w(0, 0, 0, j);
+    for (int j = 0; j < 8; ++j) frag_w(0, 0, 0, j);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int s = 0; s < nk; ++s) {
-    issue(s + 1);   // past the end: a harmless reload into the idle buffer
-    // k-step 0 of stage s from F0, reading k-step 1 of stage s into F1
+    for (int s = 0; s < nk; ++s) {
+      if (s >= 1 && s + 1 < nk) issue(cur, s + 1);
+      // k-step 0 of stage s from F0, reading k-step 1 of stage s into F1
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mfma_16x16x32(acc[i][j], wb[0][j], xa[0][i]);
+        frag_x(1, s, 1, i);
+        frag_w(1, s, 1, i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // first half of k-step 1
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
+      __builtin_amdgcn_sched_barrier(0);
+      // stage s + 1 has landed everywhere and nobody reads stage s's buffer any more
+      wait_vm_all();
+      __syncthreads();
+      // second half of k-step 1, reading k-step 0 of stage s + 1 into F0 (after the last stage
+      // the reads return whatever the buffer holds; they are overwritten before any use)
+#pragma unroll
+      for (int i = 4; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
+        frag_x(0, s + 1, 0, 2 * (i - 4));
+        frag_x(0, s + 1, 0, 2 * (i - 4) + 1);
+        frag_w(0, s + 1, 0, 2 * (i - 4));
+        frag_w(0, s + 1, 0, 2 * (i - 4) + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Every wave is past the last barrier of this tile, so both LDS buffers are free: request the
+    // next tile's first two stages before storing this one (after the last tile: a reload of this
+    // one, drained before the workgroup ends).
+    issue(nxt, 0);
+    issue(nxt, 1);
+    // let the last MFMAs retire before their accumulators are read
+    // (the most recently written accumulators pass through the wait so that no read of them can
+    // be scheduled before it)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]), "+a"(acc[7][3]),
+                   "+a"(acc[7][4]), "+a"(acc[7][5]), "+a"(acc[7][6]), "+a"(acc[7][7])
+                 :
+                 : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    // per-lane epilogue offsets, recomputed for every tile rather than held across the main loop
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    const int efr = lane_o & 15, efc = lane_o >> 4;
+
+    // Epilogue, one 16-row block at a time through a per-wave LDS area. Lane (fr, fc) holds
+    // features 4 fc .. 4 fc + 3 of row fr of every 16 x 16 block; swapping the odd 16-lane rows of
+    // block 2 jp with the even rows of block 2 jp + 1 leaves 8 consecutive features per lane (lane
+    // row fc gets columns 8 (fc / 2) + 16 (fc % 2) .. + 7 of the 32-column pair), written to LDS as
+    // one 16-byte chunk of a 256-byte row. Read back, each lane holds 16 bytes of one row and a
+    // store instruction covers 4 rows x 256 contiguous bytes: whole 128-byte lines, where the
+    // MFMA layout would store 16 rows x 64 bytes (a third of the throughput per CU). The 16 chunks
+    // of an LDS row are XOR-swizzled by the row so that both the writes (16 rows, one chunk) and
+    // the reads (one row, 16 chunks) touch every bank once.
+    const i32x4_t rc = make_rsrc(C + (size_t)cur.row0 * N, (uint32_t)cur.rows * N * 2);
+    uint8_t* const ep = epi + w * EPI_BYTES;
+    const int rrow = lane_o >> 4, rchunk = lane_o & 15;   // read-back: row within 4, chunk
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) mfma_16x16x32(acc[i][j], wb[0][j], xa[0][i]);
-      frag_x(1, s, 1, i);
-      frag_w(1, s, 1, i);
+      for (int jp = 0; jp < 4; ++jp) {
+        uint32_t P[2], Q[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float a0 = acc[i][2 * jp][2 * h], a1 = acc[i][2 * jp][2 * h + 1];
+          float b0 = acc[i][2 * jp + 1][2 * h], b1 = acc[i][2 * jp + 1][2 * h + 1];
+          if (SILU) {
+            a0 = silu_fast(a0);
+            a1 = silu_fast(a1);
+            b0 = silu_fast(b0);
+            b1 = silu_fast(b1);
+          }
+          const auto r = __builtin_amdgcn_permlane16_swap(f32_to_bf16_bits(a0) | (f32_to_bf16_bits(a1) << 16),
+                                                          f32_to_bf16_bits(b0) | (f32_to_bf16_bits(b1) << 16),
+                                                          false, false);
+          P[h] = r[0];
+          Q[h] = r[1];
+        }
+        const int chunk = jp * 4 + ((efc >> 1) | ((efc & 1) << 1));
+        *(uint4*)(ep + efr * 256 + ((chunk ^ efr) << 4)) = uint4{P[0], P[1], Q[0], Q[1]};
+      }
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int row = qd * 4 + rrow;
+        const uint4 v = *(const uint4*)(ep + row * 256 + ((rchunk ^ row) << 4));
+        const int m = wm * 128 + i * 16 + row;
+        const int n = wn * 128 + rchunk * 8;
+        const uint32_t off = (n < cur.cols) ? (uint32_t)(m * N + cur.n0 + n) * 2u : 0x80000000u;
+        store16(rc, off, u32x4_t{v.x, v.y, v.z, v.w});
+      }
+      // one 16-row block at a time: keeps the epilogue from pulling every accumulator into VGPRs
+      __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // first half of k-step 1
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
-    __builtin_amdgcn_sched_barrier(0);
-    // stage s + 1 has landed everywhere and nobody reads stage s's buffer any more
-    wait_loads_all();
-    __syncthreads();
-    // second half of k-step 1, reading k-step 0 of stage s + 1 into F0
-#pragma unroll
-    for (int i = 4; i < 8; ++i) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
-      frag_x(0, s + 1, 0, 2 * (i - 4));
-      frag_x(0, s + 1, 0, 2 * (i - 4) + 1);
-      frag_w(0, s + 1, 0, 2 * (i - 4));
-      frag_w(0, s + 1, 0, 2 * (i - 4) + 1);
-    }
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    if (!more) break;
+    cur = nxt;
+    local = nlocal;
   }
-  wait_loads_all();
-  // let the last MFMAs retire before their accumulators are read
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-
-  // epilogue: lane holds output features n = 4*(lane/16) + 0..3 of row m = lane % 16 of each
-  // 16 x 16 block
-  uint16_t* __restrict__ C = (uint16_t*)p.C;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int m = row0 + wm * 128 + i * 16 + fr;
-    if (m >= row_end) continue;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = n0 + wn * 128 + j * 16 + 4 * fc;
-      if (n >= N) continue;
-      float v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = SILU ? silu_fast(acc[i][j][u]) : acc[i][j][u];
-      uint2 o;
-      o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-      o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-      *(uint2*)(C + (size_t)m * N + n) = o;
-    }
-    // one 16-row block at a time: keeps the epilogue from pulling every accumulator into VGPRs
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  wait_vm_all();
 }
 
 int gemm_big_grid(int max_rows, int E, int N) {
-  return ((max_rows + BIG_BM - 1) / BIG_BM + E) * ((N + BIG_BN - 1) / BIG_BN);
+  const long tiles = (long)((max_rows + BIG_BM - 1) / BIG_BM + E) * ((N + BIG_BN - 1) / BIG_BN);
+  return (int)(tiles < MAX_WGS ? tiles : MAX_WGS);
 }
 
 hipError_t launch_gemm_big(const GemmParams& p, bool silu, hipStream_t s) {
