@@ -143,6 +143,8 @@ int gemm_max_mtiles(int max_rows, int E);
 hipError_t launch_gemm(const GemmParams& p, bool bf16, bool silu, hipStream_t s);
 int gemm_big_grid(int max_rows, int E, int N);
 hipError_t launch_gemm_big(const GemmParams& p, bool silu, hipStream_t s);
+int gemm_stream_grid(int E, int N);
+hipError_t launch_gemm_stream(const GemmParams& p, bool silu, hipStream_t s);
 
 hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s);
 
