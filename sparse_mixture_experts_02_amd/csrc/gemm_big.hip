@@ -9,8 +9,11 @@
 //    8 XCDs (workgroup ids are dealt to XCDs round robin) works through one contiguous range of
 //    tile ids, ordered in groups of 4 m-tiles x all n-tiles so that the tiles running together on
 //    one XCD share rows of A and B in its L2.
-//  * 4 waves in a 2 x 2 arrangement, each owning a 128 x 128 quarter of the tile as 8 x 8
-//    v_mfma_f32_16x16x32_bf16 blocks (256 fp32 accumulators per lane, kept in AGPRs).
+//  * 8 waves in a 2 x 4 arrangement, each owning 128 rows x 64 output features of the tile as
+//    8 x 4 v_mfma_f32_16x16x32_bf16 blocks (128 fp32 accumulators per lane, kept in AGPRs), so
+//    that each SIMD runs two waves: when one stalls issuing its direct loads or at a wait, the
+//    other keeps the matrix core busy (two waves per SIMD measured ~9% faster than one wave
+//    owning a 128 x 128 quarter, although the LDS fragment reads grow by half).
 //  * K advances 64 elements (128 bytes of every row) per stage. Two LDS stages (2 x (A + B) x
 //    256 rows x 128 B = 128 KiB) are filled by direct buffer -> LDS 16-byte loads; stage s + 1 is
 //    requested when stage s starts. A stage is two k-steps of 32; operand fragments are read one
@@ -24,7 +27,7 @@
 //    of the finished tile runs while they load.
 //  * Epilogue: the MFMA leaves 4 consecutive output features of one row per lane; it is turned
 //    into whole output rows through a small per-wave LDS area (see the epilogue) and stored with
-//    16-byte buffer stores, 4 rows x 256 contiguous bytes per instruction, through a buffer
+//    16-byte buffer stores, 8 rows x 128 contiguous bytes per instruction, through a buffer
 //    resource sized to the tile's valid rows (lanes past N get an out-of-range offset).
 // K must be a multiple of 64 and N of 8.
 #include "moe_internal.h"
@@ -38,7 +41,7 @@ constexpr int TILE_BYTES = BIG_BM * ROWB;     // one operand, one stage: 32 KiB
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;   // A + B
 constexpr int GROUP_M = 4;
 constexpr int MAX_WGS = 256;                  // one workgroup per CU
-constexpr int EPI_BYTES = 16 * 256;            // per wave: 16 output rows x 128 bf16
+constexpr int EPI_BYTES = 16 * 128;            // per wave: 16 output rows x 64 bf16
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
@@ -102,11 +105,11 @@ struct Tile {
 }  // namespace
 
 template <bool SILU>
-__global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p) {
+__global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
 
   __shared__ int seg[MOE_MAX_EXPERTS_DEV + 1];
-  __shared__ __attribute__((aligned(16))) uint8_t epi[4 * EPI_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t epi[8 * EPI_BYTES];
 
   const int tid = threadIdx.x;
   const int E = p.E, N = p.N;
@@ -166,14 +169,14 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p) {
 
   // Direct loads: one instruction moves 8 rows x 128 B; lane l lands at byte 16 l of the
   // instruction's 1 KiB, i.e. row l / 8, slot l % 8, and loads the global chunk that the swizzle
-  // puts in that slot. Wave w fills rows [64 w, 64 w + 64) of both operand tiles; the offsets
+  // puts in that slot. Wave w fills rows [32 w, 32 w + 32) of both operand tiles; the offsets
   // (relative to the tile's first row) are the same for A and B.
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint32_t voff[8];
+  uint32_t voff[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = w * 64 + i * 8 + (lane >> 3);
+  for (int i = 0; i < 4; ++i) {
+    const int r = w * 32 + i * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ (((i & 1) << 2) | (lane >> 4));
     voff[i] = (uint32_t)r * (uint32_t)rowbytes + chunk * 16;
   }
@@ -183,26 +186,26 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p) {
     const int st = min(kt, nk - 1);
     const i32x4_t ra = make_rsrc(A + (size_t)t.row0 * rowbytes + st * ROWB, (uint32_t)t.rows * rowbytes);
     const i32x4_t rb = make_rsrc(B + ((size_t)t.e * N + t.n0) * rowbytes + st * ROWB, (uint32_t)t.cols * rowbytes);
-    const uint32_t sa = lds0 + (kt & 1) * STAGE_BYTES + w * 64 * ROWB;
+    const uint32_t sa = lds0 + (kt & 1) * STAGE_BYTES + w * 32 * ROWB;
     const uint32_t sb = sa + TILE_BYTES;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       load_lds16(ra, voff[i], sa + i * 8 * ROWB);
       load_lds16(rb, voff[i], sb + i * 8 * ROWB);
     }
   };
 
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w >> 2, wn = w & 3;   // 2 x 4 waves, each 128 rows x 64 output features
   const int fr = lane & 15, fc = lane >> 4;   // fragment row within 16, 16-byte chunk
-  f32x4_t acc[8][8];
-  bf16x8_t xa[2][8], wb[2][8];
+  f32x4_t acc[8][4];
+  bf16x8_t xa[2][8], wb[2][4];
   auto frag_x = [&](int buf, int stage, int ks, int i) {
     const uint8_t* sa = smem + (stage & 1) * STAGE_BYTES;
     xa[buf][i] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(sa + lds_off(wm * 128 + i * 16 + fr, ks * 4 + fc)));
   };
   auto frag_w = [&](int buf, int stage, int ks, int j) {
     const uint8_t* sb = smem + (stage & 1) * STAGE_BYTES + TILE_BYTES;
-    wb[buf][j] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(sb + lds_off(wn * 128 + j * 16 + fr, ks * 4 + fc)));
+    wb[buf][j] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(sb + lds_off(wn * 64 + j * 16 + fr, ks * 4 + fc)));
   };
 
   Tile cur = decode(start + local);
@@ -218,11 +221,11 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) frag_x(0, 0, 0, i);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) frag_w(0, 0, 0, j);
+    for (int j = 0; j < 4; ++j) frag_w(0, 0, 0, j);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     for (int s = 0; s < nk; ++s) {
       if (s >= 1 && s + 1 < nk) issue(cur, s + 1);
@@ -230,16 +233,16 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) mfma_16x16x32(acc[i][j], wb[0][j], xa[0][i]);
+        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[0][j], xa[0][i]);
+        if (i < 4) frag_w(1, s, 1, i);
         frag_x(1, s, 1, i);
-        frag_w(1, s, 1, i);
       }
       __builtin_amdgcn_sched_barrier(0);
       // first half of k-step 1
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
+        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
       __builtin_amdgcn_sched_barrier(0);
       // stage s + 1 has landed everywhere and nobody reads stage s's buffer any more
       wait_vm_all();
@@ -249,11 +252,10 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p) {
 #pragma unroll
       for (int i = 4; i < 8; ++i) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
+        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
         frag_x(0, s + 1, 0, 2 * (i - 4));
         frag_x(0, s + 1, 0, 2 * (i - 4) + 1);
-        frag_w(0, s + 1, 0, 2 * (i - 4));
-        frag_w(0, s + 1, 0, 2 * (i - 4) + 1);
+        frag_w(0, s + 1, 0, i - 4);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                  : "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]), "+a"(acc[7][3]),
-                   "+a"(acc[7][4]), "+a"(acc[7][5]), "+a"(acc[7][6]), "+a"(acc[7][7])
+                   "+a"(acc[6][0]), "+a"(acc[6][1]), "+a"(acc[6][2]), "+a"(acc[6][3])
                  :
                  : "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -282,18 +284,17 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p) {
     // features 4 fc .. 4 fc + 3 of row fr of every 16 x 16 block; swapping the odd 16-lane rows of
     // block 2 jp with the even rows of block 2 jp + 1 leaves 8 consecutive features per lane (lane
     // row fc gets columns 8 (fc / 2) + 16 (fc % 2) .. + 7 of the 32-column pair), written to LDS as
-    // one 16-byte chunk of a 256-byte row. Read back, each lane holds 16 bytes of one row and a
-    // store instruction covers 4 rows x 256 contiguous bytes: whole 128-byte lines, where the
-    // MFMA layout would store 16 rows x 64 bytes (a third of the throughput per CU). The 16 chunks
-    // of an LDS row are XOR-swizzled by the row so that both the writes (16 rows, one chunk) and
-    // the reads (one row, 16 chunks) touch every bank once.
+    // one 16-byte chunk of the wave's 128-byte row. Read back, each lane holds 16 bytes of one row
+    // and a store instruction covers 8 rows x 128 contiguous bytes: whole lines, where the MFMA
+    // layout would store 16 rows x 64 bytes (a third of the throughput per CU). The 8 chunks of an
+    // LDS row are XOR-swizzled by the row.
     const i32x4_t rc = make_rsrc(C + (size_t)cur.row0 * N, (uint32_t)cur.rows * N * 2);
     uint8_t* const ep = epi + w * EPI_BYTES;
-    const int rrow = lane_o >> 4, rchunk = lane_o & 15;   // read-back: row within 4, chunk
+    const int rrow = lane_o >> 3, rchunk = lane_o & 7;   // read-back: row within 8, chunk
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
-      for (int jp = 0; jp < 4; ++jp) {
+      for (int jp = 0; jp < 2; ++jp) {
         uint32_t P[2], Q[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -312,18 +313,17 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p) {
           Q[h] = r[1];
         }
         const int chunk = jp * 4 + ((efc >> 1) | ((efc & 1) << 1));
-        *(uint4*)(ep + efr * 256 + ((chunk ^ efr) << 4)) = uint4{P[0], P[1], Q[0], Q[1]};
+        *(uint4*)(ep + efr * 128 + ((chunk ^ (efr & 7)) << 4)) = uint4{P[0], P[1], Q[0], Q[1]};
       }
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int row = qd * 4 + rrow;
-        const uint4 v = *(const uint4*)(ep + row * 256 + ((rchunk ^ row) << 4));
+      for (int qd = 0; qd < 2; ++qd) {
+        const int row = qd * 8 + rrow;
+        const uint4 v = *(const uint4*)(ep + row * 128 + ((rchunk ^ (row & 7)) << 4));
         const int m = wm * 128 + i * 16 + row;
-        const int n = wn * 128 + rchunk * 8;
+        const int n = wn * 64 + rchunk * 8;
         const uint32_t off = (n < cur.cols) ? (uint32_t)(m * N + cur.n0 + n) * 2u : 0x80000000u;
         store16(rc, off, u32x4_t{v.x, v.y, v.z, v.w});
       }
-      // one 16-row block at a time: keeps the epilogue from pulling every accumulator into VGPRs
       __builtin_amdgcn_sched_barrier(0);
     }
     if (!more) break;
@@ -340,8 +340,8 @@ int gemm_big_grid(int max_rows, int E, int N) {
 
 hipError_t launch_gemm_big(const GemmParams& p, bool silu, hipStream_t s) {
   const int grid = gemm_big_grid(p.max_rows, p.E, p.N);
-  if (silu) gemm_big_kernel<true><<<grid, 256, 0, s>>>(p);
-  else gemm_big_kernel<false><<<grid, 256, 0, s>>>(p);
+  if (silu) gemm_big_kernel<true><<<grid, 512, 0, s>>>(p);
+  else gemm_big_kernel<false><<<grid, 512, 0, s>>>(p);
   return hipGetLastError();
 }
 

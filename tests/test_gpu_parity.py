@@ -35,6 +35,12 @@ REDUCED = {
     "not_renormalised": derived(BASE, name="not_renormalised", T=300, d_model=128, d_ffn=128, renormalize=False),
     "small_t_streaming_reduced": derived(WORKLOADS["small_t_streaming"], name="small_t_streaming_reduced",
                                          d_model=512, d_ffn=1024),
+    # weight-streaming GEMM with experts longer than one 64-row chunk (router bias skews the load)
+    # and a partial last block of output features (N = 200 and 320 are not multiples of 64)
+    "stream_skew_ntail": derived(BASE, name="stream_skew_ntail", T=256, d_model=256, d_ffn=200, router_bias=True),
+    "stream_skew": derived(BASE, name="stream_skew", T=256, d_model=192, d_ffn=320, router_bias=True),
+    # 256 x 256 GEMM with a single partial n-tile (N = 64) and a one-stage reduction (K = 64)
+    "big_ntail_k64": derived(BASE, name="big_ntail_k64", T=2048, d_model=128, d_ffn=64, num_experts=2, top_k=1),
 }
 
 
