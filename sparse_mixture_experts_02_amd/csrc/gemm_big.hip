@@ -102,6 +102,32 @@ __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)
 struct Tile {
   int e, row0, rows, n0, cols;
 };
+
+// fp32 partial sums of one 256 x 256 tile in the accumulator layout: [wave 8][16 x 16 block
+// i * 4 + j 32][lane 64] x 16 bytes
+constexpr uint32_t PART_BYTES = BIG_BM * BIG_BN * 4;
+
+// Split of the last, partial round of tiles (when there is more than one round): the R tiles
+// left over after whole rounds of G workgroups are each cut into s K-ranges (s the largest power
+// of two with s R <= G, at most 8), so that s R workgroups share the last round instead of R. The
+// parts' fp32 sums cost a write and a read of 256 KiB each and a second kernel; measured on the
+// expert-FFN shapes this repays itself for reductions of at least 64 stages (K >= 4096) and not
+// for 32, so shorter reductions are not split. Returns s (1: no split).
+__device__ __forceinline__ int tail_parts(int total, int G, int nk) {
+  const int R = total % G;
+  if (total <= G || R == 0 || nk < 64) return 1;
+  int s = 1;
+  while (s < 8 && 2 * s * R <= G) s *= 2;
+  return s;
+}
+
+// One 16-byte store of fp32 partial sums straight from the accumulator registers; the block's
+// offset goes in the scalar offset. Includes the wait states a store of more than 64 bits needs
+// before its data registers may be overwritten (the compiler does not see inside the asm).
+__device__ __forceinline__ void store_part(i32x4_t rsrc, uint32_t voff, uint32_t soff, const f32x4_t& v) {
+  asm volatile("buffer_store_dwordx4 %0, %1, %2, %3 offen\n\ts_nop 1" ::"a"(v), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory");
+}
 }  // namespace
 
 template <bool SILU>
@@ -116,10 +142,12 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   // Segment bounds, clamped into [0, max_rows] and made non-decreasing so that no offsets value
   // can send a tile outside the buffers. Kept in LDS: tiles are decoded between the kernel's own
   // counted memory operations, where a global load (and the wait for it) would not belong.
+  if (tid <= E) seg[tid] = p.offsets[tid];   // all loads in flight at once
+  __syncthreads();
   if (tid == 0) {
     int prev = 0;
     for (int e = 0; e <= E; ++e) {
-      const int o = p.offsets[e];
+      const int o = seg[e];
       prev = o < prev ? prev : (o > p.max_rows ? p.max_rows : o);
       seg[e] = prev;
     }
@@ -129,14 +157,24 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   for (int e = 0; e < E; ++e) MT += (seg[e + 1] - seg[e] + BIG_BM - 1) / BIG_BM;
   const int NT = (N + BIG_BN - 1) / BIG_BN;
   const int total = MT * NT;
-  // This XCD's contiguous range of tile ids, walked by its workgroups with a stride of their count.
+  const int rowbytes = p.K * 2;
+  const int nk = rowbytes / ROWB;
+  // Whole tiles: each XCD takes a contiguous range of tile ids, walked by its workgroups with a
+  // stride of their count. With a split tail (partial-sum workspace given, G == 256) the whole
+  // tiles are the first `full` (a multiple of G, so every workgroup gets the same number), and
+  // then workgroup v (XCD-major: the parts of one tile share an XCD) computes part v % s of tail
+  // tile v / s into partial slot v; a second kernel adds the parts and stores the tile.
   const int G = gridDim.x, xcd = blockIdx.x & 7;
-  const int q = total >> 3, rem = total & 7;
+  const int sparts = (p.sk_part != nullptr && G == MAX_WGS) ? tail_parts(total, G, nk) : 1;
+  const int full = sparts > 1 ? total - total % G : total;
+  const int q = full >> 3, rem = full & 7;
   const int cnt = (xcd < rem) ? q + 1 : q;
   const int start = (xcd < rem) ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q;
   const int step = (G - xcd + 7) >> 3;
   int local = blockIdx.x >> 3;
-  if (local >= cnt) return;
+  const int vsplit = xcd * (G >> 3) + local;
+  const bool has_split = sparts > 1 && vsplit < (total - full) * sparts;
+  if (local >= cnt && !has_split) return;
 
   auto decode = [&](int id) {
     const int group = id / (GROUP_M * NT);
@@ -161,8 +199,6 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     return t;
   };
 
-  const int rowbytes = p.K * 2;
-  const int nk = rowbytes / ROWB;
   const uint8_t* __restrict__ A = (const uint8_t*)p.A;
   const uint8_t* __restrict__ B = (const uint8_t*)p.B;
   uint16_t* __restrict__ C = (uint16_t*)p.C;
@@ -181,12 +217,13 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     voff[i] = (uint32_t)r * (uint32_t)rowbytes + chunk * 16;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  // Requests stage kt (clamped to the last one: a harmless reload) of tile t into buffer kt & 1.
-  auto issue = [&](const Tile& t, int kt) {
-    const int st = min(kt, nk - 1);
+  // Requests stage kt of a run of stages [k0, k1) of tile t (clamped to its last one: a harmless
+  // reload) into buffer (kt - k0) & 1.
+  auto issue = [&](const Tile& t, int kt, int k0 = 0, int k1 = 0x7fffffff) {
+    const int st = min(kt, min(k1, nk) - 1);
     const i32x4_t ra = make_rsrc(A + (size_t)t.row0 * rowbytes + st * ROWB, (uint32_t)t.rows * rowbytes);
     const i32x4_t rb = make_rsrc(B + ((size_t)t.e * N + t.n0) * rowbytes + st * ROWB, (uint32_t)t.cols * rowbytes);
-    const uint32_t sa = lds0 + (kt & 1) * STAGE_BYTES + w * 32 * ROWB;
+    const uint32_t sa = lds0 + ((kt - k0) & 1) * STAGE_BYTES + w * 32 * ROWB;
     const uint32_t sb = sa + TILE_BYTES;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -208,6 +245,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     wb[buf][j] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(sb + lds_off(wn * 64 + j * 16 + fr, ks * 4 + fc)));
   };
 
+  if (local < cnt) {
   Tile cur = decode(start + local);
   issue(cur, 0);
   issue(cur, 1);
@@ -331,7 +369,147 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     local = nlocal;
   }
   wait_vm_all();
+  }
+
+  if (has_split) {
+    // part `part` of tail tile `tile`: stages [k0, k1), sums to partial slot vsplit
+    const int part = vsplit % sparts;
+    const Tile t = decode(full + vsplit / sparts);
+    const int k0 = part * nk / sparts, k1 = (part + 1) * nk / sparts;
+    __syncthreads();   // the whole-tile loop may still be reading the LDS buffers
+    issue(t, k0, k0, k1);
+    issue(t, k0 + 1, k0, k1);
+    wait_vm_all();
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) frag_x(0, 0, 0, i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) frag_w(0, 0, 0, j);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < k1 - k0; ++s) {
+      if (s >= 1 && k0 + s + 1 < k1) issue(t, k0 + s + 1, k0, k1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[0][j], xa[0][i]);
+        if (i < 4) frag_w(1, s, 1, i);
+        frag_x(1, s, 1, i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm_all();
+      __syncthreads();
+#pragma unroll
+      for (int i = 4; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
+        frag_x(0, s + 1, 0, 2 * (i - 4));
+        frag_x(0, s + 1, 0, 2 * (i - 4) + 1);
+        frag_w(0, s + 1, 0, i - 4);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]), "+a"(acc[7][3]),
+                   "+a"(acc[6][0]), "+a"(acc[6][1]), "+a"(acc[6][2]), "+a"(acc[6][3])
+                 :
+                 : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    const i32x4_t rp = make_rsrc((uint8_t*)p.sk_part + (size_t)vsplit * PART_BYTES, PART_BYTES);
+    const uint32_t poff = (uint32_t)((w * 32 * 64 + lane) * 16);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) store_part(rp, poff, (i * 4 + j) * 64 * 16, acc[i][j]);
+    wait_vm_all();
+  }
 }
+
+// Adds the s partial sums of each split tail tile (in part order), applies the activation and
+// stores the tile. Item (r, w8, h): tail tile r, a quarter h of the 2048 16-byte chunks of wave
+// w8 of the GEMM's tile layout (each of 4 consecutive features of one row); the grid walks the
+// items.
+template <bool SILU>
+__global__ __launch_bounds__(256) void gemm_tail_kernel(GemmParams p, int G) {
+  __shared__ int seg[MOE_MAX_EXPERTS_DEV + 1];
+  const int E = p.E, N = p.N, tid = threadIdx.x;
+  if (tid <= E) seg[tid] = p.offsets[tid];   // all loads in flight at once
+  __syncthreads();
+  if (tid == 0) {
+    int prev = 0;
+    for (int e = 0; e <= E; ++e) {
+      const int o = seg[e];
+      prev = o < prev ? prev : (o > p.max_rows ? p.max_rows : o);
+      seg[e] = prev;
+    }
+  }
+  __syncthreads();
+  int MT = 0;
+  for (int e = 0; e < E; ++e) MT += (seg[e + 1] - seg[e] + BIG_BM - 1) / BIG_BM;
+  const int NT = (N + BIG_BN - 1) / BIG_BN;
+  const int total = MT * NT, nk = p.K / 64;
+  const int sparts = tail_parts(total, G, nk);
+  if (sparts < 2) return;
+  const int full = total - total % G;
+  for (int item = blockIdx.x; item < (total - full) * 32; item += gridDim.x) {
+  const int r = item >> 5, w8 = (item >> 2) & 7, h = item & 3;
+  // tile decode, as in the GEMM
+  const int id = full + r;
+  const int group = id / (GROUP_M * NT);
+  const int first_m = group * GROUP_M;
+  const int gm = min(GROUP_M, MT - first_m);
+  const int in_group = id - group * GROUP_M * NT;
+  const int mt = first_m + in_group % gm;
+  const int n0 = (in_group / gm) * BIG_BN, cols = min(N - n0, BIG_BN);
+  int row0 = 0, rows = 0, tstart = 0;
+  for (int ee = 0; ee < E; ++ee) {
+    const int n = (seg[ee + 1] - seg[ee] + BIG_BM - 1) / BIG_BM;
+    if (mt < tstart + n) {
+      row0 = seg[ee] + (mt - tstart) * BIG_BM;
+      rows = min(seg[ee + 1] - row0, BIG_BM);
+      break;
+    }
+    tstart += n;
+  }
+  const float4* __restrict__ part = (const float4*)p.sk_part;
+  uint16_t* __restrict__ C = (uint16_t*)p.C;
+  const int wm = w8 >> 2, wn = w8 & 3;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int chunk = h * 512 + c * 256 + tid;           // within the wave's 2048 chunks
+    const int blk = chunk >> 6, lane = chunk & 63;
+    const int m = wm * 128 + (blk >> 2) * 16 + (lane & 15);
+    const int n = wn * 64 + (blk & 3) * 16 + 4 * (lane >> 4);
+    const size_t o = (size_t)w8 * 2048 + chunk;          // 16-byte units within a slot
+    float4 s = part[(size_t)(r * sparts) * (PART_BYTES / 16) + o];
+    for (int j = 1; j < sparts; ++j) {
+      const float4 t = part[(size_t)(r * sparts + j) * (PART_BYTES / 16) + o];
+      s.x += t.x;
+      s.y += t.y;
+      s.z += t.z;
+      s.w += t.w;
+    }
+    if (m >= rows || n >= cols) continue;
+    float v[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = SILU ? silu_fast(v[u]) : v[u];
+    uint2 out;
+    out.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+    out.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+    *(uint2*)(C + (size_t)(row0 + m) * N + n0 + n) = out;
+  }
+  }
+}
+
+size_t gemm_big_part_bytes() { return (size_t)MAX_WGS * PART_BYTES; }
 
 int gemm_big_grid(int max_rows, int E, int N) {
   const long tiles = (long)((max_rows + BIG_BM - 1) / BIG_BM + E) * ((N + BIG_BN - 1) / BIG_BN);
@@ -342,6 +520,11 @@ hipError_t launch_gemm_big(const GemmParams& p, bool silu, hipStream_t s) {
   const int grid = gemm_big_grid(p.max_rows, p.E, p.N);
   if (silu) gemm_big_kernel<true><<<grid, 512, 0, s>>>(p);
   else gemm_big_kernel<false><<<grid, 512, 0, s>>>(p);
+  if (p.sk_part && grid == MAX_WGS && p.K / 64 >= 64) {   // tail_parts splits nothing below 64 stages
+    // the kernel works out how many tail tiles there are (none: it returns at once)
+    if (silu) gemm_tail_kernel<true><<<4 * MAX_WGS, 256, 0, s>>>(p, grid);
+    else gemm_tail_kernel<false><<<4 * MAX_WGS, 256, 0, s>>>(p, grid);
+  }
   return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@ struct Layout {
   size_t wsplit, psum, blk_hist, blk_base, rank_local, probsum;
   size_t logits, ids, weights, counts_pre, counts, offsets, perm, row_of, dropped, ndrop;
   size_t xp, h, y;
+  size_t sk_part;   // partial sums of the 256 x 256 grouped GEMM's split tail (empty if unused)
   size_t total;
 };
 
@@ -52,6 +53,10 @@ Layout layout(const moe_config_t& c) {
   L.xp = take(TK * d * a);
   L.h = take(TK * f * a);
   L.y = take(TK * d * a);
+  const bool bf16 = c.act_dtype == MOE_BF16;
+  const bool big = gemm_uses_big(bf16, c.d_model, c.T * c.top_k, c.num_experts) ||
+                   gemm_uses_big(bf16, c.d_ffn, c.T * c.top_k, c.num_experts);
+  L.sk_part = take(big ? gemm_big_part_bytes() : 0);
   L.total = off;
   return L;
 }
@@ -166,8 +171,9 @@ moe_status_t run_gather(const moe_config_t& c, const int32_t* ids, const void* x
 }
 
 moe_status_t run_gemm(const moe_config_t& c, const void* a, const void* b, void* out, const int32_t* offsets,
-                      int n, int kdim, bool silu, hipStream_t s) {
+                      int n, int kdim, bool silu, void* ws, hipStream_t s) {
   GemmParams p{};
+  if (gemm_uses_big(c.act_dtype == MOE_BF16, kdim, c.T * c.top_k, c.num_experts)) p.sk_part = at(ws, layout(c).sk_part);
   p.E = c.num_experts;
   p.N = n;
   p.K = kdim;
@@ -291,8 +297,8 @@ moe_status_t moe_expert_ffn(const moe_config_t* cfg, const void* xp, const int32
   if (!aligned16(xp) || !aligned16(w1) || !aligned16(w2) || !aligned16(h) || !aligned16(y))
     return MOE_ERR_INVALID_ARGUMENT;
   MOE_TRY(check_ws(cfg, ws, ws_bytes));
-  MOE_TRY(run_gemm(*cfg, xp, w1, h, offsets, cfg->d_ffn, cfg->d_model, true, stream));
-  return run_gemm(*cfg, h, w2, y, offsets, cfg->d_model, cfg->d_ffn, false, stream);
+  MOE_TRY(run_gemm(*cfg, xp, w1, h, offsets, cfg->d_ffn, cfg->d_model, true, ws, stream));
+  return run_gemm(*cfg, h, w2, y, offsets, cfg->d_model, cfg->d_ffn, false, ws, stream);
 }
 
 moe_status_t moe_combine(const moe_config_t* cfg, const void* y, const int32_t* row_of, const float* weights,
@@ -364,9 +370,9 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
   MOE_TRY(mark());
   MOE_TRY(run_gather(c, ids, x, offsets, perm, row_of, dropped, xp, ws, stream));
   MOE_TRY(mark());
-  MOE_TRY(run_gemm(c, xp, w1, h, offsets, c.d_ffn, c.d_model, true, stream));
+  MOE_TRY(run_gemm(c, xp, w1, h, offsets, c.d_ffn, c.d_model, true, ws, stream));
   MOE_TRY(mark());
-  MOE_TRY(run_gemm(c, h, w2, y, offsets, c.d_model, c.d_ffn, false, stream));
+  MOE_TRY(run_gemm(c, h, w2, y, offsets, c.d_model, c.d_ffn, false, ws, stream));
   MOE_TRY(mark());
   MOE_TRY(run_combine(c, y, row_of, weights, out, stream));
   MOE_TRY(mark());

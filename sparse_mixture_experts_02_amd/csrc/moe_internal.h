@@ -96,6 +96,9 @@ struct GemmParams {
   const void* B;            // [E, N, K] weights
   void* C;                  // [rows, N] act
   const int32_t* offsets;   // [E+1]
+  // Partial-sum workspace of the 256 x 256 kernel's split tail (gemm_big_part_bytes), or null:
+  // whole tiles only.
+  void* sk_part;
 };
 
 struct CombineParams {
@@ -142,6 +145,9 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 int gemm_max_mtiles(int max_rows, int E);
 hipError_t launch_gemm(const GemmParams& p, bool bf16, bool silu, hipStream_t s);
 int gemm_big_grid(int max_rows, int E, int N);
+size_t gemm_big_part_bytes();
+// whether launch_gemm takes the 256 x 256 kernel for these operands
+bool gemm_uses_big(bool bf16, int K, int max_rows, int E);
 hipError_t launch_gemm_big(const GemmParams& p, bool silu, hipStream_t s);
 int gemm_stream_grid(int E, int N);
 hipError_t launch_gemm_stream(const GemmParams& p, bool silu, hipStream_t s);

@@ -41,6 +41,9 @@ REDUCED = {
     "stream_skew": derived(BASE, name="stream_skew", T=256, d_model=192, d_ffn=320, router_bias=True),
     # 256 x 256 GEMM with a single partial n-tile (N = 64) and a one-stage reduction (K = 64)
     "big_ntail_k64": derived(BASE, name="big_ntail_k64", T=2048, d_model=128, d_ffn=64, num_experts=2, top_k=1),
+    # 256 x 256 GEMM2 with K = 4096 and 266 tiles: the 10 tiles past the first round of 256 are
+    # split into K-parts summed by the tail kernel
+    "big_split_tail": derived(BASE, name="big_split_tail", T=34000, d_model=64, d_ffn=4096, num_experts=2),
 }
 
 
