@@ -57,10 +57,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     }
     if constexpr (BF16) {
       uint4 o;
-      o.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
-      o.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
-      o.z = f32_to_bf16_bits(acc[4]) | (f32_to_bf16_bits(acc[5]) << 16);
-      o.w = f32_to_bf16_bits(acc[6]) | (f32_to_bf16_bits(acc[7]) << 16);
+      o.x = pack_bf16x2(acc[0], acc[1]);
+      o.y = pack_bf16x2(acc[2], acc[3]);
+      o.z = pack_bf16x2(acc[4], acc[5]);
+      o.w = pack_bf16x2(acc[6], acc[7]);
       *(uint4*)((uint16_t*)p.out + (size_t)t * d + c) = o;
     } else {
       *(float4*)((float*)p.out + (size_t)t * d + c) = make_float4(acc[0], acc[1], acc[2], acc[3]);

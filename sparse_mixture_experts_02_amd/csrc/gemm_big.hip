@@ -344,9 +344,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
             b0 = silu_fast(b0);
             b1 = silu_fast(b1);
           }
-          const auto r = __builtin_amdgcn_permlane16_swap(f32_to_bf16_bits(a0) | (f32_to_bf16_bits(a1) << 16),
-                                                          f32_to_bf16_bits(b0) | (f32_to_bf16_bits(b1) << 16),
-                                                          false, false);
+          const auto r = __builtin_amdgcn_permlane16_swap(pack_bf16x2(a0, a1), pack_bf16x2(b0, b1), false, false);
           P[h] = r[0];
           Q[h] = r[1];
         }
@@ -502,8 +500,8 @@ __global__ __launch_bounds__(256) void gemm_tail_kernel(GemmParams p, int G) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) v[u] = SILU ? silu_fast(v[u]) : v[u];
     uint2 out;
-    out.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-    out.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+    out.x = pack_bf16x2(v[0], v[1]);
+    out.y = pack_bf16x2(v[2], v[3]);
     *(uint2*)(C + (size_t)(row0 + m) * N + n0 + n) = out;
   }
   }

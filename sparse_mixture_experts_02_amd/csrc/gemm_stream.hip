@@ -171,8 +171,8 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(GemmParams p) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) v[u] = SILU ? sb_silu(acc[i][b][u]) : acc[i][b][u];
         uint2 o;
-        o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-        o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+        o.x = pack_bf16x2(v[0], v[1]);
+        o.y = pack_bf16x2(v[2], v[3]);
         *(uint2*)(C + (size_t)(m0 + r) * N + n0 + n) = o;
       }
     }
