@@ -69,9 +69,68 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   }
 }
 
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// bf16, top-k <= 2, d a multiple of 512 and at most 4096: one wave per token as above, but every
+// load of the token (up to 8 column steps x 2 rows, 16 bytes per lane each) is issued before the
+// first use, so a wave keeps all of its row reads in flight at once. Y rows are read once, with the
+// non-temporal hint (measured: 3-5% faster; the same hint on the output stores was slower). Same
+// arithmetic and order as the general kernel (fp32 FMA in slot order, one rounding).
+__global__ __launch_bounds__(256) void combine_k2_kernel(CombineParams p) {
+  constexpr int MAXU = 8;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= p.T) return;
+  const int k = p.k, d = p.d;
+  int my_row = -1;
+  float my_w = 0.0f;
+  if (lane < k) {
+    my_row = p.row_of[(size_t)t * k + lane];
+    my_w = p.weights[(size_t)t * k + lane];
+    if (my_row >= p.max_rows) my_row = -1;
+  }
+  const int r0 = __shfl(my_row, 0), r1 = k > 1 ? __shfl(my_row, 1) : -1;
+  const float w0 = __shfl(my_w, 0), w1 = k > 1 ? __shfl(my_w, 1) : 0.0f;
+  const int nu = d >> 9;   // column steps of 512
+  const u32x4_t* y0 = (const u32x4_t*)((const uint16_t*)p.y + (size_t)(r0 < 0 ? 0 : r0) * d) + lane;
+  const u32x4_t* y1 = (const u32x4_t*)((const uint16_t*)p.y + (size_t)(r1 < 0 ? 0 : r1) * d) + lane;
+  u32x4_t a[MAXU], b[MAXU];
+#pragma unroll
+  for (int u = 0; u < MAXU; ++u) {
+    if (u < nu) {
+      a[u] = r0 >= 0 ? __builtin_nontemporal_load(y0 + u * 64) : u32x4_t{0u, 0u, 0u, 0u};
+      b[u] = r1 >= 0 ? __builtin_nontemporal_load(y1 + u * 64) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+  u32x4_t* out = (u32x4_t*)((uint16_t*)p.out + (size_t)t * d) + lane;
+#pragma unroll
+  for (int u = 0; u < MAXU; ++u) {
+    if (u < nu) {
+      float acc[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = 0.0f;
+        acc[2 * q + 1] = 0.0f;
+        if (r0 >= 0) {
+          acc[2 * q] = fmaf(w0, bf16_bits_to_f32(a[u][q] & 0xFFFFu), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(w0, bf16_bits_to_f32(a[u][q] >> 16), acc[2 * q + 1]);
+        }
+        if (r1 >= 0) {
+          acc[2 * q] = fmaf(w1, bf16_bits_to_f32(b[u][q] & 0xFFFFu), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(w1, bf16_bits_to_f32(b[u][q] >> 16), acc[2 * q + 1]);
+        }
+      }
+      const u32x4_t o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                         pack_bf16x2(acc[6], acc[7])};
+      out[u * 64] = o;
+    }
+  }
+}
+
 hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s) {
   const int grid = (p.T + 3) / 4;
-  if (bf16) combine_kernel<true><<<grid, 256, 0, s>>>(p);
+  if (bf16 && p.k <= 2 && p.d % 512 == 0 && p.d <= 4096) combine_k2_kernel<<<grid, 256, 0, s>>>(p);
+  else if (bf16) combine_kernel<true><<<grid, 256, 0, s>>>(p);
   else combine_kernel<false><<<grid, 256, 0, s>>>(p);
   return hipGetLastError();
 }

@@ -17,9 +17,10 @@
 //
 // Two kernels compute the logits:
 //  * route_fast_kernel (bf16, E <= 32): a 4-wave workgroup routes 64 tokens. x rows and the
-//    split weight pass through a 4-stage LDS ring of 128-column chunks, filled with direct
-//    global -> LDS loads issued 3 chunks ahead, so each weight chunk is read once per 64 tokens
-//    and x streams with several chunks in flight.
+//    split weight pass through an LDS ring of 128-column chunks (5 stages for E <= 16, 4 for
+//    E <= 32), filled with direct global -> LDS loads issued as many chunks ahead as the ring
+//    holds, so each weight chunk is read once per 64 tokens and x streams with 48-64 KiB in flight
+//    per workgroup.
 //  * route_kernel (fp32 activations, E > 32, or given logits): one wave per 32 tokens, operands
 //    straight from global memory.
 #include "moe_internal.h"
@@ -31,7 +32,10 @@ namespace {
 constexpr int FR_TOK = 64;           // tokens per workgroup tile (16 per wave)
 constexpr int FR_COLS = 128;         // columns of x and of the weight per stage
 constexpr int FR_ROWB = 256;         // staged bytes per row per stage
-constexpr int FR_NSTAGE = 4;
+// LDS ring depth: as many stages as fit in 160 KiB (5 x 28 KiB for one 16-expert tile, 4 x 40
+// KiB for two), so that NSTAGE - 1 chunks of x are in flight per workgroup
+template <int ET>
+constexpr int fr_nstage() { return ET == 1 ? 5 : 4; }
 constexpr int FR_MAX_BLOCKS = 1024;
 }  // namespace
 
@@ -300,7 +304,10 @@ __global__ __launch_bounds__(256, 1) void route_fast_kernel(RouteParams p) {
   constexpr int XI = 4;                       // x load instructions per wave per stage (16 rows)
   constexpr int WI = 3 * ET;                  // weight load instructions per wave per stage
   constexpr int PER = XI + WI;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[FR_NSTAGE * SB];
+  constexpr int NS = fr_nstage<ET>();
+  static_assert(NS * SB <= 160 * 1024, "LDS ring too large");
+  static_assert((NS - 2) * PER <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * SB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -339,7 +346,7 @@ __global__ __launch_bounds__(256, 1) void route_fast_kernel(RouteParams p) {
     }
     auto issue = [&](int kt) {
       const int st = min(kt, nk - 1);   // past the end: reload the last chunk (uniform counts)
-      const uint32_t base = lds0 + (kt % FR_NSTAGE) * SB;
+      const uint32_t base = lds0 + (kt % NS) * SB;
 #pragma unroll
       for (int i = 0; i < XI; ++i) {
         int c = st * FR_COLS + xch[i] * 8;
@@ -355,15 +362,14 @@ __global__ __launch_bounds__(256, 1) void route_fast_kernel(RouteParams p) {
 #pragma unroll
     for (int et = 0; et < ET; ++et) acc[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    issue(0);
-    issue(1);
-    issue(2);
-    wait_vmcnt<2 * PER>();
+#pragma unroll
+    for (int kt = 0; kt < NS - 1; ++kt) issue(kt);
+    wait_vmcnt<(NS - 2) * PER>();
     __syncthreads();
     const int arow = w * 16 + (lane & 15);
     for (int s = 0; s < nk; ++s) {
-      issue(s + 3);
-      const uint8_t* sx = smem + (s % FR_NSTAGE) * SB;
+      issue(s + NS - 1);
+      const uint8_t* sx = smem + (s % NS) * SB;
       const uint8_t* sw = sx + XB;
 #pragma unroll
       for (int ks = 0; ks < FR_COLS / 32; ++ks) {
@@ -379,7 +385,7 @@ __global__ __launch_bounds__(256, 1) void route_fast_kernel(RouteParams p) {
           }
         }
       }
-      wait_vmcnt<2 * PER>();   // chunk s + 1 complete (s + 2, s + 3 may be in flight)
+      wait_vmcnt<(NS - 2) * PER>();   // chunk s + 1 complete (the NS - 2 after it may be in flight)
       __syncthreads();
     }
     wait_vmcnt<0>();           // the trailing reloads land before the ring is reused

@@ -44,6 +44,10 @@ REDUCED = {
     # 256 x 256 GEMM2 with K = 4096 and 266 tiles: the 10 tiles past the first round of 256 are
     # split into K-parts summed by the tail kernel
     "big_split_tail": derived(BASE, name="big_split_tail", T=34000, d_model=64, d_ffn=4096, num_experts=2),
+    # combine fast path (bf16, top-k <= 2, d a multiple of 512 up to 4096): top-1, and the widest row
+    "combine_top1_d512": derived(BASE, name="combine_top1_d512", T=300, d_model=512, d_ffn=256, num_experts=4,
+                                 top_k=1),
+    "combine_d4096": derived(BASE, name="combine_d4096", T=96, d_model=4096, d_ffn=128, num_experts=4),
 }
 
 
