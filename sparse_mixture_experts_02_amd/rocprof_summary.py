@@ -2,12 +2,17 @@
 
     python -m sparse_mixture_experts_02_amd.rocprof_summary stats <dir>
     python -m sparse_mixture_experts_02_amd.rocprof_summary pmc <dir> [--calib-kernel NAME --calib-bytes N]
+    python -m sparse_mixture_experts_02_amd.rocprof_summary mfma <dir>
 
 `stats` reads the *_kernel_stats.csv that `rocprofv3 --kernel-trace --stats --output-format csv`
 writes; `pmc` reads the *_counter_collection.csv of a `rocprofv3 --pmc ... --output-format csv`
 run and prints each counter's mean per dispatch for every kernel. With a calibration kernel of
 known traffic (an elementwise copy that reads and writes N bytes), FETCH_SIZE and WRITE_SIZE are
 also given as a scale factor (known bytes / counted bytes) and as scaled bytes per dispatch.
+`mfma` reads a `--pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES` run and prints, per kernel, the
+mean dispatch duration, the effective clock (GRBM_GUI_ACTIVE is summed over the 8 XCDs) and the
+fraction of SIMD cycles the matrix cores were busy (SQ_VALU_MFMA_BUSY_CYCLES over
+GRBM_GUI_ACTIVE / 8 x 1024 SIMDs).
 """
 from __future__ import annotations
 
@@ -44,13 +49,31 @@ def counters(d: str) -> dict:
     return out
 
 
+def dispatches(d: str) -> dict:
+    """{kernel: [{counter: value, ..., "dur_ns": duration} per dispatch]}"""
+    per = collections.defaultdict(dict)
+    for path in _find(d, "counter_collection.csv"):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                per[key][r["Counter_Name"]] = per[key].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                per[key]["dur_ns"] = float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = collections.defaultdict(list)
+    for (k, _), v in per.items():
+        out[k].append(v)
+    return out
+
+
+XCDS, SIMDS = 8, 1024
+
+
 def short(name: str, n: int = 70) -> str:
     return name if len(name) <= n else name[: n - 3] + "..."
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("mode", choices=["stats", "pmc"])
+    ap.add_argument("mode", choices=["stats", "pmc", "mfma"])
     ap.add_argument("dir")
     ap.add_argument("--calib-kernel", default="AUnaryFunctor",
                     help="substring naming the calibration kernel (torch.mul by a scalar)")
@@ -62,6 +85,20 @@ def main(argv=None):
         for r in sorted(rows, key=lambda r: -r["pct"]):
             print(f"{short(r['name'], 72):72s} {r['calls']:6d} {r['avg_us']:10.2f} {r['min_us']:10.2f} "
                   f"{r['max_us']:10.2f} {r['pct']:6.2f}")
+        return 0
+    if a.mode == "mfma":
+        print(f"{'kernel':72s} {'n':>4s} {'avg_us':>9s} {'clock_GHz':>9s} {'mfma_busy':>9s}")
+        for k, ds in sorted(dispatches(a.dir).items()):
+            ds = [x for x in ds if x.get("GRBM_GUI_ACTIVE", 0) > 0 and "SQ_VALU_MFMA_BUSY_CYCLES" in x]
+            if not ds:
+                continue
+            gui = sum(x["GRBM_GUI_ACTIVE"] for x in ds)
+            busy = sum(x["SQ_VALU_MFMA_BUSY_CYCLES"] for x in ds)
+            dur = sum(x["dur_ns"] for x in ds)
+            if busy <= 0:
+                continue
+            print(f"{short(k, 72):72s} {len(ds):4d} {dur / len(ds) / 1e3:9.2f} {gui / XCDS / dur:9.2f} "
+                  f"{busy / (gui / XCDS * SIMDS):9.3f}")
         return 0
     c = counters(a.dir)
     scale = {}
