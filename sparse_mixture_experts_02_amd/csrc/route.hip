@@ -1,5 +1,6 @@
 // Router kernels: logits = x W_r^T + b on MFMA, selection key, wavefront top-k, gate weights,
-// full softmax and per-wave probability sums for the aux loss -- one pass over x.
+// full softmax and partial probability sums (per workgroup or per wave) for the aux loss -- one pass
+// over x.
 //
 // [P2 §3.1] scores = W_router x, probs = softmax(scores / tau), top-k (k = 2); with Gumbel
 // noise the ranked value is (logits + g) / tau. [P4 §2.4] a linear router with softmax, the
@@ -392,7 +393,30 @@ __global__ __launch_bounds__(256, 1) void route_fast_kernel(RouteParams p) {
     __syncthreads();
     finish_tile<ET>(p, acc, t0 + w * 16, true, psum_acc);
   }
-  store_psum<ET>(p, psum_acc, blockIdx.x * 4 + w);
+  // One row of probability sums per workgroup: each wave folds its 4 row groups (as store_psum),
+  // the 4 waves' sums meet in LDS (the ring is no longer read: every wave is past the last
+  // barrier of the tile loop) and are added in wave order.
+  if (p.psum) {
+    double* wsum = (double*)smem;   // [4 waves][ET][16]
+#pragma unroll
+    for (int et = 0; et < ET; ++et) {
+      double v = psum_acc[et];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (lane < 16) wsum[(w * ET + et) * 16 + lane] = v;
+    }
+    __syncthreads();
+    if (w == 0 && lane < 16) {
+#pragma unroll
+      for (int et = 0; et < ET; ++et) {
+        const int e = et * 16 + lane;
+        const double v = ((wsum[(0 * ET + et) * 16 + lane] + wsum[(1 * ET + et) * 16 + lane]) +
+                          wsum[(2 * ET + et) * 16 + lane]) +
+                         wsum[(3 * ET + et) * 16 + lane];
+        if (e < p.E) p.psum[(size_t)blockIdx.x * p.E + e] = v;
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------ host side
@@ -414,11 +438,11 @@ static int generic_blocks(int T) {
 }
 
 int route_num_parts(int T, int E, bool bf16, bool logits_in) {
-  return use_fast(E, bf16, logits_in) ? 4 * fast_blocks(T) : generic_blocks(T);
+  return use_fast(E, bf16, logits_in) ? fast_blocks(T) : generic_blocks(T);
 }
 
 int route_max_parts(int T) {
-  const int a = 4 * fast_blocks(T), b = generic_blocks(T);
+  const int a = fast_blocks(T), b = generic_blocks(T);
   return a > b ? a : b;
 }
 
