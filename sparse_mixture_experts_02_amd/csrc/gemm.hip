@@ -155,11 +155,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 
 int gemm_max_mtiles(int max_rows, int E) { return (max_rows + GEMM_BM - 1) / GEMM_BM + E; }
 
-bool gemm_uses_big(bool bf16, int K, int max_rows, int E) { return bf16 && K % 64 == 0 && max_rows >= 256 * E; }
+// The 256 x 256 kernel prefetches two K stages ahead across its tiles, so it needs at least two
+// stages (K >= 128) per tile.
+bool gemm_uses_big(bool bf16, int K, int max_rows, int E) {
+  return bf16 && K % 64 == 0 && K >= 128 && max_rows >= 256 * E;
+}
 
 hipError_t launch_gemm(const GemmParams& p, bool bf16, bool silu, hipStream_t s) {
-  // bf16 with K a multiple of 64: on average at least 256 rows per expert, 256 x 256 tiles; at
-  // most 64, one pass over the expert weights
+  // bf16 with K a multiple of 64 (at least 128): on average at least 256 rows per expert, 256 x 256
+  // tiles; at most 64, one pass over the expert weights
   if (gemm_uses_big(bf16, p.K, p.max_rows, p.E)) return launch_gemm_big(p, silu, s);
   if (bf16 && p.K % 64 == 0 && p.max_rows <= 64 * p.E) return launch_gemm_stream(p, silu, s);
   dim3 grid(gemm_max_mtiles(p.max_rows, p.E), (p.N + GEMM_BN - 1) / GEMM_BN);

@@ -15,21 +15,26 @@
 //    other keeps the matrix core busy (two waves per SIMD measured ~9% faster than one wave
 //    owning a 128 x 128 quarter, although the LDS fragment reads grow by half).
 //  * K advances 64 elements (128 bytes of every row) per stage. Two LDS stages (2 x (A + B) x
-//    256 rows x 128 B = 128 KiB) are filled by direct buffer -> LDS 16-byte loads; stage s + 1 is
-//    requested when stage s starts. A stage is two k-steps of 32; operand fragments are read one
-//    k-step ahead, interleaved with the MFMAs, and the one barrier per stage sits in the middle of
-//    the second k-step.
+//    256 rows x 128 B = 128 KiB) are filled by direct buffer -> LDS 16-byte loads. A stage is two
+//    k-steps of 32; operand fragments are read one k-step ahead, interleaved with the MFMAs, and
+//    the one barrier per stage sits in the middle of the second k-step.
+//  * Stages are numbered across a workgroup's tiles, and the loads of stage g + 2 go into stage
+//    g's buffer as soon as the barrier in the middle of stage g has released it: the A rows spread
+//    over the rest of stage g, the B rows over the first k-step of stage g + 1. Issuing the direct
+//    loads in one burst at the top of a stage stalled the issuing waves (measured: the MFMAs were
+//    busy 55% of the time against 76% with the loads removed); spread out, and a stage earlier,
+//    they cost far less. Past a tile's last stages the loads fetch the next tile's first two
+//    stages, so the pipeline runs through the tile boundary and only the epilogue (SiLU in fp32,
+//    one rounding to bf16) pauses the matrix cores. This needs at least two stages per tile
+//    (K >= 128).
 //  * The loads address rows through buffer resources whose size is the tile's valid rows of A (or
 //    of B): rows past a segment's end or past N fall outside the resource and are not fetched.
 //    They only feed accumulators whose outputs are never stored.
-//  * Overlapped tile boundary: once the last stage of a tile has been read from LDS, the first two
-//    stages of the next tile are requested, and the epilogue (SiLU in fp32, one rounding to bf16)
-//    of the finished tile runs while they load.
 //  * Epilogue: the MFMA leaves 4 consecutive output features of one row per lane; it is turned
 //    into whole output rows through a small per-wave LDS area (see the epilogue) and stored with
 //    16-byte buffer stores, 8 rows x 128 contiguous bytes per instruction, through a buffer
 //    resource sized to the tile's valid rows (lanes past N get an out-of-range offset).
-// K must be a multiple of 64 and N of 8.
+// K must be a multiple of 64, at least 128, and N of 8.
 #include "moe_internal.h"
 
 namespace moe {
@@ -245,74 +250,22 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     wb[buf][j] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(sb + lds_off(wn * 64 + j * 16 + fr, ks * 4 + fc)));
   };
 
-  if (local < cnt) {
-  Tile cur = decode(start + local);
-  issue(cur, 0);
-  issue(cur, 1);
-  while (true) {
-    const int nlocal = local + step;
-    const bool more = nlocal < cnt;
-    const Tile nxt = more ? decode(start + nlocal) : cur;
-    // Stages 0 and 1 of `cur` are in flight (and the previous tile's epilogue stores).
-    wait_vm_all();
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 8; ++i) frag_x(0, 0, 0, i);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) frag_w(0, 0, 0, j);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // one direct load qq of a stage (0..3: A rows, 4..7: B rows of this wave) into buffer buf
+  auto ld = [&](i32x4_t ra, i32x4_t rb, int qq, int buf) {
+    const uint32_t sa = lds0 + buf * STAGE_BYTES + w * 32 * ROWB;
+    if (qq < 4) load_lds16(ra, voff[qq], sa + qq * 8 * ROWB);
+    else load_lds16(rb, voff[qq - 4], sa + TILE_BYTES + (qq - 4) * 8 * ROWB);
+  };
+  auto rs_a = [&](const Tile& t, int st) {
+    return make_rsrc(A + (size_t)t.row0 * rowbytes + st * ROWB, (uint32_t)t.rows * rowbytes);
+  };
+  auto rs_b = [&](const Tile& t, int st) {
+    return make_rsrc(B + ((size_t)t.e * N + t.n0) * rowbytes + st * ROWB, (uint32_t)t.cols * rowbytes);
+  };
 
-    for (int s = 0; s < nk; ++s) {
-      if (s >= 1 && s + 1 < nk) issue(cur, s + 1);
-      // k-step 0 of stage s from F0, reading k-step 1 of stage s into F1
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[0][j], xa[0][i]);
-        if (i < 4) frag_w(1, s, 1, i);
-        frag_x(1, s, 1, i);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // first half of k-step 1
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
-      __builtin_amdgcn_sched_barrier(0);
-      // stage s + 1 has landed everywhere and nobody reads stage s's buffer any more
-      wait_vm_all();
-      __syncthreads();
-      // second half of k-step 1, reading k-step 0 of stage s + 1 into F0 (after the last stage
-      // the reads return whatever the buffer holds; they are overwritten before any use)
-#pragma unroll
-      for (int i = 4; i < 8; ++i) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
-        frag_x(0, s + 1, 0, 2 * (i - 4));
-        frag_x(0, s + 1, 0, 2 * (i - 4) + 1);
-        frag_w(0, s + 1, 0, i - 4);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // Every wave is past the last barrier of this tile, so both LDS buffers are free: request the
-    // next tile's first two stages before storing this one (after the last tile: a reload of this
-    // one, drained before the workgroup ends).
-    issue(nxt, 0);
-    issue(nxt, 1);
-    // let the last MFMAs retire before their accumulators are read
-    // (the most recently written accumulators pass through the wait so that no read of them can
-    // be scheduled before it)
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]), "+a"(acc[7][3]),
-                   "+a"(acc[6][0]), "+a"(acc[6][1]), "+a"(acc[6][2]), "+a"(acc[6][3])
-                 :
-                 : "memory");
-    __builtin_amdgcn_sched_barrier(0);
+  // Epilogue of tile t from the accumulators (after the wait states that let the last MFMAs
+  // retire): SiLU, one rounding, and row-contiguous stores through a per-wave LDS area.
+  auto store_tile = [&](const Tile& t) {
     // per-lane epilogue offsets, recomputed for every tile rather than held across the main loop
     int lane_o = lane;
     asm volatile("" : "+v"(lane_o));
@@ -326,15 +279,15 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     // and a store instruction covers 8 rows x 128 contiguous bytes: whole lines, where the MFMA
     // layout would store 16 rows x 64 bytes (a third of the throughput per CU). The 8 chunks of an
     // LDS row are XOR-swizzled by the row.
-    const i32x4_t rc = make_rsrc(C + (size_t)cur.row0 * N, (uint32_t)cur.rows * N * 2);
+    const i32x4_t rc = make_rsrc(C + (size_t)t.row0 * N, (uint32_t)t.rows * N * 2);
     uint8_t* const ep = epi + w * EPI_BYTES;
     const int rrow = lane_o >> 3, rchunk = lane_o & 7;   // read-back: row within 8, chunk
-#pragma unroll
+  #pragma unroll
     for (int i = 0; i < 8; ++i) {
-#pragma unroll
+  #pragma unroll
       for (int jp = 0; jp < 2; ++jp) {
         uint32_t P[2], Q[2];
-#pragma unroll
+  #pragma unroll
         for (int h = 0; h < 2; ++h) {
           float a0 = acc[i][2 * jp][2 * h], a1 = acc[i][2 * jp][2 * h + 1];
           float b0 = acc[i][2 * jp + 1][2 * h], b1 = acc[i][2 * jp + 1][2 * h + 1];
@@ -351,20 +304,125 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
         const int chunk = jp * 4 + ((efc >> 1) | ((efc & 1) << 1));
         *(uint4*)(ep + efr * 128 + ((chunk ^ (efr & 7)) << 4)) = uint4{P[0], P[1], Q[0], Q[1]};
       }
-#pragma unroll
+  #pragma unroll
       for (int qd = 0; qd < 2; ++qd) {
         const int row = qd * 8 + rrow;
         const uint4 v = *(const uint4*)(ep + row * 128 + ((rchunk ^ (row & 7)) << 4));
         const int m = wm * 128 + i * 16 + row;
         const int n = wn * 64 + rchunk * 8;
-        const uint32_t off = (n < cur.cols) ? (uint32_t)(m * N + cur.n0 + n) * 2u : 0x80000000u;
+        const uint32_t off = (n < t.cols) ? (uint32_t)(m * N + t.n0 + n) * 2u : 0x80000000u;
         store16(rc, off, u32x4_t{v.x, v.y, v.z, v.w});
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  if (local < cnt) {
+  // Stages are numbered globally across this workgroup's tiles (stage s of a tile is g0 + s);
+  // stage g lives in LDS buffer g & 1. The loads of stage g + 2 go into stage g's buffer once the
+  // barrier in the middle of stage g has released it: the A rows right after that barrier, the B
+  // rows spread over the first k-step of stage g + 1, so that the loads neither arrive in one
+  // burst nor late. Past a tile's last stage they fetch the next tile's first stages.
+  Tile cur = decode(start + local);
+  int g0 = 0;
+  {
+    const i32x4_t ra0 = rs_a(cur, 0), rb0 = rs_b(cur, 0);
+#pragma unroll
+    for (int qq = 0; qq < 8; ++qq) ld(ra0, rb0, qq, 0);
+  }
+  const int s1 = min(1, nk - 1);
+  i32x4_t pra = rs_a(cur, s1), prb = rs_b(cur, s1);   // the B half is carried into stage 0
+  int pbuf = 1;
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) ld(pra, prb, qq, 1);
+  wait_vm_all();
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) frag_x(0, 0, 0, i);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) frag_w(0, 0, 0, j);
+  while (true) {
+    const int nlocal = local + step;
+    const bool more = nlocal < cnt;
+    const Tile nxt = more ? decode(start + nlocal) : cur;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int s = 0; s < nk; ++s) {
+      const int g = g0 + s;
+      // k-step 0 of stage s from F0, reading k-step 1 of stage s into F1; the B loads carried
+      // from the previous stage
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[0][j], xa[0][i]);
+        if (i & 1) ld(pra, prb, 4 + (i >> 1), pbuf);
+        if (i < 4) frag_w(1, g, 1, i);
+        frag_x(1, g, 1, i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // first half of k-step 1
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
+      __builtin_amdgcn_sched_barrier(0);
+      // stage s + 1 has landed everywhere and nobody reads stage s's buffer any more
+      wait_vm_all();
+      __syncthreads();
+      // stage g + 2: this tile's stage s + 2, else the next tile's first stages (nothing left:
+      // a resource of no records, so the loads fetch nothing)
+      const bool own = s + 2 < nk;
+      const Tile& lt = own ? cur : nxt;
+      const int lst = own ? s + 2 : min(s + 2 - nk, nk - 1);
+      i32x4_t ra = rs_a(lt, lst), rb = rs_b(lt, lst);
+      if (!own && !more) {
+        ra[2] = 0;
+        rb[2] = 0;
+      }
+      // second half of k-step 1, with the A loads of stage g + 2 and the reads of k-step 0 of
+      // stage g + 1 into F0
+#pragma unroll
+      for (int i = 4; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
+        ld(ra, rb, i - 4, g & 1);
+        if (!SILU || s + 1 < nk) {   // SiLU: after a tile's last stage, read once its epilogue is done
+          frag_x(0, g + 1, 0, 2 * (i - 4));
+          frag_x(0, g + 1, 0, 2 * (i - 4) + 1);
+          frag_w(0, g + 1, 0, i - 4);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      pra = ra;
+      prb = rb;
+      pbuf = g & 1;
+    }
+
+    // let the last MFMAs retire before their accumulators are read
+    // (the most recently written accumulators pass through the wait so that no read of them can
+    // be scheduled before it)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]), "+a"(acc[7][3]),
+                   "+a"(acc[6][0]), "+a"(acc[6][1]), "+a"(acc[6][2]), "+a"(acc[6][3])
+                 :
+                 : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    store_tile(cur);
     if (!more) break;
+    g0 += nk;
     cur = nxt;
     local = nlocal;
+    if constexpr (SILU) {
+      // k-step 0 of the new tile's stage 0 (landed before the last barrier of the previous tile)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) frag_x(0, g0, 0, i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) frag_w(0, g0, 0, j);
+    }
   }
   wait_vm_all();
   }
@@ -515,6 +573,7 @@ int gemm_big_grid(int max_rows, int E, int N) {
 }
 
 hipError_t launch_gemm_big(const GemmParams& p, bool silu, hipStream_t s) {
+  if (p.K < 128) return hipErrorInvalidValue;   // the pipeline needs two K stages per tile
   const int grid = gemm_big_grid(p.max_rows, p.E, p.N);
   if (silu) gemm_big_kernel<true><<<grid, 512, 0, s>>>(p);
   else gemm_big_kernel<false><<<grid, 512, 0, s>>>(p);
