@@ -320,9 +320,11 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   if (local < cnt) {
   // Stages are numbered globally across this workgroup's tiles (stage s of a tile is g0 + s);
   // stage g lives in LDS buffer g & 1. The loads of stage g + 2 go into stage g's buffer once the
-  // barrier in the middle of stage g has released it: the A rows right after that barrier, the B
-  // rows spread over the first k-step of stage g + 1, so that the loads neither arrive in one
-  // burst nor late. Past a tile's last stage they fetch the next tile's first stages.
+  // barrier in the middle of stage g has released it: half of them right after that barrier, the
+  // other half over the first k-step of stage g + 1, so that they neither arrive in one burst nor
+  // late. Which half goes first was measured: the B rows for the SiLU GEMM (its other half then
+  // at every other 16-row block), the A rows for the plain one (its B rows then over the first
+  // half of the k-step). Past a tile's last stage they fetch the next tile's first stages.
   Tile cur = decode(start + local);
   int g0 = 0;
   {
@@ -330,11 +332,11 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
 #pragma unroll
     for (int qq = 0; qq < 8; ++qq) ld(ra0, rb0, qq, 0);
   }
-  const int s1 = min(1, nk - 1);
-  i32x4_t pra = rs_a(cur, s1), prb = rs_b(cur, s1);   // the B half is carried into stage 0
+  // stage 1: the half that follows a mid-stage barrier now, the other half carried into stage 0
+  i32x4_t pra = rs_a(cur, 1), prb = rs_b(cur, 1);
   int pbuf = 1;
 #pragma unroll
-  for (int qq = 0; qq < 4; ++qq) ld(pra, prb, qq, 1);
+  for (int qq = 0; qq < 4; ++qq) ld(pra, prb, SILU ? 4 + qq : qq, 1);
   wait_vm_all();
   __syncthreads();
 #pragma unroll
@@ -352,13 +354,13 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
 
     for (int s = 0; s < nk; ++s) {
       const int g = g0 + s;
-      // k-step 0 of stage s from F0, reading k-step 1 of stage s into F1; the B loads carried
-      // from the previous stage
+      // k-step 0 of stage s from F0, reading k-step 1 of stage s into F1; the half of stage
+      // g + 1's loads carried from the previous stage
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[0][j], xa[0][i]);
-        if (i & 1) ld(pra, prb, 4 + (i >> 1), pbuf);
+        if (SILU ? !(i & 1) : i < 4) ld(pra, prb, SILU ? (i >> 1) : 4 + i, pbuf);
         if (i < 4) frag_w(1, g, 1, i);
         frag_x(1, g, 1, i);
       }
@@ -382,13 +384,13 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
         ra[2] = 0;
         rb[2] = 0;
       }
-      // second half of k-step 1, with the A loads of stage g + 2 and the reads of k-step 0 of
-      // stage g + 1 into F0
+      // second half of k-step 1, with the first half of stage g + 2's loads and the reads of
+      // k-step 0 of stage g + 1 into F0
 #pragma unroll
       for (int i = 4; i < 8; ++i) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
-        ld(ra, rb, i - 4, g & 1);
+        ld(ra, rb, SILU ? i : i - 4, g & 1);
         if (!SILU || s + 1 < nk) {   // SiLU: after a tile's last stage, read once its epilogue is done
           frag_x(0, g + 1, 0, 2 * (i - 4));
           frag_x(0, g + 1, 0, 2 * (i - 4) + 1);
