@@ -176,7 +176,7 @@ def main():
     gemm_tflops = 2 * flop_gemm / (t_g1 + t_g2) / 1e12
     dispatch_bytes = T * d * a + N * d * a + 12 * T * w.top_k
     combine_bytes = N * d * a + T * d * a + 8 * T * w.top_k
-    t_disp = sum(kms[names.index(n)] for n in ("dispatch_hist", "dispatch_scan", "dispatch_gather")) * 1e-3
+    t_disp = sum(kms[names.index(n)] for n in ("dispatch_hist", "dispatch_scan_aux", "dispatch_gather")) * 1e-3
     t_comb = kms[names.index("combine")] * 1e-3
 
     line = {

@@ -96,7 +96,7 @@ size_t moe_workspace_bytes(const moe_config_t* cfg);
  * [P2 §3.1] scores = W_router x, probs = softmax(scores / tau), top-k; with Gumbel noise the
  * ranked key is (logits + g) / tau. [P4 §2.4] a linear router, top-k, softmax weights.
  *   x          [T, d] act          token hidden states (ignored when logits_in != NULL)
- *   w_router   [E, d] fp32         router weight (ignored when logits_in != NULL)
+ *   w_router   [E, d] fp32         router weight, 16-byte aligned (ignored when logits_in != NULL)
  *   bias       [E] fp32 or NULL    per-expert logit bias, added after the product
  *   gumbel     [T, E] fp32 or NULL noise; when given, key = fl32(fl32(logit + g) / tau),
  *                                  otherwise key = logit. Noise changes selection only.
@@ -182,9 +182,11 @@ moe_status_t moe_aux_loss(const moe_config_t* cfg, const float* probs, const flo
  * non-NULL it holds n_events >= MOE_FORWARD_NUM_KERNELS + 1 created hipEvent_t; events[i] is
  * recorded on `stream` before kernel i and events[MOE_FORWARD_NUM_KERNELS] after the last, so
  * hipEventElapsedTime gives per-kernel times. Kernel order: route, dispatch-histogram,
- * dispatch-scan, dispatch-gather, gemm1 (W1 + SiLU), gemm2 (W2), combine, aux.
+ * dispatch-scan (with the capacity cut, and both aux losses from the pre-cut counts),
+ * dispatch-gather, gemm1 (W1 + SiLU), gemm2 (W2, with the reduction of its split tail when it
+ * has one), combine.
  */
-#define MOE_FORWARD_NUM_KERNELS 8
+#define MOE_FORWARD_NUM_KERNELS 7
 typedef struct {
   float*   logits;      /* [T, E] */
   float*   probs;       /* [T, E] */

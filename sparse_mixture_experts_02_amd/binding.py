@@ -20,9 +20,9 @@ MOE_OK = 0
 MOE_F32 = 0
 MOE_BF16 = 1
 MOE_NO_CAPACITY = -1
-MOE_FORWARD_NUM_KERNELS = 8
-FORWARD_KERNEL_NAMES = ("route", "dispatch_hist", "dispatch_scan", "dispatch_gather", "gemm1_silu",
-                        "gemm2", "combine", "aux")
+MOE_FORWARD_NUM_KERNELS = 7
+FORWARD_KERNEL_NAMES = ("route", "dispatch_hist", "dispatch_scan_aux", "dispatch_gather", "gemm1_silu", "gemm2",
+                        "combine")
 
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
                 3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}

@@ -184,57 +184,4 @@ hipError_t launch_probsum(const ProbSumParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// One block: P_i = (sum of the partial sums) / T, then both losses in double, stored as fp32.
-// The partial rows of expert e are split over the lanes (e, sub), sub = 0 .. nsub-1; each lane
-// keeps 4 independent running sums (so its loads overlap) and all sums are combined in a fixed
-// order, so the result does not depend on timing.
-__global__ __launch_bounds__(256) void aux_final_kernel(AuxParams p) {
-  __shared__ double part[256];
-  __shared__ double P[MOE_MAX_EXPERTS_DEV];
-  const int tid = threadIdx.x;
-  const int E = p.E;
-  int EPAD = 1;
-  while (EPAD < E) EPAD <<= 1;
-  const int e = tid % EPAD;
-  const int sub = tid / EPAD;
-  const int nsub = 256 / EPAD;
-  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-  if (e < E) {
-    int q = sub;
-    for (; q + 3 * nsub < p.nparts; q += 4 * nsub) {
-      a0 += p.psum[(size_t)q * E + e];
-      a1 += p.psum[(size_t)(q + nsub) * E + e];
-      a2 += p.psum[(size_t)(q + 2 * nsub) * E + e];
-      a3 += p.psum[(size_t)(q + 3 * nsub) * E + e];
-    }
-    for (; q < p.nparts; q += nsub) a0 += p.psum[(size_t)q * E + e];
-  }
-  part[tid] = (a0 + a1) + (a2 + a3);
-  __syncthreads();
-  if (tid < E) {
-    double s = 0.0;
-    for (int q = 0; q < nsub; ++q) s += part[q * EPAD + tid];
-    P[tid] = s / (double)p.T;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    double sw = 0.0, sb = 0.0;
-    const double tk = (double)p.T * (double)p.k;
-    const double uni = (double)p.k / (double)E;
-    for (int q = 0; q < E; ++q) {
-      const double c = (double)p.counts_pre[q];
-      sw += (c / tk) * P[q];
-      const double dv = c / (double)p.T - uni;
-      sb += dv * dv;
-    }
-    p.aux[0] = (float)((double)p.coef * (double)E * sw);
-    p.aux[1] = (float)((double)p.coef * sb);
-  }
-}
-
-hipError_t launch_aux_final(const AuxParams& p, hipStream_t s) {
-  aux_final_kernel<<<1, 256, 0, s>>>(p);
-  return hipGetLastError();
-}
-
 }  // namespace moe

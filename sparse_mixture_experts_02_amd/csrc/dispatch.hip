@@ -15,7 +15,7 @@ namespace moe {
 // the same expert are found with ballots (one ballot per distinct expert in the wave); the
 // rank of a lane is the number of such lanes below it. Wave counts are combined in LDS in wave
 // order, then chunk rounds in order, so rank_local is the stable rank inside the block.
-__global__ __launch_bounds__(256) void hist_kernel(HistParams p) {
+__device__ __forceinline__ void hist_block(const HistParams& p) {
   __shared__ int wave_cnt[4][MOE_MAX_EXPERTS_DEV];
   __shared__ int wave_base[4][MOE_MAX_EXPERTS_DEV];
   __shared__ int running[MOE_MAX_EXPERTS_DEV];
@@ -62,13 +62,15 @@ __global__ __launch_bounds__(256) void hist_kernel(HistParams p) {
   if (tid < E) p.blk_hist[(size_t)blockIdx.x * E + tid] = running[tid];
 }
 
+__global__ __launch_bounds__(256) void hist_kernel(HistParams p) { hist_block(p); }
+
 // ------------------------------------------------------------------------------ scan
 // One block. For each expert: exclusive scan of the block histograms (the pre-cut rank of
 // each block's first assignment), the pre-cut total, the kept count min(total, C); then the
 // exclusive scan of kept counts gives the segment offsets.
-__global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
+// `pre` (LDS, E entries) receives the pre-cut counts.
+__device__ __forceinline__ void scan_block(const ScanParams& p, int* pre) {
   __shared__ int kept[MOE_MAX_EXPERTS_DEV];
-  __shared__ int pre[MOE_MAX_EXPERTS_DEV];
   const int tid = threadIdx.x;
   const int E = p.E;
   // Threads are split into E groups of G lanes; group e scans column e. Each lane sums a
@@ -83,8 +85,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
   const int b0 = g * per;
   const int b1 = min(p.nb, b0 + per);
   int local = 0;
+  auto hist = [&](int b) { return p.blk_hist[(size_t)b * E + e]; };
   if (active)
-    for (int b = b0; b < b1; ++b) local += p.blk_hist[(size_t)b * E + e];
+    for (int b = b0; b < b1; ++b) local += hist(b);
   part[tid] = local;
   __syncthreads();
   if (active) {
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
     int run = before;
     for (int b = b0; b < b1; ++b) {
       p.blk_base[(size_t)b * E + e] = run;
-      run += p.blk_hist[(size_t)b * E + e];
+      run += hist(b);
     }
     if (g == G - 1) {
       pre[e] = run;
@@ -114,6 +117,78 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
     p.offsets[E] = off;
     *p.n_dropped = total_pre - off;
   }
+}
+
+__global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
+  __shared__ int pre[MOE_MAX_EXPERTS_DEV];
+  scan_block(p, pre);
+}
+
+// ------------------------------------------------------------------------------ aux losses
+// [P4 §3.2, P3 §3.2] One block: P_i = (sum of the partial sums) / T, then both losses in double, stored as fp32.
+// The partial rows of expert e are split over the lanes (e, sub), sub = 0 .. nsub-1; each lane
+// keeps 4 independent running sums (so its loads overlap) and all sums are combined in a fixed
+// order, so the result does not depend on timing.
+__device__ __forceinline__ void aux_block(const AuxParams& p, const int* counts_pre) {
+  __shared__ double part[256];
+  __shared__ double P[MOE_MAX_EXPERTS_DEV];
+  const int tid = threadIdx.x;
+  const int E = p.E;
+  int EPAD = 1;
+  while (EPAD < E) EPAD <<= 1;
+  const int e = tid % EPAD;
+  const int sub = tid / EPAD;
+  const int nsub = 256 / EPAD;
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  if (e < E) {
+    int q = sub;
+    for (; q + 3 * nsub < p.nparts; q += 4 * nsub) {
+      a0 += p.psum[(size_t)q * E + e];
+      a1 += p.psum[(size_t)(q + nsub) * E + e];
+      a2 += p.psum[(size_t)(q + 2 * nsub) * E + e];
+      a3 += p.psum[(size_t)(q + 3 * nsub) * E + e];
+    }
+    for (; q < p.nparts; q += nsub) a0 += p.psum[(size_t)q * E + e];
+  }
+  part[tid] = (a0 + a1) + (a2 + a3);
+  __syncthreads();
+  if (tid < E) {
+    double s = 0.0;
+    for (int q = 0; q < nsub; ++q) s += part[q * EPAD + tid];
+    P[tid] = s / (double)p.T;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double sw = 0.0, sb = 0.0;
+    const double tk = (double)p.T * (double)p.k;
+    const double uni = (double)p.k / (double)E;
+    for (int q = 0; q < E; ++q) {
+      const double c = (double)counts_pre[q];
+      sw += (c / tk) * P[q];
+      const double dv = c / (double)p.T - uni;
+      sb += dv * dv;
+    }
+    p.aux[0] = (float)((double)p.coef * (double)E * sw);
+    p.aux[1] = (float)((double)p.coef * sb);
+  }
+}
+
+__global__ __launch_bounds__(256) void aux_final_kernel(AuxParams p) { aux_block(p, p.counts_pre); }
+
+hipError_t launch_aux_final(const AuxParams& p, hipStream_t s) {
+  aux_final_kernel<<<1, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+
+// ------------------------------------------------------------------------------ scan + aux
+// The scan, then (in the same block, from the pre-cut counts it just formed) both aux losses:
+// one launch fewer in the forward pass.
+__global__ __launch_bounds__(256) void scan_aux_kernel(ScanAuxParams p) {
+  __shared__ int pre[MOE_MAX_EXPERTS_DEV];
+  scan_block(p.s, pre);
+  __syncthreads();
+  aux_block(p.a, pre);
 }
 
 // ------------------------------------------------------------------------------ gather
@@ -162,6 +237,11 @@ hipError_t launch_hist(const HistParams& p, hipStream_t s) {
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t s) {
   scan_kernel<<<1, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_aux(const ScanAuxParams& p, hipStream_t s) {
+  scan_aux_kernel<<<1, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 

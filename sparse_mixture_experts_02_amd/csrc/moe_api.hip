@@ -13,7 +13,7 @@ namespace {
 constexpr int kMaxDim = 32768;
 
 struct Layout {
-  size_t wsplit, psum, blk_hist, blk_base, rank_local, probsum;
+  size_t psum, blk_hist, blk_base, rank_local, probsum;
   size_t logits, ids, weights, counts_pre, counts, offsets, perm, row_of, dropped, ndrop;
   size_t xp, h, y;
   size_t sk_part;   // partial sums of the 256 x 256 grouped GEMM's split tail (empty if unused)
@@ -32,9 +32,7 @@ Layout layout(const moe_config_t& c) {
   };
   const size_t T = (size_t)c.T, k = (size_t)c.top_k, E = (size_t)c.num_experts;
   const size_t d = (size_t)c.d_model, f = (size_t)c.d_ffn, TK = T * k, a = act_size(c);
-  const size_t EP = 16 * (size_t)route_expert_tiles(c.num_experts);
-  L.wsplit = take(3 * EP * (size_t)route_padded_d(c.d_model) * 2);
-  L.psum = take((size_t)route_max_parts(c.T) * E * sizeof(double));
+  L.psum = take((size_t)route_max_parts(c.T, c.num_experts) * E * sizeof(double));
   const size_t nb = (size_t)dispatch_num_blocks((int)TK);
   L.blk_hist = take(nb * E * 4);
   L.blk_base = take(nb * E * 4);
@@ -87,24 +85,16 @@ int capacity_of(const moe_config_t& c) { return c.capacity < 0 ? -1 : c.capacity
 
 moe_status_t run_route(const moe_config_t& c, const void* x, const float* w_router, const float* bias,
                        const float* gumbel, const float* logits_in, float* logits_out, float* probs_out,
-                       int32_t* ids, float* weights, double* psum, void* ws, hipStream_t s) {
-  const Layout L = layout(c);
-  const bool bf16 = c.act_dtype == MOE_BF16;
-  const void* wsrc = w_router;
-  if (!logits_in && bf16) {
-    MOE_LAUNCH(launch_route_split(w_router, c.num_experts, c.d_model, at(ws, L.wsplit), s));
-    wsrc = at(ws, L.wsplit);
-  }
+                       int32_t* ids, float* weights, double* psum, hipStream_t s) {
   RouteParams p{};
   p.T = c.T;
   p.d = c.d_model;
-  p.dpad = route_padded_d(c.d_model);
   p.E = c.num_experts;
   p.k = c.top_k;
   p.tau = c.temperature;
   p.renormalize = c.renormalize;
   p.x = x;
-  p.wsplit = wsrc;
+  p.w_router = w_router;
   p.bias = logits_in ? nullptr : bias;
   p.gumbel = gumbel;
   p.logits_in = logits_in;
@@ -113,11 +103,11 @@ moe_status_t run_route(const moe_config_t& c, const void* x, const float* w_rout
   p.ids = ids;
   p.weights = weights;
   p.psum = psum;
-  MOE_LAUNCH(launch_route(p, bf16, s));
+  MOE_LAUNCH(launch_route(p, c.act_dtype == MOE_BF16, s));
   return MOE_OK;
 }
 
-moe_status_t run_hist(const moe_config_t& c, const int32_t* ids, void* ws, hipStream_t s) {
+HistParams hist_params(const moe_config_t& c, const int32_t* ids, void* ws) {
   const Layout L = layout(c);
   HistParams p{};
   p.TK = c.T * c.top_k;
@@ -125,12 +115,16 @@ moe_status_t run_hist(const moe_config_t& c, const int32_t* ids, void* ws, hipSt
   p.ids = ids;
   p.blk_hist = (int32_t*)at(ws, L.blk_hist);
   p.rank_local = (int32_t*)at(ws, L.rank_local);
-  MOE_LAUNCH(launch_hist(p, s));
+  return p;
+}
+
+moe_status_t run_hist(const moe_config_t& c, const int32_t* ids, void* ws, hipStream_t s) {
+  MOE_LAUNCH(launch_hist(hist_params(c, ids, ws), s));
   return MOE_OK;
 }
 
-moe_status_t run_scan(const moe_config_t& c, int32_t* counts_pre, int32_t* counts, int32_t* offsets,
-                      int32_t* n_dropped, void* ws, hipStream_t s) {
+ScanParams scan_params(const moe_config_t& c, int32_t* counts_pre, int32_t* counts, int32_t* offsets,
+                       int32_t* n_dropped, void* ws) {
   const Layout L = layout(c);
   ScanParams p{};
   p.TK = c.T * c.top_k;
@@ -143,7 +137,12 @@ moe_status_t run_scan(const moe_config_t& c, int32_t* counts_pre, int32_t* count
   p.counts = counts;
   p.offsets = offsets;
   p.n_dropped = n_dropped;
-  MOE_LAUNCH(launch_scan(p, s));
+  return p;
+}
+
+moe_status_t run_scan(const moe_config_t& c, int32_t* counts_pre, int32_t* counts, int32_t* offsets,
+                      int32_t* n_dropped, void* ws, hipStream_t s) {
+  MOE_LAUNCH(launch_scan(scan_params(c, counts_pre, counts, offsets, n_dropped, ws), s));
   return MOE_OK;
 }
 
@@ -201,8 +200,7 @@ moe_status_t run_combine(const moe_config_t& c, const void* y, const int32_t* ro
   return MOE_OK;
 }
 
-moe_status_t run_aux_final(const moe_config_t& c, const double* psum, int nparts, const int32_t* counts_pre,
-                           float* aux, hipStream_t s) {
+AuxParams aux_params(const moe_config_t& c, const double* psum, int nparts, const int32_t* counts_pre, float* aux) {
   AuxParams p{};
   p.T = c.T;
   p.E = c.num_experts;
@@ -213,7 +211,12 @@ moe_status_t run_aux_final(const moe_config_t& c, const double* psum, int nparts
   p.psum = psum;
   p.counts_pre = counts_pre;
   p.aux = aux;
-  MOE_LAUNCH(launch_aux_final(p, s));
+  return p;
+}
+
+moe_status_t run_aux_final(const moe_config_t& c, const double* psum, int nparts, const int32_t* counts_pre,
+                           float* aux, hipStream_t s) {
+  MOE_LAUNCH(launch_aux_final(aux_params(c, psum, nparts, counts_pre, aux), s));
   return MOE_OK;
 }
 
@@ -269,10 +272,10 @@ moe_status_t moe_route(const moe_config_t* cfg, const void* x, const float* w_ro
                        int32_t* ids, float* weights, void* ws, size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(moe_validate_config(cfg));
   if (!ids || !weights) return MOE_ERR_INVALID_ARGUMENT;
-  if (!logits_in && (!x || !w_router || !aligned16(x))) return MOE_ERR_INVALID_ARGUMENT;
+  if (!logits_in && (!x || !w_router || !aligned16(x) || !aligned16(w_router))) return MOE_ERR_INVALID_ARGUMENT;
   MOE_TRY(check_ws(cfg, ws, ws_bytes));
   return run_route(*cfg, x, w_router, bias, gumbel, logits_in, logits_out, probs_out, ids, weights, nullptr,
-                   ws, stream);
+                   stream);
 }
 
 moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* ids, const void* x, int32_t* counts_pre,
@@ -331,7 +334,8 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
                          moe_debug_outputs* dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(moe_validate_config(cfg));
   if (!x || !w_router || !w1 || !w2 || !out || !aux) return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(out)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w1) || !aligned16(w2) || !aligned16(out))
+    return MOE_ERR_INVALID_ARGUMENT;
   MOE_TRY(check_ws(cfg, ws, ws_bytes));
   moe_debug_outputs none{};
   const moe_debug_outputs& D = dbg ? *dbg : none;
@@ -362,11 +366,14 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
     return hip_status(hipEventRecord(D.events[ev++], stream));
   };
   MOE_TRY(mark());
-  MOE_TRY(run_route(c, x, w_router, bias, gumbel, nullptr, logits, probs, ids, weights, psum, ws, stream));
+  MOE_TRY(run_route(c, x, w_router, bias, gumbel, nullptr, logits, probs, ids, weights, psum, stream));
   MOE_TRY(mark());
   MOE_TRY(run_hist(c, ids, ws, stream));
   MOE_TRY(mark());
-  MOE_TRY(run_scan(c, counts_pre, counts, offsets, ndrop, ws, stream));
+  ScanAuxParams sp{};
+  sp.s = scan_params(c, counts_pre, counts, offsets, ndrop, ws);
+  sp.a = aux_params(c, psum, route_num_parts(c.T, c.num_experts, c.act_dtype == MOE_BF16, false), counts_pre, aux);
+  MOE_LAUNCH(launch_scan_aux(sp, stream));
   MOE_TRY(mark());
   MOE_TRY(run_gather(c, ids, x, offsets, perm, row_of, dropped, xp, ws, stream));
   MOE_TRY(mark());
@@ -375,9 +382,6 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
   MOE_TRY(run_gemm(c, h, w2, y, offsets, c.d_model, c.d_ffn, false, ws, stream));
   MOE_TRY(mark());
   MOE_TRY(run_combine(c, y, row_of, weights, out, stream));
-  MOE_TRY(mark());
-  MOE_TRY(run_aux_final(c, psum, route_num_parts(c.T, c.num_experts, c.act_dtype == MOE_BF16, false), counts_pre,
-                        aux, stream));
   MOE_TRY(mark());
   return MOE_OK;
 }

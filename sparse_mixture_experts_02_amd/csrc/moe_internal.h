@@ -54,11 +54,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 struct RouteParams {
   int T, d, E, k;
-  int dpad;                 // row length of the split weight planes (d rounded up to 128)
   float tau;
   int renormalize;
   const void* x;            // [T, d] act
-  const void* wsplit;       // bf16 mode: [3][16*ET][dpad] bf16 split of W_r; fp32 mode: W_r [E, d]
+  const float* w_router;    // [E, d] fp32, 16-byte aligned
   const float* bias;        // [E] or null
   const float* gumbel;      // [T, E] or null
   const float* logits_in;   // [T, E] or null (skip the product)
@@ -66,7 +65,7 @@ struct RouteParams {
   float* probs_out;         // [T, E] or null
   int32_t* ids;             // [T, k]
   float* weights;           // [T, k]
-  double* psum;             // [route_num_parts][E] per-wave probability sums, or null
+  double* psum;             // [route_num_parts][E] per-workgroup probability sums, or null
 };
 
 struct HistParams {
@@ -129,6 +128,11 @@ struct AuxParams {
   float* aux;
 };
 
+struct ScanAuxParams {
+  ScanParams s;
+  AuxParams a;              // a.counts_pre is not read: the scan's own pre-cut counts are used
+};
+
 struct ProbSumParams {
   int T, E;
   float tau;
@@ -141,15 +145,14 @@ struct ProbSumParams {
 // Each returns the launch status (hipGetLastError after the launch).
 
 int route_expert_tiles(int E);
-int route_padded_d(int d);
 int route_num_parts(int T, int E, bool bf16, bool logits_in);   // rows of psum a launch writes
-int route_max_parts(int T);
-hipError_t launch_route_split(const float* w_router, int E, int d, void* wsplit, hipStream_t s);
+int route_max_parts(int T, int E);
 hipError_t launch_route(const RouteParams& p, bool bf16, hipStream_t s);
 
 int dispatch_num_blocks(int TK);
 hipError_t launch_hist(const HistParams& p, hipStream_t s);
 hipError_t launch_scan(const ScanParams& p, hipStream_t s);
+hipError_t launch_scan_aux(const ScanAuxParams& p, hipStream_t s);
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 
 int gemm_max_mtiles(int max_rows, int E);

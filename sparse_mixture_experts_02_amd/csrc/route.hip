@@ -6,7 +6,7 @@
 // noise the ranked value is (logits + g) / tau. [P4 §2.4] a linear router with softmax, the
 // top-k experts per token, weights = softmax router scores.
 //
-// bf16 activations: W_r (fp32) is split once per call into three bf16 planes hi + mid + lo
+// bf16 activations: each fp32 router weight w is split into three bf16 values hi + mid + lo
 // (hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid); the residual is below 2^-26 |w|),
 // so x W_r^T = x hi^T + x mid^T + x lo^T runs on the bf16 MFMA (v_mfma_f32_16x16x32_bf16) with
 // exact products and fp32 accumulation. fp32 activations use v_mfma_f32_16x16x4_f32.
@@ -17,46 +17,14 @@
 // with more experts held in extra registers (ET tiles of 16).
 //
 // Two kernels compute the logits:
-//  * route_fast_kernel (bf16, E <= 32): a 4-wave workgroup routes 64 tokens. x rows and the
-//    split weight pass through an LDS ring of 128-column chunks (5 stages for E <= 16, 4 for
-//    E <= 32), filled with direct global -> LDS loads issued as many chunks ahead as the ring
-//    holds, so each weight chunk is read once per 64 tokens and x streams with 48-64 KiB in flight
-//    per workgroup.
-//  * route_kernel (fp32 activations, E > 32, or given logits): one wave per 32 tokens, operands
-//    straight from global memory.
+//  * route_ksplit_kernel (bf16): an 8-wave workgroup routes 1, 2 or 4 tiles of 16 tokens, each
+//    wave over its own range of K, with x and the fp32 weight read straight from global memory (the weight is split
+//    into its planes in registers, so no separate split pass and no staged copy of the weight).
+//  * route_kernel (fp32 activations, or given logits): one wave per 32 tokens, operands straight
+//    from global memory.
 #include "moe_internal.h"
 
 namespace moe {
-
-namespace {
-// fast kernel geometry
-constexpr int FR_TOK = 64;           // tokens per workgroup tile (16 per wave)
-constexpr int FR_COLS = 128;         // columns of x and of the weight per stage
-constexpr int FR_ROWB = 256;         // staged bytes per row per stage
-// LDS ring depth: as many stages as fit in 160 KiB (5 x 28 KiB for one 16-expert tile, 4 x 40
-// KiB for two), so that NSTAGE - 1 chunks of x are in flight per workgroup
-template <int ET>
-constexpr int fr_nstage() { return ET == 1 ? 5 : 4; }
-constexpr int FR_MAX_BLOCKS = 1024;
-}  // namespace
-
-__global__ __launch_bounds__(256) void route_split_kernel(const float* __restrict__ w, int E, int EP,
-                                                          int d, int dpad, uint16_t* __restrict__ out) {
-  const size_t n = (size_t)EP * dpad;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-    const int e = (int)(i / dpad);
-    const int c = (int)(i % dpad);
-    const float v = (e < E && c < d) ? w[(size_t)e * d + c] : 0.0f;   // zero padding
-    const uint32_t hi = f32_to_bf16_bits(v);
-    const float r1 = __fsub_rn(v, bf16_bits_to_f32(hi));
-    const uint32_t mid = f32_to_bf16_bits(r1);
-    const float r2 = __fsub_rn(r1, bf16_bits_to_f32(mid));
-    const uint32_t lo = f32_to_bf16_bits(r2);
-    out[i] = (uint16_t)hi;
-    out[n + i] = (uint16_t)mid;
-    out[2 * n + i] = (uint16_t)lo;
-  }
-}
 
 // Order-preserving map of a finite fp32 key to uint32 (larger key -> larger code), with -0.0
 // and +0.0 mapped to the same code. Every finite key maps above 0, so 0 marks "not a candidate".
@@ -183,12 +151,11 @@ __device__ __forceinline__ void store_psum(const RouteParams& p, double (&psum_a
 
 // ------------------------------------------------------------------------------ generic kernel
 
-template <bool BF16, int ET>
+template <int ET>
 __global__ __launch_bounds__(64) void route_kernel(RouteParams p) {
   const int lane = threadIdx.x;
   const int col = lane & 15;   // expert column within a 16-wide tile
   const int grp = lane >> 4;   // row group
-  constexpr int EP = 16 * ET;
   const int T = p.T, E = p.E, d = p.d;
   const int ntiles = (T + ROUTE_TILE - 1) / ROUTE_TILE;
 
@@ -216,52 +183,21 @@ __global__ __launch_bounds__(64) void route_kernel(RouteParams p) {
             acc[mt][et][r] = (t < T && e < E) ? p.logits_in[(size_t)t * E + e] : 0.0f;
           }
     } else {
-      if constexpr (BF16) {
-        const uint16_t* __restrict__ x = (const uint16_t*)p.x;
-        const uint16_t* __restrict__ ws = (const uint16_t*)p.wsplit;
-        const int dpad = p.dpad;
-        const size_t plane = (size_t)EP * dpad;
-        const int row0 = t0 + col;
-        const int row1 = t0 + 16 + col;
+      const float* __restrict__ x = (const float*)p.x;
+      const float* __restrict__ wr = p.w_router;
+      const int row0 = t0 + col;
+      const int row1 = t0 + 16 + col;
 #pragma unroll 4
-        for (int k0 = 0; k0 < d; k0 += 32) {
-          const int kc = k0 + 8 * grp;
-          const bool kin = kc < d;
-          uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
-          if (kin && row0 < T) a0 = *(const uint4*)(x + (size_t)row0 * d + kc);
-          if (kin && row1 < T) a1 = *(const uint4*)(x + (size_t)row1 * d + kc);
-          const bf16x8_t A0 = __builtin_bit_cast(bf16x8_t, a0);
-          const bf16x8_t A1 = __builtin_bit_cast(bf16x8_t, a1);
+      for (int k0 = 0; k0 < d; k0 += 4) {
+        const int kc = k0 + grp;   // d is a multiple of 8, so kc < d always
+        const float a0 = (row0 < T) ? x[(size_t)row0 * d + kc] : 0.0f;
+        const float a1 = (row1 < T) ? x[(size_t)row1 * d + kc] : 0.0f;
 #pragma unroll
-          for (int et = 0; et < ET; ++et) {
-            const size_t wrow = (size_t)(et * 16 + col) * dpad + kc;
-#pragma unroll
-            for (int s = 2; s >= 0; --s) {   // smallest plane first
-              uint4 b = make_uint4(0, 0, 0, 0);
-              if (kin) b = *(const uint4*)(ws + s * plane + wrow);
-              const bf16x8_t B = __builtin_bit_cast(bf16x8_t, b);
-              acc[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B, acc[0][et], 0, 0, 0);
-              acc[1][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, acc[1][et], 0, 0, 0);
-            }
-          }
-        }
-      } else {
-        const float* __restrict__ x = (const float*)p.x;
-        const float* __restrict__ wr = (const float*)p.wsplit;
-        const int row0 = t0 + col;
-        const int row1 = t0 + 16 + col;
-#pragma unroll 4
-        for (int k0 = 0; k0 < d; k0 += 4) {
-          const int kc = k0 + grp;   // d is a multiple of 8, so kc < d always
-          const float a0 = (row0 < T) ? x[(size_t)row0 * d + kc] : 0.0f;
-          const float a1 = (row1 < T) ? x[(size_t)row1 * d + kc] : 0.0f;
-#pragma unroll
-          for (int et = 0; et < ET; ++et) {
-            const int e = et * 16 + col;
-            const float b = (e < E) ? wr[(size_t)e * d + kc] : 0.0f;
-            acc[0][et] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b, acc[0][et], 0, 0, 0);
-            acc[1][et] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b, acc[1][et], 0, 0, 0);
-          }
+        for (int et = 0; et < ET; ++et) {
+          const int e = et * 16 + col;
+          const float b = (e < E) ? wr[(size_t)e * d + kc] : 0.0f;
+          acc[0][et] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b, acc[0][et], 0, 0, 0);
+          acc[1][et] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b, acc[1][et], 0, 0, 0);
         }
       }
     }
@@ -271,149 +207,152 @@ __global__ __launch_bounds__(64) void route_kernel(RouteParams p) {
   store_psum<ET>(p, psum_acc, blockIdx.x);
 }
 
-// ------------------------------------------------------------------------------ fast kernel
+// ------------------------------------------------------------------------------ K-split kernel
 
 namespace {
-// One direct global -> LDS 16-byte load per lane (gfx950 global_load_lds_dwordx4): lane l reads
-// sbase + voff and writes LDS bytes [lds_addr + 16 l, lds_addr + 16 l + 16). M0 carries the LDS
-// address and is restored afterwards. Issued as inline asm so that the compiler does not wait
-// on it before unrelated LDS reads; the kernel counts these loads and waits (vmcnt) itself.
-__device__ __forceinline__ void route_load_lds16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved)
-               : "s"(lds_addr), "v"(voff), "s"(sbase)
-               : "memory");
-}
+constexpr int KS_WAVES = 8;             // waves per workgroup, each taking one K range
+constexpr int KS_MAX_BLOCKS = 2048;     // grid cap (one row of probability sums per workgroup)
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+// hi + mid + lo split of 8 fp32 router weights into three bf16x8 MFMA operands (the products with
+// bf16 activations are exact in fp32, and hi + mid + lo equals w to within 2^-26 |w|)
+__device__ __forceinline__ void split3(const float4& a, const float4& b, bf16x8_t& hi, bf16x8_t& mid, bf16x8_t& lo) {
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    const float r0 = __fsub_rn(v[2 * i], bf16_bits_to_f32(h[i] & 0xffffu));
+    const float r1 = __fsub_rn(v[2 * i + 1], bf16_bits_to_f32(h[i] >> 16));
+    m[i] = pack_bf16x2(r0, r1);
+    const float q0 = __fsub_rn(r0, bf16_bits_to_f32(m[i] & 0xffffu));
+    const float q1 = __fsub_rn(r1, bf16_bits_to_f32(m[i] >> 16));
+    l[i] = pack_bf16x2(q0, q1);
+  }
+  hi = __builtin_bit_cast(bf16x8_t, uint4{h[0], h[1], h[2], h[3]});
+  mid = __builtin_bit_cast(bf16x8_t, uint4{m[0], m[1], m[2], m[3]});
+  lo = __builtin_bit_cast(bf16x8_t, uint4{l[0], l[1], l[2], l[3]});
 }
-
-// staged row r (256 bytes) holds its 16-byte chunk c in slot c ^ (r mod 16): 16 lanes reading 16
-// consecutive rows at one chunk hit 16 distinct bank groups
-__device__ __forceinline__ int fr_off(int row, int chunk) { return row * FR_ROWB + ((chunk ^ (row & 15)) << 4); }
 }  // namespace
 
-template <int ET>
-__global__ __launch_bounds__(256, 1) void route_fast_kernel(RouteParams p) {
-  constexpr int EP = 16 * ET;
-  constexpr int XB = FR_TOK * FR_ROWB;        // x chunk: 64 rows, 16 KiB
-  constexpr int WB = 3 * EP * FR_ROWB;        // weight chunk: 3 planes x EP rows, 12 KiB per ET
-  constexpr int SB = XB + WB;
-  constexpr int XI = 4;                       // x load instructions per wave per stage (16 rows)
-  constexpr int WI = 3 * ET;                  // weight load instructions per wave per stage
-  constexpr int PER = XI + WI;
-  constexpr int NS = fr_nstage<ET>();
-  static_assert(NS * SB <= 160 * 1024, "LDS ring too large");
-  static_assert((NS - 2) * PER <= 63, "vmcnt range");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * SB];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int T = p.T, d = p.d, dpad = p.dpad;
-  const int nk = dpad / FR_COLS;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  const uint8_t* __restrict__ W = (const uint8_t*)p.wsplit;
-  const int lr = lane >> 4, ls = lane & 15;   // row within an instruction's 4 rows, slot
-
-  // weight sources of this lane (same for every tile): staged weight row rr = plane * EP + e
-  uint32_t woff[WI];
-#pragma unroll
-  for (int i = 0; i < WI; ++i) {
-    const int rr = w * (WI * 4) + i * 4 + lr;
-    woff[i] = (uint32_t)rr * (uint32_t)(dpad * 2) + ((ls ^ (rr & 15)) << 4);
-  }
+// bf16 activations, E <= 64. A workgroup of 8 waves routes MT tiles of 16 tokens: wave w
+// multiplies them by the router weight over its own range of K (a contiguous run of 32-column
+// MFMA steps), reading x and the fp32 weight straight from global memory and splitting the
+// weight into its three bf16 planes in registers (once per step for all MT tiles); all loads of a
+// batch of steps are issued before its MFMAs. The 8 partial products of each tile meet in LDS and
+// wave q adds those of tile q in wave order and finishes it; the probability sums of the MT
+// finishing waves are added in wave order. MT > 1 reads each weight element once per 16 MT
+// tokens (large T); MT = 1 spreads small T over as many workgroups as possible.
+template <int ET, int MT>
+__global__ __launch_bounds__(512) void route_ksplit_kernel(RouteParams p) {
+  static_assert(MT <= KS_WAVES, "one finishing wave per tile");
+  constexpr int NB = (ET * (MT + 2) <= 6) ? 4 : ((ET * (MT + 2) <= 12) ? 2 : 1);   // k-steps per load batch
+  __shared__ f32x4_t red[KS_WAVES][MT][ET][64];
+  __shared__ double wsum[MT][ET][16];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int T = p.T, d = p.d, E = p.E;
+  const int nsteps = (d + 31) / 32;
+  const int per = (nsteps + KS_WAVES - 1) / KS_WAVES;
+  const int s0 = w * per;
+  const int s1 = min(nsteps, s0 + per);
+  const int col = lane & 15, kq = 8 * (lane >> 4);
+  const uint16_t* __restrict__ X = (const uint16_t*)p.x;
+  const float* __restrict__ W = p.w_router;
 
   double psum_acc[ET];
 #pragma unroll
   for (int et = 0; et < ET; ++et) psum_acc[et] = 0.0;
 
-  const int ntiles = (T + FR_TOK - 1) / FR_TOK;
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int t0 = tile * FR_TOK;
-    const uint8_t* __restrict__ X = (const uint8_t*)p.x + (size_t)t0 * d * 2;
-    // x sources: staged row = w * 16 + i * 4 + lr; rows past T read token T - 1 (their results
-    // are discarded); columns past d read column 0 (the weight is zero there)
-    uint32_t xrow[XI];
-    int xch[XI];
+  const int ngroups = (T + 16 * MT - 1) / (16 * MT);
+  for (int grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+    const int t0 = grp * 16 * MT;
+    const uint16_t* __restrict__ xr[MT];
 #pragma unroll
-    for (int i = 0; i < XI; ++i) {
-      const int row = w * 16 + i * 4 + lr;
-      const int tr = min(t0 + row, T - 1) - t0;
-      xrow[i] = (uint32_t)tr * (uint32_t)(d * 2);
-      xch[i] = ls ^ (row & 15);
-    }
-    auto issue = [&](int kt) {
-      const int st = min(kt, nk - 1);   // past the end: reload the last chunk (uniform counts)
-      const uint32_t base = lds0 + (kt % NS) * SB;
+    for (int mt = 0; mt < MT; ++mt) xr[mt] = X + (size_t)min(t0 + mt * 16 + col, T - 1) * d;   // rows past T: discarded
+    f32x4_t acc[MT][ET];
 #pragma unroll
-      for (int i = 0; i < XI; ++i) {
-        int c = st * FR_COLS + xch[i] * 8;
-        if (c >= d) c = 0;
-        route_load_lds16(X, xrow[i] + (uint32_t)c * 2, base + (w * 16 + i * 4) * FR_ROWB);
-      }
-      const uint8_t* wst = W + (size_t)st * FR_ROWB;
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < WI; ++i) route_load_lds16(wst, woff[i], base + XB + (w * (WI * 4) + i * 4) * FR_ROWB);
-    };
-
-    f32x4_t acc[ET];
+      for (int et = 0; et < ET; ++et) acc[mt][et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int sb = s0; sb < s1; sb += NB) {
+      uint4 xa[NB][MT];
+      float4 wv[NB][ET][2];
 #pragma unroll
-    for (int et = 0; et < ET; ++et) acc[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
+      for (int u = 0; u < NB; ++u) {
+        const int kc = (sb + u) * 32 + kq;
+        const bool kin = sb + u < s1 && kc < d;   // d is a multiple of 8: a chunk is all in or all out
 #pragma unroll
-    for (int kt = 0; kt < NS - 1; ++kt) issue(kt);
-    wait_vmcnt<(NS - 2) * PER>();
-    __syncthreads();
-    const int arow = w * 16 + (lane & 15);
-    for (int s = 0; s < nk; ++s) {
-      issue(s + NS - 1);
-      const uint8_t* sx = smem + (s % NS) * SB;
-      const uint8_t* sw = sx + XB;
-#pragma unroll
-      for (int ks = 0; ks < FR_COLS / 32; ++ks) {
-        const int ch = ks * 4 + (lane >> 4);
-        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, *(const uint4*)(sx + fr_off(arow, ch)));
+        for (int mt = 0; mt < MT; ++mt) xa[u][mt] = kin ? *(const uint4*)(xr[mt] + kc) : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int et = 0; et < ET; ++et) {
-#pragma unroll
-          for (int pl = 2; pl >= 0; --pl) {   // smallest plane first
-            const int wrow = pl * EP + et * 16 + (lane & 15);
-            const bf16x8_t B = __builtin_bit_cast(bf16x8_t, *(const uint4*)(sw + fr_off(wrow, ch)));
-            acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[et], 0, 0, 0);
+          const int e = et * 16 + col;
+          if (kin && e < E) {
+            const float4* src = (const float4*)(W + (size_t)e * d + kc);
+            wv[u][et][0] = src[0];
+            wv[u][et][1] = src[1];
+          } else {
+            wv[u][et][0] = make_float4(0.f, 0.f, 0.f, 0.f);
+            wv[u][et][1] = make_float4(0.f, 0.f, 0.f, 0.f);
           }
         }
       }
-      wait_vmcnt<(NS - 2) * PER>();   // chunk s + 1 complete (the NS - 2 after it may be in flight)
-      __syncthreads();
-    }
-    wait_vmcnt<0>();           // the trailing reloads land before the ring is reused
-    __syncthreads();
-    finish_tile<ET>(p, acc, t0 + w * 16, true, psum_acc);
-  }
-  // One row of probability sums per workgroup: each wave folds its 4 row groups (as store_psum),
-  // the 4 waves' sums meet in LDS (the ring is no longer read: every wave is past the last
-  // barrier of the tile loop) and are added in wave order.
-  if (p.psum) {
-    double* wsum = (double*)smem;   // [4 waves][ET][16]
 #pragma unroll
-    for (int et = 0; et < ET; ++et) {
-      double v = psum_acc[et];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      if (lane < 16) wsum[(w * ET + et) * 16 + lane] = v;
+      for (int u = 0; u < NB; ++u) {
+#pragma unroll
+        for (int et = 0; et < ET; ++et) {
+          bf16x8_t hi, mid, lo;
+          split3(wv[u][et][0], wv[u][et][1], hi, mid, lo);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const bf16x8_t A = __builtin_bit_cast(bf16x8_t, xa[u][mt]);
+            // smallest plane first
+            acc[mt][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, lo, acc[mt][et], 0, 0, 0);
+            acc[mt][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, mid, acc[mt][et], 0, 0, 0);
+            acc[mt][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, hi, acc[mt][et], 0, 0, 0);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int et = 0; et < ET; ++et) red[w][mt][et][lane] = acc[mt][et];
+    __syncthreads();
+    if (w < MT) {
+      f32x4_t s[ET];
+#pragma unroll
+      for (int et = 0; et < ET; ++et) {
+        s[et] = red[0][w][et][lane];
+#pragma unroll
+        for (int q = 1; q < KS_WAVES; ++q) {
+          const f32x4_t v = red[q][w][et][lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[et][r] = __fadd_rn(s[et][r], v[r]);
+        }
+      }
+      finish_tile<ET>(p, s, t0 + 16 * w, true, psum_acc);
+    }
+    __syncthreads();   // red is rewritten by the next group
+  }
+  if (p.psum) {
+    if (w < MT) {
+#pragma unroll
+      for (int et = 0; et < ET; ++et) {
+        double v = psum_acc[et];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (lane < 16) wsum[w][et][lane] = v;
+      }
     }
     __syncthreads();
     if (w == 0 && lane < 16) {
 #pragma unroll
       for (int et = 0; et < ET; ++et) {
+        double v = wsum[0][et][lane];
+#pragma unroll
+        for (int q = 1; q < MT; ++q) v += wsum[q][et][lane];
         const int e = et * 16 + lane;
-        const double v = ((wsum[(0 * ET + et) * 16 + lane] + wsum[(1 * ET + et) * 16 + lane]) +
-                          wsum[(2 * ET + et) * 16 + lane]) +
-                         wsum[(3 * ET + et) * 16 + lane];
-        if (e < p.E) p.psum[(size_t)blockIdx.x * p.E + e] = v;
+        if (e < E) p.psum[(size_t)blockIdx.x * E + e] = v;
       }
     }
   }
@@ -423,13 +362,22 @@ __global__ __launch_bounds__(256, 1) void route_fast_kernel(RouteParams p) {
 
 int route_expert_tiles(int E) { return (E + 15) / 16; }
 
-int route_padded_d(int d) { return (d + FR_COLS - 1) / FR_COLS * FR_COLS; }
 
-static bool use_fast(int E, bool bf16, bool logits_in) { return bf16 && !logits_in && route_expert_tiles(E) <= 2; }
+static bool use_ksplit(bool bf16, bool logits_in) { return bf16 && !logits_in; }
 
-static int fast_blocks(int T) {
-  const int n = (T + FR_TOK - 1) / FR_TOK;
-  return n < FR_MAX_BLOCKS ? n : FR_MAX_BLOCKS;
+// Tiles of 16 tokens per K-split workgroup: as many workgroups as possible while they fill the
+// chip, more tiles per workgroup (fewer weight re-reads) once there are enough tokens; at most 2
+// when E > 32 (LDS of the partial products).
+static int ksplit_mt(int T, int E) {
+  const int tiles = (T + 15) / 16;
+  const int mt = tiles >= 4 * 256 ? 4 : (tiles >= 2 * 256 ? 2 : 1);
+  return (route_expert_tiles(E) > 2 && mt > 2) ? 2 : mt;
+}
+
+static int ksplit_blocks(int T, int E) {
+  const int mt = ksplit_mt(T, E);
+  const int n = (T + 16 * mt - 1) / (16 * mt);
+  return n < KS_MAX_BLOCKS ? n : KS_MAX_BLOCKS;
 }
 
 static int generic_blocks(int T) {
@@ -438,45 +386,50 @@ static int generic_blocks(int T) {
 }
 
 int route_num_parts(int T, int E, bool bf16, bool logits_in) {
-  return use_fast(E, bf16, logits_in) ? fast_blocks(T) : generic_blocks(T);
+  return use_ksplit(bf16, logits_in) ? ksplit_blocks(T, E) : generic_blocks(T);
 }
 
-int route_max_parts(int T) {
-  const int a = fast_blocks(T), b = generic_blocks(T);
+int route_max_parts(int T, int E) {
+  const int a = ksplit_blocks(T, E), b = generic_blocks(T);
   return a > b ? a : b;
 }
 
-hipError_t launch_route_split(const float* w_router, int E, int d, void* wsplit, hipStream_t s) {
-  const int EP = 16 * route_expert_tiles(E);
-  const int dpad = route_padded_d(d);
-  const size_t n = (size_t)EP * dpad;
-  int blocks = (int)((n + 255) / 256);
-  if (blocks > 4096) blocks = 4096;
-  route_split_kernel<<<blocks, 256, 0, s>>>(w_router, E, EP, d, dpad, (uint16_t*)wsplit);
-  return hipGetLastError();
+template <int ET>
+static void launch_ksplit(const RouteParams& p, hipStream_t s) {
+  const int grid = ksplit_blocks(p.T, p.E);
+  switch (ksplit_mt(p.T, p.E)) {
+    case 1: route_ksplit_kernel<ET, 1><<<grid, 64 * KS_WAVES, 0, s>>>(p); break;
+    case 2: route_ksplit_kernel<ET, 2><<<grid, 64 * KS_WAVES, 0, s>>>(p); break;
+    default:
+      if constexpr (ET <= 2) route_ksplit_kernel<ET, 4><<<grid, 64 * KS_WAVES, 0, s>>>(p);
+      break;
+  }
 }
 
-template <bool BF16>
 static hipError_t launch_route_generic(const RouteParams& p, hipStream_t s) {
   const int grid = generic_blocks(p.T);
   switch (route_expert_tiles(p.E)) {
-    case 1: route_kernel<BF16, 1><<<grid, 64, 0, s>>>(p); break;
-    case 2: route_kernel<BF16, 2><<<grid, 64, 0, s>>>(p); break;
-    case 3: route_kernel<BF16, 3><<<grid, 64, 0, s>>>(p); break;
-    case 4: route_kernel<BF16, 4><<<grid, 64, 0, s>>>(p); break;
+    case 1: route_kernel<1><<<grid, 64, 0, s>>>(p); break;
+    case 2: route_kernel<2><<<grid, 64, 0, s>>>(p); break;
+    case 3: route_kernel<3><<<grid, 64, 0, s>>>(p); break;
+    case 4: route_kernel<4><<<grid, 64, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_route(const RouteParams& p, bool bf16, hipStream_t s) {
-  if (use_fast(p.E, bf16, p.logits_in != nullptr)) {
-    const int grid = fast_blocks(p.T);
-    if (route_expert_tiles(p.E) == 1) route_fast_kernel<1><<<grid, 256, 0, s>>>(p);
-    else route_fast_kernel<2><<<grid, 256, 0, s>>>(p);
+  if (use_ksplit(bf16, p.logits_in != nullptr)) {
+    switch (route_expert_tiles(p.E)) {
+      case 1: launch_ksplit<1>(p, s); break;
+      case 2: launch_ksplit<2>(p, s); break;
+      case 3: launch_ksplit<3>(p, s); break;
+      case 4: launch_ksplit<4>(p, s); break;
+      default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
   }
-  return bf16 ? launch_route_generic<true>(p, s) : launch_route_generic<false>(p, s);
+  return launch_route_generic(p, s);
 }
 
 }  // namespace moe

@@ -112,6 +112,9 @@ def test_calls_validate_before_any_launch():
     odd = ctypes.c_void_p(256 + 8)
     assert L.moe_combine(B(good), odd, fake, fake, fake, None) == 1
     assert L.moe_forward(B(good), odd, fake, None, None, fake, fake, fake, fake, None, fake, 1 << 30, None) == 1
+    # misaligned router weight (read with 16-byte loads)
+    assert L.moe_forward(B(good), fake, odd, None, None, fake, fake, fake, fake, None, fake, 1 << 30, None) == 1
+    assert L.moe_route(B(good), fake, odd, None, None, None, None, None, fake, fake, fake, 1 << 30, None) == 1
     # workspace: missing, misaligned, too small
     need = moe.workspace_bytes(_cfg())
     assert L.moe_route(B(good), fake, fake, None, None, None, None, None, fake, fake, None, need, None) == 1
