@@ -57,21 +57,13 @@ def recorded_traffic(workload: str, kernel: str):
         if line.startswith("# ") and ":" in line:
             k, v = line[2:].split(":", 1)
             rec[k.strip()] = v.strip()
+    from sparse_mixture_experts_02_amd.rocprof_summary import gemm_sources_digest
     if rec.get("grouped GEMM sources sha256") != gemm_sources_digest():
         return None
     try:
         return int(rec[f"{kernel} fetch_bytes"]) + int(rec[f"{kernel} write_bytes"])
     except KeyError:
         return None
-
-
-def gemm_sources_digest() -> str:
-    """sha256 over the grouped-GEMM kernel sources (the traffic records name the code they measured)."""
-    import hashlib
-    h = hashlib.sha256()
-    for name in ("gemm.hip", "gemm_big.hip", "gemm_stream.hip"):
-        h.update(open(os.path.join(ROOT, "sparse_mixture_experts_02_amd", "csrc", name), "rb").read())
-    return h.hexdigest()
 
 
 def cpu_baseline(w, inp, ntok: int) -> dict:

@@ -3,6 +3,7 @@
     python -m sparse_mixture_experts_02_amd.rocprof_summary stats <dir>
     python -m sparse_mixture_experts_02_amd.rocprof_summary pmc <dir> [--calib-kernel NAME --calib-bytes N]
     python -m sparse_mixture_experts_02_amd.rocprof_summary mfma <dir>
+    python -m sparse_mixture_experts_02_amd.rocprof_summary traffic <fetch_dir> <write_dir> --calib-bytes N
 
 `stats` reads the *_kernel_stats.csv that `rocprofv3 --kernel-trace --stats --output-format csv`
 writes; `pmc` reads the *_counter_collection.csv of a `rocprofv3 --pmc ... --output-format csv`
@@ -13,6 +14,10 @@ also given as a scale factor (known bytes / counted bytes) and as scaled bytes p
 mean dispatch duration, the effective clock (GRBM_GUI_ACTIVE is summed over the 8 XCDs) and the
 fraction of SIMD cycles the matrix cores were busy (SQ_VALU_MFMA_BUSY_CYCLES over
 GRBM_GUI_ACTIVE / 8 x 1024 SIMDs).
+`traffic` reads a FETCH_SIZE run and a WRITE_SIZE run (each with the calibration copy) and prints
+the calibrated bytes per dispatch of the two grouped-GEMM launches (the SiLU one as gemm1_silu,
+the other as gemm2) with a digest of the grouped-GEMM sources they measured, in the form
+bench.py reads back.
 """
 from __future__ import annotations
 
@@ -20,8 +25,21 @@ import argparse
 import collections
 import csv
 import glob
+import hashlib
 import os
 import sys
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+GEMM_SOURCES = ("gemm.hip", "gemm_big.hip", "gemm_stream.hip")
+
+
+def gemm_sources_digest() -> str:
+    """sha256 over the grouped-GEMM kernel sources (traffic records name the code they measured)."""
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _find(d: str, suffix: str) -> list:
@@ -73,8 +91,9 @@ def short(name: str, n: int = 70) -> str:
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("mode", choices=["stats", "pmc", "mfma"])
+    ap.add_argument("mode", choices=["stats", "pmc", "mfma", "traffic"])
     ap.add_argument("dir")
+    ap.add_argument("write_dir", nargs="?", default=None, help="traffic mode: the WRITE_SIZE run")
     ap.add_argument("--calib-kernel", default="AUnaryFunctor",
                     help="substring naming the calibration kernel (torch.mul by a scalar)")
     ap.add_argument("--calib-bytes", type=float, default=0.0)
@@ -100,6 +119,8 @@ def main(argv=None):
             print(f"{short(k, 72):72s} {len(ds):4d} {dur / len(ds) / 1e3:9.2f} {gui / XCDS / dur:9.2f} "
                   f"{busy / (gui / XCDS * SIMDS):9.3f}")
         return 0
+    if a.mode == "traffic":
+        return traffic(a)
     c = counters(a.dir)
     scale = {}
     if a.calib_bytes > 0:
@@ -115,6 +136,35 @@ def main(argv=None):
         mean = sum(vs) / len(vs)
         scaled = f"{mean * 1024.0 * scale[n] / 2**20:11.1f}" if n in scale else ""
         print(f"{short(k, 72):72s} {n:30s} {len(vs):4d} {mean:14.6g} {scaled}")
+    return 0
+
+
+def _calibrated_means(d: str, cname: str, calib_kernel: str, calib_bytes: float) -> dict:
+    c = counters(d)
+    vals = [v for (k, n), vs in c.items() if n == cname and calib_kernel in k for v in vs]
+    if not vals:
+        raise SystemExit(f"no calibration dispatch ({calib_kernel}) with {cname} in {d}")
+    scale = calib_bytes / (sum(vals) / len(vals) * 1024.0)
+    return {k: sum(vs) / len(vs) * 1024.0 * scale for (k, n), vs in c.items() if n == cname}, scale
+
+
+def traffic(a) -> int:
+    if not a.write_dir or a.calib_bytes <= 0:
+        raise SystemExit("traffic mode needs <fetch_dir> <write_dir> --calib-bytes N")
+    fetch, sf = _calibrated_means(a.dir, "FETCH_SIZE", a.calib_kernel, a.calib_bytes)
+    write, sw = _calibrated_means(a.write_dir, "WRITE_SIZE", a.calib_kernel, a.calib_bytes)
+    print(f"# calibration scale: FETCH_SIZE {sf:.3f}, WRITE_SIZE {sw:.3f}")
+    print(f"# grouped GEMM sources sha256: {gemm_sources_digest()}")
+    for label, flag in (("gemm1_silu", "<true>"), ("gemm2", "<false>")):
+        ks = [k for k in fetch if "gemm" in k and "tail" not in k and flag in k]
+        if len(ks) != 1:
+            continue
+        print(f"# {label} kernel: {ks[0]}")
+        print(f"# {label} fetch_bytes: {int(round(fetch[ks[0]]))}")
+        print(f"# {label} write_bytes: {int(round(write.get(ks[0], 0.0)))}")
+    print(f"{'kernel':72s} {'fetch_MiB':>10s} {'write_MiB':>10s}")
+    for k in sorted(fetch):
+        print(f"{short(k, 72):72s} {fetch[k] / 2**20:10.1f} {write.get(k, 0.0) / 2**20:10.1f}")
     return 0
 
 
