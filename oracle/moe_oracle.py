@@ -17,7 +17,9 @@ add, then an fp32 divide), because it decides an integer (the chosen experts).
 
 Readings where the pages are silent or disagree (each is listed with its reason in the design
 notes): select on the key, lowest expert index wins ties, -0.0 ties +0.0; weights are the
-softmax restricted to the selected logits; noise changes selection only; capacity keeps the
+softmax restricted to the selected logits; Gumbel noise changes selection only, additive router
+noise (the other noise mode) changes the logits themselves; padding tokens are not routed and
+are left out of the statistics; capacity keeps the
 first C assignments of an expert in (token, slot) order; a dropped slot contributes zero;
 aux losses use pre-drop counts.
 
@@ -164,30 +166,65 @@ def topk_gap(keys, k: int) -> np.ndarray:
     return kf[:, k - 1] - kf[:, k]
 
 
+def router_entropy(probs) -> np.ndarray:
+    """Per-token entropy of the router distribution, -sum_e p_e ln p_e (natural log; 0 ln 0 = 0).
+
+    P4 §3.3 monitors the router entropy next to the expert selection counts and the balance
+    loss: an entropy far below its maximum ln E means the routing has become deterministic.
+    """
+    p = np.asarray(probs, dtype=np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(p > 0.0, p * np.log(np.where(p > 0.0, p, 1.0)), 0.0)
+    return -t.sum(axis=1)
+
+
 @dataclasses.dataclass
 class Routing:
-    logits: np.ndarray      # [T, E] fp32
+    logits: np.ndarray      # [T, E] fp32 (with additive router noise when that mode is on)
     keys: np.ndarray        # [T, E] fp32
-    ids: np.ndarray         # [T, k] int32
-    weights: np.ndarray     # [T, k] fp32
-    probs: np.ndarray       # [T, E] float64
+    ids: np.ndarray         # [T, k] int32 (-1 for padding tokens)
+    weights: np.ndarray     # [T, k] fp32 (0 for padding tokens)
+    probs: np.ndarray       # [T, E] float64 (0 rows for padding tokens)
+    real: np.ndarray        # [T] bool: token takes part in routing (not padding)
+    entropy: np.ndarray     # [T] float64 router entropy (0 for padding tokens)
 
 
 def route(x=None, w_router=None, bias=None, gumbel=None, tau: float = 1.0, k: int = 2,
-          renormalize: bool = True, logits=None) -> Routing:
+          renormalize: bool = True, logits=None, noise_in_logits: bool = False,
+          token_mask=None) -> Routing:
     """Router logits -> key -> top-k -> gate weights, plus the full softmax for the aux loss.
 
-    With `logits` given, routing runs on those fp32 logits (the bias is taken as already in
-    them) instead of computing x W_r^T + b.
+    With `logits` given, routing runs on those fp32 logits (the bias, and additive noise when
+    noise_in_logits is on, are taken as already in them) instead of computing x W_r^T + b.
+
+    The noise input [T, E] enters in one of two ways. noise_in_logits=False (P2 §3.1, Gumbel
+    top-k): it perturbs the selection key only, (logits + g) / tau. noise_in_logits=True (P4
+    §3.2: Gaussian noise added to the router logits early in training, then annealed to zero;
+    the caller passes the already scaled noise): logits = fp32(logits + n), and everything
+    downstream (key, weights, probabilities, aux and entropy) uses the noisy logits.
+
+    token_mask [T] (nonzero = real token; P4 §4.1: padding tokens take no part in expert
+    selection): a padding token gets ids -1 and weights 0 in every slot, and is left out of the
+    probabilities, the entropy and the aux statistics. Its logits are still computed.
     """
     if logits is None:
         logits = router_logits(x, w_router, bias)
+        if noise_in_logits and gumbel is not None:
+            logits = np.add(_f32(logits), _f32(gumbel), dtype=np.float32)
     logits = _f32(logits)
-    keys = selection_keys(logits, gumbel, tau)
-    ids = top_k(keys, k)
-    weights = gate_weights(logits, ids, tau, renormalize)
-    probs = router_probs(logits, tau)
-    return Routing(logits, keys, ids, weights, probs)
+    T, E = logits.shape
+    real = np.ones(T, dtype=bool) if token_mask is None else (np.asarray(token_mask) != 0)
+    keys = selection_keys(logits, None if noise_in_logits else gumbel, tau)
+    ids = np.full((T, k), -1, dtype=np.int32)
+    weights = np.zeros((T, k), dtype=np.float32)
+    probs = np.zeros((T, E), dtype=np.float64)
+    entropy = np.zeros(T, dtype=np.float64)
+    if np.any(real):
+        ids[real] = top_k(keys[real], k)
+        weights[real] = gate_weights(logits[real], ids[real], tau, renormalize)
+        probs[real] = router_probs(logits[real], tau)
+        entropy[real] = router_entropy(probs[real])
+    return Routing(logits, keys, ids, weights, probs, real, entropy)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -224,7 +261,8 @@ def dispatch(ids, num_experts: int, capacity: int, x=None) -> Dispatch:
     P4 §2.4: sort the [B, K] index by expert id, count tokens per expert, split into
     per-expert segments and gather the tokens with a table lookup. P3: at most `capacity`
     assignments per expert are kept; the rest are dropped. Kept assignments of expert e fill
-    rows offsets[e] .. offsets[e] + counts[e] - 1 in token order.
+    rows offsets[e] .. offsets[e] + counts[e] - 1 in token order. An id of -1 (a padding token's
+    slot) is skipped: it is neither counted, kept nor dropped.
     """
     ids = np.asarray(ids)
     T, k = ids.shape
@@ -235,6 +273,8 @@ def dispatch(ids, num_experts: int, capacity: int, x=None) -> Dispatch:
     for t in range(T):
         for j in range(k):
             e = int(ids[t, j])
+            if e == -1:
+                continue
             if not 0 <= e < E:
                 raise ValueError("oracle dispatch: expert id out of range")
             if counts_pre[e] < capacity:
@@ -250,7 +290,7 @@ def dispatch(ids, num_experts: int, capacity: int, x=None) -> Dispatch:
     perm_token = np.full(N, -1, dtype=np.int64)
     for t in range(T):
         for j in range(k):
-            if not dropped[t, j]:
+            if pos[t, j] >= 0:
                 row = offsets[ids[t, j]] + pos[t, j]
                 row_of[t, j] = row
                 perm_token[row] = t
@@ -330,24 +370,32 @@ def combine(y, row_of, weights, storage: str, d: Optional[int] = None) -> np.nda
 # auxiliary load-balance losses  ([P4 §3.2], [P3 §3.2])
 # ---------------------------------------------------------------------------------------------
 
-def aux_loss(probs, counts_pre, k: int, coef: float):
-    """(aux_switch, aux_balance), float64.
+def aux_loss(probs, counts_pre, k: int, coef: float, real=None, entropy=None):
+    """(aux_switch, aux_balance, mean router entropy), float64, over the n real tokens.
 
-    aux_switch (P4 §3.2): coef * E * sum_i f_i * P_i with f_i = counts_pre[i] / (T k), the
+    aux_switch (P4 §3.2): coef * E * sum_i f_i * P_i with f_i = counts_pre[i] / (n k), the
     fraction of routed assignments that chose expert i, and P_i the mean router probability of
     expert i over the tokens. Uniform routing gives coef * sum_i P_i = coef.
-    aux_balance (P3 §3.2): coef * sum_i (p_i - k/E)^2 with p_i = counts_pre[i] / T, the
+    aux_balance (P3 §3.2): coef * sum_i (p_i - k/E)^2 with p_i = counts_pre[i] / n, the
     per-token probability that expert i is selected; its uniform value is k/E, so it is zero
     for perfectly uniform routing.
+    The entropy term is the mean over real tokens of the per-token router entropy (P4 §3.3).
+    Padding tokens (real == False) are left out of n, P_i and the entropy; with no real token
+    all three values are 0.
     """
     probs = np.asarray(probs, dtype=np.float64)
     T, E = probs.shape
+    real = np.ones(T, dtype=bool) if real is None else np.asarray(real, dtype=bool)
+    n = int(real.sum())
+    if n == 0:
+        return 0.0, 0.0, 0.0
     cp = np.asarray(counts_pre, dtype=np.float64)
-    P = probs.mean(axis=0)
-    f = cp / (T * k)
+    P = probs[real].sum(axis=0) / n
+    f = cp / (n * k)
     aux_switch = coef * E * float(np.sum(f * P))
-    aux_balance = coef * float(np.sum((cp / T - k / E) ** 2))
-    return aux_switch, aux_balance
+    aux_balance = coef * float(np.sum((cp / n - k / E) ** 2))
+    ent = router_entropy(probs[real]) if entropy is None else np.asarray(entropy, dtype=np.float64)[real]
+    return aux_switch, aux_balance, float(ent.sum() / n)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -367,16 +415,19 @@ class Forward:
 
 def forward(x, w_router, w1, w2, *, k: int, storage: str, bias=None, gumbel=None,
             tau: float = 1.0, capacity: Optional[int] = None, renormalize: bool = True,
-            aux_coef: float = 0.01, logits=None) -> Forward:
-    """Router -> top-k -> capacity + dispatch -> expert FFN -> weighted combine, plus aux."""
+            aux_coef: float = 0.01, logits=None, noise_in_logits: bool = False,
+            token_mask=None) -> Forward:
+    """Router -> top-k -> capacity + dispatch -> expert FFN -> weighted combine, plus aux.
+
+    aux = (aux_switch, aux_balance, mean router entropy)."""
     T = x.shape[0]
     E = w1.shape[0]
     C = T if capacity is None or capacity < 0 else capacity
-    r = route(x, w_router, bias, gumbel, tau, k, renormalize, logits)
+    r = route(x, w_router, bias, gumbel, tau, k, renormalize, logits, noise_in_logits, token_mask)
     dp = dispatch(r.ids, E, C, x)
     h, y = expert_ffn(dp.xp, dp.offsets, w1, w2, storage)
     out = combine(y, dp.row_of, r.weights, storage, d=x.shape[1])
-    aux = aux_loss(r.probs, dp.counts_pre, k, aux_coef)
+    aux = aux_loss(r.probs, dp.counts_pre, k, aux_coef, r.real, r.entropy)
     return Forward(r, dp, C, h, y, out, aux)
 
 
@@ -401,7 +452,7 @@ def forward_rows(x, w1, w2, ids, weights, dropped, token_idx, storage: str) -> n
         xt = _f64(x[t])
         acc = np.zeros(xt.shape[0], dtype=np.float64)
         for j in range(ids.shape[1]):
-            if dropped[t, j]:
+            if dropped[t, j] or ids[t, j] < 0:
                 continue
             e = int(ids[t, j])
             w1e, w2e = expert(e)

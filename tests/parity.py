@@ -158,7 +158,7 @@ def check_full(name: str, w: Workload, cfg: moe.MoEConfig, inp: dict, g: dict, s
         out_err = normwise(g["out"][sample_tokens].float().numpy(), rows)
     assert out_err <= tol, f"output normwise error {out_err}"
     # aux from the GPU's probabilities (Mode R) and the pre-cut counts
-    a_switch, a_bal = oracle.aux_loss(r.probs, dp.counts_pre, cfg.top_k, cfg.aux_coef)
+    a_switch, a_bal, _ = oracle.aux_loss(r.probs, dp.counts_pre, cfg.top_k, cfg.aux_coef)
     ga = g["aux"].numpy().astype(np.float64)
     rel = (abs(ga[0] - a_switch) / max(abs(a_switch), 1e-30), abs(ga[1] - a_bal) / max(abs(a_bal), 1e-30))
     assert rel[0] <= AUX_RTOL, f"aux_switch {ga[0]} vs {a_switch}"

@@ -374,7 +374,7 @@ def test_aux_uniform_routing():
     r = oracle.route(logits=l, k=k)
     dp = oracle.dispatch(r.ids, E, T)
     assert list(dp.counts_pre) == [T * k // E] * E
-    a_switch, a_bal = oracle.aux_loss(r.probs, dp.counts_pre, k, coef)
+    a_switch, a_bal, _ = oracle.aux_loss(r.probs, dp.counts_pre, k, coef)
     assert a_bal == 0.0
     assert abs(a_switch - coef * r.probs.mean(0).sum()) < 1e-17
     assert abs(a_switch - coef) < 1e-15
@@ -394,7 +394,7 @@ def test_aux_collapsed_routing_closed_form():
     l = np.tile(np.array([5.0, 4.0, 0.0, 0.0, 0.0, 0.0], dtype=np.float32), (T, 1))
     r = oracle.route(logits=l, k=k)
     dp = oracle.dispatch(r.ids, E, T)
-    _, a_bal = oracle.aux_loss(r.probs, dp.counts_pre, k, coef)
+    _, a_bal, _ = oracle.aux_loss(r.probs, dp.counts_pre, k, coef)
     want = coef * (k * (1 - k / E) ** 2 + (E - k) * (k / E) ** 2)
     assert abs(a_bal - want) < 1e-15
 
@@ -444,10 +444,15 @@ def test_hand_worked_4_tokens_4_experts():
          for i in range(4)]
     assert np.allclose(P, [0.2500554, 0.2614411, 0.2594867, 0.2290168], atol=1e-7)
     f = [2 / 8, 3 / 8, 2 / 8, 1 / 8]
-    a_switch, a_bal = fw.aux
+    a_switch, a_bal, ent = fw.aux
     assert abs(a_switch - 0.01 * 4 * math.fsum(fi * pi for fi, pi in zip(f, P))) < 1e-15
     assert abs(a_switch - 0.010162121) < 1e-9
     assert abs(a_bal - 0.00125) < 1e-15
+    # mean router entropy: -sum p ln p of the four tokens' softmaxes, by hand
+    H = [-math.fsum(q * math.log(q) for q in [math.exp(float(v)) / sum(math.exp(float(u)) for u in x[t])
+                                              for v in x[t]]) for t in range(4)]
+    assert abs(ent - math.fsum(H) / 4) < 1e-15
+    assert abs(H[2] - math.log(4)) < 1e-15      # token 2: four equal logits
 
 
 # ------------------------------------------------------------------------------ whole layer
@@ -460,3 +465,86 @@ def test_forward_tiny_workload_invariants():
     assert int(fw.dispatch.counts.sum()) == w.T * w.top_k
     assert fw.dispatch.n_dropped == 0
     assert np.isfinite(fw.out).all()
+
+
+# ------------------------------------------------------------------------------ router variants
+
+def _softplus(v):
+    return max(v, 0.0) + math.log1p(math.exp(-abs(v)))
+
+
+def test_entropy_closed_forms():
+    # E = 2: H = softplus(d) - d sigmoid(d), d = (a - b) / tau (a form that never takes a log of p)
+    for a, b, tau in [(0.3, -1.2, 1.0), (2.0, 2.0, 0.7), (-4.0, 5.5, 1.3), (30.0, -30.0, 1.0)]:
+        l = np.array([[a, b]], dtype=np.float32)
+        r = oracle.route(logits=l, k=1, tau=tau)
+        d = (float(np.float32(a)) - float(np.float32(b))) / float(np.float32(tau))
+        assert abs(r.entropy[0] - (_softplus(d) - d * _sigmoid(d))) < 1e-13
+    # equal logits: the maximum ln E; one expert far ahead: ~0
+    r = oracle.route(logits=np.zeros((3, 7), np.float32), k=2)
+    assert np.allclose(r.entropy, math.log(7), rtol=0, atol=1e-15)
+    l = np.array([[200.0, 0.0, 0.0, 0.0]], dtype=np.float32)
+    assert oracle.route(logits=l, k=1).entropy[0] < 1e-80
+
+
+def test_additive_noise_enters_the_logits():
+    rng = np.random.default_rng(5)
+    T, E, k = 40, 6, 2
+    x = rng.standard_normal((T, 16)).astype(np.float32)
+    wr = rng.standard_normal((E, 16)).astype(np.float32)
+    n = (0.1 * rng.standard_normal((T, E))).astype(np.float32)
+    clean = oracle.route(x, wr, k=k)
+    r = oracle.route(x, wr, gumbel=n, k=k, noise_in_logits=True, tau=0.7)
+    # the noisy logits are one fp32 add away from the clean ones
+    assert np.array_equal(r.logits, (clean.logits + n).astype(np.float32))
+    # and then routing, weights and probabilities are those of plain routing on them
+    ref = oracle.route(logits=r.logits, k=k, tau=0.7)
+    assert np.array_equal(r.ids, ref.ids) and np.array_equal(r.weights, ref.weights)
+    assert np.array_equal(r.probs, ref.probs) and np.array_equal(r.entropy, ref.entropy)
+    # zero noise changes nothing
+    z = oracle.route(x, wr, gumbel=np.zeros((T, E), np.float32), k=k, noise_in_logits=True)
+    assert np.array_equal(z.ids, clean.ids) and np.array_equal(z.weights, clean.weights)
+    # unlike selection-only (Gumbel) noise, additive noise moves the weights: a large push on
+    # expert 3 of token 0 selects it with weight ~1 in both modes, but only the additive mode
+    # gives it the weight
+    n2 = np.zeros((T, E), np.float32)
+    n2[0, 3] = 60.0
+    g = oracle.route(x, wr, gumbel=n2, k=1)
+    a = oracle.route(x, wr, gumbel=n2, k=1, noise_in_logits=True, renormalize=False)
+    assert g.ids[0, 0] == 3 and a.ids[0, 0] == 3
+    assert a.weights[0, 0] > 0.999999
+    assert abs(g.probs[0, 3] - clean.probs[0, 3]) == 0.0
+
+
+def test_padding_tokens_are_not_routed():
+    """A masked batch routes its real tokens exactly as the batch without the padding does (same
+    capacity), outputs zeros for padding, and leaves padding out of every statistic."""
+    rng = np.random.default_rng(11)
+    T, d, f, E, k = 48, 16, 24, 5, 2
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wr = rng.standard_normal((E, d)).astype(np.float32)
+    w1 = (0.3 * rng.standard_normal((E, f, d))).astype(np.float32)
+    w2 = (0.3 * rng.standard_normal((E, d, f))).astype(np.float32)
+    mask = (rng.random(T) < 0.7).astype(np.uint8)
+    mask[:3] = [0, 1, 0]
+    real = mask != 0
+    C = 13
+    full = oracle.forward(x, wr, w1, w2, k=k, storage="f32", capacity=C, token_mask=mask)
+    comp = oracle.forward(x[real], wr, w1, w2, k=k, storage="f32", capacity=C)
+    r, dp = full.routing, full.dispatch
+    assert (r.ids[~real] == -1).all() and (r.weights[~real] == 0).all()
+    assert (r.probs[~real] == 0).all() and (r.entropy[~real] == 0).all()
+    assert np.array_equal(r.ids[real], comp.routing.ids)
+    assert np.array_equal(r.weights[real], comp.routing.weights)
+    assert np.array_equal(dp.counts_pre, comp.dispatch.counts_pre)
+    assert np.array_equal(dp.counts, comp.dispatch.counts) and np.array_equal(dp.offsets, comp.dispatch.offsets)
+    assert dp.n_dropped == comp.dispatch.n_dropped
+    assert (dp.row_of[~real] == -1).all() and (dp.dropped[~real] == 0).all()
+    idx = np.flatnonzero(real)
+    assert np.array_equal(idx[comp.dispatch.perm_token], dp.perm_token)
+    assert np.array_equal(full.out[real], comp.out) and (full.out[~real] == 0).all()
+    assert np.allclose(full.aux, comp.aux, rtol=1e-14, atol=0)
+    # all padding: nothing routed, zero output, zero statistics
+    none = oracle.forward(x, wr, w1, w2, k=k, storage="f32", token_mask=np.zeros(T, np.uint8))
+    assert (none.routing.ids == -1).all() and (none.out == 0).all() and none.aux == (0.0, 0.0, 0.0)
+    assert int(none.dispatch.counts.sum()) == 0 and none.dispatch.n_dropped == 0
