@@ -107,7 +107,7 @@ def main():
     cfg = moe.config_for(w)
     ws = moe.new_workspace(cfg)
     out = torch.empty(w.T, w.d_model, dtype=cfg.torch_dtype, device="cuda")
-    aux = torch.empty(2, dtype=torch.float32, device="cuda")
+    aux = torch.empty(3, dtype=torch.float32, device="cuda")
     offsets = torch.empty(w.num_experts + 1, dtype=torch.int32, device="cuda")
     nd = torch.empty(1, dtype=torch.int32, device="cuda")
     nev = MOE_FORWARD_NUM_KERNELS + 1

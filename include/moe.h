@@ -72,13 +72,18 @@ typedef struct {
   float   aux_coef;      /* coefficient of both aux losses (P4 §2.1 uses 0.01)                 */
   moe_dtype_t act_dtype;     /* x, Xp, H, Y, out                                               */
   moe_dtype_t weight_dtype;  /* W1, W2 (must equal act_dtype)                                  */
+  int32_t noise_in_logits;   /* how the noise input enters (0 or 1):
+                                0: Gumbel top-k (P2 §3.1), it perturbs the selection key only;
+                                1: additive router noise (P4 §3.2), logits = fp32(logits + n)
+                                   and the noisy logits are used everywhere downstream         */
 } moe_config_t;
 
 /* Static text for a status code (never NULL). Host only. */
 const char* moe_status_string(moe_status_t status);
 
 /* Checks a configuration on the host; touches no GPU. Returns MOE_OK, MOE_ERR_INVALID_ARGUMENT
- * (cfg NULL, a size out of the ranges above, tau not finite and > 0, capacity < -1) or
+ * (cfg NULL, a size out of the ranges above, tau not finite and > 0, capacity < -1,
+ * renormalize or noise_in_logits not 0 or 1) or
  * MOE_ERR_UNSUPPORTED (act_dtype != weight_dtype or an unknown dtype). */
 moe_status_t moe_validate_config(const moe_config_t* cfg);
 
@@ -98,10 +103,16 @@ size_t moe_workspace_bytes(const moe_config_t* cfg);
  *   x          [T, d] act          token hidden states (ignored when logits_in != NULL)
  *   w_router   [E, d] fp32         router weight, 16-byte aligned (ignored when logits_in != NULL)
  *   bias       [E] fp32 or NULL    per-expert logit bias, added after the product
- *   gumbel     [T, E] fp32 or NULL noise; when given, key = fl32(fl32(logit + g) / tau),
- *                                  otherwise key = logit. Noise changes selection only.
+ *   noise      [T, E] fp32 or NULL noise, entering as cfg->noise_in_logits says. Mode 0 (Gumbel):
+ *                                  key = fl32(fl32(logit + g) / tau), the noise changes the
+ *                                  selection only. Mode 1 (additive): logit = fl32(logit + n)
+ *                                  (not added again to logits_in) and key = logit. Without
+ *                                  noise, key = logit.
+ *   token_mask [T] uint8 or NULL   nonzero = real token; a padding token (0) gets ids -1 and
+ *                                  weights 0 in every slot and probs_out row 0 [P4 §4.1]
  *   logits_in  [T, E] fp32 or NULL route these final logits instead of computing x W_r^T + b
- *   logits_out [T, E] fp32 or NULL the router logits (fp32 accumulation of x W_r^T, + bias)
+ *   logits_out [T, E] fp32 or NULL the router logits (fp32 accumulation of x W_r^T, + bias,
+ *                                  + additive noise in mode 1), padding tokens included
  *   probs_out  [T, E] fp32 or NULL softmax(logits / tau) over all E
  *   ids        [T, k] int32        selected experts, descending key, lowest index on ties
  *                                  (-0.0 ties +0.0)
@@ -109,9 +120,9 @@ size_t moe_workspace_bytes(const moe_config_t* cfg);
  * Workspace: per-block probability sums used by moe_forward's aux loss (unused here).
  */
 moe_status_t moe_route(const moe_config_t* cfg, const void* x, const float* w_router,
-                       const float* bias, const float* gumbel, const float* logits_in,
-                       float* logits_out, float* probs_out, int32_t* ids, float* weights,
-                       void* ws, size_t ws_bytes, hipStream_t stream);
+                       const float* bias, const float* noise, const uint8_t* token_mask,
+                       const float* logits_in, float* logits_out, float* probs_out, int32_t* ids,
+                       float* weights, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Dispatch: per-expert histogram, capacity cut, offsets and stable permutation, and the row
@@ -119,17 +130,19 @@ moe_status_t moe_route(const moe_config_t* cfg, const void* x, const float* w_ro
  * tokens per expert, split into segments, gather tokens by table lookup; [P3 §3.1] cap the
  * tokens per expert. Assignments are taken in (token, slot) order; the first C of each expert
  * are kept, the rest dropped.
- *   ids        [T, k] int32 device, each in [0, E) and distinct within a token (as moe_route
- *                                  gives; other values are not checked and give unspecified
- *                                  results)
+ *   ids        [T, k] int32 device, each in [0, E) and distinct within a token, or -1 in
+ *                                  every slot of a padding token (as moe_route gives). A -1
+ *                                  slot is neither counted, kept nor dropped (row_of -1,
+ *                                  dropped 0). Other values are not checked and give
+ *                                  unspecified results.
  *   x          [T, d] act
  *   counts_pre [E] int32           assignments per expert before the cut
  *   counts     [E] int32           kept per expert = min(counts_pre, C)
  *   offsets    [E+1] int32         exclusive scan of counts; offsets[E] = N
  *   perm_token [T*k] int32         token of row r for r < N (entries >= N untouched)
  *   row_of     [T, k] int32        row of each kept slot, -1 if dropped
- *   dropped    [T, k] uint8        1 if the slot was dropped
- *   n_dropped  [1] int32           T*k - N
+ *   dropped    [T, k] uint8        1 if the slot was dropped by the capacity cut
+ *   n_dropped  [1] int32           assignments dropped by the cut (sum of counts_pre - N)
  *   xp         [T*k, d] act        gathered rows; rows >= N untouched
  */
 moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* ids, const void* x,
@@ -164,17 +177,21 @@ moe_status_t moe_combine(const moe_config_t* cfg, const void* y, const int32_t* 
                          const float* weights, void* out, hipStream_t stream);
 
 /*
- * Auxiliary load-balance losses, aux[0] = aux_switch, aux[1] = aux_balance (device fp32):
- *   P_i = mean_t softmax(logits_t / tau)_i   (from probs when given, else from logits)
- *   aux_switch  = coef * E * sum_i (counts_pre[i] / (T k)) * P_i            [P4 §3.2]
- *   aux_balance = coef * sum_i (counts_pre[i] / T - k / E)^2                [P3 §3.2]
- * aux_switch is coef for uniform routing; aux_balance is 0 for perfectly uniform counts.
+ * Auxiliary load-balance losses and the router entropy over the n real tokens (n = T without a
+ * mask), aux[0] = aux_switch, aux[1] = aux_balance, aux[2] = mean router entropy (device fp32):
+ *   P_i = (1/n) sum_t softmax(logits_t / tau)_i  (from probs when given, else from logits)
+ *   aux_switch  = coef * E * sum_i (counts_pre[i] / (n k)) * P_i            [P4 §3.2]
+ *   aux_balance = coef * sum_i (counts_pre[i] / n - k / E)^2                [P3 §3.2]
+ *   entropy     = (1/n) sum_t -sum_i p_ti ln p_ti                            [P4 §3.3]
+ * aux_switch is coef for uniform routing; aux_balance is 0 for perfectly uniform counts. With
+ * no real token all three are 0.
  *   probs [T, E] fp32 or NULL, logits [T, E] fp32 (used when probs is NULL),
- *   counts_pre [E] int32 (pre-capacity counts from moe_dispatch).
+ *   token_mask [T] uint8 or NULL (padding tokens, 0, are left out),
+ *   counts_pre [E] int32 (pre-capacity counts from moe_dispatch), aux [3] fp32.
  */
 moe_status_t moe_aux_loss(const moe_config_t* cfg, const float* probs, const float* logits,
-                          const int32_t* counts_pre, float* aux, void* ws, size_t ws_bytes,
-                          hipStream_t stream);
+                          const uint8_t* token_mask, const int32_t* counts_pre, float* aux,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Optional outputs and timing hooks of moe_forward. Every pointer may be NULL; a non-NULL
@@ -207,14 +224,15 @@ typedef struct {
 } moe_debug_outputs;
 
 /*
- * The whole layer: route -> dispatch -> expert FFN -> combine, plus both aux losses
- * (P4 §2.4 and §3.2, P2 §3.1, P3 §3.1-3.2). Inputs as in the calls above; out [T, d] act;
- * aux [2] fp32 device. dbg may be NULL.
+ * The whole layer: route -> dispatch -> expert FFN -> combine, plus both aux losses and the
+ * router entropy (P4 §2.4, §3.2, §3.3 and §4.1, P2 §3.1, P3 §3.1-3.2). Inputs as in the calls
+ * above; out [T, d] act (zero rows for padding tokens); aux [3] fp32 device as moe_aux_loss.
+ * dbg may be NULL.
  */
 moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_router,
-                         const float* bias, const float* gumbel, const void* w1, const void* w2,
-                         void* out, float* aux, moe_debug_outputs* dbg, void* ws, size_t ws_bytes,
-                         hipStream_t stream);
+                         const float* bias, const float* noise, const uint8_t* token_mask,
+                         const void* w1, const void* w2, void* out, float* aux,
+                         moe_debug_outputs* dbg, void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -44,7 +44,7 @@ class _Config(ctypes.Structure):
                 ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("capacity", ctypes.c_int32),
                 ("temperature", ctypes.c_float), ("renormalize", ctypes.c_int32),
                 ("aux_coef", ctypes.c_float), ("act_dtype", ctypes.c_int32),
-                ("weight_dtype", ctypes.c_int32)]
+                ("weight_dtype", ctypes.c_int32), ("noise_in_logits", ctypes.c_int32)]
 
 
 class _Debug(ctypes.Structure):
@@ -67,13 +67,14 @@ class MoEConfig:
     aux_coef: float = 0.01
     dtype: str = "bf16"          # "bf16" or "f32" (activations and expert weights)
     weight_dtype: Optional[str] = None   # defaults to dtype
+    noise_in_logits: bool = False        # the noise input: Gumbel key noise (False) or additive logit noise
 
     def to_c(self) -> _Config:
         dt = {"f32": MOE_F32, "bf16": MOE_BF16}
         wd = self.weight_dtype or self.dtype
         return _Config(self.T, self.d_model, self.d_ffn, self.num_experts, self.top_k, self.capacity,
                        self.temperature, int(self.renormalize), self.aux_coef, dt.get(self.dtype, 99),
-                       dt.get(wd, 99))
+                       dt.get(wd, 99), int(self.noise_in_logits))
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -102,7 +103,7 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_bytes.restype = sz
         L.moe_workspace_bytes.argtypes = [cfgp]
         L.moe_route.restype = ctypes.c_int
-        L.moe_route.argtypes = [cfgp] + [vp] * 9 + [vp, sz, vp]
+        L.moe_route.argtypes = [cfgp] + [vp] * 10 + [vp, sz, vp]
         L.moe_dispatch.restype = ctypes.c_int
         L.moe_dispatch.argtypes = [cfgp] + [vp] * 10 + [vp, sz, vp]
         L.moe_expert_ffn.restype = ctypes.c_int
@@ -110,9 +111,9 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.restype = ctypes.c_int
         L.moe_combine.argtypes = [cfgp] + [vp] * 4 + [vp]
         L.moe_aux_loss.restype = ctypes.c_int
-        L.moe_aux_loss.argtypes = [cfgp] + [vp] * 4 + [vp, sz, vp]
+        L.moe_aux_loss.argtypes = [cfgp] + [vp] * 5 + [vp, sz, vp]
         L.moe_forward.restype = ctypes.c_int
-        L.moe_forward.argtypes = [cfgp] + [vp] * 8 + [ctypes.POINTER(_Debug), vp, sz, vp]
+        L.moe_forward.argtypes = [cfgp] + [vp] * 9 + [ctypes.POINTER(_Debug), vp, sz, vp]
         _lib = L
     return _lib
 
@@ -169,8 +170,10 @@ def _check(func: str, status: int):
         raise MoEError(func, status)
 
 
-def moe_route(cfg: MoEConfig, x, w_router, ids, weights, ws, *, bias=None, gumbel=None, logits_in=None,
-              logits_out=None, probs_out=None):
+def moe_route(cfg: MoEConfig, x, w_router, ids, weights, ws, *, bias=None, gumbel=None, token_mask=None,
+              logits_in=None, logits_out=None, probs_out=None):
+    """`gumbel` is the noise input (Gumbel key noise, or additive logit noise with
+    cfg.noise_in_logits); `token_mask` a [T] uint8 tensor, 0 marking padding tokens."""
     T, d, E, k = cfg.T, cfg.d_model, cfg.num_experts, cfg.top_k
     c = cfg.to_c()
     st = lib().moe_route(
@@ -178,6 +181,7 @@ def moe_route(cfg: MoEConfig, x, w_router, ids, weights, ws, *, bias=None, gumbe
         _ptr(x, "x", (T, d), cfg.torch_dtype) if logits_in is None else _ptr(x, "x"),
         _ptr(w_router, "w_router", (E, d), torch.float32) if logits_in is None else _ptr(w_router, "w_router"),
         _ptr(bias, "bias", (E,), torch.float32), _ptr(gumbel, "gumbel", (T, E), torch.float32),
+        _ptr(token_mask, "token_mask", (T,), torch.uint8),
         _ptr(logits_in, "logits_in", (T, E), torch.float32), _ptr(logits_out, "logits_out", (T, E), torch.float32),
         _ptr(probs_out, "probs_out", (T, E), torch.float32), _ptr(ids, "ids", (T, k), torch.int32),
         _ptr(weights, "weights", (T, k), torch.float32), _ptr(ws, "ws"), ws.numel(), _stream())
@@ -219,17 +223,18 @@ def moe_combine(cfg: MoEConfig, y, row_of, weights, out):
     _check("moe_combine", st)
 
 
-def moe_aux_loss(cfg: MoEConfig, counts_pre, aux, ws, *, probs=None, logits=None):
+def moe_aux_loss(cfg: MoEConfig, counts_pre, aux, ws, *, probs=None, logits=None, token_mask=None):
     T, E = cfg.T, cfg.num_experts
     c = cfg.to_c()
     st = lib().moe_aux_loss(ctypes.byref(c), _ptr(probs, "probs", (T, E), torch.float32),
                             _ptr(logits, "logits", (T, E), torch.float32),
-                            _ptr(counts_pre, "counts_pre", (E,), torch.int32), _ptr(aux, "aux", (2,), torch.float32),
+                            _ptr(token_mask, "token_mask", (T,), torch.uint8),
+                            _ptr(counts_pre, "counts_pre", (E,), torch.int32), _ptr(aux, "aux", (3,), torch.float32),
                             _ptr(ws, "ws"), ws.numel(), _stream())
     _check("moe_aux_loss", st)
 
 
-def moe_forward(cfg: MoEConfig, x, w_router, w1, w2, out, aux, ws, *, bias=None, gumbel=None,
+def moe_forward(cfg: MoEConfig, x, w_router, w1, w2, out, aux, ws, *, bias=None, gumbel=None, token_mask=None,
                 debug: Optional[dict] = None, events=None):
     """The whole layer. `debug` maps moe_debug_outputs field names to GPU tensors that receive
     those intermediates; `events` is a HipEvents object whose events are recorded between the
@@ -250,8 +255,9 @@ def moe_forward(cfg: MoEConfig, x, w_router, w1, w2, out, aux, ws, *, bias=None,
     st = lib().moe_forward(
         ctypes.byref(c), _ptr(x, "x", (T, d), dt), _ptr(w_router, "w_router", (E, d), torch.float32),
         _ptr(bias, "bias", (E,), torch.float32), _ptr(gumbel, "gumbel", (T, E), torch.float32),
+        _ptr(token_mask, "token_mask", (T,), torch.uint8),
         _ptr(w1, "w1", (E, f, d), dt), _ptr(w2, "w2", (E, d, f), dt), _ptr(out, "out", (T, d), dt),
-        _ptr(aux, "aux", (2,), torch.float32), ctypes.byref(dbg) if dbg is not None else None,
+        _ptr(aux, "aux", (3,), torch.float32), ctypes.byref(dbg) if dbg is not None else None,
         _ptr(ws, "ws"), ws.numel(), _stream())
     _check("moe_forward", st)
 

@@ -144,6 +144,8 @@ constexpr int PROBSUM_TOKENS = 256;  // tokens per block of the stand-alone prob
 // time; partial sums are combined in LDS in a fixed order.
 __global__ __launch_bounds__(256) void probsum_kernel(ProbSumParams p) {
   __shared__ double part[256];
+  __shared__ double hpart[256];
+  __shared__ double cpart[256];
   const int tid = threadIdx.x;
   const int E = p.E;
   int EPAD = 1;
@@ -153,11 +155,20 @@ __global__ __launch_bounds__(256) void probsum_kernel(ProbSumParams p) {
   const int nsub = 256 / EPAD;
   const int t0 = blockIdx.x * PROBSUM_TOKENS;
   const int t1 = min(p.T, t0 + PROBSUM_TOKENS);
-  double acc = 0.0;
+  double acc = 0.0, hacc = 0.0, cacc = 0.0;
   for (int t = t0 + sub; t < t1; t += nsub) {
+    if (p.token_mask && p.token_mask[t] == 0) continue;   // padding: left out
     float prob = 0.0f;
     if (p.probs) {
       prob = (e < E) ? p.probs[(size_t)t * E + e] : 0.0f;
+      if (e == 0) {   // entropy of the row, -sum p ln p (0 ln 0 = 0)
+        float h = 0.0f;
+        for (int q = 0; q < E; ++q) {
+          const float v = p.probs[(size_t)t * E + q];
+          if (v > 0.0f) h = __fsub_rn(h, v * logf(v));
+        }
+        hacc += (double)h;
+      }
     } else {
       const float* row = p.logits + (size_t)t * E;
       float mx = -INFINITY;
@@ -165,15 +176,32 @@ __global__ __launch_bounds__(256) void probsum_kernel(ProbSumParams p) {
       float s = 0.0f;
       for (int q = 0; q < E; ++q) s = __fadd_rn(s, expf(__fdiv_rn(__fsub_rn(row[q], mx), p.tau)));
       prob = (e < E) ? __fdiv_rn(expf(__fdiv_rn(__fsub_rn(row[e], mx), p.tau)), s) : 0.0f;
+      if (e == 0) {   // entropy = ln s - sum p z, z = (L - max) / tau
+        float pz = 0.0f;
+        for (int q = 0; q < E; ++q) {
+          const float z = __fdiv_rn(__fsub_rn(row[q], mx), p.tau);
+          pz = __fadd_rn(pz, __fdiv_rn(expf(z), s) * z);
+        }
+        hacc += (double)__fsub_rn(logf(s), pz);
+      }
     }
     acc += (double)prob;
+    if (e == 0) cacc += 1.0;
   }
   part[tid] = acc;
+  hpart[tid] = hacc;
+  cpart[tid] = cacc;
   __syncthreads();
+  double* out = p.psum + (size_t)blockIdx.x * (E + 2);
   if (tid < E) {
     double s = 0.0;
     for (int q = 0; q < nsub; ++q) s += part[q * EPAD + tid];
-    p.psum[(size_t)blockIdx.x * E + tid] = s;
+    out[tid] = s;
+  } else if (tid == E || tid == E + 1) {
+    const double* src = (tid == E) ? hpart : cpart;
+    double s = 0.0;
+    for (int q = 0; q < nsub; ++q) s += src[q * EPAD];
+    out[tid] = s;
   }
 }
 

@@ -131,45 +131,53 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
 // order, so the result does not depend on timing.
 __device__ __forceinline__ void aux_block(const AuxParams& p, const int* counts_pre) {
   __shared__ double part[256];
-  __shared__ double P[MOE_MAX_EXPERTS_DEV];
+  __shared__ double S[MOE_MAX_EXPERTS_DEV + 2];
   const int tid = threadIdx.x;
   const int E = p.E;
-  int EPAD = 1;
-  while (EPAD < E) EPAD <<= 1;
-  const int e = tid % EPAD;
-  const int sub = tid / EPAD;
-  const int nsub = 256 / EPAD;
+  const int C = E + 2;   // columns of a statistics row: E probability sums, entropy, count
+  int CPAD = 1;
+  while (CPAD < C) CPAD <<= 1;
+  const int c = tid % CPAD;
+  const int sub = tid / CPAD;
+  const int nsub = 256 / CPAD;
   double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-  if (e < E) {
+  if (c < C) {
     int q = sub;
     for (; q + 3 * nsub < p.nparts; q += 4 * nsub) {
-      a0 += p.psum[(size_t)q * E + e];
-      a1 += p.psum[(size_t)(q + nsub) * E + e];
-      a2 += p.psum[(size_t)(q + 2 * nsub) * E + e];
-      a3 += p.psum[(size_t)(q + 3 * nsub) * E + e];
+      a0 += p.psum[(size_t)q * C + c];
+      a1 += p.psum[(size_t)(q + nsub) * C + c];
+      a2 += p.psum[(size_t)(q + 2 * nsub) * C + c];
+      a3 += p.psum[(size_t)(q + 3 * nsub) * C + c];
     }
-    for (; q < p.nparts; q += nsub) a0 += p.psum[(size_t)q * E + e];
+    for (; q < p.nparts; q += nsub) a0 += p.psum[(size_t)q * C + c];
   }
   part[tid] = (a0 + a1) + (a2 + a3);
   __syncthreads();
-  if (tid < E) {
+  if (tid < C) {
     double s = 0.0;
-    for (int q = 0; q < nsub; ++q) s += part[q * EPAD + tid];
-    P[tid] = s / (double)p.T;
+    for (int q = 0; q < nsub; ++q) s += part[q * CPAD + tid];
+    S[tid] = s;
   }
   __syncthreads();
   if (tid == 0) {
-    double sw = 0.0, sb = 0.0;
-    const double tk = (double)p.T * (double)p.k;
-    const double uni = (double)p.k / (double)E;
-    for (int q = 0; q < E; ++q) {
-      const double c = (double)counts_pre[q];
-      sw += (c / tk) * P[q];
-      const double dv = c / (double)p.T - uni;
-      sb += dv * dv;
+    const double n = S[E + 1];   // real tokens (an exact integer)
+    double sw = 0.0, sb = 0.0, ent = 0.0;
+    if (n > 0.0) {
+      const double nk = n * (double)p.k;
+      const double uni = (double)p.k / (double)E;
+      for (int q = 0; q < E; ++q) {
+        const double cq = (double)counts_pre[q];
+        sw += (cq / nk) * (S[q] / n);
+        const double dv = cq / n - uni;
+        sb += dv * dv;
+      }
+      sw *= (double)p.coef * (double)E;
+      sb *= (double)p.coef;
+      ent = S[E] / n;
     }
-    p.aux[0] = (float)((double)p.coef * (double)E * sw);
-    p.aux[1] = (float)((double)p.coef * sb);
+    p.aux[0] = (float)sw;
+    p.aux[1] = (float)sb;
+    p.aux[2] = (float)ent;
   }
 }
 
@@ -206,13 +214,13 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
     const int e = p.ids[i];
     bool keep = false;
     int rank = 0;
-    if (e >= 0 && e < p.E) {   // an out-of-range id is treated as dropped
+    if (e >= 0 && e < p.E) {   // an id outside [0, E) (a padding token's -1) has no row
       rank = p.blk_base[(size_t)(i / DISPATCH_CHUNK) * p.E + e] + p.rank_local[i];
       keep = p.capacity < 0 || rank < p.capacity;
     }
     row = keep ? p.offsets[e] + rank : -1;
     p.row_of[i] = row;
-    p.dropped[i] = keep ? 0 : 1;
+    p.dropped[i] = (e >= 0 && e < p.E && !keep) ? 1 : 0;   // a -1 slot (padding) is not dropped
     if (keep) p.perm_token[row] = t;
   }
   int rows[MOE_MAX_TOP_K_DEV];

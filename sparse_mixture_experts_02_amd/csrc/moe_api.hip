@@ -32,12 +32,12 @@ Layout layout(const moe_config_t& c) {
   };
   const size_t T = (size_t)c.T, k = (size_t)c.top_k, E = (size_t)c.num_experts;
   const size_t d = (size_t)c.d_model, f = (size_t)c.d_ffn, TK = T * k, a = act_size(c);
-  L.psum = take((size_t)route_max_parts(c.T, c.num_experts) * E * sizeof(double));
+  L.psum = take((size_t)route_max_parts(c.T, c.num_experts) * (E + 2) * sizeof(double));
   const size_t nb = (size_t)dispatch_num_blocks((int)TK);
   L.blk_hist = take(nb * E * 4);
   L.blk_base = take(nb * E * 4);
   L.rank_local = take(TK * 4);
-  L.probsum = take((size_t)probsum_num_blocks(c.T) * E * sizeof(double));
+  L.probsum = take((size_t)probsum_num_blocks(c.T) * (E + 2) * sizeof(double));
   L.logits = take(T * E * 4);
   L.ids = take(TK * 4);
   L.weights = take(TK * 4);
@@ -84,8 +84,9 @@ int capacity_of(const moe_config_t& c) { return c.capacity < 0 ? -1 : c.capacity
 // ---- the kernel sequences, shared by the single-step calls and moe_forward
 
 moe_status_t run_route(const moe_config_t& c, const void* x, const float* w_router, const float* bias,
-                       const float* gumbel, const float* logits_in, float* logits_out, float* probs_out,
-                       int32_t* ids, float* weights, double* psum, hipStream_t s) {
+                       const float* noise, const uint8_t* token_mask, const float* logits_in,
+                       float* logits_out, float* probs_out, int32_t* ids, float* weights, double* psum,
+                       hipStream_t s) {
   RouteParams p{};
   p.T = c.T;
   p.d = c.d_model;
@@ -96,7 +97,9 @@ moe_status_t run_route(const moe_config_t& c, const void* x, const float* w_rout
   p.x = x;
   p.w_router = w_router;
   p.bias = logits_in ? nullptr : bias;
-  p.gumbel = gumbel;
+  p.gumbel = noise;
+  p.noise_in_logits = c.noise_in_logits;
+  p.token_mask = token_mask;
   p.logits_in = logits_in;
   p.logits_out = logits_out;
   p.probs_out = probs_out;
@@ -246,6 +249,7 @@ moe_status_t moe_validate_config(const moe_config_t* c) {
   if (c->capacity < MOE_NO_CAPACITY) return MOE_ERR_INVALID_ARGUMENT;
   if (!(isfinite(c->temperature) && c->temperature > 0.0f)) return MOE_ERR_INVALID_ARGUMENT;
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->noise_in_logits != 0 && c->noise_in_logits != 1) return MOE_ERR_INVALID_ARGUMENT;
   if (!isfinite(c->aux_coef)) return MOE_ERR_INVALID_ARGUMENT;
   const bool dt_ok = (c->act_dtype == MOE_F32 || c->act_dtype == MOE_BF16) &&
                      (c->weight_dtype == MOE_F32 || c->weight_dtype == MOE_BF16);
@@ -268,13 +272,14 @@ size_t moe_workspace_bytes(const moe_config_t* cfg) {
 }
 
 moe_status_t moe_route(const moe_config_t* cfg, const void* x, const float* w_router, const float* bias,
-                       const float* gumbel, const float* logits_in, float* logits_out, float* probs_out,
+                       const float* noise, const uint8_t* token_mask, const float* logits_in,
+                       float* logits_out, float* probs_out,
                        int32_t* ids, float* weights, void* ws, size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(moe_validate_config(cfg));
   if (!ids || !weights) return MOE_ERR_INVALID_ARGUMENT;
   if (!logits_in && (!x || !w_router || !aligned16(x) || !aligned16(w_router))) return MOE_ERR_INVALID_ARGUMENT;
   MOE_TRY(check_ws(cfg, ws, ws_bytes));
-  return run_route(*cfg, x, w_router, bias, gumbel, logits_in, logits_out, probs_out, ids, weights, nullptr,
+  return run_route(*cfg, x, w_router, bias, noise, token_mask, logits_in, logits_out, probs_out, ids, weights, nullptr,
                    stream);
 }
 
@@ -313,7 +318,8 @@ moe_status_t moe_combine(const moe_config_t* cfg, const void* y, const int32_t* 
 }
 
 moe_status_t moe_aux_loss(const moe_config_t* cfg, const float* probs, const float* logits,
-                          const int32_t* counts_pre, float* aux, void* ws, size_t ws_bytes, hipStream_t stream) {
+                          const uint8_t* token_mask, const int32_t* counts_pre, float* aux, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(moe_validate_config(cfg));
   if ((!probs && !logits) || !counts_pre || !aux) return MOE_ERR_INVALID_ARGUMENT;
   MOE_TRY(check_ws(cfg, ws, ws_bytes));
@@ -324,13 +330,15 @@ moe_status_t moe_aux_loss(const moe_config_t* cfg, const float* probs, const flo
   p.tau = cfg->temperature;
   p.probs = probs;
   p.logits = logits;
+  p.token_mask = token_mask;
   p.psum = (double*)at(ws, L.probsum);
   MOE_LAUNCH(launch_probsum(p, stream));
   return run_aux_final(*cfg, p.psum, probsum_num_blocks(cfg->T), counts_pre, aux, stream);
 }
 
 moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_router, const float* bias,
-                         const float* gumbel, const void* w1, const void* w2, void* out, float* aux,
+                         const float* noise, const uint8_t* token_mask, const void* w1, const void* w2,
+                         void* out, float* aux,
                          moe_debug_outputs* dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(moe_validate_config(cfg));
   if (!x || !w_router || !w1 || !w2 || !out || !aux) return MOE_ERR_INVALID_ARGUMENT;
@@ -366,7 +374,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
     return hip_status(hipEventRecord(D.events[ev++], stream));
   };
   MOE_TRY(mark());
-  MOE_TRY(run_route(c, x, w_router, bias, gumbel, nullptr, logits, probs, ids, weights, psum, stream));
+  MOE_TRY(run_route(c, x, w_router, bias, noise, token_mask, nullptr, logits, probs, ids, weights, psum, stream));
   MOE_TRY(mark());
   MOE_TRY(run_hist(c, ids, ws, stream));
   MOE_TRY(mark());

@@ -59,13 +59,15 @@ struct RouteParams {
   const void* x;            // [T, d] act
   const float* w_router;    // [E, d] fp32, 16-byte aligned
   const float* bias;        // [E] or null
-  const float* gumbel;      // [T, E] or null
+  const float* gumbel;      // [T, E] or null: Gumbel noise (selection key) or additive logit noise
+  int noise_in_logits;      // 1: the noise is added to the logits
+  const uint8_t* token_mask;   // [T] or null: 0 = padding token (not routed)
   const float* logits_in;   // [T, E] or null (skip the product)
   float* logits_out;        // [T, E] or null
   float* probs_out;         // [T, E] or null
   int32_t* ids;             // [T, k]
   float* weights;           // [T, k]
-  double* psum;             // [route_num_parts][E] per-workgroup probability sums, or null
+  double* psum;             // [route_num_parts][E + 2] per-workgroup statistics, or null
 };
 
 struct HistParams {
@@ -123,9 +125,9 @@ struct AuxParams {
   int T, E, k, nparts;
   float coef;
   float tau;
-  const double* psum;       // [nparts][E]
+  const double* psum;       // [nparts][E + 2]: probability sums, entropy sum, real-token count
   const int32_t* counts_pre;
-  float* aux;
+  float* aux;               // [3]
 };
 
 struct ScanAuxParams {
@@ -138,7 +140,8 @@ struct ProbSumParams {
   float tau;
   const float* probs;       // [T, E] or null
   const float* logits;      // [T, E] (used when probs is null)
-  double* psum;             // [gridDim][E]
+  const uint8_t* token_mask;   // [T] or null
+  double* psum;             // [gridDim][E + 2]
 };
 
 // ------------------------------------------------------------------------------ launchers

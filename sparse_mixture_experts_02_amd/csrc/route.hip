@@ -36,17 +36,34 @@ __device__ __forceinline__ uint32_t key_code(float key) {
 
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
+// Per-lane running sums for the aux statistics: the lane's probabilities of real tokens (its
+// expert column of each ET tile) and, in column 0 lanes only, the router entropy of its real
+// tokens and their count.
+template <int ET>
+struct RouteStats {
+  double p[ET];
+  double ent, cnt;
+  __device__ __forceinline__ void clear() {
+#pragma unroll
+    for (int et = 0; et < ET; ++et) p[et] = 0.0;
+    ent = 0.0;
+    cnt = 0.0;
+  }
+};
+
 // Routing of one 16-token MFMA tile whose logits (before the bias) are in acc[et]: lane l holds
-// tokens t16 + 4*(l/16) + r, r = 0..3, for expert et*16 + l%16. Adds the bias, forms the keys,
-// selects the top-k, computes the gate weights and probabilities, writes the outputs and adds
-// each lane's probabilities of valid tokens to psum_acc.
+// tokens t16 + 4*(l/16) + r, r = 0..3, for expert et*16 + l%16. Adds the bias (and the additive
+// noise in that mode), forms the keys, selects the top-k, computes the gate weights,
+// probabilities and entropy, writes the outputs and adds the statistics of real tokens to st.
+// Padding tokens (token_mask 0) are not routed: ids -1, weights 0, probabilities 0.
 template <int ET>
 __device__ __forceinline__ void finish_tile(const RouteParams& p, f32x4_t (&acc)[ET], int t16, bool add_bias,
-                                            double (&psum_acc)[ET]) {
+                                            RouteStats<ET>& st) {
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int T = p.T, E = p.E, K = p.k;
+  const bool additive = p.noise_in_logits && p.gumbel && add_bias;   // computed logits only
   if (add_bias && p.bias) {
 #pragma unroll
     for (int et = 0; et < ET; ++et) {
@@ -59,7 +76,8 @@ __device__ __forceinline__ void finish_tile(const RouteParams& p, f32x4_t (&acc)
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = t16 + 4 * grp + r;
-    const bool tok_ok = t < T;
+    const bool in_range = t < T;
+    const bool real = in_range && (!p.token_mask || p.token_mask[t] != 0);
     float L[ET];
     bool valid[ET];
     uint64_t pk[ET];
@@ -67,13 +85,16 @@ __device__ __forceinline__ void finish_tile(const RouteParams& p, f32x4_t (&acc)
 #pragma unroll
     for (int et = 0; et < ET; ++et) {
       const int e = et * 16 + col;
+      const bool ok = in_range && e < E;
       L[et] = acc[et][r];
-      valid[et] = tok_ok && e < E;
+      if (additive && ok) L[et] = __fadd_rn(L[et], p.gumbel[(size_t)t * E + e]);
+      valid[et] = real && e < E;
       slot[et] = -1;
       float key = L[et];
-      if (p.gumbel && valid[et]) key = __fdiv_rn(__fadd_rn(L[et], p.gumbel[(size_t)t * E + e]), p.tau);
+      if (p.gumbel && !p.noise_in_logits && valid[et])
+        key = __fdiv_rn(__fadd_rn(L[et], p.gumbel[(size_t)t * E + e]), p.tau);
       pk[et] = valid[et] ? (((uint64_t)key_code(key) << 8) | (uint64_t)(255 - e)) : 0ull;
-      if (valid[et] && p.logits_out) p.logits_out[(size_t)t * E + e] = L[et];
+      if (ok && p.logits_out) p.logits_out[(size_t)t * E + e] = L[et];
     }
     // k rounds of "largest remaining key": a max over the 16 lanes of the group; the low byte
     // (255 - expert) makes the lowest expert index win equal keys.
@@ -90,8 +111,8 @@ __device__ __forceinline__ void finish_tile(const RouteParams& p, f32x4_t (&acc)
           slot[et] = j;
         }
     }
-    // full softmax of logits / tau (probs, aux sums, unnormalised weights) and the softmax
-    // restricted to the selected experts (normalised weights). Exponents are formed as
+    // full softmax of logits / tau (probs, aux sums, entropy, unnormalised weights) and the
+    // softmax restricted to the selected experts (normalised weights). Exponents are formed as
     // (L - max) / tau, subtracting before scaling.
     float mx_all = -INFINITY, mx_sel = -INFINITY;
 #pragma unroll
@@ -104,11 +125,12 @@ __device__ __forceinline__ void finish_tile(const RouteParams& p, f32x4_t (&acc)
       mx_all = fmaxf(mx_all, __shfl_xor(mx_all, m));
       mx_sel = fmaxf(mx_sel, __shfl_xor(mx_sel, m));
     }
-    float ex_all[ET], ex_sel[ET];
+    float z[ET], ex_all[ET], ex_sel[ET];
     float s_all = 0.0f, s_sel = 0.0f;
 #pragma unroll
     for (int et = 0; et < ET; ++et) {
-      ex_all[et] = valid[et] ? expf(__fdiv_rn(__fsub_rn(L[et], mx_all), p.tau)) : 0.0f;
+      z[et] = valid[et] ? __fdiv_rn(__fsub_rn(L[et], mx_all), p.tau) : 0.0f;
+      ex_all[et] = valid[et] ? expf(z[et]) : 0.0f;
       ex_sel[et] = (slot[et] >= 0) ? expf(__fdiv_rn(__fsub_rn(L[et], mx_sel), p.tau)) : 0.0f;
       s_all = __fadd_rn(s_all, ex_all[et]);
       s_sel = __fadd_rn(s_sel, ex_sel[et]);
@@ -118,34 +140,61 @@ __device__ __forceinline__ void finish_tile(const RouteParams& p, f32x4_t (&acc)
       s_all = __fadd_rn(s_all, __shfl_xor(s_all, m));
       s_sel = __fadd_rn(s_sel, __shfl_xor(s_sel, m));
     }
+    // entropy -sum p ln p = ln s - sum p z, with ln p = z - ln s (no logarithm of a small p)
+    float pz = 0.0f;
 #pragma unroll
     for (int et = 0; et < ET; ++et) {
       const int e = et * 16 + col;
+      if (in_range && !real && col < K && et == 0) {   // padding token: no selection in any slot
+        p.ids[(size_t)t * K + col] = -1;
+        p.weights[(size_t)t * K + col] = 0.0f;
+      }
+      if (in_range && e < E && !real && p.probs_out) p.probs_out[(size_t)t * E + e] = 0.0f;
       if (!valid[et]) continue;
       const float prob = __fdiv_rn(ex_all[et], s_all);
+      pz = __fadd_rn(pz, prob * z[et]);
       if (p.probs_out) p.probs_out[(size_t)t * E + e] = prob;
-      psum_acc[et] += (double)prob;
+      st.p[et] += (double)prob;
       if (slot[et] >= 0) {
         const float w = p.renormalize ? __fdiv_rn(ex_sel[et], s_sel) : prob;
         p.ids[(size_t)t * K + slot[et]] = e;
         p.weights[(size_t)t * K + slot[et]] = w;
       }
     }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) pz = __fadd_rn(pz, __shfl_xor(pz, m));
+    if (real && col == 0) {
+      st.ent += (double)__fsub_rn(logf(s_all), pz);
+      st.cnt += 1.0;
+    }
   }
 }
 
-// Adds the 4 row groups of a wave (fixed order) and stores the wave's per-expert sums.
+// Row of the aux statistics of one part: [E] probability sums, entropy sum, real-token count.
+__host__ __device__ constexpr int psum_row(int E) { return E + 2; }
+
+// Adds the 4 row groups of a wave (fixed order) and stores the wave's statistics row.
 template <int ET>
-__device__ __forceinline__ void store_psum(const RouteParams& p, double (&psum_acc)[ET], int part) {
+__device__ __forceinline__ void store_psum(const RouteParams& p, RouteStats<ET>& st, int part) {
   if (!p.psum) return;
   const int lane = threadIdx.x & 63;
+  double* row = p.psum + (size_t)part * psum_row(p.E);
 #pragma unroll
   for (int et = 0; et < ET; ++et) {
-    double v = psum_acc[et];
+    double v = st.p[et];
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
     const int e = et * 16 + (lane & 15);
-    if (lane < 16 && e < p.E) p.psum[(size_t)part * p.E + e] = v;
+    if (lane < 16 && e < p.E) row[e] = v;
+  }
+  double h = st.ent, c = st.cnt;
+  h += __shfl_xor(h, 16);
+  h += __shfl_xor(h, 32);
+  c += __shfl_xor(c, 16);
+  c += __shfl_xor(c, 32);
+  if (lane == 0) {
+    row[p.E] = h;
+    row[p.E + 1] = c;
   }
 }
 
@@ -159,9 +208,8 @@ __global__ __launch_bounds__(64) void route_kernel(RouteParams p) {
   const int T = p.T, E = p.E, d = p.d;
   const int ntiles = (T + ROUTE_TILE - 1) / ROUTE_TILE;
 
-  double psum_acc[ET];
-#pragma unroll
-  for (int et = 0; et < ET; ++et) psum_acc[et] = 0.0;
+  RouteStats<ET> st;
+  st.clear();
 
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int t0 = tile * ROUTE_TILE;
@@ -201,10 +249,10 @@ __global__ __launch_bounds__(64) void route_kernel(RouteParams p) {
         }
       }
     }
-    finish_tile<ET>(p, acc[0], t0, !p.logits_in, psum_acc);
-    finish_tile<ET>(p, acc[1], t0 + 16, !p.logits_in, psum_acc);
+    finish_tile<ET>(p, acc[0], t0, !p.logits_in, st);
+    finish_tile<ET>(p, acc[1], t0 + 16, !p.logits_in, st);
   }
-  store_psum<ET>(p, psum_acc, blockIdx.x);
+  store_psum<ET>(p, st, blockIdx.x);
 }
 
 // ------------------------------------------------------------------------------ K-split kernel
@@ -247,7 +295,7 @@ __global__ __launch_bounds__(512) void route_ksplit_kernel(RouteParams p) {
   static_assert(MT <= KS_WAVES, "one finishing wave per tile");
   constexpr int NB = (ET * (MT + 2) <= 6) ? 4 : ((ET * (MT + 2) <= 12) ? 2 : 1);   // k-steps per load batch
   __shared__ f32x4_t red[KS_WAVES][MT][ET][64];
-  __shared__ double wsum[MT][ET][16];
+  __shared__ double wsum[MT][ET * 16 + 2];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = p.T, d = p.d, E = p.E;
@@ -259,9 +307,8 @@ __global__ __launch_bounds__(512) void route_ksplit_kernel(RouteParams p) {
   const uint16_t* __restrict__ X = (const uint16_t*)p.x;
   const float* __restrict__ W = p.w_router;
 
-  double psum_acc[ET];
-#pragma unroll
-  for (int et = 0; et < ET; ++et) psum_acc[et] = 0.0;
+  RouteStats<ET> st;
+  st.clear();
 
   const int ngroups = (T + 16 * MT - 1) / (16 * MT);
   for (int grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
@@ -330,7 +377,7 @@ __global__ __launch_bounds__(512) void route_ksplit_kernel(RouteParams p) {
           for (int r = 0; r < 4; ++r) s[et][r] = __fadd_rn(s[et][r], v[r]);
         }
       }
-      finish_tile<ET>(p, s, t0 + 16 * w, true, psum_acc);
+      finish_tile<ET>(p, s, t0 + 16 * w, true, st);
     }
     __syncthreads();   // red is rewritten by the next group
   }
@@ -338,21 +385,33 @@ __global__ __launch_bounds__(512) void route_ksplit_kernel(RouteParams p) {
     if (w < MT) {
 #pragma unroll
       for (int et = 0; et < ET; ++et) {
-        double v = psum_acc[et];
+        double v = st.p[et];
         v += __shfl_xor(v, 16);
         v += __shfl_xor(v, 32);
-        if (lane < 16) wsum[w][et][lane] = v;
+        if (lane < 16) wsum[w][et * 16 + lane] = v;
+      }
+      double h = st.ent, c = st.cnt;
+      h += __shfl_xor(h, 16);
+      h += __shfl_xor(h, 32);
+      c += __shfl_xor(c, 16);
+      c += __shfl_xor(c, 32);
+      if (lane == 0) {
+        wsum[w][ET * 16] = h;
+        wsum[w][ET * 16 + 1] = c;
       }
     }
     __syncthreads();
-    if (w == 0 && lane < 16) {
+    if (w == 0) {
+      double* row = p.psum + (size_t)blockIdx.x * psum_row(E);
+      for (int i = lane; i < ET * 16 + 2; i += 64) {
+        double v = wsum[0][i];
 #pragma unroll
-      for (int et = 0; et < ET; ++et) {
-        double v = wsum[0][et][lane];
-#pragma unroll
-        for (int q = 1; q < MT; ++q) v += wsum[q][et][lane];
-        const int e = et * 16 + lane;
-        if (e < E) p.psum[(size_t)blockIdx.x * E + e] = v;
+        for (int q = 1; q < MT; ++q) v += wsum[q][i];
+        if (i < ET * 16) {
+          if (i < E) row[i] = v;
+        } else {
+          row[E + (i - ET * 16)] = v;
+        }
       }
     }
   }

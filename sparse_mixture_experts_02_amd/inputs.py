@@ -43,6 +43,8 @@ class Workload:
     router_bias: bool = False
     aux_coef: float = 0.01
     renormalize: bool = True
+    router_noise: float = 0.0   # std of additive router-logit noise (0: none); excludes gumbel
+    padding: float = 0.0        # fraction of padding tokens (drawn per token; 0: no mask)
     seed: int = 0
 
     @property
@@ -80,8 +82,12 @@ def make_inputs(w: Workload) -> dict:
     """Draw the inputs of workload `w` on the CPU, in a fixed order from one seeded generator.
 
     Order: x [T,d], router weight [E,d], W1 [E,f,d], W2 [E,d,f], then (if enabled) router
-    bias [E] and Gumbel noise [T,E]. Returns CPU tensors: x/w1/w2 in the storage dtype,
-    w_router/bias/gumbel in fp32 (bias and gumbel are None when disabled).
+    bias [E], Gumbel noise [T,E], additive router noise [T,E] (standard normal times
+    router_noise), and the padding mask [T] (token t is padding when a uniform draw is below
+    `padding`). Returns CPU tensors: x/w1/w2 in the storage dtype, w_router/bias and the noise in
+    fp32, the mask in uint8 (1 = real token). The noise (Gumbel or additive: a workload has at
+    most one) is returned under "gumbel", the library's single noise input; bias, noise and mask
+    are None when disabled.
     """
     g = torch.Generator(device="cpu")
     g.manual_seed(w.seed)
@@ -99,6 +105,13 @@ def make_inputs(w: Workload) -> dict:
         tiny = 2.0 ** -53
         u = u.clamp_(tiny, 1.0 - tiny)
         gumbel = (-torch.log(-torch.log(u))).to(torch.float32)
+    if w.router_noise > 0.0:
+        if w.gumbel:
+            raise ValueError("a workload has either Gumbel or additive router noise")
+        gumbel = torch.randn(T, E, generator=g, dtype=torch.float32) * w.router_noise
+    token_mask = None
+    if w.padding > 0.0:
+        token_mask = (torch.rand(T, generator=g, dtype=torch.float64) >= w.padding).to(torch.uint8)
     st = _torch_dtype(w.dtype)
     return {
         "x": x.to(st).contiguous(),
@@ -107,13 +120,14 @@ def make_inputs(w: Workload) -> dict:
         "w2": w2.to(st).contiguous(),
         "bias": bias,
         "gumbel": gumbel,
+        "token_mask": token_mask,
     }
 
 
 def inputs_digest(inp: dict) -> str:
     """SHA-256 over the raw bytes of all input tensors (logged so runs can be compared)."""
     h = hashlib.sha256()
-    for key in ("x", "w_router", "w1", "w2", "bias", "gumbel"):
+    for key in ("x", "w_router", "w1", "w2", "bias", "gumbel", "token_mask"):
         t = inp.get(key)
         if t is None:
             h.update(b"none")

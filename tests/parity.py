@@ -53,7 +53,7 @@ def run_gpu(cfg: moe.MoEConfig, dinp: dict) -> dict:
         "h": torch.zeros(T * k, f, dtype=dt, device=dev), "y": torch.zeros(T * k, d, dtype=dt, device=dev),
     }
     out, aux = moe.forward(cfg, dinp["x"], dinp["w_router"], dinp["w1"], dinp["w2"], bias=dinp["bias"],
-                           gumbel=dinp["gumbel"], debug=dbg)
+                           gumbel=dinp["gumbel"], token_mask=dinp.get("token_mask"), debug=dbg)
     torch.cuda.synchronize()
     res = {k_: v.cpu() for k_, v in dbg.items()}
     res["out"] = out.cpu()
@@ -91,15 +91,18 @@ def check_routing_and_dispatch(w: Workload, cfg: moe.MoEConfig, inp: dict, g: di
     T, k, E = cfg.T, cfg.top_k, cfg.num_experts
     C = cfg.capacity if cfg.capacity >= 0 else T
     # Mode R: route the GPU's logits
+    mask = inp.get("token_mask")
+    mask = None if mask is None else mask.numpy()
     r = oracle.route(logits=g["logits"].numpy(), gumbel=inp["gumbel"], tau=cfg.temperature, k=k,
-                     renormalize=cfg.renormalize)
+                     renormalize=cfg.renormalize, noise_in_logits=cfg.noise_in_logits, token_mask=mask)
     assert np.array_equal(g["ids"].numpy(), r.ids), "Mode R: expert ids differ"
     w_err = float(np.max(np.abs(g["weights"].numpy().astype(np.float64) - r.weights))) if T else 0.0
     assert w_err <= W_TOL, f"Mode R: gate weights differ by {w_err}"
     probs_err = float(np.max(np.abs(g["probs"].numpy() - r.probs)))
     assert probs_err <= W_TOL, f"router probabilities differ by {probs_err}"
     # Mode E: the oracle's own logits
-    re = oracle.route(inp["x"], inp["w_router"], inp["bias"], inp["gumbel"], cfg.temperature, k, cfg.renormalize)
+    re = oracle.route(inp["x"], inp["w_router"], inp["bias"], inp["gumbel"], cfg.temperature, k, cfg.renormalize,
+                      noise_in_logits=cfg.noise_in_logits, token_mask=mask)
     l_err = float(np.max(np.abs(g["logits"].numpy().astype(np.float64) - re.logits)))
     scale = max(1.0, float(np.max(np.abs(re.logits))))
     assert l_err <= 1e-5 * scale, f"Mode E: logits differ by {l_err}"
@@ -157,12 +160,13 @@ def check_full(name: str, w: Workload, cfg: moe.MoEConfig, inp: dict, g: dict, s
                                    sample_tokens, storage)
         out_err = normwise(g["out"][sample_tokens].float().numpy(), rows)
     assert out_err <= tol, f"output normwise error {out_err}"
-    # aux from the GPU's probabilities (Mode R) and the pre-cut counts
-    a_switch, a_bal, _ = oracle.aux_loss(r.probs, dp.counts_pre, cfg.top_k, cfg.aux_coef)
+    # aux and entropy from the GPU's probabilities (Mode R) and the pre-cut counts
+    a_switch, a_bal, ent = oracle.aux_loss(r.probs, dp.counts_pre, cfg.top_k, cfg.aux_coef, r.real, r.entropy)
     ga = g["aux"].numpy().astype(np.float64)
-    rel = (abs(ga[0] - a_switch) / max(abs(a_switch), 1e-30), abs(ga[1] - a_bal) / max(abs(a_bal), 1e-30))
-    assert rel[0] <= AUX_RTOL, f"aux_switch {ga[0]} vs {a_switch}"
+    rel = tuple(abs(gv - rv) / max(abs(rv), 1e-30) for gv, rv in zip(ga, (a_switch, a_bal, ent)))
+    assert rel[0] <= AUX_RTOL or abs(ga[0] - a_switch) <= 1e-12, f"aux_switch {ga[0]} vs {a_switch}"
     assert rel[1] <= AUX_RTOL or abs(ga[1] - a_bal) <= 1e-12, f"aux_balance {ga[1]} vs {a_bal}"
+    assert rel[2] <= AUX_RTOL or abs(ga[2] - ent) <= 1e-12, f"router entropy {ga[2]} vs {ent}"
     return Report(name, l_err, nties, mism, N, dp.n_dropped, w_err, h_err, y_err, out_err, rel)
 
 

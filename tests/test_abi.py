@@ -60,6 +60,11 @@ def test_validate_rejects_bad_renormalize_flag():
     c = _cfg().to_c()
     c.renormalize = 2
     assert binding.lib().moe_validate_config(ctypes.byref(c)) == 1
+    c = _cfg().to_c()
+    c.noise_in_logits = 2
+    assert binding.lib().moe_validate_config(ctypes.byref(c)) == 1
+    c.noise_in_logits = 1
+    assert binding.lib().moe_validate_config(ctypes.byref(c)) == 0
     assert binding.lib().moe_validate_config(None) == 1
 
 
@@ -93,39 +98,53 @@ def test_calls_validate_before_any_launch():
     bad = _cfg(T=0).to_c()
     fake = ctypes.c_void_p(256)   # never dereferenced: validation fails first
     B = ctypes.byref
+    # moe_route(cfg, x, w_router, bias, noise, token_mask, logits_in, logits_out, probs_out, ids, weights, ws,
+    #           ws_bytes, stream)
+    def route(x=fake, wr=fake, ids=fake, wts=fake, ws=fake, nbytes=1 << 30, cfg=good):
+        return L.moe_route(B(cfg), x, wr, None, None, None, None, None, None, ids, wts, ws, nbytes, None)
+
+    # moe_forward(cfg, x, w_router, bias, noise, token_mask, w1, w2, out, aux, dbg, ws, ws_bytes, stream)
+    def forward(x=fake, wr=fake, w1=fake, w2=fake, out=fake, aux=fake, dbg=None, ws=fake, nbytes=1 << 30, cfg=good):
+        return L.moe_forward(B(cfg), x, wr, None, None, None, w1, w2, out, aux, dbg, ws, nbytes, None)
+
+    # moe_aux_loss(cfg, probs, logits, token_mask, counts_pre, aux, ws, ws_bytes, stream)
+    def aux_loss(probs=fake, logits=None, counts=fake, aux=fake, ws=fake, nbytes=1 << 30, cfg=good):
+        return L.moe_aux_loss(B(cfg), probs, logits, None, counts, aux, ws, nbytes, None)
+
     # invalid configuration
-    assert L.moe_route(B(bad), fake, fake, None, None, None, None, None, fake, fake, fake, 1 << 30, None) == 1
+    assert route(cfg=bad) == 1
     assert L.moe_dispatch(B(bad), *([fake] * 10), fake, 1 << 30, None) == 1
     assert L.moe_expert_ffn(B(bad), *([fake] * 6), fake, 1 << 30, None) == 1
     assert L.moe_combine(B(bad), fake, fake, fake, fake, None) == 1
-    assert L.moe_aux_loss(B(bad), fake, fake, fake, fake, fake, 1 << 30, None) == 1
-    assert L.moe_forward(B(bad), *([fake] * 8), None, fake, 1 << 30, None) == 1
+    assert aux_loss(cfg=bad) == 1
+    assert forward(cfg=bad) == 1
     # null required pointers
-    assert L.moe_route(B(good), fake, fake, None, None, None, None, None, None, fake, fake, 1 << 30, None) == 1
-    assert L.moe_route(B(good), None, None, None, None, None, None, None, fake, fake, fake, 1 << 30, None) == 1
+    assert route(ids=None) == 1
+    assert route(x=None, wr=None) == 1
     assert L.moe_dispatch(B(good), *([fake] * 9), None, fake, 1 << 30, None) == 1
     assert L.moe_expert_ffn(B(good), fake, fake, fake, None, fake, fake, fake, 1 << 30, None) == 1
     assert L.moe_combine(B(good), fake, None, fake, fake, None) == 1
-    assert L.moe_aux_loss(B(good), None, None, fake, fake, fake, 1 << 30, None) == 1
-    assert L.moe_forward(B(good), fake, fake, None, None, fake, fake, None, fake, None, fake, 1 << 30, None) == 1
+    assert aux_loss(probs=None, logits=None) == 1
+    assert forward(out=None) == 1
+    assert forward(aux=None) == 1
     # misaligned activation pointers
     odd = ctypes.c_void_p(256 + 8)
     assert L.moe_combine(B(good), odd, fake, fake, fake, None) == 1
-    assert L.moe_forward(B(good), odd, fake, None, None, fake, fake, fake, fake, None, fake, 1 << 30, None) == 1
+    assert forward(x=odd) == 1
     # misaligned router weight (read with 16-byte loads)
-    assert L.moe_forward(B(good), fake, odd, None, None, fake, fake, fake, fake, None, fake, 1 << 30, None) == 1
-    assert L.moe_route(B(good), fake, odd, None, None, None, None, None, fake, fake, fake, 1 << 30, None) == 1
+    assert forward(wr=odd) == 1
+    assert route(wr=odd) == 1
     # workspace: missing, misaligned, too small
     need = moe.workspace_bytes(_cfg())
-    assert L.moe_route(B(good), fake, fake, None, None, None, None, None, fake, fake, None, need, None) == 1
-    assert L.moe_route(B(good), fake, fake, None, None, None, None, None, fake, fake, odd, need, None) == 1
-    assert L.moe_route(B(good), fake, fake, None, None, None, None, None, fake, fake, fake, need - 1, None) == 3
+    assert route(ws=None, nbytes=need) == 1
+    assert route(ws=odd, nbytes=need) == 1
+    assert route(nbytes=need - 1) == 3
     assert L.moe_dispatch(B(good), *([fake] * 10), fake, need - 1, None) == 3
     assert L.moe_expert_ffn(B(good), *([fake] * 6), fake, 16, None) == 3
-    assert L.moe_aux_loss(B(good), fake, None, fake, fake, fake, 0, None) == 3
-    assert L.moe_forward(B(good), *([fake] * 8), None, fake, need - 1, None) == 3
+    assert aux_loss(nbytes=0) == 3
+    assert forward(nbytes=need - 1) == 3
     # too few timing events
     dbg = binding._Debug()
     dbg.events = fake
     dbg.n_events = binding.MOE_FORWARD_NUM_KERNELS
-    assert L.moe_forward(B(good), *([fake] * 8), B(dbg), fake, need, None) == 1
+    assert forward(dbg=B(dbg), nbytes=need) == 1

@@ -1,7 +1,8 @@
 """GPU parity of the HIP path against the CPU oracle, through the C ABI (needs an MI355X).
 
 Reduced sizes run every step element by element (several tiles plus ragged tails, odd expert
-counts, E up to 64, k up to 8, capacity drops, Gumbel keys, fp32 mode). The full-size workloads
+counts, E up to 64, k up to 8, capacity drops, Gumbel keys, additive router noise, padding
+tokens, fp32 mode). The full-size workloads
 check routing and dispatch exactly on every token and the layer output on sampled tokens.
 """
 import dataclasses
@@ -52,6 +53,19 @@ REDUCED = {
     "combine_top1_d512": derived(BASE, name="combine_top1_d512", T=300, d_model=512, d_ffn=256, num_experts=4,
                                  top_k=1),
     "combine_d4096": derived(BASE, name="combine_d4096", T=96, d_model=4096, d_ffn=128, num_experts=4),
+    # router variants: additive logit noise (it moves the weights and probabilities too), padding
+    # tokens (not routed, no capacity, zero output, out of the statistics), both at once in fp32,
+    # and a batch that is all padding
+    "additive_noise": derived(BASE, name="additive_noise", T=700, d_model=128, d_ffn=256, router_noise=0.1,
+                              temperature=0.8, capacity_factor=(11, 10)),
+    "padding_gumbel_capacity": derived(WORKLOADS["skewed_gumbel_capacity"], name="padding_gumbel_capacity",
+                                       T=900, d_model=128, d_ffn=192, num_experts=12, padding=0.3,
+                                       capacity_factor=(9, 10)),
+    "padding_noise_f32": derived(WORKLOADS["tiny_f32"], name="padding_noise_f32", T=300, d_model=48, d_ffn=40,
+                                 num_experts=6, top_k=3, router_noise=0.5, padding=0.25, router_bias=True),
+    "padding_e40_k4": derived(BASE, name="padding_e40_k4", T=600, d_model=64, d_ffn=96, num_experts=40, top_k=4,
+                              padding=0.5),
+    "all_padding": derived(BASE, name="all_padding", T=200, d_model=64, d_ffn=64, padding=1.0),
 }
 
 
@@ -101,10 +115,12 @@ def test_deterministic_repeat():
         assert torch.equal(a[key].view(torch.uint8), b[key].view(torch.uint8)), key
 
 
-def test_step_calls_match_forward():
+@pytest.mark.parametrize("name", ["ragged_gumbel_capacity", "padding_noise_f32", "padding_gumbel_capacity"])
+def test_step_calls_match_forward(name):
     """moe_route / moe_dispatch / moe_expert_ffn / moe_combine / moe_aux_loss called one by one
     give what moe_forward gives."""
-    w = REDUCED["ragged_gumbel_capacity"]
+    w = REDUCED[name]
+    print(f"[gpu] step calls vs forward {name}", flush=True)
     cfg = moe.config_for(w)
     dinp = to_device(make_inputs(w))
     g = run_gpu(cfg, dinp)
@@ -116,8 +132,9 @@ def test_step_calls_match_forward():
     wts = torch.empty(T, k, dtype=torch.float32, device=dev)
     logits = torch.empty(T, E, dtype=torch.float32, device=dev)
     probs = torch.empty(T, E, dtype=torch.float32, device=dev)
+    mask = dinp["token_mask"]
     moe.moe_route(cfg, dinp["x"], dinp["w_router"], ids, wts, ws, bias=dinp["bias"], gumbel=dinp["gumbel"],
-                  logits_out=logits, probs_out=probs)
+                  token_mask=mask, logits_out=logits, probs_out=probs)
     cp, cnt, off = torch.empty(E, **i32), torch.empty(E, **i32), torch.empty(E + 1, **i32)
     perm, row_of = torch.full((T * k,), -7, **i32), torch.empty(T, k, **i32)
     dropped, nd = torch.empty(T, k, dtype=torch.uint8, device=dev), torch.empty(1, **i32)
@@ -128,10 +145,10 @@ def test_step_calls_match_forward():
     moe.moe_expert_ffn(cfg, xp, off, dinp["w1"], dinp["w2"], h, y, ws)
     out = torch.empty(T, d, dtype=dt, device=dev)
     moe.moe_combine(cfg, y, row_of, wts, out)
-    aux = torch.empty(2, dtype=torch.float32, device=dev)
-    moe.moe_aux_loss(cfg, cp, aux, ws, probs=probs)
-    aux2 = torch.empty(2, dtype=torch.float32, device=dev)
-    moe.moe_aux_loss(cfg, cp, aux2, ws, logits=logits)
+    aux = torch.empty(3, dtype=torch.float32, device=dev)
+    moe.moe_aux_loss(cfg, cp, aux, ws, probs=probs, token_mask=mask)
+    aux2 = torch.empty(3, dtype=torch.float32, device=dev)
+    moe.moe_aux_loss(cfg, cp, aux2, ws, logits=logits, token_mask=mask)
     torch.cuda.synchronize()
     for name, t in [("ids", ids), ("weights", wts), ("logits", logits), ("probs", probs), ("counts_pre", cp),
                     ("counts", cnt), ("offsets", off), ("perm_token", perm), ("row_of", row_of),
@@ -139,8 +156,8 @@ def test_step_calls_match_forward():
         assert torch.equal(t.cpu(), g[name]), name
     assert torch.equal(out.cpu(), g["out"])
     ga = g["aux"].double()
-    assert torch.allclose(aux.cpu().double(), ga, rtol=1e-5, atol=0)
-    assert torch.allclose(aux2.cpu().double(), ga, rtol=1e-5, atol=0)
+    assert torch.allclose(aux.cpu().double(), ga, rtol=1e-5, atol=1e-12)
+    assert torch.allclose(aux2.cpu().double(), ga, rtol=1e-5, atol=1e-12)
 
 
 def test_route_given_logits_mode_r_hook():
