@@ -346,12 +346,26 @@ def expert_ffn(xp, offsets, w1, w2, storage: str):
     return h, y
 
 
-def combine(y, row_of, weights, storage: str, d: Optional[int] = None) -> np.ndarray:
-    """out[t] = sum over kept slots j (ascending) of w[t, j] * Y[row_of[t, j]], rounded once.
+def shared_ffn(x, w1s, w2s, storage: str):
+    """The shared expert on every token: Hs = SiLU(x W1s^T), Ys = Hs W2s^T.
+
+    P4 §5.2: shared experts are fixed experts that join every token's computation. They are
+    FFNs of the same two-layer form as the routed experts (W1s [fs, d], W2s [d, fs]); several
+    shared experts of width f are one of width n f. Hs and Ys are rounded to the storage dtype
+    like H and Y. Returns float64 arrays (Hs [T, fs], Ys [T, d]).
+    """
+    hs = round_storage(silu(_f64(x) @ _f64(w1s).T), storage)
+    ys = round_storage(hs @ _f64(w2s).T, storage)
+    return hs, ys
+
+
+def combine(y, row_of, weights, storage: str, d: Optional[int] = None, y_shared=None) -> np.ndarray:
+    """out[t] = sum over kept slots j (ascending) of w[t, j] * Y[row_of[t, j]] (+ Ys[t]), rounded once.
 
     P4 §2.4: each token's output is the weighted sum of its chosen experts' outputs. A dropped
     slot adds nothing and the remaining weights are not rescaled; a token whose slots are all
-    dropped gets zeros.
+    dropped gets zeros. P4 §5.2: a shared expert's output Ys[t] joins every token's output, with
+    no gate weight.
     """
     y = _f64(y)
     row_of = np.asarray(row_of)
@@ -363,6 +377,8 @@ def combine(y, row_of, weights, storage: str, d: Optional[int] = None) -> np.nda
         kept = row_of[:, j] >= 0
         if np.any(kept):
             out[kept] += w[kept, j][:, None] * y[row_of[kept, j]]
+    if y_shared is not None:
+        out += _f64(y_shared)
     return round_storage(out, storage)
 
 
@@ -411,31 +427,39 @@ class Forward:
     y: np.ndarray
     out: np.ndarray
     aux: tuple
+    y_shared: Optional[np.ndarray] = None
 
 
 def forward(x, w_router, w1, w2, *, k: int, storage: str, bias=None, gumbel=None,
             tau: float = 1.0, capacity: Optional[int] = None, renormalize: bool = True,
             aux_coef: float = 0.01, logits=None, noise_in_logits: bool = False,
-            token_mask=None) -> Forward:
+            token_mask=None, w1_shared=None, w2_shared=None) -> Forward:
     """Router -> top-k -> capacity + dispatch -> expert FFN -> weighted combine, plus aux.
 
-    aux = (aux_switch, aux_balance, mean router entropy)."""
+    aux = (aux_switch, aux_balance, mean router entropy). With w1_shared / w2_shared, a shared
+    expert runs on every token (padding included: it involves no selection) and its output is
+    added in the combine."""
     T = x.shape[0]
     E = w1.shape[0]
     C = T if capacity is None or capacity < 0 else capacity
     r = route(x, w_router, bias, gumbel, tau, k, renormalize, logits, noise_in_logits, token_mask)
     dp = dispatch(r.ids, E, C, x)
     h, y = expert_ffn(dp.xp, dp.offsets, w1, w2, storage)
-    out = combine(y, dp.row_of, r.weights, storage, d=x.shape[1])
+    ys = None
+    if w1_shared is not None:
+        _, ys = shared_ffn(x, w1_shared, w2_shared, storage)
+    out = combine(y, dp.row_of, r.weights, storage, d=x.shape[1], y_shared=ys)
     aux = aux_loss(r.probs, dp.counts_pre, k, aux_coef, r.real, r.entropy)
-    return Forward(r, dp, C, h, y, out, aux)
+    return Forward(r, dp, C, h, y, out, aux, ys)
 
 
-def forward_rows(x, w1, w2, ids, weights, dropped, token_idx, storage: str) -> np.ndarray:
+def forward_rows(x, w1, w2, ids, weights, dropped, token_idx, storage: str, w1_shared=None,
+                 w2_shared=None) -> np.ndarray:
     """Output rows of selected tokens only, straight from the layer's definition.
 
-    out[t] = sum over kept j of w[t, j] * W2_e SiLU(W1_e x_t) with the storage roundings of H
-    and Y; used to check sampled tokens at full size without running the whole oracle.
+    out[t] = sum over kept j of w[t, j] * W2_e SiLU(W1_e x_t) (+ W2s SiLU(W1s x_t)) with the
+    storage roundings of H and Y; used to check sampled tokens at full size without running
+    the whole oracle.
     """
     ids = np.asarray(ids)
     w = _f64(weights)
@@ -459,5 +483,8 @@ def forward_rows(x, w1, w2, ids, weights, dropped, token_idx, storage: str) -> n
             h = round_storage(silu(w1e @ xt), storage)
             y = round_storage(w2e @ h, storage)
             acc += w[t, j] * y
+        if w1_shared is not None:
+            hs = round_storage(silu(_f64(w1_shared) @ xt), storage)
+            acc += round_storage(_f64(w2_shared) @ hs, storage)
         rows.append(round_storage(acc, storage))
     return np.stack(rows) if rows else np.zeros((0, x.shape[1]))

@@ -548,3 +548,38 @@ def test_padding_tokens_are_not_routed():
     none = oracle.forward(x, wr, w1, w2, k=k, storage="f32", token_mask=np.zeros(T, np.uint8))
     assert (none.routing.ids == -1).all() and (none.out == 0).all() and none.aux == (0.0, 0.0, 0.0)
     assert int(none.dispatch.counts.sum()) == 0 and none.dispatch.n_dropped == 0
+
+
+def test_shared_expert_brute_force_and_layer_sum():
+    """P4 §5.2: a shared expert joins every token's computation. The shared FFN against a
+    fsum triple loop; the layer with it equals the routed mixture plus its output (one rounding);
+    with every routed slot dropped (C = 0) the output is the shared FFN alone, padding included."""
+    rng = np.random.default_rng(21)
+    T, d, f, fs, E, k = 9, 6, 5, 7, 3, 2
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wr = rng.standard_normal((E, d)).astype(np.float32)
+    w1 = rng.standard_normal((E, f, d)).astype(np.float32)
+    w2 = rng.standard_normal((E, d, f)).astype(np.float32)
+    w1s = rng.standard_normal((fs, d)).astype(np.float32)
+    w2s = rng.standard_normal((d, fs)).astype(np.float32)
+    hs, ys = oracle.shared_ffn(x, w1s, w2s, "f32")
+    for t in range(T):
+        h = [float(np.float32(_silu(math.fsum(float(w1s[i, c]) * float(x[t, c]) for c in range(d)))))
+             for i in range(fs)]
+        assert np.allclose(hs[t], h, rtol=2e-7, atol=0)
+        yy = [float(np.float32(math.fsum(float(w2s[o, i]) * hs[t, i] for i in range(fs)))) for o in range(d)]
+        assert np.array_equal(ys[t], yy)
+    with_s = oracle.forward(x, wr, w1, w2, k=k, storage="f32", w1_shared=w1s, w2_shared=w2s)
+    plain = oracle.forward(x, wr, w1, w2, k=k, storage="f32")
+    ref = oracle.combine(plain.y, plain.dispatch.row_of, plain.routing.weights, "f32", d=d, y_shared=ys)
+    assert np.array_equal(with_s.out, ref)
+    # one token by hand: routed slots in order, then the shared term, one rounding
+    t = 4
+    for o in range(d):
+        terms = [float(plain.routing.weights[t, j]) * plain.y[plain.dispatch.row_of[t, j], o] for j in range(k)]
+        assert with_s.out[t, o] == float(np.float32(math.fsum(terms + [ys[t, o]])))
+    mask = np.ones(T, np.uint8)
+    mask[2] = 0
+    dropped_all = oracle.forward(x, wr, w1, w2, k=k, storage="f32", capacity=0, token_mask=mask,
+                                 w1_shared=w1s, w2_shared=w2s)
+    assert np.array_equal(dropped_all.out, ys)
