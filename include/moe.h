@@ -76,6 +76,9 @@ typedef struct {
                                 0: Gumbel top-k (P2 §3.1), it perturbs the selection key only;
                                 1: additive router noise (P4 §3.2), logits = fp32(logits + n)
                                    and the noisy logits are used everywhere downstream         */
+  int32_t d_ffn_shared;      /* fs: width of the shared expert (P4 §5.2), 0 = none, else a
+                                positive multiple of 8; moe_forward then adds
+                                W2s SiLU(W1s x) to every token's output                      */
 } moe_config_t;
 
 /* Static text for a status code (never NULL). Host only. */
@@ -167,14 +170,14 @@ moe_status_t moe_expert_ffn(const moe_config_t* cfg, const void* xp, const int32
 
 /*
  * Weighted combine (unpermute). [P4 §2.4] a token's output is the sum of its selected
- * experts' outputs weighted by the gate weights:
- *   out[t] = sum_{j = 0..k-1, row_of[t,j] >= 0} weights[t,j] * y[row_of[t,j]]
- * accumulated in fp32 in slot order, rounded once to act. A token with every slot dropped gets
- * zeros. y [T*k, d] act, row_of [T, k] int32 (entries < T*k), weights [T, k] fp32,
- * out [T, d] act.
+ * experts' outputs weighted by the gate weights, [P4 §5.2] plus a shared expert's output:
+ *   out[t] = sum_{j = 0..k-1, row_of[t,j] >= 0} weights[t,j] * y[row_of[t,j]] (+ y_shared[t])
+ * accumulated in fp32 in slot order, the shared term last, rounded once to act. A token with
+ * every slot dropped and no shared term gets zeros. y [T*k, d] act, row_of [T, k] int32
+ * (entries < T*k), weights [T, k] fp32, y_shared [T, d] act or NULL, out [T, d] act.
  */
 moe_status_t moe_combine(const moe_config_t* cfg, const void* y, const int32_t* row_of,
-                         const float* weights, void* out, hipStream_t stream);
+                         const float* weights, const void* y_shared, void* out, hipStream_t stream);
 
 /*
  * Auxiliary load-balance losses and the router entropy over the n real tokens (n = T without a
@@ -199,11 +202,11 @@ moe_status_t moe_aux_loss(const moe_config_t* cfg, const float* probs, const flo
  * non-NULL it holds n_events >= MOE_FORWARD_NUM_KERNELS + 1 created hipEvent_t; events[i] is
  * recorded on `stream` before kernel i and events[MOE_FORWARD_NUM_KERNELS] after the last, so
  * hipEventElapsedTime gives per-kernel times. Kernel order: route, dispatch-histogram,
- * dispatch-scan (with the capacity cut, and both aux losses from the pre-cut counts),
- * dispatch-gather, gemm1 (W1 + SiLU), gemm2 (W2, with the reduction of its split tail when it
- * has one), combine.
+ * dispatch-scan (with the capacity cut, and both aux losses and the entropy from the pre-cut
+ * counts), dispatch-gather, gemm1 (W1 + SiLU), gemm2 (W2, with the reduction of its split tail
+ * when it has one), shared expert (both of its GEMMs; empty without one), combine.
  */
-#define MOE_FORWARD_NUM_KERNELS 7
+#define MOE_FORWARD_NUM_KERNELS 8
 typedef struct {
   float*   logits;      /* [T, E] */
   float*   probs;       /* [T, E] */
@@ -219,20 +222,24 @@ typedef struct {
   void*    xp;          /* [T*k, d] act */
   void*    h;           /* [T*k, f] act */
   void*    y;           /* [T*k, d] act */
+  void*    y_shared;    /* [T, d] act, the shared expert's output (with d_ffn_shared > 0) */
   hipEvent_t* events;
   int32_t  n_events;
 } moe_debug_outputs;
 
 /*
- * The whole layer: route -> dispatch -> expert FFN -> combine, plus both aux losses and the
- * router entropy (P4 §2.4, §3.2, §3.3 and §4.1, P2 §3.1, P3 §3.1-3.2). Inputs as in the calls
- * above; out [T, d] act (zero rows for padding tokens); aux [3] fp32 device as moe_aux_loss.
- * dbg may be NULL.
+ * The whole layer: route -> dispatch -> expert FFN (and the shared expert) -> combine, plus both
+ * aux losses and the router entropy (P4 §2.4, §3.2, §3.3, §4.1 and §5.2, P2 §3.1, P3
+ * §3.1-3.2). Inputs as in the calls above; w1_shared [fs, d] wt and w2_shared [d, fs] wt are
+ * required when cfg->d_ffn_shared > 0 and ignored otherwise (the shared expert runs on every
+ * token, padding included). out [T, d] act (routed part zero for padding tokens); aux [3] fp32
+ * device as moe_aux_loss. dbg may be NULL.
  */
 moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_router,
                          const float* bias, const float* noise, const uint8_t* token_mask,
-                         const void* w1, const void* w2, void* out, float* aux,
-                         moe_debug_outputs* dbg, void* ws, size_t ws_bytes, hipStream_t stream);
+                         const void* w1, const void* w2, const void* w1_shared,
+                         const void* w2_shared, void* out, float* aux, moe_debug_outputs* dbg,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

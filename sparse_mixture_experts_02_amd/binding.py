@@ -20,9 +20,9 @@ MOE_OK = 0
 MOE_F32 = 0
 MOE_BF16 = 1
 MOE_NO_CAPACITY = -1
-MOE_FORWARD_NUM_KERNELS = 7
+MOE_FORWARD_NUM_KERNELS = 8
 FORWARD_KERNEL_NAMES = ("route", "dispatch_hist", "dispatch_scan_aux", "dispatch_gather", "gemm1_silu", "gemm2",
-                        "combine")
+                        "shared_ffn", "combine")
 
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
                 3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
@@ -44,13 +44,14 @@ class _Config(ctypes.Structure):
                 ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("capacity", ctypes.c_int32),
                 ("temperature", ctypes.c_float), ("renormalize", ctypes.c_int32),
                 ("aux_coef", ctypes.c_float), ("act_dtype", ctypes.c_int32),
-                ("weight_dtype", ctypes.c_int32), ("noise_in_logits", ctypes.c_int32)]
+                ("weight_dtype", ctypes.c_int32), ("noise_in_logits", ctypes.c_int32),
+                ("d_ffn_shared", ctypes.c_int32)]
 
 
 class _Debug(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("logits", "probs", "ids", "weights", "counts_pre", "counts",
                                                 "offsets", "perm_token", "row_of", "dropped", "n_dropped",
-                                                "xp", "h", "y", "events")] + [("n_events", ctypes.c_int32)]
+                                                "xp", "h", "y", "y_shared", "events")] + [("n_events", ctypes.c_int32)]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -68,13 +69,14 @@ class MoEConfig:
     dtype: str = "bf16"          # "bf16" or "f32" (activations and expert weights)
     weight_dtype: Optional[str] = None   # defaults to dtype
     noise_in_logits: bool = False        # the noise input: Gumbel key noise (False) or additive logit noise
+    d_ffn_shared: int = 0                # width of the shared expert (0: none)
 
     def to_c(self) -> _Config:
         dt = {"f32": MOE_F32, "bf16": MOE_BF16}
         wd = self.weight_dtype or self.dtype
         return _Config(self.T, self.d_model, self.d_ffn, self.num_experts, self.top_k, self.capacity,
                        self.temperature, int(self.renormalize), self.aux_coef, dt.get(self.dtype, 99),
-                       dt.get(wd, 99), int(self.noise_in_logits))
+                       dt.get(wd, 99), int(self.noise_in_logits), self.d_ffn_shared)
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -109,11 +111,11 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_ffn.restype = ctypes.c_int
         L.moe_expert_ffn.argtypes = [cfgp] + [vp] * 6 + [vp, sz, vp]
         L.moe_combine.restype = ctypes.c_int
-        L.moe_combine.argtypes = [cfgp] + [vp] * 4 + [vp]
+        L.moe_combine.argtypes = [cfgp] + [vp] * 5 + [vp]
         L.moe_aux_loss.restype = ctypes.c_int
         L.moe_aux_loss.argtypes = [cfgp] + [vp] * 5 + [vp, sz, vp]
         L.moe_forward.restype = ctypes.c_int
-        L.moe_forward.argtypes = [cfgp] + [vp] * 9 + [ctypes.POINTER(_Debug), vp, sz, vp]
+        L.moe_forward.argtypes = [cfgp] + [vp] * 11 + [ctypes.POINTER(_Debug), vp, sz, vp]
         _lib = L
     return _lib
 
@@ -213,13 +215,13 @@ def moe_expert_ffn(cfg: MoEConfig, xp, offsets, w1, w2, h, y, ws):
     _check("moe_expert_ffn", st)
 
 
-def moe_combine(cfg: MoEConfig, y, row_of, weights, out):
+def moe_combine(cfg: MoEConfig, y, row_of, weights, out, *, y_shared=None):
     T, d, k = cfg.T, cfg.d_model, cfg.top_k
     c = cfg.to_c()
     dt = cfg.torch_dtype
     st = lib().moe_combine(ctypes.byref(c), _ptr(y, "y", (T * k, d), dt), _ptr(row_of, "row_of", (T, k), torch.int32),
-                           _ptr(weights, "weights", (T, k), torch.float32), _ptr(out, "out", (T, d), dt),
-                           _stream())
+                           _ptr(weights, "weights", (T, k), torch.float32), _ptr(y_shared, "y_shared", (T, d), dt),
+                           _ptr(out, "out", (T, d), dt), _stream())
     _check("moe_combine", st)
 
 
@@ -235,7 +237,7 @@ def moe_aux_loss(cfg: MoEConfig, counts_pre, aux, ws, *, probs=None, logits=None
 
 
 def moe_forward(cfg: MoEConfig, x, w_router, w1, w2, out, aux, ws, *, bias=None, gumbel=None, token_mask=None,
-                debug: Optional[dict] = None, events=None):
+                w1_shared=None, w2_shared=None, debug: Optional[dict] = None, events=None):
     """The whole layer. `debug` maps moe_debug_outputs field names to GPU tensors that receive
     those intermediates; `events` is a HipEvents object whose events are recorded between the
     kernels."""
@@ -256,7 +258,10 @@ def moe_forward(cfg: MoEConfig, x, w_router, w1, w2, out, aux, ws, *, bias=None,
         ctypes.byref(c), _ptr(x, "x", (T, d), dt), _ptr(w_router, "w_router", (E, d), torch.float32),
         _ptr(bias, "bias", (E,), torch.float32), _ptr(gumbel, "gumbel", (T, E), torch.float32),
         _ptr(token_mask, "token_mask", (T,), torch.uint8),
-        _ptr(w1, "w1", (E, f, d), dt), _ptr(w2, "w2", (E, d, f), dt), _ptr(out, "out", (T, d), dt),
+        _ptr(w1, "w1", (E, f, d), dt), _ptr(w2, "w2", (E, d, f), dt),
+        _ptr(w1_shared, "w1_shared", (cfg.d_ffn_shared, d), dt) if cfg.d_ffn_shared else None,
+        _ptr(w2_shared, "w2_shared", (d, cfg.d_ffn_shared), dt) if cfg.d_ffn_shared else None,
+        _ptr(out, "out", (T, d), dt),
         _ptr(aux, "aux", (3,), torch.float32), ctypes.byref(dbg) if dbg is not None else None,
         _ptr(ws, "ws"), ws.numel(), _stream())
     _check("moe_forward", st)

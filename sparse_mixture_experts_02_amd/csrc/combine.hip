@@ -1,8 +1,9 @@
-// Weighted combine (unpermute) and the auxiliary load-balance losses.
+// Weighted combine (unpermute) and the probability sums of the stand-alone aux-loss call.
 //
 // [P4 §2.4] a token's output is the weighted sum of its selected experts' outputs, the weights
-// being the softmax router scores. [P4 §3.2] aux = E * sum_i f_i P_i; [P3 §3.2]
-// aux = lambda * sum_i (p_i - uniform)^2.
+// being the softmax router scores; [P4 §5.2] a shared expert's output joins every token's.
+// [P4 §3.2] the aux loss averages the router probabilities per expert; [P4 §3.3] the router
+// entropy is monitored next to it.
 #include "moe_internal.h"
 
 namespace moe {
@@ -55,6 +56,25 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] = fmaf(ws[j], v[q], acc[q]);
     }
+    if (p.y_shared) {   // the shared expert's output, weight 1, after the routed slots
+      float v[8];
+      if constexpr (BF16) {
+        const uint4 u = *(const uint4*)((const uint16_t*)p.y_shared + (size_t)t * d + c);
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[2 * q] = bf16_bits_to_f32(wd[q] & 0xFFFFu);
+          v[2 * q + 1] = bf16_bits_to_f32(wd[q] >> 16);
+        }
+      } else {
+        const float4 a = *(const float4*)((const float*)p.y_shared + (size_t)t * d + c);
+        const float4 b = *(const float4*)((const float*)p.y_shared + (size_t)t * d + c + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = __fadd_rn(acc[q], v[q]);
+    }
     if constexpr (BF16) {
       uint4 o;
       o.x = pack_bf16x2(acc[0], acc[1]);
@@ -94,12 +114,15 @@ __global__ __launch_bounds__(256) void combine_k2_kernel(CombineParams p) {
   const int nu = d >> 9;   // column steps of 512
   const u32x4_t* y0 = (const u32x4_t*)((const uint16_t*)p.y + (size_t)(r0 < 0 ? 0 : r0) * d) + lane;
   const u32x4_t* y1 = (const u32x4_t*)((const uint16_t*)p.y + (size_t)(r1 < 0 ? 0 : r1) * d) + lane;
-  u32x4_t a[MAXU], b[MAXU];
+  const bool sh = p.y_shared != nullptr;
+  const u32x4_t* ys = (const u32x4_t*)((const uint16_t*)(sh ? p.y_shared : p.y) + (size_t)(sh ? t : 0) * d) + lane;
+  u32x4_t a[MAXU], b[MAXU], c[MAXU];
 #pragma unroll
   for (int u = 0; u < MAXU; ++u) {
     if (u < nu) {
       a[u] = r0 >= 0 ? __builtin_nontemporal_load(y0 + u * 64) : u32x4_t{0u, 0u, 0u, 0u};
       b[u] = r1 >= 0 ? __builtin_nontemporal_load(y1 + u * 64) : u32x4_t{0u, 0u, 0u, 0u};
+      c[u] = sh ? __builtin_nontemporal_load(ys + u * 64) : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
   u32x4_t* out = (u32x4_t*)((uint16_t*)p.out + (size_t)t * d) + lane;
@@ -118,6 +141,10 @@ __global__ __launch_bounds__(256) void combine_k2_kernel(CombineParams p) {
         if (r1 >= 0) {
           acc[2 * q] = fmaf(w1, bf16_bits_to_f32(b[u][q] & 0xFFFFu), acc[2 * q]);
           acc[2 * q + 1] = fmaf(w1, bf16_bits_to_f32(b[u][q] >> 16), acc[2 * q + 1]);
+        }
+        if (sh) {   // the shared expert's output, weight 1, after the routed slots
+          acc[2 * q] = __fadd_rn(acc[2 * q], bf16_bits_to_f32(c[u][q] & 0xFFFFu));
+          acc[2 * q + 1] = __fadd_rn(acc[2 * q + 1], bf16_bits_to_f32(c[u][q] >> 16));
         }
       }
       const u32x4_t o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),

@@ -197,6 +197,7 @@ __global__ __launch_bounds__(256) void scan_aux_kernel(ScanAuxParams p) {
   scan_block(p.s, pre);
   __syncthreads();
   aux_block(p.a, pre);
+  if (p.shared_offsets && threadIdx.x < 2) p.shared_offsets[threadIdx.x] = threadIdx.x == 0 ? 0 : p.a.T;
 }
 
 // ------------------------------------------------------------------------------ gather

@@ -16,6 +16,7 @@ struct Layout {
   size_t psum, blk_hist, blk_base, rank_local, probsum;
   size_t logits, ids, weights, counts_pre, counts, offsets, perm, row_of, dropped, ndrop;
   size_t xp, h, y;
+  size_t hs, ys, sh_off;   // shared expert: Hs [T, fs], Ys [T, d], its segment offsets [2]
   size_t sk_part;   // partial sums of the 256 x 256 grouped GEMM's split tail (empty if unused)
   size_t total;
 };
@@ -51,9 +52,14 @@ Layout layout(const moe_config_t& c) {
   L.xp = take(TK * d * a);
   L.h = take(TK * f * a);
   L.y = take(TK * d * a);
+  const size_t fs = c.d_ffn_shared > 0 ? (size_t)c.d_ffn_shared : 0;
+  L.hs = take(T * fs * a);
+  L.ys = take(fs ? T * d * a : 0);
+  L.sh_off = take(fs ? 8 : 0);
   const bool bf16 = c.act_dtype == MOE_BF16;
   const bool big = gemm_uses_big(bf16, c.d_model, c.T * c.top_k, c.num_experts) ||
-                   gemm_uses_big(bf16, c.d_ffn, c.T * c.top_k, c.num_experts);
+                   gemm_uses_big(bf16, c.d_ffn, c.T * c.top_k, c.num_experts) ||
+                   (fs && (gemm_uses_big(bf16, c.d_model, c.T, 1) || gemm_uses_big(bf16, c.d_ffn_shared, c.T, 1)));
   L.sk_part = take(big ? gemm_big_part_bytes() : 0);
   L.total = off;
   return L;
@@ -172,14 +178,18 @@ moe_status_t run_gather(const moe_config_t& c, const int32_t* ids, const void* x
   return MOE_OK;
 }
 
+// One grouped GEMM over `experts` segments of at most `rows` rows in total (the routed experts:
+// E segments of the T k permuted rows; the shared expert: one segment of the T tokens).
 moe_status_t run_gemm(const moe_config_t& c, const void* a, const void* b, void* out, const int32_t* offsets,
-                      int n, int kdim, bool silu, void* ws, hipStream_t s) {
+                      int n, int kdim, bool silu, void* ws, hipStream_t s, int experts = -1, int rows = -1) {
+  if (experts < 0) experts = c.num_experts;
+  if (rows < 0) rows = c.T * c.top_k;
   GemmParams p{};
-  if (gemm_uses_big(c.act_dtype == MOE_BF16, kdim, c.T * c.top_k, c.num_experts)) p.sk_part = at(ws, layout(c).sk_part);
-  p.E = c.num_experts;
+  if (gemm_uses_big(c.act_dtype == MOE_BF16, kdim, rows, experts)) p.sk_part = at(ws, layout(c).sk_part);
+  p.E = experts;
   p.N = n;
   p.K = kdim;
-  p.max_rows = c.T * c.top_k;
+  p.max_rows = rows;
   p.A = a;
   p.B = b;
   p.C = out;
@@ -189,13 +199,14 @@ moe_status_t run_gemm(const moe_config_t& c, const void* a, const void* b, void*
 }
 
 moe_status_t run_combine(const moe_config_t& c, const void* y, const int32_t* row_of, const float* weights,
-                         void* out, hipStream_t s) {
+                         const void* y_shared, void* out, hipStream_t s) {
   CombineParams p{};
   p.T = c.T;
   p.d = c.d_model;
   p.k = c.top_k;
   p.max_rows = c.T * c.top_k;
   p.y = y;
+  p.y_shared = y_shared;
   p.row_of = row_of;
   p.weights = weights;
   p.out = out;
@@ -250,6 +261,7 @@ moe_status_t moe_validate_config(const moe_config_t* c) {
   if (!(isfinite(c->temperature) && c->temperature > 0.0f)) return MOE_ERR_INVALID_ARGUMENT;
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
   if (c->noise_in_logits != 0 && c->noise_in_logits != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->d_ffn_shared < 0 || c->d_ffn_shared > kMaxDim || c->d_ffn_shared % 8) return MOE_ERR_INVALID_ARGUMENT;
   if (!isfinite(c->aux_coef)) return MOE_ERR_INVALID_ARGUMENT;
   const bool dt_ok = (c->act_dtype == MOE_F32 || c->act_dtype == MOE_BF16) &&
                      (c->weight_dtype == MOE_F32 || c->weight_dtype == MOE_BF16);
@@ -310,11 +322,11 @@ moe_status_t moe_expert_ffn(const moe_config_t* cfg, const void* xp, const int32
 }
 
 moe_status_t moe_combine(const moe_config_t* cfg, const void* y, const int32_t* row_of, const float* weights,
-                         void* out, hipStream_t stream) {
+                         const void* y_shared, void* out, hipStream_t stream) {
   MOE_TRY(moe_validate_config(cfg));
   if (!y || !row_of || !weights || !out) return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned16(y) || !aligned16(out)) return MOE_ERR_INVALID_ARGUMENT;
-  return run_combine(*cfg, y, row_of, weights, out, stream);
+  if (!aligned16(y) || !aligned16(out) || (y_shared && !aligned16(y_shared))) return MOE_ERR_INVALID_ARGUMENT;
+  return run_combine(*cfg, y, row_of, weights, y_shared, out, stream);
 }
 
 moe_status_t moe_aux_loss(const moe_config_t* cfg, const float* probs, const float* logits,
@@ -338,17 +350,21 @@ moe_status_t moe_aux_loss(const moe_config_t* cfg, const float* probs, const flo
 
 moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_router, const float* bias,
                          const float* noise, const uint8_t* token_mask, const void* w1, const void* w2,
-                         void* out, float* aux,
+                         const void* w1_shared, const void* w2_shared, void* out, float* aux,
                          moe_debug_outputs* dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(moe_validate_config(cfg));
   if (!x || !w_router || !w1 || !w2 || !out || !aux) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(w1) || !aligned16(w2) || !aligned16(out))
     return MOE_ERR_INVALID_ARGUMENT;
+  const bool shared = cfg->d_ffn_shared > 0;
+  if (shared && (!w1_shared || !w2_shared || !aligned16(w1_shared) || !aligned16(w2_shared)))
+    return MOE_ERR_INVALID_ARGUMENT;
   MOE_TRY(check_ws(cfg, ws, ws_bytes));
   moe_debug_outputs none{};
   const moe_debug_outputs& D = dbg ? *dbg : none;
   if (D.events && D.n_events < MOE_FORWARD_NUM_KERNELS + 1) return MOE_ERR_INVALID_ARGUMENT;
-  if ((D.xp && !aligned16(D.xp)) || (D.h && !aligned16(D.h)) || (D.y && !aligned16(D.y)))
+  if ((D.xp && !aligned16(D.xp)) || (D.h && !aligned16(D.h)) || (D.y && !aligned16(D.y)) ||
+      (D.y_shared && !aligned16(D.y_shared)))
     return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = layout(*cfg);
   const moe_config_t& c = *cfg;
@@ -381,6 +397,8 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
   ScanAuxParams sp{};
   sp.s = scan_params(c, counts_pre, counts, offsets, ndrop, ws);
   sp.a = aux_params(c, psum, route_num_parts(c.T, c.num_experts, c.act_dtype == MOE_BF16, false), counts_pre, aux);
+  int32_t* sh_off = shared ? (int32_t*)at(ws, L.sh_off) : nullptr;
+  sp.shared_offsets = sh_off;
   MOE_LAUNCH(launch_scan_aux(sp, stream));
   MOE_TRY(mark());
   MOE_TRY(run_gather(c, ids, x, offsets, perm, row_of, dropped, xp, ws, stream));
@@ -389,7 +407,15 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
   MOE_TRY(mark());
   MOE_TRY(run_gemm(c, h, w2, y, offsets, c.d_model, c.d_ffn, false, ws, stream));
   MOE_TRY(mark());
-  MOE_TRY(run_combine(c, y, row_of, weights, out, stream));
+  void* ys = nullptr;
+  if (shared) {   // one segment of all T tokens, straight from x
+    void* hs = at(ws, L.hs);
+    ys = pick(D.y_shared, L.ys);
+    MOE_TRY(run_gemm(c, x, w1_shared, hs, sh_off, c.d_ffn_shared, c.d_model, true, ws, stream, 1, c.T));
+    MOE_TRY(run_gemm(c, hs, w2_shared, ys, sh_off, c.d_model, c.d_ffn_shared, false, ws, stream, 1, c.T));
+  }
+  MOE_TRY(mark());
+  MOE_TRY(run_combine(c, y, row_of, weights, ys, out, stream));
   MOE_TRY(mark());
   return MOE_OK;
 }

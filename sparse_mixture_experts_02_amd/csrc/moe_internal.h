@@ -116,6 +116,7 @@ struct CombineParams {
   int T, d, k;
   int max_rows;             // rows of y (T * k); a row index outside [0, max_rows) counts as dropped
   const void* y;
+  const void* y_shared;     // [T, d] act added with weight 1 after the routed slots, or null
   const int32_t* row_of;
   const float* weights;
   void* out;
@@ -133,6 +134,7 @@ struct AuxParams {
 struct ScanAuxParams {
   ScanParams s;
   AuxParams a;              // a.counts_pre is not read: the scan's own pre-cut counts are used
+  int32_t* shared_offsets;  // [2] set to {0, T} (the shared expert's one segment), or null
 };
 
 struct ProbSumParams {

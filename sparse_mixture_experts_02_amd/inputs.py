@@ -45,6 +45,7 @@ class Workload:
     renormalize: bool = True
     router_noise: float = 0.0   # std of additive router-logit noise (0: none); excludes gumbel
     padding: float = 0.0        # fraction of padding tokens (drawn per token; 0: no mask)
+    d_ffn_shared: int = 0       # width of the shared expert (0: none)
     seed: int = 0
 
     @property
@@ -84,7 +85,8 @@ def make_inputs(w: Workload) -> dict:
     Order: x [T,d], router weight [E,d], W1 [E,f,d], W2 [E,d,f], then (if enabled) router
     bias [E], Gumbel noise [T,E], additive router noise [T,E] (standard normal times
     router_noise), and the padding mask [T] (token t is padding when a uniform draw is below
-    `padding`). Returns CPU tensors: x/w1/w2 in the storage dtype, w_router/bias and the noise in
+    `padding`), then the shared expert W1s [fs,d] and W2s [d,fs] (0.02 std, as the routed
+    experts). Returns CPU tensors: x/w1/w2 in the storage dtype, w_router/bias and the noise in
     fp32, the mask in uint8 (1 = real token). The noise (Gumbel or additive: a workload has at
     most one) is returned under "gumbel", the library's single noise input; bias, noise and mask
     are None when disabled.
@@ -112,6 +114,10 @@ def make_inputs(w: Workload) -> dict:
     token_mask = None
     if w.padding > 0.0:
         token_mask = (torch.rand(T, generator=g, dtype=torch.float64) >= w.padding).to(torch.uint8)
+    w1s = w2s = None
+    if w.d_ffn_shared > 0:
+        w1s = torch.randn(w.d_ffn_shared, d, generator=g, dtype=torch.float32) * 0.02
+        w2s = torch.randn(d, w.d_ffn_shared, generator=g, dtype=torch.float32) * 0.02
     st = _torch_dtype(w.dtype)
     return {
         "x": x.to(st).contiguous(),
@@ -121,13 +127,15 @@ def make_inputs(w: Workload) -> dict:
         "bias": bias,
         "gumbel": gumbel,
         "token_mask": token_mask,
+        "w1_shared": None if w1s is None else w1s.to(st).contiguous(),
+        "w2_shared": None if w2s is None else w2s.to(st).contiguous(),
     }
 
 
 def inputs_digest(inp: dict) -> str:
     """SHA-256 over the raw bytes of all input tensors (logged so runs can be compared)."""
     h = hashlib.sha256()
-    for key in ("x", "w_router", "w1", "w2", "bias", "gumbel", "token_mask"):
+    for key in ("x", "w_router", "w1", "w2", "bias", "gumbel", "token_mask", "w1_shared", "w2_shared"):
         t = inp.get(key)
         if t is None:
             h.update(b"none")

@@ -52,8 +52,11 @@ def run_gpu(cfg: moe.MoEConfig, dinp: dict) -> dict:
         "n_dropped": torch.empty(1, **i32), "xp": torch.zeros(T * k, d, dtype=dt, device=dev),
         "h": torch.zeros(T * k, f, dtype=dt, device=dev), "y": torch.zeros(T * k, d, dtype=dt, device=dev),
     }
+    if cfg.d_ffn_shared:
+        dbg["y_shared"] = torch.zeros(T, d, dtype=dt, device=dev)
     out, aux = moe.forward(cfg, dinp["x"], dinp["w_router"], dinp["w1"], dinp["w2"], bias=dinp["bias"],
-                           gumbel=dinp["gumbel"], token_mask=dinp.get("token_mask"), debug=dbg)
+                           gumbel=dinp["gumbel"], token_mask=dinp.get("token_mask"),
+                           w1_shared=dinp.get("w1_shared"), w2_shared=dinp.get("w2_shared"), debug=dbg)
     torch.cuda.synchronize()
     res = {k_: v.cpu() for k_, v in dbg.items()}
     res["out"] = out.cpu()
@@ -134,30 +137,36 @@ def check_full(name: str, w: Workload, cfg: moe.MoEConfig, inp: dict, g: dict, s
     N = int(dp.offsets[-1])
     tol = NORM_TOL[storage]
     h_err = y_err = None
+    gys = ys = None
+    if cfg.d_ffn_shared:
+        _, ys = oracle.shared_ffn(inp["x"], inp["w1_shared"], inp["w2_shared"], storage)
+        gys = g["y_shared"].float().numpy().astype(np.float64)
+        ys_err = normwise(gys, ys)
+        assert ys_err <= tol, f"shared expert output normwise error {ys_err}"
     if sample_tokens is None:
         h, y = oracle.expert_ffn(g["xp"][:N], dp.offsets, inp["w1"], inp["w2"], storage)
         h_err = normwise(g["h"][:N].float().numpy(), h)
         y_err = normwise(g["y"][:N].float().numpy(), y)
         assert h_err <= tol, f"H normwise error {h_err}"
         assert y_err <= tol, f"Y normwise error {y_err}"
-        out_ref = oracle.combine(y, dp.row_of, g["weights"].numpy(), storage, d=cfg.d_model)
+        out_ref = oracle.combine(y, dp.row_of, g["weights"].numpy(), storage, d=cfg.d_model, y_shared=ys)
         out_err = normwise(g["out"].float().numpy(), out_ref)
         # the combine alone, on the GPU's own Y: the fp32 accumulation error (k roundings, each
         # relative to the magnitude of the terms) plus one final rounding to the storage type
         gy = g["y"][:N].float().numpy().astype(np.float64)
-        out_from_gpu_y = oracle.combine(gy, dp.row_of, g["weights"].numpy(), storage, d=cfg.d_model)
-        mag = np.zeros_like(out_from_gpu_y)
+        out_from_gpu_y = oracle.combine(gy, dp.row_of, g["weights"].numpy(), storage, d=cfg.d_model, y_shared=gys)
+        mag = np.zeros_like(out_from_gpu_y) if gys is None else np.abs(gys)
         gw = np.abs(g["weights"].numpy().astype(np.float64))
         for j in range(cfg.top_k):
             kept = dp.row_of[:, j] >= 0
             mag[kept] += gw[kept, j][:, None] * np.abs(gy[dp.row_of[kept, j]])
         ulp = 2.0 ** -7 if storage == "bf16" else 2.0 ** -22
         dev = np.abs(g["out"].float().numpy() - out_from_gpu_y)
-        bound = ulp * np.abs(out_from_gpu_y) + cfg.top_k * 2.0 ** -23 * mag + 1e-38
+        bound = ulp * np.abs(out_from_gpu_y) + (cfg.top_k + 1) * 2.0 ** -23 * mag + 1e-38
         assert np.all(dev <= bound), f"combine deviates beyond its rounding bound: {np.max(dev - bound)}"
     else:
         rows = oracle.forward_rows(inp["x"], inp["w1"], inp["w2"], r.ids, g["weights"].numpy(), dp.dropped,
-                                   sample_tokens, storage)
+                                   sample_tokens, storage, inp.get("w1_shared"), inp.get("w2_shared"))
         out_err = normwise(g["out"][sample_tokens].float().numpy(), rows)
     assert out_err <= tol, f"output normwise error {out_err}"
     # aux and entropy from the GPU's probabilities (Mode R) and the pre-cut counts

@@ -51,6 +51,7 @@ def _cfg(**kw):
     ({"temperature": 0.0}, 1), ({"temperature": -1.0}, 1), ({"temperature": float("inf")}, 1),
     ({"temperature": float("nan")}, 1), ({"aux_coef": float("nan")}, 1),
     ({"dtype": "bf16", "weight_dtype": "f32"}, 2), ({"dtype": "f16"}, 1),
+    ({"d_ffn_shared": 64}, 0), ({"d_ffn_shared": 12}, 1), ({"d_ffn_shared": -8}, 1), ({"d_ffn_shared": 32776}, 1),
 ])
 def test_validate_config(kw, status):
     assert moe.validate_config(_cfg(**kw)) == status
@@ -103,9 +104,15 @@ def test_calls_validate_before_any_launch():
     def route(x=fake, wr=fake, ids=fake, wts=fake, ws=fake, nbytes=1 << 30, cfg=good):
         return L.moe_route(B(cfg), x, wr, None, None, None, None, None, None, ids, wts, ws, nbytes, None)
 
-    # moe_forward(cfg, x, w_router, bias, noise, token_mask, w1, w2, out, aux, dbg, ws, ws_bytes, stream)
-    def forward(x=fake, wr=fake, w1=fake, w2=fake, out=fake, aux=fake, dbg=None, ws=fake, nbytes=1 << 30, cfg=good):
-        return L.moe_forward(B(cfg), x, wr, None, None, None, w1, w2, out, aux, dbg, ws, nbytes, None)
+    # moe_forward(cfg, x, w_router, bias, noise, token_mask, w1, w2, w1_shared, w2_shared, out, aux, dbg, ws,
+    #             ws_bytes, stream)
+    def forward(x=fake, wr=fake, w1=fake, w2=fake, w1s=None, w2s=None, out=fake, aux=fake, dbg=None, ws=fake,
+                nbytes=1 << 30, cfg=good):
+        return L.moe_forward(B(cfg), x, wr, None, None, None, w1, w2, w1s, w2s, out, aux, dbg, ws, nbytes, None)
+
+    # moe_combine(cfg, y, row_of, weights, y_shared, out, stream)
+    def combine(y=fake, row_of=fake, wts=fake, ys=None, out=fake, cfg=good):
+        return L.moe_combine(B(cfg), y, row_of, wts, ys, out, None)
 
     # moe_aux_loss(cfg, probs, logits, token_mask, counts_pre, aux, ws, ws_bytes, stream)
     def aux_loss(probs=fake, logits=None, counts=fake, aux=fake, ws=fake, nbytes=1 << 30, cfg=good):
@@ -115,7 +122,7 @@ def test_calls_validate_before_any_launch():
     assert route(cfg=bad) == 1
     assert L.moe_dispatch(B(bad), *([fake] * 10), fake, 1 << 30, None) == 1
     assert L.moe_expert_ffn(B(bad), *([fake] * 6), fake, 1 << 30, None) == 1
-    assert L.moe_combine(B(bad), fake, fake, fake, fake, None) == 1
+    assert combine(cfg=bad) == 1
     assert aux_loss(cfg=bad) == 1
     assert forward(cfg=bad) == 1
     # null required pointers
@@ -123,14 +130,22 @@ def test_calls_validate_before_any_launch():
     assert route(x=None, wr=None) == 1
     assert L.moe_dispatch(B(good), *([fake] * 9), None, fake, 1 << 30, None) == 1
     assert L.moe_expert_ffn(B(good), fake, fake, fake, None, fake, fake, fake, 1 << 30, None) == 1
-    assert L.moe_combine(B(good), fake, None, fake, fake, None) == 1
+    assert combine(row_of=None) == 1
     assert aux_loss(probs=None, logits=None) == 1
     assert forward(out=None) == 1
     assert forward(aux=None) == 1
     # misaligned activation pointers
     odd = ctypes.c_void_p(256 + 8)
-    assert L.moe_combine(B(good), odd, fake, fake, fake, None) == 1
+    assert combine(y=odd) == 1
+    assert combine(ys=odd) == 1
     assert forward(x=odd) == 1
+    # shared expert: its weights are required (and aligned) when d_ffn_shared > 0
+    shared = _cfg(d_ffn_shared=16).to_c()
+    need_s = moe.workspace_bytes(_cfg(d_ffn_shared=16))
+    assert forward(cfg=shared, nbytes=need_s) == 1
+    assert forward(cfg=shared, w1s=fake, nbytes=need_s) == 1
+    assert forward(cfg=shared, w1s=fake, w2s=odd, nbytes=need_s) == 1
+    assert need_s > moe.workspace_bytes(_cfg())
     # misaligned router weight (read with 16-byte loads)
     assert forward(wr=odd) == 1
     assert route(wr=odd) == 1

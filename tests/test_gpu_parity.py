@@ -2,7 +2,7 @@
 
 Reduced sizes run every step element by element (several tiles plus ragged tails, odd expert
 counts, E up to 64, k up to 8, capacity drops, Gumbel keys, additive router noise, padding
-tokens, fp32 mode). The full-size workloads
+tokens, a shared expert, fp32 mode). The full-size workloads
 check routing and dispatch exactly on every token and the layer output on sampled tokens.
 """
 import dataclasses
@@ -66,6 +66,17 @@ REDUCED = {
     "padding_e40_k4": derived(BASE, name="padding_e40_k4", T=600, d_model=64, d_ffn=96, num_experts=40, top_k=4,
                               padding=0.5),
     "all_padding": derived(BASE, name="all_padding", T=200, d_model=64, d_ffn=64, padding=1.0),
+    # a shared expert on every token: 256 x 256 GEMMs (T >= 256), the weight-streaming GEMMs
+    # (T <= 64), the 128 x 128 kernel in between and in fp32, with padding and capacity drops
+    "shared_big": derived(BASE, name="shared_big", T=2000, d_model=128, d_ffn=192, d_ffn_shared=320),
+    "shared_stream_padding": derived(WORKLOADS["small_t_streaming"], name="shared_stream_padding", T=48,
+                                     d_model=256, d_ffn=128, d_ffn_shared=192, padding=0.2),
+    "shared_mid_capacity": derived(BASE, name="shared_mid_capacity", T=200, d_model=96, d_ffn=64, d_ffn_shared=136,
+                                   capacity_factor=(7, 10)),
+    "shared_f32_noise": derived(WORKLOADS["tiny_f32"], name="shared_f32_noise", T=150, d_model=40, d_ffn=24,
+                                d_ffn_shared=56, router_noise=0.2, padding=0.3),
+    "shared_top1_d512": derived(BASE, name="shared_top1_d512", T=300, d_model=512, d_ffn=256, num_experts=4,
+                                top_k=1, d_ffn_shared=256),
 }
 
 
@@ -115,7 +126,8 @@ def test_deterministic_repeat():
         assert torch.equal(a[key].view(torch.uint8), b[key].view(torch.uint8)), key
 
 
-@pytest.mark.parametrize("name", ["ragged_gumbel_capacity", "padding_noise_f32", "padding_gumbel_capacity"])
+@pytest.mark.parametrize("name", ["ragged_gumbel_capacity", "padding_noise_f32", "padding_gumbel_capacity",
+                                  "shared_mid_capacity"])
 def test_step_calls_match_forward(name):
     """moe_route / moe_dispatch / moe_expert_ffn / moe_combine / moe_aux_loss called one by one
     give what moe_forward gives."""
@@ -144,7 +156,7 @@ def test_step_calls_match_forward(name):
     y = torch.zeros(T * k, d, dtype=dt, device=dev)
     moe.moe_expert_ffn(cfg, xp, off, dinp["w1"], dinp["w2"], h, y, ws)
     out = torch.empty(T, d, dtype=dt, device=dev)
-    moe.moe_combine(cfg, y, row_of, wts, out)
+    moe.moe_combine(cfg, y, row_of, wts, out, y_shared=g["y_shared"].to(dev) if cfg.d_ffn_shared else None)
     aux = torch.empty(3, dtype=torch.float32, device=dev)
     moe.moe_aux_loss(cfg, cp, aux, ws, probs=probs, token_mask=mask)
     aux2 = torch.empty(3, dtype=torch.float32, device=dev)
