@@ -76,8 +76,11 @@ def cpu_baseline(w, inp, ntok: int) -> dict:
     g = inp["gumbel"][:ntok] if inp["gumbel"] is not None else None
     C = oracle.capacity_from_factor(ntok, w.top_k, w.num_experts, w.capacity_factor)
     t0 = time.perf_counter()
+    m = inp["token_mask"][:ntok] if inp["token_mask"] is not None else None
     oracle.forward(x, inp["w_router"], inp["w1"], inp["w2"], k=w.top_k, storage=w.dtype, bias=inp["bias"],
-                   gumbel=g, tau=w.temperature, capacity=C, renormalize=w.renormalize, aux_coef=w.aux_coef)
+                   gumbel=g, tau=w.temperature, capacity=C, renormalize=w.renormalize, aux_coef=w.aux_coef,
+                   noise_in_logits=w.router_noise > 0.0, token_mask=m, w1_shared=inp["w1_shared"],
+                   w2_shared=inp["w2_shared"])
     dt = time.perf_counter() - t0
     return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {ntok} of {w.T} tokens of {w.name} with all expert weights "
@@ -115,7 +118,8 @@ def main():
 
     def step(ev=None):
         moe.moe_forward(cfg, dev["x"], dev["w_router"], dev["w1"], dev["w2"], out, aux, ws, bias=dev["bias"],
-                        gumbel=dev["gumbel"], debug={"offsets": offsets, "n_dropped": nd}, events=ev)
+                        gumbel=dev["gumbel"], token_mask=dev["token_mask"], w1_shared=dev["w1_shared"],
+                        w2_shared=dev["w2_shared"], debug={"offsets": offsets, "n_dropped": nd}, events=ev)
 
     for _ in range(args.warmup):
         step()
@@ -166,6 +170,8 @@ def main():
         roof = {"bound": "mfma", "achieved": dom_tflops, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     gemm_tflops = 2 * flop_gemm / (t_g1 + t_g2) / 1e12
+    t_sh = kms[names.index("shared_ffn")] * 1e-3
+    shared_tflops = (4.0 * T * d * w.d_ffn_shared / t_sh / 1e12) if w.d_ffn_shared and t_sh > 0 else None
     dispatch_bytes = T * d * a + N * d * a + 12 * T * w.top_k
     combine_bytes = N * d * a + T * d * a + 8 * T * w.top_k
     t_disp = sum(kms[names.index(n)] for n in ("dispatch_hist", "dispatch_scan_aux", "dispatch_gather")) * 1e-3
@@ -186,12 +192,14 @@ def main():
         "data": "synthetic (seeded Gaussian inputs and random-init weights of the workload's shapes)",
         "config": {"workload": w.name, "T": T, "d_model": d, "d_ffn": f, "num_experts": w.num_experts,
                    "top_k": w.top_k, "capacity": cfg.capacity, "temperature": w.temperature,
-                   "gumbel": w.gumbel, "router_bias": w.router_bias, "parallelism": "single GPU"},
+                   "gumbel": w.gumbel, "router_bias": w.router_bias, "router_noise": w.router_noise,
+                   "padding": w.padding, "d_ffn_shared": w.d_ffn_shared, "parallelism": "single GPU"},
         "roofline": {"kernel": dom, **roof, "traffic": recorded_traffic(w.name, dom),
                      "traffic_unit": "bytes per dispatch beyond L2 (FETCH_SIZE+WRITE_SIZE, calibrated)",
                      "algorithmic_bytes": gemm_bytes, "algorithmic_flop": flop_gemm},
         "gemm_tflops": gemm_tflops,
         "gemm_frac_of_peak": gemm_tflops / peak,
+        "shared_ffn_tflops": shared_tflops,
         "kernel_ms": {n: float(v) for n, v in zip(names, kms)},
         "route_gbs": (T * d * a + w.num_experts * d * 4 + T * w.num_experts * 4 * (2 if w.gumbel else 1)
                       + 8 * T * w.top_k) / (kms[names.index("route")] * 1e-3) / 1e9,

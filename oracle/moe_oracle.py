@@ -307,6 +307,60 @@ def dispatch(ids, num_experts: int, capacity: int, x=None) -> Dispatch:
 
 
 # ---------------------------------------------------------------------------------------------
+# 4-bit expert weights  ([P4 §5.2])
+# ---------------------------------------------------------------------------------------------
+
+Q4_GROUP = 64
+
+
+def quantize_int4(w):
+    """Symmetric group-wise int4 codes of bf16 weights w [..., K] (K a multiple of 64).
+
+    P4 §5.2 proposes 4-bit expert weights. Per group of 64 consecutive in-features: the scale is
+    s = bf16(fp32(amax / 7)) (an fp32 divide, then one round-to-nearest-even to bf16); the codes
+    are q = clamp(rint(fp32(w / s)), -8, 7), ties to even, and 0 where s = 0. Returns (codes as
+    int8 [..., K], scales as float64 [..., K / 64] holding bf16 values).
+    """
+    w32 = _f32(w)
+    K = w32.shape[-1]
+    if K % Q4_GROUP:
+        raise ValueError("oracle quantize_int4: K must be a multiple of 64")
+    g = w32.reshape(*w32.shape[:-1], K // Q4_GROUP, Q4_GROUP)
+    amax = np.abs(g).max(axis=-1)
+    s = round_bf16(np.divide(amax, np.float32(7.0), dtype=np.float32).astype(np.float64))
+    s32 = s.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(s32 > 0, np.divide(g, np.where(s32 > 0, s32, np.float32(1.0)), dtype=np.float32), 0)
+    q = np.clip(np.rint(r.astype(np.float64)), -8, 7).astype(np.int8)
+    return q.reshape(w32.shape), s
+
+
+def dequantize_int4(codes, scales) -> np.ndarray:
+    """w' = bf16(q * s) per element (q * s is exact in float64), float64 result."""
+    q = np.asarray(codes, dtype=np.float64)
+    K = q.shape[-1]
+    s = np.repeat(np.asarray(scales, dtype=np.float64), Q4_GROUP, axis=-1)
+    assert s.shape[-1] == K
+    return round_bf16(q * s)
+
+
+def pack_int4(codes, scales) -> np.ndarray:
+    """The packed byte layout of a 4-bit weight: all codes, two per byte (low nibble = even k,
+    two's complement nibbles), then the bf16 scales (little-endian) from the next 256-byte
+    boundary. Used to build inputs for the library's 4-bit path and to check its quantizer."""
+    q = np.asarray(codes, dtype=np.int8).reshape(-1)
+    nib = (q.astype(np.int16) & 0xF).astype(np.uint8)
+    code_bytes = (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)
+    sc = np.asarray(scales, dtype=np.float64).reshape(-1).astype(np.float32)
+    bits = (sc.view(np.uint32) >> 16).astype(np.uint16)
+    off = (code_bytes.size + 255) // 256 * 256
+    out = np.zeros(off + 2 * bits.size, dtype=np.uint8)
+    out[:code_bytes.size] = code_bytes
+    out[off:] = bits.view(np.uint8)
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
 # experts and combine  ([P4 §2.4])
 # ---------------------------------------------------------------------------------------------
 

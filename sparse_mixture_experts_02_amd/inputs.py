@@ -64,6 +64,13 @@ WORKLOADS = {
                                        temperature=0.7, gumbel=True, router_bias=True),
     "small_t_streaming": Workload("small_t_streaming", T=256, d_model=2048, d_ffn=4096, num_experts=16,
                                   top_k=2, dtype="bf16", capacity_factor=(12, 10)),
+    # the main layer with P4's router variants: additive logit noise of scale 0.1 (P4 §3.2, its
+    # value at the start of training) and 10% padding tokens (P4 §4.1)
+    "main_noise_padding": Workload("main_noise_padding", T=16384, d_model=2048, d_ffn=4096, num_experts=8,
+                                   top_k=2, dtype="bf16", router_noise=0.1, padding=0.1),
+    # the main layer with one shared expert of the routed experts' width (P4 §5.2)
+    "main_shared": Workload("main_shared", T=16384, d_model=2048, d_ffn=4096, num_experts=8, top_k=2,
+                            dtype="bf16", d_ffn_shared=4096),
 }
 
 # The workload the headline throughput is quoted on.

@@ -105,7 +105,7 @@ def test_full_size_parity(name):
     run_and_check(name, WORKLOADS[name])
 
 
-@pytest.mark.parametrize("name", ["main_bf16", "skewed_gumbel_capacity"])
+@pytest.mark.parametrize("name", ["main_bf16", "skewed_gumbel_capacity", "main_noise_padding", "main_shared"])
 def test_full_size_sampled(name):
     """Every token's routing and dispatch exactly; the output on 96 sampled tokens."""
     w = WORKLOADS[name]

@@ -583,3 +583,49 @@ def test_shared_expert_brute_force_and_layer_sum():
     dropped_all = oracle.forward(x, wr, w1, w2, k=k, storage="f32", capacity=0, token_mask=mask,
                                  w1_shared=w1s, w2_shared=w2s)
     assert np.array_equal(dropped_all.out, ys)
+
+
+# ------------------------------------------------------------------------------ 4-bit weights
+
+def test_int4_hand_group():
+    """One group worked by hand: amax 1.75 -> s = bf16(0.25) = 0.25 exactly; codes w / s."""
+    w = np.zeros((1, 64), np.float32)
+    w[0, :8] = [1.75, -1.75, 0.125, -0.375, 0.5, 0.625, 1.0, -0.0625]
+    q, s = oracle.quantize_int4(w)
+    assert s.tolist() == [[0.25]]
+    # 0.125 / 0.25 = 0.5 -> 0 (ties to even); -0.375 / 0.25 = -1.5 -> -2; 0.625 / 0.25 = 2.5 -> 2
+    assert q[0, :8].tolist() == [7, -7, 0, -2, 2, 2, 4, 0]
+    assert (q[0, 8:] == 0).all()
+    assert oracle.dequantize_int4(q, s)[0, :8].tolist() == [1.75, -1.75, 0.0, -0.5, 0.5, 0.5, 1.0, 0.0]
+
+
+def test_int4_properties():
+    rng = np.random.default_rng(4)
+    w = torch.from_numpy((0.02 * rng.standard_normal((3, 5, 256))).astype(np.float32)).to(torch.bfloat16)
+    wf = w.float().numpy().astype(np.float64)
+    q, s = oracle.quantize_int4(w)
+    assert q.dtype == np.int8 and q.min() >= -8 and q.max() <= 7
+    # the group's largest magnitude maps to +-7; every element within half a step (plus the
+    # scale's rounding) of its dequantised value
+    g = np.abs(q.reshape(3, 5, 4, 64)).max(axis=-1)
+    assert (g == 7).all()
+    dq = q.astype(np.float64) * np.repeat(s, 64, axis=-1)
+    step = np.repeat(s, 64, axis=-1)
+    assert (np.abs(dq - wf) <= 0.5 * step * (1 + 2.0 ** -7) + 1e-30).all()
+    # the bf16 scale is the fp32 quotient rounded once; a zero group has scale 0 and codes 0
+    amax = np.abs(wf.reshape(3, 5, 4, 64)).max(axis=-1)
+    assert np.array_equal(s, oracle.round_bf16((amax.astype(np.float32) / np.float32(7)).astype(np.float64)))
+    z = np.zeros((2, 64), np.float32)
+    qz, sz = oracle.quantize_int4(z)
+    assert (qz == 0).all() and (sz == 0).all()
+    # dequantised weights are bf16 values (a fixed point of the rounding)
+    d = oracle.dequantize_int4(q, s)
+    assert np.array_equal(d, oracle.round_bf16(d))
+
+
+def test_int4_packing_layout():
+    q = np.array([[-8, 7, 1, -1] + [0] * 60], dtype=np.int8)
+    s = np.array([[0.5]])
+    b = oracle.pack_int4(q, s)
+    assert b[0] == (0x8 | (0x7 << 4)) and b[1] == (0x1 | (0xF << 4))
+    assert b.size == 256 + 2 and b[256] == 0x00 and b[257] == 0x3F      # bf16(0.5) = 0x3F00
