@@ -75,9 +75,13 @@ def cpu_baseline(w, inp, ntok: int) -> dict:
     x = inp["x"][:ntok]
     g = inp["gumbel"][:ntok] if inp["gumbel"] is not None else None
     C = oracle.capacity_from_factor(ntok, w.top_k, w.num_experts, w.capacity_factor)
-    t0 = time.perf_counter()
     m = inp["token_mask"][:ntok] if inp["token_mask"] is not None else None
-    oracle.forward(x, inp["w_router"], inp["w1"], inp["w2"], k=w.top_k, storage=w.dtype, bias=inp["bias"],
+    w1, w2 = inp["w1"], inp["w2"]
+    if w.weight_dtype == "int4":   # the 4-bit layer: its dequantised weights (quantising is not timed)
+        w1 = oracle.dequantize_int4(*oracle.quantize_int4(w1))
+        w2 = oracle.dequantize_int4(*oracle.quantize_int4(w2))
+    t0 = time.perf_counter()
+    oracle.forward(x, inp["w_router"], w1, w2, k=w.top_k, storage=w.dtype, bias=inp["bias"],
                    gumbel=g, tau=w.temperature, capacity=C, renormalize=w.renormalize, aux_coef=w.aux_coef,
                    noise_in_logits=w.router_noise > 0.0, token_mask=m, w1_shared=inp["w1_shared"],
                    w2_shared=inp["w2_shared"])
@@ -108,6 +112,9 @@ def main():
     digest = inputs_digest(inp)
     dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
     cfg = moe.config_for(w)
+    if cfg.int4:   # 4-bit expert weights: packed once on the GPU, before anything is timed
+        dev["w1"] = moe.quantize_int4(dev["w1"])
+        dev["w2"] = moe.quantize_int4(dev["w2"])
     ws = moe.new_workspace(cfg)
     out = torch.empty(w.T, w.d_model, dtype=cfg.torch_dtype, device="cuda")
     aux = torch.empty(3, dtype=torch.float32, device="cuda")
@@ -161,7 +168,8 @@ def main():
     dom_tflops = flop_gemm / t_dom / 1e12
     # algorithmic bytes of one grouped GEMM launch: its activations in and out once, every expert's
     # weight matrix once
-    gemm_bytes = N * d * a + w.num_experts * d * f * a + N * f * a
+    wbytes = (0.5 + 2.0 / 64) if cfg.int4 else a   # bytes per expert weight (4-bit: codes + bf16 scales)
+    gemm_bytes = N * d * a + w.num_experts * d * f * wbytes + N * f * a
     # a launch whose flop per byte is below the machine's ridge point is bound by HBM
     hbm_bound = flop_gemm / gemm_bytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     if hbm_bound:
@@ -193,7 +201,8 @@ def main():
         "config": {"workload": w.name, "T": T, "d_model": d, "d_ffn": f, "num_experts": w.num_experts,
                    "top_k": w.top_k, "capacity": cfg.capacity, "temperature": w.temperature,
                    "gumbel": w.gumbel, "router_bias": w.router_bias, "router_noise": w.router_noise,
-                   "padding": w.padding, "d_ffn_shared": w.d_ffn_shared, "parallelism": "single GPU"},
+                   "padding": w.padding, "d_ffn_shared": w.d_ffn_shared,
+                   "expert_weights": "int4" if cfg.int4 else w.dtype, "parallelism": "single GPU"},
         "roofline": {"kernel": dom, **roof, "traffic": recorded_traffic(w.name, dom),
                      "traffic_unit": "bytes per dispatch beyond L2 (FETCH_SIZE+WRITE_SIZE, calibrated)",
                      "algorithmic_bytes": gemm_bytes, "algorithmic_flop": flop_gemm},

@@ -44,7 +44,7 @@ typedef enum {
   MOE_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed                 */
 } moe_status_t;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_INT4 = 2 } moe_dtype_t;
 
 /* Capacity value meaning "no limit" (C = T). */
 #define MOE_NO_CAPACITY (-1)
@@ -70,8 +70,9 @@ typedef struct {
   int32_t renormalize;   /* 1: gate weights = softmax over the k selected logits / tau;
                             0: gate weights = full softmax probability of each selected expert  */
   float   aux_coef;      /* coefficient of both aux losses (P4 §2.1 uses 0.01)                 */
-  moe_dtype_t act_dtype;     /* x, Xp, H, Y, out                                               */
-  moe_dtype_t weight_dtype;  /* W1, W2 (must equal act_dtype)                                  */
+  moe_dtype_t act_dtype;     /* x, Xp, H, Y, out: MOE_F32 or MOE_BF16                          */
+  moe_dtype_t weight_dtype;  /* W1, W2: act_dtype, or MOE_INT4 with bf16 activations (packed
+                                4-bit weights, see moe_quantize_int4)                          */
   int32_t noise_in_logits;   /* how the noise input enters (0 or 1):
                                 0: Gumbel top-k (P2 §3.1), it perturbs the selection key only;
                                 1: additive router noise (P4 §3.2), logits = fp32(logits + n)
@@ -86,14 +87,34 @@ const char* moe_status_string(moe_status_t status);
 
 /* Checks a configuration on the host; touches no GPU. Returns MOE_OK, MOE_ERR_INVALID_ARGUMENT
  * (cfg NULL, a size out of the ranges above, tau not finite and > 0, capacity < -1,
- * renormalize or noise_in_logits not 0 or 1) or
- * MOE_ERR_UNSUPPORTED (act_dtype != weight_dtype or an unknown dtype). */
+ * renormalize or noise_in_logits not 0 or 1, an unknown dtype) or MOE_ERR_UNSUPPORTED
+ * (act_dtype != weight_dtype, except MOE_INT4 weights with bf16 activations; MOE_INT4 weights
+ * also need d and f multiples of 512, T * k <= 64 * E (the weight-streaming regime) and no
+ * shared expert). */
 moe_status_t moe_validate_config(const moe_config_t* cfg);
 
 /* C = ceil(cf * T * k / E) for the decimal capacity factor cf = cf_num / cf_den, in exact
  * integer arithmetic (P3 §3.4 and §5.1 give factors such as 1.2 but no formula; this is the
  * plain reading). Returns -1 if T, k, E, cf_num or cf_den is not positive. Host only. */
 int32_t moe_capacity_from_factor(int32_t T, int32_t k, int32_t E, int32_t cf_num, int32_t cf_den);
+
+/*
+ * 4-bit expert weights [P4 §5.2]. A [rows, K] bf16 weight (rows a multiple of 16, K of 128) is
+ * stored as symmetric group-wise int4 along K, groups of 64: per (row, group) a bf16 scale
+ * s = bf16(fp32(amax / 7)) and codes q = clamp(rint(fp32(w / s)), -8, 7) (0 where s = 0),
+ * two's complement nibbles, two per byte (low nibble = even column). The layer uses
+ * w' = bf16(q * s). Layout, tiled so that each GEMM load instruction reads 1 KiB contiguously:
+ * the codes of rows 16 t .. + 15 and columns 128 s .. + 127 form the 1 KiB block
+ * t * K/128 + s, in which the 16 bytes at 16 * (16 g + r) hold row 16 t + r, columns
+ * 128 s + 32 g .. + 31; the scales follow from the next 256-byte boundary (the bytes in between
+ * are zero), 32 per block: row r's two groups at 2 r and 2 r + 1. For the expert weights
+ * rows = E * f, K = d (W1) and rows = E * d, K = f (W2).
+ * moe_int4_bytes: size of that buffer (0 for other sizes).
+ * moe_quantize_int4: fills it from w (device, 16-byte aligned) on `stream`; returns
+ * MOE_ERR_INVALID_ARGUMENT for other sizes or null/misaligned pointers.
+ */
+size_t moe_int4_bytes(int64_t rows, int32_t K);
+moe_status_t moe_quantize_int4(int64_t rows, int32_t K, const void* w, void* packed, hipStream_t stream);
 
 /* Workspace bytes that every call below accepts for this configuration (0 if cfg is invalid).
  * moe_forward keeps Xp, H and Y there: about (2 d + f) * T * k * sizeof(act) plus O(T k). */
@@ -155,7 +176,8 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* ids, const voi
                           hipStream_t stream);
 
 /*
- * Expert FFN as two grouped GEMMs over the expert segments given by offsets.
+ * Expert FFN as two grouped GEMMs over the expert segments given by offsets (w1/w2 are packed
+ * 4-bit buffers when cfg->weight_dtype is MOE_INT4).
  * [P4 §2.4] each expert is a two-layer FFN. For rows r in [offsets[e], offsets[e+1]):
  *   H[r] = SiLU(Xp[r] W1[e]^T)   (fp32 accumulate, SiLU in fp32, one rounding to act)
  *   Y[r] = H[r] W2[e]^T          (fp32 accumulate, one rounding to act)

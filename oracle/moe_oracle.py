@@ -345,14 +345,26 @@ def dequantize_int4(codes, scales) -> np.ndarray:
 
 
 def pack_int4(codes, scales) -> np.ndarray:
-    """The packed byte layout of a 4-bit weight: all codes, two per byte (low nibble = even k,
-    two's complement nibbles), then the bf16 scales (little-endian) from the next 256-byte
-    boundary. Used to build inputs for the library's 4-bit path and to check its quantizer."""
-    q = np.asarray(codes, dtype=np.int8).reshape(-1)
+    """The packed byte layout of a 4-bit weight [rows, K] (rows a multiple of 16, K of 128), tiled
+    so that one 1 KiB block holds 16 rows x 128 columns in the order the GEMM's lanes read them.
+
+    Codes: block (t, s) of rows 16 t .. 16 t + 15 and columns 128 s .. 128 s + 127 sits at byte
+    1024 (t K/128 + s); inside it, the 16 bytes at 16 (16 g + r) hold row 16 t + r, columns
+    128 s + 32 g .. + 31, two per byte (low nibble = even column, two's complement nibbles).
+    Scales (bf16, little-endian) follow from the next 256-byte boundary (zero bytes between):
+    block (t, s) holds 32 scales at 64 (t K/128 + s) bytes, row r's two groups at 2 r and 2 r + 1.
+    Used to build inputs for the library's 4-bit path and to check its quantiser.
+    """
+    q = np.asarray(codes, dtype=np.int8)
+    rows, K = q.shape
+    if rows % 16 or K % 128:
+        raise ValueError("oracle pack_int4: rows must be a multiple of 16 and K of 128")
     nib = (q.astype(np.int16) & 0xF).astype(np.uint8)
-    code_bytes = (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)
-    sc = np.asarray(scales, dtype=np.float64).reshape(-1).astype(np.float32)
-    bits = (sc.view(np.uint32) >> 16).astype(np.uint16)
+    nib = nib.reshape(rows // 16, 16, K // 128, 4, 32).transpose(0, 2, 3, 1, 4)   # [t, s, g, r, j]
+    code_bytes = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8).reshape(-1)
+    sc = np.asarray(scales, dtype=np.float64).astype(np.float32)
+    sc = sc.reshape(rows // 16, 16, K // 128, 2).transpose(0, 2, 1, 3).reshape(-1)   # [t, s, r, h]
+    bits = (np.ascontiguousarray(sc).view(np.uint32) >> 16).astype(np.uint16)
     off = (code_bytes.size + 255) // 256 * 256
     out = np.zeros(off + 2 * bits.size, dtype=np.uint8)
     out[:code_bytes.size] = code_bytes

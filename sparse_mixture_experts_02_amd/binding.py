@@ -19,6 +19,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so"
 MOE_OK = 0
 MOE_F32 = 0
 MOE_BF16 = 1
+MOE_INT4 = 2
 MOE_NO_CAPACITY = -1
 MOE_FORWARD_NUM_KERNELS = 8
 FORWARD_KERNEL_NAMES = ("route", "dispatch_hist", "dispatch_scan_aux", "dispatch_gather", "gemm1_silu", "gemm2",
@@ -29,7 +30,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPOR
 
 # Every symbol include/moe.h declares.
 EXPORTED_SYMBOLS = ("moe_status_string", "moe_validate_config", "moe_capacity_from_factor",
-                    "moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
+                    "moe_int4_bytes", "moe_quantize_int4", "moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
                     "moe_aux_loss", "moe_forward")
 
 
@@ -67,12 +68,12 @@ class MoEConfig:
     renormalize: bool = True
     aux_coef: float = 0.01
     dtype: str = "bf16"          # "bf16" or "f32" (activations and expert weights)
-    weight_dtype: Optional[str] = None   # defaults to dtype
+    weight_dtype: Optional[str] = None   # defaults to dtype; "int4" = packed 4-bit expert weights
     noise_in_logits: bool = False        # the noise input: Gumbel key noise (False) or additive logit noise
     d_ffn_shared: int = 0                # width of the shared expert (0: none)
 
     def to_c(self) -> _Config:
-        dt = {"f32": MOE_F32, "bf16": MOE_BF16}
+        dt = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4}
         wd = self.weight_dtype or self.dtype
         return _Config(self.T, self.d_model, self.d_ffn, self.num_experts, self.top_k, self.capacity,
                        self.temperature, int(self.renormalize), self.aux_coef, dt.get(self.dtype, 99),
@@ -81,6 +82,10 @@ class MoEConfig:
     @property
     def torch_dtype(self) -> torch.dtype:
         return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    @property
+    def int4(self) -> bool:
+        return self.weight_dtype == "int4"
 
 
 _lib = None
@@ -104,6 +109,10 @@ def lib() -> ctypes.CDLL:
         L.moe_capacity_from_factor.argtypes = [i32] * 5
         L.moe_workspace_bytes.restype = sz
         L.moe_workspace_bytes.argtypes = [cfgp]
+        L.moe_int4_bytes.restype = sz
+        L.moe_int4_bytes.argtypes = [ctypes.c_int64, i32]
+        L.moe_quantize_int4.restype = ctypes.c_int
+        L.moe_quantize_int4.argtypes = [ctypes.c_int64, i32, vp, vp, vp]
         L.moe_route.restype = ctypes.c_int
         L.moe_route.argtypes = [cfgp] + [vp] * 10 + [vp, sz, vp]
         L.moe_dispatch.restype = ctypes.c_int
@@ -138,6 +147,31 @@ def capacity_from_factor(T: int, k: int, E: int, num: int, den: int) -> int:
 def workspace_bytes(cfg: MoEConfig) -> int:
     c = cfg.to_c()
     return lib().moe_workspace_bytes(ctypes.byref(c))
+
+
+def int4_bytes(rows: int, K: int) -> int:
+    return lib().moe_int4_bytes(rows, K)
+
+
+def quantize_int4(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Packed 4-bit copy (uint8 GPU tensor) of a bf16 GPU weight [..., K] through moe_quantize_int4."""
+    K = w.shape[-1]
+    rows = w.numel() // K
+    n = int4_bytes(rows, K)
+    if n == 0:
+        raise ValueError(f"cannot quantise a [{rows}, {K}] weight (rows a multiple of 16, K of 128)")
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=w.device)
+    _check("moe_quantize_int4", lib().moe_quantize_int4(rows, K, _ptr(w, "w", dtype=torch.bfloat16),
+                                                        _ptr(out, "packed", (n,), torch.uint8), _stream()))
+    return out
+
+
+def _wptr(cfg: MoEConfig, t, name: str, rows: int, K: int, shape):
+    """Pointer of an expert weight: the bf16/fp32 tensor, or its packed 4-bit buffer."""
+    if cfg.int4:
+        return _ptr(t, name, (int4_bytes(rows, K),), torch.uint8)
+    return _ptr(t, name, shape, cfg.torch_dtype)
 
 
 def new_workspace(cfg: MoEConfig, device="cuda") -> torch.Tensor:
@@ -210,7 +244,8 @@ def moe_expert_ffn(cfg: MoEConfig, xp, offsets, w1, w2, h, y, ws):
     dt = cfg.torch_dtype
     st = lib().moe_expert_ffn(
         ctypes.byref(c), _ptr(xp, "xp", (T * k, d), dt), _ptr(offsets, "offsets", (E + 1,), torch.int32),
-        _ptr(w1, "w1", (E, f, d), dt), _ptr(w2, "w2", (E, d, f), dt), _ptr(h, "h", (T * k, f), dt),
+        _wptr(cfg, w1, "w1", E * f, d, (E, f, d)), _wptr(cfg, w2, "w2", E * d, f, (E, d, f)),
+        _ptr(h, "h", (T * k, f), dt),
         _ptr(y, "y", (T * k, d), dt), _ptr(ws, "ws"), ws.numel(), _stream())
     _check("moe_expert_ffn", st)
 
@@ -258,7 +293,7 @@ def moe_forward(cfg: MoEConfig, x, w_router, w1, w2, out, aux, ws, *, bias=None,
         ctypes.byref(c), _ptr(x, "x", (T, d), dt), _ptr(w_router, "w_router", (E, d), torch.float32),
         _ptr(bias, "bias", (E,), torch.float32), _ptr(gumbel, "gumbel", (T, E), torch.float32),
         _ptr(token_mask, "token_mask", (T,), torch.uint8),
-        _ptr(w1, "w1", (E, f, d), dt), _ptr(w2, "w2", (E, d, f), dt),
+        _wptr(cfg, w1, "w1", E * f, d, (E, f, d)), _wptr(cfg, w2, "w2", E * d, f, (E, d, f)),
         _ptr(w1_shared, "w1_shared", (cfg.d_ffn_shared, d), dt) if cfg.d_ffn_shared else None,
         _ptr(w2_shared, "w2_shared", (d, cfg.d_ffn_shared), dt) if cfg.d_ffn_shared else None,
         _ptr(out, "out", (T, d), dt),

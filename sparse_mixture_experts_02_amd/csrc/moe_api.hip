@@ -194,7 +194,12 @@ moe_status_t run_gemm(const moe_config_t& c, const void* a, const void* b, void*
   p.B = b;
   p.C = out;
   p.offsets = offsets;
-  MOE_LAUNCH(launch_gemm(p, c.act_dtype == MOE_BF16, silu, s));
+  if (c.weight_dtype == MOE_INT4) {
+    p.q4_scale_off = q4_scale_offset((size_t)experts * (size_t)n, kdim);
+    MOE_LAUNCH(launch_gemm_q4(p, silu, s));
+  } else {
+    MOE_LAUNCH(launch_gemm(p, c.act_dtype == MOE_BF16, silu, s));
+  }
   return MOE_OK;
 }
 
@@ -264,8 +269,15 @@ moe_status_t moe_validate_config(const moe_config_t* c) {
   if (c->d_ffn_shared < 0 || c->d_ffn_shared > kMaxDim || c->d_ffn_shared % 8) return MOE_ERR_INVALID_ARGUMENT;
   if (!isfinite(c->aux_coef)) return MOE_ERR_INVALID_ARGUMENT;
   const bool dt_ok = (c->act_dtype == MOE_F32 || c->act_dtype == MOE_BF16) &&
-                     (c->weight_dtype == MOE_F32 || c->weight_dtype == MOE_BF16);
+                     (c->weight_dtype == MOE_F32 || c->weight_dtype == MOE_BF16 || c->weight_dtype == MOE_INT4);
   if (!dt_ok) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->weight_dtype == MOE_INT4) {
+    // 4-bit weights: bf16 activations, whole groups of four 128-column stages, the
+    // weight-streaming regime (at most 64 rows per expert on average), no shared expert
+    const bool ok = c->act_dtype == MOE_BF16 && c->d_model % 512 == 0 && c->d_ffn % 512 == 0 &&
+                    (long long)c->T * c->top_k <= 64LL * c->num_experts && c->d_ffn_shared == 0;
+    return ok ? MOE_OK : MOE_ERR_UNSUPPORTED;
+  }
   if (c->act_dtype != c->weight_dtype) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -276,6 +288,19 @@ int32_t moe_capacity_from_factor(int32_t T, int32_t k, int32_t E, int32_t cf_num
   const long long den = (long long)cf_den * E;
   const long long c = (num + den - 1) / den;
   return c > 0x7fffffffLL ? 0x7fffffff : (int32_t)c;
+}
+
+size_t moe_int4_bytes(int64_t rows, int32_t K) {
+  if (rows < 16 || rows % 16 || K < 128 || K % 128) return 0;
+  return q4_bytes((size_t)rows, K);
+}
+
+moe_status_t moe_quantize_int4(int64_t rows, int32_t K, const void* w, void* packed, hipStream_t stream) {
+  if (rows < 16 || rows % 16 || K < 128 || K % 128 || K > kMaxDim || !w || !packed || !aligned16(w) ||
+      !aligned16(packed))
+    return MOE_ERR_INVALID_ARGUMENT;
+  MOE_LAUNCH(launch_quantize_q4(w, (size_t)rows, K, packed, stream));
+  return MOE_OK;
 }
 
 size_t moe_workspace_bytes(const moe_config_t* cfg) {

@@ -110,6 +110,8 @@ struct GemmParams {
   // Partial-sum workspace of the 256 x 256 kernel's split tail (gemm_big_part_bytes), or null:
   // whole tiles only.
   void* sk_part;
+  // 4-bit weights: B is the packed buffer (codes, then bf16 scales from this byte offset)
+  size_t q4_scale_off;
 };
 
 struct CombineParams {
@@ -169,6 +171,12 @@ bool gemm_uses_big(bool bf16, int K, int max_rows, int E);
 hipError_t launch_gemm_big(const GemmParams& p, bool silu, hipStream_t s);
 int gemm_stream_grid(int E, int N);
 hipError_t launch_gemm_stream(const GemmParams& p, bool silu, hipStream_t s);
+
+// 4-bit weights (packed codes + scales of a [rows, K] weight)
+size_t q4_scale_offset(size_t rows, int K);
+size_t q4_bytes(size_t rows, int K);
+hipError_t launch_quantize_q4(const void* w, size_t rows, int K, void* out, hipStream_t s);
+hipError_t launch_gemm_q4(const GemmParams& p, bool silu, hipStream_t s);
 
 hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s);
 

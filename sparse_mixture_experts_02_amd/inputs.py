@@ -46,6 +46,7 @@ class Workload:
     router_noise: float = 0.0   # std of additive router-logit noise (0: none); excludes gumbel
     padding: float = 0.0        # fraction of padding tokens (drawn per token; 0: no mask)
     d_ffn_shared: int = 0       # width of the shared expert (0: none)
+    weight_dtype: Optional[str] = None   # "int4": the library gets 4-bit copies of W1/W2
     seed: int = 0
 
     @property
@@ -68,6 +69,9 @@ WORKLOADS = {
     # value at the start of training) and 10% padding tokens (P4 §4.1)
     "main_noise_padding": Workload("main_noise_padding", T=16384, d_model=2048, d_ffn=4096, num_experts=8,
                                    top_k=2, dtype="bf16", router_noise=0.1, padding=0.1),
+    # the weight-streaming layer with 4-bit expert weights (P4 §5.2)
+    "small_t_int4": Workload("small_t_int4", T=256, d_model=2048, d_ffn=4096, num_experts=16, top_k=2,
+                             dtype="bf16", capacity_factor=(12, 10), weight_dtype="int4"),
     # the main layer with one shared expert of the routed experts' width (P4 §5.2)
     "main_shared": Workload("main_shared", T=16384, d_model=2048, d_ffn=4096, num_experts=8, top_k=2,
                             dtype="bf16", d_ffn_shared=4096),

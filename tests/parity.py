@@ -179,10 +179,24 @@ def check_full(name: str, w: Workload, cfg: moe.MoEConfig, inp: dict, g: dict, s
     return Report(name, l_err, nties, mism, N, dp.n_dropped, w_err, h_err, y_err, out_err, rel)
 
 
+def int4_inputs(inp: dict, dinp: dict):
+    """4-bit weights: the library gets its own packed copies of W1/W2 (moe_quantize_int4 on the
+    GPU); the oracle gets the dequantised weights bf16(q s) of its own quantiser."""
+    oinp = dict(inp)
+    dinp = dict(dinp)
+    for key in ("w1", "w2"):
+        oinp[key] = oracle.dequantize_int4(*oracle.quantize_int4(inp[key]))
+        dinp[key] = moe.quantize_int4(dinp[key])
+    return oinp, dinp
+
+
 def run_and_check(name: str, w: Workload, cfg: Optional[moe.MoEConfig] = None, sample_tokens=None) -> Report:
     inp = make_inputs(w)
     cfg = cfg or moe.config_for(w)
-    g = run_gpu(cfg, to_device(inp))
+    dinp = to_device(inp)
+    if cfg.int4:
+        inp, dinp = int4_inputs(inp, dinp)
+    g = run_gpu(cfg, dinp)
     rep = check_full(name, w, cfg, inp, g, sample_tokens)
     print(rep, flush=True)
     return rep

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared_functions():
     text = open(os.path.join(ROOT, "include", "moe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -52,6 +52,12 @@ def _cfg(**kw):
     ({"temperature": float("nan")}, 1), ({"aux_coef": float("nan")}, 1),
     ({"dtype": "bf16", "weight_dtype": "f32"}, 2), ({"dtype": "f16"}, 1),
     ({"d_ffn_shared": 64}, 0), ({"d_ffn_shared": 12}, 1), ({"d_ffn_shared": -8}, 1), ({"d_ffn_shared": 32776}, 1),
+    # 4-bit weights: bf16 activations, d and f multiples of 512, the weight-streaming regime, no shared expert
+    ({"dtype": "bf16", "weight_dtype": "int4", "d_model": 512, "d_ffn": 1024, "T": 128}, 0),
+    ({"dtype": "f32", "weight_dtype": "int4", "d_model": 512, "d_ffn": 512}, 2),
+    ({"dtype": "bf16", "weight_dtype": "int4", "d_model": 256, "d_ffn": 512}, 2),
+    ({"dtype": "bf16", "weight_dtype": "int4", "d_model": 512, "d_ffn": 512, "T": 129}, 2),
+    ({"dtype": "bf16", "weight_dtype": "int4", "d_model": 512, "d_ffn": 512, "d_ffn_shared": 64}, 2),
 ])
 def test_validate_config(kw, status):
     assert moe.validate_config(_cfg(**kw)) == status
@@ -80,6 +86,18 @@ def test_capacity_from_factor_matches_oracle():
                                                               2 ** 31 - 1)
     assert moe.capacity_from_factor(0, 2, 4, 1, 1) == -1
     assert moe.capacity_from_factor(4, 2, 4, 0, 1) == -1
+
+
+def test_int4_sizes_and_quantize_validation():
+    assert moe.int4_bytes(16 * 4096, 2048) == 16 * 4096 * 1024 + 16 * 4096 * 32 * 2
+    assert moe.int4_bytes(16, 128) == 1024 + 16 * 2 * 2
+    assert moe.int4_bytes(0, 128) == 0 and moe.int4_bytes(24, 128) == 0 and moe.int4_bytes(16, 192) == 0
+    L = binding.lib()
+    fake, odd = ctypes.c_void_p(256), ctypes.c_void_p(264)
+    assert L.moe_quantize_int4(16, 192, fake, fake, None) == 1
+    assert L.moe_quantize_int4(20, 128, fake, fake, None) == 1
+    assert L.moe_quantize_int4(16, 128, None, fake, None) == 1
+    assert L.moe_quantize_int4(16, 128, fake, odd, None) == 1
 
 
 def test_workspace_bytes():

@@ -77,6 +77,15 @@ REDUCED = {
                                 d_ffn_shared=56, router_noise=0.2, padding=0.3),
     "shared_top1_d512": derived(BASE, name="shared_top1_d512", T=300, d_model=512, d_ffn=256, num_experts=4,
                                 top_k=1, d_ffn_shared=256),
+    # 4-bit expert weights in the weight-streaming regime: capacity drops, experts longer than one
+    # 64-row chunk (router bias), padding with additive noise, top-1
+    "int4_capacity": derived(WORKLOADS["small_t_int4"], name="int4_capacity", T=100, d_model=512, d_ffn=512,
+                             num_experts=4),
+    "int4_skew": derived(WORKLOADS["small_t_int4"], name="int4_skew", T=256, d_model=512, d_ffn=1536, num_experts=8,
+                         router_bias=True, capacity_factor=None),
+    "int4_padding_noise_top1": derived(WORKLOADS["small_t_int4"], name="int4_padding_noise_top1", T=120,
+                                       d_model=512, d_ffn=1024, num_experts=6, top_k=1, padding=0.3,
+                                       router_noise=0.1),
 }
 
 
@@ -99,7 +108,7 @@ def test_zero_capacity_drops_everything():
     check_full("zero_capacity", w, cfg, inp, g)
 
 
-@pytest.mark.parametrize("name", ["small_bf16", "small_t_streaming"])
+@pytest.mark.parametrize("name", ["small_bf16", "small_t_streaming", "small_t_int4"])
 def test_full_size_parity(name):
     print(f"[gpu] full-size parity {name}", flush=True)
     run_and_check(name, WORKLOADS[name])
@@ -189,3 +198,17 @@ def test_route_given_logits_mode_r_hook():
     r = oracle.route(logits=l.numpy(), k=k)
     assert np.array_equal(ids.cpu().numpy(), r.ids)
     assert np.max(np.abs(wts.cpu().numpy() - r.weights)) <= 1e-6
+
+
+@pytest.mark.parametrize("rows,K", [(48, 128), (320, 2048), (16, 4096)])
+def test_quantize_int4_bit_exact(rows, K):
+    """moe_quantize_int4 writes exactly the oracle's codes and scales (packed layout)."""
+    gen = torch.Generator().manual_seed(rows + K)
+    w = (torch.randn(rows, K, generator=gen) * 0.02).to(torch.bfloat16)
+    w[0, :64] = 0                                   # a zero group
+    w[1, :64] = torch.tensor([0.25 * 7] + [0.125, -0.375, 0.625] * 21, dtype=torch.float32).to(torch.bfloat16)
+    print(f"[gpu] quantize_int4 rows={rows} K={K}", flush=True)
+    packed = moe.quantize_int4(w.cuda())
+    torch.cuda.synchronize()
+    want = oracle.pack_int4(*oracle.quantize_int4(w))
+    assert np.array_equal(packed.cpu().numpy(), want)

@@ -624,8 +624,31 @@ def test_int4_properties():
 
 
 def test_int4_packing_layout():
-    q = np.array([[-8, 7, 1, -1] + [0] * 60], dtype=np.int8)
-    s = np.array([[0.5]])
+    """Tiled layout, checked element by element against its definition with plain loops."""
+    rng = np.random.default_rng(9)
+    rows, K = 32, 256
+    q = rng.integers(-8, 8, size=(rows, K)).astype(np.int8)
+    s = oracle.round_bf16(rng.random((rows, K // 64)))
     b = oracle.pack_int4(q, s)
-    assert b[0] == (0x8 | (0x7 << 4)) and b[1] == (0x1 | (0xF << 4))
-    assert b.size == 256 + 2 and b[256] == 0x00 and b[257] == 0x3F      # bf16(0.5) = 0x3F00
+    off = (rows * K // 2 + 255) // 256 * 256
+    assert b.size == off + rows * (K // 64) * 2
+    for r in range(rows):
+        t, rr = divmod(r, 16)
+        for k in range(K):
+            st, kk = divmod(k, 128)
+            g, j = divmod(kk, 32)
+            byte = b[1024 * (t * (K // 128) + st) + 16 * (16 * g + rr) + j // 2]
+            nib = (byte >> 4) if j % 2 else (byte & 0xF)
+            assert nib == (int(q[r, k]) & 0xF)
+        for gi in range(K // 64):
+            st, h = divmod(gi, 2)
+            i = off + 64 * (t * (K // 128) + st) + 2 * (2 * rr + h)
+            bits = int(b[i]) | (int(b[i + 1]) << 8)
+            assert np.float32(s[r, gi]).view(np.uint32) >> 16 == bits
+    assert (b[rows * K // 2:off] == 0).all()
+    # one hand-made case: codes -8, 7 at row 0, columns 0, 1; code 1 at row 1, column 32
+    q = np.zeros((16, 128), np.int8)
+    q[0, 0], q[0, 1], q[1, 32] = -8, 7, 1
+    b = oracle.pack_int4(q, np.full((16, 2), 0.5))
+    assert b[0] == (0x8 | (0x7 << 4)) and b[16 * (16 * 1 + 1)] == 0x1
+    assert b[1024] == 0x00 and b[1025] == 0x3F      # bf16(0.5) = 0x3F00, little-endian
