@@ -324,23 +324,33 @@ __global__ __launch_bounds__(512) void route_ksplit_kernel(RouteParams p) {
     for (int sb = s0; sb < s1; sb += NB) {
       uint4 xa[NB][MT];
       float4 wv[NB][ET][2];
+      // Every load is issued unconditionally from a valid address (column 0 for steps past the
+      // range, the last expert for lanes past E) and masked afterwards: loads behind branches
+      // make the compiler wait for all outstanding loads at the join.
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
-        const int kc = (sb + u) * 32 + kq;
-        const bool kin = sb + u < s1 && kc < d;   // d is a multiple of 8: a chunk is all in or all out
+        const int kr = (sb + u) * 32 + kq;
+        const bool kin = sb + u < s1 && kr < d;   // d is a multiple of 8: a chunk is all in or all out
+        const int kc = kin ? kr : 0;
+        // the masks are opaque to the compiler, so it cannot turn the masking back into a branch
+        uint32_t mk = kin ? 0xffffffffu : 0u;
+        asm volatile("" : "+v"(mk));
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) xa[u][mt] = kin ? *(const uint4*)(xr[mt] + kc) : make_uint4(0, 0, 0, 0);
+        for (int mt = 0; mt < MT; ++mt) {
+          const uint4 v = *(const uint4*)(xr[mt] + kc);
+          xa[u][mt] = make_uint4(v.x & mk, v.y & mk, v.z & mk, v.w & mk);
+        }
 #pragma unroll
         for (int et = 0; et < ET; ++et) {
           const int e = et * 16 + col;
-          if (kin && e < E) {
-            const float4* src = (const float4*)(W + (size_t)e * d + kc);
-            wv[u][et][0] = src[0];
-            wv[u][et][1] = src[1];
-          } else {
-            wv[u][et][0] = make_float4(0.f, 0.f, 0.f, 0.f);
-            wv[u][et][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-          }
+          uint32_t mw = (kin && e < E) ? 0xffffffffu : 0u;
+          asm volatile("" : "+v"(mw));
+          const uint4* src = (const uint4*)(W + (size_t)min(e, E - 1) * d + kc);
+          const uint4 w0 = src[0], w1 = src[1];
+          wv[u][et][0] = make_float4(__uint_as_float(w0.x & mw), __uint_as_float(w0.y & mw),
+                                     __uint_as_float(w0.z & mw), __uint_as_float(w0.w & mw));
+          wv[u][et][1] = make_float4(__uint_as_float(w1.x & mw), __uint_as_float(w1.y & mw),
+                                     __uint_as_float(w1.z & mw), __uint_as_float(w1.w & mw));
         }
       }
 #pragma unroll
