@@ -24,7 +24,8 @@ first C assignments of an expert in (token, slot) order; a dropped slot contribu
 aux losses use pre-drop counts.
 
 Every function is pinned by the CPU tests in tests/test_oracle_pins.py (brute force, closed
-forms, invariants and a hand-worked example). There is no "parity unpinned" function.
+forms, invariants, a hand-worked example, and finite differences for the backward pass). There
+is no "parity unpinned" function.
 """
 from __future__ import annotations
 
@@ -52,7 +53,10 @@ def round_bf16(a) -> np.ndarray:
 
 
 def round_storage(a, storage: str) -> np.ndarray:
-    """Round float64 values to the storage dtype ("bf16" or "f32"); float64 result."""
+    """Round float64 values to the storage dtype ("bf16" or "f32"); float64 result. "f64" keeps
+    them (the exact layer, used to check the backward pass by finite differences)."""
+    if storage == "f64":
+        return np.asarray(a, dtype=np.float64)
     if storage == "bf16":
         return round_bf16(a)
     if storage == "f32":
@@ -77,8 +81,9 @@ def _f32(a) -> np.ndarray:
 # routing  ([P2 §3.1], [P4 §1.3, §2.4])
 # ---------------------------------------------------------------------------------------------
 
-def router_logits(x, w_router, bias=None) -> np.ndarray:
-    """logits[t, e] = sum_c x[t, c] * W_r[e, c] + b[e], exact in float64, rounded once to fp32.
+def router_logits(x, w_router, bias=None, exact: bool = False) -> np.ndarray:
+    """logits[t, e] = sum_c x[t, c] * W_r[e, c] + b[e], exact in float64, rounded once to fp32
+    (kept in float64 with exact=True).
 
     P4 §2.4: the router is a linear layer producing one score per expert; P2 §3.1 writes
     scores = W_router x. The per-expert bias is the workload's load-skew term.
@@ -86,7 +91,7 @@ def router_logits(x, w_router, bias=None) -> np.ndarray:
     l = _f64(x) @ _f64(w_router).T
     if bias is not None:
         l = l + _f64(bias)[None, :]
-    return l.astype(np.float32)
+    return l if exact else l.astype(np.float32)
 
 
 def selection_keys(logits, gumbel=None, tau: float = 1.0) -> np.ndarray:
@@ -137,7 +142,7 @@ def router_probs(logits, tau: float = 1.0) -> np.ndarray:
     return p / p.sum(axis=1, keepdims=True)
 
 
-def gate_weights(logits, ids, tau: float = 1.0, renormalize: bool = True) -> np.ndarray:
+def gate_weights(logits, ids, tau: float = 1.0, renormalize: bool = True, exact: bool = False) -> np.ndarray:
     """Gate weight of each selected expert, fp32.
 
     P4 §2.4: the output is the weighted sum of the chosen experts' outputs, weighted by the
@@ -155,7 +160,7 @@ def gate_weights(logits, ids, tau: float = 1.0, renormalize: bool = True) -> np.
     else:
         p = router_probs(logits, tau)
         w = np.take_along_axis(p, ids.astype(np.int64), axis=1)
-    return w.astype(np.float32)
+    return w if exact else w.astype(np.float32)
 
 
 def topk_gap(keys, k: int) -> np.ndarray:
@@ -191,7 +196,7 @@ class Routing:
 
 def route(x=None, w_router=None, bias=None, gumbel=None, tau: float = 1.0, k: int = 2,
           renormalize: bool = True, logits=None, noise_in_logits: bool = False,
-          token_mask=None) -> Routing:
+          token_mask=None, exact: bool = False) -> Routing:
     """Router logits -> key -> top-k -> gate weights, plus the full softmax for the aux loss.
 
     With `logits` given, routing runs on those fp32 logits (the bias, and additive noise when
@@ -206,22 +211,31 @@ def route(x=None, w_router=None, bias=None, gumbel=None, tau: float = 1.0, k: in
     token_mask [T] (nonzero = real token; P4 §4.1: padding tokens take no part in expert
     selection): a padding token gets ids -1 and weights 0 in every slot, and is left out of the
     probabilities, the entropy and the aux statistics. Its logits are still computed.
+
+    exact=True keeps logits, keys and weights in float64 (the exact layer of the finite-difference
+    checks of the backward pass).
     """
-    if logits is None:
-        logits = router_logits(x, w_router, bias)
+    if exact:
+        logits = router_logits(x, w_router, bias, exact=True) if logits is None else _f64(logits)
         if noise_in_logits and gumbel is not None:
-            logits = np.add(_f32(logits), _f32(gumbel), dtype=np.float32)
-    logits = _f32(logits)
+            logits = logits + _f64(gumbel)
+        keys = logits if (gumbel is None or noise_in_logits) else (logits + _f64(gumbel)) / float(tau)
+    else:
+        if logits is None:
+            logits = router_logits(x, w_router, bias)
+            if noise_in_logits and gumbel is not None:
+                logits = np.add(_f32(logits), _f32(gumbel), dtype=np.float32)
+        logits = _f32(logits)
+        keys = selection_keys(logits, None if noise_in_logits else gumbel, tau)
     T, E = logits.shape
     real = np.ones(T, dtype=bool) if token_mask is None else (np.asarray(token_mask) != 0)
-    keys = selection_keys(logits, None if noise_in_logits else gumbel, tau)
     ids = np.full((T, k), -1, dtype=np.int32)
-    weights = np.zeros((T, k), dtype=np.float32)
+    weights = np.zeros((T, k), dtype=np.float64 if exact else np.float32)
     probs = np.zeros((T, E), dtype=np.float64)
     entropy = np.zeros(T, dtype=np.float64)
     if np.any(real):
         ids[real] = top_k(keys[real], k)
-        weights[real] = gate_weights(logits[real], ids[real], tau, renormalize)
+        weights[real] = gate_weights(logits[real], ids[real], tau, renormalize, exact)
         probs[real] = router_probs(logits[real], tau)
         entropy[real] = router_entropy(probs[real])
     return Routing(logits, keys, ids, weights, probs, real, entropy)
@@ -499,7 +513,7 @@ class Forward:
 def forward(x, w_router, w1, w2, *, k: int, storage: str, bias=None, gumbel=None,
             tau: float = 1.0, capacity: Optional[int] = None, renormalize: bool = True,
             aux_coef: float = 0.01, logits=None, noise_in_logits: bool = False,
-            token_mask=None, w1_shared=None, w2_shared=None) -> Forward:
+            token_mask=None, w1_shared=None, w2_shared=None, exact: bool = False) -> Forward:
     """Router -> top-k -> capacity + dispatch -> expert FFN -> weighted combine, plus aux.
 
     aux = (aux_switch, aux_balance, mean router entropy). With w1_shared / w2_shared, a shared
@@ -508,7 +522,7 @@ def forward(x, w_router, w1, w2, *, k: int, storage: str, bias=None, gumbel=None
     T = x.shape[0]
     E = w1.shape[0]
     C = T if capacity is None or capacity < 0 else capacity
-    r = route(x, w_router, bias, gumbel, tau, k, renormalize, logits, noise_in_logits, token_mask)
+    r = route(x, w_router, bias, gumbel, tau, k, renormalize, logits, noise_in_logits, token_mask, exact)
     dp = dispatch(r.ids, E, C, x)
     h, y = expert_ffn(dp.xp, dp.offsets, w1, w2, storage)
     ys = None
@@ -554,3 +568,117 @@ def forward_rows(x, w1, w2, ids, weights, dropped, token_idx, storage: str, w1_s
             acc += round_storage(_f64(w2_shared) @ hs, storage)
         rows.append(round_storage(acc, storage))
     return np.stack(rows) if rows else np.zeros((0, x.shape[1]))
+
+
+# ---------------------------------------------------------------------------------------------
+# backward pass  ([P4 §2.4, §3.2; P2 §3.1])
+# ---------------------------------------------------------------------------------------------
+
+def silu_grad(a) -> np.ndarray:
+    """d SiLU(a) / da = sigmoid(a) (1 + a (1 - sigmoid(a))), float64."""
+    a = np.asarray(a, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        sg = 1.0 / (1.0 + np.exp(-a))
+    return sg * (1.0 + a * (1.0 - sg))
+
+
+@dataclasses.dataclass
+class Grads:
+    dx: np.ndarray          # [T, d]
+    dw_router: np.ndarray   # [E, d]
+    dbias: np.ndarray       # [E]
+    dw1: np.ndarray         # [E, f, d]
+    dw2: np.ndarray         # [E, d, f]
+    dlogits: np.ndarray     # [T, E]
+    dweights: np.ndarray    # [T, k] gradient of the gate weights (0 for dropped and padding slots)
+    dw1_shared: Optional[np.ndarray] = None
+    dw2_shared: Optional[np.ndarray] = None
+
+
+def backward(fw: Forward, x, w_router, w1, w2, d_out, *, storage: str, tau: float = 1.0,
+             renormalize: bool = True, aux_coef: float = 0.01, d_aux: float = 1.0, w1_shared=None,
+             w2_shared=None) -> Grads:
+    """Gradients of  L = sum(d_out * out) + d_aux * aux_switch  with respect to x, the router
+    weight and bias, the expert weights and the shared expert's weights, float64.
+
+    P4 §2.4 trains the layer end to end: the output is the gate-weighted sum of the chosen
+    experts' FFN outputs, so the gradient reaches the experts through their outputs and the
+    router through the gate weights (the selection itself, the capacity cut and the noise are
+    piecewise constant: they pass no gradient). P4 §3.2 adds aux_switch = coef E sum_i f_i P_i
+    to the loss: f_i (counts) is constant, P_i is the mean router probability, so the aux term
+    reaches the router through the probabilities (aux_balance depends on counts only).
+    The forward's stored values are used as they are (H, Y after their storage rounding; the
+    shared expert's Hs is recomputed with the same rounding); the pre-activations W1 Xp and
+    W1s x are recomputed in float64.
+    """
+    r, dp = fw.routing, fw.dispatch
+    x64, wr64 = _f64(x), _f64(w_router)
+    w1_64, w2_64 = _f64(w1), _f64(w2)
+    go = _f64(d_out)
+    T, d = x64.shape
+    E, f, _ = w1_64.shape
+    k = r.ids.shape[1]
+    w = _f64(r.weights)
+    y = _f64(fw.y)
+    h = _f64(fw.h)
+    row_of = np.asarray(dp.row_of)
+    N = int(dp.offsets[-1])
+    # combine: dY[row] = w dOut[t]; dw[t, j] = <dOut[t], Y[row]>
+    dy = np.zeros((N, d), dtype=np.float64)
+    dwts = np.zeros((T, k), dtype=np.float64)
+    for j in range(k):
+        kept = row_of[:, j] >= 0
+        dy[row_of[kept, j]] = w[kept, j][:, None] * go[kept]
+        dwts[kept, j] = np.sum(go[kept] * y[row_of[kept, j]], axis=1)
+    # experts
+    perm = np.asarray(dp.perm_token).astype(np.int64)
+    xp = x64[perm]
+    dw1 = np.zeros_like(w1_64)
+    dw2 = np.zeros_like(w2_64)
+    dxp = np.zeros((N, d), dtype=np.float64)
+    for e in range(E):
+        r0, r1 = int(dp.offsets[e]), int(dp.offsets[e + 1])
+        if r1 == r0:
+            continue
+        a1 = xp[r0:r1] @ w1_64[e].T
+        dw2[e] = dy[r0:r1].T @ h[r0:r1]
+        da = (dy[r0:r1] @ w2_64[e]) * silu_grad(a1)
+        dw1[e] = da.T @ xp[r0:r1]
+        dxp[r0:r1] = da @ w1_64[e]
+    dx = np.zeros_like(x64)
+    np.add.at(dx, perm, dxp)
+    # shared expert: its output joins every token's with weight 1
+    dw1s = dw2s = None
+    if w1_shared is not None:
+        w1s, w2s = _f64(w1_shared), _f64(w2_shared)
+        a_s = x64 @ w1s.T
+        hs = round_storage(silu(a_s), storage)
+        dw2s = go.T @ hs
+        das = (go @ w2s) * silu_grad(a_s)
+        dw1s = das.T @ x64
+        dx += das @ w1s
+    # router: gate weights, then the aux term through the probabilities
+    dl = np.zeros((T, E), dtype=np.float64)
+    real = np.asarray(r.real, dtype=bool)
+    ids = np.asarray(r.ids).astype(np.int64)
+    for t in np.flatnonzero(real):
+        sel = ids[t]
+        if renormalize:
+            ww = w[t]
+            dl[t, sel] += ww * (dwts[t] - np.dot(ww, dwts[t]))
+        else:
+            p = r.probs[t]
+            g = np.zeros(E)
+            g[sel] = dwts[t]
+            dl[t] += p * (g - np.dot(p, g))
+    n = int(real.sum())
+    if n > 0 and d_aux != 0.0:
+        f_i = np.asarray(dp.counts_pre, dtype=np.float64) / (n * k)
+        g = d_aux * aux_coef * E * f_i / n
+        p = r.probs[real]
+        dl[real] += p * (g[None, :] - (p @ g)[:, None])
+    dl /= float(np.float32(tau))
+    dwr = dl.T @ x64
+    db = dl.sum(axis=0)
+    dx += dl @ wr64
+    return Grads(dx, dwr, db, dw1, dw2, dl, dwts, dw1s, dw2s)

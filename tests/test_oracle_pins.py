@@ -652,3 +652,87 @@ def test_int4_packing_layout():
     b = oracle.pack_int4(q, np.full((16, 2), 0.5))
     assert b[0] == (0x8 | (0x7 << 4)) and b[16 * (16 * 1 + 1)] == 0x1
     assert b[1024] == 0x00 and b[1025] == 0x3F      # bf16(0.5) = 0x3F00, little-endian
+
+
+# ------------------------------------------------------------------------------ backward pass
+
+def _fd_case(seed, T=24, d=12, f=10, E=5, k=2, tau=0.8, renormalize=True, capacity=None, mask=False,
+             shared=False, noise=False):
+    rng = np.random.default_rng(seed)
+    P = {"x": rng.standard_normal((T, d)), "wr": rng.standard_normal((E, d)) / np.sqrt(d),
+         "b": rng.standard_normal(E) * 0.5, "w1": rng.standard_normal((E, f, d)) * 0.3,
+         "w2": rng.standard_normal((E, d, f)) * 0.3}
+    if shared:
+        P["w1s"] = rng.standard_normal((7, d)) * 0.3
+        P["w2s"] = rng.standard_normal((d, 7)) * 0.3
+    extra = {"noise": rng.standard_normal((T, E)) * 0.1 if noise else None,
+             "mask": (rng.random(T) < 0.75).astype(np.uint8) if mask else None,
+             "d_out": rng.standard_normal((T, d))}
+    cfg = dict(k=k, tau=tau, renormalize=renormalize, capacity=capacity)
+    return P, extra, cfg
+
+
+def _loss(P, extra, cfg, d_aux):
+    fw = oracle.forward(P["x"], P["wr"], P["w1"], P["w2"], k=cfg["k"], storage="f64", bias=P["b"],
+                        gumbel=extra["noise"], tau=cfg["tau"], capacity=cfg["capacity"],
+                        renormalize=cfg["renormalize"], aux_coef=0.05, noise_in_logits=extra["noise"] is not None,
+                        token_mask=extra["mask"], w1_shared=P.get("w1s"), w2_shared=P.get("w2s"), exact=True)
+    return float(np.sum(extra["d_out"] * fw.out)) + d_aux * fw.aux[0], fw
+
+
+@pytest.mark.parametrize("case", [
+    dict(seed=1),
+    dict(seed=2, renormalize=False, tau=1.0),
+    dict(seed=3, capacity=7, k=3),                       # capacity drops (the cut is constant)
+    dict(seed=4, mask=True, noise=True, shared=True),    # padding, additive noise, a shared expert
+    dict(seed=5, k=1, E=3, tau=0.6),
+])
+def test_backward_matches_finite_differences(case):
+    """Central differences of L = sum(d_out * out) + d_aux * aux_switch along random directions,
+    on the exact (float64, unrounded) layer, against the oracle's backward pass."""
+    P, extra, cfg = _fd_case(**case)
+    d_aux = 3.0
+    L0, fw = _loss(P, extra, cfg, d_aux)
+    g = oracle.backward(fw, P["x"], P["wr"], P["w1"], P["w2"], extra["d_out"], storage="f64", tau=cfg["tau"],
+                        renormalize=cfg["renormalize"], aux_coef=0.05, d_aux=d_aux,
+                        w1_shared=P.get("w1s"), w2_shared=P.get("w2s"))
+    grads = {"x": g.dx, "wr": g.dw_router, "b": g.dbias, "w1": g.dw1, "w2": g.dw2}
+    if "w1s" in P:
+        grads.update({"w1s": g.dw1_shared, "w2s": g.dw2_shared})
+    rng = np.random.default_rng(100 + case["seed"])
+    eps = 1e-6
+    for name, grad in grads.items():
+        v = rng.standard_normal(P[name].shape)
+        Pp = dict(P); Pp[name] = P[name] + eps * v
+        Pm = dict(P); Pm[name] = P[name] - eps * v
+        lp, fp_ = _loss(Pp, extra, cfg, d_aux)
+        lm, fm_ = _loss(Pm, extra, cfg, d_aux)
+        # the routing must not change under the perturbation (it passes no gradient)
+        assert np.array_equal(fp_.routing.ids, fw.routing.ids) and np.array_equal(fm_.routing.ids, fw.routing.ids)
+        fd = (lp - lm) / (2 * eps)
+        an = float(np.sum(grad * v))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_backward_closed_forms():
+    """One token, one expert (k = 1, E = 1): w = 1, so dw_router = 0 without the aux term; the
+    expert gradients are outer products written out by hand."""
+    rng = np.random.default_rng(7)
+    d, f = 4, 3
+    x = rng.standard_normal((1, d))
+    w1 = rng.standard_normal((1, f, d))
+    w2 = rng.standard_normal((1, d, f))
+    wr = rng.standard_normal((1, d))
+    go = rng.standard_normal((1, d))
+    fw = oracle.forward(x, wr, w1, w2, k=1, storage="f64", exact=True)
+    g = oracle.backward(fw, x, wr, w1, w2, go, storage="f64", d_aux=0.0)
+    a = x[0] @ w1[0].T
+    h = a / (1 + np.exp(-a))
+    sg = 1 / (1 + np.exp(-a))
+    dh = go[0] @ w2[0]
+    da = dh * (sg + a * sg * (1 - sg))
+    assert np.allclose(g.dw2[0], np.outer(go[0], h), rtol=1e-13, atol=1e-15)
+    assert np.allclose(g.dw1[0], np.outer(da, x[0]), rtol=1e-13, atol=1e-15)
+    assert np.allclose(g.dx[0], da @ w1[0][:, :], rtol=1e-13, atol=1e-15)
+    assert np.all(g.dw_router == 0) and np.all(g.dbias == 0)
+    assert abs(g.dweights[0, 0] - float(go[0] @ (w2[0] @ h))) < 1e-13
