@@ -263,6 +263,33 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
                          const void* w2_shared, void* out, float* aux, moe_debug_outputs* dbg,
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Backward pass [P4 §2.4: the layer is trained end to end]. Gradients of
+ * L = sum(d_out * out) (+ d_aux * aux_switch) flow back through the combine, the expert FFNs and
+ * the gather; the selection, the capacity cut and the noise pass none. The calls mirror the
+ * forward ones and take the forward's intermediates (moe_forward's debug outputs). Products
+ * accumulate in fp32; stored gradients are rounded once to act.
+ * moe_backward_workspace_bytes: the workspace the backward calls take (0 if cfg is invalid).
+ * moe_combine_backward: dy[row_of[t,j]] = weights[t,j] * d_out[t] (act; rows of dropped slots
+ *   untouched) and dweights[t,j] = <d_out[t], y[row_of[t,j]]> (fp32; 0 without a row).
+ *   d_out [T, d] act, y [T*k, d] act, row_of [T, k], weights [T, k] fp32, dy [T*k, d] act,
+ *   dweights [T, k] fp32.
+ * moe_expert_ffn_backward: dxp = (dy W2_e * SiLU'(xp W1_e^T)) W1_e over each expert's rows
+ *   (the pre-activation is recomputed; bf16/fp32 weights only). xp, dy, dxp [T*k, d] act (rows
+ *   >= N of dxp untouched), offsets [E+1] as in the forward.
+ * moe_dispatch_backward: dx[t] = sum over kept slots of dxp[row_of[t,j]] (fp32, one rounding);
+ *   dx [T, d] act.
+ */
+size_t moe_backward_workspace_bytes(const moe_config_t* cfg);
+moe_status_t moe_combine_backward(const moe_config_t* cfg, const void* d_out, const void* y,
+                                  const int32_t* row_of, const float* weights, void* dy,
+                                  float* dweights, hipStream_t stream);
+moe_status_t moe_expert_ffn_backward(const moe_config_t* cfg, const void* xp, const int32_t* offsets,
+                                     const void* w1, const void* w2, const void* dy, void* dxp,
+                                     void* ws, size_t ws_bytes, hipStream_t stream);
+moe_status_t moe_dispatch_backward(const moe_config_t* cfg, const void* dxp, const int32_t* row_of,
+                                   void* dx, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

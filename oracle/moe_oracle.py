@@ -582,6 +582,55 @@ def silu_grad(a) -> np.ndarray:
     return sg * (1.0 + a * (1.0 - sg))
 
 
+def combine_backward(d_out, y, row_of, weights, storage: str):
+    """The combine's backward: dY[row_of[t, j]] = w[t, j] dOut[t] (rounded to the storage dtype)
+    and dw[t, j] = <dOut[t], Y[row_of[t, j]]> (float64; 0 for a slot without a row)."""
+    go, y, w = _f64(d_out), _f64(y), _f64(weights)
+    row_of = np.asarray(row_of)
+    T, k = row_of.shape
+    dy = np.zeros((y.shape[0], go.shape[1]), dtype=np.float64)
+    dw = np.zeros((T, k), dtype=np.float64)
+    for j in range(k):
+        kept = row_of[:, j] >= 0
+        dy[row_of[kept, j]] = w[kept, j][:, None] * go[kept]
+        dw[kept, j] = np.sum(go[kept] * y[row_of[kept, j]], axis=1)
+    return round_storage(dy, storage), dw
+
+
+def expert_ffn_backward(xp, offsets, w1, w2, h, dy, storage: str):
+    """The expert FFNs' backward over each expert's rows: with A = Xp W1_e^T (recomputed),
+    dA = (dY W2_e) * SiLU'(A), dXp = dA W1_e (rounded to the storage dtype), dW2_e = dY^T H,
+    dW1_e = dA^T Xp (float64)."""
+    xp, w1, w2, h, dy = _f64(xp), _f64(w1), _f64(w2), _f64(h), _f64(dy)
+    E = w1.shape[0]
+    N = int(offsets[-1])
+    dxp = np.zeros((N, xp.shape[1]), dtype=np.float64)
+    dw1 = np.zeros_like(w1)
+    dw2 = np.zeros_like(w2)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        a1 = xp[r0:r1] @ w1[e].T
+        dw2[e] = dy[r0:r1].T @ h[r0:r1]
+        da = (dy[r0:r1] @ w2[e]) * silu_grad(a1)
+        dw1[e] = da.T @ xp[r0:r1]
+        dxp[r0:r1] = da @ w1[e]
+    return round_storage(dxp, storage), dw1, dw2
+
+
+def dispatch_backward(dxp, row_of, T: int, storage: str):
+    """The gather's backward: dx[t] = sum over the token's kept slots of dXp[row_of[t, j]], in slot
+    order, rounded once to the storage dtype."""
+    dxp = _f64(dxp)
+    row_of = np.asarray(row_of)
+    dx = np.zeros((T, dxp.shape[1]), dtype=np.float64)
+    for j in range(row_of.shape[1]):
+        kept = row_of[:, j] >= 0
+        dx[kept] += dxp[row_of[kept, j]]
+    return round_storage(dx, storage)
+
+
 @dataclasses.dataclass
 class Grads:
     dx: np.ndarray          # [T, d]
@@ -622,31 +671,10 @@ def backward(fw: Forward, x, w_router, w1, w2, d_out, *, storage: str, tau: floa
     y = _f64(fw.y)
     h = _f64(fw.h)
     row_of = np.asarray(dp.row_of)
-    N = int(dp.offsets[-1])
-    # combine: dY[row] = w dOut[t]; dw[t, j] = <dOut[t], Y[row]>
-    dy = np.zeros((N, d), dtype=np.float64)
-    dwts = np.zeros((T, k), dtype=np.float64)
-    for j in range(k):
-        kept = row_of[:, j] >= 0
-        dy[row_of[kept, j]] = w[kept, j][:, None] * go[kept]
-        dwts[kept, j] = np.sum(go[kept] * y[row_of[kept, j]], axis=1)
-    # experts
+    dy, dwts = combine_backward(go, y, row_of, w, "f64")
     perm = np.asarray(dp.perm_token).astype(np.int64)
-    xp = x64[perm]
-    dw1 = np.zeros_like(w1_64)
-    dw2 = np.zeros_like(w2_64)
-    dxp = np.zeros((N, d), dtype=np.float64)
-    for e in range(E):
-        r0, r1 = int(dp.offsets[e]), int(dp.offsets[e + 1])
-        if r1 == r0:
-            continue
-        a1 = xp[r0:r1] @ w1_64[e].T
-        dw2[e] = dy[r0:r1].T @ h[r0:r1]
-        da = (dy[r0:r1] @ w2_64[e]) * silu_grad(a1)
-        dw1[e] = da.T @ xp[r0:r1]
-        dxp[r0:r1] = da @ w1_64[e]
-    dx = np.zeros_like(x64)
-    np.add.at(dx, perm, dxp)
+    dxp, dw1, dw2 = expert_ffn_backward(x64[perm], dp.offsets, w1_64, w2_64, h, dy, "f64")
+    dx = dispatch_backward(dxp, row_of, T, "f64")
     # shared expert: its output joins every token's with weight 1
     dw1s = dw2s = None
     if w1_shared is not None:

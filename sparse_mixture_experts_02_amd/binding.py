@@ -31,7 +31,8 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPOR
 # Every symbol include/moe.h declares.
 EXPORTED_SYMBOLS = ("moe_status_string", "moe_validate_config", "moe_capacity_from_factor",
                     "moe_int4_bytes", "moe_quantize_int4", "moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-                    "moe_aux_loss", "moe_forward")
+                    "moe_aux_loss", "moe_forward", "moe_backward_workspace_bytes", "moe_combine_backward",
+                    "moe_expert_ffn_backward", "moe_dispatch_backward")
 
 
 class MoEError(RuntimeError):
@@ -123,6 +124,14 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [cfgp] + [vp] * 5 + [vp]
         L.moe_aux_loss.restype = ctypes.c_int
         L.moe_aux_loss.argtypes = [cfgp] + [vp] * 5 + [vp, sz, vp]
+        L.moe_backward_workspace_bytes.restype = sz
+        L.moe_backward_workspace_bytes.argtypes = [cfgp]
+        L.moe_combine_backward.restype = ctypes.c_int
+        L.moe_combine_backward.argtypes = [cfgp] + [vp] * 6 + [vp]
+        L.moe_expert_ffn_backward.restype = ctypes.c_int
+        L.moe_expert_ffn_backward.argtypes = [cfgp] + [vp] * 6 + [vp, sz, vp]
+        L.moe_dispatch_backward.restype = ctypes.c_int
+        L.moe_dispatch_backward.argtypes = [cfgp] + [vp] * 3 + [vp]
         L.moe_forward.restype = ctypes.c_int
         L.moe_forward.argtypes = [cfgp] + [vp] * 11 + [ctypes.POINTER(_Debug), vp, sz, vp]
         _lib = L
@@ -300,6 +309,52 @@ def moe_forward(cfg: MoEConfig, x, w_router, w1, w2, out, aux, ws, *, bias=None,
         _ptr(aux, "aux", (3,), torch.float32), ctypes.byref(dbg) if dbg is not None else None,
         _ptr(ws, "ws"), ws.numel(), _stream())
     _check("moe_forward", st)
+
+
+# ------------------------------------------------------------------------------ backward pass
+
+def backward_workspace_bytes(cfg: MoEConfig) -> int:
+    c = cfg.to_c()
+    return lib().moe_backward_workspace_bytes(ctypes.byref(c))
+
+
+def new_backward_workspace(cfg: MoEConfig, device="cuda") -> torch.Tensor:
+    n = backward_workspace_bytes(cfg)
+    if n == 0:
+        raise MoEError("moe_backward_workspace_bytes", validate_config(cfg))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_combine_backward(cfg: MoEConfig, d_out, y, row_of, weights, dy, dweights):
+    T, d, k = cfg.T, cfg.d_model, cfg.top_k
+    c = cfg.to_c()
+    dt = cfg.torch_dtype
+    st = lib().moe_combine_backward(
+        ctypes.byref(c), _ptr(d_out, "d_out", (T, d), dt), _ptr(y, "y", (T * k, d), dt),
+        _ptr(row_of, "row_of", (T, k), torch.int32), _ptr(weights, "weights", (T, k), torch.float32),
+        _ptr(dy, "dy", (T * k, d), dt), _ptr(dweights, "dweights", (T, k), torch.float32), _stream())
+    _check("moe_combine_backward", st)
+
+
+def moe_expert_ffn_backward(cfg: MoEConfig, xp, offsets, w1, w2, dy, dxp, ws):
+    T, d, f, E, k = cfg.T, cfg.d_model, cfg.d_ffn, cfg.num_experts, cfg.top_k
+    c = cfg.to_c()
+    dt = cfg.torch_dtype
+    st = lib().moe_expert_ffn_backward(
+        ctypes.byref(c), _ptr(xp, "xp", (T * k, d), dt), _ptr(offsets, "offsets", (E + 1,), torch.int32),
+        _ptr(w1, "w1", (E, f, d), dt), _ptr(w2, "w2", (E, d, f), dt), _ptr(dy, "dy", (T * k, d), dt),
+        _ptr(dxp, "dxp", (T * k, d), dt), _ptr(ws, "ws"), ws.numel(), _stream())
+    _check("moe_expert_ffn_backward", st)
+
+
+def moe_dispatch_backward(cfg: MoEConfig, dxp, row_of, dx):
+    T, d, k = cfg.T, cfg.d_model, cfg.top_k
+    c = cfg.to_c()
+    dt = cfg.torch_dtype
+    st = lib().moe_dispatch_backward(ctypes.byref(c), _ptr(dxp, "dxp", (T * k, d), dt),
+                                     _ptr(row_of, "row_of", (T, k), torch.int32), _ptr(dx, "dx", (T, d), dt),
+                                     _stream())
+    _check("moe_dispatch_backward", st)
 
 
 # ------------------------------------------------------------------------------ HIP events

@@ -20,7 +20,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   float my_w = 0.0f;
   if (lane < k) {
     my_row = p.row_of[(size_t)t * k + lane];
-    my_w = p.weights[(size_t)t * k + lane];
+    my_w = p.weights ? p.weights[(size_t)t * k + lane] : 1.0f;   // no weights: plain sum of the rows
     if (my_row >= p.max_rows) my_row = -1;
   }
   int rows[MOE_MAX_TOP_K_DEV];
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void combine_k2_kernel(CombineParams p) {
   float my_w = 0.0f;
   if (lane < k) {
     my_row = p.row_of[(size_t)t * k + lane];
-    my_w = p.weights[(size_t)t * k + lane];
+    my_w = p.weights ? p.weights[(size_t)t * k + lane] : 1.0f;   // no weights: plain sum of the rows
     if (my_row >= p.max_rows) my_row = -1;
   }
   const int r0 = __shfl(my_row, 0), r1 = k > 1 ? __shfl(my_row, 1) : -1;

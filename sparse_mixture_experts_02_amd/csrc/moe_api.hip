@@ -65,6 +65,34 @@ Layout layout(const moe_config_t& c) {
   return L;
 }
 
+// Backward-pass workspace: transposed expert weights, the recomputed pre-activation and the
+// gradient of H (turned into the gradient of the pre-activation in place).
+struct BwdLayout {
+  size_t w1t, w2t, a1, dh, sk_part, total;
+};
+
+BwdLayout bwd_layout(const moe_config_t& c) {
+  BwdLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  const size_t a = act_size(c), E = (size_t)c.num_experts, d = (size_t)c.d_model, f = (size_t)c.d_ffn;
+  const size_t TK = (size_t)c.T * (size_t)c.top_k;
+  L.w1t = take(E * d * f * a);
+  L.w2t = take(E * d * f * a);
+  L.a1 = take(TK * f * a);
+  L.dh = take(TK * f * a);
+  const bool bf16 = c.act_dtype == MOE_BF16;
+  const bool big = gemm_uses_big(bf16, c.d_model, c.T * c.top_k, c.num_experts) ||
+                   gemm_uses_big(bf16, c.d_ffn, c.T * c.top_k, c.num_experts);
+  L.sk_part = take(big ? gemm_big_part_bytes() : 0);
+  L.total = off;
+  return L;
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
@@ -180,12 +208,14 @@ moe_status_t run_gather(const moe_config_t& c, const int32_t* ids, const void* x
 
 // One grouped GEMM over `experts` segments of at most `rows` rows in total (the routed experts:
 // E segments of the T k permuted rows; the shared expert: one segment of the T tokens).
-moe_status_t run_gemm(const moe_config_t& c, const void* a, const void* b, void* out, const int32_t* offsets,
-                      int n, int kdim, bool silu, void* ws, hipStream_t s, int experts = -1, int rows = -1) {
+// `sk` is the split-tail partial-sum region of the caller's workspace (null: no split tail).
+moe_status_t run_gemm_sk(const moe_config_t& c, const void* a, const void* b, void* out, const int32_t* offsets,
+                         int n, int kdim, bool silu, void* sk, hipStream_t s, int experts = -1, int rows = -1,
+                         bool int4 = false) {
   if (experts < 0) experts = c.num_experts;
   if (rows < 0) rows = c.T * c.top_k;
   GemmParams p{};
-  if (gemm_uses_big(c.act_dtype == MOE_BF16, kdim, rows, experts)) p.sk_part = at(ws, layout(c).sk_part);
+  if (gemm_uses_big(c.act_dtype == MOE_BF16, kdim, rows, experts)) p.sk_part = sk;
   p.E = experts;
   p.N = n;
   p.K = kdim;
@@ -194,13 +224,19 @@ moe_status_t run_gemm(const moe_config_t& c, const void* a, const void* b, void*
   p.B = b;
   p.C = out;
   p.offsets = offsets;
-  if (c.weight_dtype == MOE_INT4) {
+  if (int4) {
     p.q4_scale_off = q4_scale_offset((size_t)experts * (size_t)n, kdim);
     MOE_LAUNCH(launch_gemm_q4(p, silu, s));
   } else {
     MOE_LAUNCH(launch_gemm(p, c.act_dtype == MOE_BF16, silu, s));
   }
   return MOE_OK;
+}
+
+moe_status_t run_gemm(const moe_config_t& c, const void* a, const void* b, void* out, const int32_t* offsets,
+                      int n, int kdim, bool silu, void* ws, hipStream_t s, int experts = -1, int rows = -1) {
+  return run_gemm_sk(c, a, b, out, offsets, n, kdim, silu, at(ws, layout(c).sk_part), s, experts, rows,
+                     c.weight_dtype == MOE_INT4 && experts < 0);
 }
 
 moe_status_t run_combine(const moe_config_t& c, const void* y, const int32_t* row_of, const float* weights,
@@ -443,6 +479,66 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
   MOE_TRY(run_combine(c, y, row_of, weights, ys, out, stream));
   MOE_TRY(mark());
   return MOE_OK;
+}
+
+// ---- backward pass
+
+size_t moe_backward_workspace_bytes(const moe_config_t* cfg) {
+  if (moe_validate_config(cfg) != MOE_OK) return 0;
+  return bwd_layout(*cfg).total;
+}
+
+moe_status_t moe_combine_backward(const moe_config_t* cfg, const void* d_out, const void* y, const int32_t* row_of,
+                                  const float* weights, void* dy, float* dweights, hipStream_t stream) {
+  MOE_TRY(moe_validate_config(cfg));
+  if (!d_out || !y || !row_of || !weights || !dy || !dweights) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(d_out) || !aligned16(y) || !aligned16(dy)) return MOE_ERR_INVALID_ARGUMENT;
+  CombineBwdParams p{};
+  p.T = cfg->T;
+  p.d = cfg->d_model;
+  p.k = cfg->top_k;
+  p.max_rows = cfg->T * cfg->top_k;
+  p.d_out = d_out;
+  p.y = y;
+  p.row_of = row_of;
+  p.weights = weights;
+  p.dy = dy;
+  p.dweights = dweights;
+  MOE_LAUNCH(launch_combine_bwd(p, cfg->act_dtype == MOE_BF16, stream));
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn_backward(const moe_config_t* cfg, const void* xp, const int32_t* offsets,
+                                     const void* w1, const void* w2, const void* dy, void* dxp, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(moe_validate_config(cfg));
+  if (cfg->weight_dtype == MOE_INT4) return MOE_ERR_UNSUPPORTED;
+  if (!xp || !offsets || !w1 || !w2 || !dy || !dxp || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(xp) || !aligned16(w1) || !aligned16(w2) || !aligned16(dy) || !aligned16(dxp) || !aligned16(ws))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const moe_config_t& c = *cfg;
+  const BwdLayout L = bwd_layout(c);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const int a = (int)act_size(c), E = c.num_experts, d = c.d_model, f = c.d_ffn;
+  void* w1t = at(ws, L.w1t);   // [E, d, f]
+  void* w2t = at(ws, L.w2t);   // [E, f, d]
+  void* a1 = at(ws, L.a1);     // [T k, f] pre-activation Xp W1^T
+  void* dh = at(ws, L.dh);     // [T k, f] dH, then dA in place
+  void* sk = at(ws, L.sk_part);
+  MOE_LAUNCH(launch_transpose(w1, w1t, E, f, d, a, stream));
+  MOE_LAUNCH(launch_transpose(w2, w2t, E, d, f, a, stream));
+  MOE_TRY(run_gemm_sk(c, xp, w1, a1, offsets, f, d, false, sk, stream));
+  MOE_TRY(run_gemm_sk(c, dy, w2t, dh, offsets, f, d, false, sk, stream));
+  MOE_LAUNCH(launch_silu_bwd(dh, a1, dh, (size_t)c.T * c.top_k * f, c.act_dtype == MOE_BF16, stream));
+  MOE_TRY(run_gemm_sk(c, dh, w1t, dxp, offsets, d, f, false, sk, stream));
+  return MOE_OK;
+}
+
+moe_status_t moe_dispatch_backward(const moe_config_t* cfg, const void* dxp, const int32_t* row_of, void* dx,
+                                   hipStream_t stream) {
+  MOE_TRY(moe_validate_config(cfg));
+  if (!dxp || !row_of || !dx || !aligned16(dxp) || !aligned16(dx)) return MOE_ERR_INVALID_ARGUMENT;
+  return run_combine(*cfg, dxp, row_of, nullptr, nullptr, dx, stream);
 }
 
 }  // extern "C"

@@ -120,8 +120,19 @@ struct CombineParams {
   const void* y;
   const void* y_shared;     // [T, d] act added with weight 1 after the routed slots, or null
   const int32_t* row_of;
-  const float* weights;
+  const float* weights;     // [T, k], or null: every kept row with weight 1
   void* out;
+};
+
+struct CombineBwdParams {
+  int T, d, k;
+  int max_rows;
+  const void* d_out;        // [T, d] act
+  const void* y;            // [T*k, d] act (forward expert outputs)
+  const int32_t* row_of;    // [T, k]
+  const float* weights;     // [T, k]
+  void* dy;                 // [T*k, d] act: dY[row] = w * dOut[t]
+  float* dweights;          // [T, k]: <dOut[t], Y[row]>, 0 for slots without a row
 };
 
 struct AuxParams {
@@ -179,6 +190,13 @@ hipError_t launch_quantize_q4(const void* w, size_t rows, int K, void* out, hipS
 hipError_t launch_gemm_q4(const GemmParams& p, bool silu, hipStream_t s);
 
 hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s);
+
+// backward pass
+hipError_t launch_combine_bwd(const CombineBwdParams& p, bool bf16, hipStream_t s);
+// out[b, c, r] = in[b, r, c] for a batch of [R, C] matrices (elements of `elem` bytes, 2 or 4)
+hipError_t launch_transpose(const void* in, void* out, int B, int R, int C, int elem, hipStream_t s);
+// dA = dH * SiLU'(A), elementwise over n values (act dtype)
+hipError_t launch_silu_bwd(const void* dh, const void* a, void* da, size_t n, bool bf16, hipStream_t s);
 
 int probsum_num_blocks(int T);
 hipError_t launch_probsum(const ProbSumParams& p, hipStream_t s);
