@@ -274,9 +274,11 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
  *   untouched) and dweights[t,j] = <d_out[t], y[row_of[t,j]]> (fp32; 0 without a row).
  *   d_out [T, d] act, y [T*k, d] act, row_of [T, k], weights [T, k] fp32, dy [T*k, d] act,
  *   dweights [T, k] fp32.
- * moe_expert_ffn_backward: dxp = (dy W2_e * SiLU'(xp W1_e^T)) W1_e over each expert's rows
- *   (the pre-activation is recomputed; bf16/fp32 weights only). xp, dy, dxp [T*k, d] act (rows
- *   >= N of dxp untouched), offsets [E+1] as in the forward.
+ * moe_expert_ffn_backward: over each expert's rows, with A = xp W1_e^T (recomputed) and
+ *   dA = (dy W2_e) * SiLU'(A): dxp = dA W1_e (act; rows >= N untouched), and when not NULL
+ *   dw2[e] = dy^T h (fp32 [E, d, f], needs h) and dw1[e] = dA^T xp (fp32 [E, f, d]); an expert
+ *   with no rows gets zero weight gradients. bf16/fp32 weights only. xp, dy, dxp [T*k, d] act,
+ *   h [T*k, f] act (the forward's H), offsets [E+1] as in the forward.
  * moe_dispatch_backward: dx[t] = sum over kept slots of dxp[row_of[t,j]] (fp32, one rounding);
  *   dx [T, d] act.
  */
@@ -285,8 +287,9 @@ moe_status_t moe_combine_backward(const moe_config_t* cfg, const void* d_out, co
                                   const int32_t* row_of, const float* weights, void* dy,
                                   float* dweights, hipStream_t stream);
 moe_status_t moe_expert_ffn_backward(const moe_config_t* cfg, const void* xp, const int32_t* offsets,
-                                     const void* w1, const void* w2, const void* dy, void* dxp,
-                                     void* ws, size_t ws_bytes, hipStream_t stream);
+                                     const void* w1, const void* w2, const void* h, const void* dy,
+                                     void* dxp, float* dw1, float* dw2, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
 moe_status_t moe_dispatch_backward(const moe_config_t* cfg, const void* dxp, const int32_t* row_of,
                                    void* dx, hipStream_t stream);
 

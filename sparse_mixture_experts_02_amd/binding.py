@@ -129,7 +129,7 @@ def lib() -> ctypes.CDLL:
         L.moe_combine_backward.restype = ctypes.c_int
         L.moe_combine_backward.argtypes = [cfgp] + [vp] * 6 + [vp]
         L.moe_expert_ffn_backward.restype = ctypes.c_int
-        L.moe_expert_ffn_backward.argtypes = [cfgp] + [vp] * 6 + [vp, sz, vp]
+        L.moe_expert_ffn_backward.argtypes = [cfgp] + [vp] * 9 + [vp, sz, vp]
         L.moe_dispatch_backward.restype = ctypes.c_int
         L.moe_dispatch_backward.argtypes = [cfgp] + [vp] * 3 + [vp]
         L.moe_forward.restype = ctypes.c_int
@@ -336,14 +336,16 @@ def moe_combine_backward(cfg: MoEConfig, d_out, y, row_of, weights, dy, dweights
     _check("moe_combine_backward", st)
 
 
-def moe_expert_ffn_backward(cfg: MoEConfig, xp, offsets, w1, w2, dy, dxp, ws):
+def moe_expert_ffn_backward(cfg: MoEConfig, xp, offsets, w1, w2, dy, dxp, ws, *, h=None, dw1=None, dw2=None):
     T, d, f, E, k = cfg.T, cfg.d_model, cfg.d_ffn, cfg.num_experts, cfg.top_k
     c = cfg.to_c()
     dt = cfg.torch_dtype
     st = lib().moe_expert_ffn_backward(
         ctypes.byref(c), _ptr(xp, "xp", (T * k, d), dt), _ptr(offsets, "offsets", (E + 1,), torch.int32),
-        _ptr(w1, "w1", (E, f, d), dt), _ptr(w2, "w2", (E, d, f), dt), _ptr(dy, "dy", (T * k, d), dt),
-        _ptr(dxp, "dxp", (T * k, d), dt), _ptr(ws, "ws"), ws.numel(), _stream())
+        _ptr(w1, "w1", (E, f, d), dt), _ptr(w2, "w2", (E, d, f), dt), _ptr(h, "h", (T * k, f), dt),
+        _ptr(dy, "dy", (T * k, d), dt), _ptr(dxp, "dxp", (T * k, d), dt),
+        _ptr(dw1, "dw1", (E, f, d), torch.float32), _ptr(dw2, "dw2", (E, d, f), torch.float32),
+        _ptr(ws, "ws"), ws.numel(), _stream())
     _check("moe_expert_ffn_backward", st)
 
 

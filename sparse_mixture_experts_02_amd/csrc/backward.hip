@@ -128,3 +128,97 @@ hipError_t launch_silu_bwd(const void* dh, const void* a, void* da, size_t n, bo
 }
 
 }  // namespace moe
+
+namespace moe {
+
+// Weight gradients of the grouped GEMMs: for every expert e,
+//   G[e][m][n] = sum over the expert's rows r of P[r][m] * Q[r][n]     (fp32 result)
+// a product whose reduction runs over the expert's segment of the permuted rows (dW2 = dY^T H,
+// dW1 = dA^T Xp). bf16: 64 x 64 output tiles of 4 waves (16 rows each, four 16 x 16 MFMA blocks);
+// 32 rows of P and Q per step are staged through LDS transposed (the reduction index becomes
+// the contiguous one), then v_mfma_f32_16x16x32_bf16. fp32: one output per thread, fp32 FMA in
+// row order.
+__global__ __launch_bounds__(256) void grad_w_bf16_kernel(GradWParams p) {
+  constexpr int TP = 32 + 8;   // padded row of the transposed tiles (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t PT[64 * TP];
+  __shared__ __attribute__((aligned(16))) uint16_t QT[64 * TP];
+  const int e = blockIdx.y;
+  const int tilesN = (p.N + 63) / 64;
+  const int m0 = (blockIdx.x / tilesN) * 64, n0 = (blockIdx.x % tilesN) * 64;
+  int r0 = p.offsets[e], r1 = p.offsets[e + 1];
+  r0 = r0 < 0 ? 0 : (r0 > p.max_rows ? p.max_rows : r0);
+  r1 = r1 < r0 ? r0 : (r1 > p.max_rows ? p.max_rows : r1);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int fr = lane & 15, fg = lane >> 4;
+  const uint16_t* __restrict__ P = (const uint16_t*)p.P;
+  const uint16_t* __restrict__ Q = (const uint16_t*)p.Q;
+  f32x4_t acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int rr = tid >> 3, cc = (tid & 7) * 8;   // the loader's row within the step and column
+  for (int r = r0; r < r1; r += 32) {
+    uint4 pv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
+    if (r + rr < r1) {
+      if (m0 + cc < p.M) pv = *(const uint4*)(P + (size_t)(r + rr) * p.M + m0 + cc);
+      if (n0 + cc < p.N) qv = *(const uint4*)(Q + (size_t)(r + rr) * p.N + n0 + cc);
+    }
+    __syncthreads();   // the previous step's fragments have been read
+    const uint32_t pw[4] = {pv.x, pv.y, pv.z, pv.w}, qw[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      PT[(cc + 2 * q) * TP + rr] = (uint16_t)(pw[q] & 0xFFFFu);
+      PT[(cc + 2 * q + 1) * TP + rr] = (uint16_t)(pw[q] >> 16);
+      QT[(cc + 2 * q) * TP + rr] = (uint16_t)(qw[q] & 0xFFFFu);
+      QT[(cc + 2 * q + 1) * TP + rr] = (uint16_t)(qw[q] >> 16);
+    }
+    __syncthreads();
+    const bf16x8_t A = __builtin_bit_cast(bf16x8_t, *(const uint4*)(PT + (16 * w + fr) * TP + 8 * fg));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8_t B = __builtin_bit_cast(bf16x8_t, *(const uint4*)(QT + (16 * j + fr) * TP + 8 * fg));
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[j], 0, 0, 0);
+    }
+  }
+  // lane holds rows m0 + 16 w + 4 fg .. + 3 of column n0 + 16 j + fr
+  float* __restrict__ G = p.G + (size_t)e * p.M * p.N;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + 16 * j + fr;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int m = m0 + 16 * w + 4 * fg + t;
+      if (m < p.M && n < p.N) G[(size_t)m * p.N + n] = acc[j][t];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void grad_w_f32_kernel(GradWParams p) {
+  const int e = blockIdx.y;
+  int r0 = p.offsets[e], r1 = p.offsets[e + 1];
+  r0 = r0 < 0 ? 0 : (r0 > p.max_rows ? p.max_rows : r0);
+  r1 = r1 < r0 ? r0 : (r1 > p.max_rows ? p.max_rows : r1);
+  const float* __restrict__ P = (const float*)p.P;
+  const float* __restrict__ Q = (const float*)p.Q;
+  const size_t MN = (size_t)p.M * p.N;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < MN; i += (size_t)gridDim.x * blockDim.x) {
+    const int m = (int)(i / p.N), n = (int)(i % p.N);
+    float s = 0.0f;
+    for (int r = r0; r < r1; ++r) s = fmaf(P[(size_t)r * p.M + m], Q[(size_t)r * p.N + n], s);
+    p.G[(size_t)e * MN + i] = s;
+  }
+}
+
+hipError_t launch_grad_w(const GradWParams& p, bool bf16, hipStream_t s) {
+  if (bf16) {
+    dim3 grid(((p.M + 63) / 64) * ((p.N + 63) / 64), p.E);
+    grad_w_bf16_kernel<<<grid, 256, 0, s>>>(p);
+  } else {
+    size_t blocks = ((size_t)p.M * p.N + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    dim3 grid((unsigned)blocks, p.E);
+    grad_w_f32_kernel<<<grid, 256, 0, s>>>(p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

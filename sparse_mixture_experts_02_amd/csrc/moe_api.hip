@@ -509,16 +509,18 @@ moe_status_t moe_combine_backward(const moe_config_t* cfg, const void* d_out, co
 }
 
 moe_status_t moe_expert_ffn_backward(const moe_config_t* cfg, const void* xp, const int32_t* offsets,
-                                     const void* w1, const void* w2, const void* dy, void* dxp, void* ws,
-                                     size_t ws_bytes, hipStream_t stream) {
+                                     const void* w1, const void* w2, const void* h, const void* dy, void* dxp,
+                                     float* dw1, float* dw2, void* ws, size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(moe_validate_config(cfg));
   if (cfg->weight_dtype == MOE_INT4) return MOE_ERR_UNSUPPORTED;
-  if (!xp || !offsets || !w1 || !w2 || !dy || !dxp || !ws) return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned16(xp) || !aligned16(w1) || !aligned16(w2) || !aligned16(dy) || !aligned16(dxp) || !aligned16(ws))
+  if (!xp || !offsets || !w1 || !w2 || !dy || !dxp || !ws || (dw2 && !h)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(xp) || !aligned16(w1) || !aligned16(w2) || !aligned16(dy) || !aligned16(dxp) || !aligned16(ws) ||
+      (h && !aligned16(h)))
     return MOE_ERR_INVALID_ARGUMENT;
   const moe_config_t& c = *cfg;
   const BwdLayout L = bwd_layout(c);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const bool bf16 = c.act_dtype == MOE_BF16;
   const int a = (int)act_size(c), E = c.num_experts, d = c.d_model, f = c.d_ffn;
   void* w1t = at(ws, L.w1t);   // [E, d, f]
   void* w2t = at(ws, L.w2t);   // [E, f, d]
@@ -529,8 +531,28 @@ moe_status_t moe_expert_ffn_backward(const moe_config_t* cfg, const void* xp, co
   MOE_LAUNCH(launch_transpose(w2, w2t, E, d, f, a, stream));
   MOE_TRY(run_gemm_sk(c, xp, w1, a1, offsets, f, d, false, sk, stream));
   MOE_TRY(run_gemm_sk(c, dy, w2t, dh, offsets, f, d, false, sk, stream));
-  MOE_LAUNCH(launch_silu_bwd(dh, a1, dh, (size_t)c.T * c.top_k * f, c.act_dtype == MOE_BF16, stream));
+  GradWParams g{};
+  g.E = E;
+  g.max_rows = c.T * c.top_k;
+  g.offsets = offsets;
+  if (dw2) {   // dW2_e = dY^T H over the expert's rows: [d, f]
+    g.M = d;
+    g.N = f;
+    g.P = dy;
+    g.Q = h;
+    g.G = dw2;
+    MOE_LAUNCH(launch_grad_w(g, bf16, stream));
+  }
+  MOE_LAUNCH(launch_silu_bwd(dh, a1, dh, (size_t)c.T * c.top_k * f, bf16, stream));
   MOE_TRY(run_gemm_sk(c, dh, w1t, dxp, offsets, d, f, false, sk, stream));
+  if (dw1) {   // dW1_e = dA^T Xp over the expert's rows: [f, d]
+    g.M = f;
+    g.N = d;
+    g.P = dh;
+    g.Q = xp;
+    g.G = dw1;
+    MOE_LAUNCH(launch_grad_w(g, bf16, stream));
+  }
   return MOE_OK;
 }
 

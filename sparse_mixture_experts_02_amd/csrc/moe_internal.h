@@ -192,6 +192,15 @@ hipError_t launch_gemm_q4(const GemmParams& p, bool silu, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s);
 
 // backward pass
+struct GradWParams {
+  int E, M, N;              // output per expert [M, N]
+  int max_rows;             // rows of P and Q (T * k)
+  const void* P;            // [rows, M] act
+  const void* Q;            // [rows, N] act
+  const int32_t* offsets;   // [E+1] expert segments of the rows
+  float* G;                 // [E, M, N] fp32
+};
+hipError_t launch_grad_w(const GradWParams& p, bool bf16, hipStream_t s);
 hipError_t launch_combine_bwd(const CombineBwdParams& p, bool bf16, hipStream_t s);
 // out[b, c, r] = in[b, r, c] for a batch of [R, C] matrices (elements of `elem` bytes, 2 or 4)
 hipError_t launch_transpose(const void* in, void* out, int B, int R, int C, int elem, hipStream_t s);

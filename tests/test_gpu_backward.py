@@ -54,7 +54,10 @@ def test_backward_steps(name):
     moe.moe_combine_backward(cfg, d_out.to(dev), y, row_of, wts, dy, dwt)
     ws = moe.new_backward_workspace(cfg)
     dxp = torch.zeros(T * k, d, dtype=dt, device=dev)
-    moe.moe_expert_ffn_backward(cfg, xp, off, dinp["w1"], dinp["w2"], dy, dxp, ws)
+    f = cfg.d_ffn
+    dw1 = torch.full((E, f, d), float("nan"), dtype=torch.float32, device=dev)
+    dw2 = torch.full((E, d, f), float("nan"), dtype=torch.float32, device=dev)
+    moe.moe_expert_ffn_backward(cfg, xp, off, dinp["w1"], dinp["w2"], dy, dxp, ws, h=h.to(dev), dw1=dw1, dw2=dw2)
     dx = torch.empty(T, d, dtype=dt, device=dev)
     moe.moe_dispatch_backward(cfg, dxp, row_of, dx)
     torch.cuda.synchronize()
@@ -65,13 +68,19 @@ def test_backward_steps(name):
     dw_err = normwise(dwt.cpu().numpy(), dw_ref)
     assert dw_err <= 1e-5, f"gate-weight gradient normwise error {dw_err}"
     # expert FFN backward on the GPU's dY
-    dxp_ref, _, _ = oracle.expert_ffn_backward(g["xp"][:N], g["offsets"].numpy(), inp["w1"], inp["w2"], h[:N],
-                                               dy.cpu()[:N], st)
+    dxp_ref, dw1_ref, dw2_ref = oracle.expert_ffn_backward(g["xp"][:N], g["offsets"].numpy(), inp["w1"],
+                                                           inp["w2"], h[:N], dy.cpu()[:N], st)
     dxp_err = normwise(dxp.cpu().float().numpy()[:N], dxp_ref)
     assert dxp_err <= tol, f"dXp normwise error {dxp_err}"
+    # weight gradients: dW2 from the GPU's dY and H exactly as the oracle has them; dW1 from the
+    # GPU's dA (bf16-rounded there), so its tolerance is the storage one
+    dw2_err = normwise(dw2.cpu().numpy(), dw2_ref)
+    dw1_err = normwise(dw1.cpu().numpy(), dw1_ref)
+    assert dw2_err <= (1e-5 if st == "f32" else 1e-5), f"dW2 normwise error {dw2_err}"
+    assert dw1_err <= tol, f"dW1 normwise error {dw1_err}"
     # gather backward on the GPU's dXp
     dx_ref = oracle.dispatch_backward(dxp.cpu()[:max(N, 1)], g["row_of"].numpy(), T, st)
     dx_err = normwise(dx.cpu().float().numpy(), dx_ref)
     assert dx_err <= tol, f"dx normwise error {dx_err}"
-    print(f"[gpu] {name}: dY {normwise(gdy, dy_ref[:N]):.2e} dw {dw_err:.2e} dXp {dxp_err:.2e} dx {dx_err:.2e}",
-          flush=True)
+    print(f"[gpu] {name}: dY {normwise(gdy, dy_ref[:N]):.2e} dw {dw_err:.2e} dXp {dxp_err:.2e} dx {dx_err:.2e} "
+          f"dW2 {dw2_err:.2e} dW1 {dw1_err:.2e}", flush=True)
