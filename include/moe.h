@@ -281,6 +281,20 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
  *   h [T*k, f] act (the forward's H), offsets [E+1] as in the forward.
  * moe_dispatch_backward: dx[t] = sum over kept slots of dxp[row_of[t,j]] (fp32, one rounding);
  *   dx [T, d] act.
+ * moe_route_backward: the router's share [P2 §3.1 softmax gating with temperature; P4 §3.2
+ *   aux_switch through the mean probabilities]. Per real token (token_mask NULL or nonzero),
+ *   with the gate weights w and their gradients dw (moe_combine_backward's dweights):
+ *   renormalised weights (softmax over the k selected logits / tau) give
+ *   dL[t, sel_j] = w_j (dw_j - sum_i w_i dw_i) / tau; otherwise (w = the full softmax p)
+ *   dL[t] = p * (g - <p, g>) / tau with g the dw scattered to the selected experts. d_aux != 0
+ *   adds p * (a - <p, a>) / tau with a_e = d_aux coef E f_e / n, f_e = counts_pre[e] / (n k),
+ *   n = sum(counts_pre) / k the real tokens. Padding tokens get dL = 0. Then, each when not
+ *   NULL: dx[t] += dL[t] W_r (fp32 products, the sum added to dx's act value with one more
+ *   rounding), dw_router = dL^T x (fp32 [E, d], deterministic order), dbias = sum_t dL[t].
+ *   logits [T, E] fp32 are the forward's (moe_route's logits_out: bias and additive noise in
+ *   them); ids, weights [T, k] as moe_route wrote them; dweights [T, k] fp32; counts_pre [E]
+ *   (needed when d_aux != 0); dlogits [T, E] fp32 out (required). dx needs w_router; dw_router
+ *   needs x and the backward workspace. Noise and the selection pass no gradient.
  */
 size_t moe_backward_workspace_bytes(const moe_config_t* cfg);
 moe_status_t moe_combine_backward(const moe_config_t* cfg, const void* d_out, const void* y,
@@ -292,6 +306,12 @@ moe_status_t moe_expert_ffn_backward(const moe_config_t* cfg, const void* xp, co
                                      hipStream_t stream);
 moe_status_t moe_dispatch_backward(const moe_config_t* cfg, const void* dxp, const int32_t* row_of,
                                    void* dx, hipStream_t stream);
+moe_status_t moe_route_backward(const moe_config_t* cfg, const void* x, const float* w_router,
+                                const float* logits, const int32_t* ids, const float* weights,
+                                const float* dweights, const int32_t* counts_pre,
+                                const uint8_t* token_mask, float d_aux, float* dlogits, void* dx,
+                                float* dw_router, float* dbias, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
 
 #ifdef __cplusplus
 }

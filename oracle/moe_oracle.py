@@ -685,28 +685,57 @@ def backward(fw: Forward, x, w_router, w1, w2, d_out, *, storage: str, tau: floa
         das = (go @ w2s) * silu_grad(a_s)
         dw1s = das.T @ x64
         dx += das @ w1s
-    # router: gate weights, then the aux term through the probabilities
+    dl = router_backward(r.probs, r.ids, w, r.real, dwts, dp.counts_pre, tau=tau, renormalize=renormalize,
+                         aux_coef=aux_coef, d_aux=d_aux)
+    dwr, db, dx_r = router_input_grads(dl, x64, wr64)
+    dx += dx_r
+    return Grads(dx, dwr, db, dw1, dw2, dl, dwts, dw1s, dw2s)
+
+
+def router_backward(probs, ids, weights, real, dweights, counts_pre, *, tau: float, renormalize: bool,
+                    aux_coef: float, d_aux: float) -> np.ndarray:
+    """Gradient of the router logits [T, E], float64, from the gate-weight gradients and the aux term.
+
+    P2 §3.1: the gate weights are a softmax of logits / tau, over the k selected logits when
+    renormalised (w_j = exp(z_j) / sum_sel exp(z_i)), else over all E (w_j = p_j); the softmax
+    Jacobian gives dz = w (dw - <w, dw>) on the selected entries (the renormalised case) or
+    p (g - <p, g>) with g the dw scattered over the experts. P4 §3.2's aux_switch
+    = coef E sum_i f_i P_i with constant f_i = counts_pre_i / (n k) and P_i the mean of p_i over
+    the n real tokens has d aux / d p[t, i] = coef E f_i / n, which reaches the logits through the
+    same softmax Jacobian. The chain rule through z = logits / tau divides both by tau. Padding
+    tokens (real False) get zeros.
+    """
+    probs = np.asarray(probs, dtype=np.float64)
+    w = _f64(weights)
+    dwts = _f64(dweights)
+    T, E = probs.shape
+    k = np.asarray(ids).shape[1]
     dl = np.zeros((T, E), dtype=np.float64)
-    real = np.asarray(r.real, dtype=bool)
-    ids = np.asarray(r.ids).astype(np.int64)
+    real = np.asarray(real, dtype=bool)
+    ids = np.asarray(ids).astype(np.int64)
     for t in np.flatnonzero(real):
         sel = ids[t]
         if renormalize:
             ww = w[t]
             dl[t, sel] += ww * (dwts[t] - np.dot(ww, dwts[t]))
         else:
-            p = r.probs[t]
+            p = probs[t]
             g = np.zeros(E)
             g[sel] = dwts[t]
             dl[t] += p * (g - np.dot(p, g))
     n = int(real.sum())
     if n > 0 and d_aux != 0.0:
-        f_i = np.asarray(dp.counts_pre, dtype=np.float64) / (n * k)
+        f_i = np.asarray(counts_pre, dtype=np.float64) / (n * k)
         g = d_aux * aux_coef * E * f_i / n
-        p = r.probs[real]
+        p = probs[real]
         dl[real] += p * (g[None, :] - (p @ g)[:, None])
     dl /= float(np.float32(tau))
-    dwr = dl.T @ x64
-    db = dl.sum(axis=0)
-    dx += dl @ wr64
-    return Grads(dx, dwr, db, dw1, dw2, dl, dwts, dw1s, dw2s)
+    return dl
+
+
+def router_input_grads(dl, x, w_router):
+    """The linear router's gradients from dL = d loss / d logits (logits = x W_r^T + b): dW_r = dL^T x,
+    db = sum over tokens of dL, dx = dL W_r; float64."""
+    dl = np.asarray(dl, dtype=np.float64)
+    x64, wr64 = _f64(x), _f64(w_router)
+    return dl.T @ x64, dl.sum(axis=0), dl @ wr64

@@ -32,7 +32,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPOR
 EXPORTED_SYMBOLS = ("moe_status_string", "moe_validate_config", "moe_capacity_from_factor",
                     "moe_int4_bytes", "moe_quantize_int4", "moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
                     "moe_aux_loss", "moe_forward", "moe_backward_workspace_bytes", "moe_combine_backward",
-                    "moe_expert_ffn_backward", "moe_dispatch_backward")
+                    "moe_expert_ffn_backward", "moe_dispatch_backward", "moe_route_backward")
 
 
 class MoEError(RuntimeError):
@@ -132,6 +132,8 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_ffn_backward.argtypes = [cfgp] + [vp] * 9 + [vp, sz, vp]
         L.moe_dispatch_backward.restype = ctypes.c_int
         L.moe_dispatch_backward.argtypes = [cfgp] + [vp] * 3 + [vp]
+        L.moe_route_backward.restype = ctypes.c_int
+        L.moe_route_backward.argtypes = [cfgp] + [vp] * 8 + [ctypes.c_float] + [vp] * 5 + [sz, vp]
         L.moe_forward.restype = ctypes.c_int
         L.moe_forward.argtypes = [cfgp] + [vp] * 11 + [ctypes.POINTER(_Debug), vp, sz, vp]
         _lib = L
@@ -357,6 +359,24 @@ def moe_dispatch_backward(cfg: MoEConfig, dxp, row_of, dx):
                                      _ptr(row_of, "row_of", (T, k), torch.int32), _ptr(dx, "dx", (T, d), dt),
                                      _stream())
     _check("moe_dispatch_backward", st)
+
+
+def moe_route_backward(cfg: MoEConfig, logits, ids, weights, dweights, dlogits, *, x=None, w_router=None,
+                       counts_pre=None, token_mask=None, d_aux: float = 0.0, dx=None, dw_router=None, dbias=None,
+                       ws=None):
+    T, d, E, k = cfg.T, cfg.d_model, cfg.num_experts, cfg.top_k
+    c = cfg.to_c()
+    dt = cfg.torch_dtype
+    f32 = torch.float32
+    st = lib().moe_route_backward(
+        ctypes.byref(c), _ptr(x, "x", (T, d), dt), _ptr(w_router, "w_router", (E, d), f32),
+        _ptr(logits, "logits", (T, E), f32), _ptr(ids, "ids", (T, k), torch.int32),
+        _ptr(weights, "weights", (T, k), f32), _ptr(dweights, "dweights", (T, k), f32),
+        _ptr(counts_pre, "counts_pre", (E,), torch.int32), _ptr(token_mask, "token_mask", (T,), torch.uint8),
+        float(d_aux), _ptr(dlogits, "dlogits", (T, E), f32), _ptr(dx, "dx", (T, d), dt),
+        _ptr(dw_router, "dw_router", (E, d), f32), _ptr(dbias, "dbias", (E,), f32), _ptr(ws, "ws"),
+        0 if ws is None else ws.numel(), _stream())
+    _check("moe_route_backward", st)
 
 
 # ------------------------------------------------------------------------------ HIP events

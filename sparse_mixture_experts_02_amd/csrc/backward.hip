@@ -222,3 +222,234 @@ hipError_t launch_grad_w(const GradWParams& p, bool bf16, hipStream_t s) {
 }
 
 }  // namespace moe
+
+namespace moe {
+
+// Router backward, per token (one wave, lane e = expert e; E <= 64): the gradient of the logits
+// from the gate-weight gradients (softmax over the selected logits / tau, or the full softmax
+// when the weights are not renormalised) plus the aux_switch term through the probabilities:
+//   d aux_switch / d p[t, i] = d_aux coef E f_i / n,  f_i = counts_pre[i] / (n k),
+// with n = sum(counts_pre) / k real tokens. Padding tokens get zero. Everything in fp32.
+__global__ __launch_bounds__(256) void route_bwd_kernel(RouteBwdParams p) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= p.T) return;
+  const int E = p.E, K = p.k;
+  const bool ok = lane < E;
+  const bool real = !p.token_mask || p.token_mask[t] != 0;
+  float dl = 0.0f;
+  if (real) {
+    const float L = ok ? p.logits[(size_t)t * E + lane] : -INFINITY;
+    float mx = L;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+    const float z = ok ? __fdiv_rn(__fsub_rn(L, mx), p.tau) : 0.0f;
+    const float ex = ok ? expf(z) : 0.0f;
+    float s = ex;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) s = __fadd_rn(s, __shfl_xor(s, m));
+    const float prob = ex / s;
+    // this lane's selected slot, its weight and weight gradient
+    float wj = 0.0f, gj = 0.0f;
+    for (int j = 0; j < K; ++j) {
+      if (p.ids[(size_t)t * K + j] == lane) {
+        wj = p.weights[(size_t)t * K + j];
+        gj = p.dweights[(size_t)t * K + j];
+      }
+    }
+    float g = 0.0f;
+    if (p.renormalize) {
+      float wg = wj * gj;   // sum over the selected of w_j dw_j
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) wg += __shfl_xor(wg, m);
+      g = wj * (gj - wg);
+    } else {
+      float pg = prob * gj;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) pg += __shfl_xor(pg, m);
+      g = prob * (gj - pg);
+    }
+    // n k = the assignments of all real tokens = the sum of the pre-capacity counts
+    const int cnt = (ok && p.counts_pre) ? p.counts_pre[lane] : 0;
+    int nk = cnt;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) nk += __shfl_xor(nk, m);
+    if (p.d_aux != 0.0f && nk > 0) {
+      const float n = (float)(nk / K);
+      const float ga = ok ? p.d_aux * p.coef * (float)E * ((float)cnt / (float)nk) / n : 0.0f;
+      float pga = prob * ga;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) pga += __shfl_xor(pga, m);
+      g += prob * (ga - pga);
+    }
+    dl = ok ? g / p.tau : 0.0f;
+  }
+  if (ok) p.dlogits[(size_t)t * E + lane] = dl;
+}
+
+// dx[t] += sum_e dL[t, e] W_r[e]: a [T, E] x [E, d] product in fp32 FMAs (the router weight is
+// fp32). A block owns 64 tokens x 256 columns: the tokens' dL rows sit in LDS, each thread keeps
+// one column's 64 token sums in registers and reads every W_r[e, c] once. The sum is rounded once
+// more to act when added to dx.
+constexpr int RB_TOK = 64;
+template <bool BF16>
+__global__ __launch_bounds__(256) void route_bwd_dx_kernel(RouteBwdParams p) {
+  __shared__ float sdl[RB_TOK][64];
+  const int E = p.E, d = p.d;
+  const int t0 = blockIdx.y * RB_TOK;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  for (int i = threadIdx.x; i < RB_TOK * 64; i += 256) {
+    const int tt = i >> 6, e = i & 63;
+    const int t = t0 + tt;
+    sdl[tt][e] = (t < p.T && e < E) ? p.dlogits[(size_t)t * E + e] : 0.0f;
+  }
+  __syncthreads();
+  if (c >= d) return;
+  float acc[RB_TOK];
+#pragma unroll
+  for (int tt = 0; tt < RB_TOK; ++tt) acc[tt] = 0.0f;
+  for (int e = 0; e < E; ++e) {
+    const float w = p.w_router[(size_t)e * d + c];
+#pragma unroll
+    for (int tt = 0; tt < RB_TOK; ++tt) acc[tt] = fmaf(sdl[tt][e], w, acc[tt]);
+  }
+  const int nt = min(RB_TOK, p.T - t0);
+#pragma unroll
+  for (int tt = 0; tt < RB_TOK; ++tt) {
+    if (tt < nt) {
+      const size_t o = (size_t)(t0 + tt) * d + c;
+      if constexpr (BF16) {
+        uint16_t* dx = (uint16_t*)p.dx;
+        dx[o] = (uint16_t)f32_to_bf16_bits(__fadd_rn(bf16_bits_to_f32(dx[o]), acc[tt]));
+      } else {
+        float* dx = (float*)p.dx;
+        dx[o] = __fadd_rn(dx[o], acc[tt]);
+      }
+    }
+  }
+}
+
+// dW_r[e, c] = sum_t dL[t, e] x[t, c]: a [E, T] x [T, d] product, split over token chunks. A block
+// owns one chunk x 256 columns and keeps, per thread, one column's EM expert sums; the chunk's dL
+// rows stream through LDS 64 tokens at a time. Chunk partials [chunks, E, d] are summed in chunk
+// order by route_bwd_reduce_kernel (deterministic).
+template <bool BF16, int EM>
+__global__ __launch_bounds__(256) void route_bwd_w_kernel(RouteBwdParams p) {
+  __shared__ float sdl[RB_TOK][EM];
+  const int E = p.E, d = p.d;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int tb = blockIdx.y * p.chunk_tokens;
+  const int te = min(p.T, tb + p.chunk_tokens);
+  float acc[EM];
+#pragma unroll
+  for (int e = 0; e < EM; ++e) acc[e] = 0.0f;
+  for (int t0 = tb; t0 < te; t0 += RB_TOK) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < RB_TOK * EM; i += 256) {
+      const int tt = i / EM, e = i % EM;
+      const int t = t0 + tt;
+      sdl[tt][e] = (t < te && e < E) ? p.dlogits[(size_t)t * E + e] : 0.0f;
+    }
+    __syncthreads();
+    if (c < d) {
+      const int nt = min(RB_TOK, te - t0);
+      for (int tt = 0; tt < nt; ++tt) {
+        const size_t o = (size_t)(t0 + tt) * d + c;
+        const float xv = BF16 ? bf16_bits_to_f32(((const uint16_t*)p.x)[o]) : ((const float*)p.x)[o];
+#pragma unroll
+        for (int e = 0; e < EM; ++e) acc[e] = fmaf(sdl[tt][e], xv, acc[e]);
+      }
+    }
+  }
+  if (c < d) {
+    float* part = p.part + (size_t)blockIdx.y * E * d;
+#pragma unroll
+    for (int e = 0; e < EM; ++e)
+      if (e < E) part[(size_t)e * d + c] = acc[e];
+  }
+}
+
+// dW_r = the chunk partials summed in chunk order; db[e] = sum_t dL[t, e] (a fixed-order tree over
+// 256 strided partial sums), from the blocks of the last grid row.
+__global__ __launch_bounds__(256) void route_bwd_reduce_kernel(RouteBwdParams p) {
+  const size_t n = (size_t)p.E * p.d;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (blockIdx.y == 0) {
+    if (i < n && p.dw_router) {
+      float acc = 0.0f;
+      for (int ch = 0; ch < p.chunks; ++ch) acc += p.part[(size_t)ch * n + i];
+      p.dw_router[i] = acc;
+    }
+    return;
+  }
+  // blockIdx.y == 1: bias gradient, expert blockIdx.x
+  __shared__ float red[256];
+  const int e = blockIdx.x;
+  if (e >= p.E || !p.dbias) return;
+  float acc = 0.0f;
+  for (int t = threadIdx.x; t < p.T; t += 256) acc += p.dlogits[(size_t)t * p.E + e];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int m = 128; m >= 1; m >>= 1) {
+    if ((int)threadIdx.x < m) red[threadIdx.x] += red[threadIdx.x + m];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) p.dbias[e] = red[0];
+}
+
+// token chunks of the router weight gradient: about 512 blocks in all, chunks a multiple of 64
+// tokens long (at most 512 chunks, so the partials take at most 512 * 256 * E fp32 per 256 columns).
+void route_bwd_chunks(int T, int d, int* chunks, int* chunk_tokens) {
+  const int col_tiles = (d + 255) / 256;
+  const int max_chunks = (T + RB_TOK - 1) / RB_TOK;
+  int ch = (512 + col_tiles - 1) / col_tiles;
+  ch = max(1, min(ch, max_chunks));
+  int tok = (T + ch - 1) / ch;
+  tok = (tok + RB_TOK - 1) / RB_TOK * RB_TOK;
+  *chunk_tokens = tok;
+  *chunks = (T + tok - 1) / tok;
+}
+
+size_t route_bwd_part_bytes(int T, int d, int E) {
+  int ch = 0, tok = 0;
+  route_bwd_chunks(T, d, &ch, &tok);
+  return (size_t)ch * E * d * sizeof(float);
+}
+
+hipError_t launch_route_bwd(const RouteBwdParams& p_in, bool bf16, hipStream_t s) {
+  RouteBwdParams p = p_in;
+  route_bwd_chunks(p.T, p.d, &p.chunks, &p.chunk_tokens);
+  const int grid = (p.T + 3) / 4;
+  route_bwd_kernel<<<grid, 256, 0, s>>>(p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int col_tiles = (p.d + 255) / 256;
+  if (p.dx) {
+    dim3 g(col_tiles, (p.T + RB_TOK - 1) / RB_TOK);
+    if (bf16) route_bwd_dx_kernel<true><<<g, 256, 0, s>>>(p);
+    else route_bwd_dx_kernel<false><<<g, 256, 0, s>>>(p);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (p.dw_router) {
+    dim3 g(col_tiles, p.chunks);
+#define MOE_RBW(EMV)                                                         \
+    if (bf16) route_bwd_w_kernel<true, EMV><<<g, 256, 0, s>>>(p);            \
+    else route_bwd_w_kernel<false, EMV><<<g, 256, 0, s>>>(p);
+    if (p.E <= 16) { MOE_RBW(16) }
+    else if (p.E <= 32) { MOE_RBW(32) }
+    else { MOE_RBW(64) }
+#undef MOE_RBW
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (p.dw_router || p.dbias) {
+    const size_t n = (size_t)p.E * p.d;
+    const int gx = (int)std::max<size_t>((n + 255) / 256, (size_t)p.E);
+    route_bwd_reduce_kernel<<<dim3(gx, 2), 256, 0, s>>>(p);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
+}  // namespace moe

@@ -68,7 +68,7 @@ Layout layout(const moe_config_t& c) {
 // Backward-pass workspace: transposed expert weights, the recomputed pre-activation and the
 // gradient of H (turned into the gradient of the pre-activation in place).
 struct BwdLayout {
-  size_t w1t, w2t, a1, dh, sk_part, total;
+  size_t w1t, w2t, a1, dh, sk_part, rw_part, total;
 };
 
 BwdLayout bwd_layout(const moe_config_t& c) {
@@ -89,6 +89,7 @@ BwdLayout bwd_layout(const moe_config_t& c) {
   const bool big = gemm_uses_big(bf16, c.d_model, c.T * c.top_k, c.num_experts) ||
                    gemm_uses_big(bf16, c.d_ffn, c.T * c.top_k, c.num_experts);
   L.sk_part = take(big ? gemm_big_part_bytes() : 0);
+  L.rw_part = take(route_bwd_part_bytes(c.T, c.d_model, c.num_experts));
   L.total = off;
   return L;
 }
@@ -561,6 +562,45 @@ moe_status_t moe_dispatch_backward(const moe_config_t* cfg, const void* dxp, con
   MOE_TRY(moe_validate_config(cfg));
   if (!dxp || !row_of || !dx || !aligned16(dxp) || !aligned16(dx)) return MOE_ERR_INVALID_ARGUMENT;
   return run_combine(*cfg, dxp, row_of, nullptr, nullptr, dx, stream);
+}
+
+moe_status_t moe_route_backward(const moe_config_t* cfg, const void* x, const float* w_router, const float* logits,
+                                const int32_t* ids, const float* weights, const float* dweights,
+                                const int32_t* counts_pre, const uint8_t* token_mask, float d_aux, float* dlogits,
+                                void* dx, float* dw_router, float* dbias, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  MOE_TRY(moe_validate_config(cfg));
+  if (!logits || !ids || !weights || !dweights || !dlogits || !isfinite(d_aux)) return MOE_ERR_INVALID_ARGUMENT;
+  if (d_aux != 0.0f && !counts_pre) return MOE_ERR_INVALID_ARGUMENT;
+  if ((dx && (!w_router || !aligned16(dx))) || (dw_router && (!x || !aligned16(x) || !ws || !aligned16(ws))))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const moe_config_t& c = *cfg;
+  const BwdLayout L = bwd_layout(c);
+  if (dw_router && ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  RouteBwdParams p{};
+  p.T = c.T;
+  p.d = c.d_model;
+  p.E = c.num_experts;
+  p.k = c.top_k;
+  p.tau = c.temperature;
+  p.coef = c.aux_coef;
+  p.d_aux = d_aux;
+  p.renormalize = c.renormalize;
+  p.x = x;
+  p.w_router = w_router;
+  p.logits = logits;
+  p.ids = ids;
+  p.weights = weights;
+  p.dweights = dweights;
+  p.counts_pre = d_aux != 0.0f ? counts_pre : nullptr;
+  p.token_mask = token_mask;
+  p.dlogits = dlogits;
+  p.dx = dx;
+  p.dw_router = dw_router;
+  p.dbias = dbias;
+  p.part = dw_router ? (float*)at(ws, L.rw_part) : nullptr;
+  MOE_LAUNCH(launch_route_bwd(p, c.act_dtype == MOE_BF16, stream));
+  return MOE_OK;
 }
 
 }  // extern "C"

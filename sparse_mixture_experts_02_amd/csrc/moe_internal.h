@@ -201,6 +201,27 @@ struct GradWParams {
   float* G;                 // [E, M, N] fp32
 };
 hipError_t launch_grad_w(const GradWParams& p, bool bf16, hipStream_t s);
+struct RouteBwdParams {
+  int T, d, E, k;
+  float tau, coef, d_aux;
+  int renormalize;
+  const void* x;            // [T, d] act
+  const float* w_router;    // [E, d]
+  const float* logits;      // [T, E] (the forward's logits, noise included in the additive mode)
+  const int32_t* ids;       // [T, k]
+  const float* weights;     // [T, k]
+  const float* dweights;    // [T, k]
+  const int32_t* counts_pre;   // [E]
+  const uint8_t* token_mask;   // [T] or null
+  float* dlogits;           // [T, E] out
+  void* dx;                 // [T, d] act, accumulated into, or null
+  float* dw_router;         // [E, d] or null
+  float* dbias;             // [E] or null
+  float* part;              // [chunks, E, d] fp32 workspace of the router weight gradient
+  int chunks, chunk_tokens; // set by launch_route_bwd
+};
+size_t route_bwd_part_bytes(int T, int d, int E);
+hipError_t launch_route_bwd(const RouteBwdParams& p, bool bf16, hipStream_t s);
 hipError_t launch_combine_bwd(const CombineBwdParams& p, bool bf16, hipStream_t s);
 // out[b, c, r] = in[b, r, c] for a batch of [R, C] matrices (elements of `elem` bytes, 2 or 4)
 hipError_t launch_transpose(const void* in, void* out, int B, int R, int C, int elem, hipStream_t s);

@@ -181,3 +181,27 @@ def test_calls_validate_before_any_launch():
     dbg.events = fake
     dbg.n_events = binding.MOE_FORWARD_NUM_KERNELS
     assert forward(dbg=B(dbg), nbytes=need) == 1
+
+
+def test_route_backward_validation():
+    L = binding.lib()
+    good = _cfg().to_c()
+    fake, odd = ctypes.c_void_p(256), ctypes.c_void_p(264)
+    B = ctypes.byref
+    need = moe.backward_workspace_bytes(_cfg())
+
+    # moe_route_backward(cfg, x, w_router, logits, ids, weights, dweights, counts_pre, token_mask, d_aux,
+    #                    dlogits, dx, dw_router, dbias, ws, ws_bytes, stream)
+    def rb(x=fake, wr=fake, logits=fake, dl=fake, counts=fake, d_aux=1.0, dx=fake, dwr=fake, ws=fake, nbytes=need,
+           cfg=good):
+        return L.moe_route_backward(B(cfg), x, wr, logits, fake, fake, fake, counts, None, d_aux, dl, dx, dwr, None,
+                                    ws, nbytes, None)
+
+    assert rb(cfg=_cfg(T=0).to_c()) == 1
+    assert rb(logits=None) == 1 and rb(dl=None) == 1
+    assert rb(counts=None) == 1                       # the aux term needs the counts
+    assert rb(d_aux=float("nan")) == 1
+    assert rb(dx=fake, wr=None) == 1 and rb(dx=odd) == 1
+    assert rb(dwr=fake, x=None) == 1 and rb(x=odd) == 1 and rb(ws=None) == 1
+    assert rb(nbytes=need - 1) == 3
+    assert need > moe.backward_workspace_bytes(_cfg(T=32)) > 0

@@ -4,7 +4,9 @@ Each step gets the GPU's own inputs (the forward's intermediates, the previous s
 as the forward parity does: moe_combine_backward against the combine's backward,
 moe_expert_ffn_backward against the expert FFNs' backward, moe_dispatch_backward against the
 gather's backward. Tolerances as the forward's (normwise 2e-2 bf16, 1e-5 fp32); the gate-weight
-gradients (fp32 dot products) normwise 1e-5.
+gradients (fp32 dot products) normwise 1e-5. moe_route_backward against the oracle's router
+backward on the GPU's logits, ids, weights and counts with seeded gate-weight gradients: the
+logit, router-weight and bias gradients normwise 1e-5 (fp32 against float64), dx as stored.
 """
 import numpy as np
 import pytest
@@ -84,3 +86,63 @@ def test_backward_steps(name):
     assert dx_err <= tol, f"dx normwise error {dx_err}"
     print(f"[gpu] {name}: dY {normwise(gdy, dy_ref[:N]):.2e} dw {dw_err:.2e} dXp {dxp_err:.2e} dx {dx_err:.2e} "
           f"dW2 {dw2_err:.2e} dW1 {dw1_err:.2e}", flush=True)
+
+
+ROUTER_CASES = {
+    # renormalised weights, aux term, bf16 x (dW_r with 16 experts per thread)
+    "rbwd_bf16": (derived(BASE, name="rbwd_bf16", T=700, d_model=264, num_experts=8), 0.7),
+    # full-softmax weights, fp32, 5 experts, ragged tokens and columns
+    "rbwd_f32_full_softmax": (derived(WORKLOADS["tiny_f32"], name="rbwd_f32_full_softmax", T=333, d_model=40,
+                                      num_experts=5, top_k=3, renormalize=False, temperature=0.7), 1.3),
+    # padding, Gumbel selection, capacity, 32 experts
+    "rbwd_padding_gumbel": (derived(WORKLOADS["skewed_gumbel_capacity"], name="rbwd_padding_gumbel", T=900,
+                                    d_model=512, d_ffn=64, num_experts=24, padding=0.25), 1.0),
+    # additive noise in the logits, 64 experts, no aux gradient
+    "rbwd_noise_e64": (derived(WORKLOADS["main_noise_padding"], name="rbwd_noise_e64", T=520, d_model=128,
+                               d_ffn=64, num_experts=64, top_k=4), 0.0),
+    # the layer's full size (16384 tokens, d 2048, 8 experts)
+    "rbwd_main": (BASE, 1.0),
+}
+
+
+@pytest.mark.parametrize("name", list(ROUTER_CASES))
+def test_router_backward(name):
+    w, d_aux = ROUTER_CASES[name]
+    print(f"[gpu] router backward {name}: {w} d_aux={d_aux}", flush=True)
+    cfg = moe.config_for(w)
+    inp = make_inputs(w)
+    dinp = to_device(inp)
+    g = run_gpu(cfg, dinp)
+    T, d, E, k = cfg.T, cfg.d_model, cfg.num_experts, cfg.top_k
+    dt = cfg.torch_dtype
+    gen = torch.Generator().manual_seed(91)
+    dwts = torch.randn(T, k, generator=gen)
+    dx0 = torch.randn(T, d, generator=gen).to(dt)
+    dev = "cuda"
+    mask = inp.get("token_mask")
+    dlog = torch.full((T, E), float("nan"), device=dev)
+    dx = dx0.to(dev)
+    dwr = torch.full((E, d), float("nan"), device=dev)
+    db = torch.full((E,), float("nan"), device=dev)
+    ws = moe.new_backward_workspace(cfg)
+    moe.moe_route_backward(cfg, g["logits"].to(dev), g["ids"].to(dev), g["weights"].to(dev), dwts.to(dev), dlog,
+                           x=dinp["x"], w_router=dinp["w_router"], counts_pre=g["counts_pre"].to(dev),
+                           token_mask=dinp.get("token_mask"), d_aux=d_aux, dx=dx, dw_router=dwr, dbias=db, ws=ws)
+    torch.cuda.synchronize()
+    real = np.ones(T, dtype=bool) if mask is None else mask.numpy() != 0
+    probs = np.zeros((T, E))
+    probs[real] = oracle.router_probs(g["logits"].numpy()[real], cfg.temperature)
+    dl_ref = oracle.router_backward(probs, g["ids"].numpy(), g["weights"].numpy(), real, dwts.numpy(),
+                                    g["counts_pre"].numpy(), tau=cfg.temperature, renormalize=cfg.renormalize,
+                                    aux_coef=cfg.aux_coef, d_aux=d_aux)
+    dwr_ref, db_ref, dxr_ref = oracle.router_input_grads(dl_ref, inp["x"], inp["w_router"])
+    errs = {"dL": normwise(dlog.cpu().numpy(), dl_ref), "dW_r": normwise(dwr.cpu().numpy(), dwr_ref),
+            "db": normwise(db.cpu().numpy(), db_ref)}
+    dx_ref = dx0.double().numpy() + dxr_ref
+    errs["dx"] = normwise(dx.cpu().double().numpy(), dx_ref)
+    print(f"[gpu] {name}: " + " ".join(f"{a} {b:.2e}" for a, b in errs.items()), flush=True)
+    assert not real.all() or np.all(np.isfinite(dlog.cpu().numpy()))
+    assert np.all(dlog.cpu().numpy()[~real] == 0.0), "padding tokens must get a zero logit gradient"
+    # fp32 arithmetic against float64: 1e-5 normwise; dx is stored in act (one more rounding)
+    assert errs["dL"] <= 1e-5 and errs["dW_r"] <= 1e-5 and errs["db"] <= 1e-5, errs
+    assert errs["dx"] <= (1e-5 if cfg.dtype == "f32" else 4e-3), errs
