@@ -306,6 +306,25 @@ moe_status_t moe_expert_ffn_backward(const moe_config_t* cfg, const void* xp, co
                                      hipStream_t stream);
 moe_status_t moe_dispatch_backward(const moe_config_t* cfg, const void* dxp, const int32_t* row_of,
                                    void* dx, hipStream_t stream);
+/*
+ * moe_backward: the whole layer's backward pass in one call (the five steps above plus the shared
+ * expert's: dHs = d_out W2s, dAs = dHs * SiLU'(x W1s^T), dx += dAs W1s, dW2s = d_out^T Hs,
+ * dW1s = dAs^T x). It reads the forward's intermediates (logits, ids, weights, counts, row map,
+ * Xp, H, Y, Hs) from fwd_ws, the workspace of a moe_forward call with the same cfg, inputs and
+ * token_mask, made with dbg NULL or with only its events set (debug buffers divert those
+ * intermediates) and not reused since. d_out [T, d] act; dx [T, d] act out (required); the
+ * weight gradients are fp32 outputs written when not NULL: dw_router [E, d], dbias [E],
+ * dw1 [E, f, d], dw2 [E, d, f], dw1_shared [fs, d], dw2_shared [d, fs]. ws is the backward
+ * workspace (moe_backward_workspace_bytes). bf16/fp32 weights only (MOE_ERR_UNSUPPORTED for
+ * 4-bit weights). Calls that share fwd_ws or ws must not overlap.
+ */
+moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const float* w_router,
+                          const uint8_t* token_mask, const void* w1, const void* w2,
+                          const void* w1_shared, const void* w2_shared, const void* d_out,
+                          float d_aux, const void* fwd_ws, size_t fwd_ws_bytes, void* dx,
+                          float* dw_router, float* dbias, float* dw1, float* dw2,
+                          float* dw1_shared, float* dw2_shared, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
 moe_status_t moe_route_backward(const moe_config_t* cfg, const void* x, const float* w_router,
                                 const float* logits, const int32_t* ids, const float* weights,
                                 const float* dweights, const int32_t* counts_pre,

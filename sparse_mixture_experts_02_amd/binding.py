@@ -32,7 +32,8 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPOR
 EXPORTED_SYMBOLS = ("moe_status_string", "moe_validate_config", "moe_capacity_from_factor",
                     "moe_int4_bytes", "moe_quantize_int4", "moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
                     "moe_aux_loss", "moe_forward", "moe_backward_workspace_bytes", "moe_combine_backward",
-                    "moe_expert_ffn_backward", "moe_dispatch_backward", "moe_route_backward")
+                    "moe_expert_ffn_backward", "moe_dispatch_backward", "moe_route_backward",
+                    "moe_backward")
 
 
 class MoEError(RuntimeError):
@@ -134,6 +135,8 @@ def lib() -> ctypes.CDLL:
         L.moe_dispatch_backward.argtypes = [cfgp] + [vp] * 3 + [vp]
         L.moe_route_backward.restype = ctypes.c_int
         L.moe_route_backward.argtypes = [cfgp] + [vp] * 8 + [ctypes.c_float] + [vp] * 5 + [sz, vp]
+        L.moe_backward.restype = ctypes.c_int
+        L.moe_backward.argtypes = [cfgp] + [vp] * 8 + [ctypes.c_float, vp, sz] + [vp] * 8 + [sz, vp]
         L.moe_forward.restype = ctypes.c_int
         L.moe_forward.argtypes = [cfgp] + [vp] * 11 + [ctypes.POINTER(_Debug), vp, sz, vp]
         _lib = L
@@ -377,6 +380,29 @@ def moe_route_backward(cfg: MoEConfig, logits, ids, weights, dweights, dlogits, 
         _ptr(dw_router, "dw_router", (E, d), f32), _ptr(dbias, "dbias", (E,), f32), _ptr(ws, "ws"),
         0 if ws is None else ws.numel(), _stream())
     _check("moe_route_backward", st)
+
+
+def moe_backward(cfg: MoEConfig, x, w_router, w1, w2, d_out, fwd_ws, dx, ws, *, token_mask=None, w1_shared=None,
+                 w2_shared=None, d_aux: float = 0.0, dw_router=None, dbias=None, dw1=None, dw2=None,
+                 dw1_shared=None, dw2_shared=None):
+    """The layer's backward from the intermediates moe_forward left in `fwd_ws`."""
+    T, d, f, E = cfg.T, cfg.d_model, cfg.d_ffn, cfg.num_experts
+    fs = cfg.d_ffn_shared
+    dt = cfg.torch_dtype
+    f32 = torch.float32
+    c = cfg.to_c()
+    st = lib().moe_backward(
+        ctypes.byref(c), _ptr(x, "x", (T, d), dt), _ptr(w_router, "w_router", (E, d), f32),
+        _ptr(token_mask, "token_mask", (T,), torch.uint8), _ptr(w1, "w1", (E, f, d), dt),
+        _ptr(w2, "w2", (E, d, f), dt), _ptr(w1_shared, "w1_shared", (fs, d), dt) if fs else None,
+        _ptr(w2_shared, "w2_shared", (d, fs), dt) if fs else None, _ptr(d_out, "d_out", (T, d), dt),
+        float(d_aux), _ptr(fwd_ws, "fwd_ws"), fwd_ws.numel(), _ptr(dx, "dx", (T, d), dt),
+        _ptr(dw_router, "dw_router", (E, d), f32), _ptr(dbias, "dbias", (E,), f32),
+        _ptr(dw1, "dw1", (E, f, d), f32), _ptr(dw2, "dw2", (E, d, f), f32),
+        _ptr(dw1_shared, "dw1_shared", (fs, d), f32) if fs else None,
+        _ptr(dw2_shared, "dw2_shared", (d, fs), f32) if fs else None,
+        _ptr(ws, "ws"), ws.numel(), _stream())
+    _check("moe_backward", st)
 
 
 # ------------------------------------------------------------------------------ HIP events

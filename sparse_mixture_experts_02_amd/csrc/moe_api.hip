@@ -68,7 +68,10 @@ Layout layout(const moe_config_t& c) {
 // Backward-pass workspace: transposed expert weights, the recomputed pre-activation and the
 // gradient of H (turned into the gradient of the pre-activation in place).
 struct BwdLayout {
-  size_t w1t, w2t, a1, dh, sk_part, rw_part, total;
+  size_t w1t, w2t, a1, dh, sk_part, rw_part;
+  size_t dy, dwts, dxp, dlogits;              // moe_backward's own intermediates
+  size_t w1st, w2st, as, dhs, dxs;            // the shared expert's (empty without one)
+  size_t total;
 };
 
 BwdLayout bwd_layout(const moe_config_t& c) {
@@ -86,10 +89,21 @@ BwdLayout bwd_layout(const moe_config_t& c) {
   L.a1 = take(TK * f * a);
   L.dh = take(TK * f * a);
   const bool bf16 = c.act_dtype == MOE_BF16;
+  const size_t T = (size_t)c.T, fs = c.d_ffn_shared > 0 ? (size_t)c.d_ffn_shared : 0;
   const bool big = gemm_uses_big(bf16, c.d_model, c.T * c.top_k, c.num_experts) ||
-                   gemm_uses_big(bf16, c.d_ffn, c.T * c.top_k, c.num_experts);
+                   gemm_uses_big(bf16, c.d_ffn, c.T * c.top_k, c.num_experts) ||
+                   (fs && (gemm_uses_big(bf16, c.d_model, c.T, 1) || gemm_uses_big(bf16, c.d_ffn_shared, c.T, 1)));
   L.sk_part = take(big ? gemm_big_part_bytes() : 0);
   L.rw_part = take(route_bwd_part_bytes(c.T, c.d_model, c.num_experts));
+  L.dy = take(TK * d * a);
+  L.dwts = take(TK * 4);
+  L.dxp = take(TK * d * a);
+  L.dlogits = take(T * E * 4);
+  L.w1st = take(fs * d * a);
+  L.w2st = take(fs * d * a);
+  L.as = take(T * fs * a);
+  L.dhs = take(T * fs * a);
+  L.dxs = take(fs ? T * d * a : 0);
   L.total = off;
   return L;
 }
@@ -276,6 +290,47 @@ moe_status_t run_aux_final(const moe_config_t& c, const double* psum, int nparts
   return MOE_OK;
 }
 
+// The routed experts' backward: dXp, and dW1 / dW2 when asked for (shared by moe_expert_ffn_backward
+// and moe_backward).
+moe_status_t expert_ffn_bwd(const moe_config_t& c, const BwdLayout& L, const void* xp, const int32_t* offsets,
+                            const void* w1, const void* w2, const void* h, const void* dy, void* dxp, float* dw1,
+                            float* dw2, void* ws, hipStream_t stream) {
+  const bool bf16 = c.act_dtype == MOE_BF16;
+  const int a = (int)act_size(c), E = c.num_experts, d = c.d_model, f = c.d_ffn;
+  void* w1t = at(ws, L.w1t);   // [E, d, f]
+  void* w2t = at(ws, L.w2t);   // [E, f, d]
+  void* a1 = at(ws, L.a1);     // [T k, f] pre-activation Xp W1^T
+  void* dh = at(ws, L.dh);     // [T k, f] dH, then dA in place
+  void* sk = at(ws, L.sk_part);
+  MOE_LAUNCH(launch_transpose(w1, w1t, E, f, d, a, stream));
+  MOE_LAUNCH(launch_transpose(w2, w2t, E, d, f, a, stream));
+  MOE_TRY(run_gemm_sk(c, xp, w1, a1, offsets, f, d, false, sk, stream));
+  MOE_TRY(run_gemm_sk(c, dy, w2t, dh, offsets, f, d, false, sk, stream));
+  GradWParams g{};
+  g.E = E;
+  g.max_rows = c.T * c.top_k;
+  g.offsets = offsets;
+  if (dw2) {   // dW2_e = dY^T H over the expert's rows: [d, f]
+    g.M = d;
+    g.N = f;
+    g.P = dy;
+    g.Q = h;
+    g.G = dw2;
+    MOE_LAUNCH(launch_grad_w(g, bf16, stream));
+  }
+  MOE_LAUNCH(launch_silu_bwd(dh, a1, dh, (size_t)c.T * c.top_k * f, bf16, stream));
+  MOE_TRY(run_gemm_sk(c, dh, w1t, dxp, offsets, d, f, false, sk, stream));
+  if (dw1) {   // dW1_e = dA^T Xp over the expert's rows: [f, d]
+    g.M = f;
+    g.N = d;
+    g.P = dh;
+    g.Q = xp;
+    g.G = dw1;
+    MOE_LAUNCH(launch_grad_w(g, bf16, stream));
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -431,7 +486,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
   const Layout L = layout(*cfg);
   const moe_config_t& c = *cfg;
   auto pick = [&](void* user, size_t off) { return user ? user : (void*)at(ws, off); };
-  float* logits = (float*)D.logits;  // written only when requested
+  float* logits = (float*)pick(D.logits, L.logits);   // kept for moe_backward
   float* probs = D.probs;
   int32_t* ids = (int32_t*)pick(D.ids, L.ids);
   float* weights = (float*)pick(D.weights, L.weights);
@@ -518,43 +573,9 @@ moe_status_t moe_expert_ffn_backward(const moe_config_t* cfg, const void* xp, co
   if (!aligned16(xp) || !aligned16(w1) || !aligned16(w2) || !aligned16(dy) || !aligned16(dxp) || !aligned16(ws) ||
       (h && !aligned16(h)))
     return MOE_ERR_INVALID_ARGUMENT;
-  const moe_config_t& c = *cfg;
-  const BwdLayout L = bwd_layout(c);
+  const BwdLayout L = bwd_layout(*cfg);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  const bool bf16 = c.act_dtype == MOE_BF16;
-  const int a = (int)act_size(c), E = c.num_experts, d = c.d_model, f = c.d_ffn;
-  void* w1t = at(ws, L.w1t);   // [E, d, f]
-  void* w2t = at(ws, L.w2t);   // [E, f, d]
-  void* a1 = at(ws, L.a1);     // [T k, f] pre-activation Xp W1^T
-  void* dh = at(ws, L.dh);     // [T k, f] dH, then dA in place
-  void* sk = at(ws, L.sk_part);
-  MOE_LAUNCH(launch_transpose(w1, w1t, E, f, d, a, stream));
-  MOE_LAUNCH(launch_transpose(w2, w2t, E, d, f, a, stream));
-  MOE_TRY(run_gemm_sk(c, xp, w1, a1, offsets, f, d, false, sk, stream));
-  MOE_TRY(run_gemm_sk(c, dy, w2t, dh, offsets, f, d, false, sk, stream));
-  GradWParams g{};
-  g.E = E;
-  g.max_rows = c.T * c.top_k;
-  g.offsets = offsets;
-  if (dw2) {   // dW2_e = dY^T H over the expert's rows: [d, f]
-    g.M = d;
-    g.N = f;
-    g.P = dy;
-    g.Q = h;
-    g.G = dw2;
-    MOE_LAUNCH(launch_grad_w(g, bf16, stream));
-  }
-  MOE_LAUNCH(launch_silu_bwd(dh, a1, dh, (size_t)c.T * c.top_k * f, bf16, stream));
-  MOE_TRY(run_gemm_sk(c, dh, w1t, dxp, offsets, d, f, false, sk, stream));
-  if (dw1) {   // dW1_e = dA^T Xp over the expert's rows: [f, d]
-    g.M = f;
-    g.N = d;
-    g.P = dh;
-    g.Q = xp;
-    g.G = dw1;
-    MOE_LAUNCH(launch_grad_w(g, bf16, stream));
-  }
-  return MOE_OK;
+  return expert_ffn_bwd(*cfg, L, xp, offsets, w1, w2, h, dy, dxp, dw1, dw2, ws, stream);
 }
 
 moe_status_t moe_dispatch_backward(const moe_config_t* cfg, const void* dxp, const int32_t* row_of, void* dx,
@@ -600,6 +621,123 @@ moe_status_t moe_route_backward(const moe_config_t* cfg, const void* x, const fl
   p.dbias = dbias;
   p.part = dw_router ? (float*)at(ws, L.rw_part) : nullptr;
   MOE_LAUNCH(launch_route_bwd(p, c.act_dtype == MOE_BF16, stream));
+  return MOE_OK;
+}
+
+moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const float* w_router, const uint8_t* token_mask,
+                          const void* w1, const void* w2, const void* w1_shared, const void* w2_shared,
+                          const void* d_out, float d_aux, const void* fwd_ws, size_t fwd_ws_bytes, void* dx,
+                          float* dw_router, float* dbias, float* dw1, float* dw2, float* dw1_shared,
+                          float* dw2_shared, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(moe_validate_config(cfg));
+  const moe_config_t& c = *cfg;
+  if (c.weight_dtype == MOE_INT4) return MOE_ERR_UNSUPPORTED;
+  const bool shared = c.d_ffn_shared > 0;
+  if (!x || !w_router || !w1 || !w2 || !d_out || !fwd_ws || !dx || !ws || !isfinite(d_aux))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w1) || !aligned16(w2) || !aligned16(d_out) ||
+      !aligned16(fwd_ws) || !aligned16(dx) || !aligned16(ws))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (shared && (!w1_shared || !w2_shared || !aligned16(w1_shared) || !aligned16(w2_shared)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const Layout F = layout(c);
+  const BwdLayout L = bwd_layout(c);
+  if (fwd_ws_bytes < F.total || ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const bool bf16 = c.act_dtype == MOE_BF16;
+  const int a = (int)act_size(c), T = c.T, d = c.d_model;
+  void* fw = const_cast<void*>(fwd_ws);   // read only
+  const float* logits = (const float*)at(fw, F.logits);
+  const int32_t* ids = (const int32_t*)at(fw, F.ids);
+  const float* weights = (const float*)at(fw, F.weights);
+  const int32_t* counts_pre = (const int32_t*)at(fw, F.counts_pre);
+  const int32_t* offsets = (const int32_t*)at(fw, F.offsets);
+  const int32_t* row_of = (const int32_t*)at(fw, F.row_of);
+  const void* xp = at(fw, F.xp);
+  const void* h = at(fw, F.h);
+  const void* y = at(fw, F.y);
+  void* dy = at(ws, L.dy);
+  float* dwts = (float*)at(ws, L.dwts);
+  void* dxp = at(ws, L.dxp);
+  float* dlogits = (float*)at(ws, L.dlogits);
+  // combine: dY = w dOut on each kept slot's row, dw = <dOut, Y>
+  CombineBwdParams cp{};
+  cp.T = T;
+  cp.d = d;
+  cp.k = c.top_k;
+  cp.max_rows = T * c.top_k;
+  cp.d_out = d_out;
+  cp.y = y;
+  cp.row_of = row_of;
+  cp.weights = weights;
+  cp.dy = dy;
+  cp.dweights = dwts;
+  MOE_LAUNCH(launch_combine_bwd(cp, bf16, stream));
+  // routed experts
+  MOE_TRY(expert_ffn_bwd(c, L, xp, offsets, w1, w2, h, dy, dxp, dw1, dw2, ws, stream));
+  // shared expert: one segment of all T tokens; its output joined every token's with weight 1
+  void* dxs = nullptr;
+  if (shared) {
+    const int fs = c.d_ffn_shared;
+    const int32_t* sh_off = (const int32_t*)at(fw, F.sh_off);
+    const void* hs = at(fw, F.hs);
+    void* w1st = at(ws, L.w1st);   // [d, fs]
+    void* w2st = at(ws, L.w2st);   // [fs, d]
+    void* as = at(ws, L.as);       // [T, fs] pre-activation x W1s^T (recomputed)
+    void* dhs = at(ws, L.dhs);     // [T, fs] dHs, then dAs in place
+    void* sk = at(ws, L.sk_part);
+    dxs = at(ws, L.dxs);
+    MOE_LAUNCH(launch_transpose(w1_shared, w1st, 1, fs, d, a, stream));
+    MOE_LAUNCH(launch_transpose(w2_shared, w2st, 1, d, fs, a, stream));
+    MOE_TRY(run_gemm_sk(c, x, w1_shared, as, sh_off, fs, d, false, sk, stream, 1, T));
+    MOE_TRY(run_gemm_sk(c, d_out, w2st, dhs, sh_off, fs, d, false, sk, stream, 1, T));
+    GradWParams g{};
+    g.E = 1;
+    g.max_rows = T;
+    g.offsets = sh_off;
+    if (dw2_shared) {   // dW2s = dOut^T Hs: [d, fs]
+      g.M = d;
+      g.N = fs;
+      g.P = d_out;
+      g.Q = hs;
+      g.G = dw2_shared;
+      MOE_LAUNCH(launch_grad_w(g, bf16, stream));
+    }
+    MOE_LAUNCH(launch_silu_bwd(dhs, as, dhs, (size_t)T * fs, bf16, stream));
+    MOE_TRY(run_gemm_sk(c, dhs, w1st, dxs, sh_off, d, fs, false, sk, stream, 1, T));
+    if (dw1_shared) {   // dW1s = dAs^T x: [fs, d]
+      g.M = fs;
+      g.N = d;
+      g.P = dhs;
+      g.Q = x;
+      g.G = dw1_shared;
+      MOE_LAUNCH(launch_grad_w(g, bf16, stream));
+    }
+  }
+  // gather backward (plus the shared expert's dx), then the router's share
+  MOE_TRY(run_combine(c, dxp, row_of, nullptr, dxs, dx, stream));
+  RouteBwdParams p{};
+  p.T = T;
+  p.d = d;
+  p.E = c.num_experts;
+  p.k = c.top_k;
+  p.tau = c.temperature;
+  p.coef = c.aux_coef;
+  p.d_aux = d_aux;
+  p.renormalize = c.renormalize;
+  p.x = x;
+  p.w_router = w_router;
+  p.logits = logits;
+  p.ids = ids;
+  p.weights = weights;
+  p.dweights = dwts;
+  p.counts_pre = counts_pre;
+  p.token_mask = token_mask;
+  p.dlogits = dlogits;
+  p.dx = dx;
+  p.dw_router = dw_router;
+  p.dbias = dbias;
+  p.part = dw_router ? (float*)at(ws, L.rw_part) : nullptr;
+  MOE_LAUNCH(launch_route_bwd(p, bf16, stream));
   return MOE_OK;
 }
 

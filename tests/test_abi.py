@@ -205,3 +205,28 @@ def test_route_backward_validation():
     assert rb(dwr=fake, x=None) == 1 and rb(x=odd) == 1 and rb(ws=None) == 1
     assert rb(nbytes=need - 1) == 3
     assert need > moe.backward_workspace_bytes(_cfg(T=32)) > 0
+
+
+def test_whole_backward_validation():
+    L = binding.lib()
+    fake, odd = ctypes.c_void_p(256), ctypes.c_void_p(264)
+    B = ctypes.byref
+    need_f, need_b = moe.workspace_bytes(_cfg()), moe.backward_workspace_bytes(_cfg())
+
+    # moe_backward(cfg, x, w_router, token_mask, w1, w2, w1s, w2s, d_out, d_aux, fwd_ws, fwd_bytes, dx,
+    #              dw_router, dbias, dw1, dw2, dw1s, dw2s, ws, ws_bytes, stream)
+    def bw(cfg=None, x=fake, d_out=fake, fwd=fake, fb=need_f, dx=fake, ws=fake, wb=need_b, w1s=None, w2s=None,
+           d_aux=0.0):
+        c = cfg or _cfg().to_c()
+        return L.moe_backward(B(c), x, fake, None, fake, fake, w1s, w2s, d_out, d_aux, fwd, fb, dx, None, None,
+                              None, None, None, None, ws, wb, None)
+
+    assert bw(cfg=_cfg(T=0).to_c()) == 1
+    assert bw(x=None) == 1 and bw(d_out=None) == 1 and bw(fwd=None) == 1 and bw(dx=None) == 1 and bw(ws=None) == 1
+    assert bw(x=odd) == 1 and bw(fwd=odd) == 1 and bw(dx=odd) == 1
+    assert bw(d_aux=float("inf")) == 1
+    assert bw(fb=need_f - 1) == 3 and bw(wb=need_b - 1) == 3
+    shared = _cfg(d_ffn_shared=16)
+    assert bw(cfg=shared.to_c(), fb=moe.workspace_bytes(shared), wb=moe.backward_workspace_bytes(shared)) == 1
+    q4 = _cfg(dtype="bf16", weight_dtype="int4", d_model=512, d_ffn=1024, T=128)
+    assert bw(cfg=q4.to_c(), fb=1 << 40, wb=1 << 40) == 2

@@ -146,3 +146,88 @@ def test_router_backward(name):
     # fp32 arithmetic against float64: 1e-5 normwise; dx is stored in act (one more rounding)
     assert errs["dL"] <= 1e-5 and errs["dW_r"] <= 1e-5 and errs["db"] <= 1e-5, errs
     assert errs["dx"] <= (1e-5 if cfg.dtype == "f32" else 4e-3), errs
+
+
+FULL_CASES = {
+    "bwd_all_bf16": (derived(BASE, name="bwd_all_bf16", T=600, d_model=256, d_ffn=384, num_experts=6), 0.7),
+    # fp32, full-softmax weights, capacity drops, Gumbel selection, bias
+    "bwd_all_f32_capacity": (derived(WORKLOADS["skewed_gumbel_capacity"], name="bwd_all_f32_capacity", T=300,
+                                     d_model=64, d_ffn=96, num_experts=5, top_k=3, dtype="f32", renormalize=False,
+                                     capacity_factor=(4, 5)), 1.0),
+    # shared expert, additive noise, padding tokens
+    "bwd_all_shared_noise_padding": (derived(WORKLOADS["main_noise_padding"], name="bwd_all_shared_noise_padding",
+                                             T=520, d_model=128, d_ffn=192, num_experts=8, d_ffn_shared=160),
+                                     1.0),
+    # 256 x 256 grouped GEMMs on both the routed and the shared products
+    "bwd_all_big_shared": (derived(BASE, name="bwd_all_big_shared", T=2048, d_model=128, d_ffn=256, num_experts=2,
+                                   d_ffn_shared=256), 0.5),
+}
+
+
+def _oracle_forward_from_gpu(g, inp, cfg):
+    """The oracle's Forward record holding the GPU forward's own routing, dispatch, H and Y."""
+    T, E = cfg.T, cfg.num_experts
+    mask = inp.get("token_mask")
+    real = np.ones(T, dtype=bool) if mask is None else mask.numpy() != 0
+    logits = g["logits"].numpy()
+    probs = np.zeros((T, E))
+    probs[real] = oracle.router_probs(logits[real], cfg.temperature)
+    N = int(g["offsets"][-1])
+    r = oracle.Routing(logits, None, g["ids"].numpy(), g["weights"].numpy(), probs, real, None)
+    dp = oracle.Dispatch(g["counts_pre"].numpy(), g["counts"].numpy(), g["offsets"].numpy(),
+                         g["perm_token"].numpy()[:N], g["row_of"].numpy(), g["dropped"].numpy(),
+                         int(g["n_dropped"][0]), None)
+    return oracle.Forward(r, dp, cfg.capacity, g["h"][:N], g["y"][:N], g["out"], tuple(g["aux"].tolist()))
+
+
+@pytest.mark.parametrize("name", list(FULL_CASES))
+def test_moe_backward_whole_layer(name):
+    """moe_backward from the forward's workspace against the oracle's backward of the same forward."""
+    w, d_aux = FULL_CASES[name]
+    print(f"[gpu] moe_backward {name}: {w} d_aux={d_aux}", flush=True)
+    cfg = moe.config_for(w)
+    inp = make_inputs(w)
+    dinp = to_device(inp)
+    g = run_gpu(cfg, dinp)          # the intermediates, from a forward with debug buffers
+    T, d, f, E = cfg.T, cfg.d_model, cfg.d_ffn, cfg.num_experts
+    fs = cfg.d_ffn_shared
+    dt, st = cfg.torch_dtype, cfg.dtype
+    dev = "cuda"
+    fwd_ws = moe.new_workspace(cfg, dev)
+    out, aux = moe.forward(cfg, dinp["x"], dinp["w_router"], dinp["w1"], dinp["w2"], bias=dinp["bias"],
+                           gumbel=dinp["gumbel"], token_mask=dinp.get("token_mask"), w1_shared=dinp.get("w1_shared"),
+                           w2_shared=dinp.get("w2_shared"), ws=fwd_ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), g["out"]), "the forward is deterministic"
+    gen = torch.Generator().manual_seed(5)
+    d_out = torch.randn(T, d, generator=gen).to(dt)
+    nan = float("nan")
+    grads = {"dx": torch.full((T, d), nan, dtype=dt, device=dev),
+             "dw_router": torch.full((E, d), nan, device=dev), "dbias": torch.full((E,), nan, device=dev),
+             "dw1": torch.full((E, f, d), nan, device=dev), "dw2": torch.full((E, d, f), nan, device=dev)}
+    if fs:
+        grads["dw1_shared"] = torch.full((fs, d), nan, device=dev)
+        grads["dw2_shared"] = torch.full((d, fs), nan, device=dev)
+    ws = moe.new_backward_workspace(cfg)
+    moe.moe_backward(cfg, dinp["x"], dinp["w_router"], dinp["w1"], dinp["w2"], d_out.to(dev), fwd_ws, grads["dx"], ws,
+                     token_mask=dinp.get("token_mask"), w1_shared=dinp.get("w1_shared"),
+                     w2_shared=dinp.get("w2_shared"), d_aux=d_aux,
+                     **{k: v for k, v in grads.items() if k != "dx"})
+    torch.cuda.synchronize()
+    fw = _oracle_forward_from_gpu(g, inp, cfg)
+    ref = oracle.backward(fw, inp["x"], inp["w_router"], inp["w1"], inp["w2"], d_out, storage=st,
+                          tau=cfg.temperature, renormalize=cfg.renormalize, aux_coef=cfg.aux_coef, d_aux=d_aux,
+                          w1_shared=inp.get("w1_shared"), w2_shared=inp.get("w2_shared"))
+    pairs = {"dx": ref.dx, "dw_router": ref.dw_router, "dbias": ref.dbias, "dw1": ref.dw1, "dw2": ref.dw2}
+    if fs:
+        pairs["dw1_shared"] = ref.dw1_shared
+        pairs["dw2_shared"] = ref.dw2_shared
+    errs = {n: normwise(grads[n].cpu().double().numpy(), r) for n, r in pairs.items()}
+    print(f"[gpu] {name}: " + " ".join(f"{a} {b:.2e}" for a, b in errs.items()), flush=True)
+    # bf16: the products stored in bf16 (dY, dA, dXp, dx) give the storage tolerance; the router's
+    # gradients come from fp32 gate-weight gradients (1e-5 for fp32 arithmetic, 1e-4 once dx's
+    # bf16 values are not involved)
+    tol = NORM_TOL[st]
+    for n, e in errs.items():
+        lim = 1e-4 if (n in ("dw_router", "dbias")) else tol
+        assert e <= lim, (n, errs)
