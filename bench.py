@@ -1,6 +1,7 @@
 """Benchmark of the MoE-layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload main_bf16] [--no-cpu-baseline]
+                    [--backward]
 
 One step = one moe_forward call (router, dispatch, both grouped GEMMs, combine, aux loss) over
 the workload's seeded synthetic batch, with inputs already resident in HBM. W untimed steps,
@@ -41,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens of the CPU-oracle sample (0 = the whole workload)")
+    ap.add_argument("--backward", action="store_true",
+                    help="after the forward measurement, time moe_backward (all gradients) the same way "
+                         "and add a 'backward' object to the line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, run one elementwise copy of this many MiB (a known-size "
                          "kernel to scale hardware byte counters against)")
@@ -91,6 +95,49 @@ def cpu_baseline(w, inp, ntok: int) -> dict:
     return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {ntok} of {w.T} tokens of {w.name} with all expert weights "
                       f"(oracle.forward, float64, numpy/OpenBLAS); {dt:.2f} s"}
+
+
+def bench_backward(args, w, cfg, dev, ws, N: int) -> dict:
+    """moe_backward over the forward's workspace (a forward pass without debug outputs): W untimed then K
+    timed calls between two device synchronisations. Each call produces dx and every weight
+    gradient (router, bias, W1, W2, the shared expert's)."""
+    import torch
+
+    import sparse_mixture_experts_02_amd as moe
+    if cfg.int4:
+        return {"skipped": "4-bit expert weights have no backward"}
+    T, d, f, E = w.T, w.d_model, w.d_ffn, w.num_experts
+    fs = w.d_ffn_shared
+    dt = cfg.torch_dtype
+    gen = torch.Generator().manual_seed(5)
+    d_out = torch.randn(T, d, generator=gen).to(dt).cuda()
+    z = lambda *shape: torch.empty(*shape, dtype=torch.float32, device="cuda")
+    grads = {"dw_router": z(E, d), "dbias": z(E), "dw1": z(E, f, d), "dw2": z(E, d, f)}
+    if fs:
+        grads.update(dw1_shared=z(fs, d), dw2_shared=z(d, fs))
+    dx = torch.empty(T, d, dtype=dt, device="cuda")
+    bws = moe.new_backward_workspace(cfg)
+
+    def bstep():
+        moe.moe_backward(cfg, dev["x"], dev["w_router"], dev["w1"], dev["w2"], d_out, ws, dx, bws,
+                         token_mask=dev["token_mask"], w1_shared=dev["w1_shared"], w2_shared=dev["w2_shared"],
+                         d_aux=1.0, **grads)
+
+    for _ in range(args.warmup):
+        bstep()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        bstep()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # the backward's matrix products: the recomputed pre-activation, dH, dXp, dW2 and dW1 of the
+    # routed experts (2 N d f flop each), and the shared expert's five of 2 T d fs
+    flop = 5 * 2.0 * N * d * f + 5 * 2.0 * T * d * fs
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    return {"ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "matmul_flop": flop,
+            "matmul_tflops": flop / (ms * 1e-3) / 1e12, "frac_of_peak": flop / (ms * 1e-3) / 1e12 / peak,
+            "steps": args.steps, "warmup": args.warmup}
 
 
 def main():
@@ -230,6 +277,12 @@ def main():
         "n_dropped": n_dropped,
         "inputs_sha256": digest,
     }
+    if args.backward:
+        # a forward pass without debug outputs leaves every intermediate the backward reads in ws
+        moe.moe_forward(cfg, dev["x"], dev["w_router"], dev["w1"], dev["w2"], out, aux, ws, bias=dev["bias"],
+                        gumbel=dev["gumbel"], token_mask=dev["token_mask"], w1_shared=dev["w1_shared"],
+                        w2_shared=dev["w2_shared"])
+        line["backward"] = bench_backward(args, w, cfg, dev, ws, N)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_sample_tokens)
     print(json.dumps(line), flush=True)

@@ -134,62 +134,131 @@ namespace moe {
 // Weight gradients of the grouped GEMMs: for every expert e,
 //   G[e][m][n] = sum over the expert's rows r of P[r][m] * Q[r][n]     (fp32 result)
 // a product whose reduction runs over the expert's segment of the permuted rows (dW2 = dY^T H,
-// dW1 = dA^T Xp). bf16: 64 x 64 output tiles of 4 waves (16 rows each, four 16 x 16 MFMA blocks);
-// 32 rows of P and Q per step are staged through LDS transposed (the reduction index becomes
-// the contiguous one), then v_mfma_f32_16x16x32_bf16. fp32: one output per thread, fp32 FMA in
-// row order.
-__global__ __launch_bounds__(256) void grad_w_bf16_kernel(GradWParams p) {
-  constexpr int TP = 32 + 8;   // padded row of the transposed tiles (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t PT[64 * TP];
-  __shared__ __attribute__((aligned(16))) uint16_t QT[64 * TP];
-  const int e = blockIdx.y;
-  const int tilesN = (p.N + 63) / 64;
-  const int m0 = (blockIdx.x / tilesN) * 64, n0 = (blockIdx.x % tilesN) * 64;
+// dW1 = dA^T Xp). fp32: one output per thread, fp32 FMA in row order. bf16 (grad_w_bf16_kernel):
+//  * one 128 x 128 output tile of one expert per workgroup; 4 waves in 2 x 2, each 64 x 64 =
+//    4 x 4 blocks of v_mfma_f32_16x16x32_bf16. Tiles are numbered so that each XCD takes a
+//    contiguous range (the same expert, neighbouring tiles: its L2 serves their shared rows).
+//  * the reduction runs in stages of 64 rows. P and Q are row-major in r, and an MFMA operand
+//    wants 8 consecutive r per lane, so each thread loads an 8 x 8 block (8 rows x 16 bytes,
+//    whole 128-byte lines along m or n), transposes it in registers (v_perm pairs of halves) and
+//    writes 8 16-byte rows of r into LDS: [m or n][r] with a 72-element pitch (the MFMA operand
+//    reads of 8 lanes then cover all banks).
+//  * two LDS buffers: the loads of stage s + 1 are issued before the 32 MFMAs of stage s and
+//    written to the other buffer after them; one barrier per stage. Rows past the segment's end
+//    (and columns past M or N, whole 8-column blocks since both are multiples of 8) are loaded
+//    from a clamped address and replaced by zeros.
+constexpr int GW_TILE = 128, GW_BK = 64, GW_TP = GW_BK + 8;
+
+__device__ __forceinline__ uint4 gw_load(const uint16_t* __restrict__ src, size_t off) {
+  return *(const uint4*)(src + off);
+}
+
+__global__ __launch_bounds__(256, 2) void grad_w_bf16_kernel(GradWParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][GW_TILE * GW_TP];
+  const int tilesM = (p.M + GW_TILE - 1) / GW_TILE, tilesN = (p.N + GW_TILE - 1) / GW_TILE;
+  const int per_e = tilesM * tilesN, total = per_e * p.E;
+  int b = blockIdx.x;
+  if ((total & 7) == 0) b = (b & 7) * (total >> 3) + (b >> 3);   // contiguous tile range per XCD
+  const int e = b / per_e, rem = b - e * per_e;
+  const int m0 = (rem / tilesN) * GW_TILE, n0 = (rem % tilesN) * GW_TILE;
   int r0 = p.offsets[e], r1 = p.offsets[e + 1];
   r0 = r0 < 0 ? 0 : (r0 > p.max_rows ? p.max_rows : r0);
   r1 = r1 < r0 ? r0 : (r1 > p.max_rows ? p.max_rows : r1);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int fr = lane & 15, fg = lane >> 4;
-  const uint16_t* __restrict__ P = (const uint16_t*)p.P;
-  const uint16_t* __restrict__ Q = (const uint16_t*)p.Q;
-  f32x4_t acc[4];
+  // loader: operand op (P for threads 0..127, Q for 128..255), 8 x 8 block (rb, cb) of a stage
+  // (8 consecutive lanes: the 8 row blocks of one column block, so that their transposed 16-byte
+  // LDS writes are contiguous; a wave's loads are 8 rows x 128 contiguous bytes)
+  const int op = tid >> 7, bi = tid & 127, rb = bi & 7, cb = bi >> 3;
+  const int width = op ? p.N : p.M;
+  const int col = (op ? n0 : m0) + 8 * cb;
+  const bool col_ok = col < width;
+  const uint16_t* __restrict__ src = (const uint16_t*)(op ? p.Q : p.P) + (col_ok ? col : 0);
+  uint16_t* const dst0 = &lds[0][op][(8 * cb) * GW_TP + 8 * rb];
+  uint16_t* const dst1 = &lds[1][op][(8 * cb) * GW_TP + 8 * rb];
+  uint4 v[8];
+  auto load_stage = [&](int r) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int rr = tid >> 3, cc = (tid & 7) * 8;   // the loader's row within the step and column
-  for (int r = r0; r < r1; r += 32) {
-    uint4 pv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
-    if (r + rr < r1) {
-      if (m0 + cc < p.M) pv = *(const uint4*)(P + (size_t)(r + rr) * p.M + m0 + cc);
-      if (n0 + cc < p.N) qv = *(const uint4*)(Q + (size_t)(r + rr) * p.N + n0 + cc);
+    for (int i = 0; i < 8; ++i) {
+      const int row = r + 8 * rb + i;
+      v[i] = gw_load(src, (size_t)(row < r1 ? row : r0) * width);
     }
-    __syncthreads();   // the previous step's fragments have been read
-    const uint32_t pw[4] = {pv.x, pv.y, pv.z, pv.w}, qw[4] = {qv.x, qv.y, qv.z, qv.w};
+  };
+  auto store_stage = [&](int r, uint16_t* dst) {
+    // zero the rows past the segment and the columns past the matrix, then transpose: output
+    // dword q of column j holds rows 2q (low half) and 2q + 1 (high half)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      PT[(cc + 2 * q) * TP + rr] = (uint16_t)(pw[q] & 0xFFFFu);
-      PT[(cc + 2 * q + 1) * TP + rr] = (uint16_t)(pw[q] >> 16);
-      QT[(cc + 2 * q) * TP + rr] = (uint16_t)(qw[q] & 0xFFFFu);
-      QT[(cc + 2 * q + 1) * TP + rr] = (uint16_t)(qw[q] >> 16);
+    for (int i = 0; i < 8; ++i) {
+      uint32_t mk = (col_ok && (r + 8 * rb + i < r1)) ? 0xFFFFFFFFu : 0u;
+      asm volatile("" : "+v"(mk));   // a mask, not a branch around the loaded values
+      v[i].x &= mk;
+      v[i].y &= mk;
+      v[i].z &= mk;
+      v[i].w &= mk;
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = ((const uint32_t*)&v[2 * q])[j >> 1];
+        const uint32_t hi = ((const uint32_t*)&v[2 * q + 1])[j >> 1];
+        o[q] = __builtin_amdgcn_perm(hi, lo, sel);
+      }
+      *(uint4*)(dst + j * GW_TP) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  };
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int wm = w >> 1, wn = w & 1;
+  const int ns = (r1 - r0 + GW_BK - 1) / GW_BK;
+  if (ns > 0) {
+    load_stage(r0);
+    store_stage(r0, dst0);
     __syncthreads();
-    const bf16x8_t A = __builtin_bit_cast(bf16x8_t, *(const uint4*)(PT + (16 * w + fr) * TP + 8 * fg));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8_t B = __builtin_bit_cast(bf16x8_t, *(const uint4*)(QT + (16 * j + fr) * TP + 8 * fg));
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[j], 0, 0, 0);
-    }
   }
-  // lane holds rows m0 + 16 w + 4 fg .. + 3 of column n0 + 16 j + fr
+  for (int s = 0; s < ns; ++s) {
+    const int rn = r0 + (s + 1) * GW_BK;
+    load_stage(rn);   // past the last stage: clamped rows, all replaced by zeros
+    __builtin_amdgcn_sched_barrier(0);   // the loads go out before this stage's MFMAs
+    const uint16_t* A = &lds[s & 1][0][0];
+    const uint16_t* B = &lds[s & 1][1][0];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8_t af[4], bfr[4];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        af[mi] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(A + (64 * wm + 16 * mi + fr) * GW_TP + 32 * ks + 8 * fg));
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+        bfr[ni] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(B + (64 * wn + 16 * ni + fr) * GW_TP + 32 * ks + 8 * fg));
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // and are waited for only after them
+    store_stage(rn, (s & 1) ? dst0 : dst1);
+    __syncthreads();
+  }
+  // lane holds rows m0 + 64 wm + 16 mi + 4 fg .. + 3 of column n0 + 64 wn + 16 ni + fr
   float* __restrict__ G = p.G + (size_t)e * p.M * p.N;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + 16 * j + fr;
+  for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int m = m0 + 16 * w + 4 * fg + t;
-      if (m < p.M && n < p.N) G[(size_t)m * p.N + n] = acc[j][t];
+    for (int ni = 0; ni < 4; ++ni) {
+      const int n = n0 + 64 * wn + 16 * ni + fr;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int m = m0 + 64 * wm + 16 * mi + 4 * fg + t;
+        if (m < p.M && n < p.N) G[(size_t)m * p.N + n] = acc[mi][ni][t];
+      }
     }
-  }
 }
 
 __global__ __launch_bounds__(256) void grad_w_f32_kernel(GradWParams p) {
@@ -210,8 +279,9 @@ __global__ __launch_bounds__(256) void grad_w_f32_kernel(GradWParams p) {
 
 hipError_t launch_grad_w(const GradWParams& p, bool bf16, hipStream_t s) {
   if (bf16) {
-    dim3 grid(((p.M + 63) / 64) * ((p.N + 63) / 64), p.E);
-    grad_w_bf16_kernel<<<grid, 256, 0, s>>>(p);
+    const int tiles = ((p.M + GW_TILE - 1) / GW_TILE) * ((p.N + GW_TILE - 1) / GW_TILE) * p.E;
+    if (tiles == 0) return hipSuccess;
+    grad_w_bf16_kernel<<<tiles, 256, 0, s>>>(p);
   } else {
     size_t blocks = ((size_t)p.M * p.N + 255) / 256;
     if (blocks > 4096) blocks = 4096;
