@@ -137,21 +137,17 @@ namespace moe {
 // dW1 = dA^T Xp). fp32: one output per thread, fp32 FMA in row order. bf16 (grad_w_bf16_kernel):
 //  * one 128 x 128 output tile of one expert per workgroup; 4 waves in 2 x 2, each 64 x 64 =
 //    4 x 4 blocks of v_mfma_f32_16x16x32_bf16. Tiles are numbered so that each XCD takes a
-//    contiguous range (the same expert, neighbouring tiles: its L2 serves their shared rows).
+//    contiguous range (the same expert), walked in groups of 8 m-tiles: the tiles in flight on
+//    an XCD share their rows of P and Q 8 ways in its L2.
 //  * the reduction runs in stages of 64 rows. P and Q are row-major in r, and an MFMA operand
 //    wants 8 consecutive r per lane, so each thread loads an 8 x 8 block (8 rows x 16 bytes,
 //    whole 128-byte lines along m or n), transposes it in registers (v_perm pairs of halves) and
 //    writes 8 16-byte rows of r into LDS: [m or n][r] with a 72-element pitch (the MFMA operand
 //    reads of 8 lanes then cover all banks).
-//  * two LDS buffers: the loads of stage s + 1 are issued before the 32 MFMAs of stage s and
-//    written to the other buffer after them; one barrier per stage. Rows past the segment's end
-//    (and columns past M or N, whole 8-column blocks since both are multiples of 8) are loaded
-//    from a clamped address and replaced by zeros.
+//  * two LDS buffers and two register sets: the loads of stage s + 2 are issued before the 32
+//    MFMAs of stage s, and stage s + 1 (requested a stage earlier) is transposed into the other
+//    buffer alongside them; one barrier per stage.
 constexpr int GW_TILE = 128, GW_BK = 64, GW_TP = GW_BK + 8;
-
-__device__ __forceinline__ uint4 gw_load(const uint16_t* __restrict__ src, size_t off) {
-  return *(const uint4*)(src + off);
-}
 
 __global__ __launch_bounds__(256, 2) void grad_w_bf16_kernel(GradWParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][GW_TILE * GW_TP];
@@ -159,74 +155,74 @@ __global__ __launch_bounds__(256, 2) void grad_w_bf16_kernel(GradWParams p) {
   const int per_e = tilesM * tilesN, total = per_e * p.E;
   int b = blockIdx.x;
   if ((total & 7) == 0) b = (b & 7) * (total >> 3) + (b >> 3);   // contiguous tile range per XCD
+  // within an expert, groups of 8 m-tiles walked n-tile by n-tile: the tiles running together on
+  // an XCD form 8 x 8 blocks and share their operand rows 8 ways in its L2
   const int e = b / per_e, rem = b - e * per_e;
-  const int m0 = (rem / tilesN) * GW_TILE, n0 = (rem % tilesN) * GW_TILE;
+  const int grp = rem / (8 * tilesN), gm0 = grp * 8, gsz = min(8, tilesM - gm0);
+  const int in = rem - grp * 8 * tilesN;
+  const int m0 = (gm0 + in % gsz) * GW_TILE, n0 = (in / gsz) * GW_TILE;
   int r0 = p.offsets[e], r1 = p.offsets[e + 1];
   r0 = r0 < 0 ? 0 : (r0 > p.max_rows ? p.max_rows : r0);
   r1 = r1 < r0 ? r0 : (r1 > p.max_rows ? p.max_rows : r1);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int fr = lane & 15, fg = lane >> 4;
-  // loader: operand op (P for threads 0..127, Q for 128..255), 8 x 8 block (rb, cb) of a stage
-  // (8 consecutive lanes: the 8 row blocks of one column block, so that their transposed 16-byte
-  // LDS writes are contiguous; a wave's loads are 8 rows x 128 contiguous bytes)
+  // loader: operand op (P for threads 0..127, Q for 128..255; one operand per wave), 8 x 8 block
+  // (rb, cb) of a stage (8 consecutive lanes: the 8 row blocks of one column block, so that their
+  // transposed 16-byte LDS writes are contiguous; a wave's loads are 8 rows x 128 contiguous
+  // bytes). The loads go through a buffer resource per stage covering the stage's valid rows:
+  // rows past the segment's end read as zeros, and so do columns past M or N (whole 8-column
+  // blocks, both being multiples of 8), given an offset outside every resource.
   const int op = tid >> 7, bi = tid & 127, rb = bi & 7, cb = bi >> 3;
-  const int width = op ? p.N : p.M;
+  const int width = __builtin_amdgcn_readfirstlane(op ? p.N : p.M);
+  const uint64_t opnd = (uint64_t)(uintptr_t)(op ? p.Q : p.P);
+  const uint32_t opnd_lo = __builtin_amdgcn_readfirstlane((uint32_t)opnd);
+  const uint32_t opnd_hi = __builtin_amdgcn_readfirstlane((uint32_t)(opnd >> 32));
+  const uint16_t* const src = (const uint16_t*)(uintptr_t)(((uint64_t)opnd_hi << 32) | opnd_lo);
+  const uint32_t rowb = (uint32_t)width * 2u;
   const int col = (op ? n0 : m0) + 8 * cb;
-  const bool col_ok = col < width;
-  const uint16_t* __restrict__ src = (const uint16_t*)(op ? p.Q : p.P) + (col_ok ? col : 0);
+  uint32_t voff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) voff[i] = col < width ? (uint32_t)(8 * rb + i) * rowb + (uint32_t)col * 2u : 0x80000000u;
   uint16_t* const dst0 = &lds[0][op][(8 * cb) * GW_TP + 8 * rb];
   uint16_t* const dst1 = &lds[1][op][(8 * cb) * GW_TP + 8 * rb];
-  uint4 v[8];
-  auto load_stage = [&](int r) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = r + 8 * rb + i;
-      v[i] = gw_load(src, (size_t)(row < r1 ? row : r0) * width);
-    }
-  };
-  auto store_stage = [&](int r, uint16_t* dst) {
-    // zero the rows past the segment and the columns past the matrix, then transpose: output
-    // dword q of column j holds rows 2q (low half) and 2q + 1 (high half)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t mk = (col_ok && (r + 8 * rb + i < r1)) ? 0xFFFFFFFFu : 0u;
-      asm volatile("" : "+v"(mk));   // a mask, not a branch around the loaded values
-      v[i].x &= mk;
-      v[i].y &= mk;
-      v[i].z &= mk;
-      v[i].w &= mk;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t o[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = ((const uint32_t*)&v[2 * q])[j >> 1];
-        const uint32_t hi = ((const uint32_t*)&v[2 * q + 1])[j >> 1];
-        o[q] = __builtin_amdgcn_perm(hi, lo, sel);
-      }
-      *(uint4*)(dst + j * GW_TP) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-  };
+  // Two register sets: stage s + 2 is requested before stage s's MFMAs, and stage s + 1's rows
+  // (requested a stage earlier, so already landed or close) are transposed into the other LDS
+  // buffer while those MFMAs run.
+  uint4 va[8], vb[8];
+#define GW_LOAD(V, R)                                                                          \
+  {                                                                                            \
+    const int r_ = (R);                                                                        \
+    const int nrows_ = r_ < r1 ? min(GW_BK, r1 - r_) : 0;                                      \
+    const __amdgpu_buffer_rsrc_t rs_ = __builtin_amdgcn_make_buffer_rsrc(                      \
+        (void*)(src + (size_t)(r_ < r1 ? r_ : r0) * width), 0, nrows_ * (int)rowb, 0x00020000); \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                            \
+      const auto t_ = __builtin_amdgcn_raw_buffer_load_b128(rs_, (int)voff[i], 0, 0);           \
+      V[i] = make_uint4(t_[0], t_[1], t_[2], t_[3]);                                           \
+    }                                                                                          \
+  }
+  // transpose: output dword q of column j holds rows 2q (low half) and 2q + 1 (high half)
+#define GW_STORE(V, DST)                                                           \
+  {                                                                                \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                \
+      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;                    \
+      uint32_t o[4];                                                               \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                              \
+        const uint32_t lo = ((const uint32_t*)&V[2 * q])[j >> 1];                  \
+        const uint32_t hi = ((const uint32_t*)&V[2 * q + 1])[j >> 1];              \
+        o[q] = __builtin_amdgcn_perm(hi, lo, sel);                                 \
+      }                                                                            \
+      *(uint4*)((DST) + j * GW_TP) = make_uint4(o[0], o[1], o[2], o[3]);           \
+    }                                                                              \
+  }
   f32x4_t acc[4][4];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int wm = w >> 1, wn = w & 1;
-  const int ns = (r1 - r0 + GW_BK - 1) / GW_BK;
-  if (ns > 0) {
-    load_stage(r0);
-    store_stage(r0, dst0);
-    __syncthreads();
-  }
-  for (int s = 0; s < ns; ++s) {
-    const int rn = r0 + (s + 1) * GW_BK;
-    load_stage(rn);   // past the last stage: clamped rows, all replaced by zeros
-    __builtin_amdgcn_sched_barrier(0);   // the loads go out before this stage's MFMAs
-    const uint16_t* A = &lds[s & 1][0][0];
-    const uint16_t* B = &lds[s & 1][1][0];
+  auto mfma_stage = [&](int buf) {
+    const uint16_t* A = &lds[buf][0][0];
+    const uint16_t* B = &lds[buf][1][0];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8_t af[4], bfr[4];
@@ -242,10 +238,32 @@ __global__ __launch_bounds__(256, 2) void grad_w_bf16_kernel(GradWParams p) {
         for (int ni = 0; ni < 4; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);   // and are waited for only after them
-    store_stage(rn, (s & 1) ? dst0 : dst1);
+  };
+  const int ns = (r1 - r0 + GW_BK - 1) / GW_BK;
+  if (ns > 0) {
+    GW_LOAD(va, r0);
+    GW_STORE(va, dst0);
+    GW_LOAD(vb, r0 + GW_BK);
     __syncthreads();
   }
+  // past the last stage the loads see an empty resource and return zeros
+  for (int s = 0; s < ns; s += 2) {
+    // stage s is in buffer 0, stage s + 1 in flight in vb
+    GW_LOAD(va, r0 + (s + 2) * GW_BK);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_stage(0);
+    GW_STORE(vb, dst1);
+    __syncthreads();
+    if (s + 1 >= ns) break;
+    // stage s + 1 is in buffer 1, stage s + 2 in flight in va
+    GW_LOAD(vb, r0 + (s + 3) * GW_BK);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_stage(1);
+    GW_STORE(va, dst0);
+    __syncthreads();
+  }
+#undef GW_LOAD
+#undef GW_STORE
   // lane holds rows m0 + 64 wm + 16 mi + 4 fg .. + 3 of column n0 + 64 wn + 16 ni + fr
   float* __restrict__ G = p.G + (size_t)e * p.M * p.N;
 #pragma unroll
