@@ -72,7 +72,7 @@ hipError_t launch_combine_bwd(const CombineBwdParams& p, bool bf16, hipStream_t 
   return hipGetLastError();
 }
 
-// 64 x 64 tiles through LDS (one padding column against bank conflicts).
+// fp32: 64 x 64 tiles through LDS (one padding column against bank conflicts).
 template <typename TE>
 __global__ __launch_bounds__(256) void transpose_kernel(const TE* __restrict__ in, TE* __restrict__ out, int R, int C) {
   __shared__ TE tile[64][65];
@@ -92,34 +92,82 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TE* __restrict__ i
   }
 }
 
+// bf16 (R and C multiples of 8): no LDS. Each thread moves one 8 x 8 block: 8 loads of 16 bytes
+// (rows 8 rb .. 8 rb + 7), a register transpose (v_perm of half-words) and 8 stores of 16 bytes.
+// A wave covers 64 x 64: lane = rb + 8 cb, so each load instruction reads 8 rows x 128
+// contiguous bytes and each store writes 8 output rows x 128 contiguous bytes.
+__global__ __launch_bounds__(256) void transpose_b16_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
+                                                            int R, int C) {
+  const size_t b = blockIdx.z;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = blockIdx.y * 64 + 8 * (lane & 7);
+  const int c = blockIdx.x * 256 + 64 * w + 8 * (lane >> 3);
+  if (r >= R || c >= C) return;
+  const uint16_t* src = in + b * (size_t)R * C + (size_t)r * C + c;
+  uint16_t* dst = out + b * (size_t)R * C + (size_t)c * R + r;
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = *(const uint4*)(src + (size_t)i * C);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = __builtin_amdgcn_perm(((const uint32_t*)&v[2 * q + 1])[j >> 1], ((const uint32_t*)&v[2 * q])[j >> 1], sel);
+    *(uint4*)(dst + (size_t)j * R) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 hipError_t launch_transpose(const void* in, void* out, int B, int R, int C, int elem, hipStream_t s) {
-  dim3 grid((C + 63) / 64, (R + 63) / 64, B);
-  if (elem == 2) transpose_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)in, (uint16_t*)out, R, C);
-  else transpose_kernel<float><<<grid, 256, 0, s>>>((const float*)in, (float*)out, R, C);
+  if (elem == 2) {
+    dim3 grid((C + 255) / 256, (R + 63) / 64, B);
+    transpose_b16_kernel<<<grid, 256, 0, s>>>((const uint16_t*)in, (uint16_t*)out, R, C);
+  } else {
+    dim3 grid((C + 63) / 64, (R + 63) / 64, B);
+    transpose_kernel<float><<<grid, 256, 0, s>>>((const float*)in, (float*)out, R, C);
+  }
   return hipGetLastError();
 }
 
 // dA = dH * SiLU'(A), SiLU'(a) = s (1 + a (1 - s)) with s = sigmoid(a), in fp32, one rounding.
+// 16 bytes per thread and step (8 bf16 or 4 fp32 elements; n is a multiple of 8).
 template <bool BF16>
 __global__ __launch_bounds__(256) void silu_bwd_kernel(const void* dh, const void* a, void* da, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-    float g, x;
-    if constexpr (BF16) {
-      g = bf16_bits_to_f32(((const uint16_t*)dh)[i]);
-      x = bf16_bits_to_f32(((const uint16_t*)a)[i]);
-    } else {
-      g = ((const float*)dh)[i];
-      x = ((const float*)a)[i];
+  constexpr int V = BF16 ? 8 : 4;
+  const size_t nv = n / V;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nv; i += (size_t)gridDim.x * blockDim.x) {
+    const uint4 gv = ((const uint4*)dh)[i];
+    const uint4 xv = ((const uint4*)a)[i];
+    const uint32_t* gw = (const uint32_t*)&gv;
+    const uint32_t* xw = (const uint32_t*)&xv;
+    uint4 ov;
+    uint32_t* ow = (uint32_t*)&ov;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (BF16) {
+        uint32_t lohi[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float g = bf16_bits_to_f32((gw[q] >> (16 * h)) & 0xFFFFu);
+          const float x = bf16_bits_to_f32((xw[q] >> (16 * h)) & 0xFFFFu);
+          const float sg = 1.0f / (1.0f + expf(-x));
+          lohi[h] = f32_to_bf16_bits(g * (sg * (1.0f + x * (1.0f - sg))));
+        }
+        ow[q] = lohi[0] | (lohi[1] << 16);
+      } else {
+        const float g = __uint_as_float(gw[q]), x = __uint_as_float(xw[q]);
+        const float sg = 1.0f / (1.0f + expf(-x));
+        ow[q] = __float_as_uint(g * (sg * (1.0f + x * (1.0f - sg))));
+      }
     }
-    const float sg = 1.0f / (1.0f + expf(-x));
-    const float v = g * (sg * (1.0f + x * (1.0f - sg)));
-    if constexpr (BF16) ((uint16_t*)da)[i] = (uint16_t)f32_to_bf16_bits(v);
-    else ((float*)da)[i] = v;
+    ((uint4*)da)[i] = ov;
   }
 }
 
 hipError_t launch_silu_bwd(const void* dh, const void* a, void* da, size_t n, bool bf16, hipStream_t s) {
-  size_t blocks = (n + 255) / 256;
+  const size_t nv = n / (bf16 ? 8 : 4);
+  size_t blocks = (nv + 255) / 256;
   if (blocks > 16384) blocks = 16384;
   if (blocks == 0) return hipSuccess;
   if (bf16) silu_bwd_kernel<true><<<(unsigned)blocks, 256, 0, s>>>(dh, a, da, n);
