@@ -142,15 +142,21 @@ def router_probs(logits, tau: float = 1.0) -> np.ndarray:
     return p / p.sum(axis=1, keepdims=True)
 
 
-def gate_weights(logits, ids, tau: float = 1.0, renormalize: bool = True, exact: bool = False) -> np.ndarray:
+def gate_weights(logits, ids, tau: float = 1.0, renormalize: bool = True, exact: bool = False,
+                 straight_through: bool = False) -> np.ndarray:
     """Gate weight of each selected expert, fp32.
 
     P4 §2.4: the output is the weighted sum of the chosen experts' outputs, weighted by the
     softmax router scores. renormalize=True: softmax over the k selected (clean) logits / tau,
     so a token's weights sum to 1. renormalize=False: the full-softmax probability of each
-    selected expert (the page's literal wording).
+    selected expert (the page's literal wording). straight_through=True (P2 §3.1's
+    straight-through estimator): the routing matrix is the k-hot selection plus
+    softmax - detach(softmax), whose value is the k-hot matrix, so every selected expert has
+    weight exactly 1 (the softmax only shapes the backward pass).
     """
     ids = np.asarray(ids)
+    if straight_through:
+        return np.ones(ids.shape, dtype=np.float64 if exact else np.float32)
     if renormalize:
         s = _f64(logits) / float(np.float32(tau))
         sel = np.take_along_axis(s, ids.astype(np.int64), axis=1)
@@ -196,7 +202,7 @@ class Routing:
 
 def route(x=None, w_router=None, bias=None, gumbel=None, tau: float = 1.0, k: int = 2,
           renormalize: bool = True, logits=None, noise_in_logits: bool = False,
-          token_mask=None, exact: bool = False) -> Routing:
+          token_mask=None, exact: bool = False, straight_through: bool = False) -> Routing:
     """Router logits -> key -> top-k -> gate weights, plus the full softmax for the aux loss.
 
     With `logits` given, routing runs on those fp32 logits (the bias, and additive noise when
@@ -235,7 +241,7 @@ def route(x=None, w_router=None, bias=None, gumbel=None, tau: float = 1.0, k: in
     entropy = np.zeros(T, dtype=np.float64)
     if np.any(real):
         ids[real] = top_k(keys[real], k)
-        weights[real] = gate_weights(logits[real], ids[real], tau, renormalize, exact)
+        weights[real] = gate_weights(logits[real], ids[real], tau, renormalize, exact, straight_through)
         probs[real] = router_probs(logits[real], tau)
         entropy[real] = router_entropy(probs[real])
     return Routing(logits, keys, ids, weights, probs, real, entropy)
@@ -513,7 +519,8 @@ class Forward:
 def forward(x, w_router, w1, w2, *, k: int, storage: str, bias=None, gumbel=None,
             tau: float = 1.0, capacity: Optional[int] = None, renormalize: bool = True,
             aux_coef: float = 0.01, logits=None, noise_in_logits: bool = False,
-            token_mask=None, w1_shared=None, w2_shared=None, exact: bool = False) -> Forward:
+            token_mask=None, w1_shared=None, w2_shared=None, exact: bool = False,
+            straight_through: bool = False) -> Forward:
     """Router -> top-k -> capacity + dispatch -> expert FFN -> weighted combine, plus aux.
 
     aux = (aux_switch, aux_balance, mean router entropy). With w1_shared / w2_shared, a shared
@@ -522,7 +529,8 @@ def forward(x, w_router, w1, w2, *, k: int, storage: str, bias=None, gumbel=None
     T = x.shape[0]
     E = w1.shape[0]
     C = T if capacity is None or capacity < 0 else capacity
-    r = route(x, w_router, bias, gumbel, tau, k, renormalize, logits, noise_in_logits, token_mask, exact)
+    r = route(x, w_router, bias, gumbel, tau, k, renormalize, logits, noise_in_logits, token_mask, exact,
+              straight_through=straight_through)
     dp = dispatch(r.ids, E, C, x)
     h, y = expert_ffn(dp.xp, dp.offsets, w1, w2, storage)
     ys = None
@@ -646,7 +654,7 @@ class Grads:
 
 def backward(fw: Forward, x, w_router, w1, w2, d_out, *, storage: str, tau: float = 1.0,
              renormalize: bool = True, aux_coef: float = 0.01, d_aux: float = 1.0, w1_shared=None,
-             w2_shared=None) -> Grads:
+             w2_shared=None, straight_through: bool = False) -> Grads:
     """Gradients of  L = sum(d_out * out) + d_aux * aux_switch  with respect to x, the router
     weight and bias, the expert weights and the shared expert's weights, float64.
 
@@ -659,6 +667,11 @@ def backward(fw: Forward, x, w_router, w1, w2, d_out, *, storage: str, tau: floa
     The forward's stored values are used as they are (H, Y after their storage rounding; the
     shared expert's Hs is recomputed with the same rounding); the pre-activations W1 Xp and
     W1s x are recomputed in float64.
+    straight_through (P2 §3.1): the forward's weights are the k-hot selection (all 1) and the
+    gradient goes through the full softmax of logits / tau, as for full-softmax weights: the
+    derivative of softmax - detach(softmax) is the softmax's. A non-selected (or dropped) expert
+    gets no gradient: its output is not computed for the token (P2 §3.2 runs each expert on its
+    own tokens only).
     """
     r, dp = fw.routing, fw.dispatch
     x64, wr64 = _f64(x), _f64(w_router)
@@ -685,8 +698,8 @@ def backward(fw: Forward, x, w_router, w1, w2, d_out, *, storage: str, tau: floa
         das = (go @ w2s) * silu_grad(a_s)
         dw1s = das.T @ x64
         dx += das @ w1s
-    dl = router_backward(r.probs, r.ids, w, r.real, dwts, dp.counts_pre, tau=tau, renormalize=renormalize,
-                         aux_coef=aux_coef, d_aux=d_aux)
+    dl = router_backward(r.probs, r.ids, w, r.real, dwts, dp.counts_pre, tau=tau,
+                         renormalize=renormalize and not straight_through, aux_coef=aux_coef, d_aux=d_aux)
     dwr, db, dx_r = router_input_grads(dl, x64, wr64)
     dx += dx_r
     return Grads(dx, dwr, db, dw1, dw2, dl, dwts, dw1s, dw2s)

@@ -736,3 +736,72 @@ def test_backward_closed_forms():
     assert np.allclose(g.dx[0], da @ w1[0][:, :], rtol=1e-13, atol=1e-15)
     assert np.all(g.dw_router == 0) and np.all(g.dbias == 0)
     assert abs(g.dweights[0, 0] - float(go[0] @ (w2[0] @ h))) < 1e-13
+
+
+# ------------------------------------------------------------------------------ straight-through estimator
+
+def test_straight_through_forward_value():
+    """P2 §3.1: the routing matrix k-hot + softmax - detach(softmax) has the k-hot value, so the
+    output is the plain sum of the selected experts' FFN outputs (written out per token here)."""
+    P, extra, cfg = _fd_case(11, T=9, k=2, tau=0.7)
+    fw = oracle.forward(P["x"], P["wr"], P["w1"], P["w2"], k=2, storage="f64", bias=P["b"], tau=0.7,
+                        exact=True, straight_through=True)
+    assert np.all(fw.routing.weights == 1.0)
+    ref = oracle.forward(P["x"], P["wr"], P["w1"], P["w2"], k=2, storage="f64", bias=P["b"], tau=0.7, exact=True)
+    assert np.array_equal(fw.routing.ids, ref.routing.ids)        # the selection is unchanged
+    for t in range(P["x"].shape[0]):
+        acc = np.zeros(P["x"].shape[1])
+        for e in fw.routing.ids[t]:
+            a = P["w1"][e] @ P["x"][t]
+            acc += P["w2"][e] @ (a / (1.0 + np.exp(-a)))
+        assert np.allclose(fw.out[t], acc, rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("case", [dict(seed=12), dict(seed=13, capacity=6, k=3, tau=1.0)])
+def test_straight_through_backward_is_the_surrogate_gradient(case):
+    """The estimator's gradient is the derivative of its surrogate: the layer with gate weights
+    1 + p_e(theta) - p_e(theta_0) on the kept slots (p = softmax(logits / tau) written with scipy,
+    the selection held at theta_0's), plus d_aux * aux_switch. Central differences of that
+    surrogate against the oracle's backward with straight_through."""
+    from scipy.special import softmax
+    P, extra, cfg = _fd_case(**case)
+    d_aux, coef = 2.0, 0.05
+
+    def fwd(Q):
+        return oracle.forward(Q["x"], Q["wr"], Q["w1"], Q["w2"], k=cfg["k"], storage="f64", bias=Q["b"],
+                              tau=cfg["tau"], capacity=cfg["capacity"], aux_coef=coef, exact=True,
+                              straight_through=True)
+
+    fw0 = fwd(P)
+    p0 = softmax((P["x"] @ P["wr"].T + P["b"]) / cfg["tau"], axis=1)
+
+    def surrogate(Q):
+        fw = fwd(Q)
+        assert np.array_equal(fw.routing.ids, fw0.routing.ids)
+        p = softmax((Q["x"] @ Q["wr"].T + Q["b"]) / cfg["tau"], axis=1)
+        out = np.zeros_like(Q["x"])
+        for t in range(Q["x"].shape[0]):
+            for j, e in enumerate(fw.routing.ids[t]):
+                row = fw.dispatch.row_of[t, j]
+                if row >= 0:
+                    out[t] += (1.0 + p[t, e] - p0[t, e]) * fw.y[row]
+        return float(np.sum(extra["d_out"] * out)) + d_aux * fw.aux[0]
+
+    g = oracle.backward(fw0, P["x"], P["wr"], P["w1"], P["w2"], extra["d_out"], storage="f64", tau=cfg["tau"],
+                        aux_coef=coef, d_aux=d_aux, straight_through=True)
+    if case.get("capacity"):
+        assert fw0.dispatch.n_dropped > 0
+    rng = np.random.default_rng(200 + case["seed"])
+    eps = 1e-6
+    for name, grad in {"x": g.dx, "wr": g.dw_router, "b": g.dbias, "w1": g.dw1, "w2": g.dw2}.items():
+        v = rng.standard_normal(P[name].shape)
+        Pp = dict(P); Pp[name] = P[name] + eps * v
+        Pm = dict(P); Pm[name] = P[name] - eps * v
+        fd = (surrogate(Pp) - surrogate(Pm)) / (2 * eps)
+        an = float(np.sum(grad * v))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+    # and it differs from the renormalised layer's true gradient (the estimator is not a gradient
+    # of the layer's output)
+    g_true = oracle.backward(fw0, P["x"], P["wr"], P["w1"], P["w2"], extra["d_out"], storage="f64",
+                             tau=cfg["tau"], aux_coef=coef, d_aux=d_aux)
+    assert not np.allclose(g.dw_router, g_true.dw_router)
