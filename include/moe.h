@@ -80,6 +80,11 @@ typedef struct {
   int32_t d_ffn_shared;      /* fs: width of the shared expert (P4 §5.2), 0 = none, else a
                                 positive multiple of 8; moe_forward then adds
                                 W2s SiLU(W1s x) to every token's output                      */
+  int32_t straight_through;  /* 0 or 1. 1: P2 §3.1's straight-through estimator. The routing
+                                matrix k-hot + softmax - detach(softmax) has the k-hot value,
+                                so every selected expert's gate weight is exactly 1
+                                (renormalize is not used). The backward calls take the gradient
+                                through the full softmax of logits / tau, as for renormalize 0. */
 } moe_config_t;
 
 /* Static text for a status code (never NULL). Host only. */
@@ -87,7 +92,7 @@ const char* moe_status_string(moe_status_t status);
 
 /* Checks a configuration on the host; touches no GPU. Returns MOE_OK, MOE_ERR_INVALID_ARGUMENT
  * (cfg NULL, a size out of the ranges above, tau not finite and > 0, capacity < -1,
- * renormalize or noise_in_logits not 0 or 1, an unknown dtype) or MOE_ERR_UNSUPPORTED
+ * renormalize, noise_in_logits or straight_through not 0 or 1, an unknown dtype) or MOE_ERR_UNSUPPORTED
  * (act_dtype != weight_dtype, except MOE_INT4 weights with bf16 activations; MOE_INT4 weights
  * also need d and f multiples of 512, T * k <= 64 * E (the weight-streaming regime) and no
  * shared expert). */
@@ -285,8 +290,9 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
  *   aux_switch through the mean probabilities]. Per real token (token_mask NULL or nonzero),
  *   with the gate weights w and their gradients dw (moe_combine_backward's dweights):
  *   renormalised weights (softmax over the k selected logits / tau) give
- *   dL[t, sel_j] = w_j (dw_j - sum_i w_i dw_i) / tau; otherwise (w = the full softmax p)
- *   dL[t] = p * (g - <p, g>) / tau with g the dw scattered to the selected experts. d_aux != 0
+ *   dL[t, sel_j] = w_j (dw_j - sum_i w_i dw_i) / tau; otherwise (w = the full softmax p, or
+ *   cfg.straight_through, whose forward weights are 1) dL[t] = p * (g - <p, g>) / tau with g
+ *   the dw scattered to the selected experts. d_aux != 0
  *   adds p * (a - <p, a>) / tau with a_e = d_aux coef E f_e / n, f_e = counts_pre[e] / (n k),
  *   n = sum(counts_pre) / k the real tokens. Padding tokens get dL = 0. Then, each when not
  *   NULL: dx[t] += dL[t] W_r (fp32 products, the sum added to dx's act value with one more

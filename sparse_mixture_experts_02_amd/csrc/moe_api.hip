@@ -143,6 +143,7 @@ moe_status_t run_route(const moe_config_t& c, const void* x, const float* w_rout
   p.k = c.top_k;
   p.tau = c.temperature;
   p.renormalize = c.renormalize;
+  p.straight_through = c.straight_through;
   p.x = x;
   p.w_router = w_router;
   p.bias = logits_in ? nullptr : bias;
@@ -358,6 +359,7 @@ moe_status_t moe_validate_config(const moe_config_t* c) {
   if (!(isfinite(c->temperature) && c->temperature > 0.0f)) return MOE_ERR_INVALID_ARGUMENT;
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
   if (c->noise_in_logits != 0 && c->noise_in_logits != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->straight_through != 0 && c->straight_through != 1) return MOE_ERR_INVALID_ARGUMENT;
   if (c->d_ffn_shared < 0 || c->d_ffn_shared > kMaxDim || c->d_ffn_shared % 8) return MOE_ERR_INVALID_ARGUMENT;
   if (!isfinite(c->aux_coef)) return MOE_ERR_INVALID_ARGUMENT;
   const bool dt_ok = (c->act_dtype == MOE_F32 || c->act_dtype == MOE_BF16) &&
@@ -606,7 +608,7 @@ moe_status_t moe_route_backward(const moe_config_t* cfg, const void* x, const fl
   p.tau = c.temperature;
   p.coef = c.aux_coef;
   p.d_aux = d_aux;
-  p.renormalize = c.renormalize;
+  p.renormalize = c.renormalize && !c.straight_through;   // the estimator: full-softmax gradient
   p.x = x;
   p.w_router = w_router;
   p.logits = logits;
@@ -723,7 +725,7 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const float* w
   p.tau = c.temperature;
   p.coef = c.aux_coef;
   p.d_aux = d_aux;
-  p.renormalize = c.renormalize;
+  p.renormalize = c.renormalize && !c.straight_through;   // the estimator: full-softmax gradient
   p.x = x;
   p.w_router = w_router;
   p.logits = logits;

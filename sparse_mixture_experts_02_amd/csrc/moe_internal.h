@@ -56,6 +56,7 @@ struct RouteParams {
   int T, d, E, k;
   float tau;
   int renormalize;
+  int straight_through;     // gate weight 1 for every selected expert
   const void* x;            // [T, d] act
   const float* w_router;    // [E, d] fp32, 16-byte aligned
   const float* bias;        // [E] or null

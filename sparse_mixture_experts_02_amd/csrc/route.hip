@@ -156,7 +156,7 @@ __device__ __forceinline__ void finish_tile(const RouteParams& p, f32x4_t (&acc)
       if (p.probs_out) p.probs_out[(size_t)t * E + e] = prob;
       st.p[et] += (double)prob;
       if (slot[et] >= 0) {
-        const float w = p.renormalize ? __fdiv_rn(ex_sel[et], s_sel) : prob;
+        const float w = p.straight_through ? 1.0f : (p.renormalize ? __fdiv_rn(ex_sel[et], s_sel) : prob);
         p.ids[(size_t)t * K + slot[et]] = e;
         p.weights[(size_t)t * K + slot[et]] = w;
       }

@@ -47,6 +47,7 @@ class Workload:
     padding: float = 0.0        # fraction of padding tokens (drawn per token; 0: no mask)
     d_ffn_shared: int = 0       # width of the shared expert (0: none)
     weight_dtype: Optional[str] = None   # "int4": the library gets 4-bit copies of W1/W2
+    straight_through: bool = False       # gate weights 1, gradient through the full softmax
     seed: int = 0
 
     @property

@@ -20,7 +20,8 @@ def config_for(w: Workload, T: Optional[int] = None) -> MoEConfig:
     return MoEConfig(T=T, d_model=w.d_model, d_ffn=w.d_ffn, num_experts=w.num_experts, top_k=w.top_k,
                      capacity=cap, temperature=w.temperature, renormalize=w.renormalize,
                      aux_coef=w.aux_coef, dtype=w.dtype, noise_in_logits=w.router_noise > 0.0,
-                     d_ffn_shared=w.d_ffn_shared, weight_dtype=w.weight_dtype)
+                     d_ffn_shared=w.d_ffn_shared, weight_dtype=w.weight_dtype,
+                     straight_through=w.straight_through)
 
 
 def forward(cfg: MoEConfig, x, w_router, w1, w2, *, bias=None, gumbel=None, token_mask=None, w1_shared=None,

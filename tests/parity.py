@@ -97,7 +97,8 @@ def check_routing_and_dispatch(w: Workload, cfg: moe.MoEConfig, inp: dict, g: di
     mask = inp.get("token_mask")
     mask = None if mask is None else mask.numpy()
     r = oracle.route(logits=g["logits"].numpy(), gumbel=inp["gumbel"], tau=cfg.temperature, k=k,
-                     renormalize=cfg.renormalize, noise_in_logits=cfg.noise_in_logits, token_mask=mask)
+                     renormalize=cfg.renormalize, noise_in_logits=cfg.noise_in_logits, token_mask=mask,
+                     straight_through=cfg.straight_through)
     assert np.array_equal(g["ids"].numpy(), r.ids), "Mode R: expert ids differ"
     w_err = float(np.max(np.abs(g["weights"].numpy().astype(np.float64) - r.weights))) if T else 0.0
     assert w_err <= W_TOL, f"Mode R: gate weights differ by {w_err}"
@@ -105,7 +106,7 @@ def check_routing_and_dispatch(w: Workload, cfg: moe.MoEConfig, inp: dict, g: di
     assert probs_err <= W_TOL, f"router probabilities differ by {probs_err}"
     # Mode E: the oracle's own logits
     re = oracle.route(inp["x"], inp["w_router"], inp["bias"], inp["gumbel"], cfg.temperature, k, cfg.renormalize,
-                      noise_in_logits=cfg.noise_in_logits, token_mask=mask)
+                      noise_in_logits=cfg.noise_in_logits, token_mask=mask, straight_through=cfg.straight_through)
     l_err = float(np.max(np.abs(g["logits"].numpy().astype(np.float64) - re.logits)))
     scale = max(1.0, float(np.max(np.abs(re.logits))))
     assert l_err <= 1e-5 * scale, f"Mode E: logits differ by {l_err}"

@@ -72,6 +72,10 @@ def test_validate_rejects_bad_renormalize_flag():
     assert binding.lib().moe_validate_config(ctypes.byref(c)) == 1
     c.noise_in_logits = 1
     assert binding.lib().moe_validate_config(ctypes.byref(c)) == 0
+    c.straight_through = 2
+    assert binding.lib().moe_validate_config(ctypes.byref(c)) == 1
+    c.straight_through = 1
+    assert binding.lib().moe_validate_config(ctypes.byref(c)) == 0
     assert binding.lib().moe_validate_config(None) == 1
 
 

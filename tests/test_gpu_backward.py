@@ -100,6 +100,9 @@ ROUTER_CASES = {
     # additive noise in the logits, 64 experts, no aux gradient
     "rbwd_noise_e64": (derived(WORKLOADS["main_noise_padding"], name="rbwd_noise_e64", T=520, d_model=128,
                                d_ffn=64, num_experts=64, top_k=4), 0.0),
+    # the straight-through estimator with Gumbel selection and capacity (P2 §3.1)
+    "rbwd_straight_through": (derived(WORKLOADS["skewed_gumbel_capacity"], name="rbwd_straight_through", T=800,
+                                      d_model=256, d_ffn=64, straight_through=True), 1.0),
     # the layer's full size (16384 tokens, d 2048, 8 experts)
     "rbwd_main": (BASE, 1.0),
 }
@@ -133,7 +136,8 @@ def test_router_backward(name):
     probs = np.zeros((T, E))
     probs[real] = oracle.router_probs(g["logits"].numpy()[real], cfg.temperature)
     dl_ref = oracle.router_backward(probs, g["ids"].numpy(), g["weights"].numpy(), real, dwts.numpy(),
-                                    g["counts_pre"].numpy(), tau=cfg.temperature, renormalize=cfg.renormalize,
+                                    g["counts_pre"].numpy(), tau=cfg.temperature,
+                                    renormalize=cfg.renormalize and not cfg.straight_through,
                                     aux_coef=cfg.aux_coef, d_aux=d_aux)
     dwr_ref, db_ref, dxr_ref = oracle.router_input_grads(dl_ref, inp["x"], inp["w_router"])
     errs = {"dL": normwise(dlog.cpu().numpy(), dl_ref), "dW_r": normwise(dwr.cpu().numpy(), dwr_ref),
@@ -158,6 +162,9 @@ FULL_CASES = {
     "bwd_all_shared_noise_padding": (derived(WORKLOADS["main_noise_padding"], name="bwd_all_shared_noise_padding",
                                              T=520, d_model=128, d_ffn=192, num_experts=8, d_ffn_shared=160),
                                      1.0),
+    # the straight-through estimator: unit gate weights, Gumbel selection, capacity drops
+    "bwd_all_straight_through": (derived(WORKLOADS["skewed_gumbel_capacity"], name="bwd_all_straight_through",
+                                         T=600, d_model=128, d_ffn=192, num_experts=8, straight_through=True), 1.0),
     # 256 x 256 grouped GEMMs on both the routed and the shared products
     "bwd_all_big_shared": (derived(BASE, name="bwd_all_big_shared", T=2048, d_model=128, d_ffn=256, num_experts=2,
                                    d_ffn_shared=256), 0.5),
@@ -217,6 +224,7 @@ def test_moe_backward_whole_layer(name):
     fw = _oracle_forward_from_gpu(g, inp, cfg)
     ref = oracle.backward(fw, inp["x"], inp["w_router"], inp["w1"], inp["w2"], d_out, storage=st,
                           tau=cfg.temperature, renormalize=cfg.renormalize, aux_coef=cfg.aux_coef, d_aux=d_aux,
+                          straight_through=cfg.straight_through,
                           w1_shared=inp.get("w1_shared"), w2_shared=inp.get("w2_shared"))
     pairs = {"dx": ref.dx, "dw_router": ref.dw_router, "dbias": ref.dbias, "dw1": ref.dw1, "dw2": ref.dw2}
     if fs:

@@ -34,6 +34,9 @@ REDUCED = {
     "single_expert": derived(BASE, name="single_expert", T=200, d_model=128, d_ffn=128, num_experts=1, top_k=1),
     "one_token": derived(BASE, name="one_token", T=1, d_model=128, d_ffn=64, num_experts=8),
     "not_renormalised": derived(BASE, name="not_renormalised", T=300, d_model=128, d_ffn=128, renormalize=False),
+    # P2 §3.1's straight-through estimator: Gumbel selection, every selected expert with weight 1
+    "straight_through_gumbel": derived(WORKLOADS["skewed_gumbel_capacity"], name="straight_through_gumbel", T=700,
+                                       d_model=256, d_ffn=256, straight_through=True),
     "small_t_streaming_reduced": derived(WORKLOADS["small_t_streaming"], name="small_t_streaming_reduced",
                                          d_model=512, d_ffn=1024),
     # weight-streaming GEMM with experts longer than one 64-row chunk (router bias skews the load)
