@@ -239,3 +239,74 @@ def test_moe_backward_whole_layer(name):
     for n, e in errs.items():
         lim = 1e-4 if (n in ("dw_router", "dbias")) else tol
         assert e <= lim, (n, errs)
+
+
+def test_moe_backward_main_size_sampled():
+    """moe_backward at the layer's full size (16384 tokens, d 2048, f 4096, 8 experts, top-2; the
+    launch configuration bench.py --backward times) on outputs the oracle can form exactly one by
+    one: the hidden units are independent in dW1 / dW2 (the oracle's expert backward on 16
+    sampled units gives those rows of dW1 and columns of dW2 exactly), dXp is per row (the
+    oracle's expert backward on 48 sampled tokens' rows gives their dx), and the router gradients
+    are cheap in full."""
+    w, d_aux = BASE, 1.0
+    print(f"[gpu] moe_backward full size sampled: {w}", flush=True)
+    cfg = moe.config_for(w)
+    inp = make_inputs(w)
+    dinp = to_device(inp)
+    g = run_gpu(cfg, dinp)
+    T, d, f, E, k = cfg.T, cfg.d_model, cfg.d_ffn, cfg.num_experts, cfg.top_k
+    dt = cfg.torch_dtype
+    dev = "cuda"
+    fwd_ws = moe.new_workspace(cfg, dev)
+    moe.forward(cfg, dinp["x"], dinp["w_router"], dinp["w1"], dinp["w2"], bias=dinp["bias"], gumbel=dinp["gumbel"],
+                ws=fwd_ws)
+    gen = torch.Generator().manual_seed(6)
+    d_out = torch.randn(T, d, generator=gen).to(dt)
+    dx = torch.empty(T, d, dtype=dt, device=dev)
+    dwr = torch.empty(E, d, device=dev)
+    db = torch.empty(E, device=dev)
+    dw1 = torch.empty(E, f, d, device=dev)
+    dw2 = torch.empty(E, d, f, device=dev)
+    moe.moe_backward(cfg, dinp["x"], dinp["w_router"], dinp["w1"], dinp["w2"], d_out.to(dev), fwd_ws, dx,
+                     moe.new_backward_workspace(cfg), d_aux=d_aux, dw_router=dwr, dbias=db, dw1=dw1, dw2=dw2)
+    torch.cuda.synchronize()
+    row_of = g["row_of"].numpy()
+    offsets = g["offsets"].numpy()
+    N = int(offsets[-1])
+    dy, dwts = oracle.combine_backward(d_out, g["y"], row_of, g["weights"].numpy(), "f64")
+    rng = np.random.default_rng(8)
+    # 16 hidden units: dW1[:, u, :] and dW2[:, :, u]
+    u = np.sort(rng.choice(f, 16, replace=False))
+    w1_64 = inp["w1"].double().numpy()
+    w2_64 = inp["w2"].double().numpy()
+    h = g["h"][:N]
+    _, dw1_u, dw2_u = oracle.expert_ffn_backward(g["xp"][:N], offsets, w1_64[:, u, :], w2_64[:, :, u],
+                                                 h[:, u], dy[:N], "f64")
+    e1 = normwise(dw1.cpu().numpy()[:, u, :], dw1_u)
+    e2 = normwise(dw2.cpu().numpy()[:, :, u], dw2_u)
+    # 48 tokens: their kept rows, ascending (grouped by expert), through the full expert weights
+    toks = np.sort(rng.choice(T, 48, replace=False))
+    rows = np.sort(row_of[toks][row_of[toks] >= 0])
+    off_s = np.searchsorted(rows, offsets).astype(np.int32)
+    dxp_s, _, _ = oracle.expert_ffn_backward(g["xp"][rows], off_s, w1_64, w2_64, g["h"][rows], dy[rows], "f64")
+    where = {int(r): i for i, r in enumerate(rows)}
+    probs = oracle.router_probs(g["logits"].numpy(), cfg.temperature)
+    real = np.ones(T, dtype=bool)
+    dl = oracle.router_backward(probs, g["ids"].numpy(), g["weights"].numpy(), real, dwts, g["counts_pre"].numpy(),
+                                tau=cfg.temperature, renormalize=cfg.renormalize, aux_coef=cfg.aux_coef, d_aux=d_aux)
+    dwr_ref, db_ref, _ = oracle.router_input_grads(dl, inp["x"], inp["w_router"])
+    wr64 = inp["w_router"].double().numpy()
+    dx_ref = np.zeros((len(toks), d))
+    for i, t in enumerate(toks):
+        for j in range(k):
+            if row_of[t, j] >= 0:
+                dx_ref[i] += dxp_s[where[int(row_of[t, j])]]
+        dx_ref[i] += dl[t] @ wr64
+    ex = normwise(dx.cpu().double().numpy()[toks], dx_ref)
+    er = normwise(dwr.cpu().numpy(), dwr_ref)
+    eb = normwise(db.cpu().numpy(), db_ref)
+    print(f"[gpu] full size: dW1[units] {e1:.2e} dW2[units] {e2:.2e} dx[tokens] {ex:.2e} dW_r {er:.2e} db {eb:.2e}",
+          flush=True)
+    tol = NORM_TOL[cfg.dtype]
+    assert e1 <= tol and e2 <= tol and ex <= tol, (e1, e2, ex)
+    assert er <= 1e-4 and eb <= 1e-4, (er, eb)
