@@ -1,14 +1,15 @@
 """Benchmark of the MoE-layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload main_bf16] [--no-cpu-baseline]
-                    [--backward]
+                    [--backward] [--no-cold-cache]
 
 One step = one moe_forward call (router, dispatch, both grouped GEMMs, combine, aux loss) over
 the workload's seeded synthetic batch, with inputs already resident in HBM. W untimed steps,
 then exactly K timed steps between two device synchronisations (the throughput), then K more
 steps with HIP events recorded by the library between its kernels on the launch stream (the
 per-kernel durations; the events themselves add a few microseconds per step, so they are kept
-out of the throughput's steps).
+out of the throughput's steps), then K cold-cache steps: a 1 GiB write before each evicts the
+L2s and the Infinity Cache, and events bracket the step alone (median, p10, p90).
 
 Prints one JSON line: tokens/s of the whole layer, the roofline of the dominant kernel (the
 slower grouped GEMM: MFMA bound on the large workloads, HBM bound when a few tokens per expert
@@ -42,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens of the CPU-oracle sample (0 = the whole workload)")
+    ap.add_argument("--no-cold-cache", action="store_true",
+                    help="skip the cold-cache steps (the hardware-counter runs use this: their per-dispatch "
+                         "bytes are those of warm steps, like the roofline's durations)")
     ap.add_argument("--backward", action="store_true",
                     help="after the forward measurement, time moe_backward (all gradients) the same way "
                          "and add a 'backward' object to the line")
@@ -196,6 +200,22 @@ def main():
     t3 = time.perf_counter()
     ms_per_step_events = (t3 - t2) * 1e3 / args.steps
 
+    # cold cache: before each of K more steps, a 1 GiB write evicts the L2s and the 256 MB Infinity
+    # Cache; HIP events on the launch stream bracket the step alone (the flush is outside them)
+    cold_ms = None
+    if not args.no_cold_cache:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        for i in range(args.steps):
+            flush.fill_(float(i))
+            ev0[i].record()
+            step()
+            ev1[i].record()
+        torch.cuda.synchronize()
+        cold_ms = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)])
+        del flush
+
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -206,9 +226,11 @@ def main():
         del src, dst
 
     per_kernel = np.zeros((args.steps, MOE_FORWARD_NUM_KERNELS))
+    warm_ms = np.zeros(args.steps)
     for i, ev in enumerate(events):
         for j in range(MOE_FORWARD_NUM_KERNELS):
             per_kernel[i, j] = ev.elapsed_ms(j, j + 1)
+        warm_ms[i] = ev.elapsed_ms(0, MOE_FORWARD_NUM_KERNELS)
         ev.close()
     kms = per_kernel.mean(axis=0)
     N = int(offsets[-1].item())
@@ -273,6 +295,13 @@ def main():
                       + 8 * T * w.top_k) / (kms[names.index("route")] * 1e-3) / 1e9,
         "dispatch_gbs": dispatch_bytes / t_disp / 1e9,
         "combine_gbs": combine_bytes / t_comb / 1e9,
+        "cold_cache": None if cold_ms is None else {
+            "ms_median": float(np.median(cold_ms)), "ms_p10": float(np.percentile(cold_ms, 10)),
+            "ms_p90": float(np.percentile(cold_ms, 90)), "tokens_per_s_median": T / (float(np.median(cold_ms)) * 1e-3),
+            "protocol": "1 GiB buffer written before each step (outside the timed events)"},
+        "warm_cache_events": {"ms_median": float(np.median(warm_ms)), "ms_p10": float(np.percentile(warm_ms, 10)),
+                              "ms_p90": float(np.percentile(warm_ms, 90)),
+                              "note": "steps with the per-kernel events, caches warm from the previous step"},
         "kept_rows": N,
         "n_dropped": n_dropped,
         "inputs_sha256": digest,
