@@ -8,6 +8,8 @@ gradients (fp32 dot products) normwise 1e-5. moe_route_backward against the orac
 backward on the GPU's logits, ids, weights and counts with seeded gate-weight gradients: the
 logit, router-weight and bias gradients normwise 1e-5 (fp32 against float64), dx as stored.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -168,6 +170,15 @@ FULL_CASES = {
     # 256 x 256 grouped GEMMs on both the routed and the shared products
     "bwd_all_big_shared": (derived(BASE, name="bwd_all_big_shared", T=2048, d_model=128, d_ffn=256, num_experts=2,
                                    d_ffn_shared=256), 0.5),
+    # degenerate cases: every slot dropped (C = 0: only the aux term reaches the router), one token,
+    # the most experts and slots (64, top-8: most experts get no rows), every token padding
+    "bwd_all_zero_capacity": (derived(BASE, name="bwd_all_zero_capacity", T=200, d_model=64, d_ffn=64,
+                                      num_experts=4), 1.0, {"capacity": 0}),
+    "bwd_all_one_token": (derived(BASE, name="bwd_all_one_token", T=1, d_model=64, d_ffn=64, num_experts=4), 1.0),
+    "bwd_all_e64_k8": (derived(BASE, name="bwd_all_e64_k8", T=300, d_model=64, d_ffn=64, num_experts=64, top_k=8),
+                       1.0),
+    "bwd_all_all_padding": (derived(WORKLOADS["main_noise_padding"], name="bwd_all_all_padding", T=100, d_model=64,
+                                    d_ffn=64, padding=1.0), 1.0),
 }
 
 
@@ -190,9 +201,11 @@ def _oracle_forward_from_gpu(g, inp, cfg):
 @pytest.mark.parametrize("name", list(FULL_CASES))
 def test_moe_backward_whole_layer(name):
     """moe_backward from the forward's workspace against the oracle's backward of the same forward."""
-    w, d_aux = FULL_CASES[name]
-    print(f"[gpu] moe_backward {name}: {w} d_aux={d_aux}", flush=True)
+    w, d_aux, *changes = FULL_CASES[name]
+    print(f"[gpu] moe_backward {name}: {w} d_aux={d_aux} {changes}", flush=True)
     cfg = moe.config_for(w)
+    if changes:
+        cfg = dataclasses.replace(cfg, **changes[0])
     inp = make_inputs(w)
     dinp = to_device(inp)
     g = run_gpu(cfg, dinp)          # the intermediates, from a forward with debug buffers
