@@ -131,11 +131,15 @@ hipError_t launch_transpose(const void* in, void* out, int B, int R, int C, int 
 }
 
 // dA = dH * SiLU'(A), SiLU'(a) = s (1 + a (1 - s)) with s = sigmoid(a), in fp32, one rounding.
-// 16 bytes per thread and step (8 bf16 or 4 fp32 elements; n is a multiple of 8).
+// 16 bytes per thread and step (8 bf16 or 4 fp32 elements; cols is a multiple of 8). Rows past
+// *nrows (the kept rows, read on the device; clamped to max_rows) are left alone.
 template <bool BF16>
-__global__ __launch_bounds__(256) void silu_bwd_kernel(const void* dh, const void* a, void* da, size_t n) {
+__global__ __launch_bounds__(256) void silu_bwd_kernel(const void* dh, const void* a, void* da, const int32_t* nrows,
+                                                       int max_rows, int cols) {
   constexpr int V = BF16 ? 8 : 4;
-  const size_t nv = n / V;
+  int r = *nrows;
+  r = r < 0 ? 0 : (r > max_rows ? max_rows : r);
+  const size_t nv = (size_t)r * cols / V;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nv; i += (size_t)gridDim.x * blockDim.x) {
     const uint4 gv = ((const uint4*)dh)[i];
     const uint4 xv = ((const uint4*)a)[i];
@@ -165,13 +169,14 @@ __global__ __launch_bounds__(256) void silu_bwd_kernel(const void* dh, const voi
   }
 }
 
-hipError_t launch_silu_bwd(const void* dh, const void* a, void* da, size_t n, bool bf16, hipStream_t s) {
-  const size_t nv = n / (bf16 ? 8 : 4);
+hipError_t launch_silu_bwd(const void* dh, const void* a, void* da, const int32_t* nrows, int max_rows, int cols,
+                           bool bf16, hipStream_t s) {
+  const size_t nv = (size_t)max_rows * cols / (bf16 ? 8 : 4);
   size_t blocks = (nv + 255) / 256;
   if (blocks > 16384) blocks = 16384;
   if (blocks == 0) return hipSuccess;
-  if (bf16) silu_bwd_kernel<true><<<(unsigned)blocks, 256, 0, s>>>(dh, a, da, n);
-  else silu_bwd_kernel<false><<<(unsigned)blocks, 256, 0, s>>>(dh, a, da, n);
+  if (bf16) silu_bwd_kernel<true><<<(unsigned)blocks, 256, 0, s>>>(dh, a, da, nrows, max_rows, cols);
+  else silu_bwd_kernel<false><<<(unsigned)blocks, 256, 0, s>>>(dh, a, da, nrows, max_rows, cols);
   return hipGetLastError();
 }
 

@@ -319,7 +319,7 @@ moe_status_t expert_ffn_bwd(const moe_config_t& c, const BwdLayout& L, const voi
     g.G = dw2;
     MOE_LAUNCH(launch_grad_w(g, bf16, stream));
   }
-  MOE_LAUNCH(launch_silu_bwd(dh, a1, dh, (size_t)c.T * c.top_k * f, bf16, stream));
+  MOE_LAUNCH(launch_silu_bwd(dh, a1, dh, offsets + E, c.T * c.top_k, f, bf16, stream));
   MOE_TRY(run_gemm_sk(c, dh, w1t, dxp, offsets, d, f, false, sk, stream));
   if (dw1) {   // dW1_e = dA^T Xp over the expert's rows: [f, d]
     g.M = f;
@@ -704,7 +704,7 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const float* w
       g.G = dw2_shared;
       MOE_LAUNCH(launch_grad_w(g, bf16, stream));
     }
-    MOE_LAUNCH(launch_silu_bwd(dhs, as, dhs, (size_t)T * fs, bf16, stream));
+    MOE_LAUNCH(launch_silu_bwd(dhs, as, dhs, sh_off + 1, T, fs, bf16, stream));
     MOE_TRY(run_gemm_sk(c, dhs, w1st, dxs, sh_off, d, fs, false, sk, stream, 1, T));
     if (dw1_shared) {   // dW1s = dAs^T x: [fs, d]
       g.M = fs;

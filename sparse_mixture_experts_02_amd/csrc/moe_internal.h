@@ -227,7 +227,9 @@ hipError_t launch_combine_bwd(const CombineBwdParams& p, bool bf16, hipStream_t 
 // out[b, c, r] = in[b, r, c] for a batch of [R, C] matrices (elements of `elem` bytes, 2 or 4)
 hipError_t launch_transpose(const void* in, void* out, int B, int R, int C, int elem, hipStream_t s);
 // dA = dH * SiLU'(A), elementwise over n values (act dtype)
-hipError_t launch_silu_bwd(const void* dh, const void* a, void* da, size_t n, bool bf16, hipStream_t s);
+// nrows: device pointer to the number of rows to process (at most max_rows), e.g. offsets + E
+hipError_t launch_silu_bwd(const void* dh, const void* a, void* da, const int32_t* nrows, int max_rows, int cols,
+                           bool bf16, hipStream_t s);
 
 int probsum_num_blocks(int T);
 hipError_t launch_probsum(const ProbSumParams& p, hipStream_t s);
