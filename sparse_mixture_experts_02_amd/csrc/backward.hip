@@ -200,16 +200,15 @@ namespace moe {
 //  * two LDS buffers and two register sets: the loads of stage s + 2 are issued before the 32
 //    MFMAs of stage s, and stage s + 1 (requested a stage earlier) is transposed into the other
 //    buffer alongside them; one barrier per stage.
-constexpr int GW_TILE = 128, GW_BK = 64, GW_TP = GW_BK + 8;
+constexpr int GW_TILE = 256, GW_BK = 64, GW_TP = GW_BK + 8;
 
-__global__ __launch_bounds__(256, 2) void grad_w_bf16_kernel(GradWParams p) {
+__global__ __launch_bounds__(512, 1) void grad_w_bf16_kernel(GradWParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][GW_TILE * GW_TP];
   const int tilesM = (p.M + GW_TILE - 1) / GW_TILE, tilesN = (p.N + GW_TILE - 1) / GW_TILE;
   const int per_e = tilesM * tilesN, total = per_e * p.E;
   int b = blockIdx.x;
   if ((total & 7) == 0) b = (b & 7) * (total >> 3) + (b >> 3);   // contiguous tile range per XCD
-  // within an expert, groups of 8 m-tiles walked n-tile by n-tile: the tiles running together on
-  // an XCD form 8 x 8 blocks and share their operand rows 8 ways in its L2
+  // within an expert, groups of 8 m-tiles walked n-tile by n-tile
   const int e = b / per_e, rem = b - e * per_e;
   const int grp = rem / (8 * tilesN), gm0 = grp * 8, gsz = min(8, tilesM - gm0);
   const int in = rem - grp * 8 * tilesN;
@@ -219,13 +218,13 @@ __global__ __launch_bounds__(256, 2) void grad_w_bf16_kernel(GradWParams p) {
   r1 = r1 < r0 ? r0 : (r1 > p.max_rows ? p.max_rows : r1);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int fr = lane & 15, fg = lane >> 4;
-  // loader: operand op (P for threads 0..127, Q for 128..255; one operand per wave), 8 x 8 block
+  // loader: operand op (P for threads 0..255, Q for 256..511; one operand per wave), 8 x 8 block
   // (rb, cb) of a stage (8 consecutive lanes: the 8 row blocks of one column block, so that their
   // transposed 16-byte LDS writes are contiguous; a wave's loads are 8 rows x 128 contiguous
   // bytes). The loads go through a buffer resource per stage covering the stage's valid rows:
   // rows past the segment's end read as zeros, and so do columns past M or N (whole 8-column
   // blocks, both being multiples of 8), given an offset outside every resource.
-  const int op = tid >> 7, bi = tid & 127, rb = bi & 7, cb = bi >> 3;
+  const int op = tid >> 8, bi = tid & 255, rb = bi & 7, cb = bi >> 3;
   const int width = __builtin_amdgcn_readfirstlane(op ? p.N : p.M);
   const uint64_t opnd = (uint64_t)(uintptr_t)(op ? p.Q : p.P);
   const uint32_t opnd_lo = __builtin_amdgcn_readfirstlane((uint32_t)opnd);
@@ -238,10 +237,7 @@ __global__ __launch_bounds__(256, 2) void grad_w_bf16_kernel(GradWParams p) {
   for (int i = 0; i < 8; ++i) voff[i] = col < width ? (uint32_t)(8 * rb + i) * rowb + (uint32_t)col * 2u : 0x80000000u;
   uint16_t* const dst0 = &lds[0][op][(8 * cb) * GW_TP + 8 * rb];
   uint16_t* const dst1 = &lds[1][op][(8 * cb) * GW_TP + 8 * rb];
-  // Two register sets: stage s + 2 is requested before stage s's MFMAs, and stage s + 1's rows
-  // (requested a stage earlier, so already landed or close) are transposed into the other LDS
-  // buffer while those MFMAs run.
-  uint4 va[8], vb[8];
+  uint4 va[8];
 #define GW_LOAD(V, R)                                                                          \
   {                                                                                            \
     const int r_ = (R);                                                                        \
@@ -267,66 +263,61 @@ __global__ __launch_bounds__(256, 2) void grad_w_bf16_kernel(GradWParams p) {
       *(uint4*)((DST) + j * GW_TP) = make_uint4(o[0], o[1], o[2], o[3]);           \
     }                                                                              \
   }
-  f32x4_t acc[4][4];
+  // 8 waves in 2 x 4, each 128 x 64 of the tile: 8 x 4 blocks of 16 x 16
+  f32x4_t acc[8][4];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w >> 2, wn = w & 3;
   auto mfma_stage = [&](int buf) {
     const uint16_t* A = &lds[buf][0][0];
     const uint16_t* B = &lds[buf][1][0];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t af[4], bfr[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        af[mi] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(A + (64 * wm + 16 * mi + fr) * GW_TP + 32 * ks + 8 * fg));
+      bf16x8_t bfr[4];
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
         bfr[ni] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(B + (64 * wn + 16 * ni + fr) * GW_TP + 32 * ks + 8 * fg));
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < 8; ++mi) {
+        const bf16x8_t af =
+            __builtin_bit_cast(bf16x8_t, *(const uint4*)(A + (128 * wm + 16 * mi + fr) * GW_TP + 32 * ks + 8 * fg));
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[ni], acc[mi][ni], 0, 0, 0);
+      }
     }
   };
+  // one register set: stage s + 1 is requested before stage s's MFMAs and transposed into the
+  // other LDS buffer after them; one barrier per stage; past the last stage the loads see an
+  // empty resource and return zeros
   const int ns = (r1 - r0 + GW_BK - 1) / GW_BK;
   if (ns > 0) {
     GW_LOAD(va, r0);
     GW_STORE(va, dst0);
-    GW_LOAD(vb, r0 + GW_BK);
     __syncthreads();
   }
-  // past the last stage the loads see an empty resource and return zeros
-  for (int s = 0; s < ns; s += 2) {
-    // stage s is in buffer 0, stage s + 1 in flight in vb
-    GW_LOAD(va, r0 + (s + 2) * GW_BK);
+  for (int s = 0; s < ns; ++s) {
+    GW_LOAD(va, r0 + (s + 1) * GW_BK);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_stage(0);
-    GW_STORE(vb, dst1);
-    __syncthreads();
-    if (s + 1 >= ns) break;
-    // stage s + 1 is in buffer 1, stage s + 2 in flight in va
-    GW_LOAD(vb, r0 + (s + 3) * GW_BK);
+    mfma_stage(s & 1);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_stage(1);
-    GW_STORE(va, dst0);
+    GW_STORE(va, (s & 1) ? dst0 : dst1);
     __syncthreads();
   }
 #undef GW_LOAD
 #undef GW_STORE
-  // lane holds rows m0 + 64 wm + 16 mi + 4 fg .. + 3 of column n0 + 64 wn + 16 ni + fr
+  // lane holds rows m0 + 128 wm + 16 mi + 4 fg .. + 3 of column n0 + 64 wn + 16 ni + fr
   float* __restrict__ G = p.G + (size_t)e * p.M * p.N;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
       const int n = n0 + 64 * wn + 16 * ni + fr;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int m = m0 + 64 * wm + 16 * mi + 4 * fg + t;
+        const int m = m0 + 128 * wm + 16 * mi + 4 * fg + t;
         if (m < p.M && n < p.N) G[(size_t)m * p.N + n] = acc[mi][ni][t];
       }
     }
@@ -352,7 +343,7 @@ hipError_t launch_grad_w(const GradWParams& p, bool bf16, hipStream_t s) {
   if (bf16) {
     const int tiles = ((p.M + GW_TILE - 1) / GW_TILE) * ((p.N + GW_TILE - 1) / GW_TILE) * p.E;
     if (tiles == 0) return hipSuccess;
-    grad_w_bf16_kernel<<<tiles, 256, 0, s>>>(p);
+    grad_w_bf16_kernel<<<tiles, 512, 0, s>>>(p);
   } else {
     size_t blocks = ((size_t)p.M * p.N + 255) / 256;
     if (blocks > 4096) blocks = 4096;
