@@ -205,9 +205,11 @@ constexpr int GW_TILE = 256, GW_BK = 64, GW_TP = GW_BK + 8;
 __global__ __launch_bounds__(512, 1) void grad_w_bf16_kernel(GradWParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][GW_TILE * GW_TP];
   const int tilesM = (p.M + GW_TILE - 1) / GW_TILE, tilesN = (p.N + GW_TILE - 1) / GW_TILE;
-  const int per_e = tilesM * tilesN, total = per_e * p.E;
+  const int per_e = tilesM * tilesN, total = per_e * p.E * p.splits;
   int b = blockIdx.x;
-  if ((total & 7) == 0) b = (b & 7) * (total >> 3) + (b >> 3);   // contiguous tile range per XCD
+  if ((total & 7) == 0) b = (b & 7) * (total >> 3) + (b >> 3);   // contiguous block range per XCD
+  const int part = b % p.splits;
+  b /= p.splits;
   // within an expert, groups of 8 m-tiles walked n-tile by n-tile
   const int e = b / per_e, rem = b - e * per_e;
   const int grp = rem / (8 * tilesN), gm0 = grp * 8, gsz = min(8, tilesM - gm0);
@@ -216,6 +218,11 @@ __global__ __launch_bounds__(512, 1) void grad_w_bf16_kernel(GradWParams p) {
   int r0 = p.offsets[e], r1 = p.offsets[e + 1];
   r0 = r0 < 0 ? 0 : (r0 > p.max_rows ? p.max_rows : r0);
   r1 = r1 < r0 ? r0 : (r1 > p.max_rows ? p.max_rows : r1);
+  if (p.splits == 2) {   // this block's half of the segment, split at a whole stage
+    const int mid = min(r1, r0 + ((r1 - r0 + 2 * GW_BK - 1) / (2 * GW_BK)) * GW_BK);
+    if (part == 0) r1 = mid;
+    else r0 = mid;
+  }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int fr = lane & 15, fg = lane >> 4;
   // loader: operand op (P for threads 0..255, Q for 256..511; one operand per wave), 8 x 8 block
@@ -318,7 +325,12 @@ __global__ __launch_bounds__(512, 1) void grad_w_bf16_kernel(GradWParams p) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int m = m0 + 128 * wm + 16 * mi + 4 * fg + t;
-        if (m < p.M && n < p.N) G[(size_t)m * p.N + n] = acc[mi][ni][t];
+        if (m < p.M && n < p.N) {
+          // two halves: each adds its partial sum to the zeroed G (0 + a is exact and a + b
+          // commutes, so the result does not depend on which half lands first)
+          if (p.splits == 2) atomicAdd(&G[(size_t)m * p.N + n], acc[mi][ni][t]);
+          else G[(size_t)m * p.N + n] = acc[mi][ni][t];
+        }
       }
     }
 }
@@ -339,11 +351,24 @@ __global__ __launch_bounds__(256) void grad_w_f32_kernel(GradWParams p) {
   }
 }
 
-hipError_t launch_grad_w(const GradWParams& p, bool bf16, hipStream_t s) {
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* x, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) x[i] = 0.0f;
+}
+
+hipError_t launch_grad_w(const GradWParams& p_in, bool bf16, hipStream_t s) {
+  GradWParams p = p_in;
+  p.splits = 1;
   if (bf16) {
     const int tiles = ((p.M + GW_TILE - 1) / GW_TILE) * ((p.N + GW_TILE - 1) / GW_TILE) * p.E;
     if (tiles == 0) return hipSuccess;
-    grad_w_bf16_kernel<<<tiles, 512, 0, s>>>(p);
+    if (tiles < 256) {   // fewer tiles than CUs (a shared expert: E = 1): split each reduction in two
+      p.splits = 2;
+      const size_t n = (size_t)p.E * p.M * p.N;
+      zero_f32_kernel<<<(unsigned)std::min<size_t>((n + 255) / 256, 8192), 256, 0, s>>>(p.G, n);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
+    grad_w_bf16_kernel<<<tiles * p.splits, 512, 0, s>>>(p);
   } else {
     size_t blocks = ((size_t)p.M * p.N + 255) / 256;
     if (blocks > 4096) blocks = 4096;

@@ -200,6 +200,7 @@ struct GradWParams {
   const void* Q;            // [rows, N] act
   const int32_t* offsets;   // [E+1] expert segments of the rows
   float* G;                 // [E, M, N] fp32
+  int splits;               // set by launch_grad_w: 1, or 2 (each tile's rows in two halves, added into G)
 };
 hipError_t launch_grad_w(const GradWParams& p, bool bf16, hipStream_t s);
 struct RouteBwdParams {

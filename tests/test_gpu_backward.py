@@ -323,3 +323,32 @@ def test_moe_backward_main_size_sampled():
     tol = NORM_TOL[cfg.dtype]
     assert e1 <= tol and e2 <= tol and ex <= tol, (e1, e2, ex)
     assert er <= 1e-4 and eb <= 1e-4, (er, eb)
+
+
+def test_moe_backward_is_deterministic():
+    """Two moe_backward calls on the same forward give bit-identical gradients, including the
+    weight gradients whose reduction is split in two halves added into a zeroed output (a
+    shared expert's, and the routed experts' when there are fewer tiles than CUs)."""
+    w = derived(BASE, name="bwd_repeat", T=1500, d_model=256, d_ffn=512, num_experts=4, d_ffn_shared=512)
+    print(f"[gpu] moe_backward repeat: {w}", flush=True)
+    cfg = moe.config_for(w)
+    dinp = to_device(make_inputs(w))
+    T, d, f, E, fs = cfg.T, cfg.d_model, cfg.d_ffn, cfg.num_experts, cfg.d_ffn_shared
+    fwd_ws = moe.new_workspace(cfg, "cuda")
+    moe.forward(cfg, dinp["x"], dinp["w_router"], dinp["w1"], dinp["w2"], w1_shared=dinp["w1_shared"],
+                w2_shared=dinp["w2_shared"], ws=fwd_ws)
+    d_out = torch.randn(T, d, generator=torch.Generator().manual_seed(3)).to(cfg.torch_dtype).cuda()
+    runs = []
+    for _ in range(2):
+        g = {"dw_router": torch.empty(E, d, device="cuda"), "dbias": torch.empty(E, device="cuda"),
+             "dw1": torch.empty(E, f, d, device="cuda"), "dw2": torch.empty(E, d, f, device="cuda"),
+             "dw1_shared": torch.empty(fs, d, device="cuda"), "dw2_shared": torch.empty(d, fs, device="cuda")}
+        dx = torch.empty(T, d, dtype=cfg.torch_dtype, device="cuda")
+        moe.moe_backward(cfg, dinp["x"], dinp["w_router"], dinp["w1"], dinp["w2"], d_out, fwd_ws, dx,
+                         moe.new_backward_workspace(cfg), w1_shared=dinp["w1_shared"], w2_shared=dinp["w2_shared"],
+                         d_aux=1.0, **g)
+        g["dx"] = dx
+        runs.append({k: v.cpu() for k, v in g.items()})
+    torch.cuda.synchronize()
+    for k in runs[0]:
+        assert torch.equal(runs[0][k], runs[1][k]), k
