@@ -445,43 +445,45 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(RouteBwdParams p) {
 }
 
 // dx[t] += sum_e dL[t, e] W_r[e]: a [T, E] x [E, d] product in fp32 FMAs (the router weight is
-// fp32). A block owns 64 tokens x 256 columns: the tokens' dL rows sit in LDS, each thread keeps
-// one column's 64 token sums in registers and reads every W_r[e, c] once. The sum is rounded once
-// more to act when added to dx.
+// fp32). A block owns 64 tokens x 256 columns: the tokens' dL rows sit in LDS (read back as
+// 16-byte vectors, the same address for every lane), each thread keeps its column's EM router
+// weights in registers and adds each token's sum to dx as soon as it is formed (one more rounding
+// to act).
 constexpr int RB_TOK = 64;
-template <bool BF16>
+template <bool BF16, int EM>
 __global__ __launch_bounds__(256) void route_bwd_dx_kernel(RouteBwdParams p) {
-  __shared__ float sdl[RB_TOK][64];
+  __shared__ __attribute__((aligned(16))) float sdl[RB_TOK][EM];
   const int E = p.E, d = p.d;
   const int t0 = blockIdx.y * RB_TOK;
   const int c = blockIdx.x * 256 + threadIdx.x;
-  for (int i = threadIdx.x; i < RB_TOK * 64; i += 256) {
-    const int tt = i >> 6, e = i & 63;
+  for (int i = threadIdx.x; i < RB_TOK * EM; i += 256) {
+    const int tt = i / EM, e = i % EM;
     const int t = t0 + tt;
     sdl[tt][e] = (t < p.T && e < E) ? p.dlogits[(size_t)t * E + e] : 0.0f;
   }
   __syncthreads();
   if (c >= d) return;
-  float acc[RB_TOK];
+  float wv[EM];
 #pragma unroll
-  for (int tt = 0; tt < RB_TOK; ++tt) acc[tt] = 0.0f;
-  for (int e = 0; e < E; ++e) {
-    const float w = p.w_router[(size_t)e * d + c];
-#pragma unroll
-    for (int tt = 0; tt < RB_TOK; ++tt) acc[tt] = fmaf(sdl[tt][e], w, acc[tt]);
-  }
+  for (int e = 0; e < EM; ++e) wv[e] = e < E ? p.w_router[(size_t)e * d + c] : 0.0f;
   const int nt = min(RB_TOK, p.T - t0);
+  for (int tt = 0; tt < nt; ++tt) {
+    float a = 0.0f;
 #pragma unroll
-  for (int tt = 0; tt < RB_TOK; ++tt) {
-    if (tt < nt) {
-      const size_t o = (size_t)(t0 + tt) * d + c;
-      if constexpr (BF16) {
-        uint16_t* dx = (uint16_t*)p.dx;
-        dx[o] = (uint16_t)f32_to_bf16_bits(__fadd_rn(bf16_bits_to_f32(dx[o]), acc[tt]));
-      } else {
-        float* dx = (float*)p.dx;
-        dx[o] = __fadd_rn(dx[o], acc[tt]);
-      }
+    for (int e4 = 0; e4 < EM / 4; ++e4) {
+      const float4 v = *(const float4*)&sdl[tt][4 * e4];
+      a = fmaf(v.x, wv[4 * e4], a);
+      a = fmaf(v.y, wv[4 * e4 + 1], a);
+      a = fmaf(v.z, wv[4 * e4 + 2], a);
+      a = fmaf(v.w, wv[4 * e4 + 3], a);
+    }
+    const size_t o = (size_t)(t0 + tt) * d + c;
+    if constexpr (BF16) {
+      uint16_t* dx = (uint16_t*)p.dx;
+      dx[o] = (uint16_t)f32_to_bf16_bits(__fadd_rn(bf16_bits_to_f32(dx[o]), a));
+    } else {
+      float* dx = (float*)p.dx;
+      dx[o] = __fadd_rn(dx[o], a);
     }
   }
 }
@@ -583,8 +585,14 @@ hipError_t launch_route_bwd(const RouteBwdParams& p_in, bool bf16, hipStream_t s
   const int col_tiles = (p.d + 255) / 256;
   if (p.dx) {
     dim3 g(col_tiles, (p.T + RB_TOK - 1) / RB_TOK);
-    if (bf16) route_bwd_dx_kernel<true><<<g, 256, 0, s>>>(p);
-    else route_bwd_dx_kernel<false><<<g, 256, 0, s>>>(p);
+#define MOE_RBDX(EMV)                                                        \
+    if (bf16) route_bwd_dx_kernel<true, EMV><<<g, 256, 0, s>>>(p);           \
+    else route_bwd_dx_kernel<false, EMV><<<g, 256, 0, s>>>(p);
+    if (p.E <= 8) { MOE_RBDX(8) }
+    else if (p.E <= 16) { MOE_RBDX(16) }
+    else if (p.E <= 32) { MOE_RBDX(32) }
+    else { MOE_RBDX(64) }
+#undef MOE_RBDX
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -593,7 +601,8 @@ hipError_t launch_route_bwd(const RouteBwdParams& p_in, bool bf16, hipStream_t s
 #define MOE_RBW(EMV)                                                         \
     if (bf16) route_bwd_w_kernel<true, EMV><<<g, 256, 0, s>>>(p);            \
     else route_bwd_w_kernel<false, EMV><<<g, 256, 0, s>>>(p);
-    if (p.E <= 16) { MOE_RBW(16) }
+    if (p.E <= 8) { MOE_RBW(8) }
+    else if (p.E <= 16) { MOE_RBW(16) }
     else if (p.E <= 32) { MOE_RBW(32) }
     else { MOE_RBW(64) }
 #undef MOE_RBW
