@@ -488,12 +488,97 @@ __global__ __launch_bounds__(256) void route_bwd_dx_kernel(RouteBwdParams p) {
   }
 }
 
-// dW_r[e, c] = sum_t dL[t, e] x[t, c]: a [E, T] x [T, d] product, split over token chunks. A block
-// owns one chunk x 256 columns and keeps, per thread, one column's EM expert sums; the chunk's dL
-// rows stream through LDS 64 tokens at a time. Chunk partials [chunks, E, d] are summed in chunk
-// order by route_bwd_reduce_kernel (deterministic).
+// dW_r[e, c] = sum_t dL[t, e] x[t, c]: a [E, T] x [T, d] product, split over token chunks. A
+// thread owns 8 consecutive columns (one 16-byte load of x per token for bf16, two for fp32) and
+// their 8 EM sums; a block covers 2048 columns of one chunk. The chunk's dL rows stream through
+// LDS 64 tokens at a time and are read back as 16-byte vectors (the same address for every lane).
+// Four tokens per step keep several loads in flight. Chunk partials [chunks, E, d] are summed in
+// chunk order by route_bwd_reduce_kernel (deterministic).
+constexpr int RB_COLS = 2048;   // columns per block (256 threads x 8)
 template <bool BF16, int EM>
 __global__ __launch_bounds__(256) void route_bwd_w_kernel(RouteBwdParams p) {
+  __shared__ __attribute__((aligned(16))) float sdl[RB_TOK][EM];
+  const int E = p.E, d = p.d;
+  const int c8 = blockIdx.x * RB_COLS + 8 * threadIdx.x;
+  const bool active = c8 < d;
+  const int tb = blockIdx.y * p.chunk_tokens;
+  const int te = min(p.T, tb + p.chunk_tokens);
+  float acc[EM][8];
+#pragma unroll
+  for (int e = 0; e < EM; ++e)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[e][q] = 0.0f;
+  auto load8 = [&](int t, float (&xv)[8]) {
+    if constexpr (BF16) {
+      const uint4 u = *(const uint4*)((const uint16_t*)p.x + (size_t)t * d + c8);
+      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xv[2 * q] = bf16_bits_to_f32(w4[q] & 0xFFFFu);
+        xv[2 * q + 1] = bf16_bits_to_f32(w4[q] >> 16);
+      }
+    } else {
+      const float4 a = *(const float4*)((const float*)p.x + (size_t)t * d + c8);
+      const float4 b = *(const float4*)((const float*)p.x + (size_t)t * d + c8 + 4);
+      xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
+      xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
+    }
+  };
+  auto fma_token = [&](int tt, const float (&xv)[8]) {
+#pragma unroll
+    for (int e4 = 0; e4 < EM / 4; ++e4) {
+      const float4 l = *(const float4*)&sdl[tt][4 * e4];
+      const float lv[4] = {l.x, l.y, l.z, l.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[4 * e4 + u][q] = fmaf(lv[u], xv[q], acc[4 * e4 + u][q]);
+    }
+  };
+  for (int t0 = tb; t0 < te; t0 += RB_TOK) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < RB_TOK * EM; i += 256) {
+      const int tt = i / EM, e = i % EM;
+      const int t = t0 + tt;
+      sdl[tt][e] = (t < te && e < E) ? p.dlogits[(size_t)t * E + e] : 0.0f;
+    }
+    __syncthreads();
+    if (active) {
+      const int nt = min(RB_TOK, te - t0);
+      int tt = 0;
+      for (; tt + 4 <= nt; tt += 4) {   // four tokens' loads before their FMAs, in token order
+        float x0[8], x1[8], x2[8], x3[8];
+        load8(t0 + tt, x0);
+        load8(t0 + tt + 1, x1);
+        load8(t0 + tt + 2, x2);
+        load8(t0 + tt + 3, x3);
+        fma_token(tt, x0);
+        fma_token(tt + 1, x1);
+        fma_token(tt + 2, x2);
+        fma_token(tt + 3, x3);
+      }
+      for (; tt < nt; ++tt) {
+        float xv[8];
+        load8(t0 + tt, xv);
+        fma_token(tt, xv);
+      }
+    }
+  }
+  if (active) {
+    float* part = p.part + (size_t)blockIdx.y * E * d;
+#pragma unroll
+    for (int e = 0; e < EM; ++e)
+      if (e < E) {
+        *(float4*)&part[(size_t)e * d + c8] = make_float4(acc[e][0], acc[e][1], acc[e][2], acc[e][3]);
+        *(float4*)&part[(size_t)e * d + c8 + 4] = make_float4(acc[e][4], acc[e][5], acc[e][6], acc[e][7]);
+      }
+  }
+}
+
+// The same product for 32 or 64 experts (8 columns' sums per thread would not fit in registers):
+// one column per thread, 256 columns per block, the same chunks and partial layout.
+template <bool BF16, int EM>
+__global__ __launch_bounds__(256) void route_bwd_w1_kernel(RouteBwdParams p) {
   __shared__ float sdl[RB_TOK][EM];
   const int E = p.E, d = p.d;
   const int c = blockIdx.x * 256 + threadIdx.x;
@@ -536,7 +621,8 @@ __global__ __launch_bounds__(256) void route_bwd_reduce_kernel(RouteBwdParams p)
   if (blockIdx.y == 0) {
     if (i < n && p.dw_router) {
       float acc = 0.0f;
-      for (int ch = 0; ch < p.chunks; ++ch) acc += p.part[(size_t)ch * n + i];
+#pragma unroll 8
+      for (int ch = 0; ch < p.chunks; ++ch) acc += p.part[(size_t)ch * n + i];   // chunk order
       p.dw_router[i] = acc;
     }
     return;
@@ -556,10 +642,10 @@ __global__ __launch_bounds__(256) void route_bwd_reduce_kernel(RouteBwdParams p)
   if (threadIdx.x == 0) p.dbias[e] = red[0];
 }
 
-// token chunks of the router weight gradient: about 512 blocks in all, chunks a multiple of 64
-// tokens long (at most 512 chunks, so the partials take at most 512 * 256 * E fp32 per 256 columns).
+// token chunks of the router weight gradient: about 512 blocks of 2048 columns in all, chunks a
+// multiple of 64 tokens long; the partials take chunks * E * d fp32, chunks <= 512 / ceil(d / 2048).
 void route_bwd_chunks(int T, int d, int* chunks, int* chunk_tokens) {
-  const int col_tiles = (d + 255) / 256;
+  const int col_tiles = (d + RB_COLS - 1) / RB_COLS;
   const int max_chunks = (T + RB_TOK - 1) / RB_TOK;
   int ch = (512 + col_tiles - 1) / col_tiles;
   ch = max(1, min(ch, max_chunks));
@@ -597,14 +683,17 @@ hipError_t launch_route_bwd(const RouteBwdParams& p_in, bool bf16, hipStream_t s
     if (err != hipSuccess) return err;
   }
   if (p.dw_router) {
-    dim3 g(col_tiles, p.chunks);
-#define MOE_RBW(EMV)                                                         \
-    if (bf16) route_bwd_w_kernel<true, EMV><<<g, 256, 0, s>>>(p);            \
-    else route_bwd_w_kernel<false, EMV><<<g, 256, 0, s>>>(p);
-    if (p.E <= 8) { MOE_RBW(8) }
-    else if (p.E <= 16) { MOE_RBW(16) }
-    else if (p.E <= 32) { MOE_RBW(32) }
-    else { MOE_RBW(64) }
+    dim3 g((p.d + RB_COLS - 1) / RB_COLS, p.chunks);
+#define MOE_RBW(K, EMV)                                                      \
+    if (bf16) K<true, EMV><<<g, 256, 0, s>>>(p);                             \
+    else K<false, EMV><<<g, 256, 0, s>>>(p);
+    if (p.E <= 8) { MOE_RBW(route_bwd_w_kernel, 8) }
+    else if (p.E <= 16) { MOE_RBW(route_bwd_w_kernel, 16) }
+    else {
+      g.x = (p.d + 255) / 256;
+      if (p.E <= 32) { MOE_RBW(route_bwd_w1_kernel, 32) }
+      else { MOE_RBW(route_bwd_w1_kernel, 64) }
+    }
 #undef MOE_RBW
     err = hipGetLastError();
     if (err != hipSuccess) return err;
