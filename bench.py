@@ -102,9 +102,13 @@ def cpu_baseline(w, inp, ntok: int) -> dict:
 
 
 def bench_backward(args, w, cfg, dev, ws, N: int) -> dict:
-    """moe_backward over the forward's workspace (a forward pass without debug outputs): W untimed then K
-    timed calls between two device synchronisations. Each call produces dx and every weight
-    gradient (router, bias, W1, W2, the shared expert's)."""
+    """moe_backward over a forward pass's workspace: W untimed then K timed calls between two
+    device synchronisations, each producing dx and every weight gradient (router, bias, W1, W2,
+    the shared expert's). Two configurations: the layer's own (the backward recomputes the
+    pre-activation Xp W1^T) and keep_preact (the training setting: the forward keeps it, so the
+    backward skips that grouped GEMM); for the latter the forward is timed too."""
+    import dataclasses
+
     import torch
 
     import sparse_mixture_experts_02_amd as moe
@@ -120,27 +124,49 @@ def bench_backward(args, w, cfg, dev, ws, N: int) -> dict:
     if fs:
         grads.update(dw1_shared=z(fs, d), dw2_shared=z(d, fs))
     dx = torch.empty(T, d, dtype=dt, device="cuda")
-    bws = moe.new_backward_workspace(cfg)
+    out = torch.empty(T, d, dtype=dt, device="cuda")
+    aux = torch.empty(3, dtype=torch.float32, device="cuda")
 
-    def bstep():
-        moe.moe_backward(cfg, dev["x"], dev["w_router"], dev["w1"], dev["w2"], d_out, ws, dx, bws,
+    def fwd(c, wsp):
+        moe.moe_forward(c, dev["x"], dev["w_router"], dev["w1"], dev["w2"], out, aux, wsp, bias=dev["bias"],
+                        gumbel=dev["gumbel"], token_mask=dev["token_mask"], w1_shared=dev["w1_shared"],
+                        w2_shared=dev["w2_shared"])
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
+    def bwd(c, wsp, bws):
+        moe.moe_backward(c, dev["x"], dev["w_router"], dev["w1"], dev["w2"], d_out, wsp, dx, bws,
                          token_mask=dev["token_mask"], w1_shared=dev["w1_shared"], w2_shared=dev["w2_shared"],
                          d_aux=1.0, **grads)
 
-    for _ in range(args.warmup):
-        bstep()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        bstep()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    # the backward's matrix products: the recomputed pre-activation, dH, dXp, dW2 and dW1 of the
-    # routed experts (2 N d f flop each), and the shared expert's five of 2 T d fs
-    flop = 5 * 2.0 * N * d * f + 5 * 2.0 * T * d * fs
+    # the layer's own configuration: a forward without debug outputs leaves every intermediate
+    fwd(cfg, ws)
+    bws = moe.new_backward_workspace(cfg)
+    ms = timed(lambda: bwd(cfg, ws, bws))
+    # the training configuration
+    cfg_t = dataclasses.replace(cfg, keep_preact=True)
+    ws_t = moe.new_workspace(cfg_t)
+    fwd_t_ms = timed(lambda: fwd(cfg_t, ws_t))
+    fwd(cfg_t, ws_t)
+    bwd_t_ms = timed(lambda: bwd(cfg_t, ws_t, bws))
+    # the backward's matrix products: the pre-activation Xp W1^T (recomputed unless kept), dH, dXp,
+    # dW2 and dW1 of the routed experts (2 N d f flop each), and the shared expert's five of 2 T d fs
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    flop = 5 * 2.0 * N * d * f + 5 * 2.0 * T * d * fs
+    flop_t = 4 * 2.0 * N * d * f + 5 * 2.0 * T * d * fs
     return {"ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "matmul_flop": flop,
             "matmul_tflops": flop / (ms * 1e-3) / 1e12, "frac_of_peak": flop / (ms * 1e-3) / 1e12 / peak,
+            "keep_preact": {"forward_ms": fwd_t_ms, "backward_ms": bwd_t_ms, "training_step_ms": fwd_t_ms + bwd_t_ms,
+                            "training_tokens_per_s": T / ((fwd_t_ms + bwd_t_ms) * 1e-3),
+                            "backward_matmul_tflops": flop_t / (bwd_t_ms * 1e-3) / 1e12},
             "steps": args.steps, "warmup": args.warmup}
 
 
@@ -307,10 +333,6 @@ def main():
         "inputs_sha256": digest,
     }
     if args.backward:
-        # a forward pass without debug outputs leaves every intermediate the backward reads in ws
-        moe.moe_forward(cfg, dev["x"], dev["w_router"], dev["w1"], dev["w2"], out, aux, ws, bias=dev["bias"],
-                        gumbel=dev["gumbel"], token_mask=dev["token_mask"], w1_shared=dev["w1_shared"],
-                        w2_shared=dev["w2_shared"])
         line["backward"] = bench_backward(args, w, cfg, dev, ws, N)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_sample_tokens)

@@ -85,6 +85,12 @@ typedef struct {
                                 so every selected expert's gate weight is exactly 1
                                 (renormalize is not used). The backward calls take the gradient
                                 through the full softmax of logits / tau, as for renormalize 0. */
+  int32_t keep_preact;       /* 0 or 1. 1 (training): moe_forward also keeps the pre-activation
+                                A = Xp W1^T (rounded once to act) in its workspace, and
+                                moe_backward reads it instead of recomputing it: one grouped GEMM
+                                less per backward for one [T*k, f] write per forward. The values
+                                are the ones a recompute would give, bit for bit. Not with
+                                MOE_INT4 weights (MOE_ERR_UNSUPPORTED).                      */
 } moe_config_t;
 
 /* Static text for a status code (never NULL). Host only. */
@@ -92,7 +98,7 @@ const char* moe_status_string(moe_status_t status);
 
 /* Checks a configuration on the host; touches no GPU. Returns MOE_OK, MOE_ERR_INVALID_ARGUMENT
  * (cfg NULL, a size out of the ranges above, tau not finite and > 0, capacity < -1,
- * renormalize, noise_in_logits or straight_through not 0 or 1, an unknown dtype) or MOE_ERR_UNSUPPORTED
+ * renormalize, noise_in_logits, straight_through or keep_preact not 0 or 1, an unknown dtype) or MOE_ERR_UNSUPPORTED
  * (act_dtype != weight_dtype, except MOE_INT4 weights with bf16 activations; MOE_INT4 weights
  * also need d and f multiples of 512, T * k <= 64 * E (the weight-streaming regime) and no
  * shared expert). */

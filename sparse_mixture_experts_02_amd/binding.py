@@ -48,7 +48,8 @@ class _Config(ctypes.Structure):
                 ("temperature", ctypes.c_float), ("renormalize", ctypes.c_int32),
                 ("aux_coef", ctypes.c_float), ("act_dtype", ctypes.c_int32),
                 ("weight_dtype", ctypes.c_int32), ("noise_in_logits", ctypes.c_int32),
-                ("d_ffn_shared", ctypes.c_int32), ("straight_through", ctypes.c_int32)]
+                ("d_ffn_shared", ctypes.c_int32), ("straight_through", ctypes.c_int32),
+                ("keep_preact", ctypes.c_int32)]
 
 
 class _Debug(ctypes.Structure):
@@ -74,13 +75,15 @@ class MoEConfig:
     noise_in_logits: bool = False        # the noise input: Gumbel key noise (False) or additive logit noise
     d_ffn_shared: int = 0                # width of the shared expert (0: none)
     straight_through: bool = False       # gate weights 1, gradient through the full softmax
+    keep_preact: bool = False            # training: the forward keeps Xp W1^T for the backward
 
     def to_c(self) -> _Config:
         dt = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4}
         wd = self.weight_dtype or self.dtype
         return _Config(self.T, self.d_model, self.d_ffn, self.num_experts, self.top_k, self.capacity,
                        self.temperature, int(self.renormalize), self.aux_coef, dt.get(self.dtype, 99),
-                       dt.get(wd, 99), int(self.noise_in_logits), self.d_ffn_shared, int(self.straight_through))
+                       dt.get(wd, 99), int(self.noise_in_logits), self.d_ffn_shared, int(self.straight_through),
+                       int(self.keep_preact))
 
     @property
     def torch_dtype(self) -> torch.dtype:

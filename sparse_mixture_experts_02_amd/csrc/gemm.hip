@@ -142,6 +142,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
         const int row = row0 + wm * 64 + i * 16 + 4 * fg + r;
         if (row < row_end && col < N) {
           float v = acc[i][j][r];
+          if (SILU && p.C2) {   // the pre-activation, rounded once
+            if constexpr (BF16)
+              ((uint16_t*)p.C2)[(size_t)row * N + col] = (uint16_t)f32_to_bf16_bits(v);
+            else
+              ((float*)p.C2)[(size_t)row * N + col] = v;
+          }
           if (SILU) v = v / (1.0f + expf(-v));
           if constexpr (BF16)
             ((uint16_t*)p.C)[(size_t)row * N + col] = (uint16_t)f32_to_bf16_bits(v);

@@ -37,6 +37,8 @@
 // K must be a multiple of 64, at least 128, and N of 8.
 #include "moe_internal.h"
 
+#include <type_traits>
+
 namespace moe {
 
 namespace {
@@ -135,7 +137,7 @@ __device__ __forceinline__ void store_part(i32x4_t rsrc, uint32_t voff, uint32_t
 }
 }  // namespace
 
-template <bool SILU>
+template <bool SILU, bool PRE>
 __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
 
@@ -264,8 +266,10 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   };
 
   // Epilogue of tile t from the accumulators (after the wait states that let the last MFMAs
-  // retire): SiLU, one rounding, and row-contiguous stores through a per-wave LDS area.
-  auto store_tile = [&](const Tile& t) {
+  // retire): SiLU (when S), one rounding, and row-contiguous stores to dst through a per-wave
+  // LDS area.
+  auto store_pass = [&](const Tile& t, auto silu_c, uint16_t* dst) {
+    constexpr bool S = decltype(silu_c)::value;
     // per-lane epilogue offsets, recomputed for every tile rather than held across the main loop
     int lane_o = lane;
     asm volatile("" : "+v"(lane_o));
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     // and a store instruction covers 8 rows x 128 contiguous bytes: whole lines, where the MFMA
     // layout would store 16 rows x 64 bytes (a third of the throughput per CU). The 8 chunks of an
     // LDS row are XOR-swizzled by the row.
-    const i32x4_t rc = make_rsrc(C + (size_t)t.row0 * N, (uint32_t)t.rows * N * 2);
+    const i32x4_t rc = make_rsrc(dst + (size_t)t.row0 * N, (uint32_t)t.rows * N * 2);
     uint8_t* const ep = epi + w * EPI_BYTES;
     const int rrow = lane_o >> 3, rchunk = lane_o & 7;   // read-back: row within 8, chunk
   #pragma unroll
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
         for (int h = 0; h < 2; ++h) {
           float a0 = acc[i][2 * jp][2 * h], a1 = acc[i][2 * jp][2 * h + 1];
           float b0 = acc[i][2 * jp + 1][2 * h], b1 = acc[i][2 * jp + 1][2 * h + 1];
-          if (SILU) {
+          if constexpr (S) {
             a0 = silu_fast(a0);
             a1 = silu_fast(a1);
             b0 = silu_fast(b0);
@@ -314,6 +318,15 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
         store16(rc, off, u32x4_t{v.x, v.y, v.z, v.w});
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // PRE (a SiLU GEMM with p.C2): also the pre-activation, same tile, before the SiLU pass
+  auto store_tile = [&](const Tile& t) {
+    if constexpr (SILU) {
+      if constexpr (PRE) store_pass(t, std::false_type{}, (uint16_t*)p.C2);
+      store_pass(t, std::true_type{}, C);
+    } else {
+      store_pass(t, std::false_type{}, C);
     }
   };
 
@@ -557,6 +570,12 @@ __global__ __launch_bounds__(256) void gemm_tail_kernel(GemmParams p, int G) {
     }
     if (m >= rows || n >= cols) continue;
     float v[4] = {s.x, s.y, s.z, s.w};
+    if (SILU && p.C2) {   // the pre-activation, rounded once
+      uint2 a;
+      a.x = pack_bf16x2(v[0], v[1]);
+      a.y = pack_bf16x2(v[2], v[3]);
+      *(uint2*)((uint16_t*)p.C2 + (size_t)(row0 + m) * N + n0 + n) = a;
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) v[u] = SILU ? silu_fast(v[u]) : v[u];
     uint2 out;
@@ -577,8 +596,9 @@ int gemm_big_grid(int max_rows, int E, int N) {
 hipError_t launch_gemm_big(const GemmParams& p, bool silu, hipStream_t s) {
   if (p.K < 128) return hipErrorInvalidValue;   // the pipeline needs two K stages per tile
   const int grid = gemm_big_grid(p.max_rows, p.E, p.N);
-  if (silu) gemm_big_kernel<true><<<grid, 512, 0, s>>>(p);
-  else gemm_big_kernel<false><<<grid, 512, 0, s>>>(p);
+  if (silu && p.C2) gemm_big_kernel<true, true><<<grid, 512, 0, s>>>(p);
+  else if (silu) gemm_big_kernel<true, false><<<grid, 512, 0, s>>>(p);
+  else gemm_big_kernel<false, false><<<grid, 512, 0, s>>>(p);
   if (p.sk_part && grid == MAX_WGS && p.K / 64 >= 64) {   // tail_parts splits nothing below 64 stages
     // the kernel works out how many tail tiles there are (none: it returns at once)
     if (silu) gemm_tail_kernel<true><<<4 * MAX_WGS, 256, 0, s>>>(p, grid);

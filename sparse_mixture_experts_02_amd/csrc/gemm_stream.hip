@@ -168,6 +168,12 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(GemmParams p) {
         const int n = w * (SB_N / 4) + b * 16 + 4 * fc;
         if (n >= cols) continue;
         float v[4];
+        if (SILU && p.C2) {   // the pre-activation, rounded once
+          uint2 a;
+          a.x = pack_bf16x2(acc[i][b][0], acc[i][b][1]);
+          a.y = pack_bf16x2(acc[i][b][2], acc[i][b][3]);
+          *(uint2*)((uint16_t*)p.C2 + (size_t)(m0 + r) * N + n0 + n) = a;
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) v[u] = SILU ? sb_silu(acc[i][b][u]) : acc[i][b][u];
         uint2 o;

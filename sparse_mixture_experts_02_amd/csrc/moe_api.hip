@@ -17,6 +17,7 @@ struct Layout {
   size_t logits, ids, weights, counts_pre, counts, offsets, perm, row_of, dropped, ndrop;
   size_t xp, h, y;
   size_t hs, ys, sh_off;   // shared expert: Hs [T, fs], Ys [T, d], its segment offsets [2]
+  size_t a1;               // keep_preact: the pre-activation A = Xp W1^T [T k, f]
   size_t sk_part;   // partial sums of the 256 x 256 grouped GEMM's split tail (empty if unused)
   size_t total;
 };
@@ -56,6 +57,7 @@ Layout layout(const moe_config_t& c) {
   L.hs = take(T * fs * a);
   L.ys = take(fs ? T * d * a : 0);
   L.sh_off = take(fs ? 8 : 0);
+  L.a1 = take(c.keep_preact ? TK * f * a : 0);
   const bool bf16 = c.act_dtype == MOE_BF16;
   const bool big = gemm_uses_big(bf16, c.d_model, c.T * c.top_k, c.num_experts) ||
                    gemm_uses_big(bf16, c.d_ffn, c.T * c.top_k, c.num_experts) ||
@@ -227,7 +229,7 @@ moe_status_t run_gather(const moe_config_t& c, const int32_t* ids, const void* x
 // `sk` is the split-tail partial-sum region of the caller's workspace (null: no split tail).
 moe_status_t run_gemm_sk(const moe_config_t& c, const void* a, const void* b, void* out, const int32_t* offsets,
                          int n, int kdim, bool silu, void* sk, hipStream_t s, int experts = -1, int rows = -1,
-                         bool int4 = false) {
+                         bool int4 = false, void* pre = nullptr) {
   if (experts < 0) experts = c.num_experts;
   if (rows < 0) rows = c.T * c.top_k;
   GemmParams p{};
@@ -239,6 +241,7 @@ moe_status_t run_gemm_sk(const moe_config_t& c, const void* a, const void* b, vo
   p.A = a;
   p.B = b;
   p.C = out;
+  p.C2 = silu ? pre : nullptr;
   p.offsets = offsets;
   if (int4) {
     p.q4_scale_off = q4_scale_offset((size_t)experts * (size_t)n, kdim);
@@ -250,9 +253,10 @@ moe_status_t run_gemm_sk(const moe_config_t& c, const void* a, const void* b, vo
 }
 
 moe_status_t run_gemm(const moe_config_t& c, const void* a, const void* b, void* out, const int32_t* offsets,
-                      int n, int kdim, bool silu, void* ws, hipStream_t s, int experts = -1, int rows = -1) {
+                      int n, int kdim, bool silu, void* ws, hipStream_t s, int experts = -1, int rows = -1,
+                      void* pre = nullptr) {
   return run_gemm_sk(c, a, b, out, offsets, n, kdim, silu, at(ws, layout(c).sk_part), s, experts, rows,
-                     c.weight_dtype == MOE_INT4 && experts < 0);
+                     c.weight_dtype == MOE_INT4 && experts < 0, pre);
 }
 
 moe_status_t run_combine(const moe_config_t& c, const void* y, const int32_t* row_of, const float* weights,
@@ -295,7 +299,7 @@ moe_status_t run_aux_final(const moe_config_t& c, const double* psum, int nparts
 // and moe_backward).
 moe_status_t expert_ffn_bwd(const moe_config_t& c, const BwdLayout& L, const void* xp, const int32_t* offsets,
                             const void* w1, const void* w2, const void* h, const void* dy, void* dxp, float* dw1,
-                            float* dw2, void* ws, hipStream_t stream) {
+                            float* dw2, void* ws, hipStream_t stream, const void* a_kept = nullptr) {
   const bool bf16 = c.act_dtype == MOE_BF16;
   const int a = (int)act_size(c), E = c.num_experts, d = c.d_model, f = c.d_ffn;
   void* w1t = at(ws, L.w1t);   // [E, d, f]
@@ -305,7 +309,8 @@ moe_status_t expert_ffn_bwd(const moe_config_t& c, const BwdLayout& L, const voi
   void* sk = at(ws, L.sk_part);
   MOE_LAUNCH(launch_transpose(w1, w1t, E, f, d, a, stream));
   MOE_LAUNCH(launch_transpose(w2, w2t, E, d, f, a, stream));
-  MOE_TRY(run_gemm_sk(c, xp, w1, a1, offsets, f, d, false, sk, stream));
+  if (a_kept) a1 = const_cast<void*>(a_kept);   // the forward's own pre-activation (read only)
+  else MOE_TRY(run_gemm_sk(c, xp, w1, a1, offsets, f, d, false, sk, stream));
   MOE_TRY(run_gemm_sk(c, dy, w2t, dh, offsets, f, d, false, sk, stream));
   GradWParams g{};
   g.E = E;
@@ -360,6 +365,7 @@ moe_status_t moe_validate_config(const moe_config_t* c) {
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
   if (c->noise_in_logits != 0 && c->noise_in_logits != 1) return MOE_ERR_INVALID_ARGUMENT;
   if (c->straight_through != 0 && c->straight_through != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->keep_preact != 0 && c->keep_preact != 1) return MOE_ERR_INVALID_ARGUMENT;
   if (c->d_ffn_shared < 0 || c->d_ffn_shared > kMaxDim || c->d_ffn_shared % 8) return MOE_ERR_INVALID_ARGUMENT;
   if (!isfinite(c->aux_coef)) return MOE_ERR_INVALID_ARGUMENT;
   const bool dt_ok = (c->act_dtype == MOE_F32 || c->act_dtype == MOE_BF16) &&
@@ -369,7 +375,8 @@ moe_status_t moe_validate_config(const moe_config_t* c) {
     // 4-bit weights: bf16 activations, whole groups of four 128-column stages, the
     // weight-streaming regime (at most 64 rows per expert on average), no shared expert
     const bool ok = c->act_dtype == MOE_BF16 && c->d_model % 512 == 0 && c->d_ffn % 512 == 0 &&
-                    (long long)c->T * c->top_k <= 64LL * c->num_experts && c->d_ffn_shared == 0;
+                    (long long)c->T * c->top_k <= 64LL * c->num_experts && c->d_ffn_shared == 0 &&
+                    c->keep_preact == 0;
     return ok ? MOE_OK : MOE_ERR_UNSUPPORTED;
   }
   if (c->act_dtype != c->weight_dtype) return MOE_ERR_UNSUPPORTED;
@@ -522,7 +529,8 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
   MOE_TRY(mark());
   MOE_TRY(run_gather(c, ids, x, offsets, perm, row_of, dropped, xp, ws, stream));
   MOE_TRY(mark());
-  MOE_TRY(run_gemm(c, xp, w1, h, offsets, c.d_ffn, c.d_model, true, ws, stream));
+  MOE_TRY(run_gemm(c, xp, w1, h, offsets, c.d_ffn, c.d_model, true, ws, stream, -1, -1,
+                   c.keep_preact ? at(ws, L.a1) : nullptr));
   MOE_TRY(mark());
   MOE_TRY(run_gemm(c, h, w2, y, offsets, c.d_model, c.d_ffn, false, ws, stream));
   MOE_TRY(mark());
@@ -675,7 +683,8 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const float* w
   cp.dweights = dwts;
   MOE_LAUNCH(launch_combine_bwd(cp, bf16, stream));
   // routed experts
-  MOE_TRY(expert_ffn_bwd(c, L, xp, offsets, w1, w2, h, dy, dxp, dw1, dw2, ws, stream));
+  MOE_TRY(expert_ffn_bwd(c, L, xp, offsets, w1, w2, h, dy, dxp, dw1, dw2, ws, stream,
+                         c.keep_preact ? at(fw, F.a1) : nullptr));
   // shared expert: one segment of all T tokens; its output joined every token's with weight 1
   void* dxs = nullptr;
   if (shared) {

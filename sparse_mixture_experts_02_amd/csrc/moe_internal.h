@@ -113,6 +113,9 @@ struct GemmParams {
   void* sk_part;
   // 4-bit weights: B is the packed buffer (codes, then bf16 scales from this byte offset)
   size_t q4_scale_off;
+  // SiLU GEMMs: when not null, also receives the pre-activation (the accumulator rounded once to
+  // act, before the SiLU), [rows, N] like C
+  void* C2;
 };
 
 struct CombineParams {

@@ -76,6 +76,17 @@ def test_validate_rejects_bad_renormalize_flag():
     assert binding.lib().moe_validate_config(ctypes.byref(c)) == 1
     c.straight_through = 1
     assert binding.lib().moe_validate_config(ctypes.byref(c)) == 0
+    c.keep_preact = 2
+    assert binding.lib().moe_validate_config(ctypes.byref(c)) == 1
+    c.keep_preact = 1
+    assert binding.lib().moe_validate_config(ctypes.byref(c)) == 0
+    q4 = _cfg(dtype="bf16", weight_dtype="int4", d_model=512, d_ffn=1024, T=128)
+    assert moe.validate_config(q4) == 0
+    assert moe.validate_config(__import__("dataclasses").replace(q4, keep_preact=True)) == 2
+    # the kept pre-activation [T*k, f] act is part of the forward workspace
+    base = _cfg()
+    kept = __import__("dataclasses").replace(base, keep_preact=True)
+    assert moe.workspace_bytes(kept) >= moe.workspace_bytes(base) + base.T * base.top_k * base.d_ffn * 4
     assert binding.lib().moe_validate_config(None) == 1
 
 

@@ -352,3 +352,46 @@ def test_moe_backward_is_deterministic():
     torch.cuda.synchronize()
     for k in runs[0]:
         assert torch.equal(runs[0][k], runs[1][k]), k
+
+
+KEEP_CASES = {
+    "keep_big": derived(BASE, name="keep_big", T=2048, d_model=128, d_ffn=256, num_experts=2),
+    "keep_main": BASE,                                                    # 256 x 256 tiles + split tail
+    "keep_stream": derived(WORKLOADS["small_t_streaming"], name="keep_stream", T=96, d_model=256, d_ffn=512),
+    "keep_f32": derived(WORKLOADS["tiny_f32"], name="keep_f32", T=150, d_model=48, d_ffn=40, num_experts=5, top_k=3),
+    "keep_shared_padding": derived(WORKLOADS["main_noise_padding"], name="keep_shared_padding", T=520, d_model=128,
+                                   d_ffn=192, d_ffn_shared=160),
+}
+
+
+@pytest.mark.parametrize("name", list(KEEP_CASES))
+def test_keep_preact_is_bitwise_the_recompute(name):
+    """keep_preact = 1: the forward's SiLU GEMM also stores its pre-activation and moe_backward
+    reads it instead of recomputing it. Same kernels, tiles and reduction order, so the output
+    and every gradient must be bit-identical to the recomputing path."""
+    w = KEEP_CASES[name]
+    print(f"[gpu] keep_preact {name}: {w}", flush=True)
+    cfg0 = moe.config_for(w)
+    cfg1 = dataclasses.replace(cfg0, keep_preact=True)
+    dinp = to_device(make_inputs(w))
+    T, d, f, E, fs = cfg0.T, cfg0.d_model, cfg0.d_ffn, cfg0.num_experts, cfg0.d_ffn_shared
+    d_out = torch.randn(T, d, generator=torch.Generator().manual_seed(4)).to(cfg0.torch_dtype).cuda()
+    res = []
+    for cfg in (cfg0, cfg1):
+        ws = moe.new_workspace(cfg, "cuda")
+        out, aux = moe.forward(cfg, dinp["x"], dinp["w_router"], dinp["w1"], dinp["w2"], bias=dinp["bias"],
+                               gumbel=dinp["gumbel"], token_mask=dinp.get("token_mask"),
+                               w1_shared=dinp.get("w1_shared"), w2_shared=dinp.get("w2_shared"), ws=ws)
+        g = {"dw_router": torch.empty(E, d, device="cuda"), "dbias": torch.empty(E, device="cuda"),
+             "dw1": torch.empty(E, f, d, device="cuda"), "dw2": torch.empty(E, d, f, device="cuda")}
+        if fs:
+            g.update(dw1_shared=torch.empty(fs, d, device="cuda"), dw2_shared=torch.empty(d, fs, device="cuda"))
+        dx = torch.empty(T, d, dtype=cfg.torch_dtype, device="cuda")
+        moe.moe_backward(cfg, dinp["x"], dinp["w_router"], dinp["w1"], dinp["w2"], d_out, ws, dx,
+                         moe.new_backward_workspace(cfg), token_mask=dinp.get("token_mask"),
+                         w1_shared=dinp.get("w1_shared"), w2_shared=dinp.get("w2_shared"), d_aux=1.0, **g)
+        g.update(out=out, aux=aux, dx=dx)
+        torch.cuda.synchronize()
+        res.append({k: v.cpu() for k, v in g.items()})
+    for k in res[0]:
+        assert torch.equal(res[0][k], res[1][k]), k
