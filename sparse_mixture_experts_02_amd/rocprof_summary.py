@@ -155,7 +155,9 @@ def traffic(a) -> int:
     write, sw = _calibrated_means(a.write_dir, "WRITE_SIZE", a.calib_kernel, a.calib_bytes)
     print(f"# calibration scale: FETCH_SIZE {sf:.3f}, WRITE_SIZE {sw:.3f}")
     print(f"# grouped GEMM sources sha256: {gemm_sources_digest()}")
-    for label, flag in (("gemm1_silu", "<true>"), ("gemm2", "<false>")):
+    # the grouped GEMMs' first template argument is the SiLU flag (gemm_big_kernel<true, false>,
+    # gemm_stream_kernel<true>, gemm_q4_kernel<true>)
+    for label, flag in (("gemm1_silu", "<true"), ("gemm2", "<false")):
         ks = [k for k in fetch if "gemm" in k and "tail" not in k and flag in k]
         if len(ks) != 1:
             continue
