@@ -1,7 +1,7 @@
 """Benchmark of the MoE-layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload main_bf16] [--no-cpu-baseline]
-                    [--backward] [--no-cold-cache]
+                    [--no-backward] [--no-cold-cache]
 
 One step = one moe_forward call (router, dispatch, both grouped GEMMs, combine, aux loss) over
 the workload's seeded synthetic batch, with inputs already resident in HBM. W untimed steps,
@@ -9,7 +9,9 @@ then exactly K timed steps between two device synchronisations (the throughput),
 steps with HIP events recorded by the library between its kernels on the launch stream (the
 per-kernel durations; the events themselves add a few microseconds per step, so they are kept
 out of the throughput's steps), then K cold-cache steps: a 1 GiB write before each evicts the
-L2s and the Infinity Cache, and events bracket the step alone (median, p10, p90).
+L2s and the Infinity Cache, and events bracket the step alone (median, p10, p90). Then the
+backward leg (unless --no-backward): moe_backward timed over W + K calls, in the layer's own
+configuration and with keep_preact (the training setting, whose forward is timed too).
 
 Prints one JSON line: tokens/s of the whole layer, the roofline of the dominant kernel (the
 slower grouped GEMM: MFMA bound on the large workloads, HBM bound when a few tokens per expert
@@ -47,8 +49,9 @@ def parse():
                     help="skip the cold-cache steps (the hardware-counter runs use this: their per-dispatch "
                          "bytes are those of warm steps, like the roofline's durations)")
     ap.add_argument("--backward", action="store_true",
-                    help="after the forward measurement, time moe_backward (all gradients) the same way "
-                         "and add a 'backward' object to the line")
+                    help="kept for older command lines: the backward leg runs by default")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward leg (moe_backward timed the same way, in a 'backward' object)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, run one elementwise copy of this many MiB (a known-size "
                          "kernel to scale hardware byte counters against)")
@@ -332,7 +335,7 @@ def main():
         "n_dropped": n_dropped,
         "inputs_sha256": digest,
     }
-    if args.backward:
+    if not args.no_backward:
         line["backward"] = bench_backward(args, w, cfg, dev, ws, N)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_sample_tokens)
