@@ -65,9 +65,69 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdParams p) {
   }
 }
 
+// bf16, top-k <= 2, d a multiple of 512 up to 4096: the same arithmetic in the same order, with
+// every load of the token (its dOut row once, the rows of both slots) issued before the first use.
+__global__ __launch_bounds__(256) void combine_bwd_k2_kernel(CombineBwdParams p) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= p.T) return;
+  const int k = p.k, d = p.d, nch = d / 512;
+  int rows[2] = {-1, -1};
+  for (int j = 0; j < k; ++j) {
+    const int r = p.row_of[(size_t)t * k + j];
+    rows[j] = (r >= p.max_rows) ? -1 : r;
+  }
+  uint4 g[8], y[2][8];
+  const uint16_t* go = (const uint16_t*)p.d_out + (size_t)t * d + lane * 8;
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    if (q < nch) g[q] = *(const uint4*)(go + 512 * q);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (j >= k || rows[j] < 0) continue;   // uniform across the wave
+    const uint16_t* yr = (const uint16_t*)p.y + (size_t)rows[j] * d + lane * 8;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q < nch) y[j][q] = *(const uint4*)(yr + 512 * q);
+  }
+  for (int j = 0; j < k; ++j) {
+    if (rows[j] < 0) {
+      if (lane == 0) p.dweights[(size_t)t * k + j] = 0.0f;
+      continue;
+    }
+    const float w = p.weights[(size_t)t * k + j];
+    float dot = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (q >= nch) break;
+      const uint32_t wg[4] = {g[q].x, g[q].y, g[q].z, g[q].w};
+      const uint4 yq = j == 0 ? y[0][q] : y[1][q];
+      const uint32_t wy[4] = {yq.x, yq.y, yq.z, yq.w};
+      float gf[8];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        gf[2 * h] = bf16_bits_to_f32(wg[h] & 0xFFFFu);
+        gf[2 * h + 1] = bf16_bits_to_f32(wg[h] >> 16);
+        dot = fmaf(gf[2 * h], bf16_bits_to_f32(wy[h] & 0xFFFFu), dot);
+        dot = fmaf(gf[2 * h + 1], bf16_bits_to_f32(wy[h] >> 16), dot);
+      }
+      uint4 o;
+      o.x = pack_bf16x2(w * gf[0], w * gf[1]);
+      o.y = pack_bf16x2(w * gf[2], w * gf[3]);
+      o.z = pack_bf16x2(w * gf[4], w * gf[5]);
+      o.w = pack_bf16x2(w * gf[6], w * gf[7]);
+      *(uint4*)((uint16_t*)p.dy + (size_t)rows[j] * d + lane * 8 + 512 * q) = o;
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);
+    if (lane == 0) p.dweights[(size_t)t * k + j] = dot;
+  }
+}
+
 hipError_t launch_combine_bwd(const CombineBwdParams& p, bool bf16, hipStream_t s) {
   const int grid = (p.T + 3) / 4;
-  if (bf16) combine_bwd_kernel<true><<<grid, 256, 0, s>>>(p);
+  if (bf16 && p.k <= 2 && p.d % 512 == 0 && p.d <= 4096) combine_bwd_k2_kernel<<<grid, 256, 0, s>>>(p);
+  else if (bf16) combine_bwd_kernel<true><<<grid, 256, 0, s>>>(p);
   else combine_bwd_kernel<false><<<grid, 256, 0, s>>>(p);
   return hipGetLastError();
 }

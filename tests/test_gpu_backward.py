@@ -31,6 +31,8 @@ CASES = {
                                     d_model=128, d_ffn=192, num_experts=8, padding=0.2, capacity_factor=(9, 10)),
     # 256 x 256 grouped GEMMs for the backward products (K = 128 and 256)
     "bwd_big": derived(BASE, name="bwd_big", T=2048, d_model=128, d_ffn=256, num_experts=2),
+    # d a multiple of 512 with top-2: the combine backward that loads a token's rows up front
+    "bwd_k2_prefetch": derived(BASE, name="bwd_k2_prefetch", T=700, d_model=1024, d_ffn=256, num_experts=4),
     # weight-streaming GEMMs (at most 64 rows per expert)
     "bwd_stream": derived(WORKLOADS["small_t_streaming"], name="bwd_stream", T=96, d_model=256, d_ffn=512),
 }
