@@ -64,6 +64,13 @@ __device__ __forceinline__ float silu_fast(float v) {
   return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// SiLU'(a) = s (1 + a (1 - s)), s = sigmoid(a), with the same hardware exp2 and reciprocal (the
+// product dH SiLU'(a) is rounded to bf16 right after).
+__device__ __forceinline__ float dsilu_fast(float a) {
+  const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * 1.44269504088896341f));
+  return s * (1.0f + a * (1.0f - s));
+}
+
 // acc += A * B on v_mfma_f32_16x16x32_bf16 with the accumulator bound to AGPRs (inline asm keeps
 // all 256 accumulators of a lane in the AGPR file). Same-shape MFMAs chained on one accumulator
 // are interlocked by the hardware; the first read of the results after the loop is preceded by
@@ -268,8 +275,10 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   // Epilogue of tile t from the accumulators (after the wait states that let the last MFMAs
   // retire): SiLU (when S), one rounding, and row-contiguous stores to dst through a per-wave
   // LDS area.
-  auto store_pass = [&](const Tile& t, auto silu_c, uint16_t* dst) {
-    constexpr bool S = decltype(silu_c)::value;
+  // MODE 0: the accumulator; 1: SiLU of it; 2: it times SiLU'(A), A = p.C2 at the same place
+  // (the backward's dA = dH SiLU'(A), one rounding)
+  auto store_pass = [&](const Tile& t, auto mode_c, uint16_t* dst) {
+    constexpr int MODE = decltype(mode_c)::value;
     // per-lane epilogue offsets, recomputed for every tile rather than held across the main loop
     int lane_o = lane;
     asm volatile("" : "+v"(lane_o));
@@ -286,8 +295,26 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     const i32x4_t rc = make_rsrc(dst + (size_t)t.row0 * N, (uint32_t)t.rows * N * 2);
     uint8_t* const ep = epi + w * EPI_BYTES;
     const int rrow = lane_o >> 3, rchunk = lane_o & 7;   // read-back: row within 8, chunk
+    // MODE 2: A's 4 features of each 16 x 16 block of row block i, one row block ahead, through a
+    // resource sized to the tile's valid rows (columns past the tile get an out-of-range offset)
+    uint2 pa[2][4];
+    auto load_pre = [&](int i, uint2 (&dstv)[4]) {
+      const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((const uint16_t*)p.C2 + (size_t)t.row0 * N), 0, t.rows * N * 2, 0x00020000);
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = wn * 64 + 16 * j + 4 * efc;
+        const uint32_t off = (n < t.cols) ? (uint32_t)((wm * 128 + 16 * i + efr) * N + t.n0 + n) * 2u : 0x80000000u;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(ra, (int)off, 0, 0);
+        dstv[j] = uint2{v[0], v[1]};
+      }
+    };
+    if constexpr (MODE == 2) load_pre(0, pa[0]);
   #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      if constexpr (MODE == 2) {
+        if (i + 1 < 8) load_pre(i + 1, pa[(i + 1) & 1]);
+      }
   #pragma unroll
       for (int jp = 0; jp < 2; ++jp) {
         uint32_t P[2], Q[2];
@@ -295,11 +322,19 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
         for (int h = 0; h < 2; ++h) {
           float a0 = acc[i][2 * jp][2 * h], a1 = acc[i][2 * jp][2 * h + 1];
           float b0 = acc[i][2 * jp + 1][2 * h], b1 = acc[i][2 * jp + 1][2 * h + 1];
-          if constexpr (S) {
+          if constexpr (MODE == 1) {
             a0 = silu_fast(a0);
             a1 = silu_fast(a1);
             b0 = silu_fast(b0);
             b1 = silu_fast(b1);
+          }
+          if constexpr (MODE == 2) {
+            const uint32_t wa = h ? pa[i & 1][2 * jp].y : pa[i & 1][2 * jp].x;
+            const uint32_t wb = h ? pa[i & 1][2 * jp + 1].y : pa[i & 1][2 * jp + 1].x;
+            a0 *= dsilu_fast(bf16_bits_to_f32(wa & 0xFFFFu));
+            a1 *= dsilu_fast(bf16_bits_to_f32(wa >> 16));
+            b0 *= dsilu_fast(bf16_bits_to_f32(wb & 0xFFFFu));
+            b1 *= dsilu_fast(bf16_bits_to_f32(wb >> 16));
           }
           const auto r = __builtin_amdgcn_permlane16_swap(pack_bf16x2(a0, a1), pack_bf16x2(b0, b1), false, false);
           P[h] = r[0];
@@ -320,13 +355,16 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // PRE (a SiLU GEMM with p.C2): also the pre-activation, same tile, before the SiLU pass
+  // PRE with SILU (p.C2 set): also the pre-activation, same tile, before the SiLU pass.
+  // PRE without SILU (p.dsilu): the product times SiLU'(p.C2).
   auto store_tile = [&](const Tile& t) {
     if constexpr (SILU) {
-      if constexpr (PRE) store_pass(t, std::false_type{}, (uint16_t*)p.C2);
-      store_pass(t, std::true_type{}, C);
+      if constexpr (PRE) store_pass(t, std::integral_constant<int, 0>{}, (uint16_t*)p.C2);
+      store_pass(t, std::integral_constant<int, 1>{}, C);
+    } else if constexpr (PRE) {
+      store_pass(t, std::integral_constant<int, 2>{}, C);
     } else {
-      store_pass(t, std::false_type{}, C);
+      store_pass(t, std::integral_constant<int, 0>{}, C);
     }
   };
 
@@ -570,6 +608,13 @@ __global__ __launch_bounds__(256) void gemm_tail_kernel(GemmParams p, int G) {
     }
     if (m >= rows || n >= cols) continue;
     float v[4] = {s.x, s.y, s.z, s.w};
+    if (!SILU && p.dsilu) {   // dA = dH SiLU'(A), A = p.C2 at the same place
+      const uint2 a = *(const uint2*)((const uint16_t*)p.C2 + (size_t)(row0 + m) * N + n0 + n);
+      v[0] *= dsilu_fast(bf16_bits_to_f32(a.x & 0xFFFFu));
+      v[1] *= dsilu_fast(bf16_bits_to_f32(a.x >> 16));
+      v[2] *= dsilu_fast(bf16_bits_to_f32(a.y & 0xFFFFu));
+      v[3] *= dsilu_fast(bf16_bits_to_f32(a.y >> 16));
+    }
     if (SILU && p.C2) {   // the pre-activation, rounded once
       uint2 a;
       a.x = pack_bf16x2(v[0], v[1]);
@@ -598,6 +643,7 @@ hipError_t launch_gemm_big(const GemmParams& p, bool silu, hipStream_t s) {
   const int grid = gemm_big_grid(p.max_rows, p.E, p.N);
   if (silu && p.C2) gemm_big_kernel<true, true><<<grid, 512, 0, s>>>(p);
   else if (silu) gemm_big_kernel<true, false><<<grid, 512, 0, s>>>(p);
+  else if (p.dsilu) gemm_big_kernel<false, true><<<grid, 512, 0, s>>>(p);
   else gemm_big_kernel<false, false><<<grid, 512, 0, s>>>(p);
   if (p.sk_part && grid == MAX_WGS && p.K / 64 >= 64) {   // tail_parts splits nothing below 64 stages
     // the kernel works out how many tail tiles there are (none: it returns at once)
