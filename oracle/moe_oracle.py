@@ -24,8 +24,12 @@ first C assignments of an expert in (token, slot) order; a dropped slot contribu
 aux losses use pre-drop counts.
 
 Every function is pinned by the CPU tests in tests/test_oracle_pins.py (brute force, closed
-forms, invariants, a hand-worked example, and finite differences for the backward pass). There
-is no "parity unpinned" function.
+forms, invariants, a hand-worked example, and finite differences for the backward pass).
+forward_rows, the token-by-token output used to check sampled tokens, is pinned to forward()'s
+output bit for bit on layers with capacity drops, fully dropped tokens, padding, both noise
+modes, a shared expert and the straight-through estimator, and planted mistakes in a copy of it
+(a skipped drop check, an unrounded term, a lost gate weight, a wrong expert) fail that pin.
+There is no "parity unpinned" function.
 """
 from __future__ import annotations
 

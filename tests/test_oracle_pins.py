@@ -805,3 +805,103 @@ def test_straight_through_backward_is_the_surrogate_gradient(case):
     g_true = oracle.backward(fw0, P["x"], P["wr"], P["w1"], P["w2"], extra["d_out"], storage="f64",
                              tau=cfg["tau"], aux_coef=coef, d_aux=d_aux)
     assert not np.allclose(g.dw_router, g_true.dw_router)
+
+
+# ------------------------------------------------------------------------------ output rows one by one
+
+def _rows_cases():
+    """Layers on which forward_rows must give exactly forward().out, row for row: capacity drops
+    (with tokens whose every slot is dropped), padding with additive noise, a shared expert,
+    Gumbel top-1, unnormalised weights, the straight-through estimator, bf16 and fp32."""
+    rng = np.random.default_rng(31)
+    T, d, f, fs, E = 40, 24, 20, 28, 5
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wr = rng.standard_normal((E, d)).astype(np.float32)
+    w1 = (0.4 * rng.standard_normal((E, f, d))).astype(np.float32)
+    w2 = (0.4 * rng.standard_normal((E, d, f))).astype(np.float32)
+    w1s = (0.4 * rng.standard_normal((fs, d))).astype(np.float32)
+    w2s = (0.4 * rng.standard_normal((d, fs))).astype(np.float32)
+    bias = np.array([2.5, 1.5, 0.0, -1.0, -2.0], np.float32)   # skewed load: expert 0 overflows
+    g = rng.gumbel(size=(T, E)).astype(np.float32)
+    n = (0.3 * rng.standard_normal((T, E))).astype(np.float32)
+    mask = (rng.random(T) < 0.75).astype(np.uint8)
+    mask[0] = 0
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16)
+    base = dict(x=x, w_router=wr, w1=w1, w2=w2)
+    return [
+        ("bf16_capacity", dict(base, x=bf(x), w1=bf(w1), w2=bf(w2)), dict(k=2, storage="bf16", bias=bias,
+                                                                          capacity=6)),
+        ("f32_padding_noise_shared", dict(base, w1_shared=w1s, w2_shared=w2s),
+         dict(k=2, storage="f32", gumbel=n, noise_in_logits=True, token_mask=mask, capacity=9)),
+        ("bf16_shared_capacity", dict(base, x=bf(x), w1=bf(w1), w2=bf(w2), w1_shared=bf(w1s), w2_shared=bf(w2s)),
+         dict(k=3, storage="bf16", bias=bias, capacity=5)),
+        ("f32_gumbel_top1", base, dict(k=1, storage="f32", gumbel=g, tau=0.7, bias=bias, capacity=10)),
+        ("f32_unnormalised", base, dict(k=2, storage="f32", renormalize=False, capacity=12)),
+        ("bf16_straight_through", dict(base, x=bf(x), w1=bf(w1), w2=bf(w2)),
+         dict(k=2, storage="bf16", gumbel=g, tau=0.7, straight_through=True, capacity=11)),
+    ]
+
+
+def _rows_of(fn, fw, inp, kw):
+    return fn(inp["x"], inp["w1"], inp["w2"], fw.routing.ids, fw.routing.weights, fw.dispatch.dropped,
+              np.arange(fw.out.shape[0]), kw["storage"], inp.get("w1_shared"), inp.get("w2_shared"))
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_forward_rows_equals_the_whole_layer(case):
+    """[P4 §2.4] weighted sum of the selected experts' outputs, [P4 §5.2] plus the shared expert:
+    the token-by-token output equals the permuted, grouped, combined layer bit for bit."""
+    name, inp, kw = _rows_cases()[case]
+    fw = oracle.forward(**{k_: v for k_, v in inp.items() if k_ in ("x", "w_router", "w1", "w2", "w1_shared",
+                                                                     "w2_shared")}, **kw)
+    # the cases exercise what they claim: drops, tokens with every slot dropped, padding
+    if "capacity" in name:
+        assert fw.dispatch.n_dropped > 0
+        every = (fw.dispatch.dropped.sum(1) == kw["k"]) if kw["k"] > 1 else fw.dispatch.dropped[:, 0] == 1
+        assert np.any(every), name
+    if "padding" in name:
+        assert np.any(fw.routing.ids == -1)
+    rows = _rows_of(oracle.forward_rows, fw, inp, kw)
+    assert rows.shape == fw.out.shape
+    assert np.array_equal(rows, fw.out), f"{name}: max diff {np.max(np.abs(rows - fw.out))}"
+    # sampled and unordered token indices give the same rows
+    idx = np.array([7, 3, 0, 39, 3])
+    sub = oracle.forward_rows(inp["x"], inp["w1"], inp["w2"], fw.routing.ids, fw.routing.weights,
+                              fw.dispatch.dropped, idx, kw["storage"], inp.get("w1_shared"), inp.get("w2_shared"))
+    assert np.array_equal(sub, fw.out[idx])
+
+
+_ROWS_MUTANTS = [
+    ("skips the dropped check", "if dropped[t, j] or ids[t, j] < 0:", "if ids[t, j] < 0:"),
+    ("leaves the shared term unrounded", "acc += round_storage(_f64(w2_shared) @ hs, storage)",
+     "acc += _f64(w2_shared) @ hs"),
+    ("leaves H unrounded", "h = round_storage(silu(w1e @ xt), storage)", "h = silu(w1e @ xt)"),
+    ("drops the gate weight", "acc += w[t, j] * y", "acc += y"),
+    ("takes slot 0's expert for every slot", "e = int(ids[t, j])", "e = int(ids[t, 0])"),
+    ("rounds the sum before the shared term", "            acc += round_storage(_f64(w2_shared) @ hs, storage)",
+     "            acc = round_storage(acc, storage) + round_storage(_f64(w2_shared) @ hs, storage)"),
+]
+
+
+@pytest.mark.parametrize("mutant", range(len(_ROWS_MUTANTS)))
+def test_forward_rows_pin_catches_planted_mistakes(mutant):
+    """A copy of forward_rows with one planted mistake (on the CPU, in this process only) fails
+    the pin above on at least one case."""
+    import inspect
+    import textwrap
+    from oracle import moe_oracle
+    what, old, new = _ROWS_MUTANTS[mutant]
+    src = textwrap.dedent(inspect.getsource(moe_oracle.forward_rows))
+    assert old in src, what
+    ns = dict(vars(moe_oracle))
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
+    bad = ns["forward_rows"]
+    caught = False
+    for name, inp, kw in _rows_cases():
+        fw = oracle.forward(**{k_: v for k_, v in inp.items() if k_ in ("x", "w_router", "w1", "w2", "w1_shared",
+                                                                         "w2_shared")}, **kw)
+        rows = _rows_of(bad, fw, inp, kw)
+        if rows.shape != fw.out.shape or not np.array_equal(rows, fw.out):
+            caught = True
+            break
+    assert caught, f"the pin misses a forward_rows that {what}"
