@@ -275,6 +275,31 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_forward without a caller workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). It runs the
+ * same kernels as moe_forward with dbg NULL and gives bitwise the same out and aux, with the
+ * workspace taken from a static device array of MOE_NOALLOC_SCRATCH_BYTES bytes: one per GPU the
+ * library runs on, on the device current at the call (x, the weights, out and aux must live
+ * there), located on the first call on each device and held until the process ends. It calls
+ * no allocating routine. The caller still owns and passes every input and output.
+ * Limit: a configuration whose moe_workspace_bytes exceeds MOE_NOALLOC_SCRATCH_BYTES (e.g. the
+ * large-batch layers whose grouped GEMM keeps split partial sums) returns
+ * MOE_ERR_WORKSPACE_TOO_SMALL before any launch; small-batch layers (the weight-streaming
+ * regime: 256 tokens, d 2048, f 4096, 16 experts, top-2 needs about 9 MiB) fit.
+ * The array keeps the last call's contents; nothing in it needs clearing between calls. Calls
+ * that overlap on one GPU (on different streams, or from several threads without ordering) share
+ * the array and race: serialise them. The intermediates are not exposed, so moe_backward cannot
+ * follow this call.
+ * moe_forward_noalloc_max_bytes: MOE_NOALLOC_SCRATCH_BYTES. Host only.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+size_t moe_forward_noalloc_max_bytes(void);
+moe_status_t moe_forward_noalloc(const moe_config_t* cfg, const void* x, const float* w_router,
+                                 const float* bias, const float* noise, const uint8_t* token_mask,
+                                 const void* w1, const void* w2, const void* w1_shared,
+                                 const void* w2_shared, void* out, float* aux, hipStream_t stream);
+
+/*
  * Backward pass [P4 §2.4: the layer is trained end to end]. Gradients of
  * L = sum(d_out * out) (+ d_aux * aux_switch) flow back through the combine, the expert FFNs and
  * the gather; the selection, the capacity cut and the noise pass none. The calls mirror the

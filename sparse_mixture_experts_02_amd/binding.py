@@ -33,7 +33,7 @@ EXPORTED_SYMBOLS = ("moe_status_string", "moe_validate_config", "moe_capacity_fr
                     "moe_int4_bytes", "moe_quantize_int4", "moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
                     "moe_aux_loss", "moe_forward", "moe_backward_workspace_bytes", "moe_combine_backward",
                     "moe_expert_ffn_backward", "moe_dispatch_backward", "moe_route_backward",
-                    "moe_backward")
+                    "moe_backward", "moe_forward_noalloc_max_bytes", "moe_forward_noalloc")
 
 
 class MoEError(RuntimeError):
@@ -143,6 +143,10 @@ def lib() -> ctypes.CDLL:
         L.moe_backward.argtypes = [cfgp] + [vp] * 8 + [ctypes.c_float, vp, sz] + [vp] * 8 + [sz, vp]
         L.moe_forward.restype = ctypes.c_int
         L.moe_forward.argtypes = [cfgp] + [vp] * 11 + [ctypes.POINTER(_Debug), vp, sz, vp]
+        L.moe_forward_noalloc_max_bytes.restype = sz
+        L.moe_forward_noalloc_max_bytes.argtypes = []
+        L.moe_forward_noalloc.restype = ctypes.c_int
+        L.moe_forward_noalloc.argtypes = [cfgp] + [vp] * 11 + [vp]
         _lib = L
     return _lib
 
@@ -318,6 +322,28 @@ def moe_forward(cfg: MoEConfig, x, w_router, w1, w2, out, aux, ws, *, bias=None,
         _ptr(aux, "aux", (3,), torch.float32), ctypes.byref(dbg) if dbg is not None else None,
         _ptr(ws, "ws"), ws.numel(), _stream())
     _check("moe_forward", st)
+
+
+def forward_noalloc_max_bytes() -> int:
+    return lib().moe_forward_noalloc_max_bytes()
+
+
+def moe_forward_noalloc(cfg: MoEConfig, x, w_router, w1, w2, out, aux, *, bias=None, gumbel=None, token_mask=None,
+                        w1_shared=None, w2_shared=None):
+    """The whole layer with the library's own static workspace (moe_forward_noalloc): no
+    workspace argument, nothing allocated by the call."""
+    T, d, f, E = cfg.T, cfg.d_model, cfg.d_ffn, cfg.num_experts
+    dt = cfg.torch_dtype
+    c = cfg.to_c()
+    st = lib().moe_forward_noalloc(
+        ctypes.byref(c), _ptr(x, "x", (T, d), dt), _ptr(w_router, "w_router", (E, d), torch.float32),
+        _ptr(bias, "bias", (E,), torch.float32), _ptr(gumbel, "gumbel", (T, E), torch.float32),
+        _ptr(token_mask, "token_mask", (T,), torch.uint8),
+        _wptr(cfg, w1, "w1", E * f, d, (E, f, d)), _wptr(cfg, w2, "w2", E * d, f, (E, d, f)),
+        _ptr(w1_shared, "w1_shared", (cfg.d_ffn_shared, d), dt) if cfg.d_ffn_shared else None,
+        _ptr(w2_shared, "w2_shared", (d, cfg.d_ffn_shared), dt) if cfg.d_ffn_shared else None,
+        _ptr(out, "out", (T, d), dt), _ptr(aux, "aux", (3,), torch.float32), _stream())
+    _check("moe_forward_noalloc", st)
 
 
 # ------------------------------------------------------------------------------ backward pass

@@ -4,6 +4,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
 using namespace moe;
@@ -131,6 +133,19 @@ moe_status_t check_ws(const moe_config_t* cfg, const void* ws, size_t ws_bytes) 
 uint8_t* at(void* ws, size_t off) { return (uint8_t*)ws + off; }
 
 int capacity_of(const moe_config_t& c) { return c.capacity < 0 ? -1 : c.capacity; }
+
+// The configuration and the required pointers of a whole-layer forward (host only).
+moe_status_t forward_args_status(const moe_config_t* cfg, const void* x, const float* w_router, const void* w1,
+                                 const void* w2, const void* w1_shared, const void* w2_shared, const void* out,
+                                 const float* aux) {
+  MOE_TRY(moe_validate_config(cfg));
+  if (!x || !w_router || !w1 || !w2 || !out || !aux) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w1) || !aligned16(w2) || !aligned16(out))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (cfg->d_ffn_shared > 0 && (!w1_shared || !w2_shared || !aligned16(w1_shared) || !aligned16(w2_shared)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return MOE_OK;
+}
 
 // ---- the kernel sequences, shared by the single-step calls and moe_forward
 
@@ -481,13 +496,8 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
                          const float* noise, const uint8_t* token_mask, const void* w1, const void* w2,
                          const void* w1_shared, const void* w2_shared, void* out, float* aux,
                          moe_debug_outputs* dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
-  MOE_TRY(moe_validate_config(cfg));
-  if (!x || !w_router || !w1 || !w2 || !out || !aux) return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w1) || !aligned16(w2) || !aligned16(out))
-    return MOE_ERR_INVALID_ARGUMENT;
+  MOE_TRY(forward_args_status(cfg, x, w_router, w1, w2, w1_shared, w2_shared, out, aux));
   const bool shared = cfg->d_ffn_shared > 0;
-  if (shared && (!w1_shared || !w2_shared || !aligned16(w1_shared) || !aligned16(w2_shared)))
-    return MOE_ERR_INVALID_ARGUMENT;
   MOE_TRY(check_ws(cfg, ws, ws_bytes));
   moe_debug_outputs none{};
   const moe_debug_outputs& D = dbg ? *dbg : none;
@@ -548,6 +558,57 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
   MOE_TRY(run_combine(c, y, row_of, weights, ys, out, stream));
   MOE_TRY(mark());
   return MOE_OK;
+}
+
+}  // extern "C"
+
+// ---- the forward without a caller workspace
+
+// The no-allocation variant's workspace: one array per GPU the library runs on, held until the
+// process ends. In host code this name only stands in for the array; its device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's `scratch`, looked up on the first call on that device.
+moe_status_t scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_forward_noalloc_max_bytes(void) { return (size_t)MOE_NOALLOC_SCRATCH_BYTES; }
+
+moe_status_t moe_forward_noalloc(const moe_config_t* cfg, const void* x, const float* w_router, const float* bias,
+                                 const float* noise, const uint8_t* token_mask, const void* w1, const void* w2,
+                                 const void* w1_shared, const void* w2_shared, void* out, float* aux,
+                                 hipStream_t stream) {
+  // every argument is checked before anything touches the GPU; a layer whose workspace is larger
+  // than the array is rejected
+  MOE_TRY(forward_args_status(cfg, x, w_router, w1, w2, w1_shared, w2_shared, out, aux));
+  if (layout(*cfg).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  MOE_TRY(scratch_of_current_device(&ws));
+  // the same kernels as moe_forward, on the array's memory; no step needs it cleared first (each
+  // kernel writes every workspace element that a later one reads)
+  return moe_forward(cfg, x, w_router, bias, noise, token_mask, w1, w2, w1_shared, w2_shared, out, aux, nullptr,
+                     ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // ---- backward pass

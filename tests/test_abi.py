@@ -245,3 +245,29 @@ def test_whole_backward_validation():
     assert bw(cfg=shared.to_c(), fb=moe.workspace_bytes(shared), wb=moe.backward_workspace_bytes(shared)) == 1
     q4 = _cfg(dtype="bf16", weight_dtype="int4", d_model=512, d_ffn=1024, T=128)
     assert bw(cfg=q4.to_c(), fb=1 << 40, wb=1 << 40) == 2
+
+
+def test_forward_noalloc_validates_before_touching_the_gpu():
+    """moe_forward_noalloc (the variant for callers that cannot allocate): its limit, and every
+    argument error, come back from host code before its static workspace is looked up."""
+    L = binding.lib()
+    B = ctypes.byref
+    fake = ctypes.c_void_p(256)
+    odd = ctypes.c_void_p(256 + 8)
+    assert moe.forward_noalloc_max_bytes() == 64 << 20
+
+    def fwd(cfg, x=fake, wr=fake, w1=fake, w2=fake, w1s=None, w2s=None, out=fake, aux=fake):
+        return L.moe_forward_noalloc(B(cfg.to_c()), x, wr, None, None, None, w1, w2, w1s, w2s, out, aux, None)
+
+    assert fwd(_cfg(T=0)) == 1
+    assert fwd(_cfg(), out=None) == 1
+    assert fwd(_cfg(), aux=None) == 1
+    assert fwd(_cfg(), x=odd) == 1
+    assert fwd(_cfg(d_ffn_shared=16), w1s=fake) == 1
+    # the main layer's workspace (~513 MiB) is beyond the array: rejected with a clear status
+    main = moe.config_for(WORKLOADS["main_bf16"])
+    assert moe.workspace_bytes(main) > moe.forward_noalloc_max_bytes()
+    assert fwd(main) == 3
+    # the weight-streaming layer fits
+    small = moe.config_for(WORKLOADS["small_t_streaming"])
+    assert moe.workspace_bytes(small) <= moe.forward_noalloc_max_bytes()
