@@ -1,22 +1,24 @@
 """Benchmark of the MoE-layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload main_bf16] [--no-cpu-baseline]
-                    [--no-backward] [--no-cold-cache]
+                    [--cpu-sample-tokens 4096] [--no-backward] [--no-cold-cache]
 
 One step = one moe_forward call (router, dispatch, both grouped GEMMs, combine, aux loss) over
 the workload's seeded synthetic batch, with inputs already resident in HBM. W untimed steps,
-then exactly K timed steps between two device synchronisations (the throughput), then K more
-steps with HIP events recorded by the library between its kernels on the launch stream (the
-per-kernel durations; the events themselves add a few microseconds per step, so they are kept
-out of the throughput's steps), then K cold-cache steps: a 1 GiB write before each evicts the
-L2s and the Infinity Cache, and events bracket the step alone (median, p10, p90). Then the
-backward leg (unless --no-backward): moe_backward timed over W + K calls, in the layer's own
-configuration and with keep_preact (the training setting, whose forward is timed too).
+then exactly K timed steps between two device synchronisations, each after a 1 GiB write that
+evicts the L2s and the Infinity Cache, timed by HIP events around the step alone (the
+throughput: cold cache). Then K warm steps back to back between two synchronisations (reported
+as warm_cache), then K more with HIP events recorded by the library between its kernels on the
+launch stream (the per-kernel durations and the roofline; the events themselves add a few
+microseconds per step). Then the backward leg (unless --no-backward): moe_backward timed over
+W + K calls, in the layer's own configuration and with keep_preact (the training setting, whose
+forward is timed too).
 
 Prints one JSON line: tokens/s of the whole layer, the roofline of the dominant kernel (the
 slower grouped GEMM: MFMA bound on the large workloads, HBM bound when a few tokens per expert
-make it a pass over the expert weights), and the CPU oracle timed on a bounded sample of the
-same workload on the host cores.
+make it a pass over the expert weights), the CPU oracle timed single-threaded on a bounded
+sample of the same workload on the host, and the parity of this run's output against the oracle
+on the whole workload (with the near-tie count).
 """
 from __future__ import annotations
 
@@ -43,11 +45,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
-                    help="tokens of the CPU-oracle sample (0 = the whole workload)")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096,
+                    help="tokens of the single-threaded CPU-oracle sample (0 = the whole workload)")
     ap.add_argument("--no-cold-cache", action="store_true",
-                    help="skip the cold-cache steps (the hardware-counter runs use this: their per-dispatch "
-                         "bytes are those of warm steps, like the roofline's durations)")
+                    help="time warm steps only (the hardware-counter runs use this: their per-dispatch bytes are "
+                         "those of warm steps, like the roofline's durations)")
     ap.add_argument("--backward", action="store_true",
                     help="kept for older command lines: the backward leg runs by default")
     ap.add_argument("--no-backward", action="store_true",
@@ -79,29 +81,109 @@ def recorded_traffic(workload: str, kernel: str):
         return None
 
 
-def cpu_baseline(w, inp, ntok: int) -> dict:
-    """The oracle, as it stands, on the first `ntok` tokens of the workload (all weights)."""
+def host_cpu() -> dict:
+    """The host the oracle runs on: CPU model, the cores this process may use, the machine's count."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": usable, "cpu_count": os.cpu_count()}
+
+
+def oracle_layer(w, inp, ntok: int, logits=None):
+    """The oracle's steps one by one on the first `ntok` tokens of the workload (all weights):
+    returns (out, aux, routing, per-step seconds). With `logits`, routing runs on those fp32
+    logits (the parity protocol's routing "given the fp32 router logits")."""
     import oracle
-    from threadpoolctl import threadpool_info
-    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    ntok = w.T if ntok <= 0 else min(ntok, w.T)
     x = inp["x"][:ntok]
     g = inp["gumbel"][:ntok] if inp["gumbel"] is not None else None
+    m = inp["token_mask"][:ntok].numpy() if inp["token_mask"] is not None else None
     C = oracle.capacity_from_factor(ntok, w.top_k, w.num_experts, w.capacity_factor)
-    m = inp["token_mask"][:ntok] if inp["token_mask"] is not None else None
     w1, w2 = inp["w1"], inp["w2"]
     if w.weight_dtype == "int4":   # the 4-bit layer: its dequantised weights (quantising is not timed)
         w1 = oracle.dequantize_int4(*oracle.quantize_int4(w1))
         w2 = oracle.dequantize_int4(*oracle.quantize_int4(w2))
+    secs = {}
+    t = time.perf_counter()
+    r = oracle.route(x, inp["w_router"], inp["bias"], g, w.temperature, w.top_k, w.renormalize, logits,
+                     noise_in_logits=w.router_noise > 0.0, token_mask=m, straight_through=w.straight_through)
+    secs["route"] = time.perf_counter() - t
+    t = time.perf_counter()
+    dp = oracle.dispatch(r.ids, w.num_experts, C, x)
+    secs["dispatch"] = time.perf_counter() - t
+    t = time.perf_counter()
+    _, y = oracle.expert_ffn(dp.xp, dp.offsets, w1, w2, w.dtype)
+    ys = None
+    if inp["w1_shared"] is not None:
+        _, ys = oracle.shared_ffn(x, inp["w1_shared"], inp["w2_shared"], w.dtype)
+    secs["expert_ffn"] = time.perf_counter() - t
+    t = time.perf_counter()
+    out = oracle.combine(y, dp.row_of, r.weights, w.dtype, d=w.d_model, y_shared=ys)
+    secs["combine"] = time.perf_counter() - t
+    t = time.perf_counter()
+    aux = oracle.aux_loss(r.probs, dp.counts_pre, w.top_k, w.aux_coef, r.real, r.entropy)
+    secs["aux"] = time.perf_counter() - t
+    return out, aux, r, secs
+
+
+def cpu_leg(w, inp, gpu: dict, sample_tokens: int):
+    """The CPU oracle beside the GPU: (cpu_baseline, parity).
+
+    cpu_baseline: the oracle as it stands, single-threaded (one BLAS thread), on the first
+    `sample_tokens` tokens of the workload, step by step; tokens/s of the sample.
+    parity: the oracle on the whole workload (all host threads), routed from its own fp32 logits;
+    the near-tie count (tokens whose k-th and (k+1)-th keys differ by less than 1e-4), the expert
+    ids against the GPU's, and the GPU output and aux values against the oracle's (normwise
+    output error against 2e-2 for bf16 and 1e-5 for fp32; aux relative error against 1e-5). When
+    any token's ids differ (a near tie resolved the other way), the oracle is run again routed
+    from the GPU's logits, so that the outputs compare the same routing."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+    host = host_cpu()
+    ntok = w.T if sample_tokens <= 0 else min(sample_tokens, w.T)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        _, _, _, secs = oracle_layer(w, inp, ntok)
+        dt = time.perf_counter() - t0
+    baseline = {"value": ntok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"first {ntok} of {w.T} tokens of {w.name} with all expert weights, capacity for "
+                          f"{ntok} tokens (oracle steps in float64, numpy/OpenBLAS on 1 thread); {dt:.2f} s",
+                "step_seconds": secs, **host}
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     t0 = time.perf_counter()
-    oracle.forward(x, inp["w_router"], w1, w2, k=w.top_k, storage=w.dtype, bias=inp["bias"],
-                   gumbel=g, tau=w.temperature, capacity=C, renormalize=w.renormalize, aux_coef=w.aux_coef,
-                   noise_in_logits=w.router_noise > 0.0, token_mask=m, w1_shared=inp["w1_shared"],
-                   w2_shared=inp["w2_shared"])
-    dt = time.perf_counter() - t0
-    return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {ntok} of {w.T} tokens of {w.name} with all expert weights "
-                      f"(oracle.forward, float64, numpy/OpenBLAS); {dt:.2f} s"}
+    out, aux, r, secs_full = oracle_layer(w, inp, w.T)
+    dt_full = time.perf_counter() - t0
+    baseline["whole_workload"] = {"seconds": dt_full, "threads": threads, "tokens_per_s": w.T / dt_full,
+                                  "step_seconds": secs_full}
+    real = r.real
+    gap = oracle.topk_gap(r.keys, w.top_k)
+    near = (gap < 1e-4) & real
+    gids = gpu["ids"].numpy()
+    differ = np.any(gids != r.ids, axis=1)
+    par = {"near_tie_tokens": int(near.sum()), "ids_differ_clear_gap": int(np.sum(differ & ~near)),
+           "ids_differ_near_tie": int(np.sum(differ & near)), "routing": "oracle's own logits"}
+    if differ.any():
+        out, aux, _, _ = oracle_layer(w, inp, w.T, logits=gpu["logits"].numpy())
+        par["routing"] = "the GPU's fp32 logits (ids differ on near ties)"
+    go = gpu["out"].float().numpy().astype(np.float64)
+    m = float(np.max(np.abs(out)))
+    err = float(np.max(np.abs(go - out)) / m) if m > 0 else float(np.max(np.abs(go)))
+    tol = 2e-2 if w.dtype == "bf16" else 1e-5
+    ga = gpu["aux"].numpy().astype(np.float64)
+    rel = [abs(a - b) / max(abs(b), 1e-30) if abs(a - b) > 1e-12 else 0.0 for a, b in zip(ga, aux)]
+    par.update(out_normwise_error=err, out_tol=tol, aux_rel_error=rel, aux_tol=1e-5, tokens_checked=w.T,
+               passed=bool(err <= tol and max(rel) <= 1e-5 and par["ids_differ_clear_gap"] == 0))
+    return baseline, par
 
 
 def bench_backward(args, w, cfg, dev, ws, N: int) -> dict:
@@ -213,29 +295,15 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # the timed steps: forward passes only (recording the per-kernel events costs a few
-    # microseconds per event on the GPU timeline, so they are not part of this region)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    # the same number of steps again with HIP events between the kernels: per-kernel durations
-    t2 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    t3 = time.perf_counter()
-    ms_per_step_events = (t3 - t2) * 1e3 / args.steps
-
-    # cold cache: before each of K more steps, a 1 GiB write evicts the L2s and the 256 MB Infinity
-    # Cache; HIP events on the launch stream bracket the step alone (the flush is outside them)
     cold_ms = None
     if not args.no_cold_cache:
+        # the timed steps, cold cache: before each step a 1 GiB write evicts the L2s and the
+        # 256 MB Infinity Cache, and HIP events on the launch stream bracket the step alone (the
+        # flush is outside them); exactly K steps between two device synchronisations
         flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
         for i in range(args.steps):
             flush.fill_(float(i))
             ev0[i].record()
@@ -244,6 +312,23 @@ def main():
         torch.cuda.synchronize()
         cold_ms = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)])
         del flush
+    # warm cache: K steps back to back between two device synchronisations (forward passes only:
+    # recording the per-kernel events costs a few microseconds per event on the GPU timeline)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    warm_ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # the same number of steps again with HIP events between the kernels: per-kernel durations
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    ms_per_step_events = (t3 - t2) * 1e3 / args.steps
+    ms_per_step = float(cold_ms.mean()) if cold_ms is not None else warm_ms_per_step
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -302,6 +387,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "timing": ("cold cache: mean of K steps, each after a 1 GiB write that evicts the L2s and the Infinity "
+                   "Cache, timed by HIP events on the launch stream around the step alone"
+                   if cold_ms is not None else "warm cache: K steps back to back between two synchronisations"),
         "ms_per_step_with_kernel_events": ms_per_step_events,
         "higher_is_better": True,
         "scaling": "weak",
@@ -325,9 +413,12 @@ def main():
         "dispatch_gbs": dispatch_bytes / t_disp / 1e9,
         "combine_gbs": combine_bytes / t_comb / 1e9,
         "cold_cache": None if cold_ms is None else {
-            "ms_median": float(np.median(cold_ms)), "ms_p10": float(np.percentile(cold_ms, 10)),
-            "ms_p90": float(np.percentile(cold_ms, 90)), "tokens_per_s_median": T / (float(np.median(cold_ms)) * 1e-3),
+            "ms_mean": float(cold_ms.mean()), "ms_median": float(np.median(cold_ms)),
+            "ms_p10": float(np.percentile(cold_ms, 10)), "ms_p90": float(np.percentile(cold_ms, 90)),
+            "tokens_per_s_median": T / (float(np.median(cold_ms)) * 1e-3),
             "protocol": "1 GiB buffer written before each step (outside the timed events)"},
+        "warm_cache": {"ms_per_step": warm_ms_per_step, "tokens_per_s": T / (warm_ms_per_step * 1e-3),
+                       "protocol": "K steps back to back between two device synchronisations"},
         "warm_cache_events": {"ms_median": float(np.median(warm_ms)), "ms_p10": float(np.percentile(warm_ms, 10)),
                               "ms_p90": float(np.percentile(warm_ms, 90)),
                               "note": "steps with the per-kernel events, caches warm from the previous step"},
@@ -338,7 +429,16 @@ def main():
     if not args.no_backward:
         line["backward"] = bench_backward(args, w, cfg, dev, ws, N)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_sample_tokens)
+        # one more forward with the routing captured (not timed), for the oracle's parity check
+        gids = torch.empty(w.T, w.top_k, dtype=torch.int32, device="cuda")
+        glog = torch.empty(w.T, w.num_experts, dtype=torch.float32, device="cuda")
+        moe.moe_forward(cfg, dev["x"], dev["w_router"], dev["w1"], dev["w2"], out, aux, ws, bias=dev["bias"],
+                        gumbel=dev["gumbel"], token_mask=dev["token_mask"], w1_shared=dev["w1_shared"],
+                        w2_shared=dev["w2_shared"], debug={"ids": gids, "logits": glog})
+        torch.cuda.synchronize()
+        gpu = {"ids": gids.cpu(), "logits": glog.cpu(), "out": out.cpu(), "aux": aux.cpu()}
+        line["cpu_baseline"], line["parity"] = cpu_leg(w, inp, gpu, args.cpu_sample_tokens)
+        line["near_tie_tokens"] = line["parity"]["near_tie_tokens"]
     print(json.dumps(line), flush=True)
 
 
