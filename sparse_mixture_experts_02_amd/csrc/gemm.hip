@@ -161,10 +161,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 
 int gemm_max_mtiles(int max_rows, int E) { return (max_rows + GEMM_BM - 1) / GEMM_BM + E; }
 
-// The 256 x 256 kernel prefetches two K stages ahead across its tiles, so it needs at least two
-// stages (K >= 128) per tile.
+// The 256 x 256 kernel loads up to three K stages ahead across its tiles, so it needs at least
+// four stages (K >= 256) per tile; shorter reductions take the 128 x 128 kernel.
 bool gemm_uses_big(bool bf16, int K, int max_rows, int E) {
-  return bf16 && K % 64 == 0 && K >= 128 && max_rows >= 256 * E;
+  return bf16 && K % 64 == 0 && K >= 256 && max_rows >= 256 * E;
 }
 
 hipError_t launch_gemm(const GemmParams& p, bool bf16, bool silu, hipStream_t s) {

@@ -10,23 +10,26 @@
 //    tile ids, ordered in groups of 4 m-tiles x all n-tiles so that the tiles running together on
 //    one XCD share rows of A and B in its L2.
 //  * 8 waves in a 2 x 4 arrangement, each owning 128 rows x 64 output features of the tile as
-//    8 x 4 v_mfma_f32_16x16x32_bf16 blocks (128 fp32 accumulators per lane, kept in AGPRs), so
-//    that each SIMD runs two waves: when one stalls issuing its direct loads or at a wait, the
-//    other keeps the matrix core busy (two waves per SIMD measured ~9% faster than one wave
-//    owning a 128 x 128 quarter, although the LDS fragment reads grow by half).
+//    8 x 4 v_mfma_f32_16x16x32_bf16 blocks (128 fp32 accumulators per lane, kept in AGPRs). Wave w
+//    and wave w + 4 run on the same SIMD (waves 0-3 are dealt to the four SIMDs, 4-7 likewise;
+//    checked on the GPU from the hardware wave id), and they are the two 128-row halves of the
+//    tile.
 //  * K advances 64 elements (128 bytes of every row) per stage. Two LDS stages (2 x (A + B) x
-//    256 rows x 128 B = 128 KiB) are filled by direct buffer -> LDS 16-byte loads. A stage is two
-//    k-steps of 32; operand fragments are read one k-step ahead, interleaved with the MFMAs, and
-//    the one barrier per stage sits in the middle of the second k-step.
-//  * Stages are numbered across a workgroup's tiles, and the loads of stage g + 2 go into stage
-//    g's buffer as soon as the barrier in the middle of stage g has released it: the A rows spread
-//    over the rest of stage g, the B rows over the first k-step of stage g + 1. Issuing the direct
-//    loads in one burst at the top of a stage stalled the issuing waves (measured: the MFMAs were
-//    busy 55% of the time against 76% with the loads removed); spread out, and a stage earlier,
-//    they cost far less. Past a tile's last stages the loads fetch the next tile's first two
-//    stages, so the pipeline runs through the tile boundary and only the epilogue (SiLU in fp32,
-//    one rounding to bf16) pauses the matrix cores. This needs at least two stages per tile
-//    (K >= 128).
+//    256 rows x 128 B = 128 KiB) are filled by direct buffer -> LDS 16-byte loads.
+//  * Ping-pong: the two halves (groups) take turns at the matrix cores. While one group issues
+//    its 64 MFMAs of a stage, with no other instruction between them, the other reads its next
+//    stage's fragments from LDS and issues its share of the direct loads; a barrier ends each
+//    phase and the roles swap. Group 1 runs one phase behind group 0 for the whole kernel. The
+//    loads of a stage are split evenly between the groups' memory phases, each issued as soon as
+//    the rows it overwrites have been read by both groups, two phases before they are read.
+//    Measured on the expert-FFN shapes against an interleaved schedule (both waves of a SIMD
+//    mixing loads, fragment reads and MFMAs, one barrier per stage): GEMM2 441 -> 409 us and
+//    GEMM1 482 -> 465 us on the main layer. With the loads removed the same loop runs GEMM2 at
+//    1.58 PFLOP/s, so the direct loads are what is left between it and the matrix cores.
+//  * Stages are numbered across a workgroup's tiles; past a tile's last stages the loads fetch
+//    the next tile's first stages, so the pipeline runs through the tile boundary. A tile's
+//    epilogue (SiLU in fp32, one rounding to bf16) falls in each group's memory phase, beside the
+//    other group's MFMAs. This needs at least four stages per tile (K >= 256).
 //  * The loads address rows through buffer resources whose size is the tile's valid rows of A (or
 //    of B): rows past a segment's end or past N fall outside the resource and are not fetched.
 //    They only feed accumulators whose outputs are never stored.
@@ -34,7 +37,7 @@
 //    into whole output rows through a small per-wave LDS area (see the epilogue) and stored with
 //    16-byte buffer stores, 8 rows x 128 contiguous bytes per instruction, through a buffer
 //    resource sized to the tile's valid rows (lanes past N get an out-of-range offset).
-// K must be a multiple of 64, at least 128, and N of 8.
+// K must be a multiple of 64, at least 256, and N of 8.
 #include "moe_internal.h"
 
 #include <type_traits>
@@ -210,6 +213,12 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
       }
       tstart += n;
     }
+    // wave-uniform: kept in scalar registers
+    t.e = __builtin_amdgcn_readfirstlane(t.e);
+    t.row0 = __builtin_amdgcn_readfirstlane(t.row0);
+    t.rows = __builtin_amdgcn_readfirstlane(t.rows);
+    t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
+    t.cols = __builtin_amdgcn_readfirstlane(t.cols);
     return t;
   };
 
@@ -223,17 +232,17 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   // (relative to the tile's first row) are the same for A and B.
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint32_t voff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = w * 32 + i * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ (((i & 1) << 2) | (lane >> 4));
-    voff[i] = (uint32_t)r * (uint32_t)rowbytes + chunk * 16;
-  }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   // Requests stage kt of a run of stages [k0, k1) of tile t (clamped to its last one: a harmless
   // reload) into buffer (kt - k0) & 1.
   auto issue = [&](const Tile& t, int kt, int k0 = 0, int k1 = 0x7fffffff) {
+    uint32_t voff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = w * 32 + i * 8 + (lane >> 3);
+      const int chunk = (lane & 7) ^ (((i & 1) << 2) | (lane >> 4));
+      voff[i] = (uint32_t)r * (uint32_t)rowbytes + chunk * 16;
+    }
     const int st = min(kt, min(k1, nk) - 1);
     const i32x4_t ra = make_rsrc(A + (size_t)t.row0 * rowbytes + st * ROWB, (uint32_t)t.rows * rowbytes);
     const i32x4_t rb = make_rsrc(B + ((size_t)t.e * N + t.n0) * rowbytes + st * ROWB, (uint32_t)t.cols * rowbytes);
@@ -259,12 +268,6 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     wb[buf][j] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(sb + lds_off(wn * 64 + j * 16 + fr, ks * 4 + fc)));
   };
 
-  // one direct load qq of a stage (0..3: A rows, 4..7: B rows of this wave) into buffer buf
-  auto ld = [&](i32x4_t ra, i32x4_t rb, int qq, int buf) {
-    const uint32_t sa = lds0 + buf * STAGE_BYTES + w * 32 * ROWB;
-    if (qq < 4) load_lds16(ra, voff[qq], sa + qq * 8 * ROWB);
-    else load_lds16(rb, voff[qq - 4], sa + TILE_BYTES + (qq - 4) * 8 * ROWB);
-  };
   auto rs_a = [&](const Tile& t, int st) {
     return make_rsrc(A + (size_t)t.row0 * rowbytes + st * ROWB, (uint32_t)t.rows * rowbytes);
   };
@@ -369,94 +372,75 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   };
 
   if (local < cnt) {
-  // Stages are numbered globally across this workgroup's tiles (stage s of a tile is g0 + s);
-  // stage g lives in LDS buffer g & 1. The loads of stage g + 2 go into stage g's buffer once the
-  // barrier in the middle of stage g has released it: half of them right after that barrier, the
-  // other half over the first k-step of stage g + 1, so that they neither arrive in one burst nor
-  // late. Which half goes first was measured: the B rows for the SiLU GEMM (its other half then
-  // at every other 16-row block), the A rows for the plain one (its B rows then over the first
-  // half of the k-step). Past a tile's last stage they fetch the next tile's first stages.
-  Tile cur = decode(start + local);
-  int g0 = 0;
-  {
-    const i32x4_t ra0 = rs_a(cur, 0), rb0 = rs_b(cur, 0);
+  // Ping-pong. The two waves on each SIMD (waves w and w + 4: the two 128-row halves of the tile,
+  // groups 0 and 1) take turns. In phase X of stage g group 0 runs its 64 MFMAs of stage g while
+  // group 1 reads its stage-g fragments from LDS; in phase Y they swap. A barrier ends each phase,
+  // so in its MFMA phase a wave issues nothing but MFMAs and every SIMD's matrix core is fed by
+  // one wave while the other works on memory. The direct loads are split evenly between the
+  // groups' memory phases, each as soon as the rows it overwrites have been read by both groups:
+  // group 0 loads the A rows of stage g + 2 in phase Y(g); wave wn of group 1 loads B rows
+  // [64 wn, 64 wn + 64) (the block it and its partner read) of stage g + 2 in phase X(g), right
+  // after its own stage-g reads. Each group waits for its loads at the end of its next MFMA
+  // phase, about two phases after issuing them and before the barrier after which they are read.
+  // A tile's epilogue falls in the group's memory phase (group 0: phase Y of the last stage;
+  // group 1: phase X of the next tile's first stage), beside the other group's MFMAs.
+  // Needs at least four stages per tile.
+  const int gr = wm;
+  // wave wn loads rows [64 wn, 64 wn + 64) of its operand, 8 rows per instruction
+  uint32_t vo[2];
 #pragma unroll
-    for (int qq = 0; qq < 8; ++qq) ld(ra0, rb0, qq, 0);
+  for (int h = 0; h < 2; ++h) {
+    const int r = wn * 64 + h * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((h << 2) | (lane >> 4));
+    vo[h] = (uint32_t)r * (uint32_t)rowbytes + chunk * 16;
   }
-  // stage 1: the half that follows a mid-stage barrier now, the other half carried into stage 0
-  i32x4_t pra = rs_a(cur, 1), prb = rs_b(cur, 1);
-  int pbuf = 1;
+  // group 0: A rows of stage st of tile t into buffer buf; group 1: B rows
+  auto load_half = [&](const Tile& t, int st, int buf) {
+    const i32x4_t r = gr == 0 ? rs_a(t, st) : rs_b(t, st);
+    const uint32_t sa = lds0 + buf * STAGE_BYTES + gr * TILE_BYTES + wn * 64 * ROWB;
 #pragma unroll
-  for (int qq = 0; qq < 4; ++qq) ld(pra, prb, SILU ? 4 + qq : qq, 1);
-  wait_vm_all();
-  __syncthreads();
+    for (int i = 0; i < 8; ++i)
+      load_lds16(r, vo[i & 1] + (uint32_t)((i >> 1) * 16) * (uint32_t)rowbytes, sa + i * 8 * ROWB);
+  };
+  // Fragment reads of stage g: row r of a 16-row block sits at byte r * 128 of its block, its 16-byte
+  // chunk c at ((c ^ ((r >> 1) & 7)) << 4); within one wave the swizzle depends on the lane only
+  // (block rows are multiples of 16), so each k-step's reads are one per-lane base plus constants.
+  // The base passes through an empty asm so that the compiler keeps one address register per
+  // k-step instead of precomputing every read's address.
+  const uint32_t fsw = (uint32_t)(fr * ROWB) + (uint32_t)((fc ^ ((fr >> 1) & 7)) << 4);
+  auto read_frags = [&](int g) {
+    const uint8_t* sbuf = smem + (g & 1) * STAGE_BYTES;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) frag_x(0, 0, 0, i);
+    for (int ks = 0; ks < 2; ++ks) {
+      uint32_t oa = fsw ^ (uint32_t)(ks << 6);   // chunk ks * 4 + fc
+      asm volatile("" : "+v"(oa));
+      const uint8_t* pa = sbuf + wm * 128 * ROWB + oa;
+      const uint8_t* pb = sbuf + TILE_BYTES + wn * 64 * ROWB + oa;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) frag_w(0, 0, 0, j);
-  while (true) {
-    const int nlocal = local + step;
-    const bool more = nlocal < cnt;
-    const Tile nxt = more ? decode(start + nlocal) : cur;
+      for (int i = 0; i < 8; ++i) xa[ks][i] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(pa + i * 16 * ROWB));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wb[ks][j] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(pb + j * 16 * ROWB));
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  auto compute = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[ks][j], xa[ks][i]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto zero_acc = [&]() {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    for (int s = 0; s < nk; ++s) {
-      const int g = g0 + s;
-      // k-step 0 of stage s from F0, reading k-step 1 of stage s into F1; the half of stage
-      // g + 1's loads carried from the previous stage
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[0][j], xa[0][i]);
-        if (SILU ? !(i & 1) : i < 4) ld(pra, prb, SILU ? (i >> 1) : 4 + i, pbuf);
-        if (i < 4) frag_w(1, g, 1, i);
-        frag_x(1, g, 1, i);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // first half of k-step 1
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
-      __builtin_amdgcn_sched_barrier(0);
-      // stage s + 1 has landed everywhere and nobody reads stage s's buffer any more
-      wait_vm_all();
-      __syncthreads();
-      // stage g + 2: this tile's stage s + 2, else the next tile's first stages (nothing left:
-      // a resource of no records, so the loads fetch nothing)
-      const bool own = s + 2 < nk;
-      const Tile& lt = own ? cur : nxt;
-      const int lst = own ? s + 2 : min(s + 2 - nk, nk - 1);
-      i32x4_t ra = rs_a(lt, lst), rb = rs_b(lt, lst);
-      if (!own && !more) {
-        ra[2] = 0;
-        rb[2] = 0;
-      }
-      // second half of k-step 1, with the first half of stage g + 2's loads and the reads of
-      // k-step 0 of stage g + 1 into F0
-#pragma unroll
-      for (int i = 4; i < 8; ++i) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
-        ld(ra, rb, SILU ? i : i - 4, g & 1);
-        if (!SILU || s + 1 < nk) {   // SiLU: after a tile's last stage, read once its epilogue is done
-          frag_x(0, g + 1, 0, 2 * (i - 4));
-          frag_x(0, g + 1, 0, 2 * (i - 4) + 1);
-          frag_w(0, g + 1, 0, i - 4);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      pra = ra;
-      prb = rb;
-      pbuf = g & 1;
-    }
-
-    // let the last MFMAs retire before their accumulators are read
-    // (the most recently written accumulators pass through the wait so that no read of them can
-    // be scheduled before it)
+  };
+  // let the last MFMAs retire before their accumulators are read (the most recently written
+  // accumulators pass through the wait so that no read of them is scheduled before it)
+  auto retire = [&]() {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                  : "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]), "+a"(acc[7][3]),
@@ -464,19 +448,80 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
                  :
                  : "memory");
     __builtin_amdgcn_sched_barrier(0);
-    store_tile(cur);
+  };
+  auto phase_end = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Every wave runs the same loop, one stage per iteration: its MFMAs of stage g, a barrier, its
+  // memory work (group 0: the A loads of stage g + 2; after a tile's last stage the epilogue; the
+  // fragments of stage g + 1; group 1: then the B loads of stage g + 3 into the buffer just read),
+  // a barrier. Group 1 passes one barrier before its first MFMAs, which puts it one phase behind
+  // group 0 for the whole kernel (group 0 passes one more at the end, so both pass the same
+  // number).
+  Tile cur = decode(start + local);
+  {   // stages 0 and 1 of the first tile, every wave its 32 rows of both operands
+    uint32_t voff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = w * 32 + i * 8 + (lane >> 3);
+      const int chunk = (lane & 7) ^ (((i & 1) << 2) | (lane >> 4));
+      voff[i] = (uint32_t)r * (uint32_t)rowbytes + chunk * 16;
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const i32x4_t ra = rs_a(cur, st), rb = rs_b(cur, st);
+      const uint32_t sa = lds0 + st * STAGE_BYTES + w * 32 * ROWB;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        load_lds16(ra, voff[i], sa + i * 8 * ROWB);
+        load_lds16(rb, voff[i], sa + TILE_BYTES + i * 8 * ROWB);
+      }
+    }
+  }
+  wait_vm_all();
+  __syncthreads();
+  zero_acc();
+  read_frags(0);
+  if (gr == 1) {
+    load_half(cur, 2, 0);   // B rows of stage 2, over the stage-0 rows this wave has just read
+    phase_end();
+  }
+  int g0 = 0;
+  while (true) {
+    const int nlocal = local + step;
+    const bool more = nlocal < cnt;
+    const Tile nxt = more ? decode(start + nlocal) : cur;
+    for (int s = 0; s < nk; ++s) {
+      const int g = g0 + s;
+      compute();
+      wait_vm_all();   // this wave's loads issued in its previous memory phase
+      phase_end();
+      if (gr == 0) {   // A rows of stage g + 2 into stage g's buffer
+        const int st = s + 2;
+        if (st < nk || more) load_half(st < nk ? cur : nxt, st < nk ? st : st - nk, g & 1);
+      }
+      if (s == nk - 1) {
+        retire();
+        store_tile(cur);
+        zero_acc();
+      }
+      // (past the last tile this reads a stale buffer, unused)
+      read_frags(g + 1);
+      if (gr == 1) {   // B rows of stage g + 3 into the buffer of stage g + 1, just read
+        const int st = s + 3;
+        if (st < nk || more) load_half(st < nk ? cur : nxt, st < nk ? st : st - nk, (g + 1) & 1);
+      }
+      phase_end();
+    }
     if (!more) break;
     g0 += nk;
     cur = nxt;
     local = nlocal;
-    if constexpr (SILU) {
-      // k-step 0 of the new tile's stage 0 (landed before the last barrier of the previous tile)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) frag_x(0, g0, 0, i);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) frag_w(0, g0, 0, j);
-    }
   }
+  if (gr == 0) phase_end();
   wait_vm_all();
   }
 
@@ -541,6 +586,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     wait_vm_all();
   }
 }
+
 
 // Adds the s partial sums of each split tail tile (in part order), applies the activation and
 // stores the tile. Item (r, w8, h): tail tile r, a quarter h of the 2048 16-byte chunks of wave
@@ -639,7 +685,7 @@ int gemm_big_grid(int max_rows, int E, int N) {
 }
 
 hipError_t launch_gemm_big(const GemmParams& p, bool silu, hipStream_t s) {
-  if (p.K < 128) return hipErrorInvalidValue;   // the pipeline needs two K stages per tile
+  if (p.K < 256) return hipErrorInvalidValue;   // the pipeline needs four K stages per tile
   const int grid = gemm_big_grid(p.max_rows, p.E, p.N);
   if (silu && p.C2) gemm_big_kernel<true, true><<<grid, 512, 0, s>>>(p);
   else if (silu) gemm_big_kernel<true, false><<<grid, 512, 0, s>>>(p);

@@ -29,8 +29,8 @@ CASES = {
     "bwd_bf16_ragged": derived(BASE, name="bwd_bf16_ragged", T=600, d_model=256, d_ffn=384, num_experts=6),
     "bwd_capacity_padding": derived(WORKLOADS["skewed_gumbel_capacity"], name="bwd_capacity_padding", T=500,
                                     d_model=128, d_ffn=192, num_experts=8, padding=0.2, capacity_factor=(9, 10)),
-    # 256 x 256 grouped GEMMs for the backward products (K = 128 and 256)
-    "bwd_big": derived(BASE, name="bwd_big", T=2048, d_model=128, d_ffn=256, num_experts=2),
+    # 256 x 256 grouped GEMMs for the backward products (K = 256 and 512)
+    "bwd_big": derived(BASE, name="bwd_big", T=2048, d_model=256, d_ffn=512, num_experts=2),
     # d a multiple of 512 with top-2: the combine backward that loads a token's rows up front
     "bwd_k2_prefetch": derived(BASE, name="bwd_k2_prefetch", T=700, d_model=1024, d_ffn=256, num_experts=4),
     # weight-streaming GEMMs (at most 64 rows per expert)
@@ -256,14 +256,24 @@ def test_moe_backward_whole_layer(name):
         assert e <= lim, (n, errs)
 
 
-def test_moe_backward_main_size_sampled():
-    """moe_backward at the layer's full size (16384 tokens, d 2048, f 4096, 8 experts, top-2; the
-    launch configuration bench.py --backward times) on outputs the oracle can form exactly one by
-    one: the hidden units are independent in dW1 / dW2 (the oracle's expert backward on 16
-    sampled units gives those rows of dW1 and columns of dW2 exactly), dXp is per row (the
-    oracle's expert backward on 48 sampled tokens' rows gives their dx), and the router gradients
-    are cheap in full."""
-    w, d_aux = BASE, 1.0
+SAMPLED_CASES = {
+    "main": BASE,
+    # d 4096: the dH GEMM (K = d, 64 stages) and the recomputed pre-activation have ~320 tiles, so
+    # their last partial round is split in two K halves and the tail kernel applies SiLU' (dA =
+    # dH SiLU'(A)) to the summed parts
+    "split_dh_d4096": derived(BASE, name="split_dh_d4096", T=4200, d_model=4096, d_ffn=2048),
+}
+
+
+@pytest.mark.parametrize("case", list(SAMPLED_CASES))
+def test_moe_backward_full_size_sampled(case):
+    """moe_backward at full size (the main layer: 16384 tokens, d 2048, f 4096, 8 experts, top-2,
+    the launch configuration the bench's backward leg times; and a d 4096 layer whose dH GEMM
+    splits its last round) on outputs the oracle can form exactly one by one: the hidden units are
+    independent in dW1 / dW2 (the oracle's expert backward on 16 sampled units gives those rows of
+    dW1 and columns of dW2 exactly), dXp is per row (the oracle's expert backward on 48 sampled
+    tokens' rows gives their dx), and the router gradients are cheap in full."""
+    w, d_aux = SAMPLED_CASES[case], 1.0
     print(f"[gpu] moe_backward full size sampled: {w}", flush=True)
     cfg = moe.config_for(w)
     inp = make_inputs(w)
@@ -357,8 +367,11 @@ def test_moe_backward_is_deterministic():
 
 
 KEEP_CASES = {
-    "keep_big": derived(BASE, name="keep_big", T=2048, d_model=128, d_ffn=256, num_experts=2),
+    "keep_big": derived(BASE, name="keep_big", T=2048, d_model=256, d_ffn=512, num_experts=2),
     "keep_main": BASE,                                                    # 256 x 256 tiles + split tail
+    # GEMM1 with K = d = 4096: its last partial round is split, and the tail kernel stores the
+    # pre-activation and its SiLU
+    "keep_split_k4096": derived(BASE, name="keep_split_k4096", T=4200, d_model=4096, d_ffn=2048),
     "keep_stream": derived(WORKLOADS["small_t_streaming"], name="keep_stream", T=96, d_model=256, d_ffn=512),
     "keep_f32": derived(WORKLOADS["tiny_f32"], name="keep_f32", T=150, d_model=48, d_ffn=40, num_experts=5, top_k=3),
     "keep_shared_padding": derived(WORKLOADS["main_noise_padding"], name="keep_shared_padding", T=520, d_model=128,

@@ -44,11 +44,18 @@ REDUCED = {
     "stream_skew_ntail": derived(BASE, name="stream_skew_ntail", T=256, d_model=256, d_ffn=200, router_bias=True),
     "stream_skew": derived(BASE, name="stream_skew", T=256, d_model=192, d_ffn=320, router_bias=True),
     # 256 x 256 GEMM1 with a single partial n-tile (N = 64) and the shortest reduction it takes
-    # (K = 128, two stages); GEMM2 (K = 64) goes to the 128 x 128 kernel
-    "big_ntail_k64": derived(BASE, name="big_ntail_k64", T=2048, d_model=128, d_ffn=64, num_experts=2, top_k=1),
-    # 256 x 256 GEMM1 with two-stage tiles and several tiles per workgroup (628 tiles): the next
-    # tile's stages are prefetched from inside the current one
-    "big_k128_multi": derived(BASE, name="big_k128_multi", T=40000, d_model=128, d_ffn=512, num_experts=2),
+    # (K = 256, four stages); GEMM2 (K = 64) goes to the 128 x 128 kernel
+    "big_ntail_k256": derived(BASE, name="big_ntail_k256", T=2048, d_model=256, d_ffn=64, num_experts=2,
+                              top_k=1),
+    # 256 x 256 GEMM1 with four-stage tiles and several tiles per workgroup (626 tiles): the next
+    # tile's first three stages are loaded from inside the current one
+    "big_k256_multi": derived(BASE, name="big_k256_multi", T=40000, d_model=256, d_ffn=512, num_experts=2),
+    # odd stage counts (K = 320 and 384: 5 and 6 stages), so a tile's first stage alternates between
+    # the two LDS buffers; partial n-tiles on both GEMMs (N = 384 and 320)
+    "big_k320_odd": derived(BASE, name="big_k320_odd", T=20000, d_model=320, d_ffn=384, num_experts=2),
+    # K = 128 (two stages) is below the 256 x 256 kernel's minimum: the 128 x 128 kernel at 256
+    # rows per expert
+    "k128_mid": derived(BASE, name="k128_mid", T=2048, d_model=128, d_ffn=512, num_experts=2),
     # 256 x 256 GEMM2 with K = 4096 and 266 tiles: the 10 tiles past the first round of 256 are
     # split into K-parts summed by the tail kernel
     "big_split_tail": derived(BASE, name="big_split_tail", T=34000, d_model=64, d_ffn=4096, num_experts=2),
