@@ -234,10 +234,13 @@ moe_status_t moe_aux_loss(const moe_config_t* cfg, const float* probs, const flo
  * device pointer receives the named tensor (shapes as in the calls above). When `events` is
  * non-NULL it holds n_events >= MOE_FORWARD_NUM_KERNELS + 1 created hipEvent_t; events[i] is
  * recorded on `stream` before kernel i and events[MOE_FORWARD_NUM_KERNELS] after the last, so
- * hipEventElapsedTime gives per-kernel times. Kernel order: route, dispatch-histogram,
- * dispatch-scan (with the capacity cut, and both aux losses and the entropy from the pre-cut
- * counts), dispatch-gather, gemm1 (W1 + SiLU), gemm2 (W2, with the reduction of its split tail
- * when it has one), shared expert (both of its GEMMs; empty without one), combine.
+ * hipEventElapsedTime gives per-kernel times. Kernel order: route (it also counts each token
+ * group's selections per expert), dispatch-histogram (empty: the router's counts are used),
+ * dispatch-scan (the capacity cut and the aux losses when the histogram is too large for every
+ * dispatch workgroup to sum it itself, else empty), dispatch (ranks, row map, gather; it also
+ * forms the capacity cut, the offsets and the aux losses when the scan step is empty), gemm1
+ * (W1 + SiLU), gemm2 (W2, with the reduction of its split tail when it has one), shared expert
+ * (both of its GEMMs; empty without one), combine.
  */
 #define MOE_FORWARD_NUM_KERNELS 8
 typedef struct {

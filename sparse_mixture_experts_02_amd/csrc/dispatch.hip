@@ -1,68 +1,43 @@
-// Dispatch kernels: per-expert histogram with stable in-block ranks, the cross-block scan with
-// the capacity cut, and the scatter of row indices fused with the row gather x -> Xp.
+// Dispatch kernels: per-block expert histograms, the scan of the block histograms with the
+// capacity cut, and the dispatch proper: stable ranks, the row map and the row gather x -> Xp.
 //
 // [P4 §2.4] sort the [T, k] expert index by expert id, count the tokens of each expert, split
 // them into per-expert segments and collect each expert's tokens with a table lookup.
 // [P3 §3.1, §3.4] cap the tokens one expert processes (capacity); the overflow is dropped.
 // Assignments are ranked in flattened (token, slot) order, so each expert keeps its first C
 // assignments in token order and its segment lists tokens in increasing order.
+//
+// Blocks are runs of bt consecutive tokens. blk_hist[b][e] counts the slots of block b that chose
+// expert e: in moe_forward the router writes it for its own token groups; moe_dispatch runs
+// hist_kernel. The pre-cut rank of a slot is (slots of its expert in earlier blocks) + (slots of
+// its expert earlier in its block); the dispatch workgroup of a block forms the first term from
+// the histograms and the second from the block's ids with wave ballots.
 #include "moe_internal.h"
+
+#include <type_traits>
 
 namespace moe {
 
 // ------------------------------------------------------------------------------ histogram
-// Block b ranks assignments [b*CHUNK, (b+1)*CHUNK) in order. Within a wave, the lanes that hold
-// the same expert are found with ballots (one ballot per distinct expert in the wave); the
-// rank of a lane is the number of such lanes below it. Wave counts are combined in LDS in wave
-// order, then chunk rounds in order, so rank_local is the stable rank inside the block.
-__device__ __forceinline__ void hist_block(const HistParams& p) {
-  __shared__ int wave_cnt[4][MOE_MAX_EXPERTS_DEV];
-  __shared__ int wave_base[4][MOE_MAX_EXPERTS_DEV];
-  __shared__ int running[MOE_MAX_EXPERTS_DEV];
+// One workgroup per block of bt tokens: counts per expert with LDS integer atomics (the counts do
+// not depend on their order). ids outside [0, E) (a padding token's -1) are not counted.
+__global__ __launch_bounds__(256) void hist_kernel(HistParams p) {
+  __shared__ int cnt[MOE_MAX_EXPERTS_DEV];
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int E = p.E;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-  if (tid < E) running[tid] = 0;
-  const int base = blockIdx.x * DISPATCH_CHUNK;
-  for (int round = 0; round < DISPATCH_CHUNK / 256; ++round) {
-    for (int i = tid; i < 4 * MOE_MAX_EXPERTS_DEV; i += 256) (&wave_cnt[0][0])[i] = 0;
-    __syncthreads();
-    const int i = base + round * 256 + tid;
-    int e = (i < p.TK) ? p.ids[i] : -1;
-    const bool ok = e >= 0 && e < E;   // out-of-range ids are left unranked (never written)
-    if (!ok) e = -1;
-    uint64_t todo = __ballot(ok);
-    int my_rank = 0;
-    while (todo) {
-      const int leader = __ffsll((unsigned long long)todo) - 1;
-      const int le = __shfl(e, leader);
-      const uint64_t peers = __ballot(ok && e == le);
-      if (ok && e == le) {
-        my_rank = __popcll(peers & lt_mask);
-        if (lane == leader) wave_cnt[w][e] = __popcll(peers);
-      }
-      todo &= ~peers;
+  if (tid < p.E) cnt[tid] = 0;
+  __syncthreads();
+  const int n = p.bt * p.k;
+  const size_t i0 = (size_t)blockIdx.x * n;
+  for (int i = tid; i < n; i += 256) {
+    const size_t gi = i0 + i;
+    if (gi < (size_t)p.TK) {
+      const int e = p.ids[gi];
+      if (e >= 0 && e < p.E) atomicAdd(&cnt[e], 1);
     }
-    __syncthreads();
-    if (tid < E) {
-      int run = running[tid];
-      for (int ww = 0; ww < 4; ++ww) {
-        wave_base[ww][tid] = run;
-        run += wave_cnt[ww][tid];
-      }
-      running[tid] = run;
-    }
-    __syncthreads();
-    if (ok) p.rank_local[i] = wave_base[w][e] + my_rank;
-    __syncthreads();
   }
   __syncthreads();
-  if (tid < E) p.blk_hist[(size_t)blockIdx.x * E + tid] = running[tid];
+  if (tid < p.E) p.blk_hist[(size_t)blockIdx.x * p.E + tid] = cnt[tid];
 }
-
-__global__ __launch_bounds__(256) void hist_kernel(HistParams p) { hist_block(p); }
 
 // ------------------------------------------------------------------------------ scan
 // One block. For each expert: exclusive scan of the block histograms (the pre-cut rank of
@@ -129,8 +104,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
 // The partial rows of expert e are split over the lanes (e, sub), sub = 0 .. nsub-1; each lane
 // keeps 4 independent running sums (so its loads overlap) and all sums are combined in a fixed
 // order, so the result does not depend on timing.
+template <int NT>
 __device__ __forceinline__ void aux_block(const AuxParams& p, const int* counts_pre) {
-  __shared__ double part[256];
+  __shared__ double part[NT];
   __shared__ double S[MOE_MAX_EXPERTS_DEV + 2];
   const int tid = threadIdx.x;
   const int E = p.E;
@@ -139,7 +115,7 @@ __device__ __forceinline__ void aux_block(const AuxParams& p, const int* counts_
   while (CPAD < C) CPAD <<= 1;
   const int c = tid % CPAD;
   const int sub = tid / CPAD;
-  const int nsub = 256 / CPAD;
+  const int nsub = NT / CPAD;
   double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
   if (c < C) {
     int q = sub;
@@ -181,7 +157,7 @@ __device__ __forceinline__ void aux_block(const AuxParams& p, const int* counts_
   }
 }
 
-__global__ __launch_bounds__(256) void aux_final_kernel(AuxParams p) { aux_block(p, p.counts_pre); }
+__global__ __launch_bounds__(256) void aux_final_kernel(AuxParams p) { aux_block<256>(p, p.counts_pre); }
 
 hipError_t launch_aux_final(const AuxParams& p, hipStream_t s) {
   aux_final_kernel<<<1, 256, 0, s>>>(p);
@@ -196,51 +172,197 @@ __global__ __launch_bounds__(256) void scan_aux_kernel(ScanAuxParams p) {
   __shared__ int pre[MOE_MAX_EXPERTS_DEV];
   scan_block(p.s, pre);
   __syncthreads();
-  aux_block(p.a, pre);
+  aux_block<256>(p.a, pre);
   if (p.shared_offsets && threadIdx.x < 2) p.shared_offsets[threadIdx.x] = threadIdx.x == 0 ? 0 : p.a.T;
 }
 
-// ------------------------------------------------------------------------------ gather
-// One wave per token. Lanes j < k resolve slot j: global pre-cut rank = block base + local
-// rank; kept iff rank < C; row = offsets[e] + rank. The wave then reads the token's row of x
-// once (16 B per lane per step) and writes it to each kept row of Xp.
-__global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= p.T) return;
-  const int k = p.k;
-  int row = -1;
-  if (lane < k) {
-    const int i = t * k + lane;
-    const int e = p.ids[i];
-    bool keep = false;
-    int rank = 0;
-    if (e >= 0 && e < p.E) {   // an id outside [0, E) (a padding token's -1) has no row
-      rank = p.blk_base[(size_t)(i / DISPATCH_CHUNK) * p.E + e] + p.rank_local[i];
-      keep = p.capacity < 0 || rank < p.capacity;
+// ------------------------------------------------------------------------------ dispatch
+// One workgroup of 16 waves per block of bt = 16 TB tokens (TB = 1, 2, 4).
+//  1. The block's ids into LDS. Without blk_base: the per-expert sums of the histograms over the
+//     earlier blocks (this block's base ranks) and over all blocks (the pre-cut counts), every
+//     workgroup on its own (the histograms are small and read from L2), then the kept counts
+//     min(count, C) and their exclusive scan (the segment offsets). One more workgroup (index nb)
+//     stores counts_pre, counts, offsets and n_dropped and finishes the aux losses, beside the
+//     others.
+//  2. Wave w takes tokens w + 16 i, i < TB: for each slot j the rank inside the block is the number
+//     of earlier slots of the block with the same expert (ballots over the ids in LDS), the pre-cut
+//     rank adds the block's base; kept iff rank < C; row = offset + rank. Lanes j < k write the row
+//     map. Then the wave copies its tokens' rows of x to their kept rows of Xp, the loads of all TB
+//     tokens in flight before their stores.
+template <bool FUSED, int TB>
+__global__ __launch_bounds__(1024) void dispatch_kernel(DispatchParams p) {
+  __shared__ int s_ids[DISPATCH_MAX_BT * MOE_MAX_TOP_K_DEV];
+  __shared__ int s_base[MOE_MAX_EXPERTS_DEV];
+  __shared__ int s_off[MOE_MAX_EXPERTS_DEV + 1];
+  __shared__ int s_tot[MOE_MAX_EXPERTS_DEV];
+  __shared__ int red[2][1024];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int E = p.E, k = p.k, b = blockIdx.x;
+  const bool stats = b == p.nb;   // the extra workgroup: counts, offsets, aux losses
+  const int t0 = b * p.bt;
+  const int nt = stats ? 0 : min(p.bt, p.T - t0);
+  for (int i = tid; i < nt * k; i += 1024) s_ids[i] = p.ids[(size_t)t0 * k + i];
+  if constexpr (FUSED) {
+    // thread (g, e): blocks g, g + G, ... of expert column e (consecutive threads read
+    // consecutive ints), four loads in flight
+    const int G = 1024 / E;
+    const int e = tid % E, g = tid / E;
+    int pre = 0, tot = 0;
+    if (g < G) {
+      int q = g;
+      for (; q + 3 * G < p.nb; q += 4 * G) {
+        const int v0 = p.blk_hist[(size_t)q * E + e];
+        const int v1 = p.blk_hist[(size_t)(q + G) * E + e];
+        const int v2 = p.blk_hist[(size_t)(q + 2 * G) * E + e];
+        const int v3 = p.blk_hist[(size_t)(q + 3 * G) * E + e];
+        tot += (v0 + v1) + (v2 + v3);
+        pre += (q < b ? v0 : 0) + (q + G < b ? v1 : 0) + (q + 2 * G < b ? v2 : 0) + (q + 3 * G < b ? v3 : 0);
+      }
+      for (; q < p.nb; q += G) {
+        const int v = p.blk_hist[(size_t)q * E + e];
+        tot += v;
+        pre += q < b ? v : 0;
+      }
     }
-    row = keep ? p.offsets[e] + rank : -1;
-    p.row_of[i] = row;
-    p.dropped[i] = (e >= 0 && e < p.E && !keep) ? 1 : 0;   // a -1 slot (padding) is not dropped
-    if (keep) p.perm_token[row] = t;
+    red[0][tid] = pre;
+    red[1][tid] = tot;
+    __syncthreads();
+    for (int ee = w; ee < E; ee += 16) {   // wave w: expert columns w, w + 16, ...
+      int a = 0, c = 0;
+      for (int gg = lane; gg < G; gg += 64) {
+        a += red[0][gg * E + ee];
+        c += red[1][gg * E + ee];
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        a += __shfl_xor(a, m);
+        c += __shfl_xor(c, m);
+      }
+      if (lane == 0) {
+        s_base[ee] = a;
+        s_tot[ee] = c;
+      }
+    }
+    __syncthreads();
+    if (w == 0) {   // kept counts and their exclusive scan over the experts (E <= 64: one wave)
+      const int cnt = lane < E ? s_tot[lane] : 0;
+      const int kept = (p.capacity < 0 || cnt < p.capacity) ? cnt : p.capacity;
+      int inc = kept;
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const int v = __shfl_up(inc, m);
+        if (lane >= m) inc += v;
+      }
+      if (lane < E) s_off[lane] = inc - kept;
+      if (stats) {
+        int drop = cnt - kept;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) drop += __shfl_xor(drop, m);
+        if (lane < E) {
+          p.counts_pre[lane] = cnt;
+          p.counts[lane] = kept;
+          p.offsets[lane] = inc - kept;
+        }
+        if (lane == E - 1) p.offsets[E] = inc;
+        if (lane == 0) *p.n_dropped = drop;
+        if (p.shared_offsets && lane < 2) p.shared_offsets[lane] = lane == 0 ? 0 : p.T;
+      }
+    }
+    if (stats) {
+      if (p.aux.aux) {
+        __syncthreads();
+        aux_block<1024>(p.aux, s_tot);
+      }
+      return;   // uniform within the workgroup
+    }
+  } else {
+    if (tid < E) {
+      s_base[tid] = p.blk_base[(size_t)b * E + tid];
+      s_off[tid] = p.offsets[tid];
+    }
   }
-  int rows[MOE_MAX_TOP_K_DEV];
-#pragma unroll
-  for (int j = 0; j < MOE_MAX_TOP_K_DEV; ++j) rows[j] = (j < k) ? __shfl(row, j) : -1;
+  __syncthreads();
+
+  // per-token steps, expanded at compile time for tokens i = 0 .. TB - 1 (constant indices keep the
+  // arrays below in registers)
+  auto each_token = [&](auto f) {
+    f(std::integral_constant<int, 0>{});
+    if constexpr (TB > 1) f(std::integral_constant<int, 1>{});
+    if constexpr (TB > 2) {
+      f(std::integral_constant<int, 2>{});
+      f(std::integral_constant<int, 3>{});
+    }
+  };
+  int myrow[TB];   // token i's slot-j row in lane j (-1: dropped or no row)
+  each_token([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const int tt = w + 16 * i;
+    int my_row = -1, my_drop = 0;
+    if (tt < nt) {   // uniform within the wave
+      for (int j = 0; j < k; ++j) {
+        const int pos = tt * k + j;
+        const int e = s_ids[pos];
+        const bool valid = e >= 0 && e < E;
+        int local = 0;
+        for (int q0 = 0; q0 < pos; q0 += 64) {
+          const int q = q0 + lane;
+          local += __popcll(__ballot(q < pos && s_ids[q] == e));
+        }
+        const int rank = (valid ? s_base[e] : 0) + local;
+        const bool keep = valid && (p.capacity < 0 || rank < p.capacity);
+        if (lane == j) {
+          my_row = keep ? s_off[e] + rank : -1;
+          my_drop = valid && !keep;
+        }
+      }
+      if (lane < k) {
+        const size_t idx = (size_t)(t0 + tt) * k + lane;
+        p.row_of[idx] = my_row;
+        p.dropped[idx] = (uint8_t)my_drop;
+        if (my_row >= 0) p.perm_token[my_row] = t0 + tt;
+      }
+    }
+    myrow[i] = my_row;
+  });
+  // (a native vector type: an array of HIP's uint4 structs is not kept in registers)
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   const int nvec = p.row_bytes / 16;
-  const uint4* __restrict__ src = (const uint4*)(p.x + (size_t)t * p.row_bytes);
-  for (int c = lane; c < nvec; c += 64) {
-    const uint4 v = src[c];
+  for (int c0 = 0; c0 < nvec; c0 += 256) {
+    u32x4 v[TB][4];
+    each_token([&](auto ic) {   // clamped token and column: every load is issued unconditionally
+      constexpr int i = decltype(ic)::value;
+      const u32x4* __restrict__ src = (const u32x4*)(p.x + (size_t)(t0 + min(w + 16 * i, nt - 1)) * p.row_bytes);
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOP_K_DEV; ++j)
-      if (rows[j] >= 0) ((uint4*)(p.xp + (size_t)rows[j] * p.row_bytes))[c] = v;
+      for (int u = 0; u < 4; ++u) v[i][u] = src[min(c0 + u * 64 + lane, nvec - 1)];
+    });
+    // every load has landed before the first store: without this the compiler, unable to count
+    // the conditional stores, waits for all earlier stores before each group of them
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt not waited
+    each_token([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if (w + 16 * i >= nt) return;   // uniform within the wave
+#pragma unroll
+      for (int j = 0; j < MOE_MAX_TOP_K_DEV; ++j) {   // unrolled: v stays in registers
+        if (j >= k) break;
+        const int r = __builtin_amdgcn_readlane(myrow[i], j);
+        if (r < 0) continue;
+        u32x4* __restrict__ dst = (u32x4*)(p.xp + (size_t)r * p.row_bytes);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + u * 64 + lane;
+          if (c < nvec) dst[c] = v[i][u];
+        }
+      }
+    });
   }
 }
 
-int dispatch_num_blocks(int TK) { return (TK + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK; }
+int dispatch_blocks(int T, int bt) { return (T + bt - 1) / bt; }
+
+bool dispatch_fused(int nb, int E) { return (long)nb * E <= DISPATCH_FUSED_MAX; }
 
 hipError_t launch_hist(const HistParams& p, hipStream_t s) {
-  hist_kernel<<<dispatch_num_blocks(p.TK), 256, 0, s>>>(p);
+  hist_kernel<<<dispatch_blocks(p.TK / p.k, p.bt), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -254,8 +376,20 @@ hipError_t launch_scan_aux(const ScanAuxParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const GatherParams& p, hipStream_t s) {
-  gather_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(p);
+template <int TB>
+static void launch_dispatch_tb(const DispatchParams& p, hipStream_t s) {
+  // fused: one more workgroup for the counts, offsets and aux losses
+  if (p.blk_base) dispatch_kernel<false, TB><<<p.nb, 1024, 0, s>>>(p);
+  else dispatch_kernel<true, TB><<<p.nb + 1, 1024, 0, s>>>(p);
+}
+
+hipError_t launch_dispatch(const DispatchParams& p, hipStream_t s) {
+  switch (p.bt) {   // the router's token groups (16, 32, 64) or moe_dispatch's blocks (64)
+    case 16: launch_dispatch_tb<1>(p, s); break;
+    case 32: launch_dispatch_tb<2>(p, s); break;
+    case 64: launch_dispatch_tb<4>(p, s); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -15,7 +15,7 @@ namespace {
 constexpr int kMaxDim = 32768;
 
 struct Layout {
-  size_t psum, blk_hist, blk_base, rank_local, probsum;
+  size_t psum, blk_hist, blk_base, probsum;
   size_t logits, ids, weights, counts_pre, counts, offsets, perm, row_of, dropped, ndrop;
   size_t xp, h, y;
   size_t hs, ys, sh_off;   // shared expert: Hs [T, fs], Ys [T, d], its segment offsets [2]
@@ -37,10 +37,12 @@ Layout layout(const moe_config_t& c) {
   const size_t T = (size_t)c.T, k = (size_t)c.top_k, E = (size_t)c.num_experts;
   const size_t d = (size_t)c.d_model, f = (size_t)c.d_ffn, TK = T * k, a = act_size(c);
   L.psum = take((size_t)route_max_parts(c.T, c.num_experts) * (E + 2) * sizeof(double));
-  const size_t nb = (size_t)dispatch_num_blocks((int)TK);
+  // histogram blocks: the router's token groups (moe_forward) or moe_dispatch's own blocks
+  const size_t nb_route = (size_t)dispatch_blocks(c.T, route_block_tokens(c.T, c.num_experts, c.act_dtype == MOE_BF16, false));
+  const size_t nb_own = (size_t)dispatch_blocks(c.T, DISPATCH_BLOCK_TOKENS);
+  const size_t nb = nb_route > nb_own ? nb_route : nb_own;
   L.blk_hist = take(nb * E * 4);
   L.blk_base = take(nb * E * 4);
-  L.rank_local = take(TK * 4);
   L.probsum = take((size_t)probsum_num_blocks(c.T) * (E + 2) * sizeof(double));
   L.logits = take(T * E * 4);
   L.ids = take(TK * 4);
@@ -152,7 +154,7 @@ moe_status_t forward_args_status(const moe_config_t* cfg, const void* x, const f
 moe_status_t run_route(const moe_config_t& c, const void* x, const float* w_router, const float* bias,
                        const float* noise, const uint8_t* token_mask, const float* logits_in,
                        float* logits_out, float* probs_out, int32_t* ids, float* weights, double* psum,
-                       hipStream_t s) {
+                       hipStream_t s, int32_t* blk_hist = nullptr) {
   RouteParams p{};
   p.T = c.T;
   p.d = c.d_model;
@@ -173,32 +175,17 @@ moe_status_t run_route(const moe_config_t& c, const void* x, const float* w_rout
   p.ids = ids;
   p.weights = weights;
   p.psum = psum;
+  p.blk_hist = blk_hist;
   MOE_LAUNCH(launch_route(p, c.act_dtype == MOE_BF16, s));
   return MOE_OK;
 }
 
-HistParams hist_params(const moe_config_t& c, const int32_t* ids, void* ws) {
-  const Layout L = layout(c);
-  HistParams p{};
-  p.TK = c.T * c.top_k;
-  p.E = c.num_experts;
-  p.ids = ids;
-  p.blk_hist = (int32_t*)at(ws, L.blk_hist);
-  p.rank_local = (int32_t*)at(ws, L.rank_local);
-  return p;
-}
-
-moe_status_t run_hist(const moe_config_t& c, const int32_t* ids, void* ws, hipStream_t s) {
-  MOE_LAUNCH(launch_hist(hist_params(c, ids, ws), s));
-  return MOE_OK;
-}
-
-ScanParams scan_params(const moe_config_t& c, int32_t* counts_pre, int32_t* counts, int32_t* offsets,
+ScanParams scan_params(const moe_config_t& c, int nb, int32_t* counts_pre, int32_t* counts, int32_t* offsets,
                        int32_t* n_dropped, void* ws) {
   const Layout L = layout(c);
   ScanParams p{};
   p.TK = c.T * c.top_k;
-  p.nb = dispatch_num_blocks(p.TK);
+  p.nb = nb;
   p.E = c.num_experts;
   p.capacity = capacity_of(c);
   p.blk_hist = (const int32_t*)at(ws, L.blk_hist);
@@ -210,32 +197,55 @@ ScanParams scan_params(const moe_config_t& c, int32_t* counts_pre, int32_t* coun
   return p;
 }
 
-moe_status_t run_scan(const moe_config_t& c, int32_t* counts_pre, int32_t* counts, int32_t* offsets,
-                      int32_t* n_dropped, void* ws, hipStream_t s) {
-  MOE_LAUNCH(launch_scan(scan_params(c, counts_pre, counts, offsets, n_dropped, ws), s));
-  return MOE_OK;
-}
-
-moe_status_t run_gather(const moe_config_t& c, const int32_t* ids, const void* x, const int32_t* offsets,
-                        int32_t* perm_token, int32_t* row_of, uint8_t* dropped, void* xp, void* ws,
-                        hipStream_t s) {
+// The dispatch of blocks of bt tokens whose histograms are in the workspace. When the histogram is
+// small every dispatch workgroup sums it itself (blk_base null; the aux losses, when `aux` is
+// given, and the shared expert's offsets come from its block 0); otherwise the one-workgroup scan
+// (with the aux losses) runs first. `scan_mark` records the timing event between the two.
+template <typename Mark>
+moe_status_t run_dispatch(const moe_config_t& c, int bt, const int32_t* ids, const void* x, int32_t* counts_pre,
+                          int32_t* counts, int32_t* offsets, int32_t* n_dropped, int32_t* perm_token, int32_t* row_of,
+                          uint8_t* dropped, void* xp, void* ws, const AuxParams* aux, int32_t* shared_offsets,
+                          Mark scan_mark, hipStream_t s) {
   const Layout L = layout(c);
-  GatherParams p{};
+  const int nb = dispatch_blocks(c.T, bt);
+  DispatchParams p{};
   p.T = c.T;
   p.k = c.top_k;
   p.E = c.num_experts;
   p.row_bytes = (int)(c.d_model * act_size(c));
   p.capacity = capacity_of(c);
+  p.bt = bt;
+  p.nb = nb;
   p.ids = ids;
-  p.blk_base = (const int32_t*)at(ws, L.blk_base);
-  p.rank_local = (const int32_t*)at(ws, L.rank_local);
+  p.blk_hist = (const int32_t*)at(ws, L.blk_hist);
+  p.counts_pre = counts_pre;
+  p.counts = counts;
   p.offsets = offsets;
+  p.n_dropped = n_dropped;
   p.x = (const uint8_t*)x;
   p.row_of = row_of;
   p.dropped = dropped;
   p.perm_token = perm_token;
   p.xp = (uint8_t*)xp;
-  MOE_LAUNCH(launch_gather(p, s));
+  if (dispatch_fused(nb, c.num_experts)) {
+    if (aux) p.aux = *aux;
+    p.shared_offsets = shared_offsets;
+    MOE_TRY(scan_mark());
+  } else {
+    const ScanParams sp = scan_params(c, nb, counts_pre, counts, offsets, n_dropped, ws);
+    if (aux) {
+      ScanAuxParams sa{};
+      sa.s = sp;
+      sa.a = *aux;
+      sa.shared_offsets = shared_offsets;
+      MOE_LAUNCH(launch_scan_aux(sa, s));
+    } else {
+      MOE_LAUNCH(launch_scan(sp, s));
+    }
+    MOE_TRY(scan_mark());
+    p.blk_base = (const int32_t*)at(ws, L.blk_base);
+  }
+  MOE_LAUNCH(launch_dispatch(p, s));
   return MOE_OK;
 }
 
@@ -449,9 +459,17 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* ids, const voi
     return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(x) || !aligned16(xp)) return MOE_ERR_INVALID_ARGUMENT;
   MOE_TRY(check_ws(cfg, ws, ws_bytes));
-  MOE_TRY(run_hist(*cfg, ids, ws, stream));
-  MOE_TRY(run_scan(*cfg, counts_pre, counts, offsets, n_dropped, ws, stream));
-  return run_gather(*cfg, ids, x, offsets, perm_token, row_of, dropped, xp, ws, stream);
+  const Layout L = layout(*cfg);
+  HistParams hp{};
+  hp.TK = cfg->T * cfg->top_k;
+  hp.E = cfg->num_experts;
+  hp.k = cfg->top_k;
+  hp.bt = DISPATCH_BLOCK_TOKENS;
+  hp.ids = ids;
+  hp.blk_hist = (int32_t*)at(ws, L.blk_hist);
+  MOE_LAUNCH(launch_hist(hp, stream));
+  return run_dispatch(*cfg, DISPATCH_BLOCK_TOKENS, ids, x, counts_pre, counts, offsets, n_dropped, perm_token,
+                      row_of, dropped, xp, ws, nullptr, nullptr, [] { return MOE_OK; }, stream);
 }
 
 moe_status_t moe_expert_ffn(const moe_config_t* cfg, const void* xp, const int32_t* offsets, const void* w1,
@@ -529,18 +547,16 @@ moe_status_t moe_forward(const moe_config_t* cfg, const void* x, const float* w_
     return hip_status(hipEventRecord(D.events[ev++], stream));
   };
   MOE_TRY(mark());
-  MOE_TRY(run_route(c, x, w_router, bias, noise, token_mask, nullptr, logits, probs, ids, weights, psum, stream));
+  // the router also counts each of its token groups' selections per expert (the dispatch histogram)
+  MOE_TRY(run_route(c, x, w_router, bias, noise, token_mask, nullptr, logits, probs, ids, weights, psum, stream,
+                    (int32_t*)at(ws, L.blk_hist)));
   MOE_TRY(mark());
-  MOE_TRY(run_hist(c, ids, ws, stream));
-  MOE_TRY(mark());
-  ScanAuxParams sp{};
-  sp.s = scan_params(c, counts_pre, counts, offsets, ndrop, ws);
-  sp.a = aux_params(c, psum, route_num_parts(c.T, c.num_experts, c.act_dtype == MOE_BF16, false), counts_pre, aux);
+  MOE_TRY(mark());   // no separate histogram step
+  const AuxParams ap =
+      aux_params(c, psum, route_num_parts(c.T, c.num_experts, c.act_dtype == MOE_BF16, false), counts_pre, aux);
   int32_t* sh_off = shared ? (int32_t*)at(ws, L.sh_off) : nullptr;
-  sp.shared_offsets = sh_off;
-  MOE_LAUNCH(launch_scan_aux(sp, stream));
-  MOE_TRY(mark());
-  MOE_TRY(run_gather(c, ids, x, offsets, perm, row_of, dropped, xp, ws, stream));
+  MOE_TRY(run_dispatch(c, route_block_tokens(c.T, c.num_experts, c.act_dtype == MOE_BF16, false), ids, x, counts_pre,
+                       counts, offsets, ndrop, perm, row_of, dropped, xp, ws, &ap, sh_off, mark, stream));
   MOE_TRY(mark());
   MOE_TRY(run_gemm(c, xp, w1, h, offsets, c.d_ffn, c.d_model, true, ws, stream, -1, -1,
                    c.keep_preact ? at(ws, L.a1) : nullptr));

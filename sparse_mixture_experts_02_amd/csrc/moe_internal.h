@@ -19,8 +19,13 @@ constexpr int MOE_MAX_TOP_K_DEV = 8;
 constexpr int ROUTE_TILE = 32;
 constexpr int ROUTE_MAX_WAVES = 2048;
 
-// Dispatch: assignments per histogram block.
-constexpr int DISPATCH_CHUNK = 512;
+// Dispatch: tokens per histogram block of moe_dispatch's own histogram kernel (moe_forward uses
+// the router's token groups, 16, 32 or 64 tokens), the most tokens a block may have, and the
+// largest histogram (blocks x experts) that every dispatch workgroup sums itself (beyond it a
+// one-workgroup scan kernel forms the block prefixes first).
+constexpr int DISPATCH_BLOCK_TOKENS = 64;
+constexpr int DISPATCH_MAX_BT = 64;
+constexpr int DISPATCH_FUSED_MAX = 16384;
 
 // Grouped GEMM tile (rows of the permuted activations x output columns).
 constexpr int GEMM_BM = 128;
@@ -69,13 +74,13 @@ struct RouteParams {
   int32_t* ids;             // [T, k]
   float* weights;           // [T, k]
   double* psum;             // [route_num_parts][E + 2] per-workgroup statistics, or null
+  int32_t* blk_hist;        // [route_blocks][E] selections per expert of each token group, or null
 };
 
 struct HistParams {
-  int TK, E;                // TK = T * k assignments
+  int TK, E, k, bt;         // TK = T * k assignments; bt tokens per block
   const int32_t* ids;       // [TK]
   int32_t* blk_hist;        // [nb][E]
-  int32_t* rank_local;      // [TK]
 };
 
 struct ScanParams {
@@ -88,17 +93,36 @@ struct ScanParams {
   int32_t* n_dropped;       // [1]
 };
 
-struct GatherParams {
+struct AuxParams {
+  int T, E, k, nparts;
+  float coef;
+  float tau;
+  const double* psum;       // [nparts][E + 2]: probability sums, entropy sum, real-token count
+  const int32_t* counts_pre;
+  float* aux;               // [3]
+};
+
+// The dispatch proper: one workgroup per block of bt tokens ranks its slots and gathers its rows.
+// With blk_base null it also sums the block histograms itself (block prefix and totals), and
+// block 0 writes counts_pre, counts, offsets, n_dropped (and, with aux.aux set, the aux losses and
+// shared_offsets); otherwise blk_base and offsets come from the scan kernel.
+struct DispatchParams {
   int T, k, E, row_bytes, capacity;
-  const int32_t* ids;
-  const int32_t* blk_base;
-  const int32_t* rank_local;
-  const int32_t* offsets;
+  int bt, nb;               // tokens per block, blocks
+  const int32_t* ids;       // [T, k]
+  const int32_t* blk_hist;  // [nb][E]
+  const int32_t* blk_base;  // [nb][E] pre-cut rank of each block's first slot per expert, or null
+  int32_t* counts_pre;      // [E]
+  int32_t* counts;          // [E]
+  int32_t* offsets;         // [E+1]
+  int32_t* n_dropped;       // [1]
   const uint8_t* x;
   int32_t* row_of;
   uint8_t* dropped;
   int32_t* perm_token;
   uint8_t* xp;
+  AuxParams aux;            // aux.aux null: no aux losses
+  int32_t* shared_offsets;  // [2] set to {0, T}, or null
 };
 
 struct GemmParams {
@@ -141,15 +165,6 @@ struct CombineBwdParams {
   float* dweights;          // [T, k]: <dOut[t], Y[row]>, 0 for slots without a row
 };
 
-struct AuxParams {
-  int T, E, k, nparts;
-  float coef;
-  float tau;
-  const double* psum;       // [nparts][E + 2]: probability sums, entropy sum, real-token count
-  const int32_t* counts_pre;
-  float* aux;               // [3]
-};
-
 struct ScanAuxParams {
   ScanParams s;
   AuxParams a;              // a.counts_pre is not read: the scan's own pre-cut counts are used
@@ -173,11 +188,14 @@ int route_num_parts(int T, int E, bool bf16, bool logits_in);   // rows of psum 
 int route_max_parts(int T, int E);
 hipError_t launch_route(const RouteParams& p, bool bf16, hipStream_t s);
 
-int dispatch_num_blocks(int TK);
+// token groups of the router's histogram (blocks of moe_forward's dispatch) and their count
+int route_block_tokens(int T, int E, bool bf16, bool logits_in);
+int dispatch_blocks(int T, int bt);
+bool dispatch_fused(int nb, int E);
 hipError_t launch_hist(const HistParams& p, hipStream_t s);
 hipError_t launch_scan(const ScanParams& p, hipStream_t s);
 hipError_t launch_scan_aux(const ScanAuxParams& p, hipStream_t s);
-hipError_t launch_gather(const GatherParams& p, hipStream_t s);
+hipError_t launch_dispatch(const DispatchParams& p, hipStream_t s);
 
 int gemm_max_mtiles(int max_rows, int E);
 hipError_t launch_gemm(const GemmParams& p, bool bf16, bool silu, hipStream_t s);

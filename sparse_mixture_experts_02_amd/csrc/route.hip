@@ -55,10 +55,11 @@ struct RouteStats {
 // tokens t16 + 4*(l/16) + r, r = 0..3, for expert et*16 + l%16. Adds the bias (and the additive
 // noise in that mode), forms the keys, selects the top-k, computes the gate weights,
 // probabilities and entropy, writes the outputs and adds the statistics of real tokens to st.
-// Padding tokens (token_mask 0) are not routed: ids -1, weights 0, probabilities 0.
+// Padding tokens (token_mask 0) are not routed: ids -1, weights 0, probabilities 0. cnt[et] counts
+// the lane's selections (expert et * 16 + l % 16 over its 4 tokens), for the dispatch histogram.
 template <int ET>
 __device__ __forceinline__ void finish_tile(const RouteParams& p, f32x4_t (&acc)[ET], int t16, bool add_bias,
-                                            RouteStats<ET>& st) {
+                                            RouteStats<ET>& st, int (&cnt)[ET]) {
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
@@ -111,6 +112,8 @@ __device__ __forceinline__ void finish_tile(const RouteParams& p, f32x4_t (&acc)
           slot[et] = j;
         }
     }
+#pragma unroll
+    for (int et = 0; et < ET; ++et) cnt[et] += slot[et] >= 0 ? 1 : 0;
     // full softmax of logits / tau (probs, aux sums, entropy, unnormalised weights) and the
     // softmax restricted to the selected experts (normalised weights). Exponents are formed as
     // (L - max) / tau, subtracting before scaling.
@@ -198,6 +201,17 @@ __device__ __forceinline__ void store_psum(const RouteParams& p, RouteStats<ET>&
   }
 }
 
+// Sums a wave's selection counts over its 4 row groups: lane l < 16 then holds the count of expert
+// et * 16 + l in cnt[et].
+template <int ET>
+__device__ __forceinline__ void reduce_counts(int (&cnt)[ET]) {
+#pragma unroll
+  for (int et = 0; et < ET; ++et) {
+    cnt[et] += __shfl_xor(cnt[et], 16);
+    cnt[et] += __shfl_xor(cnt[et], 32);
+  }
+}
+
 // ------------------------------------------------------------------------------ generic kernel
 
 template <int ET>
@@ -249,8 +263,19 @@ __global__ __launch_bounds__(64) void route_kernel(RouteParams p) {
         }
       }
     }
-    finish_tile<ET>(p, acc[0], t0, !p.logits_in, st);
-    finish_tile<ET>(p, acc[1], t0 + 16, !p.logits_in, st);
+    int cnt[ET];
+#pragma unroll
+    for (int et = 0; et < ET; ++et) cnt[et] = 0;
+    finish_tile<ET>(p, acc[0], t0, !p.logits_in, st, cnt);
+    finish_tile<ET>(p, acc[1], t0 + 16, !p.logits_in, st, cnt);
+    if (p.blk_hist) {   // the tile is one block of the dispatch histogram
+      reduce_counts<ET>(cnt);
+#pragma unroll
+      for (int et = 0; et < ET; ++et) {
+        const int e = et * 16 + lane;
+        if (lane < 16 && e < E) p.blk_hist[(size_t)tile * E + e] = cnt[et];
+      }
+    }
   }
   store_psum<ET>(p, st, blockIdx.x);
 }
@@ -296,6 +321,7 @@ __global__ __launch_bounds__(512) void route_ksplit_kernel(RouteParams p) {
   constexpr int NB = (ET * (MT + 2) <= 6) ? 4 : ((ET * (MT + 2) <= 12) ? 2 : 1);   // k-steps per load batch
   __shared__ f32x4_t red[KS_WAVES][MT][ET][64];
   __shared__ double wsum[MT][ET * 16 + 2];
+  __shared__ int hc[MT][ET * 16];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = p.T, d = p.d, E = p.E;
@@ -387,9 +413,28 @@ __global__ __launch_bounds__(512) void route_ksplit_kernel(RouteParams p) {
           for (int r = 0; r < 4; ++r) s[et][r] = __fadd_rn(s[et][r], v[r]);
         }
       }
-      finish_tile<ET>(p, s, t0 + 16 * w, true, st);
+      int cnt[ET];
+#pragma unroll
+      for (int et = 0; et < ET; ++et) cnt[et] = 0;
+      finish_tile<ET>(p, s, t0 + 16 * w, true, st, cnt);
+      if (p.blk_hist) {
+        reduce_counts<ET>(cnt);
+#pragma unroll
+        for (int et = 0; et < ET; ++et)
+          if (lane < 16) hc[w][et * 16 + lane] = cnt[et];
+      }
     }
     __syncthreads();   // red is rewritten by the next group
+    // the group is one block of the dispatch histogram: its MT tiles' counts (hc is rewritten
+    // only after the next group's first barrier, which wave 0 passes after these reads)
+    if (p.blk_hist && w == 0) {
+      for (int e = lane; e < E; e += 64) {
+        int v = 0;
+#pragma unroll
+        for (int q = 0; q < MT; ++q) v += hc[q][e];
+        p.blk_hist[(size_t)grp * E + e] = v;
+      }
+    }
   }
   if (p.psum) {
     if (w < MT) {
@@ -452,6 +497,10 @@ static int ksplit_blocks(int T, int E) {
 static int generic_blocks(int T) {
   const int n = (T + ROUTE_TILE - 1) / ROUTE_TILE;
   return n < ROUTE_MAX_WAVES ? n : ROUTE_MAX_WAVES;
+}
+
+int route_block_tokens(int T, int E, bool bf16, bool logits_in) {
+  return use_ksplit(bf16, logits_in) ? 16 * ksplit_mt(T, E) : ROUTE_TILE;
 }
 
 int route_num_parts(int T, int E, bool bf16, bool logits_in) {
