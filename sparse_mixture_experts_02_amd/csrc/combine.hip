@@ -96,6 +96,10 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 // first use, so a wave keeps all of its row reads in flight at once. Y rows are read once, with the
 // non-temporal hint (measured: 3-5% faster; the same hint on the output stores was slower). Same
 // arithmetic and order as the general kernel (fp32 FMA in slot order, one rounding).
+// The loads are unconditional (a slot without a row reads row 0 and its terms are replaced by 0
+// with a select, never multiplied: the row may hold anything), followed by one explicit wait, so
+// that the compiler places no wait between the column steps' stores (a wait there would also
+// wait for the previous step's store).
 __global__ __launch_bounds__(256) void combine_k2_kernel(CombineParams p) {
   constexpr int MAXU = 8;
   const int lane = threadIdx.x & 63;
@@ -111,20 +115,22 @@ __global__ __launch_bounds__(256) void combine_k2_kernel(CombineParams p) {
   }
   const int r0 = __shfl(my_row, 0), r1 = k > 1 ? __shfl(my_row, 1) : -1;
   const float w0 = __shfl(my_w, 0), w1 = k > 1 ? __shfl(my_w, 1) : 0.0f;
+  const bool h0 = r0 >= 0, h1 = r1 >= 0;
   const int nu = d >> 9;   // column steps of 512
-  const u32x4_t* y0 = (const u32x4_t*)((const uint16_t*)p.y + (size_t)(r0 < 0 ? 0 : r0) * d) + lane;
-  const u32x4_t* y1 = (const u32x4_t*)((const uint16_t*)p.y + (size_t)(r1 < 0 ? 0 : r1) * d) + lane;
+  const u32x4_t* y0 = (const u32x4_t*)((const uint16_t*)p.y + (size_t)(h0 ? r0 : 0) * d) + lane;
+  const u32x4_t* y1 = (const u32x4_t*)((const uint16_t*)p.y + (size_t)(h1 ? r1 : 0) * d) + lane;
   const bool sh = p.y_shared != nullptr;
   const u32x4_t* ys = (const u32x4_t*)((const uint16_t*)(sh ? p.y_shared : p.y) + (size_t)(sh ? t : 0) * d) + lane;
   u32x4_t a[MAXU], b[MAXU], c[MAXU];
 #pragma unroll
   for (int u = 0; u < MAXU; ++u) {
-    if (u < nu) {
-      a[u] = r0 >= 0 ? __builtin_nontemporal_load(y0 + u * 64) : u32x4_t{0u, 0u, 0u, 0u};
-      b[u] = r1 >= 0 ? __builtin_nontemporal_load(y1 + u * 64) : u32x4_t{0u, 0u, 0u, 0u};
-      c[u] = sh ? __builtin_nontemporal_load(ys + u * 64) : u32x4_t{0u, 0u, 0u, 0u};
+    if (u < nu) {   // uniform
+      a[u] = __builtin_nontemporal_load(y0 + u * 64);
+      b[u] = __builtin_nontemporal_load(y1 + u * 64);
+      if (sh) c[u] = __builtin_nontemporal_load(ys + u * 64);   // uniform (a kernel argument)
     }
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): every row has landed
   u32x4_t* out = (u32x4_t*)((uint16_t*)p.out + (size_t)t * d) + lane;
 #pragma unroll
   for (int u = 0; u < MAXU; ++u) {
@@ -132,16 +138,14 @@ __global__ __launch_bounds__(256) void combine_k2_kernel(CombineParams p) {
       float acc[8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        acc[2 * q] = 0.0f;
-        acc[2 * q + 1] = 0.0f;
-        if (r0 >= 0) {
-          acc[2 * q] = fmaf(w0, bf16_bits_to_f32(a[u][q] & 0xFFFFu), acc[2 * q]);
-          acc[2 * q + 1] = fmaf(w0, bf16_bits_to_f32(a[u][q] >> 16), acc[2 * q + 1]);
-        }
-        if (r1 >= 0) {
-          acc[2 * q] = fmaf(w1, bf16_bits_to_f32(b[u][q] & 0xFFFFu), acc[2 * q]);
-          acc[2 * q + 1] = fmaf(w1, bf16_bits_to_f32(b[u][q] >> 16), acc[2 * q + 1]);
-        }
+        const float x0 = fmaf(w0, bf16_bits_to_f32(a[u][q] & 0xFFFFu), 0.0f);
+        const float x1 = fmaf(w0, bf16_bits_to_f32(a[u][q] >> 16), 0.0f);
+        acc[2 * q] = h0 ? x0 : 0.0f;
+        acc[2 * q + 1] = h0 ? x1 : 0.0f;
+        const float y0v = fmaf(w1, bf16_bits_to_f32(b[u][q] & 0xFFFFu), acc[2 * q]);
+        const float y1v = fmaf(w1, bf16_bits_to_f32(b[u][q] >> 16), acc[2 * q + 1]);
+        acc[2 * q] = h1 ? y0v : acc[2 * q];
+        acc[2 * q + 1] = h1 ? y1v : acc[2 * q + 1];
         if (sh) {   // the shared expert's output, weight 1, after the routed slots
           acc[2 * q] = __fadd_rn(acc[2 * q], bf16_bits_to_f32(c[u][q] & 0xFFFFu));
           acc[2 * q + 1] = __fadd_rn(acc[2 * q + 1], bf16_bits_to_f32(c[u][q] >> 16));

@@ -35,6 +35,8 @@ CASES = {
     "bwd_k2_prefetch": derived(BASE, name="bwd_k2_prefetch", T=700, d_model=1024, d_ffn=256, num_experts=4),
     # weight-streaming GEMMs (at most 64 rows per expert)
     "bwd_stream": derived(WORKLOADS["small_t_streaming"], name="bwd_stream", T=96, d_model=256, d_ffn=512),
+    # one round of 32 tiles with 16 stages per tile for the dH GEMM (K = d = 1024)
+    "bwd_split_single": derived(BASE, name="bwd_split_single", T=2048, d_model=1024, d_ffn=512, num_experts=2),
 }
 
 
@@ -372,6 +374,8 @@ KEEP_CASES = {
     # GEMM1 with K = d = 4096: its last partial round is split, and the tail kernel stores the
     # pre-activation and its SiLU
     "keep_split_k4096": derived(BASE, name="keep_split_k4096", T=4200, d_model=4096, d_ffn=2048),
+    # one round of 32 tiles with 16 stages per tile, pre-activation kept
+    "keep_split_single": derived(BASE, name="keep_split_single", T=2048, d_model=1024, d_ffn=512, num_experts=2),
     "keep_stream": derived(WORKLOADS["small_t_streaming"], name="keep_stream", T=96, d_model=256, d_ffn=512),
     "keep_f32": derived(WORKLOADS["tiny_f32"], name="keep_f32", T=150, d_model=48, d_ffn=40, num_experts=5, top_k=3),
     "keep_shared_padding": derived(WORKLOADS["main_noise_padding"], name="keep_shared_padding", T=520, d_model=128,

@@ -53,6 +53,8 @@ REDUCED = {
     # odd stage counts (K = 320 and 384: 5 and 6 stages), so a tile's first stage alternates between
     # the two LDS buffers; partial n-tiles on both GEMMs (N = 384 and 320)
     "big_k320_odd": derived(BASE, name="big_k320_odd", T=20000, d_model=320, d_ffn=384, num_experts=2),
+    # one round of 32 tiles with 16 stages per tile (GEMM2: K = 512)
+    "split_single_round": derived(BASE, name="split_single_round", T=2048, d_model=1024, d_ffn=512, num_experts=2),
     # K = 128 (two stages) is below the 256 x 256 kernel's minimum: the 128 x 128 kernel at 256
     # rows per expert
     "k128_mid": derived(BASE, name="k128_mid", T=2048, d_model=128, d_ffn=512, num_experts=2),
