@@ -339,6 +339,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # the cost of an event interval with no kernel in it (two records back to back on the launch
+    # stream): every per-kernel interval carries it, which matters for the short kernels
+    gap_ev = moe.HipEvents(2 * args.steps)
+    for i in range(args.steps):
+        gap_ev.record(2 * i)
+        gap_ev.record(2 * i + 1)
+    torch.cuda.synchronize()
+    event_gap_ms = float(np.median([gap_ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps)]))
+    gap_ev.close()
+
     per_kernel = np.zeros((args.steps, MOE_FORWARD_NUM_KERNELS))
     warm_ms = np.zeros(args.steps)
     for i, ev in enumerate(events):
@@ -346,7 +356,8 @@ def main():
             per_kernel[i, j] = ev.elapsed_ms(j, j + 1)
         warm_ms[i] = ev.elapsed_ms(0, MOE_FORWARD_NUM_KERNELS)
         ev.close()
-    kms = per_kernel.mean(axis=0)
+    kms_raw = per_kernel.mean(axis=0)
+    kms = np.maximum(kms_raw - event_gap_ms, 0.0)   # net of the event interval's own cost
     N = int(offsets[-1].item())
     n_dropped = int(nd.item())
 
@@ -408,6 +419,11 @@ def main():
         "gemm_frac_of_peak": gemm_tflops / peak,
         "shared_ffn_tflops": shared_tflops,
         "kernel_ms": {n: float(v) for n, v in zip(names, kms)},
+        "kernel_ms_event_intervals": {n: float(v) for n, v in zip(names, kms_raw)},
+        "event_gap_ms": event_gap_ms,
+        "kernel_ms_note": ("kernel_ms = mean HIP-event interval around each kernel step on the launch stream, less "
+                           "event_gap_ms (the median interval between two events recorded back to back); the GB/s "
+                           "and the roofline use these net times"),
         "route_gbs": (T * d * a + w.num_experts * d * 4 + T * w.num_experts * 4 * (2 if w.gumbel else 1)
                       + 8 * T * w.top_k) / (kms[names.index("route")] * 1e-3) / 1e9,
         "dispatch_gbs": dispatch_bytes / t_disp / 1e9,

@@ -43,6 +43,9 @@ REDUCED = {
     # and a partial last block of output features (N = 200 and 320 are not multiples of 64)
     "stream_skew_ntail": derived(BASE, name="stream_skew_ntail", T=256, d_model=256, d_ffn=200, router_bias=True),
     "stream_skew": derived(BASE, name="stream_skew", T=256, d_model=192, d_ffn=320, router_bias=True),
+    # weight streaming over 64 experts with an N that is not a multiple of 64 (GEMM1: N = 576)
+    "stream_e64_ntail": derived(WORKLOADS["small_t_streaming"], name="stream_e64_ntail", T=300,
+                                     d_model=256, d_ffn=576, num_experts=64, capacity_factor=None),
     # 256 x 256 GEMM1 with a single partial n-tile (N = 64) and the shortest reduction it takes
     # (K = 256, four stages); GEMM2 (K = 64) goes to the 128 x 128 kernel
     "big_ntail_k256": derived(BASE, name="big_ntail_k256", T=2048, d_model=256, d_ffn=64, num_experts=2,
