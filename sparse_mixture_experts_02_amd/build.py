@@ -3,7 +3,8 @@
     python -m sparse_mixture_experts_02_amd.build
 
 Every source under csrc/ is compiled to an object in _build/ (in parallel), then linked into
-sparse_mixture_experts_02_amd/libmoe.so. Always rebuilds.
+sparse_mixture_experts_02_amd/libmoe.so. Always rebuilds. (build_sanitized.py builds the same
+sources with host-side sanitizers for the CPU tests of the C ABI.)
 """
 from __future__ import annotations
 

@@ -3,6 +3,7 @@
 #include "../../include/moe.h"
 
 #include <math.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -135,6 +136,17 @@ moe_status_t check_ws(const moe_config_t* cfg, const void* ws, size_t ws_bytes) 
 uint8_t* at(void* ws, size_t off) { return (uint8_t*)ws + off; }
 
 int capacity_of(const moe_config_t& c) { return c.capacity < 0 ? -1 : c.capacity; }
+
+// The integer a caller stored in an enum-typed field or argument. A C caller may store any int
+// there, and in C++ loading a value outside the enumerators' range through the enum type is
+// undefined, so values not yet validated are read as their bytes.
+template <typename En>
+int enum_int(const En& v) {
+  static_assert(sizeof(En) == sizeof(int), "C enums are int-sized");
+  int i;
+  memcpy(&i, &v, sizeof i);
+  return i;
+}
 
 // The configuration and the required pointers of a whole-layer forward (host only).
 moe_status_t forward_args_status(const moe_config_t* cfg, const void* x, const float* w_router, const void* w1,
@@ -370,7 +382,7 @@ moe_status_t expert_ffn_bwd(const moe_config_t& c, const BwdLayout& L, const voi
 extern "C" {
 
 const char* moe_status_string(moe_status_t status) {
-  switch (status) {
+  switch (enum_int(status)) {
     case MOE_OK: return "ok";
     case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
     case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
@@ -396,18 +408,18 @@ moe_status_t moe_validate_config(const moe_config_t* c) {
   if (c->keep_preact != 0 && c->keep_preact != 1) return MOE_ERR_INVALID_ARGUMENT;
   if (c->d_ffn_shared < 0 || c->d_ffn_shared > kMaxDim || c->d_ffn_shared % 8) return MOE_ERR_INVALID_ARGUMENT;
   if (!isfinite(c->aux_coef)) return MOE_ERR_INVALID_ARGUMENT;
-  const bool dt_ok = (c->act_dtype == MOE_F32 || c->act_dtype == MOE_BF16) &&
-                     (c->weight_dtype == MOE_F32 || c->weight_dtype == MOE_BF16 || c->weight_dtype == MOE_INT4);
+  const int act = enum_int(c->act_dtype), wt = enum_int(c->weight_dtype);
+  const bool dt_ok = (act == MOE_F32 || act == MOE_BF16) && (wt == MOE_F32 || wt == MOE_BF16 || wt == MOE_INT4);
   if (!dt_ok) return MOE_ERR_INVALID_ARGUMENT;
-  if (c->weight_dtype == MOE_INT4) {
+  if (wt == MOE_INT4) {
     // 4-bit weights: bf16 activations, whole groups of four 128-column stages, the
     // weight-streaming regime (at most 64 rows per expert on average), no shared expert
-    const bool ok = c->act_dtype == MOE_BF16 && c->d_model % 512 == 0 && c->d_ffn % 512 == 0 &&
+    const bool ok = act == MOE_BF16 && c->d_model % 512 == 0 && c->d_ffn % 512 == 0 &&
                     (long long)c->T * c->top_k <= 64LL * c->num_experts && c->d_ffn_shared == 0 &&
                     c->keep_preact == 0;
     return ok ? MOE_OK : MOE_ERR_UNSUPPORTED;
   }
-  if (c->act_dtype != c->weight_dtype) return MOE_ERR_UNSUPPORTED;
+  if (act != wt) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
