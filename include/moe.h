@@ -22,8 +22,11 @@
  *  - Errors: every call returns a moe_status_t. Arguments are validated on the host before any
  *    launch; on a validation error nothing is launched. A failed kernel launch returns
  *    MOE_ERR_HIP. Inputs must be finite; results for NaN/Inf inputs are unspecified.
- *  - Determinism: no floating-point atomics; two calls with the same inputs give bitwise equal
- *    outputs.
+ *  - Determinism: two calls with the same inputs give bitwise equal outputs. Floating-point
+ *    atomics appear in one place only: the backward's weight gradients, when there are fewer
+ *    output tiles than CUs, add the two halves of a tile's reduction into a zeroed output with
+ *    fp32 atomic adds; 0 + a is exact and a + b commutes, so the bits do not depend on which half
+ *    lands first.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
