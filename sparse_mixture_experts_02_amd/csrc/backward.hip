@@ -247,7 +247,7 @@ namespace moe {
 // Weight gradients of the grouped GEMMs: for every expert e,
 //   G[e][m][n] = sum over the expert's rows r of P[r][m] * Q[r][n]     (fp32 result)
 // a product whose reduction runs over the expert's segment of the permuted rows (dW2 = dY^T H,
-// dW1 = dA^T Xp). fp32: one output per thread, fp32 FMA in row order. bf16 (grad_w_bf16_kernel):
+// dW1 = dA^T Xp). bf16 (grad_w_bf16_kernel):
 //  * one 128 x 128 output tile of one expert per workgroup; 4 waves in 2 x 2, each 64 x 64 =
 //    4 x 4 blocks of v_mfma_f32_16x16x32_bf16. Tiles are numbered so that each XCD takes a
 //    contiguous range (the same expert), walked in groups of 8 m-tiles: the tiles in flight on
@@ -395,20 +395,107 @@ __global__ __launch_bounds__(512, 1) void grad_w_bf16_kernel(GradWParams p) {
     }
 }
 
+// fp32: one 128 x 128 output tile of one expert per workgroup; 4 waves in 2 x 2, each 64 x 64 =
+// 4 x 4 blocks of v_mfma_f32_16x16x4_f32 (exact fp32 products, fp32 sums). The reduction runs
+// in stages of 16 rows: P and Q are row-major in r, which is already the operand order of this
+// MFMA (a lane takes one element of one row), so each stage is copied row for row into LDS
+// ([r][m] and [r][n], pitch 144 floats: the 4 rows a wave reads at once fall in different
+// banks) and the next stage is fetched into registers while the current one is multiplied.
+// Rows past the segment's end and columns past M or N read as zeros.
+constexpr int GF_TILE = 128, GF_BK = 16, GF_PITCH = GF_TILE + 16;
+
 __global__ __launch_bounds__(256) void grad_w_f32_kernel(GradWParams p) {
-  const int e = blockIdx.y;
+  __shared__ __attribute__((aligned(16))) float lds[2][2][GF_BK * GF_PITCH];
+  const int tilesM = (p.M + GF_TILE - 1) / GF_TILE, tilesN = (p.N + GF_TILE - 1) / GF_TILE;
+  const int per_e = tilesM * tilesN;
+  const int e = blockIdx.x / per_e, rem = blockIdx.x - e * per_e;
+  const int m0 = (rem % tilesM) * GF_TILE, n0 = (rem / tilesM) * GF_TILE;
   int r0 = p.offsets[e], r1 = p.offsets[e + 1];
   r0 = r0 < 0 ? 0 : (r0 > p.max_rows ? p.max_rows : r0);
   r1 = r1 < r0 ? r0 : (r1 > p.max_rows ? p.max_rows : r1);
-  const float* __restrict__ P = (const float*)p.P;
-  const float* __restrict__ Q = (const float*)p.Q;
-  const size_t MN = (size_t)p.M * p.N;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < MN; i += (size_t)gridDim.x * blockDim.x) {
-    const int m = (int)(i / p.N), n = (int)(i % p.N);
-    float s = 0.0f;
-    for (int r = r0; r < r1; ++r) s = fmaf(P[(size_t)r * p.M + m], Q[(size_t)r * p.N + n], s);
-    p.G[(size_t)e * MN + i] = s;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int fr = lane & 15, fg = lane >> 4;
+  // loader: thread t moves the 16-byte pieces t and t + 256 of each operand's stage (16 rows x
+  // 128 columns = 32 pieces per row), through a buffer resource covering the stage's valid rows
+  int lrow[2], lcol[2];
+  uint32_t voffP[2], voffQ[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int idx = tid + 256 * h;
+    lrow[h] = idx >> 5;
+    lcol[h] = 4 * (idx & 31);
+    voffP[h] = m0 + lcol[h] < p.M ? (uint32_t)(lrow[h] * p.M + m0 + lcol[h]) * 4u : 0x80000000u;
+    voffQ[h] = n0 + lcol[h] < p.N ? (uint32_t)(lrow[h] * p.N + n0 + lcol[h]) * 4u : 0x80000000u;
   }
+  const float* const P = (const float*)p.P;
+  const float* const Q = (const float*)p.Q;
+  f32x4_t vp[2], vq[2];
+  auto load = [&](int r) {
+    const int nrows = r < r1 ? min(GF_BK, r1 - r) : 0;
+    const int rb = r < r1 ? r : r0;
+    const __amdgpu_buffer_rsrc_t rp =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(P + (size_t)rb * p.M), 0, nrows * p.M * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rq =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Q + (size_t)rb * p.N), 0, nrows * p.N * 4, 0x00020000);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      vp[h] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, (int)voffP[h], 0, 0));
+      vq[h] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)voffQ[h], 0, 0));
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      *(f32x4_t*)&lds[buf][0][lrow[h] * GF_PITCH + lcol[h]] = vp[h];
+      *(f32x4_t*)&lds[buf][1][lrow[h] * GF_PITCH + lcol[h]] = vq[h];
+    }
+  };
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int wm = w >> 1, wn = w & 1;
+  const int ns = (r1 - r0 + GF_BK - 1) / GF_BK;
+  if (ns > 0) {
+    load(r0);
+    store(0);
+    __syncthreads();
+  }
+  for (int s = 0; s < ns; ++s) {
+    load(r0 + (s + 1) * GF_BK);   // past the last stage: an empty resource, zeros
+    const float* A = &lds[s & 1][0][0];
+    const float* B = &lds[s & 1][1][0];
+#pragma unroll
+    for (int kk = 0; kk < GF_BK / 4; ++kk) {
+      float af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        af[i] = A[(4 * kk + fg) * GF_PITCH + 64 * wm + 16 * i + fr];
+        bfr[i] = B[(4 * kk + fg) * GF_PITCH + 64 * wn + 16 * i + fr];
+      }
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+    }
+    store((s + 1) & 1);
+    __syncthreads();
+  }
+  // lane holds rows m0 + 64 wm + 16 mi + 4 fg .. + 3 of column n0 + 64 wn + 16 ni + fr
+  float* __restrict__ G = p.G + (size_t)e * p.M * p.N;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int n = n0 + 64 * wn + 16 * ni + fr;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int m = m0 + 64 * wm + 16 * mi + 4 * fg + t;
+        if (m < p.M && n < p.N) G[(size_t)m * p.N + n] = acc[mi][ni][t];
+      }
+    }
 }
 
 __global__ __launch_bounds__(256) void zero_f32_kernel(float* x, size_t n) {
@@ -430,10 +517,9 @@ hipError_t launch_grad_w(const GradWParams& p_in, bool bf16, hipStream_t s) {
     }
     grad_w_bf16_kernel<<<tiles * p.splits, 512, 0, s>>>(p);
   } else {
-    size_t blocks = ((size_t)p.M * p.N + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    dim3 grid((unsigned)blocks, p.E);
-    grad_w_f32_kernel<<<grid, 256, 0, s>>>(p);
+    const int tiles = ((p.M + GF_TILE - 1) / GF_TILE) * ((p.N + GF_TILE - 1) / GF_TILE) * p.E;
+    if (tiles == 0) return hipSuccess;
+    grad_w_f32_kernel<<<tiles, 256, 0, s>>>(p);
   }
   return hipGetLastError();
 }

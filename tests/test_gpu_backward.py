@@ -26,6 +26,10 @@ BASE = WORKLOADS["main_bf16"]
 
 CASES = {
     "bwd_f32": derived(WORKLOADS["tiny_f32"], name="bwd_f32", T=200, d_model=48, d_ffn=40, num_experts=5, top_k=3),
+    # fp32 weight gradients over several 128 x 128 tiles (ragged in both M and N) and many
+    # 16-row stages with a ragged last one
+    "bwd_f32_tiles": derived(WORKLOADS["tiny_f32"], name="bwd_f32_tiles", T=900, d_model=136, d_ffn=264,
+                             num_experts=3, top_k=2),
     "bwd_bf16_ragged": derived(BASE, name="bwd_bf16_ragged", T=600, d_model=256, d_ffn=384, num_experts=6),
     "bwd_capacity_padding": derived(WORKLOADS["skewed_gumbel_capacity"], name="bwd_capacity_padding", T=500,
                                     d_model=128, d_ffn=192, num_experts=8, padding=0.2, capacity_factor=(9, 10)),
