@@ -47,14 +47,24 @@ __device__ __forceinline__ float q4_silu(float v) {
   return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// 8 signed nibbles (nibble i = k offset i) times the scale, as one bf16x8 MFMA operand.
+// 8 signed nibbles (nibble i = k offset i) times the scale s, as one bf16x8 MFMA operand. Each
+// nibble's sign bit is flipped so that the nibbles read as u = q + 8 in [0, 15]; the even and odd
+// nibbles are spread into bytes and converted by the byte-to-float conversions; then
+// fma(u, s, -8 s) = q s exactly (u s and 8 s are exact in fp32, and so is their difference,
+// which has at most 12 significant bits), and the bf16 conversion rounds once.
 __device__ __forceinline__ bf16x8_t q4_dequant(uint32_t word, float s) {
+  const uint32_t u = word ^ 0x88888888u;
+  uint32_t ev = u & 0x0F0F0F0Fu, od = (u >> 4) & 0x0F0F0F0Fu;
+  // opaque to the optimiser, which would otherwise fold the masks into one bit-field extract per
+  // nibble and lose the per-byte conversions
+  asm("" : "+v"(ev));
+  asm("" : "+v"(od));
+  const float ms = -8.0f * s;
   uint32_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    // signed extract: the builtin's result type follows its first operand, so that must be int
-    const float a = (float)(int)__builtin_amdgcn_sbfe((int)word, 8 * i, 4) * s;
-    const float b = (float)(int)__builtin_amdgcn_sbfe((int)word, 8 * i + 4, 4) * s;
+    const float a = __builtin_fmaf((float)((ev >> (8 * i)) & 0xFFu), s, ms);
+    const float b = __builtin_fmaf((float)((od >> (8 * i)) & 0xFFu), s, ms);
     o[i] = pack_bf16x2(a, b);
   }
   return __builtin_bit_cast(bf16x8_t, uint4{o[0], o[1], o[2], o[3]});
