@@ -138,6 +138,51 @@ __device__ __forceinline__ int tail_parts(int total, int G, int nk) {
   return s;
 }
 
+// Narrow tiles for the partial last round of reductions under 64 stages, where splitting K does
+// not repay its partial sums: when at most 64 tiles are left over after whole rounds of the 256
+// workgroups, each is cut along N into s = 4 or 8 slices of 256 / s output features (s R <= 256),
+// which the workgroups compute at full K after their whole tiles, so that s R workgroups share the
+// last round instead of R and nothing is added up afterwards. A slice loads all 256 rows of A for
+// 1 / s of the tile's products, so halves (s = 2, R up to 128) cost more than they save: measured
+// on the main expert-FFN layer (80 tiles left over) the last round took longer as 160 halves
+// than as 80 whole tiles. Returns s (1: no narrow tail).
+__device__ __forceinline__ int narrow_parts(int total, int G, int nk) {
+  const int R = total % G;
+  if (nk >= 64 || G != MAX_WGS || R == 0 || 4 * R > G) return 1;
+  return 8 * R <= G ? 8 : 4;
+}
+
+// Tile id -> (expert, rows, output features): ids run over groups of GROUP_M m-tiles x all NT
+// n-tiles, the m-tiles of all experts numbered consecutively from the (clamped) segment bounds.
+// The fields are wave-uniform and kept in scalar registers.
+__device__ __forceinline__ Tile decode_tile(int id, int MT, int NT, int N, int E, const int* seg) {
+  const int group = id / (GROUP_M * NT);
+  const int first_m = group * GROUP_M;
+  const int gm = min(GROUP_M, MT - first_m);
+  const int in_group = id - group * GROUP_M * NT;
+  const int mt = first_m + in_group % gm;
+  const int nt = in_group / gm;
+  Tile t{0, 0, 0, nt * BIG_BN, min(N - nt * BIG_BN, BIG_BN)};
+  int tstart = 0;
+  for (int ee = 0; ee < E; ++ee) {
+    const int lo = seg[ee], hi = seg[ee + 1];
+    const int n = (hi - lo + BIG_BM - 1) / BIG_BM;
+    if (mt < tstart + n) {
+      t.e = ee;
+      t.row0 = lo + (mt - tstart) * BIG_BM;
+      t.rows = min(hi - t.row0, BIG_BM);
+      break;
+    }
+    tstart += n;
+  }
+  t.e = __builtin_amdgcn_readfirstlane(t.e);
+  t.row0 = __builtin_amdgcn_readfirstlane(t.row0);
+  t.rows = __builtin_amdgcn_readfirstlane(t.rows);
+  t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
+  t.cols = __builtin_amdgcn_readfirstlane(t.cols);
+  return t;
+}
+
 // One 16-byte store of fp32 partial sums straight from the accumulator registers; the block's
 // offset goes in the scalar offset. Includes the wait states a store of more than 64 bits needs
 // before its data registers may be overwritten (the compiler does not see inside the asm).
@@ -147,12 +192,119 @@ __device__ __forceinline__ void store_part(i32x4_t rsrc, uint32_t voff, uint32_t
 }
 }  // namespace
 
+// A narrow-tail slice (see narrow_parts): 256 rows x BN (64 or 32) output features of tile t from
+// feature n0 (bcols valid) at full K, by the 8 waves of the workgroup after its whole tiles, in
+// the whole-tile kernel's LDS: a 3-stage ring (A: 256 rows, B: 64 rows, 128 bytes of each per
+// stage, swizzled as the whole tiles) filled by direct buffer -> LDS loads two stages ahead, one
+// barrier per stage. Wave w owns rows [32 w, 32 w + 32) x all BN features as 2 x BN / 16 MFMA
+// blocks with the weight fragment first. Epilogue per lane (4 consecutive features of one row):
+// MODE 0 the accumulator, 1 its SiLU, 2 also the pre-activation to C2 first, 3 times SiLU'(C2);
+// one rounding.
+constexpr int NR_STAGES = 3;
+constexpr int NR_BROWS = 64;                                   // B rows staged (the widest slice)
+constexpr int NR_STAGE_BYTES = TILE_BYTES + NR_BROWS * ROWB;   // 40 KiB
+constexpr int NR_LPS = 5;   // load instructions per wave and stage: 4 of A, 1 of B
+
+template <int MODE, int BN>
+__device__ __forceinline__ void narrow_slice(const GemmParams& p, uint8_t* smem, const Tile& t, int n0, int bcols) {
+  constexpr int NJ = BN / 16;   // 16-feature blocks per wave
+  const int N = p.N, rowbytes = p.K * 2, nk = p.K / 64;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int fr = lane & 15, fc = lane >> 4;
+  const uint8_t* __restrict__ A = (const uint8_t*)p.A + (size_t)t.row0 * rowbytes;
+  const uint8_t* __restrict__ B = (const uint8_t*)p.B + ((size_t)t.e * N + n0) * rowbytes;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  // wave w loads A rows 32 w + 8 i + lane / 8 (i < 4) and B rows 8 w + lane / 8 (B rows at or past
+  // bcols are outside the resource: zeros, nothing fetched); lane l fills slot l % 8 of its row
+  // with the chunk the swizzle puts there
+  uint32_t va[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = w * 32 + i * 8 + (lane >> 3);
+    va[i] = (uint32_t)r * (uint32_t)rowbytes + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+  }
+  const int rbw = w * 8 + (lane >> 3);
+  const uint32_t vb = (uint32_t)rbw * (uint32_t)rowbytes + (((lane & 7) ^ ((rbw >> 1) & 7)) << 4);
+  auto issue = [&](int st) {
+    const int slot = st % NR_STAGES;
+    st = min(st, nk - 1);   // past the end: a harmless reload, so every stage issues NR_LPS loads
+    const i32x4_t ra = make_rsrc(A + st * ROWB, (uint32_t)t.rows * rowbytes);
+    const i32x4_t rb = make_rsrc(B + st * ROWB, (uint32_t)bcols * rowbytes);
+    const uint32_t base = lds0 + slot * NR_STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load_lds16(ra, va[i], base + (w * 32 + i * 8) * ROWB);
+    load_lds16(rb, vb, base + TILE_BYTES + w * 8 * ROWB);
+  };
+  f32x4_t acc[2][NJ];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  issue(0);
+  issue(1);
+  for (int s = 0; s < nk; ++s) {
+    // this wave's loads of stage s have landed (those of stage s + 1 may still be in flight);
+    // after the barrier every wave's have, and the slot of stage s + 2 was last read in stage s - 1
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NR_LPS) : "memory");
+    __syncthreads();
+    issue(s + 2);
+    const uint8_t* sa = smem + (s % NR_STAGES) * NR_STAGE_BYTES;
+    const uint8_t* sb = sa + TILE_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8_t xa[2], wb[NJ];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        xa[i] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(sa + lds_off(w * 32 + 16 * i + fr, ks * 4 + fc)));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        wb[j] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(sb + lds_off(16 * j + fr, ks * 4 + fc)));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[j], xa[i], acc[i][j], 0, 0, 0);
+    }
+  }
+  wait_vm_all();   // the clamped reloads of the last two iterations
+  // lane holds features 4 fc .. + 3 of row fr of each 16 x 16 block
+  uint16_t* __restrict__ C = (uint16_t*)p.C;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = w * 32 + 16 * i + fr;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int n = 16 * j + 4 * fc;
+      if (r >= t.rows || n >= bcols) continue;
+      const size_t o = (size_t)(t.row0 + r) * N + n0 + n;
+      float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      if constexpr (MODE == 3) {   // dA = dH SiLU'(A), A = p.C2 at the same place
+        const uint2 a = *(const uint2*)((const uint16_t*)p.C2 + o);
+        v[0] *= dsilu_fast(bf16_bits_to_f32(a.x & 0xFFFFu));
+        v[1] *= dsilu_fast(bf16_bits_to_f32(a.x >> 16));
+        v[2] *= dsilu_fast(bf16_bits_to_f32(a.y & 0xFFFFu));
+        v[3] *= dsilu_fast(bf16_bits_to_f32(a.y >> 16));
+      }
+      if constexpr (MODE == 2) {   // the pre-activation, rounded once
+        *(uint2*)((uint16_t*)p.C2 + o) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
+      if constexpr (MODE == 1 || MODE == 2) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = silu_fast(v[u]);
+      }
+      *(uint2*)(C + o) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
+  }
+}
+
 template <bool SILU, bool PRE>
 __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
+  // the two operand stages and the per-wave epilogue areas; the narrow tail reuses all of it as a
+  // 3-stage ring (3 x 48 KiB)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES + 8 * EPI_BYTES];
+  uint8_t* const epi = smem + 2 * STAGE_BYTES;
 
   __shared__ int seg[MOE_MAX_EXPERTS_DEV + 1];
-  __shared__ __attribute__((aligned(16))) uint8_t epi[8 * EPI_BYTES];
 
   const int tid = threadIdx.x;
   const int E = p.E, N = p.N;
@@ -180,10 +332,13 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   // stride of their count. With a split tail (partial-sum workspace given, G == 256) the whole
   // tiles are the first `full` (a multiple of G, so every workgroup gets the same number), and
   // then workgroup v (XCD-major: the parts of one tile share an XCD) computes part v % s of tail
-  // tile v / s into partial slot v; a second kernel adds the parts and stores the tile.
+  // tile v / s into partial slot v; a second kernel adds the parts and stores the tile. With a
+  // narrow tail the whole tiles are the first `full` as well, and then workgroup v computes slice
+  // v % s of tail tile v / s (narrow_slice).
   const int G = gridDim.x, xcd = blockIdx.x & 7;
   const int sparts = (p.sk_part != nullptr && G == MAX_WGS) ? tail_parts(total, G, nk) : 1;
-  const int full = sparts > 1 ? total - total % G : total;
+  const int nparts = narrow_parts(total, G, nk);
+  const int full = (sparts > 1 || nparts > 1) ? total - total % G : total;
   const int q = full >> 3, rem = full & 7;
   const int cnt = (xcd < rem) ? q + 1 : q;
   const int start = (xcd < rem) ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q;
@@ -191,36 +346,10 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   int local = blockIdx.x >> 3;
   const int vsplit = xcd * (G >> 3) + local;
   const bool has_split = sparts > 1 && vsplit < (total - full) * sparts;
-  if (local >= cnt && !has_split) return;
+  const bool has_narrow = nparts > 1 && vsplit < (total - full) * nparts;
+  if (local >= cnt && !has_split && !has_narrow) return;
 
-  auto decode = [&](int id) {
-    const int group = id / (GROUP_M * NT);
-    const int first_m = group * GROUP_M;
-    const int gm = min(GROUP_M, MT - first_m);
-    const int in_group = id - group * GROUP_M * NT;
-    const int mt = first_m + in_group % gm;
-    const int nt = in_group / gm;
-    Tile t{0, 0, 0, nt * BIG_BN, min(N - nt * BIG_BN, BIG_BN)};
-    int tstart = 0;
-    for (int ee = 0; ee < E; ++ee) {
-      const int lo = seg[ee], hi = seg[ee + 1];
-      const int n = (hi - lo + BIG_BM - 1) / BIG_BM;
-      if (mt < tstart + n) {
-        t.e = ee;
-        t.row0 = lo + (mt - tstart) * BIG_BM;
-        t.rows = min(hi - t.row0, BIG_BM);
-        break;
-      }
-      tstart += n;
-    }
-    // wave-uniform: kept in scalar registers
-    t.e = __builtin_amdgcn_readfirstlane(t.e);
-    t.row0 = __builtin_amdgcn_readfirstlane(t.row0);
-    t.rows = __builtin_amdgcn_readfirstlane(t.rows);
-    t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
-    t.cols = __builtin_amdgcn_readfirstlane(t.cols);
-    return t;
-  };
+  auto decode = [&](int id) { return decode_tile(id, MT, NT, N, E, seg); };
 
   const uint8_t* __restrict__ A = (const uint8_t*)p.A;
   const uint8_t* __restrict__ B = (const uint8_t*)p.B;
@@ -585,6 +714,20 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
       for (int j = 0; j < 4; ++j) store_part(rp, poff, (i * 4 + j) * 64 * 16, acc[i][j]);
     wait_vm_all();
   }
+
+  if (has_narrow) {
+    // slice vsplit % s of leftover tile vsplit / s (XCD-major numbering: the slices of a tile share
+    // an XCD and its L2 copy of the tile's rows of A)
+    __syncthreads();   // every wave is done with the whole-tile buffers and epilogue areas
+    const Tile t = decode(full + vsplit / nparts);
+    const int bn = BIG_BN / nparts, sl = vsplit % nparts;
+    const int bcols = min(t.cols - sl * bn, bn);
+    if (bcols > 0) {   // slices past N of a narrower last n-tile have nothing to do
+      constexpr int MODE = SILU ? (PRE ? 2 : 1) : (PRE ? 3 : 0);
+      if (nparts == 4) narrow_slice<MODE, 64>(p, smem, t, t.n0 + sl * bn, bcols);
+      else narrow_slice<MODE, 32>(p, smem, t, t.n0 + sl * bn, bcols);
+    }
+  }
 }
 
 
@@ -686,7 +829,8 @@ int gemm_big_grid(int max_rows, int E, int N) {
 
 hipError_t launch_gemm_big(const GemmParams& p, bool silu, hipStream_t s) {
   if (p.K < 256) return hipErrorInvalidValue;   // the pipeline needs four K stages per tile
-  const int grid = gemm_big_grid(p.max_rows, p.E, p.N);
+  // reductions under 64 stages always get all 256 workgroups, so that a narrow tail has them
+  const int grid = p.K / 64 < 64 ? MAX_WGS : gemm_big_grid(p.max_rows, p.E, p.N);
   if (silu && p.C2) gemm_big_kernel<true, true><<<grid, 512, 0, s>>>(p);
   else if (silu) gemm_big_kernel<true, false><<<grid, 512, 0, s>>>(p);
   else if (p.dsilu) gemm_big_kernel<false, true><<<grid, 512, 0, s>>>(p);
