@@ -13,8 +13,8 @@
 //
 // Lane layout of a 16x16 MFMA result: lane l holds rows 4*(l/16) .. 4*(l/16)+3 of column l%16.
 // Rows are tokens and columns are experts, so the 16 lanes of a row group hold all (up to 16)
-// experts of 4 tokens: top-k and softmax are reductions over those 16 lanes (xor 1, 2, 4, 8),
-// with more experts held in extra registers (ET tiles of 16).
+// experts of 4 tokens: top-k and softmax are reductions over those 16 lanes (DPP moves within
+// the row), with more experts held in extra registers (ET tiles of 16).
 //
 // Two kernels compute the logits:
 //  * route_ksplit_kernel (bf16): an 8-wave workgroup routes 1, 2 or 4 tiles of 16 tokens, each
@@ -34,7 +34,47 @@ __device__ __forceinline__ uint32_t key_code(float key) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Reductions over the 16 lanes of a row (one token's experts) with DPP moves, so the data stays in
+// the vector registers: partners lane ^ 1 and lane ^ 2 (quad permutes), then the mirror within
+// each half row (lane i of 8 with 7 - i) and within the row (i of 16 with 15 - i). Each step
+// combines a value with its partner's by a commutative op, so every lane of the row ends with the
+// same bits.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) { return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v))); }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+}
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<DPP_XOR1>(v));
+  v = fmaxf(v, dpp_f32<DPP_XOR2>(v));
+  v = fmaxf(v, dpp_f32<DPP_HALF_MIRROR>(v));
+  return fmaxf(v, dpp_f32<DPP_MIRROR>(v));
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v = __fadd_rn(v, dpp_f32<DPP_XOR1>(v));
+  v = __fadd_rn(v, dpp_f32<DPP_XOR2>(v));
+  v = __fadd_rn(v, dpp_f32<DPP_HALF_MIRROR>(v));
+  return __fadd_rn(v, dpp_f32<DPP_MIRROR>(v));
+}
+
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t row16_max_u64(uint64_t v) {
+  v = max_u64(v, dpp_u64<DPP_XOR1>(v));
+  v = max_u64(v, dpp_u64<DPP_XOR2>(v));
+  v = max_u64(v, dpp_u64<DPP_HALF_MIRROR>(v));
+  return max_u64(v, dpp_u64<DPP_MIRROR>(v));
+}
 
 // Per-lane running sums for the aux statistics: the lane's probabilities of real tokens (its
 // expert column of each ET tile) and, in column 0 lanes only, the router entropy of its real
@@ -103,8 +143,7 @@ __device__ __forceinline__ void finish_tile(const RouteParams& p, f32x4_t (&acc)
       uint64_t best = 0;
 #pragma unroll
       for (int et = 0; et < ET; ++et) best = max_u64(best, pk[et]);
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) best = max_u64(best, __shfl_xor(best, m));
+      best = row16_max_u64(best);
 #pragma unroll
       for (int et = 0; et < ET; ++et)
         if (best != 0ull && pk[et] == best) {
@@ -123,11 +162,8 @@ __device__ __forceinline__ void finish_tile(const RouteParams& p, f32x4_t (&acc)
       if (valid[et]) mx_all = fmaxf(mx_all, L[et]);
       if (slot[et] >= 0) mx_sel = fmaxf(mx_sel, L[et]);
     }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-      mx_all = fmaxf(mx_all, __shfl_xor(mx_all, m));
-      mx_sel = fmaxf(mx_sel, __shfl_xor(mx_sel, m));
-    }
+    mx_all = row16_max(mx_all);
+    mx_sel = row16_max(mx_sel);
     float z[ET], ex_all[ET], ex_sel[ET];
     float s_all = 0.0f, s_sel = 0.0f;
 #pragma unroll
@@ -138,11 +174,8 @@ __device__ __forceinline__ void finish_tile(const RouteParams& p, f32x4_t (&acc)
       s_all = __fadd_rn(s_all, ex_all[et]);
       s_sel = __fadd_rn(s_sel, ex_sel[et]);
     }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-      s_all = __fadd_rn(s_all, __shfl_xor(s_all, m));
-      s_sel = __fadd_rn(s_sel, __shfl_xor(s_sel, m));
-    }
+    s_all = row16_sum(s_all);
+    s_sel = row16_sum(s_sel);
     // entropy -sum p ln p = ln s - sum p z, with ln p = z - ln s (no logarithm of a small p)
     float pz = 0.0f;
 #pragma unroll
@@ -164,8 +197,7 @@ __device__ __forceinline__ void finish_tile(const RouteParams& p, f32x4_t (&acc)
         p.weights[(size_t)t * K + slot[et]] = w;
       }
     }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) pz = __fadd_rn(pz, __shfl_xor(pz, m));
+    pz = row16_sum(pz);
     if (real && col == 0) {
       st.ent += (double)__fsub_rn(logf(s_all), pz);
       st.cnt += 1.0;
