@@ -248,22 +248,37 @@ namespace moe {
 //   G[e][m][n] = sum over the expert's rows r of P[r][m] * Q[r][n]     (fp32 result)
 // a product whose reduction runs over the expert's segment of the permuted rows (dW2 = dY^T H,
 // dW1 = dA^T Xp). bf16 (grad_w_bf16_kernel):
-//  * one 128 x 128 output tile of one expert per workgroup; 4 waves in 2 x 2, each 64 x 64 =
-//    4 x 4 blocks of v_mfma_f32_16x16x32_bf16. Tiles are numbered so that each XCD takes a
+//  * one 256 x 256 output tile of one expert per workgroup; 8 waves in 2 x 4, each 128 x 64 =
+//    8 x 4 blocks of v_mfma_f32_16x16x32_bf16. Tiles are numbered so that each XCD takes a
 //    contiguous range (the same expert), walked in groups of 8 m-tiles: the tiles in flight on
 //    an XCD share their rows of P and Q 8 ways in its L2.
-//  * the reduction runs in stages of 64 rows. P and Q are row-major in r, and an MFMA operand
-//    wants 8 consecutive r per lane, so each thread loads an 8 x 8 block (8 rows x 16 bytes,
-//    whole 128-byte lines along m or n), transposes it in registers (v_perm pairs of halves) and
-//    writes 8 16-byte rows of r into LDS: [m or n][r] with a 72-element pitch (the MFMA operand
-//    reads of 8 lanes then cover all banks).
-//  * two LDS buffers and two register sets: the loads of stage s + 2 are issued before the 32
-//    MFMAs of stage s, and stage s + 1 (requested a stage earlier) is transposed into the other
-//    buffer alongside them; one barrier per stage.
-constexpr int GW_TILE = 256, GW_BK = 64, GW_TP = GW_BK + 8;
+//  * the reduction runs in stages of 64 rows. P and Q are row-major in r; a stage of each (64 rows
+//    x 512 bytes of the tile's columns) is copied row for row into LDS by direct buffer -> LDS
+//    loads (2 rows per instruction), with the 16-byte chunks of row r XOR-swizzled by
+//    sw(r) = 2 ((r & 3) | ((r & 8) >> 1)). An MFMA operand wants 8 consecutive r per lane; the
+//    transposing LDS read (ds_read_b64_tr_b16) delivers 4 of them: in each group of 16 lanes,
+//    lane s reads 8 bytes of row r0 + s / 4 at column c0 + 4 (s % 4), and lane i receives column
+//    c0 + i of rows r0 .. r0 + 3. The swizzle puts the 16 rows x 32 bytes of one such read of
+//    a wave on every bank pair exactly twice (two cycles, the minimum for 512 bytes).
+//  * two LDS buffers (128 KiB); the loads of stage s + 1 are issued after the barrier that opens
+//    stage s and land while its MFMAs run.
+constexpr int GW_TILE = 256, GW_BK = 64, GW_ROWB = GW_TILE * 2;   // bytes of a staged row
+constexpr int GW_OP_BYTES = GW_BK * GW_ROWB;                        // one operand, one stage: 32 KiB
+
+typedef short gw_v4i16 __attribute__((ext_vector_type(4)));
+
+// Direct buffer -> LDS 16-byte load per lane (lane l writes LDS [lds_addr + 16 l, + 16)); M0 is
+// restored afterwards. The kernel waits for these itself (vmcnt).
+__device__ __forceinline__ void gw_load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory");
+}
 
 __global__ __launch_bounds__(512, 1) void grad_w_bf16_kernel(GradWParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][GW_TILE * GW_TP];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * 2 * GW_OP_BYTES];   // [buffer][operand]
   const int tilesM = (p.M + GW_TILE - 1) / GW_TILE, tilesN = (p.N + GW_TILE - 1) / GW_TILE;
   const int per_e = tilesM * tilesN, total = per_e * p.E * p.splits;
   int b = blockIdx.x;
@@ -283,53 +298,50 @@ __global__ __launch_bounds__(512, 1) void grad_w_bf16_kernel(GradWParams p) {
     if (part == 0) r1 = mid;
     else r0 = mid;
   }
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fg = lane >> 4;
-  // loader: operand op (P for threads 0..255, Q for 256..511; one operand per wave), 8 x 8 block
-  // (rb, cb) of a stage (8 consecutive lanes: the 8 row blocks of one column block, so that their
-  // transposed 16-byte LDS writes are contiguous; a wave's loads are 8 rows x 128 contiguous
-  // bytes). The loads go through a buffer resource per stage covering the stage's valid rows:
-  // rows past the segment's end read as zeros, and so do columns past M or N (whole 8-column
-  // blocks, both being multiples of 8), given an offset outside every resource.
-  const int op = tid >> 8, bi = tid & 255, rb = bi & 7, cb = bi >> 3;
-  const int width = __builtin_amdgcn_readfirstlane(op ? p.N : p.M);
-  const uint64_t opnd = (uint64_t)(uintptr_t)(op ? p.Q : p.P);
-  const uint32_t opnd_lo = __builtin_amdgcn_readfirstlane((uint32_t)opnd);
-  const uint32_t opnd_hi = __builtin_amdgcn_readfirstlane((uint32_t)(opnd >> 32));
-  const uint16_t* const src = (const uint16_t*)(uintptr_t)(((uint64_t)opnd_hi << 32) | opnd_lo);
-  const uint32_t rowb = (uint32_t)width * 2u;
-  const int col = (op ? n0 : m0) + 8 * cb;
-  uint32_t voff[8];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+  // loader: wave w copies rows 8 w .. 8 w + 7 of the stage of both operands, rows 8 w + 2 i +
+  // lane / 32 in instruction i; lane l fills chunk slot l % 32 of its row with the global chunk
+  // the swizzle puts there (columns past M or N get an offset outside every resource: zeros)
+  uint32_t vP[4], vQ[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) voff[i] = col < width ? (uint32_t)(8 * rb + i) * rowb + (uint32_t)col * 2u : 0x80000000u;
-  uint16_t* const dst0 = &lds[0][op][(8 * cb) * GW_TP + 8 * rb];
-  uint16_t* const dst1 = &lds[1][op][(8 * cb) * GW_TP + 8 * rb];
-  uint4 va[8];
-#define GW_LOAD(V, R)                                                                          \
-  {                                                                                            \
-    const int r_ = (R);                                                                        \
-    const int nrows_ = r_ < r1 ? min(GW_BK, r1 - r_) : 0;                                      \
-    const __amdgpu_buffer_rsrc_t rs_ = __builtin_amdgcn_make_buffer_rsrc(                      \
-        (void*)(src + (size_t)(r_ < r1 ? r_ : r0) * width), 0, nrows_ * (int)rowb, 0x00020000); \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                            \
-      const auto t_ = __builtin_amdgcn_raw_buffer_load_b128(rs_, (int)voff[i], 0, 0);           \
-      V[i] = make_uint4(t_[0], t_[1], t_[2], t_[3]);                                           \
-    }                                                                                          \
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * w + 2 * i + (lane >> 5);
+    const int sw = 2 * ((r & 3) | ((r & 8) >> 1));
+    const int c = 8 * ((lane & 31) ^ sw);   // tile column of the chunk
+    vP[i] = m0 + c < p.M ? (uint32_t)(r * p.M + m0 + c) * 2u : 0x80000000u;
+    vQ[i] = n0 + c < p.N ? (uint32_t)(r * p.N + n0 + c) * 2u : 0x80000000u;
   }
-  // transpose: output dword q of column j holds rows 2q (low half) and 2q + 1 (high half)
-#define GW_STORE(V, DST)                                                           \
-  {                                                                                \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                \
-      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;                    \
-      uint32_t o[4];                                                               \
-      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                              \
-        const uint32_t lo = ((const uint32_t*)&V[2 * q])[j >> 1];                  \
-        const uint32_t hi = ((const uint32_t*)&V[2 * q + 1])[j >> 1];              \
-        o[q] = __builtin_amdgcn_perm(hi, lo, sel);                                 \
-      }                                                                            \
-      *(uint4*)((DST) + j * GW_TP) = make_uint4(o[0], o[1], o[2], o[3]);           \
-    }                                                                              \
-  }
+  const uint16_t* const P = (const uint16_t*)p.P;
+  const uint16_t* const Q = (const uint16_t*)p.Q;
+  auto issue = [&](int r, int buf) {   // stage starting at row r (< r1)
+    const int nrows = min(GW_BK, r1 - r);
+    const __amdgpu_buffer_rsrc_t rp =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(P + (size_t)r * p.M), 0, nrows * p.M * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rq =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Q + (size_t)r * p.N), 0, nrows * p.N * 2, 0x00020000);
+    const uint32_t base = lds0 + buf * 2 * GW_OP_BYTES + 8 * w * GW_ROWB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gw_load_lds16(rp, vP[i], base + 2 * i * GW_ROWB);
+      gw_load_lds16(rq, vQ[i], base + GW_OP_BYTES + 2 * i * GW_ROWB);
+    }
+  };
+  // transposing reads: lane s = fr of group fg reads row 32 ks + 8 fg + 4 h + s / 4 (h: which half
+  // of the operand's 8 rows), byte 8 (s % 2) of chunk 2 blk + (s % 4) / 2 at its swizzled slot;
+  // with that row's swizzle 2 x, x = s / 4 + 4 (fg & 1), the slot is 2 (blk ^ x) + (s % 4) / 2
+  const int xs = (fr >> 2) | ((fg & 1) << 2);
+  const uint32_t rdl = (uint32_t)((8 * fg + (fr >> 2)) * GW_ROWB + ((fr & 3) >> 1) * 16 + (fr & 1) * 8);
+  auto tr8 = [&](const uint8_t* opbase, int ks, int blk) -> bf16x8_t {
+    const uint8_t* q = opbase + ks * 32 * GW_ROWB + rdl + ((blk ^ xs) << 5);
+    const gw_v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) gw_v4i16*)(__attribute__((address_space(3))) const uint8_t*)q);
+    const gw_v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) gw_v4i16*)(__attribute__((address_space(3))) const uint8_t*)(q + 4 * GW_ROWB));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
   // 8 waves in 2 x 4, each 128 x 64 of the tile: 8 x 4 blocks of 16 x 16
   f32x4_t acc[8][4];
 #pragma unroll
@@ -337,44 +349,30 @@ __global__ __launch_bounds__(512, 1) void grad_w_bf16_kernel(GradWParams p) {
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int wm = w >> 2, wn = w & 3;
-  auto mfma_stage = [&](int buf) {
-    const uint16_t* A = &lds[buf][0][0];
-    const uint16_t* B = &lds[buf][1][0];
+  const int ns = (r1 - r0 + GW_BK - 1) / GW_BK;
+  if (ns > 0) issue(r0, 0);
+  for (int s = 0; s < ns; ++s) {
+    // this wave's loads of stage s have landed; after the barrier every wave's have, and every
+    // wave is done with the other buffer (stage s - 1)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (s + 1 < ns) issue(r0 + (s + 1) * GW_BK, (s + 1) & 1);
+    const uint8_t* A = lds + (s & 1) * 2 * GW_OP_BYTES;
+    const uint8_t* B = A + GW_OP_BYTES;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8_t bfr[4];
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-        bfr[ni] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(B + (64 * wn + 16 * ni + fr) * GW_TP + 32 * ks + 8 * fg));
+      for (int ni = 0; ni < 4; ++ni) bfr[ni] = tr8(B, ks, 4 * wn + ni);
 #pragma unroll
       for (int mi = 0; mi < 8; ++mi) {
-        const bf16x8_t af =
-            __builtin_bit_cast(bf16x8_t, *(const uint4*)(A + (128 * wm + 16 * mi + fr) * GW_TP + 32 * ks + 8 * fg));
+        const bf16x8_t af = tr8(A, ks, 8 * wm + mi);
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[ni], acc[mi][ni], 0, 0, 0);
       }
     }
-  };
-  // one register set: stage s + 1 is requested before stage s's MFMAs and transposed into the
-  // other LDS buffer after them; one barrier per stage; past the last stage the loads see an
-  // empty resource and return zeros
-  const int ns = (r1 - r0 + GW_BK - 1) / GW_BK;
-  if (ns > 0) {
-    GW_LOAD(va, r0);
-    GW_STORE(va, dst0);
-    __syncthreads();
   }
-  for (int s = 0; s < ns; ++s) {
-    GW_LOAD(va, r0 + (s + 1) * GW_BK);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_stage(s & 1);
-    __builtin_amdgcn_sched_barrier(0);
-    GW_STORE(va, (s & 1) ? dst0 : dst1);
-    __syncthreads();
-  }
-#undef GW_LOAD
-#undef GW_STORE
   // lane holds rows m0 + 128 wm + 16 mi + 4 fg .. + 3 of column n0 + 64 wn + 16 ni + fr
   float* __restrict__ G = p.G + (size_t)e * p.M * p.N;
 #pragma unroll
