@@ -103,6 +103,16 @@ __device__ __forceinline__ void load_lds16(i32x4_t rsrc, uint32_t voff, uint32_t
                : "memory");
 }
 
+// The same with a uniform byte offset in the instruction's scalar offset register (it does not
+// take a vector register per distinct offset).
+__device__ __forceinline__ void load_lds16s(i32x4_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory");
+}
+
 // One 16-byte buffer store per lane; lanes that must not write carry an out-of-range offset. The
 // output is not read again by this kernel, so it is stored with the non-temporal hint and does not
 // displace the operand rows that the XCD's L2 is serving to the other tiles. The compiler does not
@@ -515,7 +525,13 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   // group 1: phase X of the next tile's first stage), beside the other group's MFMAs.
   // Needs at least four stages per tile.
   const int gr = wm;
-  // wave wn loads rows [64 wn, 64 wn + 64) of its operand, 8 rows per instruction
+  // group 0: A rows of stage st of tile t into buffer buf; group 1: B rows. Wave wn loads rows
+  // [64 wn, 64 wn + 64) of its operand, 8 rows per instruction: lane l fills row 8 i + l / 8 (of
+  // the wave's 64) at slot l % 8 with the chunk the swizzle puts there. The plain variants hold
+  // the two per-lane offsets (even and odd i) across the loop. The variants that also read or
+  // write C2 have no vector register to spare for them: there they are recomputed from the lane
+  // id at each call (in volatile asm, so not hoisted and held), and the row offset of i goes in
+  // the scalar offset (held, they spilled to scratch, and the reloads stalled every stage).
   uint32_t vo[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -523,13 +539,23 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     const int chunk = (lane & 7) ^ ((h << 2) | (lane >> 4));
     vo[h] = (uint32_t)r * (uint32_t)rowbytes + chunk * 16;
   }
-  // group 0: A rows of stage st of tile t into buffer buf; group 1: B rows
   auto load_half = [&](const Tile& t, int st, int buf) {
     const i32x4_t r = gr == 0 ? rs_a(t, st) : rs_b(t, st);
     const uint32_t sa = lds0 + buf * STAGE_BYTES + gr * TILE_BYTES + wn * 64 * ROWB;
+    if constexpr (PRE) {
+      int ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      const int c0 = (ln & 7) ^ (ln >> 4);
+      const uint32_t vo0 = (uint32_t)(wn * 64 + (ln >> 3)) * (uint32_t)rowbytes + (uint32_t)(c0 << 4);
+      const uint32_t vo1 = vo0 + 8u * (uint32_t)rowbytes + (uint32_t)(((c0 ^ 4) - c0) * 16);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      load_lds16(r, vo[i & 1] + (uint32_t)((i >> 1) * 16) * (uint32_t)rowbytes, sa + i * 8 * ROWB);
+      for (int i = 0; i < 8; ++i)
+        load_lds16s(r, (i & 1) ? vo1 : vo0, (uint32_t)((i >> 1) * 16) * (uint32_t)rowbytes, sa + i * 8 * ROWB);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        load_lds16(r, vo[i & 1] + (uint32_t)((i >> 1) * 16) * (uint32_t)rowbytes, sa + i * 8 * ROWB);
+    }
   };
   // Fragment reads of stage g: row r of a 16-row block sits at byte r * 128 of its block, its 16-byte
   // chunk c at ((c ^ ((r >> 1) & 7)) << 4); within one wave the swizzle depends on the lane only
