@@ -317,7 +317,8 @@ moe_status_t moe_forward_noalloc(const moe_config_t* cfg, const void* x, const f
  *   d_out [T, d] act, y [T*k, d] act, row_of [T, k], weights [T, k] fp32, dy [T*k, d] act,
  *   dweights [T, k] fp32.
  * moe_expert_ffn_backward: over each expert's rows, with A = xp W1_e^T (recomputed) and
- *   dA = (dy W2_e) * SiLU'(A): dxp = dA W1_e (act; rows >= N untouched), and when not NULL
+ *   dA = (dy W2_e) * SiLU'(A) (the product dy W2_e rounded to act, then dA rounded to act):
+ *   dxp = dA W1_e (act; rows >= N untouched), and when not NULL
  *   dw2[e] = dy^T h (fp32 [E, d, f], needs h) and dw1[e] = dA^T xp (fp32 [E, f, d]); an expert
  *   with no rows gets zero weight gradients. bf16/fp32 weights only. xp, dy, dxp [T*k, d] act,
  *   h [T*k, f] act (the forward's H), offsets [E+1] as in the forward.

@@ -67,13 +67,6 @@ __device__ __forceinline__ float silu_fast(float v) {
   return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// SiLU'(a) = s (1 + a (1 - s)), s = sigmoid(a), with the same hardware exp2 and reciprocal (the
-// product dH SiLU'(a) is rounded to bf16 right after).
-__device__ __forceinline__ float dsilu_fast(float a) {
-  const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * 1.44269504088896341f));
-  return s * (1.0f + a * (1.0f - s));
-}
-
 // acc += A * B on v_mfma_f32_16x16x32_bf16 with the accumulator bound to AGPRs (inline asm keeps
 // all 256 accumulators of a lane in the AGPR file). Same-shape MFMAs chained on one accumulator
 // are interlocked by the hardware; the first read of the results after the loop is preceded by
@@ -208,7 +201,7 @@ __device__ __forceinline__ void store_part(i32x4_t rsrc, uint32_t voff, uint32_t
 // stage, swizzled as the whole tiles) filled by direct buffer -> LDS loads two stages ahead, one
 // barrier per stage. Wave w owns rows [32 w, 32 w + 32) x all BN features as 2 x BN / 16 MFMA
 // blocks with the weight fragment first. Epilogue per lane (4 consecutive features of one row):
-// MODE 0 the accumulator, 1 its SiLU, 2 also the pre-activation to C2 first, 3 times SiLU'(C2);
+// MODE 0 the accumulator, 1 its SiLU, 2 also the pre-activation to C2 first;
 // one rounding.
 constexpr int NR_STAGES = 3;
 constexpr int NR_BROWS = 64;                                   // B rows staged (the widest slice)
@@ -288,13 +281,6 @@ __device__ __forceinline__ void narrow_slice(const GemmParams& p, uint8_t* smem,
       if (r >= t.rows || n >= bcols) continue;
       const size_t o = (size_t)(t.row0 + r) * N + n0 + n;
       float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-      if constexpr (MODE == 3) {   // dA = dH SiLU'(A), A = p.C2 at the same place
-        const uint2 a = *(const uint2*)((const uint16_t*)p.C2 + o);
-        v[0] *= dsilu_fast(bf16_bits_to_f32(a.x & 0xFFFFu));
-        v[1] *= dsilu_fast(bf16_bits_to_f32(a.x >> 16));
-        v[2] *= dsilu_fast(bf16_bits_to_f32(a.y & 0xFFFFu));
-        v[3] *= dsilu_fast(bf16_bits_to_f32(a.y >> 16));
-      }
       if constexpr (MODE == 2) {   // the pre-activation, rounded once
         *(uint2*)((uint16_t*)p.C2 + o) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
@@ -309,6 +295,7 @@ __device__ __forceinline__ void narrow_slice(const GemmParams& p, uint8_t* smem,
 
 template <bool SILU, bool PRE>
 __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
+  static_assert(SILU || !PRE, "the pre-activation is kept by the SiLU GEMM only");
   // the two operand stages and the per-wave epilogue areas; the narrow tail reuses all of it as a
   // 3-stage ring (3 x 48 KiB)
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES + 8 * EPI_BYTES];
@@ -417,8 +404,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   // Epilogue of tile t from the accumulators (after the wait states that let the last MFMAs
   // retire): SiLU (when S), one rounding, and row-contiguous stores to dst through a per-wave
   // LDS area.
-  // MODE 0: the accumulator; 1: SiLU of it; 2: it times SiLU'(A), A = p.C2 at the same place
-  // (the backward's dA = dH SiLU'(A), one rounding)
+  // MODE 0: the accumulator; 1: SiLU of it
   auto store_pass = [&](const Tile& t, auto mode_c, uint16_t* dst) {
     constexpr int MODE = decltype(mode_c)::value;
     // per-lane epilogue offsets, recomputed for every tile rather than held across the main loop
@@ -437,26 +423,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     const i32x4_t rc = make_rsrc(dst + (size_t)t.row0 * N, (uint32_t)t.rows * N * 2);
     uint8_t* const ep = epi + w * EPI_BYTES;
     const int rrow = lane_o >> 3, rchunk = lane_o & 7;   // read-back: row within 8, chunk
-    // MODE 2: A's 4 features of each 16 x 16 block of row block i, one row block ahead, through a
-    // resource sized to the tile's valid rows (columns past the tile get an out-of-range offset)
-    uint2 pa[2][4];
-    auto load_pre = [&](int i, uint2 (&dstv)[4]) {
-      const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)((const uint16_t*)p.C2 + (size_t)t.row0 * N), 0, t.rows * N * 2, 0x00020000);
-  #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = wn * 64 + 16 * j + 4 * efc;
-        const uint32_t off = (n < t.cols) ? (uint32_t)((wm * 128 + 16 * i + efr) * N + t.n0 + n) * 2u : 0x80000000u;
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(ra, (int)off, 0, 0);
-        dstv[j] = uint2{v[0], v[1]};
-      }
-    };
-    if constexpr (MODE == 2) load_pre(0, pa[0]);
   #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if constexpr (MODE == 2) {
-        if (i + 1 < 8) load_pre(i + 1, pa[(i + 1) & 1]);
-      }
   #pragma unroll
       for (int jp = 0; jp < 2; ++jp) {
         uint32_t P[2], Q[2];
@@ -469,14 +437,6 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
             a1 = silu_fast(a1);
             b0 = silu_fast(b0);
             b1 = silu_fast(b1);
-          }
-          if constexpr (MODE == 2) {
-            const uint32_t wa = h ? pa[i & 1][2 * jp].y : pa[i & 1][2 * jp].x;
-            const uint32_t wb = h ? pa[i & 1][2 * jp + 1].y : pa[i & 1][2 * jp + 1].x;
-            a0 *= dsilu_fast(bf16_bits_to_f32(wa & 0xFFFFu));
-            a1 *= dsilu_fast(bf16_bits_to_f32(wa >> 16));
-            b0 *= dsilu_fast(bf16_bits_to_f32(wb & 0xFFFFu));
-            b1 *= dsilu_fast(bf16_bits_to_f32(wb >> 16));
           }
           const auto r = __builtin_amdgcn_permlane16_swap(pack_bf16x2(a0, a1), pack_bf16x2(b0, b1), false, false);
           P[h] = r[0];
@@ -497,14 +457,11 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // PRE with SILU (p.C2 set): also the pre-activation, same tile, before the SiLU pass.
-  // PRE without SILU (p.dsilu): the product times SiLU'(p.C2).
+  // PRE (with SILU, p.C2 set): also the pre-activation, same tile, before the SiLU pass.
   auto store_tile = [&](const Tile& t) {
     if constexpr (SILU) {
       if constexpr (PRE) store_pass(t, std::integral_constant<int, 0>{}, (uint16_t*)p.C2);
       store_pass(t, std::integral_constant<int, 1>{}, C);
-    } else if constexpr (PRE) {
-      store_pass(t, std::integral_constant<int, 2>{}, C);
     } else {
       store_pass(t, std::integral_constant<int, 0>{}, C);
     }
@@ -528,10 +485,10 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   // group 0: A rows of stage st of tile t into buffer buf; group 1: B rows. Wave wn loads rows
   // [64 wn, 64 wn + 64) of its operand, 8 rows per instruction: lane l fills row 8 i + l / 8 (of
   // the wave's 64) at slot l % 8 with the chunk the swizzle puts there. The plain variants hold
-  // the two per-lane offsets (even and odd i) across the loop. The variants that also read or
-  // write C2 have no vector register to spare for them: there they are recomputed from the lane
-  // id at each call (in volatile asm, so not hoisted and held), and the row offset of i goes in
-  // the scalar offset (held, they spilled to scratch, and the reloads stalled every stage).
+  // the two per-lane offsets (even and odd i) across the loop. The variant that also writes the
+  // pre-activation has no vector register to spare for them: there they are recomputed from the
+  // lane id at each call (in volatile asm, so not hoisted and held), and the row offset of i goes
+  // in the scalar offset (held, they spilled to scratch, and the reloads stalled every stage).
   uint32_t vo[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -749,7 +706,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     const int bn = BIG_BN / nparts, sl = vsplit % nparts;
     const int bcols = min(t.cols - sl * bn, bn);
     if (bcols > 0) {   // slices past N of a narrower last n-tile have nothing to do
-      constexpr int MODE = SILU ? (PRE ? 2 : 1) : (PRE ? 3 : 0);
+      constexpr int MODE = SILU ? (PRE ? 2 : 1) : 0;
       if (nparts == 4) narrow_slice<MODE, 64>(p, smem, t, t.n0 + sl * bn, bcols);
       else narrow_slice<MODE, 32>(p, smem, t, t.n0 + sl * bn, bcols);
     }
@@ -823,13 +780,6 @@ __global__ __launch_bounds__(256) void gemm_tail_kernel(GemmParams p, int G) {
     }
     if (m >= rows || n >= cols) continue;
     float v[4] = {s.x, s.y, s.z, s.w};
-    if (!SILU && p.dsilu) {   // dA = dH SiLU'(A), A = p.C2 at the same place
-      const uint2 a = *(const uint2*)((const uint16_t*)p.C2 + (size_t)(row0 + m) * N + n0 + n);
-      v[0] *= dsilu_fast(bf16_bits_to_f32(a.x & 0xFFFFu));
-      v[1] *= dsilu_fast(bf16_bits_to_f32(a.x >> 16));
-      v[2] *= dsilu_fast(bf16_bits_to_f32(a.y & 0xFFFFu));
-      v[3] *= dsilu_fast(bf16_bits_to_f32(a.y >> 16));
-    }
     if (SILU && p.C2) {   // the pre-activation, rounded once
       uint2 a;
       a.x = pack_bf16x2(v[0], v[1]);
@@ -859,7 +809,6 @@ hipError_t launch_gemm_big(const GemmParams& p, bool silu, hipStream_t s) {
   const int grid = p.K / 64 < 64 ? MAX_WGS : gemm_big_grid(p.max_rows, p.E, p.N);
   if (silu && p.C2) gemm_big_kernel<true, true><<<grid, 512, 0, s>>>(p);
   else if (silu) gemm_big_kernel<true, false><<<grid, 512, 0, s>>>(p);
-  else if (p.dsilu) gemm_big_kernel<false, true><<<grid, 512, 0, s>>>(p);
   else gemm_big_kernel<false, false><<<grid, 512, 0, s>>>(p);
   if (p.sk_part && grid == MAX_WGS && p.K / 64 >= 64) {   // tail_parts splits nothing below 64 stages
     // the kernel works out how many tail tiles there are (none: it returns at once)

@@ -266,7 +266,7 @@ moe_status_t run_dispatch(const moe_config_t& c, int bt, const int32_t* ids, con
 // `sk` is the split-tail partial-sum region of the caller's workspace (null: no split tail).
 moe_status_t run_gemm_sk(const moe_config_t& c, const void* a, const void* b, void* out, const int32_t* offsets,
                          int n, int kdim, bool silu, void* sk, hipStream_t s, int experts = -1, int rows = -1,
-                         bool int4 = false, void* pre = nullptr, bool dsilu = false) {
+                         bool int4 = false, void* pre = nullptr) {
   if (experts < 0) experts = c.num_experts;
   if (rows < 0) rows = c.T * c.top_k;
   GemmParams p{};
@@ -278,8 +278,7 @@ moe_status_t run_gemm_sk(const moe_config_t& c, const void* a, const void* b, vo
   p.A = a;
   p.B = b;
   p.C = out;
-  p.C2 = (silu || dsilu) ? pre : nullptr;
-  p.dsilu = dsilu ? 1 : 0;
+  p.C2 = silu ? pre : nullptr;
   p.offsets = offsets;
   if (int4) {
     p.q4_scale_off = q4_scale_offset((size_t)experts * (size_t)n, kdim);
@@ -349,9 +348,7 @@ moe_status_t expert_ffn_bwd(const moe_config_t& c, const BwdLayout& L, const voi
   MOE_LAUNCH(launch_transpose(w2, w2t, E, d, f, a, stream));
   if (a_kept) a1 = const_cast<void*>(a_kept);   // the forward's own pre-activation (read only)
   else MOE_TRY(run_gemm_sk(c, xp, w1, a1, offsets, f, d, false, sk, stream));
-  // on the 256 x 256 path the dH GEMM's epilogue multiplies by SiLU'(A) itself (one rounding)
-  const bool fuse = bf16 && gemm_uses_big(true, d, c.T * c.top_k, E);
-  MOE_TRY(run_gemm_sk(c, dy, w2t, dh, offsets, f, d, false, sk, stream, -1, -1, false, fuse ? a1 : nullptr, fuse));
+  MOE_TRY(run_gemm_sk(c, dy, w2t, dh, offsets, f, d, false, sk, stream));
   GradWParams g{};
   g.E = E;
   g.max_rows = c.T * c.top_k;
@@ -364,7 +361,9 @@ moe_status_t expert_ffn_bwd(const moe_config_t& c, const BwdLayout& L, const voi
     g.G = dw2;
     MOE_LAUNCH(launch_grad_w(g, bf16, stream));
   }
-  if (!fuse) MOE_LAUNCH(launch_silu_bwd(dh, a1, dh, offsets + E, c.T * c.top_k, f, bf16, stream));
+  // dA = dH SiLU'(A), in place (an elementwise pass: measured faster than multiplying in the GEMM's
+  // epilogue, whose reads of A wait a round trip per 16-row block)
+  MOE_LAUNCH(launch_silu_bwd(dh, a1, dh, offsets + E, c.T * c.top_k, f, bf16, stream));
   MOE_TRY(run_gemm_sk(c, dh, w1t, dxp, offsets, d, f, false, sk, stream));
   if (dw1) {   // dW1_e = dA^T Xp over the expert's rows: [f, d]
     g.M = f;
@@ -792,9 +791,7 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const float* w
     MOE_LAUNCH(launch_transpose(w1_shared, w1st, 1, fs, d, a, stream));
     MOE_LAUNCH(launch_transpose(w2_shared, w2st, 1, d, fs, a, stream));
     MOE_TRY(run_gemm_sk(c, x, w1_shared, as, sh_off, fs, d, false, sk, stream, 1, T));
-    const bool fuse_s = bf16 && gemm_uses_big(true, d, T, 1);
-    MOE_TRY(run_gemm_sk(c, d_out, w2st, dhs, sh_off, fs, d, false, sk, stream, 1, T, false, fuse_s ? as : nullptr,
-                        fuse_s));
+    MOE_TRY(run_gemm_sk(c, d_out, w2st, dhs, sh_off, fs, d, false, sk, stream, 1, T));
     GradWParams g{};
     g.E = 1;
     g.max_rows = T;
@@ -807,7 +804,7 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const float* w
       g.G = dw2_shared;
       MOE_LAUNCH(launch_grad_w(g, bf16, stream));
     }
-    if (!fuse_s) MOE_LAUNCH(launch_silu_bwd(dhs, as, dhs, sh_off + 1, T, fs, bf16, stream));
+    MOE_LAUNCH(launch_silu_bwd(dhs, as, dhs, sh_off + 1, T, fs, bf16, stream));
     MOE_TRY(run_gemm_sk(c, dhs, w1st, dxs, sh_off, d, fs, false, sk, stream, 1, T));
     if (dw1_shared) {   // dW1s = dAs^T x: [fs, d]
       g.M = fs;

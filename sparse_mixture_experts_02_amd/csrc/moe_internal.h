@@ -140,8 +140,6 @@ struct GemmParams {
   // SiLU GEMMs: when not null, also receives the pre-activation (the accumulator rounded once to
   // act, before the SiLU), [rows, N] like C
   void* C2;
-  // plain GEMMs on the 256 x 256 path (bf16): 1 = store C = acc * SiLU'(C2), C2 read-only [rows, N]
-  int dsilu;
 };
 
 struct CombineParams {
