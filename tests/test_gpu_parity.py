@@ -64,6 +64,10 @@ REDUCED = {
     # 256 x 256 GEMM2 with K = 4096 and 266 tiles: the 10 tiles past the first round of 256 are
     # split into K-parts summed by the tail kernel
     "big_split_tail": derived(BASE, name="big_split_tail", T=34000, d_model=64, d_ffn=4096, num_experts=2),
+    # 256 x 256 GEMMs whose tiles overrun whole rounds by a few tiles (GEMM1: 516 = 2 x 256 + 4,
+    # GEMM2: 258), the leftover ones being the experts' last m-tiles of 82 rows: narrow slices of
+    # mostly empty tiles after several rounds
+    "big_small_tail": derived(BASE, name="big_small_tail", T=32850, d_model=256, d_ffn=512, num_experts=2),
     # combine fast path (bf16, top-k <= 2, d a multiple of 512 up to 4096): top-1, and the widest row
     "combine_top1_d512": derived(BASE, name="combine_top1_d512", T=300, d_model=512, d_ffn=256, num_experts=4,
                                  top_k=1),
