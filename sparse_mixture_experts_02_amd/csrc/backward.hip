@@ -252,33 +252,50 @@ namespace moe {
 //    8 x 4 blocks of v_mfma_f32_16x16x32_bf16. Tiles are numbered so that each XCD takes a
 //    contiguous range (the same expert), walked in groups of 8 m-tiles: the tiles in flight on
 //    an XCD share their rows of P and Q 8 ways in its L2.
-//  * the reduction runs in stages of 64 rows. P and Q are row-major in r; a stage of each (64 rows
-//    x 512 bytes of the tile's columns) is copied row for row into LDS by direct buffer -> LDS
-//    loads (2 rows per instruction), with the 16-byte chunks of row r XOR-swizzled by
-//    sw(r) = 2 ((r & 3) | ((r & 8) >> 1)). An MFMA operand wants 8 consecutive r per lane; the
-//    transposing LDS read (ds_read_b64_tr_b16) delivers 4 of them: in each group of 16 lanes,
-//    lane s reads 8 bytes of row r0 + s / 4 at column c0 + 4 (s % 4), and lane i receives column
-//    c0 + i of rows r0 .. r0 + 3. The swizzle puts the 16 rows x 32 bytes of one such read of
-//    a wave on every bank pair exactly twice (two cycles, the minimum for 512 bytes).
-//  * two LDS buffers (128 KiB); the loads of stage s + 1 are issued after the barrier that opens
-//    stage s and land while its MFMAs run.
-constexpr int GW_TILE = 256, GW_BK = 64, GW_ROWB = GW_TILE * 2;   // bytes of a staged row
-constexpr int GW_OP_BYTES = GW_BK * GW_ROWB;                        // one operand, one stage: 32 KiB
+//  * the reduction runs in stages of 64 rows. P and Q are row-major in r; a stage of each operand
+//    (64 rows x the tile's 256 columns) sits in LDS as four 64-column blocks of 64 rows x 128
+//    bytes, filled row for row by direct buffer -> LDS loads (8 rows x 128 bytes per
+//    instruction). An MFMA operand wants 8 consecutive r per lane; the transposing LDS read
+//    (ds_read_b64_tr_b16) delivers 4 of them: in each group of 16 lanes, lane s reads 8 bytes of
+//    row r0 + s / 4 at column c0 + 4 (s % 4), and lane i receives column c0 + i of rows
+//    r0 .. r0 + 3. Within a row the four 32-byte quarters are XOR-swizzled by
+//    f(r) = ((r >> 1) & 1) | (((r >> 3) & 1) << 1), which puts the 16 rows x 32 bytes of one such
+//    read of a wave on every bank octet exactly twice (two cycles, the minimum for 512 bytes).
+//  * ping-pong, as in the forward's grouped GEMM: the two waves of each SIMD (w and w + 4, the
+//    tile's two 128-row halves in m, groups 0 and 1) take turns at the matrix core. In one phase a
+//    group issues its stage's 64 MFMAs and nothing else while the other reads its next fragments
+//    from LDS and issues its share of the direct loads; a barrier ends each phase. Group 1 runs
+//    one phase behind group 0. Group 0 loads P, group 1 loads Q: wave wn of a group fills
+//    64-column block wn of its operand. P of stage s + 2 goes into stage s's buffer right after
+//    the phase in which group 1 read stage s; Q of stage s + 3 goes into stage s + 1's buffer
+//    right after wave wn of group 1 has read that block, which its partner in group 0 read one
+//    phase before. Each group waits for its loads at the end of its next MFMA phase.
+constexpr int GW_TILE = 256, GW_BK = 64;
+constexpr int GW_CB_BYTES = GW_BK * 128;            // one 64-column block of one operand: 8 KiB
+constexpr int GW_OP_BYTES = 4 * GW_CB_BYTES;        // one operand, one stage: 32 KiB
+constexpr int GW_STAGE_BYTES = 2 * GW_OP_BYTES;     // P and Q
 
 typedef short gw_v4i16 __attribute__((ext_vector_type(4)));
 
-// Direct buffer -> LDS 16-byte load per lane (lane l writes LDS [lds_addr + 16 l, + 16)); M0 is
-// restored afterwards. The kernel waits for these itself (vmcnt).
-__device__ __forceinline__ void gw_load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_addr) {
+// Direct buffer -> LDS 16-byte load per lane (lane l writes LDS [lds_addr + 16 l, + 16)), with a
+// uniform byte offset in the scalar offset register; M0 is restored afterwards. The kernel waits
+// for these itself (vmcnt).
+__device__ __forceinline__ void gw_load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
+                                              uint32_t lds_addr) {
   uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
                : "=&s"(saved)
-               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
                : "memory");
 }
 
+__device__ __forceinline__ gw_v4i16 gw_read_tr(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) gw_v4i16*)(uintptr_t)addr);
+}
+
 __global__ __launch_bounds__(512, 1) void grad_w_bf16_kernel(GradWParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * 2 * GW_OP_BYTES];   // [buffer][operand]
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * GW_STAGE_BYTES];   // [buffer][P, Q][block]
   const int tilesM = (p.M + GW_TILE - 1) / GW_TILE, tilesN = (p.N + GW_TILE - 1) / GW_TILE;
   const int per_e = tilesM * tilesN, total = per_e * p.E * p.splits;
   int b = blockIdx.x;
@@ -298,82 +315,125 @@ __global__ __launch_bounds__(512, 1) void grad_w_bf16_kernel(GradWParams p) {
     if (part == 0) r1 = mid;
     else r0 = mid;
   }
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  r1 = __builtin_amdgcn_readfirstlane(r1);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gr = w >> 2, wn = w & 3;
   const int fr = lane & 15, fg = lane >> 4;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
-  // loader: wave w copies rows 8 w .. 8 w + 7 of the stage of both operands, rows 8 w + 2 i +
-  // lane / 32 in instruction i; lane l fills chunk slot l % 32 of its row with the global chunk
-  // the swizzle puts there (columns past M or N get an offset outside every resource: zeros)
-  uint32_t vP[4], vQ[4];
+
+  // Loader: wave wn of group gr copies 64-column block wn of its operand (P for group 0, Q for
+  // group 1). Instruction i (i < 8) fills rows 8 i .. 8 i + 7 of the block; lane l fills 16-byte
+  // slot l % 8 of row 8 i + l / 8 with the global chunk the swizzle puts there, chunk
+  // (l % 8) ^ 2 f(row) (f of that row is ((l >> 4) & 1) | ((i & 1) << 1)). Offsets relative to the
+  // stage's first row; the row offset 16 (i / 2) rows goes in the scalar offset. Columns past M
+  // (or N) get an offset outside every resource (zeros, nothing fetched); rows past the segment's
+  // end fall outside the stage's resource.
+  const int opc = gr == 0 ? p.M : p.N;   // columns of this wave's operand
+  const uint32_t rs = (uint32_t)opc * 2u;  // its row stride in bytes
+  const int cb0 = (gr == 0 ? m0 : n0) + 64 * wn;
+  uint32_t vo[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 8 * w + 2 * i + (lane >> 5);
-    const int sw = 2 * ((r & 3) | ((r & 8) >> 1));
-    const int c = 8 * ((lane & 31) ^ sw);   // tile column of the chunk
-    vP[i] = m0 + c < p.M ? (uint32_t)(r * p.M + m0 + c) * 2u : 0x80000000u;
-    vQ[i] = n0 + c < p.N ? (uint32_t)(r * p.N + n0 + c) * 2u : 0x80000000u;
+  for (int h = 0; h < 2; ++h) {
+    const int chunk = (lane & 7) ^ ((((lane >> 4) & 1) << 1) | (h << 2));
+    const int c = cb0 + 8 * chunk;
+    vo[h] = c < opc ? (uint32_t)(8 * h + (lane >> 3)) * rs + (uint32_t)c * 2u : 0x80000000u;
   }
-  const uint16_t* const P = (const uint16_t*)p.P;
-  const uint16_t* const Q = (const uint16_t*)p.Q;
-  auto issue = [&](int r, int buf) {   // stage starting at row r (< r1)
+  const uint16_t* const src = (const uint16_t*)(gr == 0 ? p.P : p.Q);
+  auto load_stage = [&](int st, int buf) {   // stage st (< number of stages) into buffer buf
+    const int r = r0 + st * GW_BK;
     const int nrows = min(GW_BK, r1 - r);
-    const __amdgpu_buffer_rsrc_t rp =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(P + (size_t)r * p.M), 0, nrows * p.M * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rq =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Q + (size_t)r * p.N), 0, nrows * p.N * 2, 0x00020000);
-    const uint32_t base = lds0 + buf * 2 * GW_OP_BYTES + 8 * w * GW_ROWB;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(src + (size_t)r * opc), 0, nrows * rs, 0x00020000);
+    const uint32_t base = lds0 + buf * GW_STAGE_BYTES + gr * GW_OP_BYTES + wn * GW_CB_BYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      gw_load_lds16(rp, vP[i], base + 2 * i * GW_ROWB);
-      gw_load_lds16(rq, vQ[i], base + GW_OP_BYTES + 2 * i * GW_ROWB);
+    for (int i = 0; i < 8; ++i) gw_load_lds16(rsrc, vo[i & 1], (uint32_t)(i >> 1) * 16u * rs, base + i * 1024);
+  };
+
+  // Fragment reads: lane s = fr of group fg reads, for block u (16 columns at 16 u of a 64-column
+  // block) and half hh, row 32 ks + 8 fg + 4 hh + fr / 4, bytes 8 (fr % 4) of quarter u ^ f(row);
+  // f(row) = (fr >> 3) | ((fg & 1) << 1) for every ks and hh. The per-lane part without the
+  // quarter is rd; quarter u is an XOR of bits 5-6, which no other term of the address touches,
+  // so each u gets its own address register and the rest are immediate offsets.
+  const uint32_t rd = (uint32_t)((8 * fg + (fr >> 2)) * 128 + 8 * (fr & 3) + 32 * ((fr >> 3) | ((fg & 1) << 1)));
+  bf16x8_t xa[2][8], wb[2][4];
+  auto read_frags = [&](int g) {
+    const uint32_t bufb = lds0 + (g & 1) * GW_STAGE_BYTES;
+    const uint32_t pb = bufb + gr * 2 * GW_CB_BYTES;          // blocks 2 gr, 2 gr + 1 of P
+    const uint32_t qb = bufb + GW_OP_BYTES + wn * GW_CB_BYTES;  // block wn of Q
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t ru = rd ^ (uint32_t)(32 * u);
+      asm volatile("" : "+v"(ru));
+      const uint32_t pa = pb + ru, qa = qb + ru;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {   // P blocks u (block 2 gr) and 4 + u (block 2 gr + 1)
+          const uint32_t a = pa + half * GW_CB_BYTES + ks * 32 * 128;
+          const gw_v4i16 lo = gw_read_tr(a), hi = gw_read_tr(a + 4 * 128);
+          xa[ks][4 * half + u] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+        const uint32_t a = qa + ks * 32 * 128;
+        const gw_v4i16 lo = gw_read_tr(a), hi = gw_read_tr(a + 4 * 128);
+        wb[ks][u] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
-  // transposing reads: lane s = fr of group fg reads row 32 ks + 8 fg + 4 h + s / 4 (h: which half
-  // of the operand's 8 rows), byte 8 (s % 2) of chunk 2 blk + (s % 4) / 2 at its swizzled slot;
-  // with that row's swizzle 2 x, x = s / 4 + 4 (fg & 1), the slot is 2 (blk ^ x) + (s % 4) / 2
-  const int xs = (fr >> 2) | ((fg & 1) << 2);
-  const uint32_t rdl = (uint32_t)((8 * fg + (fr >> 2)) * GW_ROWB + ((fr & 3) >> 1) * 16 + (fr & 1) * 8);
-  auto tr8 = [&](const uint8_t* opbase, int ks, int blk) -> bf16x8_t {
-    const uint8_t* q = opbase + ks * 32 * GW_ROWB + rdl + ((blk ^ xs) << 5);
-    const gw_v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) gw_v4i16*)(__attribute__((address_space(3))) const uint8_t*)q);
-    const gw_v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) gw_v4i16*)(__attribute__((address_space(3))) const uint8_t*)(q + 4 * GW_ROWB));
-    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-  // 8 waves in 2 x 4, each 128 x 64 of the tile: 8 x 4 blocks of 16 x 16
   f32x4_t acc[8][4];
 #pragma unroll
   for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int wm = w >> 2, wn = w & 3;
-  const int ns = (r1 - r0 + GW_BK - 1) / GW_BK;
-  if (ns > 0) issue(r0, 0);
-  for (int s = 0; s < ns; ++s) {
-    // this wave's loads of stage s have landed; after the barrier every wave's have, and every
-    // wave is done with the other buffer (stage s - 1)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (s + 1 < ns) issue(r0 + (s + 1) * GW_BK, (s + 1) & 1);
-    const uint8_t* A = lds + (s & 1) * 2 * GW_OP_BYTES;
-    const uint8_t* B = A + GW_OP_BYTES;
+  auto compute = [&]() {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t bfr[4];
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) bfr[ni] = tr8(B, ks, 4 * wn + ni);
-#pragma unroll
-      for (int mi = 0; mi < 8; ++mi) {
-        const bf16x8_t af = tr8(A, ks, 8 * wm + mi);
+      for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[ni], acc[mi][ni], 0, 0, 0);
-      }
+          asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[mi][ni]) : "v"(xa[ks][mi]), "v"(wb[ks][ni]));
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto phase_end = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  const int ns = (r1 - r0 + GW_BK - 1) / GW_BK;
+  if (ns > 0) {
+    load_stage(0, 0);
+    if (ns > 1) load_stage(1, 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    read_frags(0);
+    if (gr == 1) {
+      phase_end();   // group 0's stage-0 reads are done too: Q of stage 2 may replace stage 0's
+      if (ns > 2) load_stage(2, 0);
     }
+    for (int s = 0; s < ns; ++s) {
+      compute();
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of its previous memory phase
+      phase_end();
+      if (gr == 0 && s + 2 < ns) load_stage(s + 2, s & 1);
+      if (s + 1 < ns) read_frags(s + 1);
+      if (gr == 1 && s + 3 < ns) load_stage(s + 3, (s + 1) & 1);
+      phase_end();
+    }
+    if (gr == 0) phase_end();
+    // let the last MFMAs retire before their accumulators are read
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]), "+a"(acc[7][3]),
+                   "+a"(acc[6][0]), "+a"(acc[6][1]), "+a"(acc[6][2]), "+a"(acc[6][3])
+                 :
+                 : "memory");
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // lane holds rows m0 + 128 wm + 16 mi + 4 fg .. + 3 of column n0 + 64 wn + 16 ni + fr
+  // lane holds rows m0 + 128 gr + 16 mi + 4 fg .. + 3 of column n0 + 64 wn + 16 ni + fr
   float* __restrict__ G = p.G + (size_t)e * p.M * p.N;
 #pragma unroll
   for (int mi = 0; mi < 8; ++mi)
@@ -382,7 +442,7 @@ __global__ __launch_bounds__(512, 1) void grad_w_bf16_kernel(GradWParams p) {
       const int n = n0 + 64 * wn + 16 * ni + fr;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int m = m0 + 128 * wm + 16 * mi + 4 * fg + t;
+        const int m = m0 + 128 * gr + 16 * mi + 4 * fg + t;
         if (m < p.M && n < p.N) {
           // two halves: each adds its partial sum to the zeroed G (0 + a is exact and a + b
           // commutes, so the result does not depend on which half lands first)
