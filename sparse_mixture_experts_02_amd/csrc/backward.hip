@@ -649,13 +649,112 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(RouteBwdParams p) {
 }
 
 // dx[t] += sum_e dL[t, e] W_r[e]: a [T, E] x [E, d] product in fp32 FMAs (the router weight is
-// fp32). A block owns 64 tokens x 256 columns: the tokens' dL rows sit in LDS (read back as
-// 16-byte vectors, the same address for every lane), each thread keeps its column's EM router
-// weights in registers and adds each token's sum to dx as soon as it is formed (one more rounding
-// to act).
+// fp32), each token's sum added to dx with one more rounding to act. The tokens' dL rows sit in
+// LDS (read back as 16-byte vectors, the same address for every lane).
+// Up to 16 experts (route_bwd_dx_kernel): a block owns RB_DX_TOK tokens x 2048 columns, a thread 8
+// consecutive columns with their EM x 8 router weights in registers; the dx values of 8 (EM 16:
+// 4) tokens are loaded (16 bytes per token for bf16) before any of them is updated, and the
+// blocks are short so that several run on each CU. 32 or 64 experts (route_bwd_dx1_kernel): one column per thread,
+// 256 columns per block, one token at a time.
 constexpr int RB_TOK = 64;
+constexpr int RB_DX_COLS = 2048;   // columns per block of route_bwd_dx_kernel (256 threads x 8)
+constexpr int RB_DX_TOK = 16;      // tokens per block of route_bwd_dx_kernel
+typedef unsigned rb_u32x4 __attribute__((ext_vector_type(4)));
 template <bool BF16, int EM>
 __global__ __launch_bounds__(256) void route_bwd_dx_kernel(RouteBwdParams p) {
+  constexpr int NB = EM <= 8 ? 8 : 4;   // tokens whose dx is in flight at once
+  __shared__ __attribute__((aligned(16))) float sdl[RB_DX_TOK][EM];
+  const int E = p.E, d = p.d;
+  const int t0 = blockIdx.y * RB_DX_TOK;
+  const int c8 = blockIdx.x * RB_DX_COLS + 8 * threadIdx.x;
+  for (int i = threadIdx.x; i < RB_DX_TOK * EM; i += 256) {
+    const int tt = i / EM, e = i % EM;
+    const int t = t0 + tt;
+    sdl[tt][e] = (t < p.T && e < E) ? p.dlogits[(size_t)t * E + e] : 0.0f;
+  }
+  __syncthreads();
+  if (c8 >= d) return;
+  float wv[EM][8];
+#pragma unroll
+  for (int e = 0; e < EM; ++e) {
+    if (e < E) {
+      const float4 a = *(const float4*)&p.w_router[(size_t)e * d + c8];
+      const float4 b = *(const float4*)&p.w_router[(size_t)e * d + c8 + 4];
+      wv[e][0] = a.x; wv[e][1] = a.y; wv[e][2] = a.z; wv[e][3] = a.w;
+      wv[e][4] = b.x; wv[e][5] = b.y; wv[e][6] = b.z; wv[e][7] = b.w;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) wv[e][q] = 0.0f;
+    }
+  }
+  const int nt = min(RB_DX_TOK, p.T - t0);
+  // the sum of token tt's dL row against the 8 columns' weights, expert order
+  auto sums = [&](int tt, float (&a)[8]) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a[q] = 0.0f;
+#pragma unroll
+    for (int e4 = 0; e4 < EM / 4; ++e4) {
+      const float4 v = *(const float4*)&sdl[tt][4 * e4];
+      const float lv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) a[q] = fmaf(lv[u], wv[4 * e4 + u][q], a[q]);
+    }
+  };
+  if constexpr (BF16) {
+    uint16_t* const dx = (uint16_t*)p.dx;
+    auto update = [&](int tt, const rb_u32x4& v) {
+      float a[8];
+      sums(tt, a);
+      rb_u32x4 o;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float lo = __fadd_rn(bf16_bits_to_f32(v[h] & 0xFFFFu), a[2 * h]);
+        const float hi = __fadd_rn(bf16_bits_to_f32(v[h] >> 16), a[2 * h + 1]);
+        o[h] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+      }
+      *(rb_u32x4*)(dx + (size_t)(t0 + tt) * d + c8) = o;
+    };
+    int tb = 0;
+    for (; tb + NB <= nt; tb += NB) {   // NB tokens' loads, unconditionally, before the updates
+      rb_u32x4 v[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) v[j] = *(const rb_u32x4*)(dx + (size_t)(t0 + tb + j) * d + c8);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) update(tb + j, v[j]);
+    }
+    for (; tb < nt; ++tb) update(tb, *(const rb_u32x4*)(dx + (size_t)(t0 + tb) * d + c8));
+  } else {
+    float* const dx = (float*)p.dx;
+    auto update = [&](int tt, const float4& v0, const float4& v1) {
+      float a[8];
+      sums(tt, a);
+      const float4 r0 = make_float4(__fadd_rn(v0.x, a[0]), __fadd_rn(v0.y, a[1]), __fadd_rn(v0.z, a[2]),
+                                    __fadd_rn(v0.w, a[3]));
+      const float4 r1 = make_float4(__fadd_rn(v1.x, a[4]), __fadd_rn(v1.y, a[5]), __fadd_rn(v1.z, a[6]),
+                                    __fadd_rn(v1.w, a[7]));
+      *(float4*)(dx + (size_t)(t0 + tt) * d + c8) = r0;
+      *(float4*)(dx + (size_t)(t0 + tt) * d + c8 + 4) = r1;
+    };
+    int tb = 0;
+    for (; tb + NB <= nt; tb += NB) {   // NB tokens' loads, unconditionally, before the updates
+      float4 v[NB][2];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        v[j][0] = *(const float4*)(dx + (size_t)(t0 + tb + j) * d + c8);
+        v[j][1] = *(const float4*)(dx + (size_t)(t0 + tb + j) * d + c8 + 4);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) update(tb + j, v[j][0], v[j][1]);
+    }
+    for (; tb < nt; ++tb)
+      update(tb, *(const float4*)(dx + (size_t)(t0 + tb) * d + c8), *(const float4*)(dx + (size_t)(t0 + tb) * d + c8 + 4));
+  }
+}
+
+template <bool BF16, int EM>
+__global__ __launch_bounds__(256) void route_bwd_dx1_kernel(RouteBwdParams p) {
   __shared__ __attribute__((aligned(16))) float sdl[RB_TOK][EM];
   const int E = p.E, d = p.d;
   const int t0 = blockIdx.y * RB_TOK;
@@ -693,17 +792,22 @@ __global__ __launch_bounds__(256) void route_bwd_dx_kernel(RouteBwdParams p) {
 }
 
 // dW_r[e, c] = sum_t dL[t, e] x[t, c]: a [E, T] x [T, d] product, split over token chunks. A
-// thread owns 8 consecutive columns (one 16-byte load of x per token for bf16, two for fp32) and
-// their 8 EM sums; a block covers 2048 columns of one chunk. The chunk's dL rows stream through
-// LDS 64 tokens at a time and are read back as 16-byte vectors (the same address for every lane).
-// Four tokens per step keep several loads in flight. Chunk partials [chunks, E, d] are summed in
-// chunk order by route_bwd_reduce_kernel (deterministic).
-constexpr int RB_COLS = 2048;   // columns per block (256 threads x 8)
+// column thread owns 8 consecutive columns (one 16-byte load of x per token for bf16, two for
+// fp32) and their 8 EM sums; a block covers 2048 columns of one chunk with two such threads per
+// column group (512 threads: two waves per SIMD, so one's FMAs overlap the other's loads). The
+// chunk's dL rows stream through LDS 64 tokens at a time and are read back as 16-byte vectors
+// (the same address for every lane); half h of the block takes tokens 32 h .. 32 h + 31 of every
+// 64, with 16 tokens' loads (8 with 16 experts; 4 for fp32) issued before their FMAs. The two
+// halves' sums are added (half 0 + half 1) through LDS. Chunk partials [chunks, E, d] are summed
+// in a fixed order by route_bwd_reduce_kernel (deterministic).
+constexpr int RB_COLS = 2048;   // columns per block (256 column threads x 8)
 template <bool BF16, int EM>
-__global__ __launch_bounds__(256) void route_bwd_w_kernel(RouteBwdParams p) {
+__global__ __launch_bounds__(512) void route_bwd_w_kernel(RouteBwdParams p) {
   __shared__ __attribute__((aligned(16))) float sdl[RB_TOK][EM];
+  __shared__ __attribute__((aligned(16))) float xch[8][256][8];   // half 1's sums, 8 experts at a time
   const int E = p.E, d = p.d;
-  const int c8 = blockIdx.x * RB_COLS + 8 * threadIdx.x;
+  const int ct = threadIdx.x & 255, half = threadIdx.x >> 8;
+  const int c8 = blockIdx.x * RB_COLS + 8 * ct;
   const bool active = c8 < d;
   const int tb = blockIdx.y * p.chunk_tokens;
   const int te = min(p.T, tb + p.chunk_tokens);
@@ -741,41 +845,80 @@ __global__ __launch_bounds__(256) void route_bwd_w_kernel(RouteBwdParams p) {
   };
   for (int t0 = tb; t0 < te; t0 += RB_TOK) {
     __syncthreads();
-    for (int i = threadIdx.x; i < RB_TOK * EM; i += 256) {
+    for (int i = threadIdx.x; i < RB_TOK * EM; i += 512) {
       const int tt = i / EM, e = i % EM;
       const int t = t0 + tt;
       sdl[tt][e] = (t < te && e < E) ? p.dlogits[(size_t)t * E + e] : 0.0f;
     }
     __syncthreads();
     if (active) {
-      const int nt = min(RB_TOK, te - t0);
+      const int h0 = half * (RB_TOK / 2);
+      const int nt = min(RB_TOK / 2, te - t0 - h0);   // this half's tokens of the batch (may be <= 0)
       int tt = 0;
-      for (; tt + 4 <= nt; tt += 4) {   // four tokens' loads before their FMAs, in token order
-        float x0[8], x1[8], x2[8], x3[8];
-        load8(t0 + tt, x0);
-        load8(t0 + tt + 1, x1);
-        load8(t0 + tt + 2, x2);
-        load8(t0 + tt + 3, x3);
-        fma_token(tt, x0);
-        fma_token(tt + 1, x1);
-        fma_token(tt + 2, x2);
-        fma_token(tt + 3, x3);
+      if constexpr (BF16) {
+        // NB tokens' 16-byte loads before their FMAs (token order is kept for the sums)
+        constexpr int NB = EM <= 8 ? 16 : 8;
+        for (; tt + NB <= nt; tt += NB) {
+          rb_u32x4 u[NB];
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            u[j] = *(const rb_u32x4*)((const uint16_t*)p.x + (size_t)(t0 + h0 + tt + j) * d + c8);
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            float xv[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              xv[2 * q] = bf16_bits_to_f32(u[j][q] & 0xFFFFu);
+              xv[2 * q + 1] = bf16_bits_to_f32(u[j][q] >> 16);
+            }
+            fma_token(h0 + tt + j, xv);
+          }
+        }
+      } else {
+        for (; tt + 4 <= nt; tt += 4) {   // four tokens' loads before their FMAs, in token order
+          float x0[8], x1[8], x2[8], x3[8];
+          load8(t0 + h0 + tt, x0);
+          load8(t0 + h0 + tt + 1, x1);
+          load8(t0 + h0 + tt + 2, x2);
+          load8(t0 + h0 + tt + 3, x3);
+          fma_token(h0 + tt, x0);
+          fma_token(h0 + tt + 1, x1);
+          fma_token(h0 + tt + 2, x2);
+          fma_token(h0 + tt + 3, x3);
+        }
       }
       for (; tt < nt; ++tt) {
         float xv[8];
-        load8(t0 + tt, xv);
-        fma_token(tt, xv);
+        load8(t0 + h0 + tt, xv);
+        fma_token(h0 + tt, xv);
       }
     }
   }
-  if (active) {
-    float* part = p.part + (size_t)blockIdx.y * E * d;
+  // half 0 += half 1, 8 experts at a time through LDS
+  float* part = p.part + (size_t)blockIdx.y * E * d;
 #pragma unroll
-    for (int e = 0; e < EM; ++e)
-      if (e < E) {
-        *(float4*)&part[(size_t)e * d + c8] = make_float4(acc[e][0], acc[e][1], acc[e][2], acc[e][3]);
-        *(float4*)&part[(size_t)e * d + c8 + 4] = make_float4(acc[e][4], acc[e][5], acc[e][6], acc[e][7]);
+  for (int eb = 0; eb < EM; eb += 8) {
+    __syncthreads();
+    if (half == 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        *(float4*)&xch[e][ct][0] = make_float4(acc[eb + e][0], acc[eb + e][1], acc[eb + e][2], acc[eb + e][3]);
+        *(float4*)&xch[e][ct][4] = make_float4(acc[eb + e][4], acc[eb + e][5], acc[eb + e][6], acc[eb + e][7]);
       }
+    }
+    __syncthreads();
+    if (half == 0 && active) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (eb + e >= E) continue;
+        const float4 a = *(const float4*)&xch[e][ct][0];
+        const float4 b = *(const float4*)&xch[e][ct][4];
+        *(float4*)&part[(size_t)(eb + e) * d + c8] =
+            make_float4(acc[eb + e][0] + a.x, acc[eb + e][1] + a.y, acc[eb + e][2] + a.z, acc[eb + e][3] + a.w);
+        *(float4*)&part[(size_t)(eb + e) * d + c8 + 4] =
+            make_float4(acc[eb + e][4] + b.x, acc[eb + e][5] + b.y, acc[eb + e][6] + b.z, acc[eb + e][7] + b.w);
+      }
+    }
   }
 }
 
@@ -817,17 +960,56 @@ __global__ __launch_bounds__(256) void route_bwd_w1_kernel(RouteBwdParams p) {
   }
 }
 
-// dW_r = the chunk partials summed in chunk order; db[e] = sum_t dL[t, e] (a fixed-order tree over
-// 256 strided partial sums), from the blocks of the last grid row.
+// dW_r = the chunk partials summed in a fixed order: the chunks fall into RB_RG contiguous groups,
+// each summed in chunk order by one thread (4 consecutive outputs, 16-byte loads, 8 chunks' loads
+// in flight), and the group sums are added in group order. A block covers 16 output quads x the
+// RB_RG groups. db[e] = sum_t dL[t, e] (a fixed-order tree over 256 strided partial sums), from
+// the blocks of the last grid row.
+constexpr int RB_RG = 16;
 __global__ __launch_bounds__(256) void route_bwd_reduce_kernel(RouteBwdParams p) {
-  const size_t n = (size_t)p.E * p.d;
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (blockIdx.y == 0) {
-    if (i < n && p.dw_router) {
-      float acc = 0.0f;
-#pragma unroll 8
-      for (int ch = 0; ch < p.chunks; ++ch) acc += p.part[(size_t)ch * n + i];   // chunk order
-      p.dw_router[i] = acc;
+    __shared__ float4 red[RB_RG][16];
+    const int nq = p.E * p.d / 4;   // output quads
+    const int oq = threadIdx.x & 15, g = threadIdx.x >> 4;
+    const int q = blockIdx.x * 16 + oq;
+    if (!p.dw_router) return;
+    const int c0 = g * p.chunks / RB_RG, c1 = (g + 1) * p.chunks / RB_RG;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (q < nq) {
+      const float4* __restrict__ part = (const float4*)p.part;
+      int ch = c0;
+      for (; ch + 8 <= c1; ch += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = part[(size_t)(ch + j) * nq + q];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          acc.x += v[j].x;
+          acc.y += v[j].y;
+          acc.z += v[j].z;
+          acc.w += v[j].w;
+        }
+      }
+      for (; ch < c1; ++ch) {
+        const float4 v = part[(size_t)ch * nq + q];
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+      }
+    }
+    red[g][oq] = acc;
+    __syncthreads();
+    if (g == 0 && q < nq) {
+      float4 s = red[0][oq];
+      for (int j = 1; j < RB_RG; ++j) {
+        const float4 v = red[j][oq];
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
+      }
+      ((float4*)p.dw_router)[q] = s;
     }
     return;
   }
@@ -836,7 +1018,15 @@ __global__ __launch_bounds__(256) void route_bwd_reduce_kernel(RouteBwdParams p)
   const int e = blockIdx.x;
   if (e >= p.E || !p.dbias) return;
   float acc = 0.0f;
-  for (int t = threadIdx.x; t < p.T; t += 256) acc += p.dlogits[(size_t)t * p.E + e];
+  int t = threadIdx.x;
+  for (; t + 15 * 256 < p.T; t += 16 * 256) {   // 16 loads in flight, added in token order
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = p.dlogits[(size_t)(t + j * 256) * p.E + e];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc += v[j];
+  }
+  for (; t < p.T; t += 256) acc += p.dlogits[(size_t)t * p.E + e];
   red[threadIdx.x] = acc;
   __syncthreads();
   for (int m = 128; m >= 1; m >>= 1) {
@@ -872,39 +1062,42 @@ hipError_t launch_route_bwd(const RouteBwdParams& p_in, bool bf16, hipStream_t s
   route_bwd_kernel<<<grid, 256, 0, s>>>(p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int col_tiles = (p.d + 255) / 256;
   if (p.dx) {
-    dim3 g(col_tiles, (p.T + RB_TOK - 1) / RB_TOK);
-#define MOE_RBDX(EMV)                                                        \
-    if (bf16) route_bwd_dx_kernel<true, EMV><<<g, 256, 0, s>>>(p);           \
-    else route_bwd_dx_kernel<false, EMV><<<g, 256, 0, s>>>(p);
-    if (p.E <= 8) { MOE_RBDX(8) }
-    else if (p.E <= 16) { MOE_RBDX(16) }
-    else if (p.E <= 32) { MOE_RBDX(32) }
-    else { MOE_RBDX(64) }
+    dim3 g((p.d + RB_DX_COLS - 1) / RB_DX_COLS, (p.T + RB_DX_TOK - 1) / RB_DX_TOK);
+#define MOE_RBDX(K, EMV)                                                     \
+    if (bf16) K<true, EMV><<<g, 256, 0, s>>>(p);                             \
+    else K<false, EMV><<<g, 256, 0, s>>>(p);
+    if (p.E <= 8) { MOE_RBDX(route_bwd_dx_kernel, 8) }
+    else if (p.E <= 16) { MOE_RBDX(route_bwd_dx_kernel, 16) }
+    else {
+      g.x = (p.d + 255) / 256;
+      g.y = (p.T + RB_TOK - 1) / RB_TOK;
+      if (p.E <= 32) { MOE_RBDX(route_bwd_dx1_kernel, 32) }
+      else { MOE_RBDX(route_bwd_dx1_kernel, 64) }
+    }
 #undef MOE_RBDX
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   if (p.dw_router) {
     dim3 g((p.d + RB_COLS - 1) / RB_COLS, p.chunks);
-#define MOE_RBW(K, EMV)                                                      \
-    if (bf16) K<true, EMV><<<g, 256, 0, s>>>(p);                             \
-    else K<false, EMV><<<g, 256, 0, s>>>(p);
-    if (p.E <= 8) { MOE_RBW(route_bwd_w_kernel, 8) }
-    else if (p.E <= 16) { MOE_RBW(route_bwd_w_kernel, 16) }
+#define MOE_RBW(K, EMV, NT)                                                  \
+    if (bf16) K<true, EMV><<<g, NT, 0, s>>>(p);                              \
+    else K<false, EMV><<<g, NT, 0, s>>>(p);
+    if (p.E <= 8) { MOE_RBW(route_bwd_w_kernel, 8, 512) }
+    else if (p.E <= 16) { MOE_RBW(route_bwd_w_kernel, 16, 512) }
     else {
       g.x = (p.d + 255) / 256;
-      if (p.E <= 32) { MOE_RBW(route_bwd_w1_kernel, 32) }
-      else { MOE_RBW(route_bwd_w1_kernel, 64) }
+      if (p.E <= 32) { MOE_RBW(route_bwd_w1_kernel, 32, 256) }
+      else { MOE_RBW(route_bwd_w1_kernel, 64, 256) }
     }
 #undef MOE_RBW
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   if (p.dw_router || p.dbias) {
-    const size_t n = (size_t)p.E * p.d;
-    const int gx = (int)std::max<size_t>((n + 255) / 256, (size_t)p.E);
+    const size_t nq = (size_t)p.E * p.d / 4;
+    const int gx = (int)std::max<size_t>((nq + 15) / 16, (size_t)p.E);
     route_bwd_reduce_kernel<<<dim3(gx, 2), 256, 0, s>>>(p);
     err = hipGetLastError();
   }
