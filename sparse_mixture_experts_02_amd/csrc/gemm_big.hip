@@ -146,19 +146,60 @@ __device__ __forceinline__ int tail_parts(int total, int G, int nk) {
 // workgroups, each is cut along N into s = 4 or 8 slices of 256 / s output features (s R <= 256),
 // which the workgroups compute at full K after their whole tiles, so that s R workgroups share the
 // last round instead of R and nothing is added up afterwards. A slice loads all 256 rows of A for
-// 1 / s of the tile's products, so halves (s = 2, R up to 128) cost more than they save: measured
-// on the main expert-FFN layer (80 tiles left over) the last round took longer as 160 halves
-// than as 80 whole tiles. Returns s (1: no narrow tail).
-__device__ __forceinline__ int narrow_parts(int total, int G, int nk) {
+// 1 / s of the tile's products, so halves of full tiles cost more than they save (measured on the
+// main expert-FFN layer: 160 halves of full tiles took longer than 80 whole tiles). The leftover
+// tiles are the last ids, which hold the experts' partial m-tiles with the fewest rows (see
+// decode_tile); when they all have at most 128 rows, halves (s = 2, R up to 128) pay: the waves
+// whose rows are all past the tile's end skip their products, and A's missing rows are not
+// fetched. tiny: the tiles are in that order and the leftover ones have at most 128 rows.
+// Returns s (1: no narrow tail).
+__device__ __forceinline__ int narrow_parts(int total, int G, int nk, bool tiny) {
   const int R = total % G;
-  if (nk >= 64 || G != MAX_WGS || R == 0 || 4 * R > G) return 1;
-  return 8 * R <= G ? 8 : 4;
+  if (nk >= 64 || G != MAX_WGS || R == 0) return 1;
+  if (4 * R <= G) return 8 * R <= G ? 8 : 4;
+  return tiny ? 2 : 1;
+}
+
+// The m-tiles are numbered expert by expert (each expert's from its first row), or, when that
+// makes the partial last round of a reduction under 64 stages hold between 65 and 128 tiles of at
+// most 128 rows each (see narrow_parts), every expert's full 256-row m-tiles first (expert order)
+// and then the experts' partial last m-tiles, most rows first (ties: lower expert first), so that
+// the partial last round holds the emptiest ones. (Sorting in every case measured slower where
+// many experts have partial m-tiles: a group of m-tiles from different experts shares no weight
+// rows in L2.) The order of the partial m-tiles is formed once per workgroup by one wave (lane e
+// ranks expert e's remainder) into porder[]. seg: the clamped segment bounds in LDS.
+__device__ __forceinline__ void order_partials(const int* seg, int E, int* porder) {
+  const int lane = threadIdx.x & 63;
+  if (lane >= E) return;
+  const int mine = (seg[lane + 1] - seg[lane]) % BIG_BM;
+  if (mine == 0) return;
+  int rank = 0;
+  for (int e = 0; e < E; ++e) {
+    const int r = (seg[e + 1] - seg[e]) % BIG_BM;
+    rank += (r > mine || (r == mine && e < lane)) ? 1 : 0;
+  }
+  porder[rank] = lane;
+}
+
+// Whether the sorted order applies (see above); returns the MF to decode with (0: expert order).
+// total: the tiles, MT the m-tiles, MF0 the full m-tiles, G the workgroups, nk the stages.
+__device__ __forceinline__ int sorted_mf(int total, int MT, int MF0, int NT, int G, int nk, const int* seg,
+                                         const int* porder) {
+  const int R = total % G;
+  if (nk >= 64 || G != MAX_WGS || 4 * R <= G || 2 * R > G || MF0 == MT) return 0;
+  // the leftover tiles lie in m-tiles from the first of the group holding tile total - R on
+  const int first_m = ((total - R) / (GROUP_M * NT)) * GROUP_M;
+  if (first_m < MF0) return 0;
+  const int ee = porder[first_m - MF0];   // the partial m-tile with the most rows among them
+  return (seg[ee + 1] - seg[ee]) % BIG_BM <= 128 ? MF0 : 0;
 }
 
 // Tile id -> (expert, rows, output features): ids run over groups of GROUP_M m-tiles x all NT
-// n-tiles, the m-tiles of all experts numbered consecutively from the (clamped) segment bounds.
-// The fields are wave-uniform and kept in scalar registers.
-__device__ __forceinline__ Tile decode_tile(int id, int MT, int NT, int N, int E, const int* seg) {
+// n-tiles, the m-tiles in the order above (MF > 0 with sorted partials: MF full m-tiles in expert
+// order, then the partial ones in porder; MF = 0: expert by expert). The fields are wave-uniform
+// and kept in scalar registers.
+__device__ __forceinline__ Tile decode_tile(int id, int MT, int MF, int NT, int N, int E, const int* seg,
+                                            const int* porder) {
   const int group = id / (GROUP_M * NT);
   const int first_m = group * GROUP_M;
   const int gm = min(GROUP_M, MT - first_m);
@@ -166,17 +207,27 @@ __device__ __forceinline__ Tile decode_tile(int id, int MT, int NT, int N, int E
   const int mt = first_m + in_group % gm;
   const int nt = in_group / gm;
   Tile t{0, 0, 0, nt * BIG_BN, min(N - nt * BIG_BN, BIG_BN)};
-  int tstart = 0;
-  for (int ee = 0; ee < E; ++ee) {
-    const int lo = seg[ee], hi = seg[ee + 1];
-    const int n = (hi - lo + BIG_BM - 1) / BIG_BM;
-    if (mt < tstart + n) {
-      t.e = ee;
-      t.row0 = lo + (mt - tstart) * BIG_BM;
-      t.rows = min(hi - t.row0, BIG_BM);
-      break;
+  if (MF > 0 && mt >= MF) {
+    const int ee = porder[mt - MF];
+    const int len = seg[ee + 1] - seg[ee];
+    t.e = ee;
+    t.row0 = seg[ee] + (len / BIG_BM) * BIG_BM;
+    t.rows = len % BIG_BM;
+  } else {
+    // expert by expert (MF = 0), or among the full m-tiles (rounding the counts down)
+    const int round = MF > 0 ? 0 : BIG_BM - 1;
+    int tstart = 0;
+    for (int ee = 0; ee < E; ++ee) {
+      const int lo = seg[ee], hi = seg[ee + 1];
+      const int n = (hi - lo + round) / BIG_BM;
+      if (mt < tstart + n) {
+        t.e = ee;
+        t.row0 = lo + (mt - tstart) * BIG_BM;
+        t.rows = min(hi - t.row0, BIG_BM);
+        break;
+      }
+      tstart += n;
     }
-    tstart += n;
   }
   t.e = __builtin_amdgcn_readfirstlane(t.e);
   t.row0 = __builtin_amdgcn_readfirstlane(t.row0);
@@ -195,22 +246,24 @@ __device__ __forceinline__ void store_part(i32x4_t rsrc, uint32_t voff, uint32_t
 }
 }  // namespace
 
-// A narrow-tail slice (see narrow_parts): 256 rows x BN (64 or 32) output features of tile t from
-// feature n0 (bcols valid) at full K, by the 8 waves of the workgroup after its whole tiles, in
-// the whole-tile kernel's LDS: a 3-stage ring (A: 256 rows, B: 64 rows, 128 bytes of each per
-// stage, swizzled as the whole tiles) filled by direct buffer -> LDS loads two stages ahead, one
-// barrier per stage. Wave w owns rows [32 w, 32 w + 32) x all BN features as 2 x BN / 16 MFMA
-// blocks with the weight fragment first. Epilogue per lane (4 consecutive features of one row):
-// MODE 0 the accumulator, 1 its SiLU, 2 also the pre-activation to C2 first;
-// one rounding.
+// A narrow-tail slice (see narrow_parts): 256 rows x BN (128, 64 or 32) output features of tile t
+// from feature n0 (bcols valid) at full K, by the 8 waves of the workgroup after its whole tiles,
+// in the whole-tile kernel's LDS: a 3-stage ring (A: 256 rows, B: max(BN, 64) rows, 128 bytes of
+// each per stage, swizzled as the whole tiles) filled by direct buffer -> LDS loads two stages
+// ahead, one barrier per stage. Wave w owns rows [32 w, 32 w + 32) x all BN features as
+// 2 x BN / 16 MFMA blocks with the weight fragment first; a wave whose rows all lie past the
+// tile's end reads no fragments and issues no MFMAs (it still loads and passes the barriers).
+// Epilogue per lane (4 consecutive features of one row): MODE 0 the accumulator, 1 its SiLU, 2
+// also the pre-activation to C2 first; one rounding.
 constexpr int NR_STAGES = 3;
-constexpr int NR_BROWS = 64;                                   // B rows staged (the widest slice)
-constexpr int NR_STAGE_BYTES = TILE_BYTES + NR_BROWS * ROWB;   // 40 KiB
-constexpr int NR_LPS = 5;   // load instructions per wave and stage: 4 of A, 1 of B
 
 template <int MODE, int BN>
 __device__ __forceinline__ void narrow_slice(const GemmParams& p, uint8_t* smem, const Tile& t, int n0, int bcols) {
-  constexpr int NJ = BN / 16;   // 16-feature blocks per wave
+  constexpr int NJ = BN / 16;                   // 16-feature blocks per wave
+  constexpr int BROWS = BN < 64 ? 64 : BN;      // B rows staged
+  constexpr int NR_STAGE_BYTES = TILE_BYTES + BROWS * ROWB;   // 40 or 48 KiB
+  constexpr int NR_LPS = 4 + BROWS / 64;        // load instructions per wave and stage
+  static_assert(NR_STAGES * NR_STAGE_BYTES <= 2 * STAGE_BYTES + 8 * EPI_BYTES, "ring exceeds the LDS");
   const int N = p.N, rowbytes = p.K * 2, nk = p.K / 64;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -218,9 +271,10 @@ __device__ __forceinline__ void narrow_slice(const GemmParams& p, uint8_t* smem,
   const uint8_t* __restrict__ A = (const uint8_t*)p.A + (size_t)t.row0 * rowbytes;
   const uint8_t* __restrict__ B = (const uint8_t*)p.B + ((size_t)t.e * N + n0) * rowbytes;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  // wave w loads A rows 32 w + 8 i + lane / 8 (i < 4) and B rows 8 w + lane / 8 (B rows at or past
-  // bcols are outside the resource: zeros, nothing fetched); lane l fills slot l % 8 of its row
-  // with the chunk the swizzle puts there
+  // wave w loads A rows 32 w + 8 i + lane / 8 (i < 4) and B rows 64 h + 8 w + lane / 8 (h <
+  // BROWS / 64; B rows at or past bcols are outside the resource: zeros, nothing fetched); lane l
+  // fills slot l % 8 of its row with the chunk the swizzle puts there (the swizzle of B row r
+  // depends on r % 16 only, so one offset serves every h)
   uint32_t va[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -237,8 +291,11 @@ __device__ __forceinline__ void narrow_slice(const GemmParams& p, uint8_t* smem,
     const uint32_t base = lds0 + slot * NR_STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < 4; ++i) load_lds16(ra, va[i], base + (w * 32 + i * 8) * ROWB);
-    load_lds16(rb, vb, base + TILE_BYTES + w * 8 * ROWB);
+#pragma unroll
+    for (int h = 0; h < BROWS / 64; ++h)
+      load_lds16(rb, vb + (uint32_t)(64 * h) * (uint32_t)rowbytes, base + TILE_BYTES + (64 * h + w * 8) * ROWB);
   };
+  const bool live = w * 32 < t.rows;   // wave-uniform
   f32x4_t acc[2][NJ];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -254,6 +311,7 @@ __device__ __forceinline__ void narrow_slice(const GemmParams& p, uint8_t* smem,
     issue(s + 2);
     const uint8_t* sa = smem + (s % NR_STAGES) * NR_STAGE_BYTES;
     const uint8_t* sb = sa + TILE_BYTES;
+    if (!live) continue;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8_t xa[2], wb[NJ];
@@ -302,12 +360,14 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   uint8_t* const epi = smem + 2 * STAGE_BYTES;
 
   __shared__ int seg[MOE_MAX_EXPERTS_DEV + 1];
+  __shared__ int porder[MOE_MAX_EXPERTS_DEV];
 
   const int tid = threadIdx.x;
   const int E = p.E, N = p.N;
   // Segment bounds, clamped into [0, max_rows] and made non-decreasing so that no offsets value
-  // can send a tile outside the buffers. Kept in LDS: tiles are decoded between the kernel's own
-  // counted memory operations, where a global load (and the wait for it) would not belong.
+  // can send a tile outside the buffers, and the order of the partial m-tiles. Kept in LDS: tiles
+  // are decoded between the kernel's own counted memory operations, where a global load (and the
+  // wait for it) would not belong.
   if (tid <= E) seg[tid] = p.offsets[tid];   // all loads in flight at once
   __syncthreads();
   if (tid == 0) {
@@ -319,8 +379,16 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     }
   }
   __syncthreads();
-  int MT = 0;
-  for (int e = 0; e < E; ++e) MT += (seg[e + 1] - seg[e] + BIG_BM - 1) / BIG_BM;
+  if constexpr (!PRE) {   // the pre-activation variant keeps the expert order (no registers to spare)
+    if (tid < 64) order_partials(seg, E, porder);
+    __syncthreads();
+  }
+  int MT = 0, MF0 = 0;
+  for (int e = 0; e < E; ++e) {
+    const int len = seg[e + 1] - seg[e];
+    MF0 += len / BIG_BM;
+    MT += (len + BIG_BM - 1) / BIG_BM;
+  }
   const int NT = (N + BIG_BN - 1) / BIG_BN;
   const int total = MT * NT;
   const int rowbytes = p.K * 2;
@@ -333,8 +401,10 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   // narrow tail the whole tiles are the first `full` as well, and then workgroup v computes slice
   // v % s of tail tile v / s (narrow_slice).
   const int G = gridDim.x, xcd = blockIdx.x & 7;
+  const int MF = PRE ? 0 : sorted_mf(total, MT, MF0, NT, G, nk, seg, porder);
+  auto decode = [&](int id) { return decode_tile(id, MT, MF, NT, N, E, seg, porder); };
   const int sparts = (p.sk_part != nullptr && G == MAX_WGS) ? tail_parts(total, G, nk) : 1;
-  const int nparts = narrow_parts(total, G, nk);
+  const int nparts = narrow_parts(total, G, nk, MF > 0);
   const int full = (sparts > 1 || nparts > 1) ? total - total % G : total;
   const int q = full >> 3, rem = full & 7;
   const int cnt = (xcd < rem) ? q + 1 : q;
@@ -346,7 +416,6 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   const bool has_narrow = nparts > 1 && vsplit < (total - full) * nparts;
   if (local >= cnt && !has_split && !has_narrow) return;
 
-  auto decode = [&](int id) { return decode_tile(id, MT, NT, N, E, seg); };
 
   const uint8_t* __restrict__ A = (const uint8_t*)p.A;
   const uint8_t* __restrict__ B = (const uint8_t*)p.B;
@@ -707,7 +776,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     const int bcols = min(t.cols - sl * bn, bn);
     if (bcols > 0) {   // slices past N of a narrower last n-tile have nothing to do
       constexpr int MODE = SILU ? (PRE ? 2 : 1) : 0;
-      if (nparts == 4) narrow_slice<MODE, 64>(p, smem, t, t.n0 + sl * bn, bcols);
+      if (!PRE && nparts == 2) narrow_slice<MODE, 128>(p, smem, t, t.n0 + sl * bn, bcols);
+      else if (nparts == 4) narrow_slice<MODE, 64>(p, smem, t, t.n0 + sl * bn, bcols);
       else narrow_slice<MODE, 32>(p, smem, t, t.n0 + sl * bn, bcols);
     }
   }
@@ -742,24 +812,10 @@ __global__ __launch_bounds__(256) void gemm_tail_kernel(GemmParams p, int G) {
   const int full = total - total % G;
   for (int item = blockIdx.x; item < (total - full) * 32; item += gridDim.x) {
   const int r = item >> 5, w8 = (item >> 2) & 7, h = item & 3;
-  // tile decode, as in the GEMM
-  const int id = full + r;
-  const int group = id / (GROUP_M * NT);
-  const int first_m = group * GROUP_M;
-  const int gm = min(GROUP_M, MT - first_m);
-  const int in_group = id - group * GROUP_M * NT;
-  const int mt = first_m + in_group % gm;
-  const int n0 = (in_group / gm) * BIG_BN, cols = min(N - n0, BIG_BN);
-  int row0 = 0, rows = 0, tstart = 0;
-  for (int ee = 0; ee < E; ++ee) {
-    const int n = (seg[ee + 1] - seg[ee] + BIG_BM - 1) / BIG_BM;
-    if (mt < tstart + n) {
-      row0 = seg[ee] + (mt - tstart) * BIG_BM;
-      rows = min(seg[ee + 1] - row0, BIG_BM);
-      break;
-    }
-    tstart += n;
-  }
+  // as in the GEMM, whose tiles are in expert order whenever it splits (the sorted order is only
+  // taken for reductions under 64 stages)
+  const Tile tt = decode_tile(full + r, MT, 0, NT, N, E, seg, nullptr);
+  const int n0 = tt.n0, cols = tt.cols, row0 = tt.row0, rows = tt.rows;
   const float4* __restrict__ part = (const float4*)p.sk_part;
   uint16_t* __restrict__ C = (uint16_t*)p.C;
   const int wm = w8 >> 2, wn = w8 & 3;

@@ -39,6 +39,8 @@ CASES = {
     "bwd_k2_prefetch": derived(BASE, name="bwd_k2_prefetch", T=700, d_model=1024, d_ffn=256, num_experts=4),
     # weight-streaming GEMMs (at most 64 rows per expert)
     "bwd_stream": derived(WORKLOADS["small_t_streaming"], name="bwd_stream", T=96, d_model=256, d_ffn=512),
+    # half-width narrow slices of the emptiest last m-tiles on the recompute and dH GEMMs
+    "bwd_half_slices": derived(BASE, name="bwd_half_slices", T=4104, d_model=256, d_ffn=4096),
     # one round of 32 tiles with 16 stages per tile for the dH GEMM (K = d = 1024)
     "bwd_split_single": derived(BASE, name="bwd_split_single", T=2048, d_model=1024, d_ffn=512, num_experts=2),
 }
@@ -381,6 +383,8 @@ KEEP_CASES = {
     # one round of 32 tiles with 16 stages per tile, pre-activation kept
     "keep_split_single": derived(BASE, name="keep_split_single", T=2048, d_model=1024, d_ffn=512, num_experts=2),
     "keep_stream": derived(WORKLOADS["small_t_streaming"], name="keep_stream", T=96, d_model=256, d_ffn=512),
+    # half-width narrow slices storing the pre-activation too
+    "keep_half_slices": derived(BASE, name="keep_half_slices", T=4104, d_model=256, d_ffn=4096),
     "keep_f32": derived(WORKLOADS["tiny_f32"], name="keep_f32", T=150, d_model=48, d_ffn=40, num_experts=5, top_k=3),
     "keep_shared_padding": derived(WORKLOADS["main_noise_padding"], name="keep_shared_padding", T=520, d_model=128,
                                    d_ffn=192, d_ffn_shared=160),

@@ -68,6 +68,10 @@ REDUCED = {
     # GEMM2: 258), the leftover ones being the experts' last m-tiles of 82 rows: narrow slices of
     # mostly empty tiles after several rounds
     "big_small_tail": derived(BASE, name="big_small_tail", T=32850, d_model=256, d_ffn=512, num_experts=2),
+    # GEMM1 (N = 4096, K = 256) with 608 tiles: the 96 left over after two rounds are the experts'
+    # emptiest last m-tiles (74 rows or fewer), cut into 192 half-width slices whose empty waves
+    # skip their products
+    "big_half_slices": derived(BASE, name="big_half_slices", T=4104, d_model=256, d_ffn=4096),
     # combine fast path (bf16, top-k <= 2, d a multiple of 512 up to 4096): top-1, and the widest row
     "combine_top1_d512": derived(BASE, name="combine_top1_d512", T=300, d_model=512, d_ffn=256, num_experts=4,
                                  top_k=1),
