@@ -26,9 +26,11 @@
 //  * v_mfma_f32_16x16x32_bf16 with the weight fragment first (16-row blocks past the chunk's
 //    rows are skipped), fp32 accumulation, the epilogue of the bf16 weight-streaming kernel (SiLU
 //    in fp32, one rounding).
-// K must be a multiple of 128 QPD (whole groups of QPD stages; the library asks for 512) and N of
+// K must be a multiple of 128 WPD (whole groups of WPD stages; the library asks for 512) and N of
 // 128 (whole 128-feature blocks of whole tiles).
 #include "moe_internal.h"
+
+#include <type_traits>
 
 namespace moe {
 
@@ -40,7 +42,10 @@ constexpr int QN = 128;           // output features per workgroup (16 per wave)
 constexpr int QNB = QN / (16 * QW);   // 16-feature blocks per wave
 constexpr int QK = 128;           // columns per stage (two scale groups: one per two lane groups)
 constexpr int QAL = QM * QK / 8 / (64 * QW);   // 16-byte activation loads per thread per stage
-constexpr int QPD = 2;            // stages of codes and activations in flight per lane
+constexpr int QPD = 2;            // stages of activations in flight per lane
+// stages of weight codes and scales in flight per lane (4 measured slower than 2: the kernel is
+// bound by its vector instructions, not by the weight stream's latency)
+constexpr int WPD = 2;
 
 __device__ __forceinline__ float q4_silu(float v) {
   const float e = __builtin_amdgcn_exp2f(-v * 1.44269504088896341f);
@@ -177,8 +182,10 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(4, 4)))
                 (fg >> 1);
   }
 
-  for (int m0 = lo; m0 < hi; m0 += QM) {
-    const int rows = min(hi - m0, QM);
+  // one chunk of at most QM rows with NRB 16-row blocks (NRB = ceil(rows / 16)), so that no
+  // per-block branch sits inside the stage loop
+  auto chunk = [&](int m0, int rows, auto nrb_c) {
+    constexpr int NRB = decltype(nrb_c)::value;
     // activation stage: 64 rows x 16 chunks of 8 columns; thread t moves chunks t + 64 QW i. Rows
     // past the chunk read its last row instead (they only feed outputs that are not stored), and
     // stages past the end read the last stage: no load sits behind a branch, so the compiler's
@@ -195,33 +202,37 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     };
     auto ldq = [&](int st, int b) -> uint4 { return *(const uint4*)(bcode[b] + (size_t)min(st, nk - 1) * 1024); };
     auto lds = [&](int st, int b) -> uint16_t { return bscale[b][min(st, nk - 1) * 32]; };
-    // weight codes and activations of stage t sit in slot t % QPD, loaded at stage t - QPD; the
-    // activations go to LDS buffer t & 1 at the end of stage t - 1 and are read in stage t
-    uint4 bq[QPD * QNB];
-    uint16_t bs[QPD * QNB];
+    // weight codes of stage t sit in slot t % WPD, loaded at stage t - WPD; activations of stage t
+    // in slot t % QPD, loaded at stage t - QPD, go to LDS buffer t & 1 at the end of stage t - 1
+    // and are read in stage t
+    uint4 bq[WPD * QNB];
+    uint16_t bs[WPD * QNB];
     uint4 ra[QPD * QAL];
 #pragma unroll
-    for (int u = 0; u < QPD; ++u) {
+    for (int u = 0; u < WPD; ++u)
 #pragma unroll
       for (int b = 0; b < QNB; ++b) {
         bq[u * QNB + b] = ldq(u, b);
         bs[u * QNB + b] = lds(u, b);
       }
 #pragma unroll
-      for (int i = 0; i < QAL; ++i) ra[u * QAL + i] = lda(u, i);
-    }
-    f32x4_t acc[4][QNB];
+    for (int u = 0; u < QPD; ++u)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < QAL; ++i) ra[u * QAL + i] = lda(u, i);
+    f32x4_t acc[NRB][QNB];
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
 #pragma unroll
       for (int b = 0; b < QNB; ++b) acc[i][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < QAL; ++i) sta(0, i, ra[i]);
     __syncthreads();
-    for (int s0 = 0; s0 < nk; s0 += QPD) {
+    static_assert(WPD % QPD == 0, "the unrolled loop covers whole periods of both rings");
+    for (int s0 = 0; s0 < nk; s0 += WPD) {
 #pragma unroll
-      for (int u = 0; u < QPD; ++u) {
-        const int s = s0 + u;   // s % QPD == u (nk is a multiple of QPD)
+      for (int uw = 0; uw < WPD; ++uw) {
+        const int s = s0 + uw;   // s % WPD == uw (nk is a multiple of WPD)
+        const int u = uw % QPD;  // s % QPD
 #pragma unroll
         for (int i = 0; i < QAL; ++i) ra[u * QAL + i] = lda(s + QPD, i);
         const uint16_t* a = sA[s & 1];
@@ -229,12 +240,11 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(4, 4)))
         for (int ks = 0; ks < QK / 32; ++ks) {
 #pragma unroll
           for (int b = 0; b < QNB; ++b) {
-            const uint4 cw = bq[u * QNB + b];
+            const uint4 cw = bq[uw * QNB + b];
             const uint32_t word = ks == 0 ? cw.x : ks == 1 ? cw.y : ks == 2 ? cw.z : cw.w;
-            const bf16x8_t Bf = q4_dequant(word, bf16_bits_to_f32(bs[u * QNB + b]));
+            const bf16x8_t Bf = q4_dequant(word, bf16_bits_to_f32(bs[uw * QNB + b]));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if (i * 16 >= rows) break;   // uniform: 16-row blocks past the chunk's rows are skipped
+            for (int i = 0; i < NRB; ++i) {
               const int r = i * 16 + fr, ch = 4 * fg + ks;   // columns 32 fg + 8 ks .. + 7 of the stage
               const bf16x8_t X = __builtin_bit_cast(bf16x8_t, *(const uint4*)(a + r * QK + ((ch ^ (r & 7)) << 3)));
               acc[i][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Bf, X, acc[i][b], 0, 0, 0);
@@ -243,8 +253,8 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(4, 4)))
         }
 #pragma unroll
         for (int b = 0; b < QNB; ++b) {
-          bq[u * QNB + b] = ldq(s + QPD, b);
-          bs[u * QNB + b] = lds(s + QPD, b);
+          bq[uw * QNB + b] = ldq(s + WPD, b);
+          bs[uw * QNB + b] = lds(s + WPD, b);
         }
         // the next stage's activations into the other buffer (after the last stage: a harmless
         // copy of the last stage into the buffer nobody reads any more)
@@ -257,7 +267,7 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(4, 4)))
 
     // lane holds features n0 + 16 w + 4 fg .. + 3 of row m0 + 16 i + fr
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NRB; ++i) {
       const int r = i * 16 + fr;
       if (r >= rows) continue;
 #pragma unroll
@@ -273,6 +283,14 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(4, 4)))
         *(uint2*)(C + (size_t)(m0 + r) * N + n0 + n) = o;
       }
     }
+  };
+  for (int m0 = lo; m0 < hi; m0 += QM) {
+    const int rows = min(hi - m0, QM);
+    const int nrb = __builtin_amdgcn_readfirstlane((rows + 15) / 16);
+    if (nrb == 1) chunk(m0, rows, std::integral_constant<int, 1>{});
+    else if (nrb == 2) chunk(m0, rows, std::integral_constant<int, 2>{});
+    else if (nrb == 3) chunk(m0, rows, std::integral_constant<int, 3>{});
+    else chunk(m0, rows, std::integral_constant<int, 4>{});
   }
 }
 
