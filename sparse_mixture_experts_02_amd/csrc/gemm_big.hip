@@ -182,11 +182,18 @@ __device__ __forceinline__ void order_partials(const int* seg, int E, int* porde
 }
 
 // Whether the sorted order applies (see above); returns the MF to decode with (0: expert order).
-// total: the tiles, MT the m-tiles, MF0 the full m-tiles, G the workgroups, nk the stages.
-__device__ __forceinline__ int sorted_mf(int total, int MT, int MF0, int NT, int G, int nk, const int* seg,
-                                         const int* porder) {
+// total: the tiles, MT the m-tiles, MF0 the full m-tiles, G the workgroups, nk the stages. For 64
+// stages or more, the leftover tiles of a K-split tail (split: the kernel splits, and the product
+// allows it, GemmParams::sort_split) in the same way: the waves of a part whose rows all lie past
+// the tile's end skip their products.
+__device__ __forceinline__ int sorted_mf(int total, int MT, int MF0, int NT, int G, int nk, bool split,
+                                         const int* seg, const int* porder) {
   const int R = total % G;
-  if (nk >= 64 || G != MAX_WGS || 4 * R <= G || 2 * R > G || MF0 == MT) return 0;
+  if (G != MAX_WGS || MF0 == MT || R == 0 || 2 * R > G) return 0;
+  if (nk < 64 ? 4 * R <= G : !split) return 0;
+  // the partial m-tiles that do not fit in the leftover round end up in groups of m-tiles from
+  // different experts inside the whole rounds (no weight rows shared in L2): at most one group
+  if ((MT - MF0) * NT - R > GROUP_M * NT) return 0;
   // the leftover tiles lie in m-tiles from the first of the group holding tile total - R on
   const int first_m = ((total - R) / (GROUP_M * NT)) * GROUP_M;
   if (first_m < MF0) return 0;
@@ -401,9 +408,9 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   // narrow tail the whole tiles are the first `full` as well, and then workgroup v computes slice
   // v % s of tail tile v / s (narrow_slice).
   const int G = gridDim.x, xcd = blockIdx.x & 7;
-  const int MF = PRE ? 0 : sorted_mf(total, MT, MF0, NT, G, nk, seg, porder);
-  auto decode = [&](int id) { return decode_tile(id, MT, MF, NT, N, E, seg, porder); };
   const int sparts = (p.sk_part != nullptr && G == MAX_WGS) ? tail_parts(total, G, nk) : 1;
+  const int MF = PRE ? 0 : sorted_mf(total, MT, MF0, NT, G, nk, p.sort_split && sparts > 1, seg, porder);
+  auto decode = [&](int id) { return decode_tile(id, MT, MF, NT, N, E, seg, porder); };
   const int nparts = narrow_parts(total, G, nk, MF > 0);
   const int full = (sparts > 1 || nparts > 1) ? total - total % G : total;
   const int q = full >> 3, rem = full & 7;
@@ -716,38 +723,49 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     issue(t, k0 + 1, k0, k1);
     wait_vm_all();
     __syncthreads();
+    // a wave whose 128 rows all lie past the tile's end reads no fragments and issues no MFMAs
+    // (it still loads its share and passes the barriers); its partial sums stay zero. Not in the
+    // pre-activation variant, whose tiles keep the expert order (and whose main loop has no
+    // registers to spare for the branches)
+    const bool live = PRE || wm * 128 < t.rows;
+    if (live) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) frag_x(0, 0, 0, i);
+      for (int i = 0; i < 8; ++i) frag_x(0, 0, 0, i);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) frag_w(0, 0, 0, j);
+      for (int j = 0; j < 4; ++j) frag_w(0, 0, 0, j);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < k1 - k0; ++s) {
       if (s >= 1 && k0 + s + 1 < k1) issue(t, k0 + s + 1, k0, k1);
+      if (live) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 8; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[0][j], xa[0][i]);
-        if (i < 4) frag_w(1, s, 1, i);
-        frag_x(1, s, 1, i);
+          for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[0][j], xa[0][i]);
+          if (i < 4) frag_w(1, s, 1, i);
+          frag_x(1, s, 1, i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
       __builtin_amdgcn_sched_barrier(0);
       wait_vm_all();
       __syncthreads();
+      if (live) {
 #pragma unroll
-      for (int i = 4; i < 8; ++i) {
+        for (int i = 4; i < 8; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
-        frag_x(0, s + 1, 0, 2 * (i - 4));
-        frag_x(0, s + 1, 0, 2 * (i - 4) + 1);
-        frag_w(0, s + 1, 0, i - 4);
+          for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[1][j], xa[1][i]);
+          frag_x(0, s + 1, 0, 2 * (i - 4));
+          frag_x(0, s + 1, 0, 2 * (i - 4) + 1);
+          frag_w(0, s + 1, 0, i - 4);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -791,6 +809,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
 template <bool SILU>
 __global__ __launch_bounds__(256) void gemm_tail_kernel(GemmParams p, int G) {
   __shared__ int seg[MOE_MAX_EXPERTS_DEV + 1];
+  __shared__ int porder[MOE_MAX_EXPERTS_DEV];
   const int E = p.E, N = p.N, tid = threadIdx.x;
   if (tid <= E) seg[tid] = p.offsets[tid];   // all loads in flight at once
   __syncthreads();
@@ -803,18 +822,24 @@ __global__ __launch_bounds__(256) void gemm_tail_kernel(GemmParams p, int G) {
     }
   }
   __syncthreads();
-  int MT = 0;
-  for (int e = 0; e < E; ++e) MT += (seg[e + 1] - seg[e] + BIG_BM - 1) / BIG_BM;
+  if (tid < 64) order_partials(seg, E, porder);
+  __syncthreads();
+  int MT = 0, MF0 = 0;
+  for (int e = 0; e < E; ++e) {
+    const int len = seg[e + 1] - seg[e];
+    MF0 += len / BIG_BM;
+    MT += (len + BIG_BM - 1) / BIG_BM;
+  }
   const int NT = (N + BIG_BN - 1) / BIG_BN;
   const int total = MT * NT, nk = p.K / 64;
   const int sparts = tail_parts(total, G, nk);
   if (sparts < 2) return;
   const int full = total - total % G;
+  // the GEMM's order (the pre-activation variant, SILU with C2, keeps the expert order)
+  const int MF = (SILU && p.C2) ? 0 : sorted_mf(total, MT, MF0, NT, G, nk, p.sort_split != 0, seg, porder);
   for (int item = blockIdx.x; item < (total - full) * 32; item += gridDim.x) {
   const int r = item >> 5, w8 = (item >> 2) & 7, h = item & 3;
-  // as in the GEMM, whose tiles are in expert order whenever it splits (the sorted order is only
-  // taken for reductions under 64 stages)
-  const Tile tt = decode_tile(full + r, MT, 0, NT, N, E, seg, nullptr);
+  const Tile tt = decode_tile(full + r, MT, MF, NT, N, E, seg, porder);   // as in the GEMM
   const int n0 = tt.n0, cols = tt.cols, row0 = tt.row0, rows = tt.rows;
   const float4* __restrict__ part = (const float4*)p.sk_part;
   uint16_t* __restrict__ C = (uint16_t*)p.C;
@@ -826,6 +851,7 @@ __global__ __launch_bounds__(256) void gemm_tail_kernel(GemmParams p, int G) {
     const int m = wm * 128 + (blk >> 2) * 16 + (lane & 15);
     const int n = wn * 64 + (blk & 3) * 16 + 4 * (lane >> 4);
     const size_t o = (size_t)w8 * 2048 + chunk;          // 16-byte units within a slot
+    if (m >= rows || n >= cols) continue;                 // never stored: not summed either
     float4 s = part[(size_t)(r * sparts) * (PART_BYTES / 16) + o];
     for (int j = 1; j < sparts; ++j) {
       const float4 t = part[(size_t)(r * sparts + j) * (PART_BYTES / 16) + o];
@@ -834,7 +860,6 @@ __global__ __launch_bounds__(256) void gemm_tail_kernel(GemmParams p, int G) {
       s.z += t.z;
       s.w += t.w;
     }
-    if (m >= rows || n >= cols) continue;
     float v[4] = {s.x, s.y, s.z, s.w};
     if (SILU && p.C2) {   // the pre-activation, rounded once
       uint2 a;

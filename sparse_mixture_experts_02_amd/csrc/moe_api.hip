@@ -266,7 +266,7 @@ moe_status_t run_dispatch(const moe_config_t& c, int bt, const int32_t* ids, con
 // `sk` is the split-tail partial-sum region of the caller's workspace (null: no split tail).
 moe_status_t run_gemm_sk(const moe_config_t& c, const void* a, const void* b, void* out, const int32_t* offsets,
                          int n, int kdim, bool silu, void* sk, hipStream_t s, int experts = -1, int rows = -1,
-                         bool int4 = false, void* pre = nullptr) {
+                         bool int4 = false, void* pre = nullptr, bool first_layer = false) {
   if (experts < 0) experts = c.num_experts;
   if (rows < 0) rows = c.T * c.top_k;
   GemmParams p{};
@@ -280,6 +280,7 @@ moe_status_t run_gemm_sk(const moe_config_t& c, const void* a, const void* b, vo
   p.C = out;
   p.C2 = silu ? pre : nullptr;
   p.offsets = offsets;
+  p.sort_split = !silu && !first_layer;
   if (int4) {
     p.q4_scale_off = q4_scale_offset((size_t)experts * (size_t)n, kdim);
     MOE_LAUNCH(launch_gemm_q4(p, silu, s));
@@ -347,7 +348,7 @@ moe_status_t expert_ffn_bwd(const moe_config_t& c, const BwdLayout& L, const voi
   MOE_LAUNCH(launch_transpose(w1, w1t, E, f, d, a, stream));
   MOE_LAUNCH(launch_transpose(w2, w2t, E, d, f, a, stream));
   if (a_kept) a1 = const_cast<void*>(a_kept);   // the forward's own pre-activation (read only)
-  else MOE_TRY(run_gemm_sk(c, xp, w1, a1, offsets, f, d, false, sk, stream));
+  else MOE_TRY(run_gemm_sk(c, xp, w1, a1, offsets, f, d, false, sk, stream, -1, -1, false, nullptr, true));
   MOE_TRY(run_gemm_sk(c, dy, w2t, dh, offsets, f, d, false, sk, stream));
   GradWParams g{};
   g.E = E;
@@ -790,7 +791,7 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const float* w
     dxs = at(ws, L.dxs);
     MOE_LAUNCH(launch_transpose(w1_shared, w1st, 1, fs, d, a, stream));
     MOE_LAUNCH(launch_transpose(w2_shared, w2st, 1, d, fs, a, stream));
-    MOE_TRY(run_gemm_sk(c, x, w1_shared, as, sh_off, fs, d, false, sk, stream, 1, T));
+    MOE_TRY(run_gemm_sk(c, x, w1_shared, as, sh_off, fs, d, false, sk, stream, 1, T, false, nullptr, true));
     MOE_TRY(run_gemm_sk(c, d_out, w2st, dhs, sh_off, fs, d, false, sk, stream, 1, T));
     GradWParams g{};
     g.E = 1;

@@ -140,6 +140,10 @@ struct GemmParams {
   // SiLU GEMMs: when not null, also receives the pre-activation (the accumulator rounded once to
   // act, before the SiLU), [rows, N] like C
   void* C2;
+  // 256 x 256 kernel: a K-split tail may hold the emptiest tiles (sorted tile order). Set for the
+  // products whose bits need not equal a first-layer product of the pre-activation variant (which
+  // keeps the expert order): the second layer and the backward's dH and dXp.
+  int sort_split;
 };
 
 struct CombineParams {

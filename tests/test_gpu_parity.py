@@ -72,6 +72,10 @@ REDUCED = {
     # emptiest last m-tiles (74 rows or fewer), cut into 192 half-width slices whose empty waves
     # skip their products
     "big_half_slices": derived(BASE, name="big_half_slices", T=4104, d_model=256, d_ffn=4096),
+    # GEMM2 (N = 256, K = 4096) with 258 tiles: the 2 left over are the experts' 50-row last m-tiles,
+    # each split into 8 K-parts whose waves past the tile's rows skip their products
+    "big_split_small_tail": derived(BASE, name="big_split_small_tail", T=32818, d_model=256, d_ffn=4096,
+                                    num_experts=2),
     # combine fast path (bf16, top-k <= 2, d a multiple of 512 up to 4096): top-1, and the widest row
     "combine_top1_d512": derived(BASE, name="combine_top1_d512", T=300, d_model=512, d_ffn=256, num_experts=4,
                                  top_k=1),
