@@ -358,9 +358,18 @@ __device__ __forceinline__ void narrow_slice(const GemmParams& p, uint8_t* smem,
   }
 }
 
-template <bool SILU, bool PRE>
+// BT: the weights are stored [E][K][N] (the transposes of the [E][N][K] layout; the backward's dH
+// and dXp read W2 and W1 as they are). A stage of B, 64 k-rows of the tile's 256 features, is then
+// staged as four 64-feature blocks of 64 rows x 128 bytes (block wn is what waves wn and wn + 4
+// read), the 32-byte quarters of row r XOR-swizzled by f(r) = ((r >> 1) & 1) | (((r >> 3) & 1) <<
+// 1), and read with the transposing LDS read (ds_read_b64_tr_b16: in each group of 16 lanes, lane s
+// reads 8 bytes of row r0 + s / 4 at column c0 + 4 (s % 4), and lane i receives column c0 + i of
+// rows r0 .. r0 + 3), two reads per MFMA operand. The swizzle puts the 16 rows x 32 bytes of one
+// such read on every bank octet exactly twice. No narrow tail (its ring stages B as [N][K]).
+template <bool SILU, bool PRE, bool BT>
 __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   static_assert(SILU || !PRE, "the pre-activation is kept by the SiLU GEMM only");
+  static_assert(!BT || !SILU, "[K, N] weights are read by the backward's plain products only");
   // the two operand stages and the per-wave epilogue areas; the narrow tail reuses all of it as a
   // 3-stage ring (3 x 48 KiB)
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES + 8 * EPI_BYTES];
@@ -409,9 +418,10 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   // v % s of tail tile v / s (narrow_slice).
   const int G = gridDim.x, xcd = blockIdx.x & 7;
   const int sparts = (p.sk_part != nullptr && G == MAX_WGS) ? tail_parts(total, G, nk) : 1;
-  const int MF = PRE ? 0 : sorted_mf(total, MT, MF0, NT, G, nk, p.sort_split && sparts > 1, seg, porder);
+  // (the sorted order pays through the narrow tail under 64 stages, which BT does not have)
+  const int MF = (PRE || (BT && nk < 64)) ? 0 : sorted_mf(total, MT, MF0, NT, G, nk, p.sort_split && sparts > 1, seg, porder);
   auto decode = [&](int id) { return decode_tile(id, MT, MF, NT, N, E, seg, porder); };
-  const int nparts = narrow_parts(total, G, nk, MF > 0);
+  const int nparts = BT ? 1 : narrow_parts(total, G, nk, MF > 0);
   const int full = (sparts > 1 || nparts > 1) ? total - total % G : total;
   const int q = full >> 3, rem = full & 7;
   const int cnt = (xcd < rem) ? q + 1 : q;
@@ -435,6 +445,32 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  // BT loads: rows 8 i + l / 8 of a 64-feature block (instruction i < 8 covers rows 8 i .. 8 i + 7),
+  // lane l filling slot l % 8 with the chunk the swizzle puts there, (l % 8) ^ 2 f(row); per-lane
+  // offset for even and odd i (the row offset 16 (i / 2) rows goes in the scalar offset), out of
+  // range for features past the tile's last one
+  const uint32_t nb2 = (uint32_t)N * 2u;   // bytes of a [K, N] row
+  auto bt_off = [&](const Tile& t, int blk, int h) -> uint32_t {
+    const int chunk = (lane & 7) ^ ((((lane >> 4) & 1) << 1) | (h << 2));
+    const int c = 64 * blk + 8 * chunk;
+    return c < t.cols ? (uint32_t)(8 * h + (lane >> 3)) * nb2 + (uint32_t)c * 2u : 0x80000000u;
+  };
+  // instructions [i0, i0 + n) of block blk of stage st of tile t into LDS (dst: the block's base),
+  // with the block's two lane offsets o0, o1 (bt_off)
+  // (n is 4 or 8 and i0 even: the loop has a fixed trip count, offsets alternate o0, o1)
+  auto load_bt_o = [&](const Tile& t, int st, uint32_t o0, uint32_t o1, int i0, auto n_c, uint32_t dst) {
+    constexpr int n = decltype(n_c)::value;
+    const i32x4_t r = make_rsrc(B + ((size_t)t.e * p.K + (size_t)st * 64) * nb2 + (size_t)t.n0 * 2u, 64u * nb2);
+    const uint32_t soff0 = (uint32_t)(i0 >> 1) * 16u * nb2;
+    const uint32_t d0 = dst + (uint32_t)i0 * 1024u;
+#pragma unroll
+    for (int k = 0; k < n; ++k)
+      load_lds16s(r, (k & 1) ? o1 : o0, soff0 + (uint32_t)((k >> 1) * 16) * nb2, d0 + k * 1024);
+  };
+  auto load_bt = [&](const Tile& t, int st, int blk, int i0, auto n_c, uint32_t dst) {
+    load_bt_o(t, st, bt_off(t, blk, 0), bt_off(t, blk, 1), i0, n_c, dst);
+  };
+  uint32_t bto0 = 0, bto1 = 0;   // the split tail's offsets (one tile: computed once)
   // Requests stage kt of a run of stages [k0, k1) of tile t (clamped to its last one: a harmless
   // reload) into buffer (kt - k0) & 1.
   auto issue = [&](const Tile& t, int kt, int k0 = 0, int k1 = 0x7fffffff) {
@@ -453,8 +489,10 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       load_lds16(ra, voff[i], sa + i * 8 * ROWB);
-      load_lds16(rb, voff[i], sb + i * 8 * ROWB);
+      if constexpr (!BT) load_lds16(rb, voff[i], sb + i * 8 * ROWB);
     }
+    if constexpr (BT)   // wave w: rows [32 (w >> 2), + 32) of block w & 3
+      load_bt_o(t, st, bto0, bto1, 4 * (w >> 2), std::integral_constant<int, 4>{}, lds0 + ((kt - k0) & 1) * STAGE_BYTES + TILE_BYTES + (w & 3) * 8192);
   };
 
   const int wm = w >> 2, wn = w & 3;   // 2 x 4 waves, each 128 rows x 64 output features
@@ -465,16 +503,30 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     const uint8_t* sa = smem + (stage & 1) * STAGE_BYTES;
     xa[buf][i] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(sa + lds_off(wm * 128 + i * 16 + fr, ks * 4 + fc)));
   };
-  auto frag_w = [&](int buf, int stage, int ks, int j) {
-    const uint8_t* sb = smem + (stage & 1) * STAGE_BYTES + TILE_BYTES;
-    wb[buf][j] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(sb + lds_off(wn * 64 + j * 16 + fr, ks * 4 + fc)));
-  };
 
   auto rs_a = [&](const Tile& t, int st) {
     return make_rsrc(A + (size_t)t.row0 * rowbytes + st * ROWB, (uint32_t)t.rows * rowbytes);
   };
   auto rs_b = [&](const Tile& t, int st) {
     return make_rsrc(B + ((size_t)t.e * N + t.n0) * rowbytes + st * ROWB, (uint32_t)t.cols * rowbytes);
+  };
+  // transposing reads of BT fragment j (16 features) of k-step ks from a block at `blk`
+  const uint32_t bt_rd = (uint32_t)((8 * fc + (fr >> 2)) * 128 + 8 * (fr & 3) + 32 * ((fr >> 3) | ((fc & 1) << 1)));
+  auto bt_frag = [&](const uint8_t* blk, int ks, int j) -> bf16x8_t {
+    uint32_t o = bt_rd ^ (uint32_t)(32 * j);
+    asm volatile("" : "+v"(o));   // formed at each read rather than four addresses held in registers
+    const uint8_t* q = blk + ks * 32 * 128 + o;
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(__attribute__((address_space(3))) const uint8_t*)q);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(__attribute__((address_space(3))) const uint8_t*)(q + 4 * 128));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto frag_w = [&](int buf, int stage, int ks, int j) {
+    const uint8_t* sb = smem + (stage & 1) * STAGE_BYTES + TILE_BYTES;
+    if constexpr (BT) wb[buf][j] = bt_frag(sb + wn * 8192, ks, j);
+    else wb[buf][j] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(sb + lds_off(wn * 64 + j * 16 + fr, ks * 4 + fc)));
   };
 
   // Epilogue of tile t from the accumulators (after the wait states that let the last MFMAs
@@ -573,6 +625,12 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     vo[h] = (uint32_t)r * (uint32_t)rowbytes + chunk * 16;
   }
   auto load_half = [&](const Tile& t, int st, int buf) {
+    if constexpr (BT) {
+      if (gr == 1) {   // block wn of B, all 64 rows
+        load_bt(t, st, wn, 0, std::integral_constant<int, 8>{}, lds0 + buf * STAGE_BYTES + TILE_BYTES + wn * 8192);
+        return;
+      }
+    }
     const i32x4_t r = gr == 0 ? rs_a(t, st) : rs_b(t, st);
     const uint32_t sa = lds0 + buf * STAGE_BYTES + gr * TILE_BYTES + wn * 64 * ROWB;
     if constexpr (PRE) {
@@ -607,7 +665,10 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) xa[ks][i] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(pa + i * 16 * ROWB));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wb[ks][j] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(pb + j * 16 * ROWB));
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (BT) wb[ks][j] = bt_frag(sbuf + TILE_BYTES + wn * 8192, ks, j);
+        else wb[ks][j] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(pb + j * 16 * ROWB));
+      }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
@@ -665,8 +726,10 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         load_lds16(ra, voff[i], sa + i * 8 * ROWB);
-        load_lds16(rb, voff[i], sa + TILE_BYTES + i * 8 * ROWB);
+        if constexpr (!BT) load_lds16(rb, voff[i], sa + TILE_BYTES + i * 8 * ROWB);
       }
+      if constexpr (BT)   // wave w: rows [32 (w >> 2), + 32) of block w & 3
+        load_bt(cur, st, w & 3, 4 * (w >> 2), std::integral_constant<int, 4>{}, lds0 + st * STAGE_BYTES + TILE_BYTES + (w & 3) * 8192);
     }
   }
   wait_vm_all();
@@ -718,6 +781,10 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     const int part = vsplit % sparts;
     const Tile t = decode(full + vsplit / sparts);
     const int k0 = part * nk / sparts, k1 = (part + 1) * nk / sparts;
+    if constexpr (BT) {
+      bto0 = bt_off(t, w & 3, 0);
+      bto1 = bt_off(t, w & 3, 1);
+    }
     __syncthreads();   // the whole-tile loop may still be reading the LDS buffers
     issue(t, k0, k0, k1);
     issue(t, k0 + 1, k0, k1);
@@ -728,16 +795,40 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     // pre-activation variant, whose tiles keep the expert order (and whose main loop has no
     // registers to spare for the branches)
     const bool live = PRE || wm * 128 < t.rows;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (BT) {
+      // one fragment slot, the reads of a stage before its MFMAs (the interleaved schedule below
+      // holds two slots, which with the transposing reads does not fit in the registers); the
+      // partner wave on the SIMD overlaps them
+      for (int s = 0; s < k1 - k0; ++s) {
+        if (s >= 1 && k0 + s + 1 < k1) issue(t, k0 + s + 1, k0, k1);
+        if (live) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) frag_x(0, s, ks, i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) frag_w(0, s, ks, j);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) mfma_16x16x32(acc[i][j], wb[0][j], xa[0][i]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm_all();
+        __syncthreads();
+      }
+    } else {
     if (live) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) frag_x(0, 0, 0, i);
 #pragma unroll
       for (int j = 0; j < 4; ++j) frag_w(0, 0, 0, j);
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < k1 - k0; ++s) {
       if (s >= 1 && k0 + s + 1 < k1) issue(t, k0 + s + 1, k0, k1);
       if (live) {
@@ -769,6 +860,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    }
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                  : "+a"(acc[7][0]), "+a"(acc[7][1]), "+a"(acc[7][2]), "+a"(acc[7][3]),
@@ -785,7 +877,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
     wait_vm_all();
   }
 
-  if (has_narrow) {
+  if constexpr (!BT) if (has_narrow) {
     // slice vsplit % s of leftover tile vsplit / s (XCD-major numbering: the slices of a tile share
     // an XCD and its L2 copy of the tile's rows of A)
     __syncthreads();   // every wave is done with the whole-tile buffers and epilogue areas
@@ -888,9 +980,11 @@ hipError_t launch_gemm_big(const GemmParams& p, bool silu, hipStream_t s) {
   if (p.K < 256) return hipErrorInvalidValue;   // the pipeline needs four K stages per tile
   // reductions under 64 stages always get all 256 workgroups, so that a narrow tail has them
   const int grid = p.K / 64 < 64 ? MAX_WGS : gemm_big_grid(p.max_rows, p.E, p.N);
-  if (silu && p.C2) gemm_big_kernel<true, true><<<grid, 512, 0, s>>>(p);
-  else if (silu) gemm_big_kernel<true, false><<<grid, 512, 0, s>>>(p);
-  else gemm_big_kernel<false, false><<<grid, 512, 0, s>>>(p);
+  if (p.b_kn && silu) return hipErrorInvalidValue;
+  if (silu && p.C2) gemm_big_kernel<true, true, false><<<grid, 512, 0, s>>>(p);
+  else if (silu) gemm_big_kernel<true, false, false><<<grid, 512, 0, s>>>(p);
+  else if (p.b_kn) gemm_big_kernel<false, false, true><<<grid, 512, 0, s>>>(p);
+  else gemm_big_kernel<false, false, false><<<grid, 512, 0, s>>>(p);
   if (p.sk_part && grid == MAX_WGS && p.K / 64 >= 64) {   // tail_parts splits nothing below 64 stages
     // the kernel works out how many tail tiles there are (none: it returns at once)
     if (silu) gemm_tail_kernel<true><<<4 * MAX_WGS, 256, 0, s>>>(p, grid);

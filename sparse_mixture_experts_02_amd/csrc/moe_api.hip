@@ -266,7 +266,7 @@ moe_status_t run_dispatch(const moe_config_t& c, int bt, const int32_t* ids, con
 // `sk` is the split-tail partial-sum region of the caller's workspace (null: no split tail).
 moe_status_t run_gemm_sk(const moe_config_t& c, const void* a, const void* b, void* out, const int32_t* offsets,
                          int n, int kdim, bool silu, void* sk, hipStream_t s, int experts = -1, int rows = -1,
-                         bool int4 = false, void* pre = nullptr, bool first_layer = false) {
+                         bool int4 = false, void* pre = nullptr, bool first_layer = false, bool b_kn = false) {
   if (experts < 0) experts = c.num_experts;
   if (rows < 0) rows = c.T * c.top_k;
   GemmParams p{};
@@ -281,6 +281,7 @@ moe_status_t run_gemm_sk(const moe_config_t& c, const void* a, const void* b, vo
   p.C2 = silu ? pre : nullptr;
   p.offsets = offsets;
   p.sort_split = !silu && !first_layer;
+  p.b_kn = b_kn ? 1 : 0;
   if (int4) {
     p.q4_scale_off = q4_scale_offset((size_t)experts * (size_t)n, kdim);
     MOE_LAUNCH(launch_gemm_q4(p, silu, s));
@@ -288,6 +289,20 @@ moe_status_t run_gemm_sk(const moe_config_t& c, const void* a, const void* b, vo
     MOE_LAUNCH(launch_gemm(p, c.act_dtype == MOE_BF16, silu, s));
   }
   return MOE_OK;
+}
+
+// out = a W^T-free product with the other layer's weights as they are: w is [E, kdim, n] (for dH:
+// W2 [E, d, f]; for dXp: W1 [E, f, d]). The 256 x 256 kernel reads that layout directly; the other
+// GEMM paths take its transpose [E, n, kdim], made here in wt.
+moe_status_t run_gemm_kn(const moe_config_t& c, const void* a, const void* w, void* wt, void* out,
+                         const int32_t* offsets, int n, int kdim, void* sk, hipStream_t s, int experts = -1,
+                         int rows = -1) {
+  const int E = experts < 0 ? c.num_experts : experts;
+  const int R = rows < 0 ? c.T * c.top_k : rows;
+  if (gemm_uses_big(c.act_dtype == MOE_BF16, kdim, R, E))
+    return run_gemm_sk(c, a, w, out, offsets, n, kdim, false, sk, s, experts, rows, false, nullptr, false, true);
+  MOE_LAUNCH(launch_transpose(w, wt, E, kdim, n, (int)act_size(c), s));
+  return run_gemm_sk(c, a, wt, out, offsets, n, kdim, false, sk, s, experts, rows);
 }
 
 moe_status_t run_gemm(const moe_config_t& c, const void* a, const void* b, void* out, const int32_t* offsets,
@@ -339,17 +354,15 @@ moe_status_t expert_ffn_bwd(const moe_config_t& c, const BwdLayout& L, const voi
                             const void* w1, const void* w2, const void* h, const void* dy, void* dxp, float* dw1,
                             float* dw2, void* ws, hipStream_t stream, const void* a_kept = nullptr) {
   const bool bf16 = c.act_dtype == MOE_BF16;
-  const int a = (int)act_size(c), E = c.num_experts, d = c.d_model, f = c.d_ffn;
-  void* w1t = at(ws, L.w1t);   // [E, d, f]
-  void* w2t = at(ws, L.w2t);   // [E, f, d]
+  const int E = c.num_experts, d = c.d_model, f = c.d_ffn;
+  void* w1t = at(ws, L.w1t);   // [E, d, f], when the GEMM path needs the transpose (run_gemm_kn)
+  void* w2t = at(ws, L.w2t);   // [E, f, d], likewise
   void* a1 = at(ws, L.a1);     // [T k, f] pre-activation Xp W1^T
   void* dh = at(ws, L.dh);     // [T k, f] dH, then dA in place
   void* sk = at(ws, L.sk_part);
-  MOE_LAUNCH(launch_transpose(w1, w1t, E, f, d, a, stream));
-  MOE_LAUNCH(launch_transpose(w2, w2t, E, d, f, a, stream));
   if (a_kept) a1 = const_cast<void*>(a_kept);   // the forward's own pre-activation (read only)
   else MOE_TRY(run_gemm_sk(c, xp, w1, a1, offsets, f, d, false, sk, stream, -1, -1, false, nullptr, true));
-  MOE_TRY(run_gemm_sk(c, dy, w2t, dh, offsets, f, d, false, sk, stream));
+  MOE_TRY(run_gemm_kn(c, dy, w2, w2t, dh, offsets, f, d, sk, stream));   // dH = dY W2_e
   GradWParams g{};
   g.E = E;
   g.max_rows = c.T * c.top_k;
@@ -365,7 +378,7 @@ moe_status_t expert_ffn_bwd(const moe_config_t& c, const BwdLayout& L, const voi
   // dA = dH SiLU'(A), in place (an elementwise pass: measured faster than multiplying in the GEMM's
   // epilogue, whose reads of A wait a round trip per 16-row block)
   MOE_LAUNCH(launch_silu_bwd(dh, a1, dh, offsets + E, c.T * c.top_k, f, bf16, stream));
-  MOE_TRY(run_gemm_sk(c, dh, w1t, dxp, offsets, d, f, false, sk, stream));
+  MOE_TRY(run_gemm_kn(c, dh, w1, w1t, dxp, offsets, d, f, sk, stream));   // dXp = dA W1_e
   if (dw1) {   // dW1_e = dA^T Xp over the expert's rows: [f, d]
     g.M = f;
     g.N = d;
@@ -746,7 +759,7 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const float* w
   const BwdLayout L = bwd_layout(c);
   if (fwd_ws_bytes < F.total || ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   const bool bf16 = c.act_dtype == MOE_BF16;
-  const int a = (int)act_size(c), T = c.T, d = c.d_model;
+  const int T = c.T, d = c.d_model;
   void* fw = const_cast<void*>(fwd_ws);   // read only
   const float* logits = (const float*)at(fw, F.logits);
   const int32_t* ids = (const int32_t*)at(fw, F.ids);
@@ -789,10 +802,8 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const float* w
     void* dhs = at(ws, L.dhs);     // [T, fs] dHs, then dAs in place
     void* sk = at(ws, L.sk_part);
     dxs = at(ws, L.dxs);
-    MOE_LAUNCH(launch_transpose(w1_shared, w1st, 1, fs, d, a, stream));
-    MOE_LAUNCH(launch_transpose(w2_shared, w2st, 1, d, fs, a, stream));
     MOE_TRY(run_gemm_sk(c, x, w1_shared, as, sh_off, fs, d, false, sk, stream, 1, T, false, nullptr, true));
-    MOE_TRY(run_gemm_sk(c, d_out, w2st, dhs, sh_off, fs, d, false, sk, stream, 1, T));
+    MOE_TRY(run_gemm_kn(c, d_out, w2_shared, w2st, dhs, sh_off, fs, d, sk, stream, 1, T));
     GradWParams g{};
     g.E = 1;
     g.max_rows = T;
@@ -806,7 +817,7 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const float* w
       MOE_LAUNCH(launch_grad_w(g, bf16, stream));
     }
     MOE_LAUNCH(launch_silu_bwd(dhs, as, dhs, sh_off + 1, T, fs, bf16, stream));
-    MOE_TRY(run_gemm_sk(c, dhs, w1st, dxs, sh_off, d, fs, false, sk, stream, 1, T));
+    MOE_TRY(run_gemm_kn(c, dhs, w1_shared, w1st, dxs, sh_off, d, fs, sk, stream, 1, T));
     if (dw1_shared) {   // dW1s = dAs^T x: [fs, d]
       g.M = fs;
       g.N = d;

@@ -144,6 +144,9 @@ struct GemmParams {
   // products whose bits need not equal a first-layer product of the pre-activation variant (which
   // keeps the expert order): the second layer and the backward's dH and dXp.
   int sort_split;
+  // 256 x 256 kernel, products without activation: B is stored [E, K, N] (the weights of the other
+  // layer as they are) instead of [E, N, K]
+  int b_kn;
 };
 
 struct CombineParams {
