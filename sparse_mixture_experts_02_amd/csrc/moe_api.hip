@@ -72,8 +72,9 @@ Layout layout(const moe_config_t& c) {
   return L;
 }
 
-// Backward-pass workspace: transposed expert weights, the recomputed pre-activation and the
-// gradient of H (turned into the gradient of the pre-activation in place).
+// Backward-pass workspace: transposed expert weights (for the GEMM paths that need them, see
+// run_gemm_kn), the recomputed pre-activation and the gradient of H (turned into the gradient of
+// the pre-activation in place).
 struct BwdLayout {
   size_t w1t, w2t, a1, dh, sk_part, rw_part;
   size_t dy, dwts, dxp, dlogits;              // moe_backward's own intermediates
@@ -291,9 +292,9 @@ moe_status_t run_gemm_sk(const moe_config_t& c, const void* a, const void* b, vo
   return MOE_OK;
 }
 
-// out = a W^T-free product with the other layer's weights as they are: w is [E, kdim, n] (for dH:
-// W2 [E, d, f]; for dXp: W1 [E, f, d]). The 256 x 256 kernel reads that layout directly; the other
-// GEMM paths take its transpose [E, n, kdim], made here in wt.
+// out = a w_e over each expert's rows, with the other layer's weights as they are: w is
+// [E, kdim, n] (for dH: W2 [E, d, f]; for dXp: W1 [E, f, d]). The 256 x 256 kernel reads that
+// layout directly; the other GEMM paths take its transpose [E, n, kdim], made here in wt.
 moe_status_t run_gemm_kn(const moe_config_t& c, const void* a, const void* w, void* wt, void* out,
                          const int32_t* offsets, int n, int kdim, void* sk, hipStream_t s, int experts = -1,
                          int rows = -1) {
