@@ -653,12 +653,23 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(GemmParams p) {
   // (block rows are multiples of 16), so each k-step's reads are one per-lane base plus constants.
   // The base passes through an empty asm so that the compiler keeps one address register per
   // k-step instead of precomputing every read's address.
+  // In the variant that also writes the pre-activation the per-lane base is formed from the lane
+  // id at each call (volatile asm, so it is neither hoisted nor held): held, the two k-step bases
+  // spilled, and each stage's reload waited for every outstanding load (vmcnt(0)), operand
+  // prefetches included.
   const uint32_t fsw = (uint32_t)(fr * ROWB) + (uint32_t)((fc ^ ((fr >> 1) & 7)) << 4);
   auto read_frags = [&](int g) {
     const uint8_t* sbuf = smem + (g & 1) * STAGE_BYTES;
+    uint32_t fsb = fsw;
+    if constexpr (PRE) {
+      int ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      const int lr = ln & 15, lc = ln >> 4;
+      fsb = (uint32_t)(lr * ROWB) + (uint32_t)((lc ^ ((lr >> 1) & 7)) << 4);
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      uint32_t oa = fsw ^ (uint32_t)(ks << 6);   // chunk ks * 4 + fc
+      uint32_t oa = fsb ^ (uint32_t)(ks << 6);   // chunk ks * 4 + fc
       asm volatile("" : "+v"(oa));
       const uint8_t* pa = sbuf + wm * 128 * ROWB + oa;
       const uint8_t* pb = sbuf + TILE_BYTES + wn * 64 * ROWB + oa;
