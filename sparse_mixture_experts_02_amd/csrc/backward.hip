@@ -65,68 +65,85 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdParams p) {
   }
 }
 
-// bf16, top-k <= 2, d a multiple of 512 up to 4096: the same arithmetic in the same order, with
-// every load of the token (its dOut row once, the rows of both slots) issued before the first use.
+typedef unsigned cb_u32x4_t __attribute__((ext_vector_type(4)));
+
+// bf16, top-k <= 2, d = 512 NU (NU = 1, 2, 4 or 8): the same arithmetic in the same order (each
+// lane's terms in column order, then the same butterfly), with every load of the token (its dOut
+// row and the rows of both slots, NU column steps of 16 bytes per lane each) issued before the
+// first use and one explicit wait after them, so that no wait of the compiler's sits between the
+// stores. The loads are unconditional: a slot without a row reads row 0 and its sum is replaced by
+// 0 with a select (the row may hold anything). Y rows are read once, with the non-temporal hint.
+// The two slots' reductions are interleaved, so their cross-lane round trips overlap.
+template <int NU>
 __global__ __launch_bounds__(256) void combine_bwd_k2_kernel(CombineBwdParams p) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= p.T) return;
-  const int k = p.k, d = p.d, nch = d / 512;
-  int rows[2] = {-1, -1};
-  for (int j = 0; j < k; ++j) {
-    const int r = p.row_of[(size_t)t * k + j];
-    rows[j] = (r >= p.max_rows) ? -1 : r;
+  const int k = p.k, d = p.d;
+  int my_row = -1;
+  float my_w = 0.0f;
+  if (lane < k) {
+    my_row = p.row_of[(size_t)t * k + lane];
+    my_w = p.weights[(size_t)t * k + lane];
+    if (my_row >= p.max_rows) my_row = -1;
   }
-  uint4 g[8], y[2][8];
-  const uint16_t* go = (const uint16_t*)p.d_out + (size_t)t * d + lane * 8;
+  const int r0 = __shfl(my_row, 0), r1 = k > 1 ? __shfl(my_row, 1) : -1;
+  const float w0 = __shfl(my_w, 0), w1 = k > 1 ? __shfl(my_w, 1) : 0.0f;
+  const bool h0 = r0 >= 0, h1 = r1 >= 0;
+  const cb_u32x4_t* gp = (const cb_u32x4_t*)((const uint16_t*)p.d_out + (size_t)t * d) + lane;
+  const cb_u32x4_t* y0 = (const cb_u32x4_t*)((const uint16_t*)p.y + (size_t)(h0 ? r0 : 0) * d) + lane;
+  const cb_u32x4_t* y1 = (const cb_u32x4_t*)((const uint16_t*)p.y + (size_t)(h1 ? r1 : 0) * d) + lane;
+  cb_u32x4_t g[NU], a[NU], b[NU];
 #pragma unroll
-  for (int q = 0; q < 8; ++q)
-    if (q < nch) g[q] = *(const uint4*)(go + 512 * q);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    if (j >= k || rows[j] < 0) continue;   // uniform across the wave
-    const uint16_t* yr = (const uint16_t*)p.y + (size_t)rows[j] * d + lane * 8;
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (q < nch) y[j][q] = *(const uint4*)(yr + 512 * q);
+  for (int u = 0; u < NU; ++u) {
+    g[u] = gp[u * 64];
+    a[u] = __builtin_nontemporal_load(y0 + u * 64);
+    if (k > 1) b[u] = __builtin_nontemporal_load(y1 + u * 64);   // uniform (a kernel argument)
   }
-  for (int j = 0; j < k; ++j) {
-    if (rows[j] < 0) {
-      if (lane == 0) p.dweights[(size_t)t * k + j] = 0.0f;
-      continue;
-    }
-    const float w = p.weights[(size_t)t * k + j];
-    float dot = 0.0f;
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): every row has landed
+  cb_u32x4_t* o0 = (cb_u32x4_t*)((uint16_t*)p.dy + (size_t)(h0 ? r0 : 0) * d) + lane;
+  cb_u32x4_t* o1 = (cb_u32x4_t*)((uint16_t*)p.dy + (size_t)(h1 ? r1 : 0) * d) + lane;
+  float dot0 = 0.0f, dot1 = 0.0f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      if (q >= nch) break;
-      const uint32_t wg[4] = {g[q].x, g[q].y, g[q].z, g[q].w};
-      const uint4 yq = j == 0 ? y[0][q] : y[1][q];
-      const uint32_t wy[4] = {yq.x, yq.y, yq.z, yq.w};
-      float gf[8];
+  for (int u = 0; u < NU; ++u) {
+    float gf[8];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        gf[2 * h] = bf16_bits_to_f32(wg[h] & 0xFFFFu);
-        gf[2 * h + 1] = bf16_bits_to_f32(wg[h] >> 16);
-        dot = fmaf(gf[2 * h], bf16_bits_to_f32(wy[h] & 0xFFFFu), dot);
-        dot = fmaf(gf[2 * h + 1], bf16_bits_to_f32(wy[h] >> 16), dot);
+    for (int h = 0; h < 4; ++h) {
+      gf[2 * h] = bf16_bits_to_f32(g[u][h] & 0xFFFFu);
+      gf[2 * h + 1] = bf16_bits_to_f32(g[u][h] >> 16);
+      dot0 = fmaf(gf[2 * h], bf16_bits_to_f32(a[u][h] & 0xFFFFu), dot0);
+      dot0 = fmaf(gf[2 * h + 1], bf16_bits_to_f32(a[u][h] >> 16), dot0);
+      if (k > 1) {
+        dot1 = fmaf(gf[2 * h], bf16_bits_to_f32(b[u][h] & 0xFFFFu), dot1);
+        dot1 = fmaf(gf[2 * h + 1], bf16_bits_to_f32(b[u][h] >> 16), dot1);
       }
-      uint4 o;
-      o.x = pack_bf16x2(w * gf[0], w * gf[1]);
-      o.y = pack_bf16x2(w * gf[2], w * gf[3]);
-      o.z = pack_bf16x2(w * gf[4], w * gf[5]);
-      o.w = pack_bf16x2(w * gf[6], w * gf[7]);
-      *(uint4*)((uint16_t*)p.dy + (size_t)rows[j] * d + lane * 8 + 512 * q) = o;
     }
+    if (h0)
+      o0[u * 64] = cb_u32x4_t{pack_bf16x2(w0 * gf[0], w0 * gf[1]), pack_bf16x2(w0 * gf[2], w0 * gf[3]),
+                              pack_bf16x2(w0 * gf[4], w0 * gf[5]), pack_bf16x2(w0 * gf[6], w0 * gf[7])};
+    if (h1)
+      o1[u * 64] = cb_u32x4_t{pack_bf16x2(w1 * gf[0], w1 * gf[1]), pack_bf16x2(w1 * gf[2], w1 * gf[3]),
+                              pack_bf16x2(w1 * gf[4], w1 * gf[5]), pack_bf16x2(w1 * gf[6], w1 * gf[7])};
+  }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);
-    if (lane == 0) p.dweights[(size_t)t * k + j] = dot;
+  for (int m = 32; m >= 1; m >>= 1) {
+    dot0 += __shfl_xor(dot0, m);
+    dot1 += __shfl_xor(dot1, m);
+  }
+  if (lane == 0) {
+    p.dweights[(size_t)t * k] = h0 ? dot0 : 0.0f;
+    if (k > 1) p.dweights[(size_t)t * k + 1] = h1 ? dot1 : 0.0f;
   }
 }
 
 hipError_t launch_combine_bwd(const CombineBwdParams& p, bool bf16, hipStream_t s) {
   const int grid = (p.T + 3) / 4;
-  if (bf16 && p.k <= 2 && p.d % 512 == 0 && p.d <= 4096) combine_bwd_k2_kernel<<<grid, 256, 0, s>>>(p);
+  const int nu = p.d / 512;
+  const bool k2 = bf16 && p.k <= 2 && p.d % 512 == 0 && (nu == 1 || nu == 2 || nu == 4 || nu == 8);
+  if (k2 && nu == 1) combine_bwd_k2_kernel<1><<<grid, 256, 0, s>>>(p);
+  else if (k2 && nu == 2) combine_bwd_k2_kernel<2><<<grid, 256, 0, s>>>(p);
+  else if (k2 && nu == 4) combine_bwd_k2_kernel<4><<<grid, 256, 0, s>>>(p);
+  else if (k2) combine_bwd_k2_kernel<8><<<grid, 256, 0, s>>>(p);
   else if (bf16) combine_bwd_kernel<true><<<grid, 256, 0, s>>>(p);
   else combine_bwd_kernel<false><<<grid, 256, 0, s>>>(p);
   return hipGetLastError();
@@ -192,7 +209,10 @@ hipError_t launch_transpose(const void* in, void* out, int B, int R, int C, int 
 
 // dA = dH * SiLU'(A), SiLU'(a) = s (1 + a (1 - s)) with s = sigmoid(a), in fp32, one rounding.
 // 16 bytes per thread and step (8 bf16 or 4 fp32 elements; cols is a multiple of 8). Rows past
-// *nrows (the kept rows, read on the device; clamped to max_rows) are left alone.
+// *nrows (the kept rows, read on the device; clamped to max_rows) are left alone. bf16: dsilu_mul
+// and one packed conversion per two results. (Multiplying in the [K, N] product's epilogue
+// instead was measured slower: holding the pre-activation's pieces for a tile there takes
+// registers that kernel does not have, and the spills wait on its operand loads.)
 template <bool BF16>
 __global__ __launch_bounds__(256) void silu_bwd_kernel(const void* dh, const void* a, void* da, const int32_t* nrows,
                                                        int max_rows, int cols) {
@@ -210,15 +230,14 @@ __global__ __launch_bounds__(256) void silu_bwd_kernel(const void* dh, const voi
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if constexpr (BF16) {
-        uint32_t lohi[2];
+        float r[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const float g = bf16_bits_to_f32((gw[q] >> (16 * h)) & 0xFFFFu);
           const float x = bf16_bits_to_f32((xw[q] >> (16 * h)) & 0xFFFFu);
-          const float sg = 1.0f / (1.0f + expf(-x));
-          lohi[h] = f32_to_bf16_bits(g * (sg * (1.0f + x * (1.0f - sg))));
+          r[h] = dsilu_mul(g, x);
         }
-        ow[q] = lohi[0] | (lohi[1] << 16);
+        ow[q] = pack_bf16x2(r[0], r[1]);
       } else {
         const float g = __uint_as_float(gw[q]), x = __uint_as_float(xw[q]);
         const float sg = 1.0f / (1.0f + expf(-x));

@@ -45,6 +45,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// g * SiLU'(x) in fp32, SiLU'(x) = s (1 + x (1 - s)) with s = sigmoid(x) from the hardware exp2
+// and reciprocal (their error is far below the bf16 rounding that follows); the FMA is explicit,
+// so the rounding does not depend on how the compiler contracts the expression.
+__device__ __forceinline__ float dsilu_mul(float g, float x) {
+  const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.44269504088896341f));
+  return g * (s * __builtin_fmaf(x, 1.0f - s, 1.0f));
+}
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
