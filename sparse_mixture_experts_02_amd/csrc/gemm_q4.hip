@@ -43,8 +43,8 @@ constexpr int QNB = QN / (16 * QW);   // 16-feature blocks per wave
 constexpr int QK = 128;           // columns per stage (two scale groups: one per two lane groups)
 constexpr int QAL = QM * QK / 8 / (64 * QW);   // 16-byte activation loads per thread per stage
 constexpr int QPD = 2;            // stages of activations in flight per lane
-// stages of weight codes and scales in flight per lane (4 measured slower than 2: the kernel is
-// bound by its vector instructions, not by the weight stream's latency)
+// stages of weight codes and scales in flight per lane (4 spill at 128 VGPRs and measured slower;
+// with the activations one stage ahead instead, so that they fit, no faster than 2)
 constexpr int WPD = 2;
 
 __device__ __forceinline__ float q4_silu(float v) {
@@ -186,8 +186,13 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(4, 4)))
   // per-block branch sits inside the stage loop
   auto chunk = [&](int m0, int rows, auto nrb_c) {
     constexpr int NRB = decltype(nrb_c)::value;
-    // activation stage: 64 rows x 16 chunks of 8 columns; thread t moves chunks t + 64 QW i. Rows
-    // past the chunk read its last row instead (they only feed outputs that are not stored), and
+    // activation loads per thread and stage that cover the chunk's NRB 16-row blocks (the rows
+    // past them are never read by the MFMAs, so they are neither loaded nor staged)
+    constexpr int QALN = (NRB * 16 * (QK / 8) + 64 * QW - 1) / (64 * QW);
+    static_assert(QALN <= QAL, "the activation stage holds QM rows");
+    // activation stage: up to 64 rows x 16 chunks of 8 columns; thread t moves chunks t + 64 QW i
+    // (i < QALN). Rows past the chunk read its last row instead (they only feed outputs that are
+    // not stored), and
     // stages past the end read the last stage: no load sits behind a branch, so the compiler's
     // load counting stays exact and the prefetch is not drained. The prefetched values are kept in
     // flat arrays indexed by constants only (so they stay in registers).
@@ -218,14 +223,14 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(4, 4)))
 #pragma unroll
     for (int u = 0; u < QPD; ++u)
 #pragma unroll
-      for (int i = 0; i < QAL; ++i) ra[u * QAL + i] = lda(u, i);
+      for (int i = 0; i < QALN; ++i) ra[u * QAL + i] = lda(u, i);
     f32x4_t acc[NRB][QNB];
 #pragma unroll
     for (int i = 0; i < NRB; ++i)
 #pragma unroll
       for (int b = 0; b < QNB; ++b) acc[i][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < QAL; ++i) sta(0, i, ra[i]);
+    for (int i = 0; i < QALN; ++i) sta(0, i, ra[i]);
     __syncthreads();
     static_assert(WPD % QPD == 0, "the unrolled loop covers whole periods of both rings");
     for (int s0 = 0; s0 < nk; s0 += WPD) {
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(4, 4)))
         const int s = s0 + uw;   // s % WPD == uw (nk is a multiple of WPD)
         const int u = uw % QPD;  // s % QPD
 #pragma unroll
-        for (int i = 0; i < QAL; ++i) ra[u * QAL + i] = lda(s + QPD, i);
+        for (int i = 0; i < QALN; ++i) ra[u * QAL + i] = lda(s + QPD, i);
         const uint16_t* a = sA[s & 1];
 #pragma unroll
         for (int ks = 0; ks < QK / 32; ++ks) {
@@ -260,7 +265,7 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(4, 4)))
         // copy of the last stage into the buffer nobody reads any more)
         const int un = (u + 1) % QPD;
 #pragma unroll
-        for (int i = 0; i < QAL; ++i) sta((s + 1) & 1, i, ra[un * QAL + i]);
+        for (int i = 0; i < QALN; ++i) sta((s + 1) & 1, i, ra[un * QAL + i]);
         __syncthreads();
       }
     }
