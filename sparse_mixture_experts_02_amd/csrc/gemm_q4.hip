@@ -192,10 +192,9 @@ __global__ __launch_bounds__(64 * QW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     static_assert(QALN <= QAL, "the activation stage holds QM rows");
     // activation stage: up to 64 rows x 16 chunks of 8 columns; thread t moves chunks t + 64 QW i
     // (i < QALN). Rows past the chunk read its last row instead (they only feed outputs that are
-    // not stored), and
-    // stages past the end read the last stage: no load sits behind a branch, so the compiler's
-    // load counting stays exact and the prefetch is not drained. The prefetched values are kept in
-    // flat arrays indexed by constants only (so they stay in registers).
+    // not stored), and stages past the end read the last stage: no load sits behind a branch, so
+    // the compiler's load counting stays exact and the prefetch is not drained. The prefetched
+    // values are kept in flat arrays indexed by constants only (so they stay in registers).
     auto lda = [&](int st, int i) -> uint4 {
       st = min(st, nk - 1);
       const int c = tid + 64 * QW * i, r = min(c >> 4, rows - 1), ch = c & 15;
