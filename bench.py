@@ -5,12 +5,13 @@
 
 One step = one moe_forward call (router, dispatch, both grouped GEMMs, combine, aux loss) over
 the workload's seeded synthetic batch, with inputs already resident in HBM. W untimed steps,
-then exactly K timed steps between two device synchronisations, each after a 1 GiB write that
-evicts the L2s and the Infinity Cache, timed by HIP events around the step alone (the
-throughput: cold cache). Then K warm steps back to back between two synchronisations (reported
-as warm_cache), then K more with HIP events recorded by the library between its kernels on the
-launch stream (the per-kernel durations and the roofline; the events themselves add a few
-microseconds per step). Then the backward leg (unless --no-backward): moe_backward timed over
+then exactly K timed steps between two device synchronisations, each after a read of a 1 GiB
+buffer that evicts the L2s and the Infinity Cache, timed by HIP events around the step alone
+(the throughput: cold cache; the flush reads, so the caches hold only clean lines of an
+unrelated buffer and no write-back of the flush's own data falls inside the timed step). Then K
+warm steps back to back between two synchronisations (reported as warm_cache), then K more with
+HIP events recorded by the library between its kernels on the launch stream (the per-kernel
+durations and the roofline; the events themselves add a few microseconds per step). Then the backward leg (unless --no-backward): moe_backward timed over
 W + K calls, in the layer's own configuration and with keep_preact (the training setting, whose
 forward is timed too).
 
@@ -297,15 +298,17 @@ def main():
     torch.cuda.synchronize()
     cold_ms = None
     if not args.no_cold_cache:
-        # the timed steps, cold cache: before each step a 1 GiB write evicts the L2s and the
-        # 256 MB Infinity Cache, and HIP events on the launch stream bracket the step alone (the
-        # flush is outside them); exactly K steps between two device synchronisations
-        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        # the timed steps, cold cache: before each step a read of 1 GiB (a reduction over a
+        # buffer written once here) evicts the L2s and the 256 MB Infinity Cache, and HIP events
+        # on the launch stream bracket the step alone (the flush is outside them); exactly K steps
+        # between two device synchronisations. The flush reads rather than writes: written, its
+        # dirty lines were written back during the next step (measured 35-40 us of the main step)
+        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         torch.cuda.synchronize()
         for i in range(args.steps):
-            flush.fill_(float(i))
+            flush_max = flush.amax()   # noqa: F841 (read for its cache effect only)
             ev0[i].record()
             step()
             ev1[i].record()
@@ -398,7 +401,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
-        "timing": ("cold cache: mean of K steps, each after a 1 GiB write that evicts the L2s and the Infinity "
+        "timing": ("cold cache: mean of K steps, each after a 1 GiB read that evicts the L2s and the Infinity "
                    "Cache, timed by HIP events on the launch stream around the step alone"
                    if cold_ms is not None else "warm cache: K steps back to back between two synchronisations"),
         "ms_per_step_with_kernel_events": ms_per_step_events,
@@ -432,7 +435,7 @@ def main():
             "ms_mean": float(cold_ms.mean()), "ms_median": float(np.median(cold_ms)),
             "ms_p10": float(np.percentile(cold_ms, 10)), "ms_p90": float(np.percentile(cold_ms, 90)),
             "tokens_per_s_median": T / (float(np.median(cold_ms)) * 1e-3),
-            "protocol": "1 GiB buffer written before each step (outside the timed events)"},
+            "protocol": "1 GiB buffer read before each step (outside the timed events)"},
         "warm_cache": {"ms_per_step": warm_ms_per_step, "tokens_per_s": T / (warm_ms_per_step * 1e-3),
                        "protocol": "K steps back to back between two device synchronisations"},
         "warm_cache_events": {"ms_median": float(np.median(warm_ms)), "ms_p10": float(np.percentile(warm_ms, 10)),
