@@ -8,7 +8,8 @@ the workload's seeded synthetic batch, with inputs already resident in HBM. W un
 then exactly K timed steps between two device synchronisations, each after a read of a 1 GiB
 buffer that evicts the L2s and the Infinity Cache, timed by HIP events around the step alone
 (the throughput: cold cache; the flush reads, so the caches hold only clean lines of an
-unrelated buffer and no write-back of the flush's own data falls inside the timed step). Then K
+unrelated buffer: after a written flush the step measured 35-40 us slower on the main layer,
+presumably from the write-back of the flush's dirty lines inside it). Then K
 warm steps back to back between two synchronisations (reported as warm_cache), then K more with
 HIP events recorded by the library between its kernels on the launch stream (the per-kernel
 durations and the roofline; the events themselves add a few microseconds per step). Then the backward leg (unless --no-backward): moe_backward timed over
@@ -301,8 +302,9 @@ def main():
         # the timed steps, cold cache: before each step a read of 1 GiB (a reduction over a
         # buffer written once here) evicts the L2s and the 256 MB Infinity Cache, and HIP events
         # on the launch stream bracket the step alone (the flush is outside them); exactly K steps
-        # between two device synchronisations. The flush reads rather than writes: written, its
-        # dirty lines were written back during the next step (measured 35-40 us of the main step)
+        # between two device synchronisations. The flush reads rather than writes: after a
+        # written flush the step measured 35-40 us slower on the main layer (presumably the
+        # write-back of the flush's dirty lines during the step)
         flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
