@@ -56,6 +56,8 @@ def parse():
                     help="kept for older command lines: the backward leg runs by default")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward leg (moe_backward timed the same way, in a 'backward' object)")
+    ap.add_argument("--no-vendor-gemm", action="store_true",
+                    help="skip the vendor dense-GEMM reference (torch.matmul on the two layers' shapes)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, run one elementwise copy of this many MiB (a known-size "
                          "kernel to scale hardware byte counters against)")
@@ -257,6 +259,40 @@ def bench_backward(args, w, cfg, dev, ws, N: int) -> dict:
             "steps": args.steps, "warmup": args.warmup}
 
 
+def vendor_gemm(N: int, d: int, f: int, steps: int) -> dict:
+    """The vendor library's dense GEMM (torch.matmul, which runs hipBLASLt) on the two layers'
+    shapes, for context beside the grouped kernels: [N, d] x [d, f] and [N, f] x [f, d] in bf16 with
+    fp32 accumulation, the operands drawn like the layer's (activations N(0, 1), weights
+    N(0, 0.02^2), the second product's left operand the SiLU of the first's output), one weight
+    matrix for all N rows (the grouped kernels use one per expert segment). Warm cache, K
+    launches back to back between two HIP events. Not part of the layer."""
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    a = torch.randn(N, d, device="cuda", generator=gen).to(torch.bfloat16)
+    w1 = (torch.randn(d, f, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+    w2 = (torch.randn(f, d, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+    h = torch.nn.functional.silu(torch.matmul(a, w1).float()).to(torch.bfloat16)
+    res = {"library": "torch.matmul (hipBLASLt), dense, one weight matrix",
+           "protocol": "warm cache: K launches back to back between two HIP events"}
+    for name, x, wt in (("gemm1_shape", a, w1), ("gemm2_shape", h, w2)):
+        for _ in range(3):
+            torch.matmul(x, wt)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            torch.matmul(x, wt)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tflops = 2.0 * N * x.shape[1] * wt.shape[1] / (ms * 1e-3) / 1e12
+        res[name] = {"m_n_k": [N, int(wt.shape[1]), int(x.shape[1])], "ms": ms, "tflops": tflops,
+                     "frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS}
+    del a, w1, w2, h
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -449,6 +485,8 @@ def main():
     }
     if not args.no_backward:
         line["backward"] = bench_backward(args, w, cfg, dev, ws, N)
+    if not args.no_vendor_gemm and w.dtype == "bf16" and w.weight_dtype is None and N > 0:
+        line["vendor_gemm"] = vendor_gemm(N, w.d_model, w.d_ffn, args.steps)
     if not args.no_cpu_baseline:
         # one more forward with the routing captured (not timed), for the oracle's parity check
         gids = torch.empty(w.T, w.top_k, dtype=torch.int32, device="cuda")
