@@ -161,10 +161,12 @@ __device__ __forceinline__ int narrow_parts(int total, int G, int nk, bool tiny)
 }
 
 // The m-tiles are numbered expert by expert (each expert's from its first row), or, when that
-// makes the partial last round of a reduction under 64 stages hold between 65 and 128 tiles of at
-// most 128 rows each (see narrow_parts), every expert's full 256-row m-tiles first (expert order)
-// and then the experts' partial last m-tiles, most rows first (ties: lower expert first), so that
-// the partial last round holds the emptiest ones. (Sorting in every case measured slower where
+// makes the partial last round of a reduction under 64 stages hold at most 128 tiles, all of them
+// partial m-tiles of at most 128 rows (see narrow_parts), every expert's full 256-row m-tiles
+// first (expert order) and then the experts' partial last m-tiles, most rows first (ties: lower
+// expert first), so that the partial last round holds the emptiest ones: its narrow slices then
+// fetch fewer rows of A (small_bf16's GEMM1, 8 tiles left over as 32-feature slices: the 86-row
+// m-tile instead of a 247-row one, 40.7 -> 37.7 us). (Sorting in every case measured slower where
 // many experts have partial m-tiles: a group of m-tiles from different experts shares no weight
 // rows in L2.) The order of the partial m-tiles is formed once per workgroup by one wave (lane e
 // ranks expert e's remainder) into porder[]. seg: the clamped segment bounds in LDS.
@@ -190,7 +192,7 @@ __device__ __forceinline__ int sorted_mf(int total, int MT, int MF0, int NT, int
                                          const int* seg, const int* porder) {
   const int R = total % G;
   if (G != MAX_WGS || MF0 == MT || R == 0 || 2 * R > G) return 0;
-  if (nk < 64 ? 4 * R <= G : !split) return 0;
+  if (nk >= 64 && !split) return 0;
   // the partial m-tiles that do not fit in the leftover round end up in groups of m-tiles from
   // different experts inside the whole rounds (no weight rows shared in L2): at most one group
   if ((MT - MF0) * NT - R > GROUP_M * NT) return 0;
