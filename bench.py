@@ -5,16 +5,16 @@
 
 One step = one moe_forward call (router, dispatch, both grouped GEMMs, combine, aux loss) over
 the workload's seeded synthetic batch, with inputs already resident in HBM. W untimed steps,
-then exactly K timed steps between two device synchronisations, each after a read of a 1 GiB
-buffer that evicts the L2s and the Infinity Cache, timed by HIP events around the step alone
-(the throughput: cold cache; the flush reads, so the caches hold only clean lines of an
-unrelated buffer: after a written flush the step measured 35-40 us slower on the main layer,
-presumably from the write-back of the flush's dirty lines inside it). Then K
-warm steps back to back between two synchronisations (reported as warm_cache), then K more with
-HIP events recorded by the library between its kernels on the launch stream (the per-kernel
-durations and the roofline; the events themselves add a few microseconds per step). Then the backward leg (unless --no-backward): moe_backward timed over
-W + K calls, in the layer's own configuration and with keep_preact (the training setting, whose
-forward is timed too).
+then exactly K timed steps between two device synchronisations, each after a 1 GiB write that
+evicts the L2s and the Infinity Cache, timed by HIP events around the step alone (the
+throughput: cold cache); K more after a read of that buffer instead are reported apart
+(cold_cache_read_flush: then no write-back of the flush's dirty lines falls inside the step).
+Then K warm steps back to back between two synchronisations (reported as warm_cache), then K
+more with HIP events recorded by the library between its kernels on the launch stream (the
+per-kernel durations and the roofline; the events themselves add a few microseconds per step).
+Then the backward leg (unless --no-backward): moe_backward timed over W + K calls, in the
+layer's own configuration and with keep_preact (the training setting, whose forward is timed
+too).
 
 Prints one JSON line: tokens/s of the whole layer, the roofline of the dominant kernel (the
 slower grouped GEMM: MFMA bound on the large workloads, HBM bound when a few tokens per expert
@@ -333,25 +333,32 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    cold_ms = None
+    cold_ms = cold_read_ms = None
     if not args.no_cold_cache:
-        # the timed steps, cold cache: before each step a read of 1 GiB (a reduction over a
-        # buffer written once here) evicts the L2s and the 256 MB Infinity Cache, and HIP events
-        # on the launch stream bracket the step alone (the flush is outside them); exactly K steps
-        # between two device synchronisations. The flush reads rather than writes: after a
-        # written flush the step measured 35-40 us slower on the main layer (presumably the
-        # write-back of the flush's dirty lines during the step)
-        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        for i in range(args.steps):
-            flush_max = flush.amax()   # noqa: F841 (read for its cache effect only)
-            ev0[i].record()
-            step()
-            ev1[i].record()
-        torch.cuda.synchronize()
-        cold_ms = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)])
+        # the timed steps, cold cache: before each step a 1 GiB write evicts the L2s and the
+        # 256 MB Infinity Cache, and HIP events on the launch stream bracket the step alone (the
+        # flush is outside them); exactly K steps between two device synchronisations. Then K
+        # more the same way after a read of the buffer instead (reported apart): after the write
+        # the step also writes back the flush's dirty lines, ~35-40 us of the main layer's step
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+
+        def cold_steps(write: bool):
+            ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+            ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            for i in range(args.steps):
+                if write:
+                    flush.fill_(float(i))
+                else:
+                    flush.amax()   # read for its cache effect only
+                ev0[i].record()
+                step()
+                ev1[i].record()
+            torch.cuda.synchronize()
+            return np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)])
+
+        cold_ms = cold_steps(True)
+        cold_read_ms = cold_steps(False)
         del flush
     # warm cache: K steps back to back between two device synchronisations (forward passes only:
     # recording the per-kernel events costs a few microseconds per event on the GPU timeline)
@@ -439,7 +446,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
-        "timing": ("cold cache: mean of K steps, each after a 1 GiB read that evicts the L2s and the Infinity "
+        "timing": ("cold cache: mean of K steps, each after a 1 GiB write that evicts the L2s and the Infinity "
                    "Cache, timed by HIP events on the launch stream around the step alone"
                    if cold_ms is not None else "warm cache: K steps back to back between two synchronisations"),
         "ms_per_step_with_kernel_events": ms_per_step_events,
@@ -473,7 +480,12 @@ def main():
             "ms_mean": float(cold_ms.mean()), "ms_median": float(np.median(cold_ms)),
             "ms_p10": float(np.percentile(cold_ms, 10)), "ms_p90": float(np.percentile(cold_ms, 90)),
             "tokens_per_s_median": T / (float(np.median(cold_ms)) * 1e-3),
-            "protocol": "1 GiB buffer read before each step (outside the timed events)"},
+            "protocol": "1 GiB buffer written before each step (outside the timed events)"},
+        "cold_cache_read_flush": None if cold_read_ms is None else {
+            "ms_mean": float(cold_read_ms.mean()), "ms_median": float(np.median(cold_read_ms)),
+            "tokens_per_s": T / (float(cold_read_ms.mean()) * 1e-3),
+            "protocol": "the same, after a read of the 1 GiB buffer instead of a write (the caches then "
+                        "hold no dirty lines of the flush, whose write-back otherwise falls inside the step)"},
         "warm_cache": {"ms_per_step": warm_ms_per_step, "tokens_per_s": T / (warm_ms_per_step * 1e-3),
                        "protocol": "K steps back to back between two device synchronisations"},
         "warm_cache_events": {"ms_median": float(np.median(warm_ms)), "ms_p10": float(np.percentile(warm_ms, 10)),
