@@ -497,7 +497,10 @@ def main():
     }
     if not args.no_backward:
         line["backward"] = bench_backward(args, w, cfg, dev, ws, N)
-    if not args.no_vendor_gemm and w.dtype == "bf16" and w.weight_dtype is None and N > 0:
+    # (only where the grouped kernels are matrix-core bound: with a few rows per expert the layer
+    # streams E weight matrices where the dense product reads one)
+    if (not args.no_vendor_gemm and w.dtype == "bf16" and w.weight_dtype is None and N > 0
+            and line["roofline"]["bound"] == "mfma"):
         line["vendor_gemm"] = vendor_gemm(N, w.d_model, w.d_ffn, args.steps)
     if not args.no_cpu_baseline:
         # one more forward with the routing captured (not timed), for the oracle's parity check
