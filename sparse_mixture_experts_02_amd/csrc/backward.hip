@@ -454,22 +454,52 @@ __global__ __launch_bounds__(512, 1) void grad_w_bf16_kernel(GradWParams p) {
   }
   // lane holds rows m0 + 128 gr + 16 mi + 4 fg .. + 3 of column n0 + 64 wn + 16 ni + fr
   float* __restrict__ G = p.G + (size_t)e * p.M * p.N;
+  if (p.splits == 2) {
 #pragma unroll
-  for (int mi = 0; mi < 8; ++mi)
+    for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int n = n0 + 64 * wn + 16 * ni + fr;
+      for (int ni = 0; ni < 4; ++ni) {
+        const int n = n0 + 64 * wn + 16 * ni + fr;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int m = m0 + 128 * gr + 16 * mi + 4 * fg + t;
-        if (m < p.M && n < p.N) {
+        for (int t = 0; t < 4; ++t) {
+          const int m = m0 + 128 * gr + 16 * mi + 4 * fg + t;
           // two halves: each adds its partial sum to the zeroed G (0 + a is exact and a + b
           // commutes, so the result does not depend on which half lands first)
-          if (p.splits == 2) atomicAdd(&G[(size_t)m * p.N + n], acc[mi][ni][t]);
-          else G[(size_t)m * p.N + n] = acc[mi][ni][t];
+          if (m < p.M && n < p.N) atomicAdd(&G[(size_t)m * p.N + n], acc[mi][ni][t]);
         }
       }
+    return;
+  }
+  // Row-major stores through LDS, one 16-row block at a time: the lane's four values (four rows
+  // of one column) go to a per-wave area, and each lane reads back four consecutive columns of
+  // one row, so that a store instruction covers 4 rows x 256 contiguous bytes (stored straight
+  // from the accumulator layout, an instruction covered 4 rows x 64 bytes with 4-byte stores:
+  // measured ~68 us of each main-size launch). Two areas per wave alternate between blocks (LDS
+  // operations of one wave complete in order, so a block's reads see its writes and the next
+  // block but one may overwrite them). Row pitch 68 floats: the four row groups of a write fall
+  // on different banks. The stage buffers are free once every wave is past its last fragment
+  // read.
+  __syncthreads();
+  constexpr int EPF = 68;
+  static_assert(8 * 2 * 16 * EPF * 4 <= 2 * GW_STAGE_BYTES, "the epilogue areas lie in the stage buffers");
+  float* const ep = (float*)lds + w * 2 * 16 * EPF;
+  const int rr = lane >> 4, rc = (lane & 15) * 4;   // read-back: row within 4, first column
+  const int n = n0 + 64 * wn + rc;
+#pragma unroll
+  for (int mi = 0; mi < 8; ++mi) {
+    float* const a = ep + (mi & 1) * 16 * EPF;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) a[(4 * fg + t) * EPF + 16 * ni + fr] = acc[mi][ni][t];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * i + rr;
+      const f32x4_t v = *(const f32x4_t*)(a + row * EPF + rc);
+      const int m = m0 + 128 * gr + 16 * mi + row;
+      if (m < p.M && n < p.N) *(f32x4_t*)(G + (size_t)m * p.N + n) = v;   // N % 4 == 0: all or none
     }
+  }
 }
 
 // fp32: one 128 x 128 output tile of one expert per workgroup; 4 waves in 2 x 2, each 64 x 64 =
