@@ -167,11 +167,19 @@ bool gemm_uses_big(bool bf16, int K, int max_rows, int E) {
   return bf16 && K % 64 == 0 && K >= 256 && max_rows >= 256 * E;
 }
 
+// The weight-streaming kernel: bf16, K a multiple of 64, at most 64 rows per expert on average
+// (and not the 256 x 256 kernel's case).
+bool gemm_uses_stream(bool bf16, int K, int max_rows, int E) {
+  return !gemm_uses_big(bf16, K, max_rows, E) && bf16 && K % 64 == 0 && max_rows <= 64 * E;
+}
+
 hipError_t launch_gemm(const GemmParams& p, bool bf16, bool silu, hipStream_t s) {
   // bf16 with K a multiple of 64 (at least 128): on average at least 256 rows per expert, 256 x 256
-  // tiles; at most 64, one pass over the expert weights
+  // tiles; at most 64, one pass over the expert weights. Weights stored [K, N] (p.b_kn) are read by
+  // those two kernels only.
   if (gemm_uses_big(bf16, p.K, p.max_rows, p.E)) return launch_gemm_big(p, silu, s);
-  if (bf16 && p.K % 64 == 0 && p.max_rows <= 64 * p.E) return launch_gemm_stream(p, silu, s);
+  if (gemm_uses_stream(bf16, p.K, p.max_rows, p.E)) return launch_gemm_stream(p, silu, s);
+  if (p.b_kn) return hipErrorInvalidValue;
   dim3 grid(gemm_max_mtiles(p.max_rows, p.E), (p.N + GEMM_BN - 1) / GEMM_BN);
   if (bf16) {
     if (silu) gemm_kernel<true, true><<<grid, 256, 0, s>>>(p);

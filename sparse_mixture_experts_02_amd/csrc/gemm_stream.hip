@@ -65,9 +65,24 @@ template <int N>
 __device__ __forceinline__ void sb_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+
+typedef short sb_v4i16 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, lane s reads 8 bytes of
+// row r0 + s / 4 at column c0 + 4 (s % 4), and lane i receives column c0 + i of rows r0 .. r0 + 3.
+__device__ __forceinline__ sb_v4i16 sb_read_tr(const uint8_t* q) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) sb_v4i16*)(__attribute__((address_space(3))) const uint8_t*)q);
+}
 }  // namespace
 
-template <bool SILU>
+// BT: the weights are stored [E][K][N] (the backward's dH and dXp read W2 and W1 as they are).
+// A stage of the block is then 64 k-rows x the workgroup's 64 features, 128 bytes of each row,
+// loaded as the [N, K] block's 64 rows are; the 32-byte quarters of k-row r are XOR-swizzled by
+// f(r) = ((r >> 1) & 1) | (((r >> 3) & 1) << 1), and wave w reads its 16 features as MFMA operands
+// with two transposing reads per operand (8 consecutive k per lane), as the 256 x 256 kernel's
+// [K, N] variant does. Features past N get an offset outside the resource (zeros).
+template <bool SILU, bool BT>
 __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[SB_STAGES * SB_STAGE_BYTES];
 
@@ -92,6 +107,8 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(GemmParams p) {
   const int rowbytes = p.K * 2, nk = p.K / 64;
   const uint8_t* __restrict__ A = (const uint8_t*)p.A;
   const uint8_t* __restrict__ Bw = (const uint8_t*)p.B + ((size_t)e * N + n0) * rowbytes;
+  const uint32_t nb2 = (uint32_t)N * 2u;   // BT: bytes of a [K, N] row
+  const uint8_t* __restrict__ Bt = (const uint8_t*)p.B + (size_t)e * (size_t)p.K * nb2 + (size_t)n0 * 2u;
   uint16_t* __restrict__ C = (uint16_t*)p.C;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 
@@ -104,9 +121,18 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(GemmParams p) {
     const bool a = j < SB_M / 32;
     const int jj = a ? j : j - SB_M / 32;
     const int r = (a ? w * (SB_M / 4) : w * (SB_N / 4)) + jj * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ ((r >> 1) & 7);   // the slot this lane fills holds that chunk
-    voff[j] = (uint32_t)r * (uint32_t)rowbytes + chunk * 16;
+    if (BT && !a) {   // k-row r of the stage, slot lane % 8 holds chunk (lane % 8) ^ 2 f(r)
+      const int chunk = (lane & 7) ^ ((((r >> 1) & 1) | (((r >> 3) & 1) << 1)) << 1);
+      voff[j] = 8 * chunk < cols ? (uint32_t)r * nb2 + (uint32_t)chunk * 16u : 0x80000000u;
+    } else {
+      const int chunk = (lane & 7) ^ ((r >> 1) & 7);   // the slot this lane fills holds that chunk
+      voff[j] = (uint32_t)r * (uint32_t)rowbytes + chunk * 16;
+    }
   }
+  // BT fragment reads: lane (fr, fc) of wave w reads k-rows 8 fc + fr / 4 (+ 4) of its k-step,
+  // bytes 8 (fr % 4) of quarter w ^ f(row)
+  const uint32_t bt_rd = (uint32_t)((8 * fc + (fr >> 2)) * 128 + 8 * (fr & 3) + 32 * ((fr >> 3) | ((fc & 1) << 1))) ^
+                         (uint32_t)(32 * w);
 
   for (int m0 = lo; m0 < hi; m0 += SB_M) {
     const int rows = min(hi - m0, SB_M);
@@ -115,7 +141,8 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(GemmParams p) {
       const int st = min(kt, nk - 1);
       const uint32_t base = lds0 + (kt % SB_STAGES) * SB_STAGE_BYTES;
       const i32x4_t rsa = sb_rsrc(A + (size_t)m0 * rowbytes + st * SB_ROWB, (uint32_t)rows * rowbytes);
-      const i32x4_t rsb = sb_rsrc(Bw + st * SB_ROWB, (uint32_t)cols * rowbytes);
+      const i32x4_t rsb = BT ? sb_rsrc(Bt + (size_t)st * 64u * nb2, 64u * nb2)
+                             : sb_rsrc(Bw + st * SB_ROWB, (uint32_t)cols * rowbytes);
 #pragma unroll
       for (int j = 0; j < SB_LOADS; ++j) {
         const bool a = j < SB_M / 32;
@@ -143,8 +170,15 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(GemmParams p) {
       for (int ks = 0; ks < 2; ++ks) {
         bf16x8_t xa[4], wb[SB_NB];
 #pragma unroll
-        for (int b = 0; b < SB_NB; ++b)
-          wb[b] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(sb + sb_off(w * (SB_N / 4) + b * 16 + fr, ks * 4 + fc)));
+        for (int b = 0; b < SB_NB; ++b) {
+          if constexpr (BT) {
+            const uint8_t* q = sb + ks * 32 * 128 + bt_rd;
+            const sb_v4i16 lo = sb_read_tr(q), hi = sb_read_tr(q + 4 * 128);
+            wb[b] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          } else {
+            wb[b] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(sb + sb_off(w * (SB_N / 4) + b * 16 + fr, ks * 4 + fc)));
+          }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           xa[i] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(sa + sb_off(i * 16 + fr, ks * 4 + fc)));
@@ -189,8 +223,10 @@ int gemm_stream_grid(int E, int N) { return E * ((N + SB_N - 1) / SB_N); }
 
 hipError_t launch_gemm_stream(const GemmParams& p, bool silu, hipStream_t s) {
   const int grid = gemm_stream_grid(p.E, p.N);
-  if (silu) gemm_stream_kernel<true><<<grid, 256, 0, s>>>(p);
-  else gemm_stream_kernel<false><<<grid, 256, 0, s>>>(p);
+  if (p.b_kn && silu) return hipErrorInvalidValue;   // [K, N] weights: the backward's plain products
+  if (p.b_kn) gemm_stream_kernel<false, true><<<grid, 256, 0, s>>>(p);
+  else if (silu) gemm_stream_kernel<true, false><<<grid, 256, 0, s>>>(p);
+  else gemm_stream_kernel<false, false><<<grid, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 

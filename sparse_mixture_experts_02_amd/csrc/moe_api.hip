@@ -293,14 +293,16 @@ moe_status_t run_gemm_sk(const moe_config_t& c, const void* a, const void* b, vo
 }
 
 // out = a w_e over each expert's rows, with the other layer's weights as they are: w is
-// [E, kdim, n] (for dH: W2 [E, d, f]; for dXp: W1 [E, f, d]). The 256 x 256 kernel reads that
-// layout directly; the other GEMM paths take its transpose [E, n, kdim], made here in wt.
+// [E, kdim, n] (for dH: W2 [E, d, f]; for dXp: W1 [E, f, d]). The 256 x 256 and weight-streaming
+// kernels read that layout directly; the other GEMM path takes its transpose [E, n, kdim], made
+// here in wt.
 moe_status_t run_gemm_kn(const moe_config_t& c, const void* a, const void* w, void* wt, void* out,
                          const int32_t* offsets, int n, int kdim, void* sk, hipStream_t s, int experts = -1,
                          int rows = -1) {
   const int E = experts < 0 ? c.num_experts : experts;
   const int R = rows < 0 ? c.T * c.top_k : rows;
-  if (gemm_uses_big(c.act_dtype == MOE_BF16, kdim, R, E))
+  const bool bf16 = c.act_dtype == MOE_BF16;
+  if (gemm_uses_big(bf16, kdim, R, E) || gemm_uses_stream(bf16, kdim, R, E))
     return run_gemm_sk(c, a, w, out, offsets, n, kdim, false, sk, s, experts, rows, false, nullptr, false, true);
   MOE_LAUNCH(launch_transpose(w, wt, E, kdim, n, (int)act_size(c), s));
   return run_gemm_sk(c, a, wt, out, offsets, n, kdim, false, sk, s, experts, rows);

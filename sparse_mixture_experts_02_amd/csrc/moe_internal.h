@@ -216,6 +216,7 @@ int gemm_big_grid(int max_rows, int E, int N);
 size_t gemm_big_part_bytes();
 // whether launch_gemm takes the 256 x 256 kernel for these operands
 bool gemm_uses_big(bool bf16, int K, int max_rows, int E);
+bool gemm_uses_stream(bool bf16, int K, int max_rows, int E);
 hipError_t launch_gemm_big(const GemmParams& p, bool silu, hipStream_t s);
 int gemm_stream_grid(int E, int N);
 hipError_t launch_gemm_stream(const GemmParams& p, bool silu, hipStream_t s);
