@@ -267,8 +267,8 @@ def test_moe_backward_whole_layer(name):
 SAMPLED_CASES = {
     "main": BASE,
     # d 4096: the dH GEMM (K = d, 64 stages) and the recomputed pre-activation have ~320 tiles, so
-    # their last partial round is split in two K halves and the tail kernel applies SiLU' (dA =
-    # dH SiLU'(A)) to the summed parts
+    # their last partial round is split in two K halves; the tail kernel sums the parts (and, for
+    # the pre-activation, stores the sum and applies SiLU to it)
     "split_dh_d4096": derived(BASE, name="split_dh_d4096", T=4200, d_model=4096, d_ffn=2048),
 }
 
