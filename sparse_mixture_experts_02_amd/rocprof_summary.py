@@ -125,9 +125,8 @@ def main(argv=None):
     scale = {}
     if a.calib_bytes > 0:
         for cname in ("FETCH_SIZE", "WRITE_SIZE"):
-            vals = [v for (k, n), vs in c.items() if n == cname and a.calib_kernel in k for v in vs]
-            if vals:
-                counted = sum(vals) / len(vals) * 1024.0       # the counters are in KiB
+            counted = _calib_counted(c, cname, a.calib_kernel)
+            if counted is not None:
                 scale[cname] = a.calib_bytes / counted if counted > 0 else float("nan")
                 print(f"calibration: {cname} reads {counted / 2**20:.1f} MiB for a kernel that moves "
                       f"{a.calib_bytes / 2**20:.1f} MiB -> scale {scale[cname]:.3f}")
@@ -139,12 +138,20 @@ def main(argv=None):
     return 0
 
 
+def _calib_counted(c: dict, cname: str, calib_kernel: str):
+    """Bytes that counter `cname` reports for the calibration copy, or None if the run has none.
+    The copy is the largest dispatch of its elementwise kernel: the program may launch the same
+    kernel for smaller scalar multiplies of its own, which must not enter the scale."""
+    vals = [v for (k, n), vs in c.items() if n == cname and calib_kernel in k for v in vs]
+    return max(vals) * 1024.0 if vals else None   # the counters are in KiB
+
+
 def _calibrated_means(d: str, cname: str, calib_kernel: str, calib_bytes: float) -> dict:
     c = counters(d)
-    vals = [v for (k, n), vs in c.items() if n == cname and calib_kernel in k for v in vs]
-    if not vals:
+    counted = _calib_counted(c, cname, calib_kernel)
+    if counted is None:
         raise SystemExit(f"no calibration dispatch ({calib_kernel}) with {cname} in {d}")
-    scale = calib_bytes / (sum(vals) / len(vals) * 1024.0)
+    scale = calib_bytes / counted
     return {k: sum(vs) / len(vs) * 1024.0 * scale for (k, n), vs in c.items() if n == cname}, scale
 
 

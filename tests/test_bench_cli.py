@@ -39,3 +39,26 @@ def test_recorded_traffic_is_dropped_when_the_sources_changed(tmp_path, monkeypa
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     _write_record(str(tmp_path), "0" * 64)
     assert bench.recorded_traffic("wl", "gemm1_silu") is None
+
+
+def _write_counters(d, cname, rows):
+    os.makedirs(d)
+    with open(os.path.join(d, "run_counter_collection.csv"), "w") as f:
+        f.write('"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"\n')
+        for i, (kernel, kib) in enumerate(rows):
+            f.write(f'{i},"{kernel}","{cname}",{kib},0,1000\n')
+
+
+def test_traffic_calibration_takes_the_copy_not_smaller_dispatches_of_its_kernel(tmp_path):
+    """The calibration copy (256 MiB read and written) shares its elementwise kernel with smaller
+    scalar multiplies of the program; the scale must come from the copy alone."""
+    from sparse_mixture_experts_02_amd.rocprof_summary import _calibrated_means
+    copy = "void at::native::vectorized_elementwise_kernel<4, at::native::AUnaryFunctor<float>>"
+    gemm = "void moe::gemm_big_kernel<true, false, false>(moe::GemmParams)"
+    mib = 1 << 20
+    fetch_dir = os.path.join(str(tmp_path), "fetch")
+    # the copy counts half its bytes, its two small siblings too; the GEMM 600 MiB
+    _write_counters(fetch_dir, "FETCH_SIZE", [(copy, 131072.0), (copy, 16384.0), (copy, 16384.0), (gemm, 614400.0)])
+    means, scale = _calibrated_means(fetch_dir, "FETCH_SIZE", "AUnaryFunctor", 256 * mib)
+    assert scale == 2.0
+    assert means[gemm] == 1200 * mib
