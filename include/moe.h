@@ -360,7 +360,10 @@ moe_status_t moe_dispatch_backward(const moe_config_t* cfg, const void* dxp, con
  * weight gradients are fp32 outputs written when not NULL: dw_router [E, d], dbias [E],
  * dw1 [E, f, d], dw2 [E, d, f], dw1_shared [fs, d], dw2_shared [d, fs]. ws is the backward
  * workspace (moe_backward_workspace_bytes). bf16/fp32 weights only (MOE_ERR_UNSUPPORTED for
- * 4-bit weights). Calls that share fwd_ws or ws must not overlap.
+ * 4-bit weights). Calls that share fwd_ws or ws must not overlap. dx: with bf16 activations,
+ * top-1 or top-2 and at most 16 experts, the kept slots' dxp rows (slot order), the shared
+ * expert's term and the router's dL W_r are summed in fp32 and rounded to act once; otherwise dx
+ * is formed as moe_dispatch_backward and then moe_route_backward form it (two roundings).
  */
 moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const float* w_router,
                           const uint8_t* token_mask, const void* w1, const void* w2,

@@ -802,6 +802,104 @@ __global__ __launch_bounds__(256) void route_bwd_dx_kernel(RouteBwdParams p) {
   }
 }
 
+// moe_backward's dx in one pass (bf16, top-1 or top-2, up to 16 experts): the sum of the token's
+// kept slots' dXp rows in slot order (as the gather backward forms it), then its shared-expert dXs
+// row, then the router term sum_e dL[t, e] W_r[e], in fp32, rounded once to act. The gather
+// backward and the router's share then need no dx written and read back between them. Layout
+// as route_bwd_dx_kernel; the rows of 4 tokens (their slots' and shared rows, 16 bytes each per
+// thread) are loaded before any of them is summed, dropped slots' rows clamped to row 0 and masked.
+constexpr int RB_DXG_TOK = 32;   // tokens per block of route_bwd_dx_gather_kernel
+constexpr int RB_DXG_NB = 4;     // tokens whose rows are in flight at once
+template <int EM>
+__global__ __launch_bounds__(256) void route_bwd_dx_gather_kernel(RouteBwdParams p) {
+  constexpr int NB = RB_DXG_NB;
+  __shared__ __attribute__((aligned(16))) float sdl[RB_DXG_TOK][EM];
+  __shared__ int srow[RB_DXG_TOK][2];
+  const int E = p.E, d = p.d, k = p.k;
+  const int t0 = blockIdx.y * RB_DXG_TOK;
+  const int c8 = blockIdx.x * RB_DX_COLS + 8 * threadIdx.x;
+  for (int i = threadIdx.x; i < RB_DXG_TOK * EM; i += 256) {
+    const int tt = i / EM, e = i % EM;
+    const int t = t0 + tt;
+    sdl[tt][e] = (t < p.T && e < E) ? p.dlogits[(size_t)t * E + e] : 0.0f;
+  }
+  for (int i = threadIdx.x; i < RB_DXG_TOK * 2; i += 256) {
+    const int tt = i >> 1, j = i & 1, t = t0 + tt;
+    const int r = (t < p.T && j < k) ? p.row_of[(size_t)t * k + j] : -1;
+    srow[tt][j] = (r >= 0 && r < p.max_rows) ? r : -1;
+  }
+  __syncthreads();
+  if (c8 >= d) return;
+  float wv[EM][8];
+#pragma unroll
+  for (int e = 0; e < EM; ++e) {
+    if (e < E) {
+      const float4 a = *(const float4*)&p.w_router[(size_t)e * d + c8];
+      const float4 b = *(const float4*)&p.w_router[(size_t)e * d + c8 + 4];
+      wv[e][0] = a.x; wv[e][1] = a.y; wv[e][2] = a.z; wv[e][3] = a.w;
+      wv[e][4] = b.x; wv[e][5] = b.y; wv[e][6] = b.z; wv[e][7] = b.w;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) wv[e][q] = 0.0f;
+    }
+  }
+  const int nt = min(RB_DXG_TOK, p.T - t0);
+  const uint16_t* const dxp = (const uint16_t*)p.dxp;
+  const uint16_t* const dxs = (const uint16_t*)p.dxs;
+  uint16_t* const dx = (uint16_t*)p.dx;
+  const bool sh = dxs != nullptr;
+  auto load = [&](int tt, rb_u32x4 (&v)[3]) {
+    v[0] = *(const rb_u32x4*)(dxp + (size_t)max(srow[tt][0], 0) * d + c8);
+    v[1] = *(const rb_u32x4*)(dxp + (size_t)max(srow[tt][1], 0) * d + c8);
+    if (sh) v[2] = *(const rb_u32x4*)(dxs + (size_t)(t0 + tt) * d + c8);
+  };
+  auto update = [&](int tt, const rb_u32x4 (&v)[3]) {
+    float a[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a[q] = 0.0f;
+#pragma unroll
+    for (int e4 = 0; e4 < EM / 4; ++e4) {
+      const float4 l = *(const float4*)&sdl[tt][4 * e4];
+      const float lv[4] = {l.x, l.y, l.z, l.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) a[q] = fmaf(lv[u], wv[4 * e4 + u][q], a[q]);
+    }
+    const bool h0 = srow[tt][0] >= 0, h1 = srow[tt][1] >= 0;
+    rb_u32x4 o;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float s2[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int sft = 16 * b;
+        float g = h0 ? fmaf(1.0f, bf16_bits_to_f32((v[0][h] >> sft) & 0xFFFFu), 0.0f) : 0.0f;
+        g = h1 ? fmaf(1.0f, bf16_bits_to_f32((v[1][h] >> sft) & 0xFFFFu), g) : g;
+        if (sh) g = __fadd_rn(g, bf16_bits_to_f32((v[2][h] >> sft) & 0xFFFFu));
+        s2[b] = __fadd_rn(g, a[2 * h + b]);
+      }
+      o[h] = f32_to_bf16_bits(s2[0]) | (f32_to_bf16_bits(s2[1]) << 16);
+    }
+    *(rb_u32x4*)(dx + (size_t)(t0 + tt) * d + c8) = o;
+  };
+  int tb = 0;
+  for (; tb + NB <= nt; tb += NB) {   // NB tokens' rows, unconditionally, before the sums
+    rb_u32x4 v[NB][3];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) load(tb + j, v[j]);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) update(tb + j, v[j]);
+  }
+  for (; tb < nt; ++tb) {
+    rb_u32x4 v[3];
+    load(tb, v);
+    update(tb, v);
+  }
+}
+
+bool route_bwd_fuses_gather(bool bf16, int E, int k) { return bf16 && E <= 16 && k <= 2; }
+
 template <bool BF16, int EM>
 __global__ __launch_bounds__(256) void route_bwd_dx1_kernel(RouteBwdParams p) {
   __shared__ __attribute__((aligned(16))) float sdl[RB_TOK][EM];
@@ -1111,7 +1209,14 @@ hipError_t launch_route_bwd(const RouteBwdParams& p_in, bool bf16, hipStream_t s
   route_bwd_kernel<<<grid, 256, 0, s>>>(p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (p.dx) {
+  if (p.dx && p.dxp) {   // dx formed from the gather and the router term (route_bwd_fuses_gather)
+    if (!route_bwd_fuses_gather(bf16, p.E, p.k)) return hipErrorInvalidValue;
+    dim3 g((p.d + RB_DX_COLS - 1) / RB_DX_COLS, (p.T + RB_DXG_TOK - 1) / RB_DXG_TOK);
+    if (p.E <= 8) route_bwd_dx_gather_kernel<8><<<g, 256, 0, s>>>(p);
+    else route_bwd_dx_gather_kernel<16><<<g, 256, 0, s>>>(p);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  } else if (p.dx) {
     dim3 g((p.d + RB_DX_COLS - 1) / RB_DX_COLS, (p.T + RB_DX_TOK - 1) / RB_DX_TOK);
 #define MOE_RBDX(K, EMV)                                                     \
     if (bf16) K<true, EMV><<<g, 256, 0, s>>>(p);                             \

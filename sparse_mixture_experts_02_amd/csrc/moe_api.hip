@@ -830,8 +830,11 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const float* w
       MOE_LAUNCH(launch_grad_w(g, bf16, stream));
     }
   }
-  // gather backward (plus the shared expert's dx), then the router's share
-  MOE_TRY(run_combine(c, dxp, row_of, nullptr, dxs, dx, stream));
+  // gather backward (plus the shared expert's dx) and the router's share: one pass that writes dx
+  // where the router backward can form it from the rows (route_bwd_fuses_gather), else the gather
+  // first and the router's share added to dx
+  const bool fused = route_bwd_fuses_gather(bf16, c.num_experts, c.top_k);
+  if (!fused) MOE_TRY(run_combine(c, dxp, row_of, nullptr, dxs, dx, stream));
   RouteBwdParams p{};
   p.T = T;
   p.d = d;
@@ -854,6 +857,12 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const float* w
   p.dw_router = dw_router;
   p.dbias = dbias;
   p.part = dw_router ? (float*)at(ws, L.rw_part) : nullptr;
+  if (fused) {
+    p.dxp = dxp;
+    p.row_of = row_of;
+    p.max_rows = T * c.top_k;
+    p.dxs = dxs;
+  }
   MOE_LAUNCH(launch_route_bwd(p, bf16, stream));
   return MOE_OK;
 }

@@ -258,7 +258,16 @@ struct RouteBwdParams {
   float* dbias;             // [E] or null
   float* part;              // [chunks, E, d] fp32 workspace of the router weight gradient
   int chunks, chunk_tokens; // set by launch_route_bwd
+  // moe_backward (route_bwd_fuses_gather): when dxp is not null, dx is written, not read: each
+  // token's dx is the sum of its kept slots' rows of dxp [max_rows, d] (row_of, slot order), then
+  // its row of dxs [T, d] when not null, then the router term, in fp32 with one rounding to act
+  const void* dxp;
+  const int32_t* row_of;    // [T, k]
+  int max_rows;
+  const void* dxs;
 };
+// Whether launch_route_bwd can also form dx from the gather (bf16, top-1 or top-2, E <= 16)
+bool route_bwd_fuses_gather(bool bf16, int E, int k);
 size_t route_bwd_part_bytes(int T, int d, int E);
 hipError_t launch_route_bwd(const RouteBwdParams& p, bool bf16, hipStream_t s);
 hipError_t launch_combine_bwd(const CombineBwdParams& p, bool bf16, hipStream_t s);
