@@ -180,6 +180,12 @@ FULL_CASES = {
     # 256 x 256 grouped GEMMs on both the routed and the shared products
     "bwd_all_big_shared": (derived(BASE, name="bwd_all_big_shared", T=2048, d_model=128, d_ffn=256, num_experts=2,
                                    d_ffn_shared=256), 0.5),
+    # dx formed in one pass from the gather and the router term: top-1 with 16 experts (a token's
+    # second row absent), and 12 experts over d = 2056 (a second 2048-column block with 8 columns)
+    "bwd_all_e16_top1": (derived(BASE, name="bwd_all_e16_top1", T=500, d_model=200, d_ffn=128, num_experts=16,
+                                 top_k=1), 1.0),
+    "bwd_all_e12_d2056": (derived(BASE, name="bwd_all_e12_d2056", T=333, d_model=2056, d_ffn=64, num_experts=12),
+                          1.0),
     # degenerate cases: every slot dropped (C = 0: only the aux term reaches the router), one token,
     # the most experts and slots (64, top-8: most experts get no rows), every token padding
     "bwd_all_zero_capacity": (derived(BASE, name="bwd_all_zero_capacity", T=200, d_model=64, d_ffn=64,
